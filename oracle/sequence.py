@@ -1,0 +1,76 @@
+"""One layer's per-chunk call sequence (oracle).
+
+Per chunk of new frames (paper.rainbus.top technical novelty: one hashing
+serves TempCache, AnnCA and AnnSA; paperlayer.ai section 3: self-attention
+keys are the current frames plus the cached earlier frames):
+
+1. hash the chunk's queries (one or two probes) and the new frames' keys;
+2. merge the new frames into the compressed cache, frame by frame (TempCache);
+3. hash the prompt keys and prune the prompt against the queries' buckets
+   (AnnCA);
+4. self-attention of the queries over the whole compressed cache, restricted
+   to their buckets, with the + ln m bias (AnnSA);
+5. cross-attention of the queries over the kept prompt tokens.
+
+Reading: merging happens every frame, in order, before attention; frames
+before the measured chunk are merged the same way as set-up.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .simhash import simhash
+from .index import bucket_index
+from .tempcache import TempCacheOracle
+from .annca import prune_prompt, cross_attention
+from .attention import bucket_attention
+
+
+def run_chunk(w, heads=None, attention=True):
+    """Run the sequence for workload-like object ``w`` on the given heads.
+
+    ``w`` provides dtype, dim, n_bits, n_probes, tau, planes [b, d], q [H, N, d],
+    and optionally k_frames/v_frames [H, F, T, d] with setup_frames, and
+    prompt_k/prompt_v [H, Np, d].  Returns a dict of per-head result dicts.
+    """
+    heads = range(w.heads) if heads is None else heads
+    scale = 1.0 / np.sqrt(w.dim)
+    res = {}
+    for h in heads:
+        r = {}
+        q = np.asarray(w.q[h], dtype=np.float64)
+        r["q_ids"] = simhash(q, w.planes, w.n_probes)
+        r["q_offsets"], r["q_perm"] = bucket_index(r["q_ids"], w.n_bits)
+        if w.k_frames is not None:
+            tc = TempCacheOracle(w.dim, w.dtype)
+            F = w.k_frames.shape[1]
+            groups = []
+            k_ids = []
+            for f in range(F):
+                kf = np.asarray(w.k_frames[h, f], dtype=np.float64)
+                ids = simhash(kf, w.planes, 1)[:, 0]
+                if f >= w.setup_frames:
+                    k_ids.append(ids)
+                if f == w.setup_frames:
+                    r["n_groups_before"] = tc.n_groups
+                g = tc.merge_frame(kf, w.v_frames[h, f], ids, w.tau)
+                if f >= w.setup_frames:
+                    groups.append(g)
+            r["k_ids"] = np.concatenate(k_ids) if k_ids else np.zeros(0, np.int64)
+            r["group_of_new"] = np.concatenate(groups) if groups else np.zeros(0, np.int64)
+            r["cache"] = tc
+            r["rep_offsets"], r["rep_perm"] = bucket_index(tc.rep_bucket, w.n_bits)
+            if attention:
+                r["o_self"], r["lse_self"] = bucket_attention(
+                    q, r["q_ids"], tc.rep_k, tc.v_mean, tc.rep_bucket,
+                    bias=tc.log_count, scale=scale)
+        if w.prompt_k is not None:
+            pk = np.asarray(w.prompt_k[h], dtype=np.float64)
+            r["p_ids"] = simhash(pk, w.planes, 1)[:, 0]
+            r["keep"], r["kept_idx"] = prune_prompt(r["q_ids"], r["p_ids"])
+            if attention:
+                r["o_cross"], r["lse_cross"] = cross_attention(
+                    q, pk, w.prompt_v[h], r["kept_idx"], scale)
+        res[h] = r
+    return res

@@ -1,0 +1,413 @@
+"""Pins of the CPU oracle to facts other than itself (no GPU needed).
+
+Each test states what fixes the expected value: the pages' Lemma 5.1, a
+library routine (torch SDPA in float64), a closed form, an invariant, or a
+tiny example worked by hand from the stated rules.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (
+    simhash, bucket_index, TempCacheOracle, prune_prompt, cross_attention,
+    dense_attention, bucket_attention, exact_dot,
+)
+from oracle.tempcache import round_to_storage
+from synth import gaussian, round_to_dtype
+
+
+def sdpa64(q, k, v, mask=None, bias=None, scale=None):
+    """torch's scaled_dot_product_attention in float64 on the CPU."""
+    qt = torch.tensor(q, dtype=torch.float64)[None, None]
+    kt = torch.tensor(k, dtype=torch.float64)[None, None]
+    vt = torch.tensor(v, dtype=torch.float64)[None, None]
+    am = None
+    if mask is not None or bias is not None:
+        am = torch.zeros(q.shape[0], k.shape[0], dtype=torch.float64)
+        if bias is not None:
+            am = am + torch.tensor(bias, dtype=torch.float64)[None, :]
+        if mask is not None:
+            am = am.masked_fill(~torch.tensor(mask), float("-inf"))
+        am = am[None, None]
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=am, scale=scale)
+    return o[0, 0].numpy()
+
+
+# --------------------------------------------------------------------------
+# SimHash
+# --------------------------------------------------------------------------
+
+def test_hash_quadrants_by_hand():
+    planes = np.array([[1.0, 0.0], [0.0, 1.0]])
+    x = np.array([[1, 2], [-1, 2], [1, -2], [-1, -2], [0, 1], [1, 0], [0, 0]], float)
+    ids = simhash(x, planes)[:, 0]
+    # bit j = [x . r_j > 0], bit 0 least significant; exact zero gives 0
+    assert ids.tolist() == [3, 2, 1, 0, 2, 1, 0]
+
+
+def test_hash_zero_vector_is_bucket_zero():
+    planes = gaussian((12, 128), 1, "bf16")
+    assert simhash(np.zeros((3, 128)), planes, 2)[:, 0].tolist() == [0, 0, 0]
+    # all distances 0: the tie goes to plane 0
+    assert simhash(np.zeros((1, 128)), planes, 2)[0, 1] == 1
+
+
+def test_hash_exact_sign_beyond_float64():
+    # x . r = 1 + 2^-60 - 1 = 2^-60 > 0, which float64 rounds to 0
+    x = np.array([[1.0, 2.0 ** -60, -1.0]])
+    r = np.array([[1.0, 1.0, 1.0]])
+    assert float(exact_dot(x[0], r[0])) == 2.0 ** -60
+    assert simhash(x, r)[0, 0] == 1
+    assert simhash(-x, r)[0, 0] == 0
+
+
+def test_second_probe_uses_normalised_distance():
+    # distances to the planes are |x.r_j|/|r_j| = 0.8 and 1.0 -> flip bit 0
+    # (the raw projections 3.2 and 1.0 would flip bit 1)
+    planes = np.array([[4.0, 0.0], [0.0, 1.0]])
+    ids = simhash(np.array([[0.8, 1.0]]), planes, 2)
+    assert ids.tolist() == [[3, 2]]
+    # equal distances: the smaller plane index is flipped
+    ids = simhash(np.array([[1.0, 1.0]]), np.eye(2), 2)
+    assert ids.tolist() == [[3, 2]]
+
+
+def test_second_probe_exact_near_tie():
+    # distances 1 and 1 + 2^-40: float64 error bounds overlap only with the
+    # exact path active when the gap is below its window; the gap here is
+    # resolvable in float64 but exercises the candidate window
+    planes = np.array([[1.0, 0.0], [0.0, 1.0]])
+    ids = simhash(np.array([[1.0 + 2.0 ** -40, 1.0]]), planes, 2)
+    assert ids.tolist() == [[3, 1]]
+
+
+def test_hash_plane_permutation_permutes_bits():
+    x = gaussian((500, 64), 2, "bf16")
+    planes = gaussian((9, 64), 3, "bf16")
+    perm = np.random.default_rng(4).permutation(9)
+    a = simhash(x, planes)[:, 0]
+    b = simhash(x, planes[perm])[:, 0]
+    bits_a = (a[:, None] >> np.arange(9)) & 1
+    bits_b = (b[:, None] >> np.arange(9)) & 1
+    assert np.array_equal(bits_b, bits_a[:, perm])
+
+
+def test_hash_negation_complements_bits():
+    x = gaussian((300, 128), 5, "bf16")
+    planes = gaussian((12, 128), 6, "bf16")
+    a = simhash(x, planes)[:, 0]
+    b = simhash(-x, planes)[:, 0]
+    assert np.array_equal(a ^ b, np.full_like(a, (1 << 12) - 1))
+
+
+def test_hash_collision_probability_charikar():
+    # P[bit agrees] = 1 - theta/pi for Gaussian hyperplanes (Charikar 2002)
+    rng = np.random.default_rng(7)
+    d = 32
+    u = rng.standard_normal(d)
+    w = rng.standard_normal(d)
+    w -= (w @ u) / (u @ u) * u
+    theta = 1.0
+    v = np.cos(theta) * u / np.linalg.norm(u) + np.sin(theta) * w / np.linalg.norm(w)
+    planes = rng.standard_normal((12, d))
+    trials = 2000
+    agree = 0
+    for t in range(trials):
+        p = rng.standard_normal((12, d))
+        ids = simhash(np.stack([u, v]), p)[:, 0]
+        agree += 12 - bin(int(ids[0] ^ ids[1])).count("1")
+    rate = agree / (12 * trials)
+    expect = 1 - theta / math.pi
+    sd = math.sqrt(expect * (1 - expect) / (12 * trials))
+    assert abs(rate - expect) < 5 * sd
+    del planes
+
+
+def test_hash_no_planes_single_bucket():
+    ids = simhash(gaussian((10, 64), 8), np.zeros((0, 64)))
+    assert ids[:, 0].tolist() == [0] * 10
+
+
+# --------------------------------------------------------------------------
+# Bucket index
+# --------------------------------------------------------------------------
+
+def test_index_by_hand_one_probe():
+    off, perm = bucket_index(np.array([3, 1, 3, 0, 1]), 2)
+    assert perm.tolist() == [3, 1, 4, 0, 2]
+    assert off.tolist() == [0, 1, 3, 3, 5]
+
+
+def test_index_by_hand_two_probes():
+    ids = np.array([[1, 0], [1, 3], [1, 0], [0, 2]])
+    off, perm = bucket_index(ids, 2)
+    # keys (first, flipped bit): (1,0) (1,1) (1,0) (0,1)
+    assert perm.tolist() == [3, 0, 2, 1]
+    assert off.tolist() == [0, 1, 4, 4, 4]
+
+
+def test_index_invariants():
+    rng = np.random.default_rng(9)
+    ids = rng.integers(0, 1 << 7, 5000)
+    off, perm = bucket_index(ids, 7)
+    assert sorted(perm.tolist()) == list(range(5000))          # a permutation
+    k = ids[perm]
+    assert np.all(np.diff(k) >= 0)                               # sorted by bucket
+    same = np.diff(k) == 0
+    assert np.all(np.diff(perm)[same] > 0)                      # stable
+    assert np.array_equal(np.diff(off), np.bincount(ids, minlength=128))
+    assert off[-1] == 5000 and off[0] == 0
+
+
+# --------------------------------------------------------------------------
+# Attention (Lemma 5.1, dense equivalence)
+# --------------------------------------------------------------------------
+
+def _dup_cache(rng, g, d, dv, max_m):
+    reps = rng.standard_normal((g, d))
+    m = rng.integers(1, max_m + 1, g)
+    keys = np.repeat(reps, m, axis=0)
+    vals = rng.standard_normal((keys.shape[0], dv))
+    owner = np.repeat(np.arange(g), m)
+    means = np.stack([vals[owner == t].mean(axis=0) for t in range(g)])
+    return reps, m, keys, vals, means
+
+
+def test_lemma_5_1_merge_is_exact():
+    rng = np.random.default_rng(10)
+    reps, m, keys, vals, means = _dup_cache(rng, 40, 64, 64, 5)
+    q = rng.standard_normal((30, 64))
+    o_full, lse_full = dense_attention(q, keys, vals)
+    o_merged, lse_merged = dense_attention(q, reps, means, bias=np.log(m))
+    assert np.max(np.abs(o_full - o_merged)) < 1e-12
+    assert np.max(np.abs(lse_full - lse_merged)) < 1e-12
+    # without the + log m shift the identity fails
+    o_nobias, _ = dense_attention(q, reps, means)
+    assert np.max(np.abs(o_full - o_nobias)) > 1e-3
+
+
+def test_lemma_no_duplicates_is_standard_attention():
+    rng = np.random.default_rng(11)
+    q, k, v = rng.standard_normal((8, 32)), rng.standard_normal((20, 32)), rng.standard_normal((20, 32))
+    o1, _ = dense_attention(q, k, v, bias=np.log(np.ones(20)))
+    assert np.max(np.abs(o1 - sdpa64(q, k, v))) < 1e-12
+
+
+def test_dense_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(12)
+    q, k, v = rng.standard_normal((16, 128)), rng.standard_normal((70, 128)), rng.standard_normal((70, 128))
+    bias = rng.standard_normal(70)
+    o, _ = dense_attention(q, k, v, bias=bias)
+    assert np.max(np.abs(o - sdpa64(q, k, v, bias=bias))) < 1e-12
+
+
+def test_one_bucket_equals_dense():
+    rng = np.random.default_rng(13)
+    q, k, v = rng.standard_normal((16, 64)), rng.standard_normal((50, 64)), rng.standard_normal((50, 64))
+    o, lse = bucket_attention(q, np.zeros((16, 1), int), k, v, np.zeros(50, int))
+    assert np.max(np.abs(o - sdpa64(q, k, v))) < 1e-12
+
+
+@pytest.mark.parametrize("probes", [1, 2])
+def test_bucket_attention_is_masked_sdpa(probes):
+    rng = np.random.default_rng(14 + probes)
+    n, m, d = 40, 300, 64
+    q, k, v = rng.standard_normal((n, d)), rng.standard_normal((m, d)), rng.standard_normal((m, d))
+    q_ids = rng.integers(0, 8, (n, probes))
+    k_b = rng.integers(0, 8, m)
+    bias = np.log(rng.integers(1, 4, m).astype(float))
+    o, lse = bucket_attention(q, q_ids, k, v, k_b, bias=bias)
+    mask = (k_b[None, :] == q_ids[:, :1])
+    if probes == 2:
+        mask |= (k_b[None, :] == q_ids[:, 1:2])
+    assert mask.any(axis=1).all()
+    ref = sdpa64(q, k, v, mask=mask, bias=bias)
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def test_empty_key_set_gives_zero():
+    q = np.ones((2, 4))
+    o, lse = bucket_attention(q, np.array([[1], [2]]), np.ones((3, 4)), np.ones((3, 4)), np.array([0, 0, 2]))
+    assert np.all(o[0] == 0) and lse[0] == -np.inf
+    assert np.allclose(o[1], 1.0)
+
+
+def test_single_key_and_equal_logits_closed_forms():
+    v = np.array([[1.0, -2.0], [3.0, 4.0]])
+    o, lse = dense_attention(np.array([[1.0, 0.0]]), np.array([[0.5, 0.5]]), v[:1])
+    assert np.array_equal(o, v[:1])
+    o, lse = dense_attention(np.array([[1.0, 0.0]]), np.array([[0.0, 1.0], [0.0, -1.0]]), v)
+    assert np.allclose(o, v.mean(axis=0), atol=0, rtol=1e-15)
+    assert abs(lse[0] - math.log(2.0)) < 1e-15
+
+
+def test_uniform_duplication_leaves_output_unchanged():
+    rng = np.random.default_rng(15)
+    q, k, v = rng.standard_normal((6, 32)), rng.standard_normal((25, 32)), rng.standard_normal((25, 32))
+    o1, _ = dense_attention(q, k, v)
+    o2, _ = dense_attention(q, k, v, bias=np.full(25, math.log(2.0)))
+    assert np.max(np.abs(o1 - o2)) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# TempCache
+# --------------------------------------------------------------------------
+
+def _run_frames(frames_k, frames_v, planes, tau, dtype="f32"):
+    tc = TempCacheOracle(frames_k.shape[-1], dtype)
+    groups = []
+    for f in range(frames_k.shape[0]):
+        ids = simhash(frames_k[f], planes)[:, 0]
+        groups.append(tc.merge_frame(frames_k[f], frames_v[f], ids, tau))
+    return tc, groups
+
+
+@pytest.mark.parametrize("tau", [0.5, 0.9, 1.0])
+def test_exact_duplicate_frames_merge_one_to_one(tau):
+    T, d, F = 64, 32, 5
+    k0 = gaussian((T, d), 20, "bf16")
+    ks = np.stack([k0] * F)
+    vs = gaussian((F, T, d), 21, "bf16")
+    tc, groups = _run_frames(ks, vs, gaussian((5, d), 22, "bf16"), tau, "bf16")
+    assert tc.n_groups == T
+    for g in groups:
+        assert g.tolist() == list(range(T))
+    assert np.all(tc.count == F)
+    assert np.array_equal(tc.v_sum, vs.astype(np.float64).sum(axis=0))
+    assert np.max(np.abs(tc.v_mean - vs.mean(axis=0))) <= 2.0 ** -8 * np.max(np.abs(vs))
+
+
+def test_threshold_above_one_merges_nothing():
+    T, d, F = 32, 16, 3
+    k0 = gaussian((T, d), 23)
+    tc, groups = _run_frames(np.stack([k0] * F), gaussian((F, T, d), 24), gaussian((3, d), 25), 1.5)
+    assert tc.n_groups == F * T
+    assert np.concatenate(groups).tolist() == list(range(F * T))
+    assert np.all(tc.count == 1)
+
+
+def test_duplicates_then_attention_is_lemma_exact():
+    # TempCache over exact duplicates composed with the biased attention must
+    # reproduce dense attention over the raw, uncompressed cache (Lemma 5.1)
+    T, d, F = 48, 32, 4
+    k0 = gaussian((T, d), 26, "bf16")
+    ks = np.stack([k0] * F)
+    vs = gaussian((F, T, d), 27, "bf16")
+    tc, _ = _run_frames(ks, vs, np.zeros((0, d)), 0.9)
+    q = gaussian((20, d), 28)
+    o_raw, _ = dense_attention(q, ks.reshape(-1, d), vs.reshape(-1, d))
+    o_tc, _ = bucket_attention(q, np.zeros((20, 1), int), tc.rep_k, tc.v_sum / tc.count[:, None],
+                               tc.rep_bucket, bias=tc.log_count)
+    assert np.max(np.abs(o_raw - o_tc)) < 1e-12
+
+
+def test_mass_conservation_random_frames():
+    T, d, F = 128, 32, 6
+    rng = np.random.default_rng(29)
+    k = np.empty((F, T, d))
+    k[0] = rng.standard_normal((T, d))
+    for f in range(1, F):
+        keep = rng.random(T) < 0.7
+        k[f] = np.where(keep[:, None], k[f - 1] + 0.02 * rng.standard_normal((T, d)),
+                        rng.standard_normal((T, d)))
+    k = round_to_dtype(k, "bf16")
+    v = gaussian((F, T, d), 30, "bf16")
+    tc, groups = _run_frames(k, v, gaussian((4, d), 31, "bf16"), 0.99, "bf16")
+    assert tc.count.sum() == F * T
+    assert np.array_equal(tc.v_sum.sum(axis=0), v.astype(np.float64).reshape(-1, d).sum(axis=0))
+    # every group's members: count equals the number of tokens mapped to it
+    allg = np.concatenate(groups)
+    assert np.array_equal(np.bincount(allg, minlength=tc.n_groups), tc.count)
+    # merged groups keep the last key as representative
+    last = {}
+    for f in range(F):
+        for j, g in enumerate(groups[f].tolist()):
+            last[g] = (f, j)
+    for g, (f, j) in last.items():
+        assert np.array_equal(tc.rep_k[g], k[f, j])
+    # within a frame no two tokens share a group (one-to-one)
+    for g in groups:
+        assert len(set(g.tolist())) == T
+    assert 0 < tc.n_groups < F * T
+
+
+def test_conflict_goes_to_highest_cosine_by_hand():
+    # frame 0: k0=(1,0) k1=(0,1); frame 1: j0=(1,.1) j1=(1,.01) j2=(0,1)
+    # j0 and j1 both pick k0; j1 has the larger cosine and wins; j0 opens
+    # group 2; j2 extends group 1.
+    tc = TempCacheOracle(2, "f32")
+    tc.merge_frame(np.array([[1.0, 0.0], [0.0, 1.0]]), np.array([[1.0, 1.0], [2.0, 2.0]]),
+                   np.zeros(2, int), 0.9)
+    g = tc.merge_frame(np.array([[1.0, 0.1], [1.0, 0.01], [0.0, 1.0]]),
+                       np.array([[3.0, 3.0], [5.0, 5.0], [4.0, 4.0]]), np.zeros(3, int), 0.9)
+    assert g.tolist() == [2, 0, 1]
+    assert tc.count.tolist() == [2, 2, 1]
+    assert tc.rep_k[0].tolist() == [1.0, 0.01]
+    assert tc.v_mean.tolist() == [[3.0, 3.0], [3.0, 3.0], [3.0, 3.0]]
+
+
+def test_ties_go_to_smaller_indices_by_hand():
+    # frame 0 has two identical keys; both new keys tie on both candidates:
+    # each picks candidate 0, and the smaller new index wins the conflict.
+    tc = TempCacheOracle(2, "f32")
+    tc.merge_frame(np.array([[1.0, 0.0], [1.0, 0.0]]), np.ones((2, 2)), np.zeros(2, int), 0.9)
+    g = tc.merge_frame(np.array([[1.0, 0.0], [3.0, 0.0]]), np.ones((2, 2)), np.zeros(2, int), 0.9)
+    assert g.tolist() == [0, 2]
+    assert tc.n_groups == 3
+    # group 1 was not extended, so its frame-0 key is no longer a candidate;
+    # frame-1 candidates are groups 0 and 2, both at cos 1: again both new
+    # keys pick candidate 0, j=0 wins and j=1 opens group 3
+    g = tc.merge_frame(np.array([[1.0, 0.0], [1.0, 0.0]]), np.ones((2, 2)), np.zeros(2, int), 0.9)
+    assert g.tolist() == [0, 3]
+    assert tc.count.tolist() == [3, 1, 1, 1]
+
+
+def test_threshold_is_inclusive_and_uses_float32_tau():
+    # cos((1,0,0,0,0), (3,2,1,1,1)) = 3/4 exactly
+    a = np.array([[1.0, 0, 0, 0, 0]])
+    b = np.array([[3.0, 2, 1, 1, 1]])
+    for tau, merges in [(0.75, True), (0.7500001, False), (0.7499999, True)]:
+        tc = TempCacheOracle(5, "f32")
+        tc.merge_frame(a, np.ones((1, 5)), np.zeros(1, int), tau)
+        g = tc.merge_frame(b, np.ones((1, 5)), np.zeros(1, int), tau)
+        assert (g[0] == 0) == merges, tau
+
+
+def test_different_buckets_never_merge():
+    tc = TempCacheOracle(2, "f32")
+    tc.merge_frame(np.array([[1.0, 0.0]]), np.ones((1, 2)), np.array([1]), 0.5)
+    g = tc.merge_frame(np.array([[1.0, 0.0]]), np.ones((1, 2)), np.array([2]), 0.5)
+    assert g.tolist() == [1]
+
+
+def test_round_to_storage_bf16_ties_to_even():
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9, -(1.0 + 2.0 ** -8)])
+    assert round_to_storage(x, "bf16").tolist() == [1.0, 1.0 + 2.0 ** -6, 1.0, -1.0]
+
+
+# --------------------------------------------------------------------------
+# AnnCA
+# --------------------------------------------------------------------------
+
+def test_prune_by_hand():
+    keep, kept = prune_prompt(np.array([[1, 5], [3, 1]]), np.array([0, 1, 2, 3, 4, 5, 1]))
+    assert keep.tolist() == [False, True, False, True, False, True, True]
+    assert kept.tolist() == [1, 3, 5, 6]
+
+
+def test_prune_single_bucket_keeps_all_and_equals_dense():
+    rng = np.random.default_rng(32)
+    q, pk, pv = rng.standard_normal((10, 64)), rng.standard_normal((40, 64)), rng.standard_normal((40, 64))
+    planes = np.zeros((0, 64))
+    keep, kept = prune_prompt(simhash(q, planes), simhash(pk, planes)[:, 0])
+    assert keep.all()
+    o, _ = cross_attention(q, pk, pv, kept)
+    assert np.max(np.abs(o - sdpa64(q, pk, pv))) < 1e-12
+
+
+def test_cross_attention_nothing_kept_is_zero():
+    o, lse = cross_attention(np.ones((3, 4)), np.ones((5, 4)), np.ones((5, 4)), np.zeros(0, int))
+    assert np.all(o == 0) and np.all(lse == -np.inf)
