@@ -1,0 +1,214 @@
+/*
+ * fastar.h -- C ABI of libfastar: the attention hot path of FAST-AR
+ * ("Fast Autoregressive Video Diffusion and World Models with Temporal Cache
+ * Compression and Sparse Attention") as hand-written HIP kernels for AMD
+ * MI355X (gfx950).
+ *
+ * Four operations, after the method's three modules and their shared hashing:
+ *   fastar_hash             SimHash bucket ids (+ bucket-contiguous index)
+ *   fastar_tempcache_merge  TempCache: merge new frames into the compressed cache
+ *   fastar_prune_prompt     AnnCA: drop prompt tokens no query shares a bucket with
+ *   fastar_bucket_attention AnnSA / AnnCA attention, online softmax on MFMA
+ *
+ * Conventions shared by every call
+ * - All tensor and array arguments are DEVICE pointers owned by the caller.
+ *   The library allocates nothing and keeps no state between calls.
+ * - Every call is enqueued on `stream` and returns without synchronising.
+ *   Counts produced on the device (groups, kept tokens) stay on the device.
+ * - Arguments are validated on the host before any launch; a failed check
+ *   returns FASTAR_ERR_INVALID or FASTAR_ERR_UNSUPPORTED and launches nothing.
+ *   A launch failure returns FASTAR_ERR_HIP.  fastar_last_error() gives a
+ *   message for the last failure in the calling thread.
+ * - Float inputs must be finite.  bf16 and fp32 are the supported dtypes;
+ *   the head dimension must be 64 or 128.
+ * - Integer decisions taken from float comparisons (hash signs, the second
+ *   probe, TempCache's arg-max, threshold and conflict tests) follow the exact
+ *   real value of the stored inputs: a decision the fast float32 evaluation
+ *   cannot certify is re-evaluated in float64 (and for hash signs, exactly).
+ *   Counters of these events accumulate in an optional fastar_diag_t.
+ */
+#ifndef FASTAR_H
+#define FASTAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FASTAR_OK = 0,
+  FASTAR_ERR_INVALID = 1,      /* bad pointer, size or combination of arguments */
+  FASTAR_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels cover   */
+  FASTAR_ERR_WORKSPACE = 3,    /* ws_bytes below what the *_workspace query says */
+  FASTAR_ERR_HIP = 4           /* a HIP launch failed                            */
+} fastar_status_t;
+
+typedef enum { FASTAR_F32 = 0, FASTAR_BF16 = 1 } fastar_dtype_t;
+
+/* A [heads][tokens][dim] tensor; dim is contiguous, strides are in elements. */
+typedef struct {
+  const void* data;
+  int32_t dtype;          /* fastar_dtype_t */
+  int32_t heads;
+  int64_t tokens;
+  int32_t dim;
+  int32_t reserved;
+  int64_t stride_head;
+  int64_t stride_token;
+} fastar_tensor_t;
+
+/* Device-side event counters.  The caller zeroes the struct; calls add. */
+typedef struct {
+  uint32_t hash_fallback_rows;   /* rows whose hash was re-evaluated in float64    */
+  uint32_t hash_exact_signs;     /* signs settled by exact expansion arithmetic     */
+  uint32_t merge_fallbacks;      /* TempCache decisions re-evaluated in float64    */
+  uint32_t unresolved;           /* decisions float64 could not certify (0 expected) */
+  uint32_t capacity_overflow;    /* new groups dropped because the cache was full  */
+  uint32_t reserved[3];
+} fastar_diag_t;
+
+const char* fastar_status_string(int status);
+const char* fastar_last_error(void);
+int fastar_version(void);
+
+/* ------------------------------------------------------------------------
+ * fastar_hash -- SimHash of the rows of x (paperlayer.ai section 5 "ANN
+ * Attention" and section 2 "Approximate nearest neighbor search"; one
+ * hashing shared by TempCache, AnnCA and AnnSA, paper.rainbus.top "technical
+ * novelty").
+ *
+ *   x        [H][N][d], bf16 or fp32.
+ *   planes   [n_bits][d], same dtype as x, contiguous: hyperplane normals r_j.
+ *   n_bits   0..15.  Bit j of an id is 1 iff x . r_j > 0 (exact value).
+ *   n_probes 1 or 2.  The second probe flips the bit of the hyperplane
+ *            nearest to x: argmin_j |x . r_j| / |r_j|, ties to smaller j
+ *            (requires n_bits >= 1).
+ *   bucket   out [H][N][n_probes] int32.
+ *   offsets  out [H][2^n_bits + 1] int32, or NULL (no index).
+ *   perm     out [H][N] int32, or NULL (together with offsets).
+ *            One probe: perm lists token indices sorted by bucket, ascending
+ *            token within a bucket; offsets[B] = number of tokens with
+ *            bucket < B.  Two probes: each token once, sorted by (first
+ *            bucket, flipped bit, token); offsets count first buckets.
+ *   ws       device workspace of at least fastar_hash_workspace() bytes.
+ *   diag     optional device counters (may be NULL).
+ * ---------------------------------------------------------------------- */
+size_t fastar_hash_workspace(int heads, int64_t n, int n_bits, int n_probes);
+fastar_status_t fastar_hash(const fastar_tensor_t* x, const void* planes, int n_bits,
+                            int n_probes, int32_t* bucket, int32_t* offsets, int32_t* perm,
+                            void* ws, size_t ws_bytes, fastar_diag_t* diag,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fastar_bucket_index -- the bucket-contiguous index of fastar_hash on its
+ * own, for ids already computed (e.g. the representatives of a cache).
+ *   bucket  [H][n][n_probes] int32.
+ *   n_valid optional device [H]: only the first min(n_valid[h], n) entries of
+ *           head h are indexed (NULL: all n).
+ *   offsets [H][2^n_bits + 1], perm [H][n]: as for fastar_hash.
+ * ---------------------------------------------------------------------- */
+size_t fastar_bucket_index_workspace(int heads, int64_t n);
+fastar_status_t fastar_bucket_index(const int32_t* bucket, int heads, int64_t n, int n_probes,
+                                    int n_bits, const int32_t* n_valid, int32_t* offsets,
+                                    int32_t* perm, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * TempCache compressed cache (paperlayer.ai section 5 "TempCache" and
+ * appendix A, Lemma 5.1: a group of m identical keys is attended exactly
+ * through one key with the group-mean value and logit + log m).
+ * Every buffer is caller-owned device memory, head-major:
+ *   rep_k      [H][capacity][dim]  representative (most recent) key, dtype
+ *   v_mean     [H][capacity][dim]  group mean value, dtype (rounded once)
+ *   v_sum      [H][capacity][dim]  float32 running value sum
+ *   count      [H][capacity]       int32 group size m
+ *   log_count  [H][capacity]       float32 ln m (the attention bias)
+ *   rep_bucket [H][capacity]       int32 bucket id of the representative
+ *   n_groups   [H]                 int32 groups in use (0 = empty cache)
+ *   frontier   [H][tokens_per_frame] int32 group of each token of the last
+ *                                  merged frame
+ * An empty cache is one with n_groups all 0; nothing else needs clearing.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t heads, dim, capacity, tokens_per_frame, n_bits, dtype;
+  void* rep_k;
+  void* v_mean;
+  float* v_sum;
+  int32_t* count;
+  float* log_count;
+  int32_t* rep_bucket;
+  int32_t* n_groups;
+  int32_t* frontier;
+} fastar_cache_t;
+
+/* fastar_tempcache_merge -- merge n_frames new frames, in order.
+ *   k_new, v_new  [H][n_frames * tokens_per_frame][dim], cache dtype.
+ *   k_new_bucket  [H][n_frames * tokens_per_frame] int32 (fastar_hash, one
+ *                 probe, same planes as the queries).
+ *   tau           cosine threshold (compared as its float32 value).
+ * For each new key j of frame f: candidates are frame f-1's tokens with j's
+ * bucket; j proposes to the candidate of largest cosine (ties to the smaller
+ * index) if that cosine >= tau; each candidate accepts its proposer of
+ * largest cosine (ties to smaller j); accepted keys extend the candidate's
+ * group (count+1, value sum += v_j, representative := k_j), all others open
+ * new groups in ascending j.
+ *   group_of_new  out [H][n_frames * tokens_per_frame] or NULL: group id of
+ *                 each new token (-1 if dropped for lack of capacity).
+ *   rep_offsets   out [H][2^n_bits + 1], rep_perm out [H][capacity], or both
+ *                 NULL: bucket index of the representatives after the merge.
+ */
+size_t fastar_tempcache_workspace(const fastar_cache_t* cache, int n_frames);
+fastar_status_t fastar_tempcache_merge(const fastar_cache_t* cache, const fastar_tensor_t* k_new,
+                                       const fastar_tensor_t* v_new,
+                                       const int32_t* k_new_bucket, int n_frames, float tau,
+                                       int32_t* group_of_new, int32_t* rep_offsets,
+                                       int32_t* rep_perm, void* ws, size_t ws_bytes,
+                                       fastar_diag_t* diag, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fastar_prune_prompt -- AnnCA (gist.science technical summary, AnnCA; the
+ * Chinese summary's method steps): per head, keep the prompt tokens whose
+ * bucket is occupied by at least one probe of at least one query.
+ *   q_bucket [H][n_q][n_probes], p_bucket [H][n_prompt] int32.
+ *   keep     out [H][n_prompt] uint8 (0/1).
+ *   kept_idx out [H][n_prompt] int32: kept indices ascending, first n_kept[h].
+ *   n_kept   out [H] int32.
+ * ---------------------------------------------------------------------- */
+fastar_status_t fastar_prune_prompt(const int32_t* q_bucket, int heads, int64_t n_q,
+                                    int n_probes, const int32_t* p_bucket, int64_t n_prompt,
+                                    int n_bits, uint8_t* keep, int32_t* kept_idx,
+                                    int32_t* n_kept, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fastar_bucket_attention -- o_q = sum_j softmax_j(scale * q.k_j + bias_j) v_j
+ * over a per-query key set (AnnSA: paperlayer.ai section 5 "AnnSA",
+ * gist.science AnnSA; bias ln m from Lemma 5.1).  Three modes:
+ *   bucket  k_offsets and k_perm given: query t attends to the keys listed in
+ *           the segments of its bucket(s) q_bucket[h][t][0..n_probes).  Rows
+ *           are visited in q_perm order (the index from fastar_hash).
+ *   list    key_list and n_key_list given: every query attends to
+ *           key_list[h][0 .. n_key_list[h]) (AnnCA over the kept prompt).
+ *   dense   neither: every query attends to all k->tokens keys.
+ *   q      [H][Nq][d]; k, v [H][Nk][d], all the same dtype.
+ *   key_bias [H][Nk] float32 or NULL (k's head stride is not used for it:
+ *           the bias row of head h starts at h * k->tokens).
+ *   out    [H][Nq][d] contiguous, dtype of q.
+ *   lse    [H][Nq] float32 natural-log normaliser, or NULL.
+ *   A query with an empty key set gets out = 0 and lse = -inf.
+ * ---------------------------------------------------------------------- */
+fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t* q_bucket,
+                                        const int32_t* q_perm, int n_probes,
+                                        const fastar_tensor_t* k, const fastar_tensor_t* v,
+                                        const float* key_bias, const int32_t* k_offsets,
+                                        const int32_t* k_perm, int n_bits,
+                                        const int32_t* key_list, const int32_t* n_key_list,
+                                        float scale, void* out, float* lse,
+                                        hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FASTAR_H */

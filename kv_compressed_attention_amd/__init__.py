@@ -1,0 +1,20 @@
+"""FAST-AR attention hot path for AMD MI355X: Python binding of libfastar.
+
+The compute runs in the HIP library ``libfastar.so`` (built in-tree by
+``__graft_entry__.build()``); this package only marshals torch tensors
+(device memory and streams) into its C ABI.  Importing the binding does not
+load the library; the first call does, and fails loudly if it is missing.
+"""
+
+from .fastar import (  # noqa: F401
+    FastarError,
+    TempCache,
+    fastar_bucket_attention,
+    fastar_bucket_index,
+    fastar_hash,
+    fastar_prune_prompt,
+    fastar_tempcache_merge,
+    fastar_version,
+    library,
+    new_diag,
+)

@@ -1,0 +1,342 @@
+// Bucket-restricted flash attention (AnnSA / AnnCA) on gfx950.
+//
+// o_q = sum_j softmax_j(scale * q.k_j + bias_j) v_j, where the key set of q
+// is the keys of its bucket(s) (AnnSA: paperlayer.ai section 5 "AnnSA",
+// gist.science AnnSA), a kept-prompt list (AnnCA), or all keys; bias_j is
+// ln m_j for a TempCache group of m_j merged keys (Lemma 5.1, paperlayer.ai
+// appendix A).
+//
+// bf16 kernel layout.  A wave owns 16 query rows, taken in index (bucket)
+// order, so a wave's rows usually share one or a few buckets.  It walks the
+// distinct buckets of its rows (both probes) in ascending order; for each it
+// streams that bucket's keys in chunks of 32 with rows outside the bucket
+// masked.  Per chunk:
+//   S^T[32 keys x 16 rows] = K Q^T   two v_mfma_f32_16x16x32_bf16 groups,
+//                                      K gathered straight from HBM (each lane
+//                                      reads 64 contiguous bytes of one key);
+//   online softmax in float32 with exp2, row max shared by the 4 lanes of a row;
+//   O^T[d x 16 rows] += V^T P^T         d/16 MFMAs.  P^T comes out of S^T's
+//                                      accumulator layout with no shuffles; V^T
+//                                      is built in registers: each lane loads 16
+//                                      contiguous bytes of 8 keys and transposes
+//                                      8x8 16-bit values, so V needs no LDS.
+// The dims of O^T are interleaved (row r of block b is dim (d/16) r + b) so
+// that every lane finally holds 32 (d=128) contiguous output dims.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace fastar {
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int NB>
+struct VRow;
+template <>
+struct VRow<8> {  // d = 128: 8 bf16 per lane per key
+  uint4 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ uint32_t get(int b) const {
+    const uint32_t w = (b < 2) ? u.x : (b < 4) ? u.y : (b < 6) ? u.z : u.w;
+    return (b & 1) ? (w >> 16) : (w & 0xFFFFu);
+  }
+};
+template <>
+struct VRow<4> {  // d = 64: 4 bf16 per lane per key
+  uint2 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ uint32_t get(int b) const {
+    const uint32_t w = (b < 2) ? u.x : u.y;
+    return (b & 1) ? (w >> 16) : (w & 0xFFFFu);
+  }
+};
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int m = 1; m < FASTAR_WAVE; m <<= 1) v = min(v, shfl_xor_i(v, m));
+  return v;
+}
+
+// MODE: 0 bucket, 1 key list, 2 dense
+template <int D, int P, int MODE>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(
+    const uint16_t* __restrict__ q, int64_t q_sh, int64_t q_st, int64_t Nq,
+    const int32_t* __restrict__ q_bucket, const int32_t* __restrict__ q_perm,
+    const uint16_t* __restrict__ k, int64_t k_sh, int64_t k_st,
+    const uint16_t* __restrict__ v, int64_t v_sh, int64_t v_st, int64_t Nk,
+    const float* __restrict__ key_bias, const int32_t* __restrict__ k_offsets,
+    const int32_t* __restrict__ k_perm, int nbits, const int32_t* __restrict__ key_list,
+    const int32_t* __restrict__ n_key_list, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  constexpr int NC = D / 32;  // k-chunks of the QK^T contraction
+  constexpr int NB = D / 16;  // 16-dim output blocks
+  const int h = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int l = lane_id();
+  const int col = l & 15;
+  const int g = l >> 4;
+  const int64_t r0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  if (r0 >= Nq) return;
+  const int64_t r = r0 + col;
+  const bool rvalid = r < Nq;
+  int64_t t = r0;
+  if (rvalid) t = (MODE == 0) ? (int64_t)q_perm[(int64_t)h * Nq + r] : r;
+
+  // B operand of S^T = K Q^T: query row `col`, dims 32c + 8g .. +8
+  bf16x8_t qop[NC];
+  {
+    const uint16_t* qrow = q + (int64_t)h * q_sh + t * q_st;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g);
+      if (!rvalid) u = make_uint4(0u, 0u, 0u, 0u);
+      qop[c] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  }
+  float m = -INFINITY;
+  float lsum = 0.f;
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kh = k + (int64_t)h * k_sh;
+  const uint16_t* vh = v + (int64_t)h * v_sh;
+  const float* bh = key_bias ? key_bias + (int64_t)h * Nk : nullptr;
+  const int32_t* idx_h = nullptr;
+  if (MODE == 0) idx_h = k_perm + (int64_t)h * Nk;
+  if (MODE == 1) idx_h = key_list + (int64_t)h * Nk;
+
+  int b0 = INT_MAX, b1 = INT_MAX;
+  if (MODE == 0 && rvalid) {
+    const int32_t* qb = q_bucket + ((int64_t)h * Nq + t) * P;
+    b0 = qb[0];
+    if (P == 2) b1 = qb[1];
+  }
+  bool first_pass = true;
+  while (true) {
+    int64_t kbeg, kend;
+    bool rowin;
+    if (MODE == 0) {
+      const int X = wave_min_i(min(b0, b1));
+      if (X == INT_MAX) break;
+      rowin = (b0 == X) || (b1 == X);
+      if (b0 == X) b0 = INT_MAX;
+      if (b1 == X) b1 = INT_MAX;
+      const int32_t* off = k_offsets + (int64_t)h * ((1 << nbits) + 1) + X;
+      kbeg = off[0];
+      kend = off[1];
+    } else {
+      if (!first_pass) break;
+      kbeg = 0;
+      kend = Nk;
+      if (MODE == 1) {
+        const int64_t nl = n_key_list[h];
+        kend = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
+      }
+      rowin = rvalid;
+    }
+    first_pass = false;
+    for (int64_t kc = kbeg; kc < kend; kc += 32) {
+      // key of slot `col` in each 16-key half (clamped to a valid key)
+      int kid[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        int64_t kk = kc + 16 * hf + col;
+        if (kk >= kend) kk = kbeg;
+        kid[hf] = (MODE == 2) ? (int)kk : idx_h[kk];
+      }
+      float s[8];
+      int sk[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint16_t* krow = kh + (int64_t)kid[hf] * k_st;
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const uint4 u = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * g);
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u), qop[c], sacc, 0, 0, 0);
+        }
+        // sacc[i] = score(key slot 16hf + 4g + i, row col)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int slot = 4 * g + i;
+          const int key = __shfl(kid[hf], slot, FASTAR_WAVE);
+          sk[4 * hf + i] = key;
+          const bool kvalid = kc + 16 * hf + slot < kend;
+          float x = sacc[i] * scale_log2;
+          if (bh) x += bh[key] * kLog2e;
+          s[4 * hf + i] = (kvalid && rowin) ? x : -INFINITY;
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float mnew = fmaxf(m, mx);
+      const float base = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = exp2f(m - base);
+      m = mnew;
+      uint32_t pw[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = f32_to_bf16_bits(exp2f(s[2 * i] - base));
+        const uint32_t hi = f32_to_bf16_bits(exp2f(s[2 * i + 1] - base));
+        psum += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
+        pw[i] = lo | (hi << 16);
+      }
+      lsum = lsum * alpha + psum;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        acc[b][0] *= alpha;
+        acc[b][1] *= alpha;
+        acc[b][2] *= alpha;
+        acc[b][3] *= alpha;
+      }
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      // V^T operand: lane (dim-row col, group g), slot si <-> key sk[si],
+      // dims NB*col .. NB*col + NB - 1 (one per output block)
+      VRow<NB> vr[8];
+#pragma unroll
+      for (int si = 0; si < 8; ++si) vr[si].load(vh + (int64_t)sk[si] * v_st + NB * col);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint4 w = make_uint4(vr[0].get(b) | (vr[1].get(b) << 16), vr[2].get(b) | (vr[3].get(b) << 16),
+                                   vr[4].get(b) | (vr[5].get(b) << 16), vr[6].get(b) | (vr[7].get(b) << 16));
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[b], 0, 0, 0);
+      }
+    }
+  }
+  lsum += shfl_xor_f(lsum, 16);
+  lsum += shfl_xor_f(lsum, 32);
+  if (!rvalid) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  // acc[b][i] = O[row col][NB*(4g+i) + b]: dims 4*NB*g .. 4*NB*g + 4*NB - 1
+  uint32_t ow[2 * NB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int b = 0; b < NB; b += 2) {
+      const uint32_t lo = f32_to_bf16_bits(acc[b][i] * inv);
+      const uint32_t hi = f32_to_bf16_bits(acc[b + 1][i] * inv);
+      ow[(i * NB + b) / 2] = lo | (hi << 16);
+    }
+  uint16_t* orow = out + ((int64_t)h * Nq + t) * D + 4 * NB * g;
+#pragma unroll
+  for (int j = 0; j < NB / 2; ++j)
+    reinterpret_cast<uint4*>(orow)[j] = make_uint4(ow[4 * j], ow[4 * j + 1], ow[4 * j + 2], ow[4 * j + 3]);
+  if (lse && g == 0) lse[(int64_t)h * Nq + t] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
+}
+
+// fp32: one query row per lane on the vector ALUs (no fp32 MFMA rounding
+// concerns; the fp32 workloads are small).
+template <int D, int P, int MODE>
+__global__ __launch_bounds__(64) void attn_f32_kernel(
+    const float* __restrict__ q, int64_t q_sh, int64_t q_st, int64_t Nq,
+    const int32_t* __restrict__ q_bucket, const int32_t* __restrict__ q_perm,
+    const float* __restrict__ k, int64_t k_sh, int64_t k_st, const float* __restrict__ v,
+    int64_t v_sh, int64_t v_st, int64_t Nk, const float* __restrict__ key_bias,
+    const int32_t* __restrict__ k_offsets, const int32_t* __restrict__ k_perm, int nbits,
+    const int32_t* __restrict__ key_list, const int32_t* __restrict__ n_key_list, float scale,
+    float* __restrict__ out, float* __restrict__ lse) {
+  const int h = blockIdx.y;
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= Nq) return;
+  const int64_t t = (MODE == 0) ? (int64_t)q_perm[(int64_t)h * Nq + r] : r;
+  float qr[D], acc[D];
+  const float* qrow = q + (int64_t)h * q_sh + t * q_st;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qr[d] = qrow[d];
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, lsum = 0.f;
+  const float* kh = k + (int64_t)h * k_sh;
+  const float* vh = v + (int64_t)h * v_sh;
+  const float* bh = key_bias ? key_bias + (int64_t)h * Nk : nullptr;
+  int buckets[2] = {0, -1};
+  int nseg = 1;
+  if (MODE == 0) {
+    const int32_t* qb = q_bucket + ((int64_t)h * Nq + t) * P;
+    buckets[0] = qb[0];
+    if (P == 2) {
+      buckets[1] = qb[1];
+      nseg = 2;
+    }
+  }
+  for (int sgi = 0; sgi < nseg; ++sgi) {
+    int64_t kbeg = 0, kend = Nk;
+    const int32_t* idx = nullptr;
+    if (MODE == 0) {
+      const int32_t* off = k_offsets + (int64_t)h * ((1 << nbits) + 1) + buckets[sgi];
+      kbeg = off[0];
+      kend = off[1];
+      idx = k_perm + (int64_t)h * Nk;
+    } else if (MODE == 1) {
+      const int64_t nl = n_key_list[h];
+      kend = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
+      idx = key_list + (int64_t)h * Nk;
+    }
+    for (int64_t kk = kbeg; kk < kend; ++kk) {
+      const int64_t key = idx ? idx[kk] : kk;
+      const float* krow = kh + key * k_st;
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) s = fmaf(qr[d], krow[d], s);
+      s = s * scale + (bh ? bh[key] : 0.f);
+      const float mnew = fmaxf(m, s);
+      const float alpha = expf(m - mnew);
+      const float p = expf(s - mnew);
+      m = mnew;
+      lsum = lsum * alpha + p;
+      const float* vrow = vh + key * v_st;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vrow[d], acc[d] * alpha);
+    }
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  float* orow = out + ((int64_t)h * Nq + t) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
+  if (lse) lse[(int64_t)h * Nq + t] = lsum > 0.f ? m + logf(lsum) : -INFINITY;
+}
+
+template <int D, int P, int MODE>
+hipError_t launch3(const AttnArgs& a, hipStream_t s) {
+  if (a.dtype == FASTAR_BF16) {
+    dim3 grid((unsigned)((a.nq + 63) / 64), (unsigned)a.heads);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, P, MODE>), grid, dim3(256), 0, s,
+                       (const uint16_t*)a.q, a.q_sh, a.q_st, a.nq, a.q_bucket, a.q_perm,
+                       (const uint16_t*)a.k, a.k_sh, a.k_st, (const uint16_t*)a.v, a.v_sh, a.v_st,
+                       a.nk, a.key_bias, a.k_offsets, a.k_perm, a.n_bits, a.key_list,
+                       a.n_key_list, a.scale * kLog2e, (uint16_t*)a.out, a.lse);
+  } else {
+    dim3 grid((unsigned)((a.nq + 63) / 64), (unsigned)a.heads);
+    hipLaunchKernelGGL((attn_f32_kernel<D, P, MODE>), grid, dim3(64), 0, s,
+                       (const float*)a.q, a.q_sh, a.q_st, a.nq, a.q_bucket, a.q_perm,
+                       (const float*)a.k, a.k_sh, a.k_st, (const float*)a.v, a.v_sh, a.v_st,
+                       a.nk, a.key_bias, a.k_offsets, a.k_perm, a.n_bits, a.key_list,
+                       a.n_key_list, a.scale, (float*)a.out, a.lse);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+  if (a.mode == 0) return a.n_probes == 2 ? launch3<D, 2, 0>(a, s) : launch3<D, 1, 0>(a, s);
+  if (a.mode == 1) return launch3<D, 1, 1>(a, s);
+  return launch3<D, 1, 2>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.heads == 0 || a.nq == 0) return hipSuccess;
+  return a.dim == 64 ? launch_d<64>(a, s) : launch_d<128>(a, s);
+}
+
+}  // namespace fastar

@@ -1,0 +1,54 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fastar.h"
+
+namespace fastar {
+
+// hash.hip ------------------------------------------------------------------
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
+hipError_t launch_hash(const fastar_tensor_t& x, const void* planes, int n_bits, int n_probes,
+                       int32_t* bucket, uint32_t* queue, uint32_t* queue_count,
+                       fastar_diag_t* diag, hipStream_t s);
+
+// index.hip -----------------------------------------------------------------
+hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int n_probes,
+                               int n_bits, const int32_t* n_valid, int32_t* offsets,
+                               int32_t* perm, int32_t* ws, hipStream_t s);
+
+// prune.hip -----------------------------------------------------------------
+hipError_t launch_prune(const int32_t* q_bucket, int heads, int64_t n_q, int n_probes,
+                        const int32_t* p_bucket, int64_t n_prompt, int n_bits, uint8_t* keep,
+                        int32_t* kept_idx, int32_t* n_kept, hipStream_t s);
+
+// attention.hip -------------------------------------------------------------
+struct AttnArgs {
+  const void* q; int64_t q_sh, q_st, nq;
+  const int32_t* q_bucket; const int32_t* q_perm; int n_probes;
+  const void* k; int64_t k_sh, k_st;
+  const void* v; int64_t v_sh, v_st; int64_t nk;
+  const float* key_bias; const int32_t* k_offsets; const int32_t* k_perm; int n_bits;
+  const int32_t* key_list; const int32_t* n_key_list;
+  float scale; void* out; float* lse;
+  int heads, dim, dtype, mode;  // mode: 0 bucket, 1 list, 2 dense
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+// tempcache.hip -------------------------------------------------------------
+struct MergeWs {
+  int32_t* ng;        // [n_frames + 1][H]
+  int32_t* target;    // [H][T]
+  float* tcos;        // [H][T]
+  int32_t* mgroup;    // [H][T]
+  int32_t* index_ws;  // bucket index scratch
+};
+hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
+                                  const fastar_tensor_t& v_new, const int32_t* k_new_bucket,
+                                  int n_frames, float tau, int32_t* group_of_new,
+                                  int32_t* rep_offsets, int32_t* rep_perm, const MergeWs& ws,
+                                  fastar_diag_t* diag, hipStream_t s);
+
+}  // namespace fastar

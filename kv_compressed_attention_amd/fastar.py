@@ -1,0 +1,287 @@
+"""ctypes binding of libfastar (include/fastar.h).
+
+Argument marshalling only: every step of the hot path runs in the HIP
+kernels of libfastar.so.  torch supplies device memory and the stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfastar.so")
+
+_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class FastarTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("tokens", ctypes.c_int64),
+        ("dim", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("stride_head", ctypes.c_int64),
+        ("stride_token", ctypes.c_int64),
+    ]
+
+
+class FastarCache(ctypes.Structure):
+    _fields_ = [
+        ("heads", ctypes.c_int32),
+        ("dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("tokens_per_frame", ctypes.c_int32),
+        ("n_bits", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("rep_k", ctypes.c_void_p),
+        ("v_mean", ctypes.c_void_p),
+        ("v_sum", ctypes.c_void_p),
+        ("count", ctypes.c_void_p),
+        ("log_count", ctypes.c_void_p),
+        ("rep_bucket", ctypes.c_void_p),
+        ("n_groups", ctypes.c_void_p),
+        ("frontier", ctypes.c_void_p),
+    ]
+
+
+class FastarError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libfastar status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_TP = ctypes.POINTER(FastarTensor)
+_CP = ctypes.POINTER(FastarCache)
+
+_SIGNATURES = {
+    "fastar_status_string": (ctypes.c_char_p, [_I]),
+    "fastar_last_error": (ctypes.c_char_p, []),
+    "fastar_version": (_I, []),
+    "fastar_hash_workspace": (_SZ, [_I, _I64, _I, _I]),
+    "fastar_hash": (_I, [_TP, _P, _I, _I, _P, _P, _P, _P, _SZ, _P, _P]),
+    "fastar_bucket_index_workspace": (_SZ, [_I, _I64]),
+    "fastar_bucket_index": (_I, [_P, _I, _I64, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "fastar_tempcache_workspace": (_SZ, [_CP, _I]),
+    "fastar_tempcache_merge": (_I, [_CP, _TP, _TP, _P, _I, _F, _P, _P, _P, _P, _SZ, _P, _P]),
+    "fastar_prune_prompt": (_I, [_P, _I, _I64, _I, _P, _I64, _I, _P, _P, _P, _P]),
+    "fastar_bucket_attention": (_I, [_TP, _P, _P, _I, _TP, _TP, _P, _P, _P, _I, _P, _P, _F, _P, _P, _P]),
+}
+
+
+def library():
+    """Load libfastar.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = library()
+        raise FastarError(status, f"{lib.fastar_status_string(status).decode()}: "
+                                  f"{lib.fastar_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("array arguments must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _desc(t: torch.Tensor) -> FastarTensor:
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError("expected a [heads, tokens, dim] tensor with a contiguous last dim")
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return FastarTensor(t.data_ptr(), _DTYPES[t.dtype], t.shape[0], t.shape[1], t.shape[2], 0,
+                        t.stride(0), t.stride(1))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _i32(shape, device):
+    return torch.empty(shape, dtype=torch.int32, device=device)
+
+
+def _ws(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes < {nbytes}")
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def new_diag(device="cuda") -> torch.Tensor:
+    """Zeroed fastar_diag_t counters (8 x int32) on the device."""
+    return torch.zeros(8, dtype=torch.int32, device=device)
+
+
+def fastar_version() -> int:
+    return library().fastar_version()
+
+
+def fastar_hash(x, planes, n_bits: int, n_probes: int = 1, with_index: bool = True,
+                bucket=None, offsets=None, perm=None, ws=None, diag=None, stream=None):
+    """Bucket ids [H, N, P] (+ offsets [H, 2^b+1], perm [H, N]) of x [H, N, d]."""
+    lib = library()
+    H, N, _ = x.shape
+    if bucket is None:
+        bucket = _i32((H, N, n_probes), x.device)
+    if with_index:
+        if offsets is None:
+            offsets = _i32((H, (1 << n_bits) + 1), x.device)
+        if perm is None:
+            perm = _i32((H, N), x.device)
+    else:
+        offsets = perm = None
+    nbytes = lib.fastar_hash_workspace(H, N, n_bits, n_probes)
+    ws = _ws(nbytes, x.device, ws)
+    d = _desc(x)
+    _check(lib.fastar_hash(ctypes.byref(d), _ptr(planes), n_bits, n_probes, _ptr(bucket),
+                           _ptr(offsets), _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(),
+                           _ptr(diag), _stream(stream)))
+    return bucket, offsets, perm
+
+
+def fastar_bucket_index(bucket, n_bits: int, n_valid=None, offsets=None, perm=None, ws=None,
+                        stream=None):
+    """Index of precomputed ids bucket [H, n, P]."""
+    lib = library()
+    H, n, P = bucket.shape
+    if offsets is None:
+        offsets = _i32((H, (1 << n_bits) + 1), bucket.device)
+    if perm is None:
+        perm = _i32((H, n), bucket.device)
+    ws = _ws(lib.fastar_bucket_index_workspace(H, n), bucket.device, ws)
+    _check(lib.fastar_bucket_index(_ptr(bucket), H, n, P, n_bits, _ptr(n_valid), _ptr(offsets),
+                                   _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+    return offsets, perm
+
+
+class TempCache:
+    """Device buffers of one layer's compressed cache (fastar_cache_t)."""
+
+    def __init__(self, heads, dim, capacity, tokens_per_frame, n_bits, dtype=torch.bfloat16,
+                 device="cuda"):
+        self.heads, self.dim, self.capacity = heads, dim, capacity
+        self.tokens_per_frame, self.n_bits, self.dtype = tokens_per_frame, n_bits, dtype
+        z = dict(device=device)
+        self.rep_k = torch.zeros(heads, capacity, dim, dtype=dtype, **z)
+        self.v_mean = torch.zeros(heads, capacity, dim, dtype=dtype, **z)
+        self.v_sum = torch.zeros(heads, capacity, dim, dtype=torch.float32, **z)
+        self.count = torch.zeros(heads, capacity, dtype=torch.int32, **z)
+        self.log_count = torch.zeros(heads, capacity, dtype=torch.float32, **z)
+        self.rep_bucket = torch.zeros(heads, capacity, dtype=torch.int32, **z)
+        self.n_groups = torch.zeros(heads, dtype=torch.int32, **z)
+        self.frontier = torch.full((heads, tokens_per_frame), -1, dtype=torch.int32, **z)
+
+    def buffers(self):
+        return dict(rep_k=self.rep_k, v_mean=self.v_mean, v_sum=self.v_sum, count=self.count,
+                    log_count=self.log_count, rep_bucket=self.rep_bucket,
+                    n_groups=self.n_groups, frontier=self.frontier)
+
+    def copy_from(self, other: "TempCache"):
+        for name, t in self.buffers().items():
+            t.copy_(getattr(other, name))
+
+    def struct(self) -> FastarCache:
+        return FastarCache(self.heads, self.dim, self.capacity, self.tokens_per_frame, self.n_bits,
+                           _DTYPES[self.dtype], self.rep_k.data_ptr(), self.v_mean.data_ptr(),
+                           self.v_sum.data_ptr(), self.count.data_ptr(),
+                           self.log_count.data_ptr(), self.rep_bucket.data_ptr(),
+                           self.n_groups.data_ptr(), self.frontier.data_ptr())
+
+    def workspace_bytes(self, n_frames: int) -> int:
+        c = self.struct()
+        return library().fastar_tempcache_workspace(ctypes.byref(c), n_frames)
+
+
+def fastar_tempcache_merge(cache: TempCache, k_new, v_new, k_new_bucket, n_frames: int,
+                           tau: float, group_of_new=None, with_index: bool = True,
+                           rep_offsets=None, rep_perm=None, ws=None, diag=None, stream=None):
+    """Merge n_frames frames (k_new, v_new [H, n_frames*T, d]) into the cache."""
+    lib = library()
+    H = cache.heads
+    dev = k_new.device
+    if with_index:
+        if rep_offsets is None:
+            rep_offsets = _i32((H, (1 << cache.n_bits) + 1), dev)
+        if rep_perm is None:
+            rep_perm = _i32((H, cache.capacity), dev)
+    else:
+        rep_offsets = rep_perm = None
+    c = cache.struct()
+    ws = _ws(lib.fastar_tempcache_workspace(ctypes.byref(c), n_frames), dev, ws)
+    dk, dv = _desc(k_new), _desc(v_new)
+    _check(lib.fastar_tempcache_merge(ctypes.byref(c), ctypes.byref(dk), ctypes.byref(dv),
+                                      _ptr(k_new_bucket), n_frames, float(tau), _ptr(group_of_new),
+                                      _ptr(rep_offsets), _ptr(rep_perm), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _ptr(diag), _stream(stream)))
+    return rep_offsets, rep_perm
+
+
+def fastar_prune_prompt(q_bucket, p_bucket, n_bits: int, keep=None, kept_idx=None, n_kept=None,
+                        stream=None):
+    """AnnCA keep mask [H, Np] (uint8), kept indices [H, Np], counts [H]."""
+    lib = library()
+    H, nq, P = q_bucket.shape
+    npr = p_bucket.shape[1]
+    dev = q_bucket.device
+    if keep is None:
+        keep = torch.empty(H, npr, dtype=torch.uint8, device=dev)
+    if kept_idx is None:
+        kept_idx = _i32((H, npr), dev)
+    if n_kept is None:
+        n_kept = _i32((H,), dev)
+    _check(lib.fastar_prune_prompt(_ptr(q_bucket), H, nq, P, _ptr(p_bucket), npr, n_bits,
+                                   _ptr(keep), _ptr(kept_idx), _ptr(n_kept), _stream(stream)))
+    return keep, kept_idx, n_kept
+
+
+def fastar_bucket_attention(q, k, v, scale: Optional[float] = None, q_bucket=None, q_perm=None,
+                            key_bias=None, k_offsets=None, k_perm=None, n_bits: int = 0,
+                            key_list=None, n_key_list=None, out=None, lse=None,
+                            want_lse: bool = True, stream=None):
+    """Bucket (AnnSA), list (AnnCA) or dense attention; returns (out, lse)."""
+    lib = library()
+    H, nq, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty(H, nq, d, dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(H, nq, dtype=torch.float32, device=q.device)
+    n_probes = 1 if q_bucket is None else q_bucket.shape[2]
+    dq, dk, dv = _desc(q), _desc(k), _desc(v)
+    _check(lib.fastar_bucket_attention(ctypes.byref(dq), _ptr(q_bucket), _ptr(q_perm), n_probes,
+                                       ctypes.byref(dk), ctypes.byref(dv), _ptr(key_bias),
+                                       _ptr(k_offsets), _ptr(k_perm), n_bits, _ptr(key_list),
+                                       _ptr(n_key_list), float(scale), _ptr(out), _ptr(lse),
+                                       _stream(stream)))
+    return out, lse

@@ -1,0 +1,107 @@
+"""One attention layer's per-chunk sequence over libfastar, with preallocated
+buffers so that repeated steps do no allocation.
+
+Order (one hashing serves all three modules; the self-attention keys are the
+compressed cache including the chunk's own frames):
+  1. hash the chunk's queries (1 or 2 probes) and build their bucket index;
+  2. hash the chunk's new keys;
+  3. TempCache-merge the new frames, frame by frame, and index the
+     representatives by bucket;
+  4. hash the prompt keys and prune them against the queries' buckets (AnnCA);
+  5. AnnSA bucket attention over the cache with the + ln m bias;
+  6. cross-attention over the kept prompt tokens.
+Every step is a libfastar call; this class only owns the torch buffers.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import fastar as fb
+
+
+class FastARLayer:
+    def __init__(self, heads: int, dim: int, n_bits: int, n_probes: int, tau: float,
+                 tokens_per_frame: int, capacity: int, n_queries: int, chunk_frames: int,
+                 n_prompt: int = 0, dtype=torch.bfloat16, device="cuda"):
+        self.heads, self.dim, self.n_bits, self.n_probes = heads, dim, n_bits, n_probes
+        self.tau, self.T, self.capacity = tau, tokens_per_frame, capacity
+        self.nq, self.chunk_frames, self.n_prompt = n_queries, chunk_frames, n_prompt
+        self.dtype, self.device = dtype, torch.device(device)
+        H, dev = heads, self.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.cache = fb.TempCache(H, dim, capacity, tokens_per_frame, n_bits, dtype, dev)
+        self.planes = torch.zeros(max(n_bits, 1), dim, dtype=dtype, device=dev)
+        nk = chunk_frames * tokens_per_frame
+        lib = fb.library()
+        ws_bytes = max(lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
+                       lib.fastar_hash_workspace(H, nk, n_bits, 1),
+                       lib.fastar_hash_workspace(H, n_prompt, n_bits, 1),
+                       self.cache.workspace_bytes(chunk_frames),
+                       self.cache.workspace_bytes(1))
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.q_ids = torch.empty(H, n_queries, n_probes, **i32)
+        self.q_off = torch.empty(H, (1 << n_bits) + 1, **i32)
+        self.q_perm = torch.empty(H, n_queries, **i32)
+        self.k_ids = torch.empty(H, nk, 1, **i32)
+        self.group_of_new = torch.empty(H, nk, **i32)
+        self.rep_off = torch.empty(H, (1 << n_bits) + 1, **i32)
+        self.rep_perm = torch.empty(H, capacity, **i32)
+        self.o_self = torch.empty(H, n_queries, dim, dtype=dtype, device=dev)
+        self.lse_self = torch.empty(H, n_queries, dtype=torch.float32, device=dev)
+        if n_prompt:
+            self.p_ids = torch.empty(H, n_prompt, 1, **i32)
+            self.keep = torch.empty(H, n_prompt, dtype=torch.uint8, device=dev)
+            self.kept_idx = torch.empty(H, n_prompt, **i32)
+            self.n_kept = torch.empty(H, **i32)
+            self.o_cross = torch.empty(H, n_queries, dim, dtype=dtype, device=dev)
+            self.lse_cross = torch.empty(H, n_queries, dtype=torch.float32, device=dev)
+        self.diag = fb.new_diag(dev)
+
+    def set_planes(self, planes: torch.Tensor):
+        if self.n_bits:
+            self.planes.copy_(planes)
+
+    # -- building blocks ----------------------------------------------------
+    def hash_keys(self, k: torch.Tensor, out: Optional[torch.Tensor] = None):
+        """One-probe bucket ids [H, n, 1] of keys k [H, n, d]."""
+        H, n, _ = k.shape
+        if out is None:
+            out = torch.empty(H, n, 1, dtype=torch.int32, device=self.device)
+        fb.fastar_hash(k, self.planes, self.n_bits, 1, with_index=False, bucket=out, ws=self.ws,
+                       diag=self.diag)
+        return out
+
+    def merge(self, k: torch.Tensor, v: torch.Tensor, n_frames: int, with_index: bool = True,
+              group_of_new: Optional[torch.Tensor] = None):
+        """Hash and merge n_frames new frames k, v [H, n_frames*T, d] (set-up path)."""
+        ids = self.hash_keys(k)
+        return fb.fastar_tempcache_merge(
+            self.cache, k, v, ids.view(self.heads, -1), n_frames, self.tau,
+            group_of_new=group_of_new, with_index=with_index, rep_offsets=self.rep_off,
+            rep_perm=self.rep_perm, ws=self.ws, diag=self.diag)
+
+    # -- one chunk ----------------------------------------------------------
+    def step(self, q, k_new, v_new, prompt_k=None, prompt_v=None):
+        fb.fastar_hash(q, self.planes, self.n_bits, self.n_probes, bucket=self.q_ids,
+                       offsets=self.q_off, perm=self.q_perm, ws=self.ws, diag=self.diag)
+        k_ids = self.hash_keys(k_new, self.k_ids)
+        fb.fastar_tempcache_merge(self.cache, k_new, v_new, k_ids.view(self.heads, -1),
+                                  self.chunk_frames, self.tau, group_of_new=self.group_of_new,
+                                  rep_offsets=self.rep_off, rep_perm=self.rep_perm, ws=self.ws,
+                                  diag=self.diag)
+        c = self.cache
+        fb.fastar_bucket_attention(q, c.rep_k, c.v_mean, q_bucket=self.q_ids, q_perm=self.q_perm,
+                                   key_bias=c.log_count, k_offsets=self.rep_off,
+                                   k_perm=self.rep_perm, n_bits=self.n_bits, out=self.o_self,
+                                   lse=self.lse_self)
+        if prompt_k is not None:
+            fb.fastar_hash(prompt_k, self.planes, self.n_bits, 1, with_index=False,
+                           bucket=self.p_ids, ws=self.ws, diag=self.diag)
+            fb.fastar_prune_prompt(self.q_ids, self.p_ids.view(self.heads, -1), self.n_bits,
+                                   keep=self.keep, kept_idx=self.kept_idx, n_kept=self.n_kept)
+            fb.fastar_bucket_attention(q, prompt_k, prompt_v, key_list=self.kept_idx,
+                                       n_key_list=self.n_kept, out=self.o_cross,
+                                       lse=self.lse_cross)

@@ -1,0 +1,150 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/fastar.h declares, and rejects bad arguments before any launch
+(so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fastar.h")
+
+fa = pytest.importorskip("kv_compressed_attention_amd")
+from kv_compressed_attention_amd import fastar as fb  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fb.LIB_PATH):
+        pytest.skip("libfastar.so not built (run __graft_entry__.build())")
+    return fa.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fastar_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for op in ("fastar_hash", "fastar_tempcache_merge", "fastar_prune_prompt",
+               "fastar_bucket_attention"):
+        assert op in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", fb.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fastar_[a-z_0-9]+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_binding_covers_every_declared_symbol():
+    assert set(fb._SIGNATURES) == set(declared_functions())
+
+
+def test_struct_layouts_match_header(lib):
+    assert ctypes.sizeof(fb.FastarTensor) == 48
+    assert ctypes.sizeof(fb.FastarCache) == 24 + 8 * 8
+
+
+def test_status_strings(lib):
+    assert lib.fastar_status_string(0) == b"ok"
+    assert lib.fastar_status_string(1) == b"invalid argument"
+    assert lib.fastar_status_string(3) == b"workspace too small"
+    assert lib.fastar_version() >= 100
+
+
+def _tensor(dtype=1, heads=2, tokens=16, dim=128, data=1 << 20):
+    return fb.FastarTensor(data, dtype, heads, tokens, dim, 0, tokens * dim, dim)
+
+
+def test_hash_rejects_bad_arguments_without_launching(lib):
+    buf = ctypes.c_void_p(1 << 20)
+    cases = [
+        (_tensor(dtype=7), 12, 1, 2),           # dtype
+        (_tensor(dim=96), 12, 1, 2),            # head dim
+        (_tensor(), 16, 1, 2),                  # n_bits > 15
+        (_tensor(), 12, 3, 2),                  # n_probes
+        (_tensor(), 0, 2, 1),                   # two probes need a bit
+        (_tensor(data=(1 << 20) + 2), 12, 1, 1),  # misaligned data
+    ]
+    for t, bits, probes, want in cases:
+        st = lib.fastar_hash(ctypes.byref(t), buf, bits, probes, buf, None, None, buf,
+                             1 << 30, None, None)
+        assert st == want, (bits, probes, st, lib.fastar_last_error())
+    # workspace too small
+    st = lib.fastar_hash(ctypes.byref(_tensor()), buf, 12, 1, buf, None, None, buf, 8, None, None)
+    assert st == 3
+    assert b"workspace" in lib.fastar_last_error()
+    # offsets without perm
+    st = lib.fastar_hash(ctypes.byref(_tensor()), buf, 12, 1, buf, buf, None, buf, 1 << 30, None, None)
+    assert st == 1
+
+
+def test_attention_rejects_bad_arguments_without_launching(lib):
+    buf = ctypes.c_void_p(1 << 20)
+    q, k = _tensor(), _tensor(tokens=32)
+    kf = _tensor(dtype=0, tokens=32)
+    # mixed dtypes
+    st = lib.fastar_bucket_attention(ctypes.byref(q), None, None, 1, ctypes.byref(kf),
+                                     ctypes.byref(kf), None, None, None, 0, None, None, 0.1,
+                                     buf, None, None)
+    assert st == 1
+    # bucket mode missing k_perm
+    st = lib.fastar_bucket_attention(ctypes.byref(q), buf, buf, 1, ctypes.byref(k), ctypes.byref(k),
+                                     None, buf, None, 4, None, None, 0.1, buf, None, None)
+    assert st == 1
+    # non-finite scale
+    st = lib.fastar_bucket_attention(ctypes.byref(q), None, None, 1, ctypes.byref(k), ctypes.byref(k),
+                                     None, None, None, 0, None, None, float("nan"), buf, None, None)
+    assert st == 1
+    # token counts of k and v differ
+    st = lib.fastar_bucket_attention(ctypes.byref(q), None, None, 1, ctypes.byref(k), ctypes.byref(q),
+                                     None, None, None, 0, None, None, 0.1, buf, None, None)
+    assert st == 1
+
+
+def test_merge_and_prune_reject_bad_arguments(lib):
+    buf = 1 << 20
+    c = fb.FastarCache(2, 128, 64, 16, 12, 1, *([buf] * 8))
+    k = _tensor(tokens=32)
+    # k_new must hold n_frames * tokens_per_frame tokens
+    st = lib.fastar_tempcache_merge(ctypes.byref(c), ctypes.byref(k), ctypes.byref(k), ctypes.c_void_p(buf),
+                                    3, 0.9, None, None, None, ctypes.c_void_p(buf), 1 << 30, None, None)
+    assert st == 1
+    # tau must be finite
+    st = lib.fastar_tempcache_merge(ctypes.byref(c), ctypes.byref(k), ctypes.byref(k), ctypes.c_void_p(buf),
+                                    2, float("inf"), None, None, None, ctypes.c_void_p(buf), 1 << 30, None, None)
+    assert st == 1
+    # capacity below one frame
+    c2 = fb.FastarCache(2, 128, 8, 16, 12, 1, *([buf] * 8))
+    st = lib.fastar_tempcache_merge(ctypes.byref(c2), ctypes.byref(k), ctypes.byref(k), ctypes.c_void_p(buf),
+                                    2, 0.9, None, None, None, ctypes.c_void_p(buf), 1 << 30, None, None)
+    assert st == 1
+    # dtype mismatch between cache and keys
+    kf = _tensor(dtype=0, tokens=32)
+    st = lib.fastar_tempcache_merge(ctypes.byref(c), ctypes.byref(kf), ctypes.byref(kf), ctypes.c_void_p(buf),
+                                    2, 0.9, None, None, None, ctypes.c_void_p(buf), 1 << 30, None, None)
+    assert st == 1
+    # prune: bits out of range, probes out of range
+    p = ctypes.c_void_p(buf)
+    assert lib.fastar_prune_prompt(p, 2, 10, 1, p, 5, 16, p, p, p, None) == 2
+    assert lib.fastar_prune_prompt(p, 2, 10, 0, p, 5, 8, p, p, p, None) == 2
+    assert lib.fastar_prune_prompt(p, 2, 10, 1, p, 5, 8, p, p, None, None) == 1
+
+
+def test_workspace_queries_scale_with_size(lib):
+    a = lib.fastar_hash_workspace(12, 4680, 12, 1)
+    b = lib.fastar_hash_workspace(24, 8192, 14, 2)
+    assert 0 < a < b
+    assert lib.fastar_bucket_index_workspace(12, 1000) >= 16 * 12 * 1000
+    c = fb.FastarCache(12, 128, 20000, 1560, 12, 1, *([0] * 8))
+    assert lib.fastar_tempcache_workspace(ctypes.byref(c), 3) >= 16 * 12 * 20000
