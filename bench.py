@@ -1,0 +1,251 @@
+"""Benchmark of one attention layer's FAST-AR hot path on one MI355X.
+
+A step is one chunk of the per-layer sequence on the layer workload (12 heads,
+d=128, 4680 queries = 3 frames x 1560 tokens, a 6-frame KV cache, 12 hash
+bits, one probe, bf16):
+  restore the compressed cache to its pre-chunk state (the merge is in place;
+  restoring makes every step identical work), hash the queries and build
+  their bucket index, hash the chunk's 3 new frames of keys, TempCache-merge
+  them frame by frame and index the representatives, then AnnSA bucket
+  attention of the queries over the compressed cache with the + ln m bias.
+The cache restore is inside the timed region (it makes the number
+conservative); stage times without it are reported in "stages_ms".
+
+Prints one JSON line.  --gpus N with N > 1 is refused: this build runs on
+one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import copy
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attention query tokens/s per layer; achieved TFLOP/s vs bf16 MFMA peak"
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", type=int, default=1, help="synthetic workload index (1, 3 or 4)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def attention_work(q_ids, rep_off, n_bits, H, nq, d, P):
+    """Algorithmic bytes and flops of one self-attention launch.
+
+    Bytes: Q and O rows (bf16), lse (fp32), the query's ids and index entry,
+    and once per (head, bucket occupied by some query probe) that bucket's
+    representative keys and mean values (bf16), bias (fp32) and index entry.
+    Flops: 4 d per attended (query, key) pair.
+    """
+    nb = 1 << n_bits
+    seg = np.diff(rep_off, axis=1)                       # keys per bucket [H, nb]
+    pairs = 0
+    kv_keys = 0
+    for h in range(H):
+        occ = np.zeros(nb, dtype=bool)
+        occ[q_ids[h].reshape(-1)] = True
+        kv_keys += int(seg[h][occ].sum())
+        pairs += int(seg[h][q_ids[h]].sum())
+    qo = H * nq * (2 * d * 2 + 4 + 4 * P + 4)
+    kv = kv_keys * (2 * d * 2 + 4 + 4)
+    return qo + kv, 4 * d * pairs, pairs
+
+
+def cpu_baseline(w, min_seconds=10.0, max_reps=20):
+    """Time the oracle on the whole chunk (all heads), repeated to >= min_seconds.
+
+    The set-up merges that build the pre-chunk cache are not timed.
+    Returns (seconds per chunk, repetitions).
+    """
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    with threadpool_limits(limits=1):
+        setup = []
+        for h in range(w.heads):
+            tc = oracle.TempCacheOracle(w.dim, w.dtype)
+            for f in range(w.setup_frames):
+                kf = w.k_frames[h, f].astype(np.float64)
+                tc.merge_frame(kf, w.v_frames[h, f], oracle.simhash(kf, w.planes, 1)[:, 0], w.tau)
+            setup.append(tc)
+        total, reps = 0.0, 0
+        while reps < max_reps and (total < min_seconds or reps == 0):
+            states = [copy.deepcopy(tc) for tc in setup]
+            t0 = time.perf_counter()
+            for h in range(w.heads):
+                tc = states[h]
+                q = w.q[h].astype(np.float64)
+                q_ids = oracle.simhash(q, w.planes, w.n_probes)
+                oracle.bucket_index(q_ids, w.n_bits)
+                for f in range(w.setup_frames, w.n_frames):
+                    kf = w.k_frames[h, f].astype(np.float64)
+                    tc.merge_frame(kf, w.v_frames[h, f], oracle.simhash(kf, w.planes, 1)[:, 0],
+                                   w.tau)
+                oracle.bucket_index(tc.rep_bucket, w.n_bits)
+                oracle.bucket_attention(q, q_ids, tc.rep_k, tc.v_mean, tc.rep_bucket,
+                                        bias=tc.log_count)
+            total += time.perf_counter() - t0
+            reps += 1
+    return total / reps, reps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(heads would shard across GPUs with no collective; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import kv_compressed_attention_amd as fa
+    from kv_compressed_attention_amd.layer import FastARLayer
+    from synth import make_workload
+
+    dev = torch.device("cuda:0")
+    w = make_workload(args.workload)
+    H, F, T, d = w.k_frames.shape
+    nq = w.n_queries
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a):
+        return torch.tensor(np.ascontiguousarray(a), dtype=torch.float32, device=dev).to(tdt)
+
+    layer = FastARLayer(H, d, w.n_bits, w.n_probes, w.tau, T, F * T, nq, w.chunk_frames,
+                        dtype=tdt, device=dev)
+    layer.set_planes(up(w.planes))
+    q = up(w.q)
+    k_set, v_set = w.frames(0, w.setup_frames)
+    for f in range(w.setup_frames):
+        layer.merge(up(w.k_frames[:, f]), up(w.v_frames[:, f]), 1, with_index=False)
+    k_new, v_new = (up(a) for a in w.frames(w.setup_frames, F))
+    del k_set, v_set
+    torch.cuda.synchronize()
+    ngb = int(layer.cache.n_groups.max().item())
+    snap = {n: t[:, :ngb].clone() if t.dim() >= 2 and n not in ("frontier",) else t.clone()
+            for n, t in layer.cache.buffers().items()}
+
+    def restore():
+        for n, t in layer.cache.buffers().items():
+            if n in ("n_groups", "frontier"):
+                t.copy_(snap[n])
+            else:
+                t[:, :ngb].copy_(snap[n])
+
+    stages = ["restore", "hash_q", "hash_k", "merge", "attention"]
+    ev = {s: [] for s in stages}
+
+    def step(record):
+        marks = []
+        if record:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record()
+            marks.append(e)
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                marks.append(e)
+        restore()
+        mark()
+        fa.fastar_hash(q, layer.planes, w.n_bits, w.n_probes, bucket=layer.q_ids,
+                       offsets=layer.q_off, perm=layer.q_perm, ws=layer.ws, diag=layer.diag)
+        mark()
+        layer.hash_keys(k_new, layer.k_ids)
+        mark()
+        fa.fastar_tempcache_merge(layer.cache, k_new, v_new, layer.k_ids.view(H, -1),
+                                  w.chunk_frames, w.tau, group_of_new=layer.group_of_new,
+                                  rep_offsets=layer.rep_off, rep_perm=layer.rep_perm,
+                                  ws=layer.ws, diag=layer.diag)
+        mark()
+        c = layer.cache
+        fa.fastar_bucket_attention(q, c.rep_k, c.v_mean, q_bucket=layer.q_ids,
+                                   q_perm=layer.q_perm, key_bias=c.log_count,
+                                   k_offsets=layer.rep_off, k_perm=layer.rep_perm,
+                                   n_bits=w.n_bits, out=layer.o_self, lse=layer.lse_self)
+        mark()
+        if record:
+            for s, a, b in zip(stages, marks[:-1], marks[1:]):
+                ev[s].append((a, b))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    # timed region: exactly K steps, with HIP events between the stages (on
+    # torch's current stream, the stream every libfastar call is enqueued on)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+
+    ms = wall * 1e3 / args.steps
+    q_ids = layer.q_ids.cpu().numpy()
+    rep_off = layer.rep_off.cpu().numpy()
+    nbytes, flops, pairs = attention_work(q_ids, rep_off, w.n_bits, H, nq, d, w.n_probes)
+    t_att = stage_ms["attention"] * 1e-3
+    achieved_gbs = nbytes / t_att / 1e9
+    tflops = flops / t_att / 1e12
+    ai = flops / nbytes
+    out = {
+        "metric": METRIC,
+        "value": nq / (ms * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "heads": H, "head_dim": d, "queries": nq,
+                   "cache_frames": F, "tokens_per_frame": T, "new_frames": w.chunk_frames,
+                   "n_bits": w.n_bits, "n_probes": w.n_probes, "tau": w.tau},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "attn_bf16_kernel (fastar_bucket_attention, bucket mode)",
+                     "bytes_per_launch": nbytes, "launch_ms": stage_ms["attention"]},
+        "attention": {"tflops": tflops, "frac_bf16_mfma_peak": tflops / PEAK_BF16_TFLOPS,
+                      "arith_intensity_flop_per_byte": ai,
+                      "roofline_tflops": min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3),
+                      "attended_pairs": pairs,
+                      "query_tokens_per_s": nq / t_att,
+                      "compressed_keys_per_head": ngb_after(layer)},
+        "stages_ms": stage_ms,
+        "path_ms_without_restore": sum(v for k, v in stage_ms.items() if k != "restore"),
+        "diag": layer.diag.tolist(),
+    }
+    if not args.no_cpu_baseline:
+        per_step, reps = cpu_baseline(w)
+        out["cpu_baseline"] = {"value": nq / per_step, "unit": "query tokens/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"the whole chunk, all {H} heads (hash queries, hash and "
+                                         f"merge {w.chunk_frames} frames, index, bucket "
+                                         f"attention; cache restore not needed), {reps} "
+                                         f"repetitions of {per_step:.2f} s, one thread"}
+    print(json.dumps(out))
+
+
+def ngb_after(layer):
+    return int(layer.cache.n_groups.max().item())
+
+
+if __name__ == "__main__":
+    main()

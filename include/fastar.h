@@ -131,6 +131,7 @@ fastar_status_t fastar_bucket_index(const int32_t* bucket, int heads, int64_t n,
  *   frontier   [H][tokens_per_frame] int32 group of each token of the last
  *                                  merged frame
  * An empty cache is one with n_groups all 0; nothing else needs clearing.
+ * tokens_per_frame must be in [1, 2048]; capacity >= tokens_per_frame.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t heads, dim, capacity, tokens_per_frame, n_bits, dtype;

@@ -153,8 +153,9 @@ fastar_status_t fastar_bucket_index(const int32_t* bucket, int heads, int64_t n,
 size_t fastar_tempcache_workspace(const fastar_cache_t* c, int n_frames) {
   if (!c || n_frames < 0 || c->heads < 0 || c->tokens_per_frame < 0 || c->capacity < 0) return 0;
   const size_t H = c->heads, T = c->tokens_per_frame;
-  return align_up(4 * (size_t)(n_frames + 1) * H) + 3 * align_up(4 * H * T) +
-         align_up(16 * H * (size_t)c->capacity);
+  const size_t ts = (size_t)fastar::tempcache_table_size(c->tokens_per_frame);
+  return align_up(4 * (size_t)(n_frames + 1) * H) + 6 * align_up(4 * H * T) +
+         3 * align_up(4 * H * ts) + align_up(16 * H * (size_t)c->capacity);
 }
 
 fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
@@ -174,8 +175,8 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
   if (c->heads != k_new->heads || c->heads != v_new->heads)
     return fail(FASTAR_ERR_INVALID, "cache, k_new and v_new must share one head count");
   if (n_frames < 0) return fail(FASTAR_ERR_INVALID, "n_frames < 0");
-  if (c->tokens_per_frame <= 0 || c->tokens_per_frame > 4096)
-    return fail(FASTAR_ERR_UNSUPPORTED, "tokens_per_frame %d not in [1, 4096]", c->tokens_per_frame);
+  if (c->tokens_per_frame <= 0 || c->tokens_per_frame > 2048)
+    return fail(FASTAR_ERR_UNSUPPORTED, "tokens_per_frame %d not in [1, 2048]", c->tokens_per_frame);
   if (k_new->tokens != (int64_t)n_frames * c->tokens_per_frame || v_new->tokens != k_new->tokens)
     return fail(FASTAR_ERR_INVALID, "k_new/v_new must hold n_frames * tokens_per_frame tokens");
   if (c->capacity < c->tokens_per_frame)
@@ -189,8 +190,8 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
     if (rep_offsets && c->heads > 0) {
       if (!ws || ws_bytes < fastar_tempcache_workspace(c, n_frames))
         return fail(FASTAR_ERR_WORKSPACE, "workspace too small");
-      const size_t off = align_up(4 * (size_t)(n_frames + 1) * c->heads) +
-                         3 * align_up(4 * (size_t)c->heads * c->tokens_per_frame);
+      const size_t off = fastar_tempcache_workspace(c, n_frames) -
+                         align_up(16 * (size_t)c->heads * (size_t)c->capacity);
       return hip_status(fastar::launch_bucket_index(c->rep_bucket, c->heads, c->capacity, 1, c->n_bits,
                                                     c->n_groups, rep_offsets, rep_perm,
                                                     (int32_t*)((char*)ws + off), stream),
@@ -207,17 +208,25 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
     return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu",
                 fastar_tempcache_workspace(c, n_frames), ws_bytes);
   const size_t H = c->heads, T = c->tokens_per_frame;
+  const size_t ts = (size_t)fastar::tempcache_table_size(c->tokens_per_frame);
   char* w = (char*)ws;
+  auto take = [&](size_t bytes) {
+    char* p = w;
+    w += align_up(bytes);
+    return (int32_t*)p;
+  };
   fastar::MergeWs mw;
-  mw.ng = (int32_t*)w;
-  w += align_up(4 * (size_t)(n_frames + 1) * H);
-  mw.target = (int32_t*)w;
-  w += align_up(4 * H * T);
-  mw.tcos = (float*)w;
-  w += align_up(4 * H * T);
-  mw.mgroup = (int32_t*)w;
-  w += align_up(4 * H * T);
-  mw.index_ws = (int32_t*)w;
+  mw.ng = take(4 * (size_t)(n_frames + 1) * H);
+  mw.target = take(4 * H * T);
+  mw.tcos = (float*)take(4 * H * T);
+  mw.mgroup = take(4 * H * T);
+  mw.gid = take(4 * H * T);
+  mw.cand = take(4 * H * T);
+  mw.candg = take(4 * H * T);
+  mw.tkey = take(4 * H * ts);
+  mw.tstart = take(4 * H * ts);
+  mw.tcount = take(4 * H * ts);
+  mw.index_ws = take(16 * H * (size_t)c->capacity);
   return hip_status(fastar::launch_tempcache_merge(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,
                                                    group_of_new, rep_offsets, rep_perm, mw, diag,
                                                    stream),

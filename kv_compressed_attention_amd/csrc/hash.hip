@@ -237,20 +237,33 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
   }
 }
 
-// Re-evaluates queued rows in float64; signs float64 cannot certify are
-// settled exactly.  One row per lane; the expansion lives in LDS.
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 1; m < FASTAR_WAVE; m <<= 1) v += __shfl_xor(v, m, FASTAR_WAVE);
+  return v;
+}
+
+// Re-evaluates queued rows in float64, one wave per row (each lane holds D/64
+// dims); a sign float64 cannot certify is settled exactly by lane 0 with an
+// expansion sum in LDS.
 template <typename T, int D, int P>
-__global__ __launch_bounds__(32) void hash_fixup_kernel(
+__global__ __launch_bounds__(256) void hash_fixup_kernel(
     const T* __restrict__ x, int64_t sh, int64_t st, int64_t N, const T* __restrict__ planes,
     int nb, int32_t* __restrict__ bucket, const uint32_t* __restrict__ queue,
     const uint32_t* __restrict__ qcount, fastar_diag_t* __restrict__ diag) {
-  __shared__ double ex[32][D + 2];
+  constexpr int L = D / FASTAR_WAVE;
+  __shared__ double ex[4][D + 2];
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
   const uint32_t n = *qcount;
-  for (uint32_t qi = blockIdx.x * 32 + threadIdx.x; qi < n; qi += gridDim.x * 32) {
+  for (uint32_t qi = blockIdx.x * 4 + wave; qi < n; qi += gridDim.x * 4) {
     const uint32_t e = queue[qi];
     const int64_t h = (int64_t)e / N;
     const int64_t row = (int64_t)e - h * N;
     const T* xr = x + h * sh + row * st;
+    double xv[L];
+#pragma unroll
+    for (int k = 0; k < L; ++k) xv[k] = (double)Elem<T>::load(xr, lane + FASTAR_WAVE * k);
     uint32_t bits = 0;
     double dist[16], derr[16];
     bool unresolved = false;
@@ -260,30 +273,37 @@ __global__ __launch_bounds__(32) void hash_fixup_kernel(
       derr[p] = 0.0;
       if (p < nb) {
         double s = 0.0, a = 0.0, n2 = 0.0;
-        for (int d = 0; d < D; ++d) {
-          const double xv = (double)Elem<T>::load(xr, d);
-          const double rv = (double)Elem<T>::load(planes, (int64_t)p * D + d);
-          const double pr = xv * rv;  // exact: at most 48 significant bits
+#pragma unroll
+        for (int k = 0; k < L; ++k) {
+          const double rv = (double)Elem<T>::load(planes, (int64_t)p * D + lane + FASTAR_WAVE * k);
+          const double pr = xv[k] * rv;  // exact: at most 48 significant bits
           s += pr;
           a += fabs(pr);
           n2 += rv * rv;
         }
-        const double bound = 2.0 * (D + 2) * 0x1p-53 * a;
+        s = wave_sum_d(s);
+        a = wave_sum_d(a);
+        n2 = wave_sum_d(n2);
+        const double bound = 2.0 * (D + 8) * 0x1p-53 * a;
         int sg;
         if (fabs(s) > bound) {
           sg = s > 0.0 ? 1 : -1;
         } else if (a == 0.0) {
           sg = 0;
         } else {
-          double* E = ex[threadIdx.x];
-          int m = 0;
-          for (int d = 0; d < D; ++d) {
-            const double xv = (double)Elem<T>::load(xr, d);
-            const double rv = (double)Elem<T>::load(planes, (int64_t)p * D + d);
-            m = grow_expansion(E, m, xv * rv);
+          int sg0 = 0;
+          if (lane == 0) {
+            double* E = ex[wave];
+            int m = 0;
+            for (int d = 0; d < D; ++d) {
+              const double xd = (double)Elem<T>::load(xr, d);
+              const double rd = (double)Elem<T>::load(planes, (int64_t)p * D + d);
+              m = grow_expansion(E, m, xd * rd);
+            }
+            sg0 = expansion_sign(E, m);
+            if (diag) atomicAdd(&diag->hash_exact_signs, 1u);
           }
-          sg = expansion_sign(E, m);
-          if (diag) atomicAdd(&diag->hash_exact_signs, 1u);
+          sg = __shfl(sg0, 0, FASTAR_WAVE);
         }
         if (sg > 0) bits |= 1u << p;
         if (P == 2) {
@@ -293,10 +313,8 @@ __global__ __launch_bounds__(32) void hash_fixup_kernel(
         }
       }
     }
-    int32_t* o = bucket + (h * N + row) * P;
-    o[0] = (int32_t)bits;
+    int j1 = 0;
     if (P == 2) {
-      int j1 = 0;
       double d1 = dist[0], e1 = derr[0];
 #pragma unroll
       for (int p = 1; p < 16; ++p) {
@@ -314,11 +332,15 @@ __global__ __launch_bounds__(32) void hash_fixup_kernel(
           if (err > 0.0 && gap <= err) unresolved = true;
         }
       }
-      o[1] = (int32_t)(bits ^ (1u << j1));
     }
-    if (diag) {
-      atomicAdd(&diag->hash_fallback_rows, 1u);
-      if (unresolved) atomicAdd(&diag->unresolved, 1u);
+    if (lane == 0) {
+      int32_t* o = bucket + (h * N + row) * P;
+      o[0] = (int32_t)bits;
+      if (P == 2) o[1] = (int32_t)(bits ^ (1u << j1));
+      if (diag) {
+        atomicAdd(&diag->hash_fallback_rows, 1u);
+        if (unresolved) atomicAdd(&diag->unresolved, 1u);
+      }
     }
   }
 }
@@ -334,7 +356,7 @@ hipError_t launch_hash_dp(const fastar_tensor_t& x, const void* planes, int nb, 
     hipLaunchKernelGGL((hash_bf16_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s,
                        (const uint16_t*)x.data, x.stride_head, x.stride_token, H, N,
                        (const uint16_t*)planes, nb, bucket, queue, qcount);
-    hipLaunchKernelGGL((hash_fixup_kernel<uint16_t, D, P>), dim3(64), dim3(32), 0, s,
+    hipLaunchKernelGGL((hash_fixup_kernel<uint16_t, D, P>), dim3(128), dim3(256), 0, s,
                        (const uint16_t*)x.data, x.stride_head, x.stride_token, N,
                        (const uint16_t*)planes, nb, bucket, queue, qcount, diag);
   } else {
@@ -343,7 +365,7 @@ hipError_t launch_hash_dp(const fastar_tensor_t& x, const void* planes, int nb, 
     hipLaunchKernelGGL((hash_f32_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s,
                        (const float*)x.data, x.stride_head, x.stride_token, H, N,
                        (const float*)planes, nb, bucket, queue, qcount);
-    hipLaunchKernelGGL((hash_fixup_kernel<float, D, P>), dim3(64), dim3(32), 0, s,
+    hipLaunchKernelGGL((hash_fixup_kernel<float, D, P>), dim3(128), dim3(256), 0, s,
                        (const float*)x.data, x.stride_head, x.stride_token, N,
                        (const float*)planes, nb, bucket, queue, qcount, diag);
   }

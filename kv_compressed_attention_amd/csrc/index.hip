@@ -156,21 +156,42 @@ __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
     __syncthreads();
     kfinal = outk;
   }
-  // offsets[B] = #items whose first bucket < B
+  // offsets[B] = #items whose first bucket < B: each run of equal buckets
+  // writes its start, then a suffix minimum fills the empty buckets
   const int nbk = 1 << nbits;
   int32_t* off = offsets + (int64_t)h * (nbk + 1);
-  for (int B = threadIdx.x; B <= nbk; B += kThreads) {
-    int64_t lo = 0, hi = nh;
-    if (passes > 0) {
-      while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if ((kfinal[mid] >> shift0) < B) lo = mid + 1;
-        else hi = mid;
-      }
-    } else {
-      lo = B == 0 ? 0 : nh;
-    }
-    off[B] = (int32_t)lo;
+  if (passes == 0) {
+    for (int B = threadIdx.x; B <= nbk; B += kThreads) off[B] = B == 0 ? 0 : (int32_t)nh;
+    return;
+  }
+  for (int B = threadIdx.x; B <= nbk; B += kThreads) off[B] = B == nbk ? (int32_t)nh : INT_MAX;
+  __threadfence_block();
+  __syncthreads();
+  for (int64_t p = threadIdx.x; p < nh; p += kThreads) {
+    const int k = kfinal[p] >> shift0;
+    if (p == 0 || (kfinal[p - 1] >> shift0) != k) off[k] = (int32_t)p;
+  }
+  __threadfence_block();
+  __syncthreads();
+  int* cmin = &cnt[0][0];  // [kThreads] chunk minima
+  const int per = (nbk + 1 + kThreads - 1) / kThreads;
+  const int c0 = threadIdx.x * per;
+  const int c1 = c0 + per < nbk + 1 ? c0 + per : nbk + 1;
+  int m = INT_MAX;
+  for (int B = c0; B < c1; ++B) m = min(m, off[B]);
+  cmin[threadIdx.x] = m;
+  __syncthreads();
+  // suffix minimum of the chunk minima (Hillis-Steele, reading to the right)
+  for (int d = 1; d < kThreads; d <<= 1) {
+    const int y = threadIdx.x + d < kThreads ? cmin[threadIdx.x + d] : INT_MAX;
+    __syncthreads();
+    cmin[threadIdx.x] = min(cmin[threadIdx.x], y);
+    __syncthreads();
+  }
+  m = threadIdx.x + 1 < kThreads ? cmin[threadIdx.x + 1] : INT_MAX;
+  for (int B = c1 - 1; B >= c0; --B) {
+    m = min(m, off[B]);
+    off[B] = m;
   }
 }
 

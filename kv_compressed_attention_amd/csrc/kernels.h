@@ -42,9 +42,16 @@ struct MergeWs {
   int32_t* ng;        // [n_frames + 1][H]
   int32_t* target;    // [H][T]
   float* tcos;        // [H][T]
-  int32_t* mgroup;    // [H][T]
+  int32_t* mgroup;    // [H][T] group a token extends, -1 for a new group
+  int32_t* gid;       // [H][T] final group of each token (-1: dropped)
+  int32_t* tkey;      // [H][tsize] previous-frame candidate table: bucket + 1
+  int32_t* tstart;    // [H][tsize] segment start
+  int32_t* tcount;    // [H][tsize] segment length
+  int32_t* cand;      // [H][T] candidate token index
+  int32_t* candg;     // [H][T] candidate group
   int32_t* index_ws;  // bucket index scratch
 };
+int tempcache_table_size(int tokens_per_frame);
 hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
                                   const fastar_tensor_t& v_new, const int32_t* k_new_bucket,
                                   int n_frames, float tau, int32_t* group_of_new,
