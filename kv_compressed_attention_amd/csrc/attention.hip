@@ -148,27 +148,39 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
         if (kk >= kend) kk = kbeg;
         kid[hf] = (MODE == 2) ? (int)kk : idx_h[kk];
       }
-      float s[8];
+      // key ids of the 8 slots this lane scores / feeds to PV:
+      // slot 4*hf + i <-> key 16*hf + 4*g + i of the chunk
       int sk[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sk[4 * hf + i] = __shfl(kid[hf], 4 * g + i, FASTAR_WAVE);
+      // issue the K and V gathers together; V does not depend on the scores
+      uint4 kraw[2][NC];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const uint16_t* krow = kh + (int64_t)kid[hf] * k_st;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kraw[hf][c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * g);
+      }
+      VRow<NB> vr[8];
+#pragma unroll
+      for (int si = 0; si < 8; ++si) vr[si].load(vh + (int64_t)sk[si] * v_st + NB * col);
+      float bias[8];
+#pragma unroll
+      for (int si = 0; si < 8; ++si) bias[si] = bh ? bh[sk[si]] * kLog2e : 0.f;
+      float s[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const uint4 u = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * g);
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, u), qop[c], sacc, 0, 0, 0);
-        }
+        for (int c = 0; c < NC; ++c)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kraw[hf][c]), qop[c], sacc, 0, 0, 0);
         // sacc[i] = score(key slot 16hf + 4g + i, row col)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int slot = 4 * g + i;
-          const int key = __shfl(kid[hf], slot, FASTAR_WAVE);
-          sk[4 * hf + i] = key;
-          const bool kvalid = kc + 16 * hf + slot < kend;
-          float x = sacc[i] * scale_log2;
-          if (bh) x += bh[key] * kLog2e;
-          s[4 * hf + i] = (kvalid && rowin) ? x : -INFINITY;
+          const bool kvalid = kc + 16 * hf + 4 * g + i < kend;
+          s[4 * hf + i] = (kvalid && rowin) ? sacc[i] * scale_log2 + bias[4 * hf + i] : -INFINITY;
         }
       }
       float mx = s[0];
@@ -199,10 +211,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
       }
       const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
       // V^T operand: lane (dim-row col, group g), slot si <-> key sk[si],
-      // dims NB*col .. NB*col + NB - 1 (one per output block)
-      VRow<NB> vr[8];
-#pragma unroll
-      for (int si = 0; si < 8; ++si) vr[si].load(vh + (int64_t)sk[si] * v_st + NB * col);
+      // dims NB*col .. NB*col + NB - 1 (one per output block), loaded above
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const uint4 w = make_uint4(vr[0].get(b) | (vr[1].get(b) << 16), vr[2].get(b) | (vr[3].get(b) << 16),

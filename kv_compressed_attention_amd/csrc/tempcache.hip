@@ -270,18 +270,38 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
     const float rj = nj2 > 0.f ? rsqrtf(nj2) : 0.f;
     Top2<float> t;
     t.init();
-    for (int k = 0; k < cnt; ++k) {
-      float r[EPL];
-      Chunk<T, EPL>::load(rk + (int64_t)cg[k] * D, r);
-      float dt = 0.f, ni2 = 0.f;
+    // candidates in batches of 4, so that their row loads overlap
+    constexpr int U = 4;
+    for (int k0 = 0; k0 < cnt; k0 += U) {
+      int gk[U], ik[U];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        dt = fmaf(a[e], r[e], dt);
-        ni2 = fmaf(r[e], r[e], ni2);
+      for (int u = 0; u < U; ++u) {
+        const int kk = k0 + u < cnt ? k0 + u : k0;
+        gk[u] = cg[kk];
+        ik[u] = ci[kk];
       }
-      dt = sum16(dt);
-      ni2 = sum16(ni2);
-      t.add((nj2 > 0.f && ni2 > 0.f) ? dt * rj * rsqrtf(ni2) : 0.f, ci[k]);
+      float r[U][EPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) Chunk<T, EPL>::load(rk + (int64_t)gk[u] * D, r[u]);
+      float dt[U], ni2[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        dt[u] = 0.f;
+        ni2[u] = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          dt[u] = fmaf(a[e], r[u][e], dt[u]);
+          ni2[u] = fmaf(r[u][e], r[u][e], ni2[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        dt[u] = sum16(dt[u]);
+        ni2[u] = sum16(ni2[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (k0 + u < cnt) t.add((nj2 > 0.f && ni2[u] > 0.f) ? dt[u] * rj * rsqrtf(ni2[u]) : 0.f, ik[u]);
     }
     const float e32 = cos_err32<D>();
     best = t.best;

@@ -46,6 +46,7 @@ def run_chunk(w, heads=None, attention=True):
             tc = TempCacheOracle(w.dim, w.dtype)
             F = w.k_frames.shape[1]
             groups = []
+            setup_groups = []
             k_ids = []
             for f in range(F):
                 kf = np.asarray(w.k_frames[h, f], dtype=np.float64)
@@ -55,10 +56,11 @@ def run_chunk(w, heads=None, attention=True):
                 if f == w.setup_frames:
                     r["n_groups_before"] = tc.n_groups
                 g = tc.merge_frame(kf, w.v_frames[h, f], ids, w.tau)
-                if f >= w.setup_frames:
-                    groups.append(g)
+                (groups if f >= w.setup_frames else setup_groups).append(g)
             r["k_ids"] = np.concatenate(k_ids) if k_ids else np.zeros(0, np.int64)
             r["group_of_new"] = np.concatenate(groups) if groups else np.zeros(0, np.int64)
+            r["setup_groups"] = (np.concatenate(setup_groups) if setup_groups
+                                 else np.zeros(0, np.int64))
             r["cache"] = tc
             r["rep_offsets"], r["rep_perm"] = bucket_index(tc.rep_bucket, w.n_bits)
             if attention:
