@@ -11,8 +11,9 @@ bits, one probe, bf16):
 The cache restore is inside the timed region (it makes the number
 conservative); stage times without it are reported in "stages_ms".
 
-Prints one JSON line.  --gpus N with N > 1 is refused: this build runs on
-one GPU.
+Prints one JSON line.  --gpus N with N > 1 is refused: the library has no
+multi-GPU path (heads are independent, so a multi-GPU layer would shard them
+with no collective).
 """
 
 from __future__ import annotations
@@ -105,11 +106,28 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=20):
     return total / reps, reps
 
 
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed counter passes, if
+    they were taken with the current attention sources (else None)."""
+    import glob
+    import hashlib
+    import re
+
+    src = b"".join(open(os.path.join(ROOT, "kv_compressed_attention_amd", "csrc", f), "rb").read()
+                   for f in ("attention.hip", "common.h"))
+    digest = hashlib.sha256(src).hexdigest()[:16]
+    for path in glob.glob(os.path.join(ROOT, "profiles", "attn_bf16_bucket_layer_*.md")):
+        m = re.search(r"traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]+)", open(path).read())
+        if m and m.group(2) == digest:
+            return int(m.group(1))
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(heads would shard across GPUs with no collective; see DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: libfastar has no multi-GPU path (heads are "
+              "independent and would shard across GPUs with no collective)", file=sys.stderr)
         sys.exit(2)
     import kv_compressed_attention_amd as fa
     from kv_compressed_attention_amd.layer import FastARLayer
@@ -144,6 +162,13 @@ def main():
                 t.copy_(snap[n])
             else:
                 t[:, :ngb].copy_(snap[n])
+
+    # a plain 64 MiB device copy before the timed region: the calibration
+    # kernel for the FETCH_SIZE / WRITE_SIZE counter passes
+    cal_src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    cal_dst.copy_(cal_src)
+    del cal_src, cal_dst
 
     stages = ["restore", "hash_q", "hash_k", "merge", "attention"]
     ev = {s: [] for s in stages}
@@ -219,7 +244,7 @@ def main():
                    "cache_frames": F, "tokens_per_frame": T, "new_frames": w.chunk_frames,
                    "n_bits": w.n_bits, "n_probes": w.n_probes, "tau": w.tau},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": recorded_traffic(),
                      "kernel": "attn_bf16_kernel (fastar_bucket_attention, bucket mode)",
                      "bytes_per_launch": nbytes, "launch_ms": stage_ms["attention"]},
         "attention": {"tflops": tflops, "frac_bf16_mfma_peak": tflops / PEAK_BF16_TFLOPS,

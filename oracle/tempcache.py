@@ -13,7 +13,7 @@ What the pages fix:
   their similarity passes a threshold (paperlayer.ai section 5, appendix C
   threshold ablation 0.9 -> 0.5).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 * similarity is the cosine (cos of a zero vector is 0); the threshold test is
   cos >= tau with tau taken as its float32 value;
 * candidates for new key j of frame f are the frame f-1 tokens whose bucket id
