@@ -152,10 +152,10 @@ fastar_status_t fastar_bucket_index(const int32_t* bucket, int heads, int64_t n,
 // ---------------------------------------------------------------------------
 size_t fastar_tempcache_workspace(const fastar_cache_t* c, int n_frames) {
   if (!c || n_frames < 0 || c->heads < 0 || c->tokens_per_frame < 0 || c->capacity < 0) return 0;
-  const size_t H = c->heads, T = c->tokens_per_frame;
+  const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
   const size_t ts = (size_t)fastar::tempcache_table_size(c->tokens_per_frame);
-  return align_up(4 * (size_t)(n_frames + 1) * H) + 6 * align_up(4 * H * T) +
-         3 * align_up(4 * H * ts) + align_up(16 * H * (size_t)c->capacity);
+  return 3 * align_up(4 * H * (F + 1) * ts) + align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
+         5 * align_up(4 * H * F * T) + align_up(16 * H * (size_t)c->capacity);
 }
 
 fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
@@ -207,7 +207,7 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
   if (!ws || ws_bytes < fastar_tempcache_workspace(c, n_frames))
     return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu",
                 fastar_tempcache_workspace(c, n_frames), ws_bytes);
-  const size_t H = c->heads, T = c->tokens_per_frame;
+  const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
   const size_t ts = (size_t)fastar::tempcache_table_size(c->tokens_per_frame);
   char* w = (char*)ws;
   auto take = [&](size_t bytes) {
@@ -216,16 +216,16 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
     return (int32_t*)p;
   };
   fastar::MergeWs mw;
-  mw.ng = take(4 * (size_t)(n_frames + 1) * H);
-  mw.target = take(4 * H * T);
-  mw.tcos = (float*)take(4 * H * T);
-  mw.mgroup = take(4 * H * T);
-  mw.gid = take(4 * H * T);
-  mw.cand = take(4 * H * T);
+  mw.tkey = take(4 * H * (F + 1) * ts);
+  mw.tstart = take(4 * H * (F + 1) * ts);
+  mw.tcount = take(4 * H * (F + 1) * ts);
+  mw.cand = take(4 * H * (F + 1) * T);
   mw.candg = take(4 * H * T);
-  mw.tkey = take(4 * H * ts);
-  mw.tstart = take(4 * H * ts);
-  mw.tcount = take(4 * H * ts);
+  mw.target = take(4 * H * F * T);
+  mw.tcos = (float*)take(4 * H * F * T);
+  mw.mgroup = take(4 * H * F * T);
+  mw.gid = take(4 * H * F * T);
+  mw.nextj = take(4 * H * F * T);
   mw.index_ws = take(16 * H * (size_t)c->capacity);
   return hip_status(fastar::launch_tempcache_merge(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,
                                                    group_of_new, rep_offsets, rep_perm, mw, diag,

@@ -39,16 +39,16 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // tempcache.hip -------------------------------------------------------------
 struct MergeWs {
-  int32_t* ng;        // [n_frames + 1][H]
-  int32_t* target;    // [H][T]
-  float* tcos;        // [H][T]
-  int32_t* mgroup;    // [H][T] group a token extends, -1 for a new group
-  int32_t* gid;       // [H][T] final group of each token (-1: dropped)
-  int32_t* tkey;      // [H][tsize] previous-frame candidate table: bucket + 1
-  int32_t* tstart;    // [H][tsize] segment start
-  int32_t* tcount;    // [H][tsize] segment length
-  int32_t* cand;      // [H][T] candidate token index
-  int32_t* candg;     // [H][T] candidate group
+  int32_t* tkey;      // [H][n_frames+1][tsize] bucket tables (see tempcache.hip)
+  int32_t* tstart;    // [H][n_frames+1][tsize]
+  int32_t* tcount;    // [H][n_frames+1][tsize]
+  int32_t* cand;      // [H][n_frames+1][T]
+  int32_t* candg;     // [H][T]
+  int32_t* target;    // [H][n_frames][T]
+  float* tcos;        // [H][n_frames][T]
+  int32_t* mgroup;    // [H][n_frames][T]
+  int32_t* gid;       // [H][n_frames][T]
+  int32_t* nextj;     // [H][n_frames][T]
   int32_t* index_ws;  // bucket index scratch
 };
 int tempcache_table_size(int tokens_per_frame);
