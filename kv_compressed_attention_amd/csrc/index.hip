@@ -10,8 +10,12 @@
 // Each wave owns a contiguous slice of the input and walks it 64 items at a
 // time in order; items with equal digits in a 64-item group are matched with
 // 8 ballots, so ranks come from popcounts and the sort is stable without
-// atomics.  Per-wave digit counters live in LDS (16 x 256 ints).  offsets[B]
-// is the lower bound of B in the sorted first-bucket column.
+// atomics.  Per-wave digit counters live in LDS (16 x 256 ints).  A head of at
+// most kLdsItems items is sorted entirely in LDS (keys and 16-bit token
+// indices, double-buffered); larger heads go through the workspace.
+// offsets[B] is the number of items whose first bucket is < B: every run of
+// equal buckets writes its start and a suffix minimum fills the gaps.  One
+// probe with at most 12 bits takes a single counting pass instead (below).
 
 #include "common.h"
 #include "kernels.h"
@@ -22,6 +26,8 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * FASTAR_WAVE;
+constexpr int U = 4;               // groups of 64 keys loaded before they are ranked
+constexpr int kLdsItems = 11264;   // 2 x (4 + 2) bytes per item in LDS
 
 __device__ __forceinline__ int32_t flip_bit(int32_t a, int32_t b) {
   const uint32_t x = (uint32_t)(a ^ b);
@@ -40,10 +46,154 @@ __device__ __forceinline__ uint64_t match_digit(uint32_t digit, bool valid) {
   return peers;
 }
 
+// One stable LSD pass on the 8-bit digit at `shift`.  load(i, key, val) reads
+// item i of the input, store(pos, key, val) writes the output.  Whole
+// workgroup; ends with a barrier.
+template <typename Load, typename Store>
+__device__ __forceinline__ void radix_pass(int64_t wbeg, int64_t wend, int shift,
+                                           int (*cnt)[256], int* dbase, Load load, Store store) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  for (int i = threadIdx.x; i < kWaves * 256; i += kThreads) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  // count the digits of this wave's slice
+  for (int64_t base = wbeg; base < wend; base += U * FASTAR_WAVE) {
+    int32_t key[U], val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * FASTAR_WAVE + lane;
+      key[u] = 0;
+      if (i < wend) load(i, key[u], val[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * FASTAR_WAVE + lane;
+      const bool valid = i < wend;
+      const uint32_t digit = ((uint32_t)key[u] >> shift) & 255u;
+      const uint64_t peers = match_digit(digit, valid);
+      if (valid && lane == __builtin_ctzll(peers)) cnt[wave][digit] += __popcll(peers);
+    }
+  }
+  __syncthreads();
+  // exclusive scan in (digit, wave) order
+  if (threadIdx.x < 256) {
+    int run = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int c = cnt[w][threadIdx.x];
+      cnt[w][threadIdx.x] = run;
+      run += c;
+    }
+    dbase[threadIdx.x] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x < FASTAR_WAVE) {
+    int t[4];
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[j] = dbase[4 * lane + j];
+      s += t[j];
+    }
+    int incl = s;
+#pragma unroll
+    for (int off = 1; off < FASTAR_WAVE; off <<= 1) {
+      const int y = __shfl_up(incl, off, FASTAR_WAVE);
+      if (lane >= off) incl += y;
+    }
+    int ex = incl - s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dbase[4 * lane + j] = ex;
+      ex += t[j];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kWaves * 256; i += kThreads) (&cnt[0][0])[i] += dbase[i & 255];
+  __syncthreads();
+  // stable scatter, same order
+  for (int64_t base = wbeg; base < wend; base += U * FASTAR_WAVE) {
+    int32_t key[U], val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * FASTAR_WAVE + lane;
+      key[u] = 0;
+      val[u] = 0;
+      if (i < wend) load(i, key[u], val[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * FASTAR_WAVE + lane;
+      const bool valid = i < wend;
+      const uint32_t digit = ((uint32_t)key[u] >> shift) & 255u;
+      const uint64_t peers = match_digit(digit, valid);
+      const int pos = valid ? cnt[wave][digit] + __popcll(peers & lanemask_lt()) : 0;
+      if (valid) {
+        store(pos, key[u], val[u]);
+        // the leader is the lowest peer: its rank is 0, so pos is the old count
+        if (lane == __builtin_ctzll(peers)) cnt[wave][digit] = pos + __popcll(peers);
+      }
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+}
+
+// offsets[B] = number of sorted items whose first bucket (key >> shift0) < B.
+template <typename KeyAt>
+__device__ __forceinline__ void write_offsets(int32_t* off, int nbk, int64_t nh, int shift0,
+                                              KeyAt key_at, int* cmin) {
+  const int lane = lane_id();
+  for (int B = threadIdx.x; B <= nbk; B += kThreads) off[B] = B == nbk ? (int32_t)nh : INT_MAX;
+  __threadfence_block();
+  __syncthreads();
+  for (int64_t p = threadIdx.x; p < nh; p += kThreads) {
+    const int k = key_at(p) >> shift0;
+    if (p == 0 || (key_at(p - 1) >> shift0) != k) off[k] = (int32_t)p;
+  }
+  __threadfence_block();
+  __syncthreads();
+  const int per = (nbk + 1 + kThreads - 1) / kThreads;
+  const int c0 = threadIdx.x * per;
+  const int c1 = c0 + per < nbk + 1 ? c0 + per : nbk + 1;
+  int m = INT_MAX;
+  for (int B = c0; B < c1; ++B) m = min(m, off[B]);
+  cmin[threadIdx.x] = m;
+  __syncthreads();
+  // suffix minimum of the chunk minima: wave 0, 16 chunks per lane
+  if (threadIdx.x < FASTAR_WAVE) {
+    constexpr int PL = kThreads / FASTAR_WAVE;
+    int v[PL];
+    int run = INT_MAX;
+#pragma unroll
+    for (int q = PL - 1; q >= 0; --q) {
+      run = min(run, cmin[lane * PL + q]);
+      v[q] = run;
+    }
+    int incl = run;
+#pragma unroll
+    for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
+      const int y = __shfl_down(incl, o, FASTAR_WAVE);
+      if (lane + o < FASTAR_WAVE) incl = min(incl, y);
+    }
+    int right = __shfl_down(incl, 1, FASTAR_WAVE);
+    if (lane == FASTAR_WAVE - 1) right = INT_MAX;
+#pragma unroll
+    for (int q = 0; q < PL; ++q) cmin[lane * PL + q] = min(v[q], right);
+  }
+  __syncthreads();
+  m = threadIdx.x + 1 < kThreads ? cmin[threadIdx.x + 1] : INT_MAX;
+  for (int B = c1 - 1; B >= c0; --B) {
+    m = min(m, off[B]);
+    off[B] = m;
+  }
+}
+
 template <int P>
 __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
     const int32_t* __restrict__ bucket, int64_t n, int nbits, const int32_t* __restrict__ n_valid,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ ws) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ ws,
+    int use_lds) {
+  extern __shared__ int32_t lds[];  // kLdsItems x (key, key, u16 val, u16 val)
   __shared__ int cnt[kWaves][256];
   __shared__ int dbase[256];
   const int h = blockIdx.x;
@@ -54,145 +204,244 @@ __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
   }
   const int32_t* ids = bucket + (int64_t)h * n * P;
   int32_t* ph = perm + (int64_t)h * n;
+  const int shift0 = (P == 2) ? 4 : 0;
+  const int passes = (nbits + shift0 + 7) / 8;
+  const int nbk = 1 << nbits;
+  int32_t* off = offsets + (int64_t)h * (nbk + 1);
+  if (passes == 0) {  // one bucket: identity
+    for (int64_t i = threadIdx.x; i < nh; i += kThreads) ph[i] = (int32_t)i;
+    for (int B = threadIdx.x; B <= nbk; B += kThreads) off[B] = B == 0 ? 0 : (int32_t)nh;
+    return;
+  }
+  const int wave = threadIdx.x >> 6;
+  const int64_t chunk = (nh + kWaves - 1) / kWaves;
+  const int64_t wbeg = (int64_t)wave * chunk < nh ? (int64_t)wave * chunk : nh;
+  const int64_t wend = wbeg + chunk < nh ? wbeg + chunk : nh;
+  auto key_of = [&](int64_t i) -> int32_t {
+    return P == 2 ? ((ids[2 * i] << 4) | flip_bit(ids[2 * i], ids[2 * i + 1])) : ids[i];
+  };
+  if (use_lds && nh <= kLdsItems) {
+    int32_t* ka = lds;
+    int32_t* kb = ka + kLdsItems;
+    uint16_t* va = reinterpret_cast<uint16_t*>(kb + kLdsItems);
+    uint16_t* vb = va + kLdsItems;
+    for (int64_t i = threadIdx.x; i < nh; i += kThreads) {
+      ka[i] = key_of(i);
+      va[i] = (uint16_t)i;
+    }
+    __syncthreads();
+    for (int pass = 0; pass < passes; ++pass) {
+      int32_t* sk = (pass & 1) ? kb : ka;
+      uint16_t* sv = (pass & 1) ? vb : va;
+      int32_t* dk = (pass & 1) ? ka : kb;
+      uint16_t* dv = (pass & 1) ? va : vb;
+      radix_pass(
+          wbeg, wend, pass * 8, cnt, dbase,
+          [&](int64_t i, int32_t& k, int32_t& v) {
+            k = sk[i];
+            v = sv[i];
+          },
+          [&](int pos, int32_t k, int32_t v) {
+            dk[pos] = k;
+            dv[pos] = (uint16_t)v;
+          });
+    }
+    const int32_t* fk = (passes & 1) ? kb : ka;
+    const uint16_t* fv = (passes & 1) ? vb : va;
+    for (int64_t i = threadIdx.x; i < nh; i += kThreads) ph[i] = fv[i];
+    write_offsets(off, nbk, nh, shift0, [&](int64_t p) { return fk[p]; }, &cnt[0][0]);
+    return;
+  }
+  // workspace path: [k0 | v0 | k1 | v1] per head
   int32_t* k0 = ws + (int64_t)h * n * 4;
   int32_t* v0 = k0 + n;
   int32_t* k1 = v0 + n;
   int32_t* v1 = k1 + n;
-  const int shift0 = (P == 2) ? 4 : 0;
-  const int keybits = nbits + shift0;
-  const int passes = (keybits + 7) / 8;
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  const int64_t chunk = (nh + kWaves - 1) / kWaves;
-  const int64_t wbeg = (int64_t)wave * chunk < nh ? (int64_t)wave * chunk : nh;
-  const int64_t wend = wbeg + chunk < nh ? wbeg + chunk : nh;
   const int32_t* kfinal = nullptr;
-
-  if (passes == 0) {
-    for (int64_t i = threadIdx.x; i < nh; i += kThreads) ph[i] = (int32_t)i;
-  }
   for (int pass = 0; pass < passes; ++pass) {
-    const int shift = pass * 8;
     const int32_t* ink = (pass & 1) ? k0 : k1;  // valid for pass >= 1
     const int32_t* inv = (pass & 1) ? v0 : v1;
     int32_t* outk = (pass & 1) ? k1 : k0;
     int32_t* outv = (pass == passes - 1) ? ph : ((pass & 1) ? v1 : v0);
-    for (int i = threadIdx.x; i < kWaves * 256; i += kThreads) (&cnt[0][0])[i] = 0;
-    __syncthreads();
-    // count digits of this wave's slice
-    for (int64_t base = wbeg; base < wend; base += FASTAR_WAVE) {
-      const int64_t i = base + lane;
-      const bool valid = i < wend;
-      int32_t key = 0;
-      if (valid) {
-        if (pass == 0) key = P == 2 ? ((ids[2 * i] << 4) | flip_bit(ids[2 * i], ids[2 * i + 1])) : ids[i];
-        else key = ink[i];
-      }
-      const uint32_t digit = ((uint32_t)key >> shift) & 255u;
-      const uint64_t peers = match_digit(digit, valid);
-      if (valid && lane == __builtin_ctzll(peers)) cnt[wave][digit] += __popcll(peers);
-    }
-    __syncthreads();
-    // exclusive scan in (digit, wave) order
-    if (threadIdx.x < 256) {
-      int run = 0;
-      for (int w = 0; w < kWaves; ++w) {
-        const int c = cnt[w][threadIdx.x];
-        cnt[w][threadIdx.x] = run;
-        run += c;
-      }
-      dbase[threadIdx.x] = run;
-    }
-    __syncthreads();
-    if (threadIdx.x < FASTAR_WAVE) {
-      int t[4];
-      int s = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        t[j] = dbase[4 * lane + j];
-        s += t[j];
-      }
-      int incl = s;
-#pragma unroll
-      for (int off = 1; off < FASTAR_WAVE; off <<= 1) {
-        const int y = __shfl_up(incl, off, FASTAR_WAVE);
-        if (lane >= off) incl += y;
-      }
-      int ex = incl - s;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dbase[4 * lane + j] = ex;
-        ex += t[j];
-      }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kWaves * 256; i += kThreads) (&cnt[0][0])[i] += dbase[i & 255];
-    __syncthreads();
-    // stable scatter
-    for (int64_t base = wbeg; base < wend; base += FASTAR_WAVE) {
-      const int64_t i = base + lane;
-      const bool valid = i < wend;
-      int32_t key = 0, val = 0;
-      if (valid) {
-        if (pass == 0) {
-          key = P == 2 ? ((ids[2 * i] << 4) | flip_bit(ids[2 * i], ids[2 * i + 1])) : ids[i];
-          val = (int32_t)i;
-        } else {
-          key = ink[i];
-          val = inv[i];
-        }
-      }
-      const uint32_t digit = ((uint32_t)key >> shift) & 255u;
-      const uint64_t peers = match_digit(digit, valid);
-      const int pos = valid ? cnt[wave][digit] + __popcll(peers & lanemask_lt()) : 0;
-      if (valid) {
-        outk[pos] = key;
-        outv[pos] = val;
-        // the leader is the lowest peer: its rank is 0, so pos is the old count
-        if (lane == __builtin_ctzll(peers)) cnt[wave][digit] = pos + __popcll(peers);
-      }
-    }
-    __threadfence_block();
-    __syncthreads();
+    radix_pass(
+        wbeg, wend, pass * 8, cnt, dbase,
+        [&](int64_t i, int32_t& k, int32_t& v) {
+          if (pass == 0) {
+            k = key_of(i);
+            v = (int32_t)i;
+          } else {
+            k = ink[i];
+            v = inv[i];
+          }
+        },
+        [&](int pos, int32_t k, int32_t v) {
+          outk[pos] = k;
+          outv[pos] = v;
+        });
     kfinal = outk;
   }
-  // offsets[B] = #items whose first bucket < B: each run of equal buckets
-  // writes its start, then a suffix minimum fills the empty buckets
+  write_offsets(off, nbk, nh, shift0, [&](int64_t p) { return kfinal[p]; }, &cnt[0][0]);
+}
+
+// One probe and at most 12 bits: a single stable counting pass.  Per-wave
+// bucket counters (kDirectWaves x 2^b int32) fit in LDS, so the exclusive scan
+// over (bucket, wave) gives both each wave's scatter bases and the offsets.
+constexpr int kDirectWaves = 8;
+constexpr int kDirectMaxBits = 12;
+
+__global__ __launch_bounds__(kDirectWaves * FASTAR_WAVE) void bucket_index_direct_kernel(
+    const int32_t* __restrict__ bucket, int64_t n, int nbits, const int32_t* __restrict__ n_valid,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+  extern __shared__ int32_t cnt[];  // [kDirectWaves][2^nbits]
+  __shared__ int wtot[kDirectWaves];
+  constexpr int NT = kDirectWaves * FASTAR_WAVE;
+  const int h = blockIdx.x;
+  int64_t nh = n;
+  if (n_valid) {
+    const int64_t v = n_valid[h];
+    nh = v < 0 ? 0 : (v < n ? v : n);
+  }
   const int nbk = 1 << nbits;
+  const uint32_t bmask = (uint32_t)nbk - 1u;
+  const int32_t* ids = bucket + (int64_t)h * n;
+  int32_t* ph = perm + (int64_t)h * n;
   int32_t* off = offsets + (int64_t)h * (nbk + 1);
-  if (passes == 0) {
-    for (int B = threadIdx.x; B <= nbk; B += kThreads) off[B] = B == 0 ? 0 : (int32_t)nh;
-    return;
-  }
-  for (int B = threadIdx.x; B <= nbk; B += kThreads) off[B] = B == nbk ? (int32_t)nh : INT_MAX;
-  __threadfence_block();
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  for (int i = threadIdx.x; i < kDirectWaves * nbk / 4; i += NT)
+    reinterpret_cast<int4*>(cnt)[i] = make_int4(0, 0, 0, 0);
+  for (int i = (kDirectWaves * nbk / 4) * 4 + threadIdx.x; i < kDirectWaves * nbk; i += NT) cnt[i] = 0;
   __syncthreads();
-  for (int64_t p = threadIdx.x; p < nh; p += kThreads) {
-    const int k = kfinal[p] >> shift0;
-    if (p == 0 || (kfinal[p - 1] >> shift0) != k) off[k] = (int32_t)p;
+  const int64_t chunk = (nh + kDirectWaves - 1) / kDirectWaves;
+  const int64_t wbeg = (int64_t)wave * chunk < nh ? (int64_t)wave * chunk : nh;
+  const int64_t wend = wbeg + chunk < nh ? wbeg + chunk : nh;
+  int32_t* wc = cnt + wave * nbk;
+  // the wave's slice is handled in tiles of kTile ids per lane, loaded together
+  constexpr int kTile = 16;
+  for (int64_t t0 = wbeg; t0 < wend; t0 += kTile * FASTAR_WAVE) {
+    uint32_t b[kTile];
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      const int64_t i = t0 + r * FASTAR_WAVE + lane;
+      b[r] = i < wend ? ((uint32_t)ids[i] & bmask) : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int r = 0; r < kTile; ++r)
+      if (b[r] != 0xFFFFFFFFu) atomicAdd(&wc[b[r]], 1);  // counts: order does not matter
   }
-  __threadfence_block();
   __syncthreads();
-  int* cmin = &cnt[0][0];  // [kThreads] chunk minima
-  const int per = (nbk + 1 + kThreads - 1) / kThreads;
-  const int c0 = threadIdx.x * per;
-  const int c1 = c0 + per < nbk + 1 ? c0 + per : nbk + 1;
-  int m = INT_MAX;
-  for (int B = c0; B < c1; ++B) m = min(m, off[B]);
-  cmin[threadIdx.x] = m;
+  // exclusive scan over (bucket, wave): each thread owns kPer consecutive
+  // buckets (2^b <= NT * kPer), read and written as 128-bit words
+  constexpr int kPer = (1 << kDirectMaxBits) / NT;
+  static_assert(kPer == 8, "layout");
+  const int B0 = threadIdx.x * kPer;
+  int cw[kDirectWaves][kPer];
+  int tot[kPer];
+  int local = 0;
+  if (nbk >= 4) {
+#pragma unroll
+    for (int w = 0; w < kDirectWaves; ++w)
+#pragma unroll
+      for (int q = 0; q < kPer; q += 4) {
+        int4 v = make_int4(0, 0, 0, 0);
+        if (B0 + q < nbk) v = *reinterpret_cast<const int4*>(&cnt[w * nbk + B0 + q]);
+        cw[w][q] = v.x;
+        cw[w][q + 1] = v.y;
+        cw[w][q + 2] = v.z;
+        cw[w][q + 3] = v.w;
+      }
+  } else {
+#pragma unroll
+    for (int w = 0; w < kDirectWaves; ++w)
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) cw[w][q] = B0 + q < nbk ? cnt[w * nbk + B0 + q] : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    tot[q] = 0;
+#pragma unroll
+    for (int w = 0; w < kDirectWaves; ++w) tot[q] += cw[w][q];
+    local += tot[q];
+  }
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
+    const int y = __shfl_up(incl, o, FASTAR_WAVE);
+    if (lane >= o) incl += y;
+  }
+  if (lane == FASTAR_WAVE - 1) wtot[wave] = incl;
   __syncthreads();
-  // suffix minimum of the chunk minima (Hillis-Steele, reading to the right)
-  for (int d = 1; d < kThreads; d <<= 1) {
-    const int y = threadIdx.x + d < kThreads ? cmin[threadIdx.x + d] : INT_MAX;
-    __syncthreads();
-    cmin[threadIdx.x] = min(cmin[threadIdx.x], y);
-    __syncthreads();
+  int run = incl - local;
+  for (int w = 0; w < wave; ++w) run += wtot[w];
+  // bucket starts, then each wave's base within each bucket
+  int start[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    start[q] = run;
+    run += tot[q];
   }
-  m = threadIdx.x + 1 < kThreads ? cmin[threadIdx.x + 1] : INT_MAX;
-  for (int B = c1 - 1; B >= c0; --B) {
-    m = min(m, off[B]);
-    off[B] = m;
+  if (nbk >= 4) {
+#pragma unroll
+    for (int w = 0; w < kDirectWaves; ++w)
+#pragma unroll
+      for (int q = 0; q < kPer; q += 4)
+        if (B0 + q < nbk) {
+          *reinterpret_cast<int4*>(&cnt[w * nbk + B0 + q]) =
+              make_int4(start[q], start[q + 1], start[q + 2], start[q + 3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) start[q + e] += cw[w][q + e];
+        }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      if (B0 + q < nbk) {
+#pragma unroll
+        for (int w = 0; w < kDirectWaves; ++w) {
+          cnt[w * nbk + B0 + q] = start[q];
+          start[q] += cw[w][q];
+        }
+      }
+    }
   }
+  __syncthreads();
+  // stable scatter: each wave walks its slice in order, 64 tokens at a time
+  for (int64_t t0 = wbeg; t0 < wend; t0 += kTile * FASTAR_WAVE) {
+    uint32_t bt[kTile];
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      const int64_t i = t0 + r * FASTAR_WAVE + lane;
+      bt[r] = i < wend ? ((uint32_t)ids[i] & bmask) : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      const int64_t i = t0 + r * FASTAR_WAVE + lane;
+      if (t0 + r * FASTAR_WAVE >= wend) break;  // uniform
+      const bool valid = i < wend;
+      const uint32_t bb = bt[r];
+      uint64_t peers = ballot64(valid);
+#pragma unroll
+      for (int k = 0; k < kDirectMaxBits; ++k) {
+        if (k < nbits) {
+          const bool bit = (bb >> k) & 1u;
+          const uint64_t bk = ballot64(valid && bit);
+          peers &= bit ? bk : ~bk;
+        }
+      }
+      if (valid) {
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+        const int pos = wc[bb] + rank;
+        ph[pos] = (int32_t)i;
+        // the lowest peer (rank 0) advances the counter
+        if (rank == 0) wc[bb] = pos + __popcll(peers);
+      }
+    }
+  }
+  // after the scatter the last wave's counter of bucket B has reached the
+  // start of bucket B + 1: the offsets are written from it, coalesced
+  __syncthreads();
+  const int32_t* last = cnt + (kDirectWaves - 1) * nbk;
+  for (int B = threadIdx.x; B <= nbk; B += NT) off[B] = B == 0 ? 0 : last[B - 1];
 }
 
 }  // namespace
@@ -201,12 +450,21 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
                                int n_bits, const int32_t* n_valid, int32_t* offsets,
                                int32_t* perm, int32_t* ws, hipStream_t s) {
   if (heads == 0) return hipSuccess;
+  if (n_probes == 1 && n_bits <= kDirectMaxBits) {
+    hipLaunchKernelGGL(bucket_index_direct_kernel, dim3(heads), dim3(kDirectWaves * FASTAR_WAVE),
+                       (size_t)kDirectWaves * ((size_t)1 << n_bits) * sizeof(int32_t), s, bucket, n,
+                       n_bits, n_valid, offsets, perm);
+    return hipGetLastError();
+  }
+  // LDS staging whenever a head can fit (n, or a device count, at most kLdsItems)
+  const int use_lds = (n <= kLdsItems || n_valid) ? 1 : 0;
+  const size_t lds = use_lds ? (size_t)kLdsItems * 12 : 0;
   if (n_probes == 2)
-    hipLaunchKernelGGL(bucket_index_kernel<2>, dim3(heads), dim3(kThreads), 0, s, bucket, n,
-                       n_bits, n_valid, offsets, perm, ws);
+    hipLaunchKernelGGL(bucket_index_kernel<2>, dim3(heads), dim3(kThreads), lds, s, bucket, n,
+                       n_bits, n_valid, offsets, perm, ws, use_lds);
   else
-    hipLaunchKernelGGL(bucket_index_kernel<1>, dim3(heads), dim3(kThreads), 0, s, bucket, n,
-                       n_bits, n_valid, offsets, perm, ws);
+    hipLaunchKernelGGL(bucket_index_kernel<1>, dim3(heads), dim3(kThreads), lds, s, bucket, n,
+                       n_bits, n_valid, offsets, perm, ws, use_lds);
   return hipGetLastError();
 }
 

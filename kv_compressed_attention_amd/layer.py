@@ -10,7 +10,10 @@ compressed cache including the chunk's own frames):
   4. hash the prompt keys and prune them against the queries' buckets (AnnCA);
   5. AnnSA bucket attention over the cache with the + ln m bias;
   6. cross-attention over the kept prompt tokens.
-Every step is a libfastar call; this class only owns the torch buffers.
+Every step is a libfastar call; this class only owns the torch buffers and
+the ordering.  The query side (1, then 4 and 6) does not touch the cache, so
+it runs on a second stream of default priority, concurrently with 2, 3 and 5
+up to 5's need for the query index; both streams join before step returns.
 """
 
 from __future__ import annotations
@@ -42,6 +45,11 @@ class FastARLayer:
                        self.cache.workspace_bytes(chunk_frames),
                        self.cache.workspace_bytes(1))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        # the query-side stream has a workspace of its own
+        ws_q = max(lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
+                   lib.fastar_hash_workspace(H, n_prompt, n_bits, 1))
+        self.ws_q = torch.empty(ws_q, dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream(device=dev)
         self.q_ids = torch.empty(H, n_queries, n_probes, **i32)
         self.q_off = torch.empty(H, (1 << n_bits) + 1, **i32)
         self.q_perm = torch.empty(H, n_queries, **i32)
@@ -84,24 +92,59 @@ class FastARLayer:
             rep_perm=self.rep_perm, ws=self.ws, diag=self.diag)
 
     # -- one chunk ----------------------------------------------------------
-    def step(self, q, k_new, v_new, prompt_k=None, prompt_v=None):
-        fb.fastar_hash(q, self.planes, self.n_bits, self.n_probes, bucket=self.q_ids,
-                       offsets=self.q_off, perm=self.q_perm, ws=self.ws, diag=self.diag)
-        k_ids = self.hash_keys(k_new, self.k_ids)
-        fb.fastar_tempcache_merge(self.cache, k_new, v_new, k_ids.view(self.heads, -1),
-                                  self.chunk_frames, self.tau, group_of_new=self.group_of_new,
-                                  rep_offsets=self.rep_off, rep_perm=self.rep_perm, ws=self.ws,
-                                  diag=self.diag)
+    def step(self, q, k_new, v_new, prompt_k=None, prompt_v=None, prepare=None, timing=None):
+        """One chunk.  ``prepare`` (optional) runs on the caller's stream before
+        the cache is touched, concurrently with the query hashing; ``timing``
+        (optional dict) receives (start, end) event pairs per stage, recorded
+        on the stream each stage runs on."""
+        main = torch.cuda.current_stream(self.device)
+        side = self.side
+
+        def ev():
+            e = torch.cuda.Event(enable_timing=timing is not None)
+            e.record()
+            return e
+
+        def timed(name, fn):
+            if timing is None:
+                return fn()
+            a = ev()
+            r = fn()
+            timing.setdefault(name, []).append((a, ev()))
+            return r
+
+        # the side stream starts after everything already queued on main
+        # (the previous step's readers of the query index included)
+        start = ev()
+        with torch.cuda.stream(side):
+            side.wait_event(start)
+            timed("hash_q", lambda: fb.fastar_hash(
+                q, self.planes, self.n_bits, self.n_probes, bucket=self.q_ids, offsets=self.q_off,
+                perm=self.q_perm, ws=self.ws_q, diag=self.diag))
+            q_done = ev()
+            if prompt_k is not None:
+                def cross():
+                    fb.fastar_hash(prompt_k, self.planes, self.n_bits, 1, with_index=False,
+                                   bucket=self.p_ids, ws=self.ws_q, diag=self.diag)
+                    fb.fastar_prune_prompt(self.q_ids, self.p_ids.view(self.heads, -1),
+                                           self.n_bits, keep=self.keep, kept_idx=self.kept_idx,
+                                           n_kept=self.n_kept)
+                    fb.fastar_bucket_attention(q, prompt_k, prompt_v, key_list=self.kept_idx,
+                                               n_key_list=self.n_kept, out=self.o_cross,
+                                               lse=self.lse_cross)
+                timed("cross", cross)
+            side_done = ev()
+        if prepare is not None:
+            timed("prepare", prepare)
+        k_ids = timed("hash_k", lambda: self.hash_keys(k_new, self.k_ids))
+        timed("merge", lambda: fb.fastar_tempcache_merge(
+            self.cache, k_new, v_new, k_ids.view(self.heads, -1), self.chunk_frames, self.tau,
+            group_of_new=self.group_of_new, rep_offsets=self.rep_off, rep_perm=self.rep_perm,
+            ws=self.ws, diag=self.diag))
+        main.wait_event(q_done)
         c = self.cache
-        fb.fastar_bucket_attention(q, c.rep_k, c.v_mean, q_bucket=self.q_ids, q_perm=self.q_perm,
-                                   key_bias=c.log_count, k_offsets=self.rep_off,
-                                   k_perm=self.rep_perm, n_bits=self.n_bits, out=self.o_self,
-                                   lse=self.lse_self)
-        if prompt_k is not None:
-            fb.fastar_hash(prompt_k, self.planes, self.n_bits, 1, with_index=False,
-                           bucket=self.p_ids, ws=self.ws, diag=self.diag)
-            fb.fastar_prune_prompt(self.q_ids, self.p_ids.view(self.heads, -1), self.n_bits,
-                                   keep=self.keep, kept_idx=self.kept_idx, n_kept=self.n_kept)
-            fb.fastar_bucket_attention(q, prompt_k, prompt_v, key_list=self.kept_idx,
-                                       n_key_list=self.n_kept, out=self.o_cross,
-                                       lse=self.lse_cross)
+        timed("attention", lambda: fb.fastar_bucket_attention(
+            q, c.rep_k, c.v_mean, q_bucket=self.q_ids, q_perm=self.q_perm, key_bias=c.log_count,
+            k_offsets=self.rep_off, k_perm=self.rep_perm, n_bits=self.n_bits, out=self.o_self,
+            lse=self.lse_self))
+        main.wait_event(side_done)
