@@ -2,16 +2,21 @@
 
 A step is one chunk of the per-layer sequence on the layer workload (12 heads,
 d=128, 4680 queries = 3 frames x 1560 tokens, a 6-frame KV cache, 12 hash
-bits, one probe, bf16):
-  restore the compressed cache to its pre-chunk state (the merge is in place;
-  restoring makes every step identical work), hash the queries and build
-  their bucket index, hash the chunk's 3 new frames of keys, TempCache-merge
-  them frame by frame and index the representatives, then AnnSA bucket
-  attention of the queries over the compressed cache with the + ln m bias.
-The query hashing and index run on a second stream, concurrently with the
-restore, key hashing and merge.  The cache restore is inside the timed region
-(it makes the number conservative); per-stage event times are reported in
-"stages_ms".
+bits, one probe, bf16): hash the queries and build their bucket index, hash
+the chunk's 3 new frames of keys, TempCache-merge them frame by frame into the
+compressed cache of the first 3 frames and index the representatives, then
+AnnSA bucket attention of the queries over the compressed cache with the
++ ln m bias.  The merge works in place, so each of the K timed steps merges
+into a resident copy of the pre-chunk cache of its own (made before the timed
+region); after the run the K merged caches are checked to be identical.
+
+The query hashing and index run on a second stream, concurrently with the key
+hashing and merge (--serial queues everything on one stream).  Each step is
+captured into a HIP graph and replayed (--eager launches every kernel from
+Python instead, with per-stage event times in "stages_ms").  The attention
+kernel's duration for the roofline comes from HIP events around K launches of
+it on its stream right after the timed region (inside a graph there is no
+stream to record them on).
 
 Prints one JSON line.  --gpus N with N > 1 is refused: the library has no
 multi-GPU path (heads are independent, so a multi-GPU layer would shard them
@@ -45,6 +50,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=1, help="synthetic workload index (1, 3 or 4)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--serial", action="store_true",
+                   help="queue every stage on one stream (no query-side stream)")
+    p.add_argument("--eager", action="store_true",
+                   help="launch every kernel from Python each step instead of replaying the "
+                        "captured HIP graphs (per-stage event times, host-launch bound)")
     return p.parse_args()
 
 
@@ -148,22 +158,20 @@ def main():
                         dtype=tdt, device=dev)
     layer.set_planes(up(w.planes))
     q = up(w.q)
-    k_set, v_set = w.frames(0, w.setup_frames)
     for f in range(w.setup_frames):
         layer.merge(up(w.k_frames[:, f]), up(w.v_frames[:, f]), 1, with_index=False)
     k_new, v_new = (up(a) for a in w.frames(w.setup_frames, F))
-    del k_set, v_set
     torch.cuda.synchronize()
-    ngb = int(layer.cache.n_groups.max().item())
-    snap = {n: t[:, :ngb].clone() if t.dim() >= 2 and n not in ("frontier",) else t.clone()
-            for n, t in layer.cache.buffers().items()}
-
-    def restore():
-        for n, t in layer.cache.buffers().items():
-            if n in ("n_groups", "frontier"):
-                t.copy_(snap[n])
-            else:
-                t[:, :ngb].copy_(snap[n])
+    # the merge is in place: every timed step gets a resident copy of the
+    # pre-chunk cache of its own, so the K steps are identical work and the
+    # timed region holds only the hot path
+    pristine = layer.cache
+    caches = []
+    for _ in range(args.steps):
+        c = fa.TempCache(H, d, F * T, T, w.n_bits, tdt, dev)
+        c.copy_from(pristine)
+        caches.append(c)
+    scratch = fa.TempCache(H, d, F * T, T, w.n_bits, tdt, dev)
 
     # a plain 64 MiB device copy before the timed region: the calibration
     # kernel for the FETCH_SIZE / WRITE_SIZE counter passes
@@ -173,24 +181,45 @@ def main():
     del cal_src, cal_dst
 
     timing = {}
+    concurrent = not args.serial
 
-    def step(record):
-        layer.step(q, k_new, v_new, prepare=restore, timing=timing if record else None)
+    def warm_step():
+        scratch.copy_from(pristine)
+        layer.step(q, k_new, v_new, cache=scratch, concurrent=concurrent)
 
     for _ in range(args.warmup):
-        step(False)
+        warm_step()
     torch.cuda.synchronize()
-    # timed region: exactly K steps, with HIP events around the stages, each
-    # recorded on the stream its stage is enqueued on (the query side runs on
-    # the layer's second stream)
+    if args.eager:
+        def step(i):
+            layer.step(q, k_new, v_new, cache=caches[i], concurrent=concurrent, timing=timing)
+    else:
+        graphs = [layer.capture(q, k_new, v_new, cache=c, concurrent=concurrent) for c in caches]
+        warm = layer.capture(q, k_new, v_new, cache=scratch, concurrent=concurrent)
+        for _ in range(args.warmup):
+            scratch.copy_from(pristine)
+            warm.replay()
+        torch.cuda.synchronize()
+
+        def step(i):
+            graphs[i].replay()
+    # timed region: exactly K steps (eager: with HIP events around the
+    # stages, each recorded on the stream its stage is enqueued on)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
+    for i in range(args.steps):
+        step(i)
     t_enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = {("restore" if s == "prepare" else s): float(np.mean([a.elapsed_time(b) for a, b in v]))
-                for s, v in timing.items()}
+    if not args.eager:
+        # the attention kernel's launch duration: HIP events around each of K
+        # launches on the stream it is launched on, same inputs and buffers
+        # as the last timed step
+        for _ in range(args.steps):
+            layer.self_attention(q, timing, caches[-1])
+        torch.cuda.synchronize()
+    stage_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in v])) for s, v in timing.items()}
+    check_steps_agree(layer, caches)
 
     ms = wall * 1e3 / args.steps
     q_ids = layer.q_ids.cpu().numpy()
@@ -225,11 +254,10 @@ def main():
                       "roofline_tflops": min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3),
                       "attended_pairs": pairs,
                       "query_tokens_per_s": nq / t_att,
-                      "compressed_keys_per_head": ngb_after(layer)},
+                      "compressed_keys_per_head": ngb_after(layer, caches[-1])},
+        "launch": ("eager" if args.eager else "hip_graph") + ("_serial" if args.serial else "_2stream"),
         "stages_ms": stage_ms,
         "host_enqueue_ms_per_step": t_enq * 1e3 / args.steps,
-        "critical_path_ms_without_restore": sum(v for k, v in stage_ms.items()
-                                                 if k not in ("restore", "hash_q")),
         "diag": layer.diag.tolist(),
     }
     if not args.no_cpu_baseline:
@@ -243,8 +271,17 @@ def main():
     print(json.dumps(out))
 
 
-def ngb_after(layer):
-    return int(layer.cache.n_groups.max().item())
+def ngb_after(layer, cache):
+    return int(cache.n_groups.max().item())
+
+
+def check_steps_agree(layer, caches):
+    """Every timed step did the same work: the caches it merged into agree."""
+    ref = caches[0]
+    for c in caches[1:]:
+        for n, t in c.buffers().items():
+            if not torch.equal(t, ref.buffers()[n]):
+                raise RuntimeError(f"timed steps disagree on the merged cache ({n})")
 
 
 if __name__ == "__main__":

@@ -12,8 +12,8 @@ compressed cache including the chunk's own frames):
   6. cross-attention over the kept prompt tokens.
 Every step is a libfastar call; this class only owns the torch buffers and
 the ordering.  The query side (1, then 4 and 6) does not touch the cache, so
-it runs on a second stream of default priority, concurrently with 2, 3 and 5
-up to 5's need for the query index; both streams join before step returns.
+it runs on a second stream of default priority, concurrently with 2 and 3 up
+to 5's need for the query index; all streams join before step returns.
 """
 
 from __future__ import annotations
@@ -92,59 +92,93 @@ class FastARLayer:
             rep_perm=self.rep_perm, ws=self.ws, diag=self.diag)
 
     # -- one chunk ----------------------------------------------------------
-    def step(self, q, k_new, v_new, prompt_k=None, prompt_v=None, prepare=None, timing=None):
-        """One chunk.  ``prepare`` (optional) runs on the caller's stream before
-        the cache is touched, concurrently with the query hashing; ``timing``
-        (optional dict) receives (start, end) event pairs per stage, recorded
-        on the stream each stage runs on."""
-        main = torch.cuda.current_stream(self.device)
-        side = self.side
+    def _ev(self, timing):
+        e = torch.cuda.Event(enable_timing=timing is not None)
+        e.record()
+        return e
 
-        def ev():
-            e = torch.cuda.Event(enable_timing=timing is not None)
-            e.record()
-            return e
+    def _timed(self, timing, name, fn):
+        if timing is None:
+            return fn()
+        a = self._ev(timing)
+        r = fn()
+        timing.setdefault(name, []).append((a, self._ev(timing)))
+        return r
 
-        def timed(name, fn):
-            if timing is None:
-                return fn()
-            a = ev()
-            r = fn()
-            timing.setdefault(name, []).append((a, ev()))
-            return r
+    def _query_hash(self, q, timing):
+        self._timed(timing, "hash_q", lambda: fb.fastar_hash(
+            q, self.planes, self.n_bits, self.n_probes, bucket=self.q_ids, offsets=self.q_off,
+            perm=self.q_perm, ws=self.ws_q, diag=self.diag))
 
-        # the side stream starts after everything already queued on main
-        # (the previous step's readers of the query index included)
-        start = ev()
-        with torch.cuda.stream(side):
-            side.wait_event(start)
-            timed("hash_q", lambda: fb.fastar_hash(
-                q, self.planes, self.n_bits, self.n_probes, bucket=self.q_ids, offsets=self.q_off,
-                perm=self.q_perm, ws=self.ws_q, diag=self.diag))
-            q_done = ev()
-            if prompt_k is not None:
-                def cross():
-                    fb.fastar_hash(prompt_k, self.planes, self.n_bits, 1, with_index=False,
-                                   bucket=self.p_ids, ws=self.ws_q, diag=self.diag)
-                    fb.fastar_prune_prompt(self.q_ids, self.p_ids.view(self.heads, -1),
-                                           self.n_bits, keep=self.keep, kept_idx=self.kept_idx,
-                                           n_kept=self.n_kept)
-                    fb.fastar_bucket_attention(q, prompt_k, prompt_v, key_list=self.kept_idx,
-                                               n_key_list=self.n_kept, out=self.o_cross,
-                                               lse=self.lse_cross)
-                timed("cross", cross)
-            side_done = ev()
-        if prepare is not None:
-            timed("prepare", prepare)
-        k_ids = timed("hash_k", lambda: self.hash_keys(k_new, self.k_ids))
-        timed("merge", lambda: fb.fastar_tempcache_merge(
-            self.cache, k_new, v_new, k_ids.view(self.heads, -1), self.chunk_frames, self.tau,
+    def _cross(self, q, prompt_k, prompt_v, timing):
+        def run():
+            fb.fastar_hash(prompt_k, self.planes, self.n_bits, 1, with_index=False,
+                           bucket=self.p_ids, ws=self.ws_q, diag=self.diag)
+            fb.fastar_prune_prompt(self.q_ids, self.p_ids.view(self.heads, -1), self.n_bits,
+                                   keep=self.keep, kept_idx=self.kept_idx, n_kept=self.n_kept)
+            fb.fastar_bucket_attention(q, prompt_k, prompt_v, key_list=self.kept_idx,
+                                       n_key_list=self.n_kept, out=self.o_cross,
+                                       lse=self.lse_cross)
+        self._timed(timing, "cross", run)
+
+    def _cache_side(self, cache, k_new, v_new, timing):
+        k_ids = self._timed(timing, "hash_k", lambda: self.hash_keys(k_new, self.k_ids))
+        self._timed(timing, "merge", lambda: fb.fastar_tempcache_merge(
+            cache, k_new, v_new, k_ids.view(self.heads, -1), self.chunk_frames, self.tau,
             group_of_new=self.group_of_new, rep_offsets=self.rep_off, rep_perm=self.rep_perm,
             ws=self.ws, diag=self.diag))
-        main.wait_event(q_done)
-        c = self.cache
-        timed("attention", lambda: fb.fastar_bucket_attention(
+
+    def self_attention(self, q, timing=None, cache=None):
+        c = self.cache if cache is None else cache
+        self._timed(timing, "attention", lambda: fb.fastar_bucket_attention(
             q, c.rep_k, c.v_mean, q_bucket=self.q_ids, q_perm=self.q_perm, key_bias=c.log_count,
             k_offsets=self.rep_off, k_perm=self.rep_perm, n_bits=self.n_bits, out=self.o_self,
             lse=self.lse_self))
+
+    def step(self, q, k_new, v_new, prompt_k=None, prompt_v=None, cache=None, concurrent=True,
+             timing=None):
+        """One chunk, merged into ``cache`` (default: the layer's own).
+
+        With ``concurrent`` the query side runs on the second stream, forked
+        after everything already queued on the caller's stream (the previous
+        step's readers of the query index included) and joined before return;
+        otherwise every stage is queued on the caller's stream in order.
+        ``timing`` (optional dict) receives (start, end) event pairs per
+        stage, recorded on the stream each stage runs on."""
+        cache = self.cache if cache is None else cache
+        if not concurrent:
+            self._query_hash(q, timing)
+            self._cache_side(cache, k_new, v_new, timing)
+            self.self_attention(q, timing, cache)
+            if prompt_k is not None:
+                self._cross(q, prompt_k, prompt_v, timing)
+            return
+        main = torch.cuda.current_stream(self.device)
+        start = self._ev(None)
+        with torch.cuda.stream(self.side):
+            self.side.wait_event(start)
+            self._query_hash(q, timing)
+            q_done = self._ev(None)
+            if prompt_k is not None:
+                self._cross(q, prompt_k, prompt_v, timing)
+            side_done = self._ev(None)
+        self._cache_side(cache, k_new, v_new, timing)
+        main.wait_event(q_done)
+        self.self_attention(q, timing, cache)
         main.wait_event(side_done)
+
+    def capture(self, q, k_new, v_new, prompt_k=None, prompt_v=None, cache=None,
+                concurrent=True):
+        """Capture one chunk on these buffers into a HIP graph, replayed with
+        ``.replay()`` on the current stream: one graph launch instead of one
+        launch per kernel.
+
+        Call after at least one eager ``step`` (first use of torch's streams
+        and events does one-time set-up, which capture does not allow).  Every
+        replay reads and writes the same addresses."""
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(q, k_new, v_new, prompt_k, prompt_v, cache=cache, concurrent=concurrent)
+        torch.cuda.synchronize(self.device)
+        return g
