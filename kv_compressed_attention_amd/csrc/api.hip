@@ -154,8 +154,9 @@ size_t fastar_tempcache_workspace(const fastar_cache_t* c, int n_frames) {
   if (!c || n_frames < 0 || c->heads < 0 || c->tokens_per_frame < 0 || c->capacity < 0) return 0;
   const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
   const size_t ts = (size_t)fastar::tempcache_table_size(c->tokens_per_frame);
-  return 3 * align_up(4 * H * (F + 1) * ts) + align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
-         5 * align_up(4 * H * F * T) + align_up(16 * H * (size_t)c->capacity);
+  return align_up(16 * H * (F + 1) * ts) + align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
+         align_up(16 * H * F * T) + align_up(4 * H * F) + 3 * align_up(4 * H * F * T) +
+         align_up(16 * H * (size_t)c->capacity);
 }
 
 fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
@@ -216,14 +217,12 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
     return (int32_t*)p;
   };
   fastar::MergeWs mw;
-  mw.tkey = take(4 * H * (F + 1) * ts);
-  mw.tstart = take(4 * H * (F + 1) * ts);
-  mw.tcount = take(4 * H * (F + 1) * ts);
+  mw.tab = (int4*)take(16 * H * (F + 1) * ts);
   mw.cand = take(4 * H * (F + 1) * T);
   mw.candg = take(4 * H * T);
-  mw.target = take(4 * H * F * T);
-  mw.tcos = (float*)take(4 * H * F * T);
-  mw.mgroup = take(4 * H * F * T);
+  mw.srec = (int4*)take(16 * H * F * T);
+  mw.nseg = take(4 * H * F);
+  mw.link = take(4 * H * F * T);
   mw.gid = take(4 * H * F * T);
   mw.nextj = take(4 * H * F * T);
   mw.index_ws = take(16 * H * (size_t)c->capacity);

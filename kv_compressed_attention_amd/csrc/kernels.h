@@ -39,14 +39,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // tempcache.hip -------------------------------------------------------------
 struct MergeWs {
-  int32_t* tkey;      // [H][n_frames+1][tsize] bucket tables (see tempcache.hip)
-  int32_t* tstart;    // [H][n_frames+1][tsize]
-  int32_t* tcount;    // [H][n_frames+1][tsize]
+  int4* tab;          // [H][n_frames+1][tsize] bucket tables (see tempcache.hip)
   int32_t* cand;      // [H][n_frames+1][T]
   int32_t* candg;     // [H][T]
-  int32_t* target;    // [H][n_frames][T]
-  float* tcos;        // [H][n_frames][T]
-  int32_t* mgroup;    // [H][n_frames][T]
+  int4* srec;         // [H][n_frames][T]
+  int32_t* nseg;      // [H][n_frames]
+  int32_t* link;      // [H][n_frames][T]
   int32_t* gid;       // [H][n_frames][T]
   int32_t* nextj;     // [H][n_frames][T]
   int32_t* index_ws;  // bucket index scratch

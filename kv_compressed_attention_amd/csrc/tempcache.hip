@@ -4,20 +4,27 @@
 // The candidates of a new key of frame f are the previous frame's tokens in
 // its bucket: for f = 0 the representatives of the cache's last frame (the
 // frontier), for f > 0 the raw keys of new frame f - 1 (each of which is the
-// representative of its group after frame f - 1).  The matches of all frames
-// therefore do not depend on each other and run in one launch; only the group
-// bookkeeping is sequential.  Four launches per call:
+// representative of its group after frame f - 1).  A key only ever competes
+// with the keys of its own bucket for a candidate, so matching and the
+// one-to-one resolution of all frames are independent per (frame, bucket)
+// and run in one launch; only the numbering of new groups is sequential.
+// Five launches per call:
 //   tc_index    per (table, head): the frontier and each new frame grouped by
-//               bucket (LDS open-addressing table -> contiguous segments);
-//   tc_match    16 lanes per new key, all frames: cosine with every candidate
-//               of its bucket, keep the best, propose if it passes tau;
-//   tc_resolve  one workgroup per head, frames in order: a candidate with
-//               several proposers keeps the one of largest cosine (ties: smaller
-//               j); the other keys open groups numbered in ascending j;
-//   tc_apply    16 lanes per touched group: follow the group's chain of tokens
-//               through the frames, accumulate the float32 value sum in frame
-//               order, write count, sum, mean (rounded once to the cache
-//               dtype), last key, its bucket and ln count.
+//               bucket (LDS open-addressing table -> contiguous segments, and
+//               the list of occupied segments of each new frame);
+//   tc_match    one wave per (frame, bucket segment): cosines of the segment's
+//               keys with the candidates of the same bucket as 16 x 16 tiles
+//               (MFMA for bf16), best candidate per key, proposal if it passes
+//               tau, then per candidate the proposer of largest cosine (ties:
+//               smaller j) wins and links to it; the other keys open groups;
+//   tc_number   one workgroup per head: new groups numbered in (frame, j)
+//               order, the group count;
+//   tc_apply    16 lanes per chain of tokens (a token that opens a group or
+//               extends a frontier group, then its links through the frames):
+//               float32 value sum in frame order, count, mean (rounded once
+//               to the cache dtype), last key, its bucket and ln count, the
+//               group of every member and the new frontier;
+//   then the bucket index of the representatives.
 // Cosines are compared in float32 against a certified error bound; a decision
 // inside the bound is redone in float64 (where products of the stored values
 // are exact) and counted in the diagnostics.
@@ -36,6 +43,12 @@ namespace {
 // first-order estimate
 template <int D>
 __device__ __forceinline__ float cos_err32() { return (float)(4 * D + 32) * 0x1p-24f; }
+// the same for a dot product accumulated by MFMA, taken (as for the hash) at
+// four times the float32 worst case: twice (4 D u + D u + 6 u)
+template <typename T, int D>
+__device__ __forceinline__ float match_err() {
+  return sizeof(T) == 2 ? (float)(10 * D + 32) * 0x1p-24f : cos_err32<D>();
+}
 template <int D>
 __device__ __forceinline__ double cos_err64() { return (double)(4 * D + 32) * 0x1p-53; }
 
@@ -123,19 +136,25 @@ __device__ __forceinline__ uint32_t slot_hash(int b, uint32_t mask) {
   return ((uint32_t)b * 2654435761u >> 7) & mask;
 }
 
+// keys are matched in tiles of this many (one wave each)
+constexpr int kKeyTile = 16;
+
 // Groups Tf tokens by bucket for one head.  get(i, b, g) gives token i's
 // bucket and group (g < 0: token left out).  Writes cand (tokens, bucket
-// segments contiguous), optionally candg (their groups) and the table
-// tkey/tstart/tcount (slot -> bucket + 1, segment).  Whole workgroup; lds
-// must hold 2 * tsize int32 + 2 * Tf int16.
+// segments contiguous), optionally candg (their groups), the open-addressing
+// table tab (slot -> {bucket + 1 (0: empty), segment start, length, 0}) and,
+// optionally, the segment records srec ({bucket, start, length, 0}, in no
+// particular order) and their number (*nseg).  Whole workgroup; lds must
+// hold 2 * tsize int32 + 2 * Tf int16.
 template <typename Get>
-__device__ void group_by_bucket(int Tf, int tsize, Get get, int32_t* lds, int32_t* tkey,
-                                int32_t* tstart, int32_t* tcount, int32_t* cand, int32_t* candg) {
+__device__ void group_by_bucket(int Tf, int tsize, Get get, int32_t* lds, int4* tab, int32_t* cand,
+                                int32_t* candg, int4* srec, int32_t* nseg) {
   int32_t* skey = lds;
   int32_t* scnt = skey + tsize;
   int16_t* slot_of = reinterpret_cast<int16_t*>(scnt + tsize);
   int16_t* pos_of = slot_of + Tf;
   __shared__ int wtot[16];
+  __shared__ int nsg;
   const uint32_t mask = (uint32_t)tsize - 1u;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -143,6 +162,7 @@ __device__ void group_by_bucket(int Tf, int tsize, Get get, int32_t* lds, int32_
     skey[s] = 0;
     scnt[s] = 0;
   }
+  if (tid == 0) nsg = 0;
   __syncthreads();
   for (int i = tid; i < Tf; i += nthr) {
     int b, g;
@@ -184,15 +204,13 @@ __device__ void group_by_bucket(int Tf, int tsize, Get get, int32_t* lds, int32_
   for (int w = 0; w < wave; ++w) run += wtot[w];
   for (int s = s0; s < s0 + per && s < tsize; ++s) {
     const int c = scnt[s];
-    if (tkey) {
-      tkey[s] = skey[s];
-      tcount[s] = c;
-      tstart[s] = run;
-    }
+    tab[s] = make_int4(skey[s], run, c, 0);
+    if (srec && c > 0) srec[atomicAdd(&nsg, 1)] = make_int4(skey[s] - 1, run, c, 0);
     scnt[s] = run;  // segment start, for the fill below
     run += c;
   }
   __syncthreads();
+  if (nseg && tid == 0) *nseg = nsg;
   for (int i = tid; i < Tf; i += nthr) {
     const int slot = slot_of[i];
     if (slot < 0) continue;
@@ -209,17 +227,15 @@ struct MergeArgs {
   int64_t kb_stride;  // F * Tf
   // per-head tables t = 0..F: table 0 indexes the cache's last frame (the
   // frontier), table f + 1 indexes new frame f, each by bucket
-  int32_t* tkey;      // [H][F+1][tsize] bucket + 1, 0 = empty slot
-  int32_t* tstart;    // [H][F+1][tsize] segment start in cand
-  int32_t* tcount;    // [H][F+1][tsize] segment length
+  int4* tab;          // [H][F+1][tsize] {bucket + 1 (0: empty), start in cand, length, 0}
   int32_t* cand;      // [H][F+1][Tf] token indices, bucket segments contiguous
   int32_t* candg;     // [H][Tf] groups of table 0's tokens
-  int32_t* target;    // [H][F][Tf] proposed previous-frame token, or -1
-  float* tcos;        // [H][F][Tf] its cosine
-  int32_t* mgroup;    // [H][F][Tf] group a token extends, -1 if it opens one
-  int32_t* gid;       // [H][F][Tf] final group of each token (-1: dropped)
-  int32_t* nextj;     // [H][F][Tf] token of the next frame that extends this
-                      //            token's group, or -1
+  int4* srec;         // [H][F][Tf] segments of table f + 1: {bucket, start, length, 0}
+  int32_t* nseg;      // [H][F] their number
+  int32_t* link;      // [H][F][Tf] f = 0: frontier group the token extends;
+                      //            f > 0: frame f - 1 token it extends; -1: opens a group
+  int32_t* gid;       // [H][F][Tf] group a token opens (-1: no room left)
+  int32_t* nextj;     // [H][F][Tf] token of frame f + 1 that extends this one, or -1
 };
 
 __device__ __forceinline__ int64_t tab_off(const MergeArgs& a, int h, int t) {
@@ -233,16 +249,14 @@ __device__ __forceinline__ int64_t frame_off(const MergeArgs& a, int h, int f) {
 }
 
 // Table 0 from the frontier (blockIdx.x == 0) or table f + 1 from new frame f.
-// One workgroup per (table, head).
+// One workgroup per (table, head).  Also clears new frame f's nextj links.
 __global__ __launch_bounds__(1024) void tc_index_kernel(
     const int32_t* __restrict__ frontier, const int32_t* __restrict__ rep_bucket,
     const int32_t* __restrict__ n_groups, const int32_t* __restrict__ kbucket, MergeArgs a) {
   extern __shared__ int32_t lds[];
   const int h = blockIdx.y;
   const int t = blockIdx.x;
-  int32_t* tk = a.tkey + tab_off(a, h, t);
-  int32_t* ts = a.tstart + tab_off(a, h, t);
-  int32_t* tc = a.tcount + tab_off(a, h, t);
+  int4* tb = a.tab + tab_off(a, h, t);
   int32_t* cd = a.cand + cand_off(a, h, t);
   if (t == 0) {
     const bool empty = n_groups[h] <= 0;
@@ -254,290 +268,547 @@ __global__ __launch_bounds__(1024) void tc_index_kernel(
           g = empty ? -1 : fr[i];
           b = g >= 0 ? rb[g] : 0;
         },
-        lds, tk, ts, tc, cd, a.candg + (int64_t)h * a.Tf);
+        lds, tb, cd, a.candg + (int64_t)h * a.Tf, nullptr, nullptr);
   } else {
-    const int32_t* kb = kbucket + (int64_t)h * a.kb_stride + (int64_t)(t - 1) * a.Tf;
+    const int f = t - 1;
+    const int32_t* kb = kbucket + (int64_t)h * a.kb_stride + (int64_t)f * a.Tf;
+    for (int i = threadIdx.x; i < a.Tf; i += blockDim.x) a.nextj[frame_off(a, h, f) + i] = -1;
     group_by_bucket(
         a.Tf, a.tsize,
         [&](int i, int& b, int& g) {
           b = kb[i];
           g = 0;
         },
-        lds, tk, ts, tc, cd, nullptr);
+        lds, tb, cd, nullptr, a.srec + frame_off(a, h, f), a.nseg + (int64_t)h * a.F + f);
   }
 }
 
-// Best previous-frame candidate of every new key of every frame, 16 lanes per
-// key (each lane d/16 dims).  Frame f's candidates are the frontier (f = 0)
-// or new frame f - 1's tokens with the key's bucket; keys are visited in
-// bucket order so that neighbouring groups of lanes share candidate rows.
+// 16 x 16 tiles of dot products, keys (rows) by candidates (columns).  Loads
+// are issued (issue_*) before they are used (finish_keys, dots), so that the
+// key rows and a tile of candidate rows are in flight together.  After
+// finish_keys, lane l (g = l >> 4) holds the squared norms of keys 4g + i in
+// kn[i]; dots gives the dots of keys 4g + i with candidate l & 15 in s[i] and
+// that candidate's squared norm in cn.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void tc_match_kernel(
-    const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
-    const int32_t* __restrict__ kbucket, const int32_t* __restrict__ n_groups, float tau,
-    MergeArgs a, fastar_diag_t* __restrict__ diag) {
-  constexpr int EPL = D / 16;
-  const int h = blockIdx.y;
-  const int f = blockIdx.z;
-  const int sub = threadIdx.x & 15;
-  const int p = blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (p >= a.Tf) return;  // whole 16-lane group
-  const int j = a.cand[cand_off(a, h, f + 1) + p];
-  const T* kj = knew + (int64_t)h * k_sh + ((int64_t)f * a.Tf + j) * k_st + sub * EPL;
-  float av[EPL];
-  Chunk<T, EPL>::load(kj, av);
-  int start = 0, cnt = 0;
-  if (f > 0 || n_groups[h] > 0) {
-    const int bj = kbucket[(int64_t)h * a.kb_stride + (int64_t)f * a.Tf + j];
-    const uint32_t mask = (uint32_t)a.tsize - 1u;
-    const int32_t* tk = a.tkey + tab_off(a, h, f);
-    uint32_t slot = slot_hash(bj, mask);
-    int w;
-    while ((w = tk[slot]) != 0 && w != bj + 1) slot = (slot + 1u) & mask;
-    if (w != 0) {
-      start = a.tstart[tab_off(a, h, f) + slot];
-      cnt = a.tcount[tab_off(a, h, f) + slot];
+struct TileDot;
+
+template <int D>
+struct TileDot<uint16_t, D> {
+  static constexpr int NC = D / 32;
+  struct Rows {
+    uint4 u[NC];  // row l & 15, dims 32c + 8g .. +8
+  };
+  Rows kr;
+  float kn[4];
+  __device__ __forceinline__ static float sumsq(const uint4& u) {
+    float s = 0.f;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(w[i] << 16);
+      const float hi = __uint_as_float(w[i] & 0xFFFF0000u);
+      s = fmaf(lo, lo, s);
+      s = fmaf(hi, hi, s);
+    }
+    return s;
+  }
+  __device__ __forceinline__ static Rows issue(const uint16_t* row) {
+    const int g = lane_id() >> 4;
+    Rows r;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      r.u[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (row) r.u[c] = *reinterpret_cast<const uint4*>(row + 32 * c + 8 * g);
+    }
+    return r;
+  }
+  __device__ __forceinline__ static float rownorm(const Rows& r) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) s += sumsq(r.u[c]);
+    s += shfl_xor_f(s, 16);
+    s += shfl_xor_f(s, 32);
+    return s;
+  }
+  __device__ __forceinline__ void issue_keys(const uint16_t* row) { kr = issue(row); }
+  __device__ __forceinline__ void finish_keys() {
+    const int g = lane_id() >> 4;
+    const float s = rownorm(kr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kn[i] = __shfl(s, 4 * g + i, FASTAR_WAVE);
+  }
+  __device__ __forceinline__ void dots(const Rows& cr, float* s, float& cn) const {
+    cn = rownorm(cr);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr.u[c]),
+                                                     __builtin_bit_cast(bf16x8_t, cr.u[c]), acc,
+                                                     0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = acc[i];
+  }
+};
+
+template <int D>
+struct TileDot<float, D> {
+  struct Rows {
+    const float* p;
+  };
+  const float* own;    // this lane's key row (l & 15)
+  const float* kr[4];  // rows of keys 4g + i (null: none)
+  float kn[4];
+  __device__ __forceinline__ static Rows issue(const float* row) { return Rows{row}; }
+  __device__ __forceinline__ void issue_keys(const float* row) { own = row; }
+  __device__ __forceinline__ void finish_keys() {
+    const int g = lane_id() >> 4;
+    const uint64_t u = (uint64_t)own;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)u, 4 * g + i, FASTAR_WAVE);
+      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(u >> 32), 4 * g + i, FASTAR_WAVE);
+      kr[i] = (const float*)(((uint64_t)hi << 32) | lo);
+      float n = 0.f;
+      if (kr[i])
+        for (int d = 0; d < D; ++d) n = fmaf(kr[i][d], kr[i][d], n);
+      kn[i] = n;
     }
   }
-  int best = -1;
-  float cb = 0.f;
-  bool prop = false;
-  if (cnt > 0) {
-    const int32_t* ci = a.cand + cand_off(a, h, f) + start;
-    const int32_t* cg = a.candg + (int64_t)h * a.Tf + start;
-    // candidate row k: the representative of its group (f == 0) or the raw key
-    // of new frame f - 1 (it is the representative of whatever group it is in)
-    const T* base0 = rep_k + (int64_t)h * a.cap * D + sub * EPL;
-    const T* base1 = knew + (int64_t)h * k_sh + (int64_t)(f - 1) * a.Tf * k_st + sub * EPL;
-    auto row = [&](int k) -> const T* {
-      return f == 0 ? base0 + (int64_t)cg[k] * D : base1 + (int64_t)ci[k] * k_st;
-    };
-    float nj2 = 0.f;
+  __device__ __forceinline__ void dots(const Rows& cr, float* s, float& cn) const {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) nj2 = fmaf(av[e], av[e], nj2);
-    nj2 = sum16(nj2);
-    const float rj = nj2 > 0.f ? rsqrtf(nj2) : 0.f;
-    Top2<float> t;
-    t.init();
-    constexpr int U = 4;  // candidates per batch, so that their row loads overlap
-    for (int k0 = 0; k0 < cnt; k0 += U) {
-      const T* rp[U];
-      int ik[U];
+    for (int i = 0; i < 4; ++i) s[i] = 0.f;
+    cn = 0.f;
+    if (!cr.p) return;
+    for (int d = 0; d < D; ++d) {
+      const float c = cr.p[d];
+      cn = fmaf(c, c, cn);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = k0 + u < cnt ? k0 + u : k0;
-        rp[u] = row(kk);
-        ik[u] = ci[kk];
-      }
-      float r[U][EPL];
-#pragma unroll
-      for (int u = 0; u < U; ++u) Chunk<T, EPL>::load(rp[u], r[u]);
-      float dt[U], ni2[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        dt[u] = 0.f;
-        ni2[u] = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          dt[u] = fmaf(av[e], r[u][e], dt[u]);
-          ni2[u] = fmaf(r[u][e], r[u][e], ni2[u]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        dt[u] = sum16(dt[u]);
-        ni2[u] = sum16(ni2[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (k0 + u < cnt) t.add((nj2 > 0.f && ni2[u] > 0.f) ? dt[u] * rj * rsqrtf(ni2[u]) : 0.f, ik[u]);
-    }
-    const float e32 = cos_err32<D>();
-    best = t.best;
-    cb = t.c1;
-    if (t.c1 < tau - e32) {
-      prop = false;  // no candidate can reach tau
-    } else if (t.c1 >= tau + e32 && t.c1 - t.c2 > 2.f * e32) {
-      prop = true;   // clear winner, clearly above tau
-    } else {
-      // float64: products of the stored values are exact
-      if (diag && sub == 0) atomicAdd(&diag->merge_fallbacks, 1u);
-      double ad[EPL];
-      double n1 = 0.0;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        ad[e] = (double)av[e];
-        n1 += ad[e] * ad[e];
-      }
-      n1 = sum16d(n1);
-      Top2<double> u;
-      u.init();
-      for (int k = 0; k < cnt; ++k) {
-        float r[EPL];
-        Chunk<T, EPL>::load(row(k), r);
-        double dt = 0.0, n2 = 0.0;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          dt += ad[e] * (double)r[e];
-          n2 += (double)r[e] * (double)r[e];
-        }
-        dt = sum16d(dt);
-        n2 = sum16d(n2);
-        u.add((n1 > 0.0 && n2 > 0.0) ? dt / sqrt(n1 * n2) : 0.0, ci[k]);
-      }
-      const double e64 = cos_err64<D>();
-      const bool sure = (u.c1 < (double)tau - e64) ||
-                        (u.c1 >= (double)tau + e64 && u.c1 - u.c2 > 2.0 * e64);
-      if (!sure && diag && sub == 0) atomicAdd(&diag->unresolved, 1u);
-      best = u.best;
-      prop = u.c1 >= (double)tau;
-      cb = (float)u.c1;
+      for (int i = 0; i < 4; ++i)
+        if (kr[i]) s[i] = fmaf(kr[i][d], c, s[i]);
     }
   }
-  if (sub == 0) {
-    a.target[frame_off(a, h, f) + j] = prop ? best : -1;
-    a.tcos[frame_off(a, h, f) + j] = cb;
+};
+
+template <typename F>
+__device__ __forceinline__ void top2_merge_xor(Top2<F>& t, int m) {
+  const F c1 = __shfl_xor(t.c1, m, FASTAR_WAVE);
+  const F c2 = __shfl_xor(t.c2, m, FASTAR_WAVE);
+  const int b = __shfl_xor(t.best, m, FASTAR_WAVE);
+  if (b < 0) return;
+  if (t.best < 0) {
+    t.c1 = c1;
+    t.c2 = c2;
+    t.best = b;
+  } else if (c1 > t.c1 || (c1 == t.c1 && b < t.best)) {
+    t.c2 = t.c1 > c2 ? t.c1 : c2;
+    t.c1 = c1;
+    t.best = b;
+  } else if (c1 > t.c2) {
+    t.c2 = c1;
   }
 }
 
+// float64 cosine of two rows, the whole wave (lane l takes dims l, l + 64, ..);
+// every lane returns it.  Products of the stored values are exact in float64.
 template <typename T, int D>
-__device__ double cos64(const T* x, const T* y) {
+__device__ double wave_cos64(const T* x, const T* y) {
   double s = 0.0, na = 0.0, nb = 0.0;
-  for (int d = 0; d < D; ++d) {
+  for (int d = lane_id(); d < D; d += FASTAR_WAVE) {
     const double u = (double)Elem<T>::load(x, d);
     const double v = (double)Elem<T>::load(y, d);
     s += u * v;
     na += u * u;
     nb += v * v;
   }
+#pragma unroll
+  for (int m = 1; m < FASTAR_WAVE; m <<= 1) {
+    s += __shfl_xor(s, m, FASTAR_WAVE);
+    na += __shfl_xor(na, m, FASTAR_WAVE);
+    nb += __shfl_xor(nb, m, FASTAR_WAVE);
+  }
   if (na == 0.0 || nb == 0.0) return 0.0;
   return s / sqrt(na * nb);
 }
 
-// One workgroup per head walks the frames in order.  Per frame: a candidate
-// proposed to by several keys keeps the proposer of largest cosine (ties to
-// smaller j); winners extend the candidate's group (mgroup, and the chain link
-// nextj of the candidate); the others are numbered as new groups in ascending
-// j (gid, group_of_new).  At the end: the frontier and the group count.
+// What one wave needs to match the keys of one (frame, bucket) segment.
 template <typename T, int D>
-__global__ __launch_bounds__(1024) void tc_resolve_kernel(
-    const T* __restrict__ rep_k, int32_t* __restrict__ frontier,
-    int32_t* __restrict__ n_groups, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
-    int32_t* __restrict__ group_of_new, MergeArgs a, fastar_diag_t* __restrict__ diag) {
-  extern __shared__ int32_t lds[];
-  const int Tf = a.Tf;
-  int32_t* plist = lds;                              // [Tf] proposer list heads
-  float* tcl = reinterpret_cast<float*>(plist + Tf); // [Tf]
-  int16_t* tg = reinterpret_cast<int16_t*>(tcl + Tf);// [Tf]
-  int16_t* nxt = tg + Tf;                            // [Tf]
+struct SegCtx {
+  const T* kf;          // frame f keys
+  const T* kp;          // frame f - 1 keys (f > 0)
+  const T* rk;          // the head's representatives
+  int64_t k_st;
+  const int32_t* keys;  // the segment's key tokens (nk)
+  const int32_t* cands; // the bucket's candidate tokens (nc)
+  const int32_t* cgs;   // their groups (f == 0)
+  int nk, nc, f;
+  float tau, e;
+  fastar_diag_t* diag;
+  __device__ __forceinline__ const T* cand_row(int k, int i, int gr) const {
+    return f == 0 ? rk + (int64_t)gr * D : kp + (int64_t)i * k_st;
+  }
+  // candidate row by position in the bucket (for the float64 paths)
+  __device__ __forceinline__ const T* cand_row_at(int k) const {
+    return cand_row(k, cands[k], f == 0 ? cgs[k] : 0);
+  }
+};
+
+// Step 1 for keys k0 .. k0 + 15 of a segment (whole wave).  The lane with
+// (l & 15) < 4 reports key r = 4 (l >> 4) + (l & 3): jrep (its token, -1: no
+// such key), p (the candidate token it proposes to, -1: none) and c (the
+// cosine).  Candidates are visited in tiles of 16, the next tile's rows
+// loading while the current one is used; float32 decisions inside the error
+// bound are redone in float64.
+template <typename T, int D>
+__device__ __forceinline__ void match_keys(const SegCtx<T, D>& x, int k0, int& jrep, int& p,
+                                           float& c) {
+  using TD = TileDot<T, D>;
+  const int lane = lane_id();
+  const int g = lane >> 4, col = lane & 15;
+  const int jr = k0 + col < x.nk ? x.keys[k0 + col] : -1;  // this lane's key row
+  jrep = __shfl(jr, 4 * g + (col & 3), FASTAR_WAVE);
+  p = -1;
+  c = 0.f;
+  if (x.nc == 0) return;
+  const bool own = col < 4 && jrep >= 0;
+  // candidate ids of the first tile, with the key rows
+  bool cv = col < x.nc;
+  int ci = cv ? x.cands[col] : 0;
+  int cgi = (cv && x.f == 0) ? x.cgs[col] : 0;
+  TD td;
+  td.issue_keys(jr >= 0 ? x.kf + (int64_t)jr * x.k_st : nullptr);
+  typename TD::Rows cr = TD::issue(cv ? x.cand_row(col, ci, cgi) : nullptr);
+  td.finish_keys();
+  Top2<float> t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i].init();
+  for (int c0 = 0; c0 < x.nc; c0 += 16) {
+    // next tile's ids, then this tile's dots, then the next tile's rows
+    const bool nv = c0 + 16 + col < x.nc;
+    const int ni = nv ? x.cands[c0 + 16 + col] : 0;
+    const int ng = (nv && x.f == 0) ? x.cgs[c0 + 16 + col] : 0;
+    float sd[4], cn;
+    td.dots(cr, sd, cn);
+    if (cv) {
+      const float rc = cn > 0.f ? rsqrtf(cn) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i].add(td.kn[i] > 0.f ? sd[i] * rsqrtf(td.kn[i]) * rc : 0.f, ci);
+    }
+    if (c0 + 16 < x.nc) cr = TD::issue(nv ? x.cand_row(c0 + 16 + col, ni, ng) : nullptr);
+    cv = nv;
+    ci = ni;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    top2_merge_xor(t[i], 1);
+    top2_merge_xor(t[i], 2);
+    top2_merge_xor(t[i], 4);
+    top2_merge_xor(t[i], 8);
+  }
+  Top2<float> m = t[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if ((col & 3) == i) {
+      m.c1 = t[i].c1;
+      m.c2 = t[i].c2;
+      m.best = t[i].best;
+    }
+  bool prop = false, amb = false;
+  if (own) {
+    if (m.c1 < x.tau - x.e) prop = false;                                  // none reaches tau
+    else if (m.c1 >= x.tau + x.e && m.c1 - m.c2 > 2.f * x.e) prop = true;  // clear winner
+    else amb = true;
+  }
+  int best = m.best;
+  float c1 = m.c1;
+  // float64 for the keys float32 cannot decide, one key at a time
+  const double e64 = cos_err64<D>();
+  uint64_t ab = ballot64(amb);
+  while (ab) {
+    const int src = __builtin_ctzll(ab);
+    ab &= ab - 1;
+    const int js = __shfl(jrep, src, FASTAR_WAVE);
+    Top2<double> u;
+    u.init();
+    for (int k = 0; k < x.nc; ++k)
+      u.add(wave_cos64<T, D>(x.kf + (int64_t)js * x.k_st, x.cand_row_at(k)), x.cands[k]);
+    if (lane == src) {
+      if (x.diag) atomicAdd(&x.diag->merge_fallbacks, 1u);
+      const bool sure = (u.c1 < (double)x.tau - e64) ||
+                        (u.c1 >= (double)x.tau + e64 && u.c1 - u.c2 > 2.0 * e64);
+      if (!sure && x.diag) atomicAdd(&x.diag->unresolved, 1u);
+      best = u.best;
+      prop = u.c1 >= (double)x.tau;
+      c1 = (float)u.c1;
+    }
+  }
+  if (own) {
+    p = prop ? best : -1;
+    c = c1;
+  }
+}
+
+// Step 2 for the keys this wave holds (one per lane; p < 0: no proposal):
+// does the key win its candidate against every other proposer of the
+// segment?  other(q, p2, c2, j2) gives segment key q's proposal; self is the
+// lane's own position (skipped).  Float32 near-ties are redone in float64.
+// Returns whether it wins.
+template <typename T, int D, typename Other>
+__device__ __forceinline__ bool resolve_keys(const SegCtx<T, D>& x, int self, int p, float c, int j,
+                                             Other other, const int32_t* fr) {
+  const int lane = lane_id();
+  bool win = p >= 0, amb = false;
+  for (int q2 = 0; q2 < x.nk; ++q2) {
+    int p2, j2;
+    float c2;
+    other(q2, p2, c2, j2);
+    if (q2 == self || p2 != p || p < 0) continue;
+    if (c2 > c + 2.f * x.e) win = false;
+    else if (c2 >= c - 2.f * x.e) amb = true;
+  }
+  const double e64 = cos_err64<D>();
+  uint64_t nb = ballot64(win && amb);
+  while (nb) {
+    const int src = __builtin_ctzll(nb);
+    nb &= nb - 1;
+    const int ps = __shfl(p, src, FASTAR_WAVE);
+    const int js = __shfl(j, src, FASTAR_WAVE);
+    const int qs = __shfl(self, src, FASTAR_WAVE);
+    const T* prev = x.f == 0 ? x.rk + (int64_t)fr[ps] * D : x.kp + (int64_t)ps * x.k_st;
+    const double dj = wave_cos64<T, D>(x.kf + (int64_t)js * x.k_st, prev);
+    bool w = true, unres = false;
+    for (int q2 = 0; q2 < x.nk; ++q2) {
+      int p2, j2;
+      float c2;
+      other(q2, p2, c2, j2);
+      if (q2 == qs || p2 != ps) continue;
+      const double dd = wave_cos64<T, D>(x.kf + (int64_t)j2 * x.k_st, prev);
+      if (fabs(dd - dj) <= 2.0 * e64) unres = true;
+      if (dd > dj || (dd == dj && j2 < js)) w = false;
+    }
+    if (lane == src) {
+      if (x.diag) atomicAdd(&x.diag->merge_fallbacks, 1u);
+      if (unres && x.diag) atomicAdd(&x.diag->unresolved, 1u);
+      win = w;
+    }
+  }
+  return win;
+}
+
+// segments a workgroup takes per round
+constexpr int kSegBatch = 64;
+
+// Workgroup b of (frame f, head h) takes the segments s = b, b + gridDim.x, ..
+// of new frame f, kSegBatch at a time, and its waves share their tiles of
+// kKeyTile keys.  Step 1 (per tile) finds each key's best candidate and its
+// proposal.  Step 2 lets every candidate keep its best proposer (ties:
+// smaller j), which links to it; the other keys of the segment open groups.
+// A one-tile segment does step 2 in registers; in a larger one every tile
+// leaves its proposals in LDS, and the wave that completes the segment's
+// last tile does step 2 for all of it.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void tc_match_kernel(
+    const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
+    const int32_t* __restrict__ frontier, const int32_t* __restrict__ n_groups, float tau,
+    MergeArgs a, fastar_diag_t* __restrict__ diag) {
+  extern __shared__ int32_t lds[];  // [3][Tf] proposals of multi-tile segments
+  __shared__ int4 brec[kSegBatch];
+  __shared__ int btile[kSegBatch + 1], bkey[kSegBatch + 1], bdone[kSegBatch];
+  const int h = blockIdx.y;
+  const int f = blockIdx.z;
+  const int lane = lane_id();
+  const int col = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t fo = frame_off(a, h, f);
+  const int nseg = a.nseg[(int64_t)h * a.F + f];
+  const int4* srec = a.srec + fo;
+  const bool have_c = f > 0 || n_groups[h] > 0;
+  const uint32_t mask = (uint32_t)a.tsize - 1u;
+  const int4* ctab = a.tab + tab_off(a, h, f);
+  const int32_t* fr = frontier + (int64_t)h * a.Tf;
+  int32_t* lp = lds;
+  float* lc = reinterpret_cast<float*>(lds + a.Tf);
+  int32_t* lj = lds + 2 * a.Tf;
+  SegCtx<T, D> x;
+  x.kf = knew + (int64_t)h * k_sh + (int64_t)f * a.Tf * k_st;
+  x.kp = f > 0 ? x.kf - (int64_t)a.Tf * k_st : x.kf;
+  x.rk = rep_k + (int64_t)h * a.cap * D;
+  x.k_st = k_st;
+  x.f = f;
+  x.tau = tau;
+  x.e = match_err<T, D>();
+  x.diag = diag;
+  const int32_t* kcand = a.cand + cand_off(a, h, f + 1);
+  const int32_t* ccand = a.cand + cand_off(a, h, f);
+  const int32_t* cgh = a.candg + (int64_t)h * a.Tf;
+  auto write = [&](int j, int p, bool win) {
+    int lk = -1;
+    if (win) {
+      lk = f == 0 ? fr[p] : p;
+      if (f > 0) a.nextj[frame_off(a, h, f - 1) + p] = j;
+    }
+    a.link[fo + j] = lk;
+  };
+  const int stride = (int)gridDim.x;
+  for (int k0b = 0; blockIdx.x + k0b * stride < nseg; k0b += kSegBatch) {
+    // the batch: its segments, tile and key offsets (wave 0)
+    if (wave == 0) {
+      const int sidx = blockIdx.x + (k0b + lane) * stride;
+      int4 r = make_int4(0, 0, 0, 0);
+      if (lane < kSegBatch && sidx < nseg) r = srec[sidx];
+      int nt = (r.z + kKeyTile - 1) / kKeyTile, nk = r.z;
+#pragma unroll
+      for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
+        const int t = __shfl_up(nt, o, FASTAR_WAVE);
+        const int k = __shfl_up(nk, o, FASTAR_WAVE);
+        if (lane >= o) {
+          nt += t;
+          nk += k;
+        }
+      }
+      if (lane < kSegBatch) {
+        brec[lane] = r;
+        btile[lane + 1] = nt;
+        bkey[lane + 1] = nk;
+        bdone[lane] = 0;
+      }
+      if (lane == 0) {
+        btile[0] = 0;
+        bkey[0] = 0;
+      }
+    }
+    __syncthreads();
+    const int ntiles = btile[kSegBatch];
+    for (int tt = wave; tt < ntiles; tt += 4) {
+      int sb = 0;  // the batch segment holding tile tt
+      while (btile[sb + 1] <= tt) ++sb;
+      const int4 rec = brec[sb];
+      x.keys = kcand + rec.y;
+      x.nk = rec.z;
+      x.nc = 0;
+      x.cands = ccand;
+      x.cgs = cgh;
+      if (have_c) {
+        // the bucket's candidate segment
+        uint32_t sl = slot_hash(rec.x, mask);
+        int4 tb;
+        while ((tb = ctab[sl]).x != 0 && tb.x != rec.x + 1) sl = (sl + 1u) & mask;
+        if (tb.x != 0) {
+          x.cands = ccand + tb.y;
+          x.cgs = cgh + tb.y;
+          x.nc = tb.z;
+        }
+      }
+      int jrep, p;
+      float c;
+      const int k0 = (tt - btile[sb]) * kKeyTile;
+      match_keys<T, D>(x, k0, jrep, p, c);
+      if (x.nk <= kKeyTile) {
+        // key q is reported by lane 16 (q >> 2) + (q & 3)
+        const int self = col < 4 ? 4 * (lane >> 4) + col : -1;
+        const bool win = resolve_keys<T, D>(
+            x, self, col < 4 ? p : -1, c, jrep,
+            [&](int q2, int& p2, float& c2, int& j2) {
+              const int src = 16 * (q2 >> 2) + (q2 & 3);
+              p2 = __shfl(p, src, FASTAR_WAVE);
+              c2 = __shfl(c, src, FASTAR_WAVE);
+              j2 = __shfl(jrep, src, FASTAR_WAVE);
+            },
+            fr);
+        if (col < 4 && jrep >= 0) write(jrep, p, win);
+        continue;
+      }
+      const int kb = bkey[sb];
+      if (col < 4 && jrep >= 0) {
+        const int q = k0 + 4 * (lane >> 4) + col;
+        lp[kb + q] = p;
+        lc[kb + q] = c;
+        lj[kb + q] = jrep;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      int done = 0;
+      if (lane == 0) done = atomicAdd(&bdone[sb], 1);
+      done = __shfl(done, 0, FASTAR_WAVE);
+      if (done != btile[sb + 1] - btile[sb] - 1) continue;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // the segment's last tile: step 2 for all of it
+      for (int q0 = 0; q0 < x.nk; q0 += FASTAR_WAVE) {
+        const int q = q0 + lane;
+        const bool v = q < x.nk;
+        const int pj = v ? lp[kb + q] : -1;
+        const float cj = v ? lc[kb + q] : 0.f;
+        const int j = v ? lj[kb + q] : -1;
+        const bool win = resolve_keys<T, D>(
+            x, q, pj, cj, j,
+            [&](int q2, int& p2, float& c2, int& j2) {
+              p2 = lp[kb + q2];
+              c2 = lc[kb + q2];
+              j2 = lj[kb + q2];
+            },
+            fr);
+        if (v) write(j, pj, win);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup per head: the tokens that open groups, in (frame, j) order,
+// get the next group ids; ids from the capacity on are dropped (-1).
+__global__ __launch_bounds__(1024) void tc_number_kernel(int32_t* __restrict__ n_groups,
+                                                         MergeArgs a) {
   __shared__ int wsum[16];
   __shared__ int running;
   const int h = blockIdx.x;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = lane_id();
-  const float e = cos_err32<D>();
-  const double e64 = cos_err64<D>();
-  int ng = n_groups[h];
-  const T* kh = knew + (int64_t)h * k_sh;
-  for (int f = 0; f < a.F; ++f) {
-    const int64_t fo = frame_off(a, h, f);
-    for (int i = tid; i < Tf; i += blockDim.x) {
-      plist[i] = -1;
-      tg[i] = (int16_t)a.target[fo + i];
-      tcl[i] = a.tcos[fo + i];
-      a.nextj[fo + i] = -1;
-    }
-    if (tid == 0) running = 0;
+  const int nw = (int)(blockDim.x >> 6);
+  const int ng0 = n_groups[h];
+  const int total = a.F * a.Tf;
+  const int32_t* lk = a.link + frame_off(a, h, 0);
+  int32_t* gd = a.gid + frame_off(a, h, 0);
+  if (tid == 0) running = 0;
+  __syncthreads();
+  for (int base = 0; base < total; base += blockDim.x) {
+    const int idx = base + tid;
+    const bool isnew = idx < total && lk[idx] < 0;
+    const uint64_t bal = ballot64(isnew);
+    if (lane == 0) wsum[wave] = __popcll(bal);
     __syncthreads();
-    for (int j = tid; j < Tf; j += blockDim.x) {
-      const int i = tg[j];
-      if (i >= 0) nxt[j] = (int16_t)atomicExch(&plist[i], j);
+    int rank = running + __popcll(bal & lanemask_lt());
+    for (int w = 0; w < wave; ++w) rank += wsum[w];
+    if (isnew) {
+      const int64_t gg = (int64_t)ng0 + rank;
+      gd[idx] = gg < a.cap ? (int32_t)gg : -1;
     }
     __syncthreads();
-    for (int j = tid; j < Tf; j += blockDim.x) {
-      const int i = tg[j];
-      bool win = i >= 0;
-      if (win) {
-        const float cj = tcl[j];
-        bool amb = false;
-        for (int j2 = plist[i]; j2 >= 0; j2 = nxt[j2]) {
-          if (j2 == j) continue;
-          const float c = tcl[j2];
-          if (c > cj + 2.f * e) win = false;
-          else if (c >= cj - 2.f * e) amb = true;
-        }
-        if (win && amb) {
-          if (diag) atomicAdd(&diag->merge_fallbacks, 1u);
-          const T* prev = f == 0 ? rep_k + ((int64_t)h * a.cap + frontier[(int64_t)h * Tf + i]) * D
-                                 : kh + ((int64_t)(f - 1) * Tf + i) * k_st;
-          const double dj = cos64<T, D>(kh + ((int64_t)f * Tf + j) * k_st, prev);
-          bool unres = false;
-          for (int j2 = plist[i]; j2 >= 0; j2 = nxt[j2]) {
-            if (j2 == j) continue;
-            const double dd = cos64<T, D>(kh + ((int64_t)f * Tf + j2) * k_st, prev);
-            if (fabs(dd - dj) <= 2.0 * e64) unres = true;
-            if (dd > dj || (dd == dj && j2 < j)) win = false;
-          }
-          if (unres && diag) atomicAdd(&diag->unresolved, 1u);
-        }
-      }
-      int mg = -1;
-      if (win) {
-        // the candidate's group; a token dropped for capacity has none
-        mg = f == 0 ? frontier[(int64_t)h * Tf + i] : a.gid[frame_off(a, h, f - 1) + i];
-        if (mg >= 0 && f > 0) a.nextj[frame_off(a, h, f - 1) + i] = j;
-      }
-      a.mgroup[fo + j] = mg;
+    if (tid == 0) {
+      int sum = 0;
+      for (int w = 0; w < nw; ++w) sum += wsum[w];
+      running += sum;
     }
-    __threadfence_block();
-    __syncthreads();
-    // number the new groups in ascending j
-    for (int base = 0; base < Tf; base += blockDim.x) {
-      const int j = base + tid;
-      const int mg = j < Tf ? a.mgroup[fo + j] : 0;
-      const bool isnew = j < Tf && mg < 0;
-      const uint64_t bal = ballot64(isnew);
-      if (lane == 0) wsum[wave] = __popcll(bal);
-      __syncthreads();
-      int rank = running + __popcll(bal & lanemask_lt());
-      for (int w = 0; w < wave; ++w) rank += wsum[w];
-      if (j < Tf) {
-        int g = isnew ? ng + rank : mg;
-        if (isnew && g >= a.cap) {
-          g = -1;
-          if (diag) atomicAdd(&diag->capacity_overflow, 1u);
-        }
-        a.gid[fo + j] = g;
-        if (group_of_new) group_of_new[(int64_t)h * a.kb_stride + (int64_t)f * Tf + j] = g;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int sum = 0;
-        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) sum += wsum[w];
-        running += sum;
-      }
-      __syncthreads();
-    }
-    ng = ng + running < a.cap ? ng + running : a.cap;
-    __threadfence_block();
     __syncthreads();
   }
-  for (int j = tid; j < Tf; j += blockDim.x) frontier[(int64_t)h * Tf + j] = a.gid[frame_off(a, h, a.F - 1) + j];
-  if (tid == 0) n_groups[h] = ng;
+  if (tid == 0) {
+    const int64_t ng = (int64_t)ng0 + running;
+    n_groups[h] = ng < a.cap ? (int32_t)ng : a.cap;
+  }
 }
 
-// Group rows, 16 lanes per group touched by the chunk (D/16 elements each).
-// A chain starts at a token that opens a new group, or at a frame-0 token that
-// extends an existing group; it follows nextj through the later frames.  Value
-// sums are accumulated frame by frame in float32, exactly as merging the
-// frames one at a time would; the representative is the chain's last key.
+// Group rows, 16 lanes per chain (D/16 elements each).  A chain starts at a
+// token that opens a group, or at a frame-0 token that extends a frontier
+// group; it follows nextj through the later frames.  Value sums are
+// accumulated frame by frame in float32, exactly as merging the frames one at
+// a time would; the representative is the chain's last key.  Every member's
+// group goes to group_of_new, last-frame members' to the frontier.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tc_apply_kernel(
     T* __restrict__ rep_k, T* __restrict__ v_mean, float* __restrict__ v_sum,
     int32_t* __restrict__ count, float* __restrict__ log_count, int32_t* __restrict__ rep_bucket,
+    int32_t* __restrict__ frontier, int32_t* __restrict__ group_of_new,
     const T* __restrict__ knew, int64_t k_sh, int64_t k_st, const T* __restrict__ vnew,
-    int64_t v_sh, int64_t v_st, const int32_t* __restrict__ kbucket, MergeArgs a) {
+    int64_t v_sh, int64_t v_st, const int32_t* __restrict__ kbucket, MergeArgs a,
+    fastar_diag_t* __restrict__ diag) {
   constexpr int EPL = D / 16;
   const int h = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -545,17 +816,34 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   if (idx >= (int64_t)a.F * a.Tf) return;
   int f = (int)(idx / a.Tf);
   int j = (int)(idx - (int64_t)f * a.Tf);
-  const int g = a.gid[frame_off(a, h, f) + j];
-  if (g < 0) return;
-  const int mg = a.mgroup[frame_off(a, h, f) + j];
-  if (mg >= 0 && f > 0) return;  // continuation of a chain that starts earlier
+  const int lk = a.link[frame_off(a, h, f) + j];
+  if (lk >= 0 && f > 0) return;  // continuation of a chain that starts earlier
+  const int g = lk < 0 ? a.gid[frame_off(a, h, f) + j] : lk;
+  auto member = [&](int ff, int jj) {
+    if (sub != 0) return;
+    if (group_of_new) group_of_new[(int64_t)h * a.kb_stride + (int64_t)ff * a.Tf + jj] = g;
+    if (ff == a.F - 1) frontier[(int64_t)h * a.Tf + jj] = g;
+    if (g < 0 && diag) atomicAdd(&diag->capacity_overflow, 1u);
+  };
+  member(f, j);
+  if (g < 0) {
+    // no room: the whole chain is left out
+    while (f + 1 < a.F) {
+      const int nx = a.nextj[frame_off(a, h, f) + j];
+      if (nx < 0) break;
+      ++f;
+      j = nx;
+      member(f, j);
+    }
+    return;
+  }
   const int64_t gi = (int64_t)h * a.cap + g;
   float sum[EPL];
   int cnt;
   {
     float vv[EPL];
     Chunk<T, EPL>::load(vnew + (int64_t)h * v_sh + ((int64_t)f * a.Tf + j) * v_st + sub * EPL, vv);
-    if (mg < 0) {
+    if (lk < 0) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) sum[e] = vv[e];
       cnt = 1;
@@ -571,6 +859,7 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
     if (nx < 0) break;
     ++f;
     j = nx;
+    member(f, j);
     float vv[EPL];
     Chunk<T, EPL>::load(vnew + (int64_t)h * v_sh + ((int64_t)f * a.Tf + j) * v_st + sub * EPL, vv);
 #pragma unroll
@@ -614,30 +903,29 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   a.F = F;
   a.tsize = table_size(Tf);
   a.kb_stride = (int64_t)F * Tf;
-  a.tkey = ws.tkey;
-  a.tstart = ws.tstart;
-  a.tcount = ws.tcount;
+  a.tab = ws.tab;
   a.cand = ws.cand;
   a.candg = ws.candg;
-  a.target = ws.target;
-  a.tcos = ws.tcos;
-  a.mgroup = ws.mgroup;
+  a.srec = ws.srec;
+  a.nseg = ws.nseg;
+  a.link = ws.link;
   a.gid = ws.gid;
   a.nextj = ws.nextj;
   const size_t index_lds = (size_t)2 * a.tsize * sizeof(int32_t) + (size_t)2 * Tf * sizeof(int16_t);
-  const size_t resolve_lds = (size_t)Tf * (2 * sizeof(int32_t) + 2 * sizeof(int16_t));
   hipLaunchKernelGGL(tc_index_kernel, dim3(F + 1, H), dim3(1024), index_lds, s, c.frontier,
                      c.rep_bucket, c.n_groups, kb, a);
-  hipLaunchKernelGGL((tc_match_kernel<T, D>), dim3((unsigned)((Tf + 15) / 16), (unsigned)H, F),
-                     dim3(256), 0, s, (const T*)c.rep_k, (const T*)kn.data, kn.stride_head,
-                     kn.stride_token, kb, c.n_groups, tau, a, diag);
-  hipLaunchKernelGGL((tc_resolve_kernel<T, D>), dim3(H), dim3(1024), resolve_lds, s,
-                     (const T*)c.rep_k, c.frontier, c.n_groups, (const T*)kn.data, kn.stride_head,
-                     kn.stride_token, group_of_new, a, diag);
+  // up to 256 waves per (frame, head), each looping over that frame's segments
+  const unsigned mx = (unsigned)std::min(64, (Tf + 3) / 4);
+  hipLaunchKernelGGL((tc_match_kernel<T, D>), dim3(mx, (unsigned)H, (unsigned)F), dim3(256),
+                     (size_t)3 * Tf * sizeof(int32_t), s,
+                     (const T*)c.rep_k, (const T*)kn.data, kn.stride_head, kn.stride_token,
+                     c.frontier, c.n_groups, tau, a, diag);
+  hipLaunchKernelGGL(tc_number_kernel, dim3(H), dim3(1024), 0, s, c.n_groups, a);
   hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)F * Tf + 15) / 16), (unsigned)H),
                      dim3(256), 0, s, (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count,
-                     c.rep_bucket, (const T*)kn.data, kn.stride_head, kn.stride_token,
-                     (const T*)vn.data, vn.stride_head, vn.stride_token, kb, a);
+                     c.rep_bucket, c.frontier, group_of_new, (const T*)kn.data, kn.stride_head,
+                     kn.stride_token, (const T*)vn.data, vn.stride_head, vn.stride_token, kb, a,
+                     diag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (rep_offsets && rep_perm)
