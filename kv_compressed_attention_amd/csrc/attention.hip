@@ -31,6 +31,8 @@ namespace fastar {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt immediate: vector memory count 0, the other counters unconstrained
+constexpr int kWaitVm0 = 0x0F70;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <int NB>
@@ -62,7 +64,7 @@ __device__ __forceinline__ int wave_min_i(int v) {
 
 // MODE: 0 bucket, 1 key list, 2 dense
 template <int D, int P, int MODE>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(
+__global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_sh, int64_t q_st, int64_t Nq,
     const int32_t* __restrict__ q_bucket, const int32_t* __restrict__ q_perm,
     const uint16_t* __restrict__ k, int64_t k_sh, int64_t k_st,
@@ -73,11 +75,17 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
     float* __restrict__ lse) {
   constexpr int NC = D / 32;  // k-chunks of the QK^T contraction
   constexpr int NB = D / 16;  // 16-dim output blocks
+  // rows of the V chunk one 16-byte-per-lane LDS load fills
+  constexpr int kVRows = 64 * 16 / (2 * D);
+  __shared__ __attribute__((aligned(16))) uint16_t vlds[4][32 * D];
+  __shared__ __attribute__((aligned(16))) float blds[4][32];
   const int h = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
+  uint16_t* vbuf = vlds[wave];
+  float* bbuf = blds[wave];
   const int64_t r0 = (int64_t)blockIdx.x * 64 + wave * 16;
   if (r0 >= Nq) return;
   const int64_t r = r0 + col;
@@ -109,116 +117,171 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(
   if (MODE == 0) idx_h = k_perm + (int64_t)h * Nk;
   if (MODE == 1) idx_h = key_list + (int64_t)h * Nk;
 
+  // passes: the distinct buckets of the wave's rows in ascending order (MODE
+  // 0; lane i holds pass i's bucket and key range), or one pass over the list
+  // or all keys.  Every pass's key range is loaded at once.
   int b0 = INT_MAX, b1 = INT_MAX;
   if (MODE == 0 && rvalid) {
     const int32_t* qb = q_bucket + ((int64_t)h * Nq + t) * P;
     b0 = qb[0];
     if (P == 2) b1 = qb[1];
   }
-  bool first_pass = true;
-  while (true) {
-    int64_t kbeg, kend;
-    bool rowin;
-    if (MODE == 0) {
-      const int X = wave_min_i(min(b0, b1));
+  int npass = 0, xs = INT_MAX, pkb = 0, pke = 0;
+  if (MODE == 0) {
+    int c0 = b0, c1 = b1;
+    while (true) {
+      const int X = wave_min_i(min(c0, c1));
       if (X == INT_MAX) break;
-      rowin = (b0 == X) || (b1 == X);
-      if (b0 == X) b0 = INT_MAX;
-      if (b1 == X) b1 = INT_MAX;
-      const int32_t* off = k_offsets + (int64_t)h * ((1 << nbits) + 1) + X;
-      kbeg = off[0];
-      kend = off[1];
-    } else {
-      if (!first_pass) break;
-      kbeg = 0;
-      kend = Nk;
-      if (MODE == 1) {
-        const int64_t nl = n_key_list[h];
-        kend = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
-      }
-      rowin = rvalid;
+      if (l == npass) xs = X;
+      if (c0 == X) c0 = INT_MAX;
+      if (c1 == X) c1 = INT_MAX;
+      ++npass;
     }
-    first_pass = false;
-    for (int64_t kc = kbeg; kc < kend; kc += 32) {
-      // key of slot `col` in each 16-key half (clamped to a valid key)
-      int kid[2];
+    if (l < npass) {
+      const int32_t* off = k_offsets + (int64_t)h * ((1 << nbits) + 1) + xs;
+      pkb = off[0];
+      pke = off[1];
+    }
+  } else {
+    npass = 1;
+    int64_t ke = Nk;
+    if (MODE == 1) {
+      const int64_t nl = n_key_list[h];
+      ke = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
+    }
+    pke = (int)ke;
+  }
+  // p is wave-uniform: read the pass's values straight into scalars
+  auto pass_beg = [&](int p) { return __builtin_amdgcn_readlane(pkb, p); };
+  auto pass_end = [&](int p) { return __builtin_amdgcn_readlane(pke, p); };
+  // first chunk of pass p or later (p == npass: done)
+  auto first_chunk = [&](int& p, int& kc) {
+    while (p < npass) {
+      kc = pass_beg(p);
+      if (kc < pass_end(p)) return;
+      ++p;
+    }
+  };
+  // key of slot `col` in each 16-key half of chunk (p, kc), clamped into the pass
+  auto chunk_ids = [&](int p, int kc, int* kid) {
+    const int kb = pass_beg(p), ke = pass_end(p);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        int64_t kk = kc + 16 * hf + col;
-        if (kk >= kend) kk = kbeg;
-        kid[hf] = (MODE == 2) ? (int)kk : idx_h[kk];
+    for (int hf = 0; hf < 2; ++hf) {
+      int kk = kc + 16 * hf + col;
+      if (kk >= ke) kk = kb;
+      kid[hf] = (MODE == 2) ? kk : idx_h[kk];
+    }
+  };
+  int p = 0, kc = 0;
+  first_chunk(p, kc);
+  int kid[2] = {0, 0};
+  if (p < npass) chunk_ids(p, kc, kid);
+  while (p < npass) {
+    // the next chunk's key ids load while this chunk's rows are in flight
+    int pn = p, kn = kc + 32;
+    if (kn >= pass_end(pn)) {
+      ++pn;
+      first_chunk(pn, kn);
+    }
+    int kid_next[2] = {0, 0};
+    if (pn < npass) chunk_ids(pn, kn, kid_next);
+    const int kend = pass_end(p);
+    bool rowin = rvalid;
+    if (MODE == 0) {
+      const int X = __builtin_amdgcn_readlane(xs, p);
+      rowin = (b0 == X) || (b1 == X);
+    }
+    // the chunk's 32 V rows go straight to the wave's LDS buffer (slot j of
+    // the chunk at row j), issued with the K gathers; V does not depend on
+    // the scores, and no registers hold it until the PV product
+#pragma unroll
+    for (int i = 0; i < 32 / kVRows; ++i) {
+      const int slot = kVRows * i + l / (64 / kVRows);
+      const int key = __shfl(kid[(kVRows * i) >> 4], slot & 15, FASTAR_WAVE);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(vh + (int64_t)key * v_st + (l % (64 / kVRows)) * 8),
+          (__attribute__((address_space(3))) void*)(vbuf + kVRows * i * D), 16, 0, 0);
+    }
+    // and the 32 biases (lane j < 32: chunk row j's)
+    if (bh && l < 32)
+      __builtin_amdgcn_global_load_lds((const void*)(bh + kid[l >> 4]), (__attribute__((address_space(3))) void*)bbuf, 4, 0, 0);
+    uint4 kraw[2][NC];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint16_t* krow = kh + (int64_t)kid[hf] * k_st;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kraw[hf][c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * g);
+    }
+    // the MFMAs below wait for the K rows, which were issued after the V rows
+    // and biases: every row load of the chunk has landed after this wait
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __asm__ volatile("" ::: "memory");
+    float s[8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      // slot 4 hf + i <-> chunk row 16 hf + 4 g + i
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bh) {
+        const float4 b4 = *reinterpret_cast<const float4*>(bbuf + 16 * hf + 4 * g);
+        bias[0] = b4.x * kLog2e;
+        bias[1] = b4.y * kLog2e;
+        bias[2] = b4.z * kLog2e;
+        bias[3] = b4.w * kLog2e;
       }
-      // key ids of the 8 slots this lane scores / feeds to PV:
-      // slot 4*hf + i <-> key 16*hf + 4*g + i of the chunk
-      int sk[8];
+      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sk[4 * hf + i] = __shfl(kid[hf], 4 * g + i, FASTAR_WAVE);
-      // issue the K and V gathers together; V does not depend on the scores
-      uint4 kraw[2][NC];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const uint16_t* krow = kh + (int64_t)kid[hf] * k_st;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) kraw[hf][c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * g);
-      }
-      VRow<NB> vr[8];
-#pragma unroll
-      for (int si = 0; si < 8; ++si) vr[si].load(vh + (int64_t)sk[si] * v_st + NB * col);
-      float bias[8];
-#pragma unroll
-      for (int si = 0; si < 8; ++si) bias[si] = bh ? bh[sk[si]] * kLog2e : 0.f;
-      float s[8];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kraw[hf][c]), qop[c], sacc, 0, 0, 0);
-        // sacc[i] = score(key slot 16hf + 4g + i, row col)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool kvalid = kc + 16 * hf + 4 * g + i < kend;
-          s[4 * hf + i] = (kvalid && rowin) ? sacc[i] * scale_log2 + bias[4 * hf + i] : -INFINITY;
-        }
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float mnew = fmaxf(m, mx);
-      const float base = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = exp2f(m - base);
-      m = mnew;
-      uint32_t pw[4];
-      float psum = 0.f;
+      for (int c = 0; c < NC; ++c)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kraw[hf][c]), qop[c], sacc, 0, 0, 0);
+      // sacc[i] = score(key slot 16hf + 4g + i, row col)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = f32_to_bf16_bits(exp2f(s[2 * i] - base));
-        const uint32_t hi = f32_to_bf16_bits(exp2f(s[2 * i + 1] - base));
-        psum += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
-        pw[i] = lo | (hi << 16);
-      }
-      lsum = lsum * alpha + psum;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        acc[b][0] *= alpha;
-        acc[b][1] *= alpha;
-        acc[b][2] *= alpha;
-        acc[b][3] *= alpha;
-      }
-      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      // V^T operand: lane (dim-row col, group g), slot si <-> key sk[si],
-      // dims NB*col .. NB*col + NB - 1 (one per output block), loaded above
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const uint4 w = make_uint4(vr[0].get(b) | (vr[1].get(b) << 16), vr[2].get(b) | (vr[3].get(b) << 16),
-                                   vr[4].get(b) | (vr[5].get(b) << 16), vr[6].get(b) | (vr[7].get(b) << 16));
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[b], 0, 0, 0);
+        const bool kvalid = kc + 16 * hf + 4 * g + i < kend;
+        s[4 * hf + i] = (kvalid && rowin) ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
       }
     }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float base = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = exp2f(m - base);
+    m = mnew;
+    uint32_t pw[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = f32_to_bf16_bits(exp2f(s[2 * i] - base));
+      const uint32_t hi = f32_to_bf16_bits(exp2f(s[2 * i + 1] - base));
+      psum += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
+      pw[i] = lo | (hi << 16);
+    }
+    lsum = lsum * alpha + psum;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      acc[b][0] *= alpha;
+      acc[b][1] *= alpha;
+      acc[b][2] *= alpha;
+      acc[b][3] *= alpha;
+    }
+    const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    // V^T operand: lane (dim-row col, group g), slot si <-> chunk row
+    // 16 (si >> 2) + 4g + (si & 3), dims NB*col .. NB*col + NB - 1 (one per
+    // output block), read back from LDS
+    VRow<NB> vr[8];
+#pragma unroll
+    for (int si = 0; si < 8; ++si) vr[si].load(vbuf + (16 * (si >> 2) + 4 * g + (si & 3)) * D + NB * col);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint4 w = make_uint4(vr[0].get(b) | (vr[1].get(b) << 16), vr[2].get(b) | (vr[3].get(b) << 16),
+                                 vr[4].get(b) | (vr[5].get(b) << 16), vr[6].get(b) | (vr[7].get(b) << 16));
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[b], 0, 0, 0);
+    }
+    p = pn;
+    kc = kn;
+    kid[0] = kid_next[0];
+    kid[1] = kid_next[1];
   }
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
