@@ -151,46 +151,40 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     }
     pke = (int)ke;
   }
-  // p is wave-uniform: read the pass's values straight into scalars
-  auto pass_beg = [&](int p) { return __builtin_amdgcn_readlane(pkb, p); };
-  auto pass_end = [&](int p) { return __builtin_amdgcn_readlane(pke, p); };
-  // first chunk of pass p or later (p == npass: done)
-  auto first_chunk = [&](int& p, int& kc) {
-    while (p < npass) {
-      kc = pass_beg(p);
-      if (kc < pass_end(p)) return;
-      ++p;
-    }
+  // the passes' key ranges, concatenated: pass p's keys are slots
+  // pre_p .. pre_p + len_p - 1 of the wave's key list
+  const int len = l < npass ? pke - pkb : 0;
+  int pre = len;
+#pragma unroll
+  for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
+    const int y = __shfl_up(pre, o, FASTAR_WAVE);
+    if (l >= o) pre += y;
+  }
+  const int total = __builtin_amdgcn_readlane(pre, FASTAR_WAVE - 1);
+  pre -= len;
+  // key and bucket of list slot j (j < total), for this lane
+  auto slot_key = [&](int j, int& key, int& bucket) {
+    int pj = 0;
+    for (int q2 = 1; q2 < npass; ++q2) pj += __builtin_amdgcn_readlane(pre, q2) <= j ? 1 : 0;
+    const int kk = __shfl(pkb, pj, FASTAR_WAVE) + j - __shfl(pre, pj, FASTAR_WAVE);
+    key = (MODE == 2) ? kk : idx_h[kk];
+    bucket = __shfl(xs, pj, FASTAR_WAVE);
   };
-  // key of slot `col` in each 16-key half of chunk (p, kc), clamped into the pass
-  auto chunk_ids = [&](int p, int kc, int* kid) {
-    const int kb = pass_beg(p), ke = pass_end(p);
+  // slot `col` of each 16-slot half of the chunk at c0 (past the end: slot 0)
+  auto chunk_ids = [&](int c0, int* kid, int* kb) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      int kk = kc + 16 * hf + col;
-      if (kk >= ke) kk = kb;
-      kid[hf] = (MODE == 2) ? kk : idx_h[kk];
+      int j = c0 + 16 * hf + col;
+      if (j >= total) j = 0;
+      slot_key(j, kid[hf], kb[hf]);
     }
   };
-  int p = 0, kc = 0;
-  first_chunk(p, kc);
-  int kid[2] = {0, 0};
-  if (p < npass) chunk_ids(p, kc, kid);
-  while (p < npass) {
+  int kid[2] = {0, 0}, kbk[2] = {0, 0};
+  if (total > 0) chunk_ids(0, kid, kbk);
+  for (int kc = 0; kc < total; kc += 32) {
     // the next chunk's key ids load while this chunk's rows are in flight
-    int pn = p, kn = kc + 32;
-    if (kn >= pass_end(pn)) {
-      ++pn;
-      first_chunk(pn, kn);
-    }
-    int kid_next[2] = {0, 0};
-    if (pn < npass) chunk_ids(pn, kn, kid_next);
-    const int kend = pass_end(p);
-    bool rowin = rvalid;
-    if (MODE == 0) {
-      const int X = __builtin_amdgcn_readlane(xs, p);
-      rowin = (b0 == X) || (b1 == X);
-    }
+    int kid_next[2] = {0, 0}, kbk_next[2] = {0, 0};
+    if (kc + 32 < total) chunk_ids(kc + 32, kid_next, kbk_next);
     // the chunk's 32 V rows go straight to the wave's LDS buffer (slot j of
     // the chunk at row j), issued with the K gathers; V does not depend on
     // the scores, and no registers hold it until the PV product
@@ -235,8 +229,11 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       // sacc[i] = score(key slot 16hf + 4g + i, row col)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool kvalid = kc + 16 * hf + 4 * g + i < kend;
-        s[4 * hf + i] = (kvalid && rowin) ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
+        // slot 4 hf + i is list slot kc + 16 hf + 4 g + i; its bucket:
+        const int sb = __shfl(kbk[hf], 4 * g + i, FASTAR_WAVE);
+        const bool kvalid = kc + 16 * hf + 4 * g + i < total;
+        const bool in = (MODE != 0) ? rvalid : (sb == b0 || sb == b1);
+        s[4 * hf + i] = (kvalid && in) ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
       }
     }
     float mx = s[0];
@@ -278,10 +275,10 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
                                  vr[4].get(b) | (vr[5].get(b) << 16), vr[6].get(b) | (vr[7].get(b) << 16));
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[b], 0, 0, 0);
     }
-    p = pn;
-    kc = kn;
     kid[0] = kid_next[0];
     kid[1] = kid_next[1];
+    kbk[0] = kbk_next[0];
+    kbk[1] = kbk_next[1];
   }
   lsum += shfl_xor_f(lsum, 16);
   lsum += shfl_xor_f(lsum, 32);
