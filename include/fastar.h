@@ -93,7 +93,8 @@ int fastar_version(void);
  *            token within a bucket; offsets[B] = number of tokens with
  *            bucket < B.  Two probes: each token once, sorted by (first
  *            bucket, flipped bit, token); offsets count first buckets.
- *   ws       device workspace of at least fastar_hash_workspace() bytes.
+ *   ws       device workspace of at least fastar_hash_workspace() bytes,
+ *            used by the index only (may be NULL when offsets is NULL).
  *   diag     optional device counters (may be NULL).
  * ---------------------------------------------------------------------- */
 size_t fastar_hash_workspace(int heads, int64_t n, int n_bits, int n_probes);

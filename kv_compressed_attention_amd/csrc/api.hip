@@ -84,8 +84,8 @@ size_t fastar_hash_workspace(int heads, int64_t n, int n_bits, int n_probes) {
   (void)n_bits;
   (void)n_probes;
   if (heads < 0 || n < 0) return 0;
-  const size_t hn = (size_t)heads * (size_t)n;
-  return align_up(4) + align_up(4 * hn) + align_up(16 * hn);
+  // the bucket index's scratch (hashing itself needs none)
+  return align_up(16 * (size_t)heads * (size_t)n);
 }
 
 fastar_status_t fastar_hash(const fastar_tensor_t* x, const void* planes, int n_bits, int n_probes,
@@ -111,18 +111,14 @@ fastar_status_t fastar_hash(const fastar_tensor_t* x, const void* planes, int n_
   if (n_bits > 0 && (!planes || !aligned16(planes)))
     return fail(FASTAR_ERR_INVALID, "planes must be a non-null, 16-byte aligned pointer");
   if (!bucket) return fail(FASTAR_ERR_INVALID, "bucket is NULL");
-  if (!ws || ws_bytes < fastar_hash_workspace(x->heads, x->tokens, n_bits, n_probes))
+  if (offsets && (!ws || ws_bytes < fastar_hash_workspace(x->heads, x->tokens, n_bits, n_probes)))
     return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu",
                 fastar_hash_workspace(x->heads, x->tokens, n_bits, n_probes), ws_bytes);
-  char* w = (char*)ws;
-  uint32_t* qcount = (uint32_t*)w;
-  uint32_t* queue = (uint32_t*)(w + align_up(4));
-  int32_t* idx_ws = (int32_t*)(w + align_up(4) + align_up(4 * (size_t)hn));
-  hipError_t e = fastar::launch_hash(*x, planes, n_bits, n_probes, bucket, queue, qcount, diag, stream);
+  hipError_t e = fastar::launch_hash(*x, planes, n_bits, n_probes, bucket, diag, stream);
   if (e != hipSuccess) return hip_status(e, "hash");
   if (offsets)
     return hip_status(fastar::launch_bucket_index(bucket, x->heads, x->tokens, n_probes, n_bits,
-                                                  nullptr, offsets, perm, idx_ws, stream),
+                                                  nullptr, offsets, perm, (int32_t*)ws, stream),
                       "bucket_index");
   return FASTAR_OK;
 }

@@ -12,9 +12,9 @@
 //
 // A float32 projection is trusted only when its magnitude exceeds an a-priori
 // bound on its rounding error, Kd * |x| * |r_j| with Kd = d * 2^-22 (four times
-// the worst case of a d-term float32 accumulation of exact products).  Rows with
-// any untrusted sign or second-probe choice are queued and re-evaluated by
-// hash_fixup_kernel in float64 (products of bf16/fp32 values are exact there),
+// the worst case of a d-term float32 accumulation of exact products).  A row
+// with any untrusted sign or second-probe choice is re-evaluated on the spot
+// by its whole wave in float64 (products of bf16/fp32 values are exact there),
 // and a sign float64 still cannot certify is settled exactly with an
 // error-free expansion sum.
 
@@ -62,17 +62,109 @@ __device__ __forceinline__ float kcert() {
   return (float)D * 0x1p-22f * (1.0f + 0x1p-10f);
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 1; m < FASTAR_WAVE; m <<= 1) v += __shfl_xor(v, m, FASTAR_WAVE);
+  return v;
+}
+
+// Re-evaluates one row in float64, the whole wave (each lane holds D/64
+// dims), and writes its ids; a sign float64 cannot certify is settled
+// exactly by lane 0 with an expansion sum in E (D + 2 doubles of LDS).
+template <typename T, int D, int P>
+__device__ void hash_fixup_row(const T* __restrict__ xr, const T* __restrict__ planes, int nb,
+                               int32_t* __restrict__ o, fastar_diag_t* __restrict__ diag,
+                               double* E) {
+  constexpr int L = D / FASTAR_WAVE;
+  const int lane = lane_id();
+  double xv[L];
+#pragma unroll
+  for (int k = 0; k < L; ++k) xv[k] = (double)Elem<T>::load(xr, lane + FASTAR_WAVE * k);
+  uint32_t bits = 0;
+  double dist[16], derr[16];
+  bool unresolved = false;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    dist[p] = 0.0;
+    derr[p] = 0.0;
+    if (p < nb) {
+      double s = 0.0, a = 0.0, n2 = 0.0;
+#pragma unroll
+      for (int k = 0; k < L; ++k) {
+        const double rv = (double)Elem<T>::load(planes, (int64_t)p * D + lane + FASTAR_WAVE * k);
+        const double pr = xv[k] * rv;  // exact: at most 48 significant bits
+        s += pr;
+        a += fabs(pr);
+        n2 += rv * rv;
+      }
+      s = wave_sum_d(s);
+      a = wave_sum_d(a);
+      n2 = wave_sum_d(n2);
+      const double bound = 2.0 * (D + 8) * 0x1p-53 * a;
+      int sg;
+      if (fabs(s) > bound) {
+        sg = s > 0.0 ? 1 : -1;
+      } else if (a == 0.0) {
+        sg = 0;
+      } else {
+        int sg0 = 0;
+        if (lane == 0) {
+          int m = 0;
+          for (int d = 0; d < D; ++d) {
+            const double xd = (double)Elem<T>::load(xr, d);
+            const double rd = (double)Elem<T>::load(planes, (int64_t)p * D + d);
+            m = grow_expansion(E, m, xd * rd);
+          }
+          sg0 = expansion_sign(E, m);
+          if (diag) atomicAdd(&diag->hash_exact_signs, 1u);
+        }
+        sg = __shfl(sg0, 0, FASTAR_WAVE);
+      }
+      if (sg > 0) bits |= 1u << p;
+      if (P == 2) {
+        const double rn = sqrt(n2);
+        dist[p] = rn > 0.0 ? fabs(s) / rn : 0.0;
+        derr[p] = (a == 0.0) ? 0.0 : (rn > 0.0 ? bound / rn : 0.0) + dist[p] * (2 * D + 8) * 0x1p-53;
+      }
+    }
+  }
+  int j1 = 0;
+  if (P == 2) {
+    double d1 = dist[0], e1 = derr[0];
+#pragma unroll
+    for (int p = 1; p < 16; ++p) {
+      if (p < nb && dist[p] < d1) {
+        j1 = p;
+        d1 = dist[p];
+        e1 = derr[p];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      if (p < nb && p != j1) {
+        const double gap = dist[p] - d1;
+        const double err = derr[p] + e1;
+        if (err > 0.0 && gap <= err) unresolved = true;
+      }
+    }
+  }
+  if (lane == 0) {
+    o[0] = (int32_t)bits;
+    if (P == 2) o[1] = (int32_t)(bits ^ (1u << j1));
+    if (diag) {
+      atomicAdd(&diag->hash_fallback_rows, 1u);
+      if (unresolved) atomicAdd(&diag->unresolved, 1u);
+    }
+  }
 }
 
 template <int D, int P>
 __global__ __launch_bounds__(256) void hash_bf16_kernel(
     const uint16_t* __restrict__ x, int64_t sh, int64_t st, int H, int64_t N,
     const uint16_t* __restrict__ planes, int nb, int32_t* __restrict__ bucket,
-    uint32_t* __restrict__ queue, uint32_t* __restrict__ qcount) {
+    fastar_diag_t* __restrict__ diag) {
   constexpr int NC = D / 32;
+  __shared__ double ex[4][D + 2];
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
@@ -154,14 +246,20 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
       const float err = 2.f * kc * xnorm + (nr.d1 + nr.d2) * 0x1p-20f + 0x1p-90f;
       if (nr.d2 - nr.d1 <= err) amb = 1;
     }
-    if (valid && g == 0) {
+    if (valid && g == 0 && !amb) {
       int32_t* o = bucket + ((int64_t)h * N + row) * P;
       o[0] = (int32_t)bits;
       if (P == 2) o[1] = (int32_t)(bits ^ (1u << nr.j1));
-      if (amb) {
-        const uint32_t slot = atomicAdd(qcount, 1u);
-        queue[slot] = (uint32_t)((int64_t)h * N + row);
-      }
+    }
+    // rows float32 cannot certify: float64 by the whole wave, one at a time
+    uint64_t ab = ballot64(valid && g == 0 && amb);
+    while (ab) {
+      const int src = __builtin_ctzll(ab);  // = the row's column (g == 0)
+      ab &= ab - 1;
+      const int64_t rr = r0 + src;
+      hash_fixup_row<uint16_t, D, P>(x + (int64_t)h * sh + rr * st, planes, nb,
+                                     bucket + ((int64_t)h * N + rr) * P, diag,
+                                     ex[threadIdx.x >> 6]);
     }
   }
 }
@@ -170,8 +268,9 @@ template <int D, int P>
 __global__ __launch_bounds__(256) void hash_f32_kernel(
     const float* __restrict__ x, int64_t sh, int64_t st, int H, int64_t N,
     const float* __restrict__ planes, int nb, int32_t* __restrict__ bucket,
-    uint32_t* __restrict__ queue, uint32_t* __restrict__ qcount) {
+    fastar_diag_t* __restrict__ diag) {
   __shared__ float sp[16][D];
+  __shared__ double ex[4][D + 2];
   __shared__ float srn[16];
   for (int i = threadIdx.x; i < 16 * D; i += blockDim.x) {
     const int p = i / D;
@@ -186,10 +285,13 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
   __syncthreads();
   const float kc = kcert<D>();
   const int64_t total = (int64_t)H * N;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int h = (int)(idx / N);
-    const int64_t row = idx - (int64_t)h * N;
+  // the loop is uniform per wave so that the wave can settle rows together
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63); base < total;
+       base += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t idx = base + lane_id();
+    const bool valid = idx < total;
+    const int h = valid ? (int)(idx / N) : 0;
+    const int64_t row = valid ? idx - (int64_t)h * N : 0;
     const float* xr = x + (int64_t)h * sh + row * st;
     float s[16];
 #pragma unroll
@@ -227,127 +329,27 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
       const float err = 2.f * kc * xnorm + (nr.d1 + nr.d2) * 0x1p-20f + 0x1p-90f;
       if (nr.d2 - nr.d1 <= err) amb = true;
     }
-    int32_t* o = bucket + idx * P;
-    o[0] = (int32_t)bits;
-    if (P == 2) o[1] = (int32_t)(bits ^ (1u << nr.j1));
-    if (amb) {
-      const uint32_t slot = atomicAdd(qcount, 1u);
-      queue[slot] = (uint32_t)idx;
-    }
-  }
-}
-
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int m = 1; m < FASTAR_WAVE; m <<= 1) v += __shfl_xor(v, m, FASTAR_WAVE);
-  return v;
-}
-
-// Re-evaluates queued rows in float64, one wave per row (each lane holds D/64
-// dims); a sign float64 cannot certify is settled exactly by lane 0 with an
-// expansion sum in LDS.
-template <typename T, int D, int P>
-__global__ __launch_bounds__(256) void hash_fixup_kernel(
-    const T* __restrict__ x, int64_t sh, int64_t st, int64_t N, const T* __restrict__ planes,
-    int nb, int32_t* __restrict__ bucket, const uint32_t* __restrict__ queue,
-    const uint32_t* __restrict__ qcount, fastar_diag_t* __restrict__ diag) {
-  constexpr int L = D / FASTAR_WAVE;
-  __shared__ double ex[4][D + 2];
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  const uint32_t n = *qcount;
-  for (uint32_t qi = blockIdx.x * 4 + wave; qi < n; qi += gridDim.x * 4) {
-    const uint32_t e = queue[qi];
-    const int64_t h = (int64_t)e / N;
-    const int64_t row = (int64_t)e - h * N;
-    const T* xr = x + h * sh + row * st;
-    double xv[L];
-#pragma unroll
-    for (int k = 0; k < L; ++k) xv[k] = (double)Elem<T>::load(xr, lane + FASTAR_WAVE * k);
-    uint32_t bits = 0;
-    double dist[16], derr[16];
-    bool unresolved = false;
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      dist[p] = 0.0;
-      derr[p] = 0.0;
-      if (p < nb) {
-        double s = 0.0, a = 0.0, n2 = 0.0;
-#pragma unroll
-        for (int k = 0; k < L; ++k) {
-          const double rv = (double)Elem<T>::load(planes, (int64_t)p * D + lane + FASTAR_WAVE * k);
-          const double pr = xv[k] * rv;  // exact: at most 48 significant bits
-          s += pr;
-          a += fabs(pr);
-          n2 += rv * rv;
-        }
-        s = wave_sum_d(s);
-        a = wave_sum_d(a);
-        n2 = wave_sum_d(n2);
-        const double bound = 2.0 * (D + 8) * 0x1p-53 * a;
-        int sg;
-        if (fabs(s) > bound) {
-          sg = s > 0.0 ? 1 : -1;
-        } else if (a == 0.0) {
-          sg = 0;
-        } else {
-          int sg0 = 0;
-          if (lane == 0) {
-            double* E = ex[wave];
-            int m = 0;
-            for (int d = 0; d < D; ++d) {
-              const double xd = (double)Elem<T>::load(xr, d);
-              const double rd = (double)Elem<T>::load(planes, (int64_t)p * D + d);
-              m = grow_expansion(E, m, xd * rd);
-            }
-            sg0 = expansion_sign(E, m);
-            if (diag) atomicAdd(&diag->hash_exact_signs, 1u);
-          }
-          sg = __shfl(sg0, 0, FASTAR_WAVE);
-        }
-        if (sg > 0) bits |= 1u << p;
-        if (P == 2) {
-          const double rn = sqrt(n2);
-          dist[p] = rn > 0.0 ? fabs(s) / rn : 0.0;
-          derr[p] = (a == 0.0) ? 0.0 : (rn > 0.0 ? bound / rn : 0.0) + dist[p] * (2 * D + 8) * 0x1p-53;
-        }
-      }
-    }
-    int j1 = 0;
-    if (P == 2) {
-      double d1 = dist[0], e1 = derr[0];
-#pragma unroll
-      for (int p = 1; p < 16; ++p) {
-        if (p < nb && dist[p] < d1) {
-          j1 = p;
-          d1 = dist[p];
-          e1 = derr[p];
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < 16; ++p) {
-        if (p < nb && p != j1) {
-          const double gap = dist[p] - d1;
-          const double err = derr[p] + e1;
-          if (err > 0.0 && gap <= err) unresolved = true;
-        }
-      }
-    }
-    if (lane == 0) {
-      int32_t* o = bucket + (h * N + row) * P;
+    if (valid && !amb) {
+      int32_t* o = bucket + idx * P;
       o[0] = (int32_t)bits;
-      if (P == 2) o[1] = (int32_t)(bits ^ (1u << j1));
-      if (diag) {
-        atomicAdd(&diag->hash_fallback_rows, 1u);
-        if (unresolved) atomicAdd(&diag->unresolved, 1u);
-      }
+      if (P == 2) o[1] = (int32_t)(bits ^ (1u << nr.j1));
+    }
+    uint64_t ab = ballot64(valid && amb);
+    while (ab) {
+      const int src = __builtin_ctzll(ab);
+      ab &= ab - 1;
+      const int64_t e = base + src;
+      const int hh = (int)(e / N);
+      const int64_t rr = e - (int64_t)hh * N;
+      hash_fixup_row<float, D, P>(x + (int64_t)hh * sh + rr * st, planes, nb, bucket + e * P, diag,
+                                  ex[threadIdx.x >> 6]);
     }
   }
 }
 
 template <int D, int P>
 hipError_t launch_hash_dp(const fastar_tensor_t& x, const void* planes, int nb, int32_t* bucket,
-                          uint32_t* queue, uint32_t* qcount, fastar_diag_t* diag, hipStream_t s) {
+                          fastar_diag_t* diag, hipStream_t s) {
   const int H = x.heads;
   const int64_t N = x.tokens;
   if (x.dtype == FASTAR_BF16) {
@@ -355,42 +357,27 @@ hipError_t launch_hash_dp(const fastar_tensor_t& x, const void* planes, int nb, 
     const int64_t blocks = (tiles + 3) / 4 < 8192 ? (tiles + 3) / 4 : 8192;
     hipLaunchKernelGGL((hash_bf16_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s,
                        (const uint16_t*)x.data, x.stride_head, x.stride_token, H, N,
-                       (const uint16_t*)planes, nb, bucket, queue, qcount);
-    hipLaunchKernelGGL((hash_fixup_kernel<uint16_t, D, P>), dim3(128), dim3(256), 0, s,
-                       (const uint16_t*)x.data, x.stride_head, x.stride_token, N,
-                       (const uint16_t*)planes, nb, bucket, queue, qcount, diag);
+                       (const uint16_t*)planes, nb, bucket, diag);
   } else {
     const int64_t total = (int64_t)H * N;
     const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
     hipLaunchKernelGGL((hash_f32_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s,
                        (const float*)x.data, x.stride_head, x.stride_token, H, N,
-                       (const float*)planes, nb, bucket, queue, qcount);
-    hipLaunchKernelGGL((hash_fixup_kernel<float, D, P>), dim3(128), dim3(256), 0, s,
-                       (const float*)x.data, x.stride_head, x.stride_token, N,
-                       (const float*)planes, nb, bucket, queue, qcount, diag);
+                       (const float*)planes, nb, bucket, diag);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
 hipError_t launch_hash(const fastar_tensor_t& x, const void* planes, int n_bits, int n_probes,
-                       int32_t* bucket, uint32_t* queue, uint32_t* queue_count,
-                       fastar_diag_t* diag, hipStream_t s) {
-  hipError_t e = launch_zero_u32(queue_count, 1, s);
-  if (e != hipSuccess) return e;
+                       int32_t* bucket, fastar_diag_t* diag, hipStream_t s) {
   if ((int64_t)x.heads * x.tokens == 0) return hipSuccess;
   if (x.dim == 64)
-    return n_probes == 1 ? launch_hash_dp<64, 1>(x, planes, n_bits, bucket, queue, queue_count, diag, s)
-                         : launch_hash_dp<64, 2>(x, planes, n_bits, bucket, queue, queue_count, diag, s);
-  return n_probes == 1 ? launch_hash_dp<128, 1>(x, planes, n_bits, bucket, queue, queue_count, diag, s)
-                       : launch_hash_dp<128, 2>(x, planes, n_bits, bucket, queue, queue_count, diag, s);
+    return n_probes == 1 ? launch_hash_dp<64, 1>(x, planes, n_bits, bucket, diag, s)
+                         : launch_hash_dp<64, 2>(x, planes, n_bits, bucket, diag, s);
+  return n_probes == 1 ? launch_hash_dp<128, 1>(x, planes, n_bits, bucket, diag, s)
+                       : launch_hash_dp<128, 2>(x, planes, n_bits, bucket, diag, s);
 }
 
 }  // namespace fastar

@@ -9,10 +9,8 @@
 namespace fastar {
 
 // hash.hip ------------------------------------------------------------------
-hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_hash(const fastar_tensor_t& x, const void* planes, int n_bits, int n_probes,
-                       int32_t* bucket, uint32_t* queue, uint32_t* queue_count,
-                       fastar_diag_t* diag, hipStream_t s);
+                       int32_t* bucket, fastar_diag_t* diag, hipStream_t s);
 
 // index.hip -----------------------------------------------------------------
 hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int n_probes,

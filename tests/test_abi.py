@@ -80,8 +80,8 @@ def test_hash_rejects_bad_arguments_without_launching(lib):
         st = lib.fastar_hash(ctypes.byref(t), buf, bits, probes, buf, None, None, buf,
                              1 << 30, None, None)
         assert st == want, (bits, probes, st, lib.fastar_last_error())
-    # workspace too small
-    st = lib.fastar_hash(ctypes.byref(_tensor()), buf, 12, 1, buf, None, None, buf, 8, None, None)
+    # workspace too small (the index needs it)
+    st = lib.fastar_hash(ctypes.byref(_tensor()), buf, 12, 1, buf, buf, buf, buf, 8, None, None)
     assert st == 3
     assert b"workspace" in lib.fastar_last_error()
     # offsets without perm
