@@ -292,9 +292,10 @@ constexpr int kDirectMaxBits = 12;
 __global__ __launch_bounds__(kDirectWaves * FASTAR_WAVE) void bucket_index_direct_kernel(
     const int32_t* __restrict__ bucket, int64_t n, int nbits, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
-  extern __shared__ int32_t cnt[];  // [kDirectWaves][2^nbits]
-  __shared__ int wtot[kDirectWaves];
+  extern __shared__ int4 cnt4[];  // [kDirectWaves][2^nbits / 4] (2^nbits >= 4)
+  __shared__ int wtot[2][kDirectWaves];
   constexpr int NT = kDirectWaves * FASTAR_WAVE;
+  int32_t* cnt = reinterpret_cast<int32_t*>(cnt4);
   const int h = blockIdx.x;
   int64_t nh = n;
   if (n_valid) {
@@ -302,15 +303,14 @@ __global__ __launch_bounds__(kDirectWaves * FASTAR_WAVE) void bucket_index_direc
     nh = v < 0 ? 0 : (v < n ? v : n);
   }
   const int nbk = 1 << nbits;
+  const int nb4 = nbk >> 2;
   const uint32_t bmask = (uint32_t)nbk - 1u;
   const int32_t* ids = bucket + (int64_t)h * n;
   int32_t* ph = perm + (int64_t)h * n;
   int32_t* off = offsets + (int64_t)h * (nbk + 1);
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  for (int i = threadIdx.x; i < kDirectWaves * nbk / 4; i += NT)
-    reinterpret_cast<int4*>(cnt)[i] = make_int4(0, 0, 0, 0);
-  for (int i = (kDirectWaves * nbk / 4) * 4 + threadIdx.x; i < kDirectWaves * nbk; i += NT) cnt[i] = 0;
+  for (int i = threadIdx.x; i < kDirectWaves * nb4; i += NT) cnt4[i] = make_int4(0, 0, 0, 0);
   __syncthreads();
   const int64_t chunk = (nh + kDirectWaves - 1) / kDirectWaves;
   const int64_t wbeg = (int64_t)wave * chunk < nh ? (int64_t)wave * chunk : nh;
@@ -330,77 +330,66 @@ __global__ __launch_bounds__(kDirectWaves * FASTAR_WAVE) void bucket_index_direc
       if (b[r] != 0xFFFFFFFFu) atomicAdd(&wc[b[r]], 1);  // counts: order does not matter
   }
   __syncthreads();
-  // exclusive scan over (bucket, wave): each thread owns kPer consecutive
-  // buckets (2^b <= NT * kPer), read and written as 128-bit words
-  constexpr int kPer = (1 << kDirectMaxBits) / NT;
-  static_assert(kPer == 8, "layout");
-  const int B0 = threadIdx.x * kPer;
-  int cw[kDirectWaves][kPer];
-  int tot[kPer];
-  int local = 0;
-  if (nbk >= 4) {
+  // exclusive scan over (bucket, wave).  Buckets go in groups of 4 (one
+  // 128-bit LDS word per wave); thread t owns groups t and t + NT, so that
+  // neighbouring lanes touch neighbouring words.  The two halves are scanned
+  // together, the second after the whole first.
+  static_assert((1 << kDirectMaxBits) / 4 == 2 * NT, "layout");
+  int4 cw[2][kDirectWaves];
+  int tot[2][4];
+  int local[2] = {0, 0};
 #pragma unroll
-    for (int w = 0; w < kDirectWaves; ++w)
+  for (int hv = 0; hv < 2; ++hv) {
+    const int gi = threadIdx.x + hv * NT;
 #pragma unroll
-      for (int q = 0; q < kPer; q += 4) {
-        int4 v = make_int4(0, 0, 0, 0);
-        if (B0 + q < nbk) v = *reinterpret_cast<const int4*>(&cnt[w * nbk + B0 + q]);
-        cw[w][q] = v.x;
-        cw[w][q + 1] = v.y;
-        cw[w][q + 2] = v.z;
-        cw[w][q + 3] = v.w;
-      }
-  } else {
+    for (int w = 0; w < kDirectWaves; ++w) cw[hv][w] = gi < nb4 ? cnt4[w * nb4 + gi] : make_int4(0, 0, 0, 0);
 #pragma unroll
-    for (int w = 0; w < kDirectWaves; ++w)
+    for (int e = 0; e < 4; ++e) tot[hv][e] = 0;
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) cw[w][q] = B0 + q < nbk ? cnt[w * nbk + B0 + q] : 0;
+    for (int w = 0; w < kDirectWaves; ++w) {
+      tot[hv][0] += cw[hv][w].x;
+      tot[hv][1] += cw[hv][w].y;
+      tot[hv][2] += cw[hv][w].z;
+      tot[hv][3] += cw[hv][w].w;
+    }
+    local[hv] = tot[hv][0] + tot[hv][1] + tot[hv][2] + tot[hv][3];
   }
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    tot[q] = 0;
-#pragma unroll
-    for (int w = 0; w < kDirectWaves; ++w) tot[q] += cw[w][q];
-    local += tot[q];
-  }
-  int incl = local;
+  int incl[2] = {local[0], local[1]};
 #pragma unroll
   for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
-    const int y = __shfl_up(incl, o, FASTAR_WAVE);
-    if (lane >= o) incl += y;
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      const int y = __shfl_up(incl[hv], o, FASTAR_WAVE);
+      if (lane >= o) incl[hv] += y;
+    }
   }
-  if (lane == FASTAR_WAVE - 1) wtot[wave] = incl;
+  if (lane == FASTAR_WAVE - 1) {
+    wtot[0][wave] = incl[0];
+    wtot[1][wave] = incl[1];
+  }
   __syncthreads();
-  int run = incl - local;
-  for (int w = 0; w < wave; ++w) run += wtot[w];
-  // bucket starts, then each wave's base within each bucket
-  int start[kPer];
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    start[q] = run;
-    run += tot[q];
+  int run[2] = {incl[0] - local[0], incl[1] - local[1]};
+  for (int w = 0; w < kDirectWaves; ++w) {
+    if (w < wave) {
+      run[0] += wtot[0][w];
+      run[1] += wtot[1][w];
+    }
+    run[1] += wtot[0][w];  // the whole first half precedes the second
   }
-  if (nbk >= 4) {
 #pragma unroll
-    for (int w = 0; w < kDirectWaves; ++w)
+  for (int hv = 0; hv < 2; ++hv) {
+    const int gi = threadIdx.x + hv * NT;
+    if (gi >= nb4) continue;
+    int4 b4 = make_int4(run[hv], run[hv] + tot[hv][0], run[hv] + tot[hv][0] + tot[hv][1],
+                        run[hv] + tot[hv][0] + tot[hv][1] + tot[hv][2]);
+    // each wave's base within each bucket
 #pragma unroll
-      for (int q = 0; q < kPer; q += 4)
-        if (B0 + q < nbk) {
-          *reinterpret_cast<int4*>(&cnt[w * nbk + B0 + q]) =
-              make_int4(start[q], start[q + 1], start[q + 2], start[q + 3]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) start[q + e] += cw[w][q + e];
-        }
-  } else {
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      if (B0 + q < nbk) {
-#pragma unroll
-        for (int w = 0; w < kDirectWaves; ++w) {
-          cnt[w * nbk + B0 + q] = start[q];
-          start[q] += cw[w][q];
-        }
-      }
+    for (int w = 0; w < kDirectWaves; ++w) {
+      cnt4[w * nb4 + gi] = b4;
+      b4.x += cw[hv][w].x;
+      b4.y += cw[hv][w].y;
+      b4.z += cw[hv][w].z;
+      b4.w += cw[hv][w].w;
     }
   }
   __syncthreads();
@@ -450,7 +439,7 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
                                int n_bits, const int32_t* n_valid, int32_t* offsets,
                                int32_t* perm, int32_t* ws, hipStream_t s) {
   if (heads == 0) return hipSuccess;
-  if (n_probes == 1 && n_bits <= kDirectMaxBits) {
+  if (n_probes == 1 && n_bits >= 2 && n_bits <= kDirectMaxBits) {
     hipLaunchKernelGGL(bucket_index_direct_kernel, dim3(heads), dim3(kDirectWaves * FASTAR_WAVE),
                        (size_t)kDirectWaves * ((size_t)1 << n_bits) * sizeof(int32_t), s, bucket, n,
                        n_bits, n_valid, offsets, perm);
