@@ -72,21 +72,26 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     const float* __restrict__ key_bias, const int32_t* __restrict__ k_offsets,
     const int32_t* __restrict__ k_perm, int nbits, const int32_t* __restrict__ key_list,
     const int32_t* __restrict__ n_key_list, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, int H) {
   constexpr int NC = D / 32;  // k-chunks of the QK^T contraction
   constexpr int NB = D / 16;  // 16-dim output blocks
   // rows of the V chunk one 16-byte-per-lane LDS load fills
   constexpr int kVRows = 64 * 16 / (2 * D);
   __shared__ __attribute__((aligned(16))) uint16_t vlds[4][32 * D];
   __shared__ __attribute__((aligned(16))) float blds[4][32];
-  const int h = blockIdx.y;
+  // logical block (row block, head), XCD-grouped
+  const int64_t nbx = (Nq + 63) / 64;
+  const int64_t lb = xcd_block(blockIdx.x, nbx * H);
+  if (lb >= nbx * H) return;
+  const int h = (int)(lb / nbx);
+  const int64_t bx = lb - (int64_t)h * nbx;
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
   uint16_t* vbuf = vlds[wave];
   float* bbuf = blds[wave];
-  const int64_t r0 = (int64_t)blockIdx.x * 64 + wave * 16;
+  const int64_t r0 = bx * 64 + wave * 16;
   if (r0 >= Nq) return;
   const int64_t r = r0 + col;
   const bool rvalid = r < Nq;
@@ -377,12 +382,13 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 template <int D, int P, int MODE>
 hipError_t launch3(const AttnArgs& a, hipStream_t s) {
   if (a.dtype == FASTAR_BF16) {
-    dim3 grid((unsigned)((a.nq + 63) / 64), (unsigned)a.heads);
+    const int64_t nb = (a.nq + 63) / 64 * a.heads;
+    dim3 grid((unsigned)(FASTAR_XCDS * xcd_span(nb)));
     hipLaunchKernelGGL((attn_bf16_kernel<D, P, MODE>), grid, dim3(256), 0, s,
                        (const uint16_t*)a.q, a.q_sh, a.q_st, a.nq, a.q_bucket, a.q_perm,
                        (const uint16_t*)a.k, a.k_sh, a.k_st, (const uint16_t*)a.v, a.v_sh, a.v_st,
                        a.nk, a.key_bias, a.k_offsets, a.k_perm, a.n_bits, a.key_list,
-                       a.n_key_list, a.scale * kLog2e, (uint16_t*)a.out, a.lse);
+                       a.n_key_list, a.scale * kLog2e, (uint16_t*)a.out, a.lse, a.heads);
   } else {
     dim3 grid((unsigned)((a.nq + 63) / 64), (unsigned)a.heads);
     hipLaunchKernelGGL((attn_f32_kernel<D, P, MODE>), grid, dim3(64), 0, s,

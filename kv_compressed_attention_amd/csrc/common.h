@@ -11,6 +11,20 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 #define FASTAR_WAVE 64
 
+// Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
+// launch order.  xcd_block maps launch index i of a 1-D grid of
+// 8 * xcd_span(n) workgroups to logical block i % 8 * xcd_span(n) + i / 8, so
+// that each XCD runs one contiguous range of logical blocks and neighbouring
+// blocks, which tend to read the same rows, share an L2.  Logical blocks >= n
+// are empty.
+#define FASTAR_XCDS 8
+__host__ __device__ __forceinline__ int64_t xcd_span(int64_t n) {
+  return (n + FASTAR_XCDS - 1) / FASTAR_XCDS;
+}
+__device__ __forceinline__ int64_t xcd_block(int64_t i, int64_t n) {
+  return (i % FASTAR_XCDS) * xcd_span(n) + i / FASTAR_XCDS;
+}
+
 // ---------------------------------------------------------------------------
 // element access
 // ---------------------------------------------------------------------------

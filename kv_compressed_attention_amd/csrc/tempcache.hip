@@ -452,12 +452,83 @@ struct SegCtx {
   }
 };
 
+// Turns the float32 best / second best of the reporting lanes' keys (m) into
+// proposals p (candidate token, -1: none) and cosines c; a key the error
+// bound cannot decide is redone in float64 by the whole wave over its
+// candidates, which cand_of(lane, list, groups, n) gives for the reporting
+// lane `lane`.
+template <typename T, int D, typename CandOf>
+__device__ __forceinline__ void decide(const SegCtx<T, D>& x, const Top2<float>& m, bool own,
+                                       int jrep, CandOf cand_of, int& p, float& c) {
+  const int lane = lane_id();
+  bool prop = false, amb = false;
+  if (own) {
+    if (m.c1 < x.tau - x.e) prop = false;                                  // none reaches tau
+    else if (m.c1 >= x.tau + x.e && m.c1 - m.c2 > 2.f * x.e) prop = true;  // clear winner
+    else amb = true;
+  }
+  int best = m.best;
+  float c1 = m.c1;
+  const double e64 = cos_err64<D>();
+  uint64_t ab = ballot64(amb);
+  while (ab) {
+    const int src = __builtin_ctzll(ab);
+    ab &= ab - 1;
+    const int js = __shfl(jrep, src, FASTAR_WAVE);
+    const int32_t* cl;
+    const int32_t* gl;
+    int n;
+    cand_of(src, cl, gl, n);
+    Top2<double> u;
+    u.init();
+    for (int k = 0; k < n; ++k)
+      u.add(wave_cos64<T, D>(x.kf + (int64_t)js * x.k_st, x.cand_row(k, cl[k], x.f == 0 ? gl[k] : 0)),
+            cl[k]);
+    if (lane == src) {
+      if (x.diag) atomicAdd(&x.diag->merge_fallbacks, 1u);
+      const bool sure = (u.c1 < (double)x.tau - e64) ||
+                        (u.c1 >= (double)x.tau + e64 && u.c1 - u.c2 > 2.0 * e64);
+      if (!sure && x.diag) atomicAdd(&x.diag->unresolved, 1u);
+      best = u.best;
+      prop = u.c1 >= (double)x.tau;
+      c1 = (float)u.c1;
+    }
+  }
+  p = -1;
+  c = 0.f;
+  if (own) {
+    p = prop ? best : -1;
+    c = c1;
+  }
+}
+
+// the reporting lane's key (r = 4 (l >> 4) + (l & 3)) takes its float32 top
+// two out of t[] after the merge over the 16 columns
+__device__ __forceinline__ Top2<float> reduce_top2(Top2<float>* t) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    top2_merge_xor(t[i], 1);
+    top2_merge_xor(t[i], 2);
+    top2_merge_xor(t[i], 4);
+    top2_merge_xor(t[i], 8);
+  }
+  const int col = lane_id() & 15;
+  Top2<float> m = t[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+    if ((col & 3) == i) {
+      m.c1 = t[i].c1;
+      m.c2 = t[i].c2;
+      m.best = t[i].best;
+    }
+  return m;
+}
+
 // Step 1 for keys k0 .. k0 + 15 of a segment (whole wave).  The lane with
 // (l & 15) < 4 reports key r = 4 (l >> 4) + (l & 3): jrep (its token, -1: no
 // such key), p (the candidate token it proposes to, -1: none) and c (the
 // cosine).  Candidates are visited in tiles of 16, the next tile's rows
-// loading while the current one is used; float32 decisions inside the error
-// bound are redone in float64.
+// loading while the current one is used.
 template <typename T, int D>
 __device__ __forceinline__ void match_keys(const SegCtx<T, D>& x, int k0, int& jrep, int& p,
                                            float& c) {
@@ -497,54 +568,52 @@ __device__ __forceinline__ void match_keys(const SegCtx<T, D>& x, int k0, int& j
     cv = nv;
     ci = ni;
   }
+  const Top2<float> m = reduce_top2(t);
+  decide<T, D>(x, m, own, jrep,
+               [&](int, const int32_t*& cl, const int32_t*& gl, int& n) {
+                 cl = x.cands;
+                 gl = x.cgs;
+                 n = x.nc;
+               },
+               p, c);
+}
+
+// Step 1 for a packed tile: up to 16 keys and 16 candidates of several small
+// segments (row / column r belongs to segment rseg / cseg, -1: empty), one
+// MFMA tile with the cosines across segments masked out.  Reports as
+// match_keys; seg_cands(s, list, groups, n) gives segment s's candidates.
+template <typename T, int D, typename SegCands>
+__device__ __forceinline__ void match_packed(const SegCtx<T, D>& x, int jr, int rseg, int ci,
+                                             int cgi, int cseg, SegCands seg_cands, int& jrep,
+                                             int& p, float& c) {
+  using TD = TileDot<T, D>;
+  const int lane = lane_id();
+  const int g = lane >> 4, col = lane & 15;
+  const int r = 4 * g + (col & 3);
+  jrep = __shfl(jr, r, FASTAR_WAVE);
+  const bool own = col < 4 && jrep >= 0;
+  TD td;
+  td.issue_keys(jr >= 0 ? x.kf + (int64_t)jr * x.k_st : nullptr);
+  typename TD::Rows cr = TD::issue(cseg >= 0 ? x.cand_row(col, ci, cgi) : nullptr);
+  td.finish_keys();
+  Top2<float> t[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[i].init();
+  float sd[4], cn;
+  td.dots(cr, sd, cn);
+  const float rc = cn > 0.f ? rsqrtf(cn) : 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    top2_merge_xor(t[i], 1);
-    top2_merge_xor(t[i], 2);
-    top2_merge_xor(t[i], 4);
-    top2_merge_xor(t[i], 8);
+    const int ks = __shfl(rseg, 4 * g + i, FASTAR_WAVE);
+    if (cseg >= 0 && ks == cseg) t[i].add(td.kn[i] > 0.f ? sd[i] * rsqrtf(td.kn[i]) * rc : 0.f, ci);
   }
-  Top2<float> m = t[0];
-#pragma unroll
-  for (int i = 1; i < 4; ++i)
-    if ((col & 3) == i) {
-      m.c1 = t[i].c1;
-      m.c2 = t[i].c2;
-      m.best = t[i].best;
-    }
-  bool prop = false, amb = false;
-  if (own) {
-    if (m.c1 < x.tau - x.e) prop = false;                                  // none reaches tau
-    else if (m.c1 >= x.tau + x.e && m.c1 - m.c2 > 2.f * x.e) prop = true;  // clear winner
-    else amb = true;
-  }
-  int best = m.best;
-  float c1 = m.c1;
-  // float64 for the keys float32 cannot decide, one key at a time
-  const double e64 = cos_err64<D>();
-  uint64_t ab = ballot64(amb);
-  while (ab) {
-    const int src = __builtin_ctzll(ab);
-    ab &= ab - 1;
-    const int js = __shfl(jrep, src, FASTAR_WAVE);
-    Top2<double> u;
-    u.init();
-    for (int k = 0; k < x.nc; ++k)
-      u.add(wave_cos64<T, D>(x.kf + (int64_t)js * x.k_st, x.cand_row_at(k)), x.cands[k]);
-    if (lane == src) {
-      if (x.diag) atomicAdd(&x.diag->merge_fallbacks, 1u);
-      const bool sure = (u.c1 < (double)x.tau - e64) ||
-                        (u.c1 >= (double)x.tau + e64 && u.c1 - u.c2 > 2.0 * e64);
-      if (!sure && x.diag) atomicAdd(&x.diag->unresolved, 1u);
-      best = u.best;
-      prop = u.c1 >= (double)x.tau;
-      c1 = (float)u.c1;
-    }
-  }
-  if (own) {
-    p = prop ? best : -1;
-    c = c1;
-  }
+  const Top2<float> m = reduce_top2(t);
+  decide<T, D>(x, m, own, jrep,
+               [&](int src, const int32_t*& cl, const int32_t*& gl, int& n) {
+                 const int rs = 4 * (src >> 4) + (src & 3);
+                 seg_cands(__shfl(rseg, rs, FASTAR_WAVE), cl, gl, n);
+               },
+               p, c);
 }
 
 // Step 2 for the keys this wave holds (one per lane; p < 0: no proposal):
@@ -598,21 +667,24 @@ __device__ __forceinline__ bool resolve_keys(const SegCtx<T, D>& x, int self, in
 constexpr int kSegBatch = 64;
 
 // Workgroup b of (frame f, head h) takes the segments s = b, b + gridDim.x, ..
-// of new frame f, kSegBatch at a time, and its waves share their tiles of
-// kKeyTile keys.  Step 1 (per tile) finds each key's best candidate and its
-// proposal.  Step 2 lets every candidate keep its best proposer (ties:
-// smaller j), which links to it; the other keys of the segment open groups.
-// A one-tile segment does step 2 in registers; in a larger one every tile
-// leaves its proposals in LDS, and the wave that completes the segment's
-// last tile does step 2 for all of it.
+// of new frame f, kSegBatch at a time.  Segments of at most 16 keys and 16
+// candidates are packed greedily into shared 16 x 16 tiles; larger ones are
+// cut into tiles of 16 keys.  The waves share the tiles.  Step 1 (per tile)
+// finds each key's best candidate and its proposal.  Step 2 lets every
+// candidate keep its best proposer (ties: smaller j), which links to it; the
+// other keys open groups.  A tile that holds whole segments does step 2 in
+// registers; in a larger segment every tile leaves its proposals in LDS, and
+// the wave that completes the segment's last tile does step 2 for all of it.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tc_match_kernel(
     const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
     const int32_t* __restrict__ frontier, const int32_t* __restrict__ n_groups, float tau,
     MergeArgs a, fastar_diag_t* __restrict__ diag) {
   extern __shared__ int32_t lds[];  // [3][Tf] proposals of multi-tile segments
-  __shared__ int4 brec[kSegBatch];
+  __shared__ int4 bseg[kSegBatch];  // {key start, keys, candidate start, candidates}
   __shared__ int btile[kSegBatch + 1], bkey[kSegBatch + 1], bdone[kSegBatch];
+  __shared__ int porder[kSegBatch], pstart[kSegBatch + 1];
+  __shared__ int npacked;
   const int h = blockIdx.y;
   const int f = blockIdx.z;
   const int lane = lane_id();
@@ -648,14 +720,30 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
     }
     a.link[fo + j] = lk;
   };
+  auto small = [](const int4& sg) { return sg.y <= 16 && sg.w <= 16; };
   const int stride = (int)gridDim.x;
   for (int k0b = 0; blockIdx.x + k0b * stride < nseg; k0b += kSegBatch) {
-    // the batch: its segments, tile and key offsets (wave 0)
+    // the batch (wave 0): segments with their candidate ranges, tiles of the
+    // large ones, and the packing of the small ones
     if (wave == 0) {
       const int sidx = blockIdx.x + (k0b + lane) * stride;
-      int4 r = make_int4(0, 0, 0, 0);
-      if (lane < kSegBatch && sidx < nseg) r = srec[sidx];
-      int nt = (r.z + kKeyTile - 1) / kKeyTile, nk = r.z;
+      const bool sv = lane < kSegBatch && sidx < nseg;
+      int4 sg = make_int4(0, 0, 0, 0);
+      if (sv) {
+        const int4 r = srec[sidx];
+        sg = make_int4(r.y, r.z, 0, 0);
+        if (have_c) {
+          uint32_t sl = slot_hash(r.x, mask);
+          int4 tb;
+          while ((tb = ctab[sl]).x != 0 && tb.x != r.x + 1) sl = (sl + 1u) & mask;
+          if (tb.x != 0) {
+            sg.z = tb.y;
+            sg.w = tb.z;
+          }
+        }
+      }
+      const bool big = sv && !small(sg);
+      int nt = big ? (sg.y + kKeyTile - 1) / kKeyTile : 0, nk = big ? sg.y : 0;
 #pragma unroll
       for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
         const int t = __shfl_up(nt, o, FASTAR_WAVE);
@@ -666,44 +754,76 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
         }
       }
       if (lane < kSegBatch) {
-        brec[lane] = r;
+        bseg[lane] = sg;
         btile[lane + 1] = nt;
         bkey[lane + 1] = nk;
         bdone[lane] = 0;
       }
+      // greedy packing in batch order (wave-uniform scalar walk)
+      const uint64_t smask = ballot64(sv && !big);
+      int ku = 0, cu = 0, pos = 0, npt = 0;
+      for (int sb = 0; sb < kSegBatch; ++sb) {
+        if (!((smask >> sb) & 1ull)) continue;
+        const int kn = __builtin_amdgcn_readlane(sg.y, sb);
+        const int cn = __builtin_amdgcn_readlane(sg.w, sb);
+        if (ku + kn > 16 || cu + cn > 16) {
+          ++npt;
+          if (lane == 0) pstart[npt] = pos;
+          ku = 0;
+          cu = 0;
+        }
+        if (lane == 0) porder[pos] = sb;
+        ++pos;
+        ku += kn;
+        cu += cn;
+      }
+      if (pos > 0) ++npt;
       if (lane == 0) {
         btile[0] = 0;
         bkey[0] = 0;
+        pstart[0] = 0;
+        pstart[npt] = pos;
+        npacked = npt;
       }
     }
     __syncthreads();
-    const int ntiles = btile[kSegBatch];
-    for (int tt = wave; tt < ntiles; tt += 4) {
-      int sb = 0;  // the batch segment holding tile tt
-      while (btile[sb + 1] <= tt) ++sb;
-      const int4 rec = brec[sb];
-      x.keys = kcand + rec.y;
-      x.nk = rec.z;
-      x.nc = 0;
-      x.cands = ccand;
-      x.cgs = cgh;
-      if (have_c) {
-        // the bucket's candidate segment
-        uint32_t sl = slot_hash(rec.x, mask);
-        int4 tb;
-        while ((tb = ctab[sl]).x != 0 && tb.x != rec.x + 1) sl = (sl + 1u) & mask;
-        if (tb.x != 0) {
-          x.cands = ccand + tb.y;
-          x.cgs = cgh + tb.y;
-          x.nc = tb.z;
+    const int nbt = btile[kSegBatch];
+    const int nwork = nbt + npacked;
+    for (int tt = wave; tt < nwork; tt += 4) {
+      if (tt >= nbt) {
+        // a packed tile of whole small segments
+        const int pt = tt - nbt;
+        const int s0 = pstart[pt], s1 = pstart[pt + 1];
+        int jr = -1, rseg = -1, ci = 0, cgi = 0, cseg = -1;
+        int ko = 0, co = 0;
+        for (int q = s0; q < s1; ++q) {
+          const int sb = porder[q];
+          const int4 sg = bseg[sb];
+          if (col >= ko && col < ko + sg.y) {
+            jr = kcand[sg.x + col - ko];
+            rseg = sb;
+          }
+          if (col >= co && col < co + sg.w) {
+            ci = ccand[sg.z + col - co];
+            if (f == 0) cgi = cgh[sg.z + col - co];
+            cseg = sb;
+          }
+          ko += sg.y;
+          co += sg.w;
         }
-      }
-      int jrep, p;
-      float c;
-      const int k0 = (tt - btile[sb]) * kKeyTile;
-      match_keys<T, D>(x, k0, jrep, p, c);
-      if (x.nk <= kKeyTile) {
-        // key q is reported by lane 16 (q >> 2) + (q & 3)
+        x.nk = ko;  // the tile's keys, for step 2
+        int jrep, p;
+        float c;
+        match_packed<T, D>(
+            x, jr, rseg, ci, cgi, cseg,
+            [&](int sb, const int32_t*& cl, const int32_t*& gl, int& n) {
+              const int4 sg = bseg[sb];
+              cl = ccand + sg.z;
+              gl = cgh + sg.z;
+              n = sg.w;
+            },
+            jrep, p, c);
+        // key q of the tile is reported by lane 16 (q >> 2) + (q & 3)
         const int self = col < 4 ? 4 * (lane >> 4) + col : -1;
         const bool win = resolve_keys<T, D>(
             x, self, col < 4 ? p : -1, c, jrep,
@@ -717,6 +837,18 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
         if (col < 4 && jrep >= 0) write(jrep, p, win);
         continue;
       }
+      int sb = 0;  // the large segment holding tile tt
+      while (btile[sb + 1] <= tt) ++sb;
+      const int4 sg = bseg[sb];
+      x.keys = kcand + sg.x;
+      x.nk = sg.y;
+      x.cands = ccand + sg.z;
+      x.cgs = cgh + sg.z;
+      x.nc = sg.w;
+      int jrep, p;
+      float c;
+      const int k0 = (tt - btile[sb]) * kKeyTile;
+      match_keys<T, D>(x, k0, jrep, p, c);
       const int kb = bkey[sb];
       if (col < 4 && jrep >= 0) {
         const int q = k0 + 4 * (lane >> 4) + col;
