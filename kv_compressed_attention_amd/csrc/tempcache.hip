@@ -888,6 +888,7 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
 // get the next group ids; ids from the capacity on are dropped (-1).
 __global__ __launch_bounds__(1024) void tc_number_kernel(int32_t* __restrict__ n_groups,
                                                          MergeArgs a) {
+  constexpr int kPerThread = 8;  // links loaded up front per thread and round
   __shared__ int wsum[16];
   __shared__ int running;
   const int h = blockIdx.x;
@@ -901,25 +902,37 @@ __global__ __launch_bounds__(1024) void tc_number_kernel(int32_t* __restrict__ n
   int32_t* gd = a.gid + frame_off(a, h, 0);
   if (tid == 0) running = 0;
   __syncthreads();
-  for (int base = 0; base < total; base += blockDim.x) {
-    const int idx = base + tid;
-    const bool isnew = idx < total && lk[idx] < 0;
-    const uint64_t bal = ballot64(isnew);
-    if (lane == 0) wsum[wave] = __popcll(bal);
-    __syncthreads();
-    int rank = running + __popcll(bal & lanemask_lt());
-    for (int w = 0; w < wave; ++w) rank += wsum[w];
-    if (isnew) {
-      const int64_t gg = (int64_t)ng0 + rank;
-      gd[idx] = gg < a.cap ? (int32_t)gg : -1;
+  for (int base0 = 0; base0 < total; base0 += kPerThread * blockDim.x) {
+    // the links of this round, all in flight together
+    int32_t l8[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int idx = base0 + u * blockDim.x + tid;
+      l8[u] = idx < total ? lk[idx] : 0;
     }
-    __syncthreads();
-    if (tid == 0) {
-      int sum = 0;
-      for (int w = 0; w < nw; ++w) sum += wsum[w];
-      running += sum;
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int base = base0 + u * blockDim.x;
+      if (base >= total) break;  // uniform
+      const int idx = base + tid;
+      const bool isnew = idx < total && l8[u] < 0;
+      const uint64_t bal = ballot64(isnew);
+      if (lane == 0) wsum[wave] = __popcll(bal);
+      __syncthreads();
+      int rank = running + __popcll(bal & lanemask_lt());
+      for (int w = 0; w < wave; ++w) rank += wsum[w];
+      if (isnew) {
+        const int64_t gg = (int64_t)ng0 + rank;
+        gd[idx] = gg < a.cap ? (int32_t)gg : -1;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int sum = 0;
+        for (int w = 0; w < nw; ++w) sum += wsum[w];
+        running += sum;
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
   if (tid == 0) {
     const int64_t ng = (int64_t)ng0 + running;
@@ -948,9 +961,20 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   if (idx >= (int64_t)a.F * a.Tf) return;
   int f = (int)(idx / a.Tf);
   int j = (int)(idx - (int64_t)f * a.Tf);
+  const T* kh = knew + (int64_t)h * k_sh + sub * EPL;
+  const T* vh = vnew + (int64_t)h * v_sh + sub * EPL;
+  const int32_t* kbh = kbucket + (int64_t)h * a.kb_stride;
+  // everything the token itself needs, in flight together: its link, the
+  // group it may open, its successor, its value and key rows and its bucket
   const int lk = a.link[frame_off(a, h, f) + j];
+  const int gd = a.gid[frame_off(a, h, f) + j];  // meaningful when lk < 0
+  int nx = f + 1 < a.F ? a.nextj[frame_off(a, h, f) + j] : -1;
+  float vv[EPL], kk[EPL];
+  Chunk<T, EPL>::load(vh + ((int64_t)f * a.Tf + j) * v_st, vv);
+  Chunk<T, EPL>::load(kh + ((int64_t)f * a.Tf + j) * k_st, kk);
+  int kb = kbh[(int64_t)f * a.Tf + j];
   if (lk >= 0 && f > 0) return;  // continuation of a chain that starts earlier
-  const int g = lk < 0 ? a.gid[frame_off(a, h, f) + j] : lk;
+  const int g = lk < 0 ? gd : lk;
   auto member = [&](int ff, int jj) {
     if (sub != 0) return;
     if (group_of_new) group_of_new[(int64_t)h * a.kb_stride + (int64_t)ff * a.Tf + jj] = g;
@@ -960,45 +984,40 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   member(f, j);
   if (g < 0) {
     // no room: the whole chain is left out
-    while (f + 1 < a.F) {
-      const int nx = a.nextj[frame_off(a, h, f) + j];
-      if (nx < 0) break;
+    while (nx >= 0) {
       ++f;
       j = nx;
       member(f, j);
+      nx = f + 1 < a.F ? a.nextj[frame_off(a, h, f) + j] : -1;
     }
     return;
   }
   const int64_t gi = (int64_t)h * a.cap + g;
   float sum[EPL];
   int cnt;
-  {
-    float vv[EPL];
-    Chunk<T, EPL>::load(vnew + (int64_t)h * v_sh + ((int64_t)f * a.Tf + j) * v_st + sub * EPL, vv);
-    if (lk < 0) {
+  if (lk < 0) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sum[e] = vv[e];
-      cnt = 1;
-    } else {
-      const float* vs = v_sum + gi * D + sub * EPL;
+    for (int e = 0; e < EPL; ++e) sum[e] = vv[e];
+    cnt = 1;
+  } else {
+    const float* vs = v_sum + gi * D + sub * EPL;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sum[e] = vs[e] + vv[e];
-      cnt = count[gi] + 1;
-    }
+    for (int e = 0; e < EPL; ++e) sum[e] = vs[e] + vv[e];
+    cnt = count[gi] + 1;
   }
-  while (f + 1 < a.F) {
-    const int nx = a.nextj[frame_off(a, h, f) + j];
-    if (nx < 0) break;
+  // the successors: each hop loads the member's rows, bucket and successor at once
+  while (nx >= 0) {
     ++f;
     j = nx;
+    nx = f + 1 < a.F ? a.nextj[frame_off(a, h, f) + j] : -1;
+    Chunk<T, EPL>::load(vh + ((int64_t)f * a.Tf + j) * v_st, vv);
+    Chunk<T, EPL>::load(kh + ((int64_t)f * a.Tf + j) * k_st, kk);
+    kb = kbh[(int64_t)f * a.Tf + j];
     member(f, j);
-    float vv[EPL];
-    Chunk<T, EPL>::load(vnew + (int64_t)h * v_sh + ((int64_t)f * a.Tf + j) * v_st + sub * EPL, vv);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) sum[e] += vv[e];
     ++cnt;
   }
-  const T* kr = knew + (int64_t)h * k_sh + ((int64_t)f * a.Tf + j) * k_st + sub * EPL;
   T* rkr = rep_k + gi * D + sub * EPL;
   T* vmr = v_mean + gi * D + sub * EPL;
   float* vsr = v_sum + gi * D + sub * EPL;
@@ -1006,14 +1025,14 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     vsr[e] = sum[e];
-    rkr[e] = kr[e];
+    Elem<T>::store(rkr, e, kk[e]);  // the last key, exactly (stored values round-trip)
     if (cnt == 1) Elem<T>::store(vmr, e, sum[e]);  // exact copy of the value
     else Elem<T>::store(vmr, e, sum[e] / fc);
   }
   if (sub == 0) {
     count[gi] = cnt;
     log_count[gi] = logf(fc);
-    rep_bucket[gi] = kbucket[(int64_t)h * a.kb_stride + (int64_t)f * a.Tf + j];
+    rep_bucket[gi] = kb;
   }
 }
 
@@ -1046,8 +1065,9 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   const size_t index_lds = (size_t)2 * a.tsize * sizeof(int32_t) + (size_t)2 * Tf * sizeof(int16_t);
   hipLaunchKernelGGL(tc_index_kernel, dim3(F + 1, H), dim3(1024), index_lds, s, c.frontier,
                      c.rep_bucket, c.n_groups, kb, a);
-  // up to 256 waves per (frame, head), each looping over that frame's segments
-  const unsigned mx = (unsigned)std::min(64, (Tf + 3) / 4);
+  // about one workgroup per 64 tokens of a frame, each taking a round of
+  // segments at a time
+  const unsigned mx = (unsigned)std::max(1, std::min(64, Tf / 64));
   hipLaunchKernelGGL((tc_match_kernel<T, D>), dim3(mx, (unsigned)H, (unsigned)F), dim3(256),
                      (size_t)3 * Tf * sizeof(int32_t), s,
                      (const T*)c.rep_k, (const T*)kn.data, kn.stride_head, kn.stride_token,
