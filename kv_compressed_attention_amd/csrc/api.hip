@@ -148,11 +148,11 @@ fastar_status_t fastar_bucket_index(const int32_t* bucket, int heads, int64_t n,
 // ---------------------------------------------------------------------------
 size_t fastar_tempcache_workspace(const fastar_cache_t* c, int n_frames) {
   if (!c || n_frames < 0 || c->heads < 0 || c->tokens_per_frame < 0 || c->capacity < 0) return 0;
+  if (c->n_bits < 0 || c->n_bits > 15) return 0;
   const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
-  const size_t ts = (size_t)fastar::tempcache_table_size(c->tokens_per_frame);
-  return align_up(16 * H * (F + 1) * ts) + align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
-         align_up(16 * H * F * T) + align_up(4 * H * F) + 3 * align_up(4 * H * F * T) +
-         align_up(16 * H * (size_t)c->capacity);
+  const size_t nb = ((size_t)1 << c->n_bits) + 1;
+  return align_up(4 * H * (F + 1) * nb) + 2 * align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
+         3 * align_up(4 * H * F * T) + align_up(16 * H * (size_t)c->capacity);
 }
 
 fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
@@ -205,7 +205,7 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
     return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu",
                 fastar_tempcache_workspace(c, n_frames), ws_bytes);
   const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
-  const size_t ts = (size_t)fastar::tempcache_table_size(c->tokens_per_frame);
+  const size_t nb = ((size_t)1 << c->n_bits) + 1;
   char* w = (char*)ws;
   auto take = [&](size_t bytes) {
     char* p = w;
@@ -213,11 +213,10 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
     return (int32_t*)p;
   };
   fastar::MergeWs mw;
-  mw.tab = (int4*)take(16 * H * (F + 1) * ts);
-  mw.cand = take(4 * H * (F + 1) * T);
+  mw.off = take(4 * H * (F + 1) * nb);
+  mw.tok = take(4 * H * (F + 1) * T);
+  mw.tbk = take(4 * H * (F + 1) * T);
   mw.candg = take(4 * H * T);
-  mw.srec = (int4*)take(16 * H * F * T);
-  mw.nseg = take(4 * H * F);
   mw.link = take(4 * H * F * T);
   mw.gid = take(4 * H * F * T);
   mw.nextj = take(4 * H * F * T);

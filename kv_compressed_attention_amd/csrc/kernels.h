@@ -37,17 +37,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // tempcache.hip -------------------------------------------------------------
 struct MergeWs {
-  int4* tab;          // [H][n_frames+1][tsize] bucket tables (see tempcache.hip)
-  int32_t* cand;      // [H][n_frames+1][T]
+  int32_t* off;       // [H][n_frames+1][2^b+1] bucket offsets per table (see tempcache.hip)
+  int32_t* tok;       // [H][n_frames+1][T] tokens sorted by bucket
+  int32_t* tbk;       // [H][n_frames+1][T] their buckets
   int32_t* candg;     // [H][T]
-  int4* srec;         // [H][n_frames][T]
-  int32_t* nseg;      // [H][n_frames]
   int32_t* link;      // [H][n_frames][T]
   int32_t* gid;       // [H][n_frames][T]
   int32_t* nextj;     // [H][n_frames][T]
   int32_t* index_ws;  // bucket index scratch
 };
-int tempcache_table_size(int tokens_per_frame);
 hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
                                   const fastar_tensor_t& v_new, const int32_t* k_new_bucket,
                                   int n_frames, float tau, int32_t* group_of_new,

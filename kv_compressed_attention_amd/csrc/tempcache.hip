@@ -9,14 +9,15 @@
 // one-to-one resolution of all frames are independent per (frame, bucket)
 // and run in one launch; only the numbering of new groups is sequential.
 // Five launches per call:
-//   tc_index    per (table, head): the frontier and each new frame grouped by
-//               bucket (LDS open-addressing table -> contiguous segments, and
-//               the list of occupied segments of each new frame);
-//   tc_match    one wave per (frame, bucket segment): cosines of the segment's
-//               keys with the candidates of the same bucket as 16 x 16 tiles
-//               (MFMA for bf16), best candidate per key, proposal if it passes
-//               tau, then per candidate the proposer of largest cosine (ties:
-//               smaller j) wins and links to it; the other keys open groups;
+//   tc_index    per (table, head): the frontier and each new frame sorted by
+//               bucket (counting sort in LDS: bucket offsets, tokens, buckets);
+//   tc_match    one workgroup per 64 sorted keys of a frame, rounded to whole
+//               buckets: cosines of 16 consecutive keys with the candidates of
+//               their buckets as 16 x 16 tiles (MFMA for bf16; pairs of
+//               different buckets masked), best candidate per key, proposal if
+//               it passes tau; then per candidate the proposer of largest
+//               cosine (ties: smaller j) wins and links to it; the other keys
+//               open groups;
 //   tc_number   one workgroup per head: new groups numbered in (frame, j)
 //               order, the group count;
 //   tc_apply    16 lanes per chain of tokens (a token that opens a group or
@@ -132,116 +133,92 @@ struct Top2 {
   }
 };
 
-__device__ __forceinline__ uint32_t slot_hash(int b, uint32_t mask) {
-  return ((uint32_t)b * 2654435761u >> 7) & mask;
-}
-
 // keys are matched in tiles of this many (one wave each)
 constexpr int kKeyTile = 16;
+// sorted keys per match workgroup (before rounding to whole buckets)
+constexpr int kKeysPerGroup = 64;
 
-// Groups Tf tokens by bucket for one head.  get(i, b, g) gives token i's
-// bucket and group (g < 0: token left out).  Writes cand (tokens, bucket
-// segments contiguous), optionally candg (their groups), the open-addressing
-// table tab (slot -> {bucket + 1 (0: empty), segment start, length, 0}) and,
-// optionally, the segment records srec ({bucket, start, length, 0}, in no
-// particular order) and their number (*nseg).  Whole workgroup; lds must
-// hold 2 * tsize int32 + 2 * Tf int16.
+// Sorts up to 2048 tokens of one head by bucket (whole workgroup of 1024
+// threads).  get(i, b, g) gives token i's bucket and group (g < 0: left out).
+// Writes off[0 .. 2^nbits] (bucket starts, then the number kept), tok (the
+// kept tokens, bucket by bucket; within a bucket in no particular order), tbk
+// (their buckets) and, if candg is given, their groups.  lds holds 2^nbits
+// int32.
 template <typename Get>
-__device__ void group_by_bucket(int Tf, int tsize, Get get, int32_t* lds, int4* tab, int32_t* cand,
-                                int32_t* candg, int4* srec, int32_t* nseg) {
-  int32_t* skey = lds;
-  int32_t* scnt = skey + tsize;
-  int16_t* slot_of = reinterpret_cast<int16_t*>(scnt + tsize);
-  int16_t* pos_of = slot_of + Tf;
+__device__ void csr_build(int Tf, int nbits, Get get, int32_t* lds, int32_t* off, int32_t* tok,
+                          int32_t* tbk, int32_t* candg) {
+  constexpr int kPer = 2;  // tokens per thread: Tf <= 2048
   __shared__ int wtot[16];
-  __shared__ int nsg;
-  const uint32_t mask = (uint32_t)tsize - 1u;
+  const int nb = 1 << nbits;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  for (int s = tid; s < tsize; s += nthr) {
-    skey[s] = 0;
-    scnt[s] = 0;
-  }
-  if (tid == 0) nsg = 0;
-  __syncthreads();
-  for (int i = tid; i < Tf; i += nthr) {
-    int b, g;
-    get(i, b, g);
-    if (g < 0) {
-      slot_of[i] = -1;
-      continue;
-    }
-    uint32_t slot = slot_hash(b, mask);
-    while (true) {
-      const int w = skey[slot];
-      if (w == b + 1) break;
-      if (w == 0) {
-        const int old = atomicCAS(&skey[slot], 0, b + 1);
-        if (old == 0 || old == b + 1) break;
-      } else {
-        slot = (slot + 1u) & mask;
-      }
-    }
-    slot_of[i] = (int16_t)slot;
-    pos_of[i] = (int16_t)atomicAdd(&scnt[slot], 1);
+  for (int s = tid; s < nb; s += nthr) lds[s] = 0;
+  int bb[kPer], gg[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * nthr;
+    bb[u] = 0;
+    gg[u] = -1;
+    if (i < Tf) get(i, bb[u], gg[u]);
   }
   __syncthreads();
-  // exclusive scan of the segment lengths over the slots
-  const int per = (tsize + nthr - 1) / nthr;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (gg[u] >= 0) atomicAdd(&lds[bb[u]], 1);
+  __syncthreads();
+  // exclusive scan of the counts (per consecutive buckets per thread)
+  const int per = (nb + nthr - 1) / nthr;
   const int s0 = tid * per;
   int local = 0;
-  for (int s = s0; s < s0 + per && s < tsize; ++s) local += scnt[s];
+  for (int s = s0; s < s0 + per && s < nb; ++s) local += lds[s];
   const int lane = lane_id(), wave = tid >> 6;
   int incl = local;
 #pragma unroll
-  for (int off = 1; off < FASTAR_WAVE; off <<= 1) {
-    const int y = __shfl_up(incl, off, FASTAR_WAVE);
-    if (lane >= off) incl += y;
+  for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
+    const int y = __shfl_up(incl, o, FASTAR_WAVE);
+    if (lane >= o) incl += y;
   }
   if (lane == FASTAR_WAVE - 1) wtot[wave] = incl;
   __syncthreads();
   int run = incl - local;
   for (int w = 0; w < wave; ++w) run += wtot[w];
-  for (int s = s0; s < s0 + per && s < tsize; ++s) {
-    const int c = scnt[s];
-    tab[s] = make_int4(skey[s], run, c, 0);
-    if (srec && c > 0) srec[atomicAdd(&nsg, 1)] = make_int4(skey[s] - 1, run, c, 0);
-    scnt[s] = run;  // segment start, for the fill below
+  for (int s = s0; s < s0 + per && s < nb; ++s) {
+    const int c = lds[s];
+    off[s] = run;
+    lds[s] = run;  // the bucket's cursor for the fill below
     run += c;
   }
+  if (tid == nthr - 1) off[nb] = run;
   __syncthreads();
-  if (nseg && tid == 0) *nseg = nsg;
-  for (int i = tid; i < Tf; i += nthr) {
-    const int slot = slot_of[i];
-    if (slot < 0) continue;
-    int b, g;
-    get(i, b, g);
-    const int k = scnt[slot] + pos_of[i];
-    cand[k] = i;
-    if (candg) candg[k] = g;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    if (gg[u] < 0) continue;
+    const int k = atomicAdd(&lds[bb[u]], 1);
+    tok[k] = tid + u * nthr;
+    tbk[k] = bb[u];
+    if (candg) candg[k] = gg[u];
   }
 }
 
 struct MergeArgs {
-  int H, Tf, cap, F, tsize;
+  int H, Tf, cap, F, nbits;
   int64_t kb_stride;  // F * Tf
-  // per-head tables t = 0..F: table 0 indexes the cache's last frame (the
-  // frontier), table f + 1 indexes new frame f, each by bucket
-  int4* tab;          // [H][F+1][tsize] {bucket + 1 (0: empty), start in cand, length, 0}
-  int32_t* cand;      // [H][F+1][Tf] token indices, bucket segments contiguous
+  // per head, tables t = 0..F sorted by bucket: table 0 holds the cache's
+  // last frame (the frontier), table f + 1 new frame f
+  int32_t* off;       // [H][F+1][2^b + 1] bucket starts, then the number kept
+  int32_t* tok;       // [H][F+1][Tf] tokens, bucket by bucket
+  int32_t* tbk;       // [H][F+1][Tf] their buckets
   int32_t* candg;     // [H][Tf] groups of table 0's tokens
-  int4* srec;         // [H][F][Tf] segments of table f + 1: {bucket, start, length, 0}
-  int32_t* nseg;      // [H][F] their number
   int32_t* link;      // [H][F][Tf] f = 0: frontier group the token extends;
                       //            f > 0: frame f - 1 token it extends; -1: opens a group
   int32_t* gid;       // [H][F][Tf] group a token opens (-1: no room left)
   int32_t* nextj;     // [H][F][Tf] token of frame f + 1 that extends this one, or -1
 };
 
-__device__ __forceinline__ int64_t tab_off(const MergeArgs& a, int h, int t) {
-  return ((int64_t)h * (a.F + 1) + t) * a.tsize;
+__device__ __forceinline__ int64_t off_off(const MergeArgs& a, int h, int t) {
+  return ((int64_t)h * (a.F + 1) + t) * ((1 << a.nbits) + 1);
 }
-__device__ __forceinline__ int64_t cand_off(const MergeArgs& a, int h, int t) {
+__device__ __forceinline__ int64_t tok_off(const MergeArgs& a, int h, int t) {
   return ((int64_t)h * (a.F + 1) + t) * a.Tf;
 }
 __device__ __forceinline__ int64_t frame_off(const MergeArgs& a, int h, int f) {
@@ -256,30 +233,31 @@ __global__ __launch_bounds__(1024) void tc_index_kernel(
   extern __shared__ int32_t lds[];
   const int h = blockIdx.y;
   const int t = blockIdx.x;
-  int4* tb = a.tab + tab_off(a, h, t);
-  int32_t* cd = a.cand + cand_off(a, h, t);
+  int32_t* off = a.off + off_off(a, h, t);
+  int32_t* tok = a.tok + tok_off(a, h, t);
+  int32_t* tbk = a.tbk + tok_off(a, h, t);
   if (t == 0) {
     const bool empty = n_groups[h] <= 0;
     const int32_t* fr = frontier + (int64_t)h * a.Tf;
     const int32_t* rb = rep_bucket + (int64_t)h * a.cap;
-    group_by_bucket(
-        a.Tf, a.tsize,
+    csr_build(
+        a.Tf, a.nbits,
         [&](int i, int& b, int& g) {
           g = empty ? -1 : fr[i];
           b = g >= 0 ? rb[g] : 0;
         },
-        lds, tb, cd, a.candg + (int64_t)h * a.Tf, nullptr, nullptr);
+        lds, off, tok, tbk, a.candg + (int64_t)h * a.Tf);
   } else {
     const int f = t - 1;
     const int32_t* kb = kbucket + (int64_t)h * a.kb_stride + (int64_t)f * a.Tf;
     for (int i = threadIdx.x; i < a.Tf; i += blockDim.x) a.nextj[frame_off(a, h, f) + i] = -1;
-    group_by_bucket(
-        a.Tf, a.tsize,
+    csr_build(
+        a.Tf, a.nbits,
         [&](int i, int& b, int& g) {
           b = kb[i];
           g = 0;
         },
-        lds, tb, cd, nullptr, a.srec + frame_off(a, h, f), a.nseg + (int64_t)h * a.F + f);
+        lds, off, tok, tbk, nullptr);
   }
 }
 
@@ -430,25 +408,20 @@ __device__ double wave_cos64(const T* x, const T* y) {
   return s / sqrt(na * nb);
 }
 
-// What one wave needs to match the keys of one (frame, bucket) segment.
+// What one wave needs to match keys of new frame f.
 template <typename T, int D>
 struct SegCtx {
   const T* kf;          // frame f keys
   const T* kp;          // frame f - 1 keys (f > 0)
   const T* rk;          // the head's representatives
   int64_t k_st;
-  const int32_t* keys;  // the segment's key tokens (nk)
-  const int32_t* cands; // the bucket's candidate tokens (nc)
-  const int32_t* cgs;   // their groups (f == 0)
-  int nk, nc, f;
+  int nk, f;            // keys that step 2 compares; the frame
   float tau, e;
   fastar_diag_t* diag;
-  __device__ __forceinline__ const T* cand_row(int k, int i, int gr) const {
+  // candidate row: the frontier group's representative (f == 0), else the
+  // frame f - 1 key
+  __device__ __forceinline__ const T* cand_row(int, int i, int gr) const {
     return f == 0 ? rk + (int64_t)gr * D : kp + (int64_t)i * k_st;
-  }
-  // candidate row by position in the bucket (for the float64 paths)
-  __device__ __forceinline__ const T* cand_row_at(int k) const {
-    return cand_row(k, cands[k], f == 0 ? cgs[k] : 0);
   }
 };
 
@@ -524,94 +497,74 @@ __device__ __forceinline__ Top2<float> reduce_top2(Top2<float>* t) {
   return m;
 }
 
-// Step 1 for keys k0 .. k0 + 15 of a segment (whole wave).  The lane with
-// (l & 15) < 4 reports key r = 4 (l >> 4) + (l & 3): jrep (its token, -1: no
-// such key), p (the candidate token it proposes to, -1: none) and c (the
+// Step 1 for keys k0 .. k0 + 15 of the bucket-sorted key table (whole wave;
+// keys past kend are empty).  Their candidates are the candidate table's
+// positions [c_lo, c_hi), the buckets from the first key's to the last key's;
+// a (key, candidate) cosine counts only when their buckets agree.  The lane
+// with (l & 15) < 4 reports key r = 4 (l >> 4) + (l & 3): jrep (its token,
+// -1: none), p (the candidate token it proposes to, -1: none) and c (the
 // cosine).  Candidates are visited in tiles of 16, the next tile's rows
 // loading while the current one is used.
 template <typename T, int D>
-__device__ __forceinline__ void match_keys(const SegCtx<T, D>& x, int k0, int& jrep, int& p,
-                                           float& c) {
+__device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t* ktok,
+                                           const int32_t* kbk, int k0, int kend,
+                                           const int32_t* ctok, const int32_t* cbk,
+                                           const int32_t* cg, const int32_t* coff, int c_lo,
+                                           int c_hi, int& jrep, int& p, float& c) {
   using TD = TileDot<T, D>;
   const int lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
-  const int jr = k0 + col < x.nk ? x.keys[k0 + col] : -1;  // this lane's key row
+  const bool kv = k0 + col < kend;
+  const int jr = kv ? ktok[k0 + col] : -1;  // this lane's key row
+  const int rb = kv ? kbk[k0 + col] : -1;   // and its bucket
   jrep = __shfl(jr, 4 * g + (col & 3), FASTAR_WAVE);
   p = -1;
   c = 0.f;
-  if (x.nc == 0) return;
+  if (c_hi <= c_lo) return;
   const bool own = col < 4 && jrep >= 0;
+  int kb4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kb4[i] = __shfl(rb, 4 * g + i, FASTAR_WAVE);
   // candidate ids of the first tile, with the key rows
-  bool cv = col < x.nc;
-  int ci = cv ? x.cands[col] : 0;
-  int cgi = (cv && x.f == 0) ? x.cgs[col] : 0;
+  bool cv = c_lo + col < c_hi;
+  int ci = cv ? ctok[c_lo + col] : 0;
+  int cb = cv ? cbk[c_lo + col] : -2;
+  int cgi = (cv && x.f == 0) ? cg[c_lo + col] : 0;
   TD td;
   td.issue_keys(jr >= 0 ? x.kf + (int64_t)jr * x.k_st : nullptr);
-  typename TD::Rows cr = TD::issue(cv ? x.cand_row(col, ci, cgi) : nullptr);
+  typename TD::Rows cr = TD::issue(cv ? x.cand_row(0, ci, cgi) : nullptr);
   td.finish_keys();
   Top2<float> t[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) t[i].init();
-  for (int c0 = 0; c0 < x.nc; c0 += 16) {
+  for (int c0 = c_lo; c0 < c_hi; c0 += 16) {
     // next tile's ids, then this tile's dots, then the next tile's rows
-    const bool nv = c0 + 16 + col < x.nc;
-    const int ni = nv ? x.cands[c0 + 16 + col] : 0;
-    const int ng = (nv && x.f == 0) ? x.cgs[c0 + 16 + col] : 0;
+    const bool nv = c0 + 16 + col < c_hi;
+    const int ni = nv ? ctok[c0 + 16 + col] : 0;
+    const int nb = nv ? cbk[c0 + 16 + col] : -2;
+    const int ng = (nv && x.f == 0) ? cg[c0 + 16 + col] : 0;
     float sd[4], cn;
     td.dots(cr, sd, cn);
     if (cv) {
       const float rc = cn > 0.f ? rsqrtf(cn) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t[i].add(td.kn[i] > 0.f ? sd[i] * rsqrtf(td.kn[i]) * rc : 0.f, ci);
+      for (int i = 0; i < 4; ++i)
+        if (kb4[i] == cb) t[i].add(td.kn[i] > 0.f ? sd[i] * rsqrtf(td.kn[i]) * rc : 0.f, ci);
     }
-    if (c0 + 16 < x.nc) cr = TD::issue(nv ? x.cand_row(c0 + 16 + col, ni, ng) : nullptr);
+    if (c0 + 16 < c_hi) cr = TD::issue(nv ? x.cand_row(0, ni, ng) : nullptr);
     cv = nv;
     ci = ni;
-  }
-  const Top2<float> m = reduce_top2(t);
-  decide<T, D>(x, m, own, jrep,
-               [&](int, const int32_t*& cl, const int32_t*& gl, int& n) {
-                 cl = x.cands;
-                 gl = x.cgs;
-                 n = x.nc;
-               },
-               p, c);
-}
-
-// Step 1 for a packed tile: up to 16 keys and 16 candidates of several small
-// segments (row / column r belongs to segment rseg / cseg, -1: empty), one
-// MFMA tile with the cosines across segments masked out.  Reports as
-// match_keys; seg_cands(s, list, groups, n) gives segment s's candidates.
-template <typename T, int D, typename SegCands>
-__device__ __forceinline__ void match_packed(const SegCtx<T, D>& x, int jr, int rseg, int ci,
-                                             int cgi, int cseg, SegCands seg_cands, int& jrep,
-                                             int& p, float& c) {
-  using TD = TileDot<T, D>;
-  const int lane = lane_id();
-  const int g = lane >> 4, col = lane & 15;
-  const int r = 4 * g + (col & 3);
-  jrep = __shfl(jr, r, FASTAR_WAVE);
-  const bool own = col < 4 && jrep >= 0;
-  TD td;
-  td.issue_keys(jr >= 0 ? x.kf + (int64_t)jr * x.k_st : nullptr);
-  typename TD::Rows cr = TD::issue(cseg >= 0 ? x.cand_row(col, ci, cgi) : nullptr);
-  td.finish_keys();
-  Top2<float> t[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) t[i].init();
-  float sd[4], cn;
-  td.dots(cr, sd, cn);
-  const float rc = cn > 0.f ? rsqrtf(cn) : 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ks = __shfl(rseg, 4 * g + i, FASTAR_WAVE);
-    if (cseg >= 0 && ks == cseg) t[i].add(td.kn[i] > 0.f ? sd[i] * rsqrtf(td.kn[i]) * rc : 0.f, ci);
+    cb = nb;
   }
   const Top2<float> m = reduce_top2(t);
   decide<T, D>(x, m, own, jrep,
                [&](int src, const int32_t*& cl, const int32_t*& gl, int& n) {
-                 const int rs = 4 * (src >> 4) + (src & 3);
-                 seg_cands(__shfl(rseg, rs, FASTAR_WAVE), cl, gl, n);
+                 // the key's own bucket
+                 const int b = __shfl(rb, 4 * (src >> 4) + (src & 3), FASTAR_WAVE);
+                 const int s = coff[b];
+                 cl = ctok + s;
+                 gl = cg + s;
+                 n = coff[b + 1] - s;
                },
                p, c);
 }
@@ -663,39 +616,42 @@ __device__ __forceinline__ bool resolve_keys(const SegCtx<T, D>& x, int self, in
   return win;
 }
 
-// segments a workgroup takes per round
-constexpr int kSegBatch = 64;
-
-// Workgroup b of (frame f, head h) takes the segments s = b, b + gridDim.x, ..
-// of new frame f, kSegBatch at a time.  Segments of at most 16 keys and 16
-// candidates are packed greedily into shared 16 x 16 tiles; larger ones are
-// cut into tiles of 16 keys.  The waves share the tiles.  Step 1 (per tile)
-// finds each key's best candidate and its proposal.  Step 2 lets every
-// candidate keep its best proposer (ties: smaller j), which links to it; the
-// other keys open groups.  A tile that holds whole segments does step 2 in
-// registers; in a larger segment every tile leaves its proposals in LDS, and
-// the wave that completes the segment's last tile does step 2 for all of it.
+// One workgroup per kKeysPerGroup positions of frame f's bucket-sorted keys,
+// rounded to whole buckets: a workgroup owns the buckets whose first key lies
+// in its positions.  Its waves take the tiles of 16 consecutive keys (step 1,
+// each key's best candidate and proposal), then, after one barrier, step 2
+// over all of its keys: every candidate keeps its best proposer (ties:
+// smaller j), which links to it; the other keys open groups.  A candidate's
+// proposers all share its bucket, so they are all in the workgroup.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tc_match_kernel(
     const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
-    const int32_t* __restrict__ frontier, const int32_t* __restrict__ n_groups, float tau,
-    MergeArgs a, fastar_diag_t* __restrict__ diag) {
-  extern __shared__ int32_t lds[];  // [3][Tf] proposals of multi-tile segments
-  __shared__ int4 bseg[kSegBatch];  // {key start, keys, candidate start, candidates}
-  __shared__ int btile[kSegBatch + 1], bkey[kSegBatch + 1], bdone[kSegBatch];
-  __shared__ int porder[kSegBatch], pstart[kSegBatch + 1];
-  __shared__ int npacked;
+    const int32_t* __restrict__ frontier, float tau, MergeArgs a,
+    fastar_diag_t* __restrict__ diag) {
+  extern __shared__ int32_t lds[];  // [3][Tf] the workgroup's proposals
   const int h = blockIdx.y;
   const int f = blockIdx.z;
   const int lane = lane_id();
   const int col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nb = 1 << a.nbits;
+  const int32_t* koff = a.off + off_off(a, h, f + 1);
+  const int32_t* ktok = a.tok + tok_off(a, h, f + 1);
+  const int32_t* kbk = a.tbk + tok_off(a, h, f + 1);
+  const int32_t* coff = a.off + off_off(a, h, f);
+  const int32_t* ctok = a.tok + tok_off(a, h, f);
+  const int32_t* cbk = a.tbk + tok_off(a, h, f);
+  const int32_t* cg = a.candg + (int64_t)h * a.Tf;
+  // the owned key positions [p0, p1)
+  const int nkt = koff[nb];
+  int p0 = blockIdx.x * kKeysPerGroup;
+  if (p0 >= nkt) return;
+  int p1 = min(p0 + kKeysPerGroup, nkt);
+  if (p0 > 0 && kbk[p0 - 1] == kbk[p0]) p0 = koff[kbk[p0] + 1];
+  if (p1 < nkt && kbk[p1 - 1] == kbk[p1]) p1 = koff[kbk[p1] + 1];
+  if (p0 >= p1) return;  // the whole workgroup: no barrier is reached
+  const int nk = p1 - p0;
   const int64_t fo = frame_off(a, h, f);
-  const int nseg = a.nseg[(int64_t)h * a.F + f];
-  const int4* srec = a.srec + fo;
-  const bool have_c = f > 0 || n_groups[h] > 0;
-  const uint32_t mask = (uint32_t)a.tsize - 1u;
-  const int4* ctab = a.tab + tab_off(a, h, f);
   const int32_t* fr = frontier + (int64_t)h * a.Tf;
   int32_t* lp = lds;
   float* lc = reinterpret_cast<float*>(lds + a.Tf);
@@ -709,178 +665,43 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
   x.tau = tau;
   x.e = match_err<T, D>();
   x.diag = diag;
-  const int32_t* kcand = a.cand + cand_off(a, h, f + 1);
-  const int32_t* ccand = a.cand + cand_off(a, h, f);
-  const int32_t* cgh = a.candg + (int64_t)h * a.Tf;
-  auto write = [&](int j, int p, bool win) {
-    int lk = -1;
-    if (win) {
-      lk = f == 0 ? fr[p] : p;
-      if (f > 0) a.nextj[frame_off(a, h, f - 1) + p] = j;
+  x.nk = nk;
+  for (int k0 = p0 + wave * kKeyTile; k0 < p1; k0 += 4 * kKeyTile) {
+    const int klast = min(k0 + kKeyTile, p1) - 1;
+    const int c_lo = coff[kbk[k0]], c_hi = coff[kbk[klast] + 1];
+    int jrep, p;
+    float c;
+    match_tile<T, D>(x, ktok, kbk, k0, p1, ctok, cbk, cg, coff, c_lo, c_hi, jrep, p, c);
+    if (col < 4 && jrep >= 0) {
+      const int q = k0 - p0 + 4 * (lane >> 4) + col;
+      lp[q] = p;
+      lc[q] = c;
+      lj[q] = jrep;
     }
-    a.link[fo + j] = lk;
-  };
-  auto small = [](const int4& sg) { return sg.y <= 16 && sg.w <= 16; };
-  const int stride = (int)gridDim.x;
-  for (int k0b = 0; blockIdx.x + k0b * stride < nseg; k0b += kSegBatch) {
-    // the batch (wave 0): segments with their candidate ranges, tiles of the
-    // large ones, and the packing of the small ones
-    if (wave == 0) {
-      const int sidx = blockIdx.x + (k0b + lane) * stride;
-      const bool sv = lane < kSegBatch && sidx < nseg;
-      int4 sg = make_int4(0, 0, 0, 0);
-      if (sv) {
-        const int4 r = srec[sidx];
-        sg = make_int4(r.y, r.z, 0, 0);
-        if (have_c) {
-          uint32_t sl = slot_hash(r.x, mask);
-          int4 tb;
-          while ((tb = ctab[sl]).x != 0 && tb.x != r.x + 1) sl = (sl + 1u) & mask;
-          if (tb.x != 0) {
-            sg.z = tb.y;
-            sg.w = tb.z;
-          }
-        }
+  }
+  __syncthreads();
+  for (int q0 = wave * FASTAR_WAVE; q0 < nk; q0 += 4 * FASTAR_WAVE) {
+    const int q = q0 + lane;
+    const bool v = q < nk;
+    const int pj = v ? lp[q] : -1;
+    const float cj = v ? lc[q] : 0.f;
+    const int j = v ? lj[q] : -1;
+    const bool win = resolve_keys<T, D>(
+        x, q, pj, cj, j,
+        [&](int q2, int& p2, float& c2, int& j2) {
+          p2 = lp[q2];
+          c2 = lc[q2];
+          j2 = lj[q2];
+        },
+        fr);
+    if (v) {
+      int lk = -1;
+      if (win) {
+        lk = f == 0 ? fr[pj] : pj;
+        if (f > 0) a.nextj[frame_off(a, h, f - 1) + pj] = j;
       }
-      const bool big = sv && !small(sg);
-      int nt = big ? (sg.y + kKeyTile - 1) / kKeyTile : 0, nk = big ? sg.y : 0;
-#pragma unroll
-      for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
-        const int t = __shfl_up(nt, o, FASTAR_WAVE);
-        const int k = __shfl_up(nk, o, FASTAR_WAVE);
-        if (lane >= o) {
-          nt += t;
-          nk += k;
-        }
-      }
-      if (lane < kSegBatch) {
-        bseg[lane] = sg;
-        btile[lane + 1] = nt;
-        bkey[lane + 1] = nk;
-        bdone[lane] = 0;
-      }
-      // greedy packing in batch order (wave-uniform scalar walk)
-      const uint64_t smask = ballot64(sv && !big);
-      int ku = 0, cu = 0, pos = 0, npt = 0;
-      for (int sb = 0; sb < kSegBatch; ++sb) {
-        if (!((smask >> sb) & 1ull)) continue;
-        const int kn = __builtin_amdgcn_readlane(sg.y, sb);
-        const int cn = __builtin_amdgcn_readlane(sg.w, sb);
-        if (ku + kn > 16 || cu + cn > 16) {
-          ++npt;
-          if (lane == 0) pstart[npt] = pos;
-          ku = 0;
-          cu = 0;
-        }
-        if (lane == 0) porder[pos] = sb;
-        ++pos;
-        ku += kn;
-        cu += cn;
-      }
-      if (pos > 0) ++npt;
-      if (lane == 0) {
-        btile[0] = 0;
-        bkey[0] = 0;
-        pstart[0] = 0;
-        pstart[npt] = pos;
-        npacked = npt;
-      }
+      a.link[fo + j] = lk;
     }
-    __syncthreads();
-    const int nbt = btile[kSegBatch];
-    const int nwork = nbt + npacked;
-    for (int tt = wave; tt < nwork; tt += 4) {
-      if (tt >= nbt) {
-        // a packed tile of whole small segments
-        const int pt = tt - nbt;
-        const int s0 = pstart[pt], s1 = pstart[pt + 1];
-        int jr = -1, rseg = -1, ci = 0, cgi = 0, cseg = -1;
-        int ko = 0, co = 0;
-        for (int q = s0; q < s1; ++q) {
-          const int sb = porder[q];
-          const int4 sg = bseg[sb];
-          if (col >= ko && col < ko + sg.y) {
-            jr = kcand[sg.x + col - ko];
-            rseg = sb;
-          }
-          if (col >= co && col < co + sg.w) {
-            ci = ccand[sg.z + col - co];
-            if (f == 0) cgi = cgh[sg.z + col - co];
-            cseg = sb;
-          }
-          ko += sg.y;
-          co += sg.w;
-        }
-        x.nk = ko;  // the tile's keys, for step 2
-        int jrep, p;
-        float c;
-        match_packed<T, D>(
-            x, jr, rseg, ci, cgi, cseg,
-            [&](int sb, const int32_t*& cl, const int32_t*& gl, int& n) {
-              const int4 sg = bseg[sb];
-              cl = ccand + sg.z;
-              gl = cgh + sg.z;
-              n = sg.w;
-            },
-            jrep, p, c);
-        // key q of the tile is reported by lane 16 (q >> 2) + (q & 3)
-        const int self = col < 4 ? 4 * (lane >> 4) + col : -1;
-        const bool win = resolve_keys<T, D>(
-            x, self, col < 4 ? p : -1, c, jrep,
-            [&](int q2, int& p2, float& c2, int& j2) {
-              const int src = 16 * (q2 >> 2) + (q2 & 3);
-              p2 = __shfl(p, src, FASTAR_WAVE);
-              c2 = __shfl(c, src, FASTAR_WAVE);
-              j2 = __shfl(jrep, src, FASTAR_WAVE);
-            },
-            fr);
-        if (col < 4 && jrep >= 0) write(jrep, p, win);
-        continue;
-      }
-      int sb = 0;  // the large segment holding tile tt
-      while (btile[sb + 1] <= tt) ++sb;
-      const int4 sg = bseg[sb];
-      x.keys = kcand + sg.x;
-      x.nk = sg.y;
-      x.cands = ccand + sg.z;
-      x.cgs = cgh + sg.z;
-      x.nc = sg.w;
-      int jrep, p;
-      float c;
-      const int k0 = (tt - btile[sb]) * kKeyTile;
-      match_keys<T, D>(x, k0, jrep, p, c);
-      const int kb = bkey[sb];
-      if (col < 4 && jrep >= 0) {
-        const int q = k0 + 4 * (lane >> 4) + col;
-        lp[kb + q] = p;
-        lc[kb + q] = c;
-        lj[kb + q] = jrep;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-      int done = 0;
-      if (lane == 0) done = atomicAdd(&bdone[sb], 1);
-      done = __shfl(done, 0, FASTAR_WAVE);
-      if (done != btile[sb + 1] - btile[sb] - 1) continue;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      // the segment's last tile: step 2 for all of it
-      for (int q0 = 0; q0 < x.nk; q0 += FASTAR_WAVE) {
-        const int q = q0 + lane;
-        const bool v = q < x.nk;
-        const int pj = v ? lp[kb + q] : -1;
-        const float cj = v ? lc[kb + q] : 0.f;
-        const int j = v ? lj[kb + q] : -1;
-        const bool win = resolve_keys<T, D>(
-            x, q, pj, cj, j,
-            [&](int q2, int& p2, float& c2, int& j2) {
-              p2 = lp[kb + q2];
-              c2 = lc[kb + q2];
-              j2 = lj[kb + q2];
-            },
-            fr);
-        if (v) write(j, pj, win);
-      }
-    }
-    __syncthreads();
   }
 }
 
@@ -1036,12 +857,6 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   }
 }
 
-int table_size(int Tf) {
-  int t = 16;
-  while (t < 2 * Tf) t <<= 1;
-  return t;
-}
-
 template <typename T, int D>
 hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fastar_tensor_t& vn,
                     const int32_t* kb, int F, float tau, int32_t* group_of_new, int32_t* rep_offsets,
@@ -1052,26 +867,22 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   a.Tf = Tf;
   a.cap = c.capacity;
   a.F = F;
-  a.tsize = table_size(Tf);
+  a.nbits = c.n_bits;
   a.kb_stride = (int64_t)F * Tf;
-  a.tab = ws.tab;
-  a.cand = ws.cand;
+  a.off = ws.off;
+  a.tok = ws.tok;
+  a.tbk = ws.tbk;
   a.candg = ws.candg;
-  a.srec = ws.srec;
-  a.nseg = ws.nseg;
   a.link = ws.link;
   a.gid = ws.gid;
   a.nextj = ws.nextj;
-  const size_t index_lds = (size_t)2 * a.tsize * sizeof(int32_t) + (size_t)2 * Tf * sizeof(int16_t);
-  hipLaunchKernelGGL(tc_index_kernel, dim3(F + 1, H), dim3(1024), index_lds, s, c.frontier,
-                     c.rep_bucket, c.n_groups, kb, a);
-  // about one workgroup per 64 tokens of a frame, each taking a round of
-  // segments at a time
-  const unsigned mx = (unsigned)std::max(1, std::min(64, Tf / 64));
-  hipLaunchKernelGGL((tc_match_kernel<T, D>), dim3(mx, (unsigned)H, (unsigned)F), dim3(256),
-                     (size_t)3 * Tf * sizeof(int32_t), s,
-                     (const T*)c.rep_k, (const T*)kn.data, kn.stride_head, kn.stride_token,
-                     c.frontier, c.n_groups, tau, a, diag);
+  hipLaunchKernelGGL(tc_index_kernel, dim3(F + 1, H), dim3(1024),
+                     ((size_t)1 << c.n_bits) * sizeof(int32_t), s, c.frontier, c.rep_bucket,
+                     c.n_groups, kb, a);
+  hipLaunchKernelGGL((tc_match_kernel<T, D>),
+                     dim3((unsigned)((Tf + kKeysPerGroup - 1) / kKeysPerGroup), (unsigned)H, (unsigned)F),
+                     dim3(256), (size_t)3 * Tf * sizeof(int32_t), s, (const T*)c.rep_k,
+                     (const T*)kn.data, kn.stride_head, kn.stride_token, c.frontier, tau, a, diag);
   hipLaunchKernelGGL(tc_number_kernel, dim3(H), dim3(1024), 0, s, c.n_groups, a);
   hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)F * Tf + 15) / 16), (unsigned)H),
                      dim3(256), 0, s, (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count,
@@ -1087,8 +898,6 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
 }
 
 }  // namespace
-
-int tempcache_table_size(int tokens_per_frame) { return table_size(tokens_per_frame); }
 
 hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
                                   const fastar_tensor_t& v_new, const int32_t* k_new_bucket,
