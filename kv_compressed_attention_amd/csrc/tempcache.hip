@@ -570,16 +570,17 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
 }
 
 // Step 2 for the keys this wave holds (one per lane; p < 0: no proposal):
-// does the key win its candidate against every other proposer of the
-// segment?  other(q, p2, c2, j2) gives segment key q's proposal; self is the
-// lane's own position (skipped).  Float32 near-ties are redone in float64.
-// Returns whether it wins.
+// does the key win its candidate against every other proposer?  other(q, p2,
+// c2, j2) gives key q's proposal (q < x.nk); the lane compares with keys
+// qlo .. qhi - 1, which must hold every other proposer of its candidate; self
+// is the lane's own position (skipped).  Float32 near-ties are redone in
+// float64.  Returns whether it wins.
 template <typename T, int D, typename Other>
 __device__ __forceinline__ bool resolve_keys(const SegCtx<T, D>& x, int self, int p, float c, int j,
-                                             Other other, const int32_t* fr) {
+                                             int qlo, int qhi, Other other, const int32_t* fr) {
   const int lane = lane_id();
   bool win = p >= 0, amb = false;
-  for (int q2 = 0; q2 < x.nk; ++q2) {
+  for (int q2 = qlo; q2 < qhi; ++q2) {
     int p2, j2;
     float c2;
     other(q2, p2, c2, j2);
@@ -686,8 +687,16 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
     const int pj = v ? lp[q] : -1;
     const float cj = v ? lc[q] : 0.f;
     const int j = v ? lj[q] : -1;
+    // a candidate's proposers all have its bucket: the key's own bucket is
+    // the only range to compare with
+    int qlo = 0, qhi = 0;
+    if (v && pj >= 0) {
+      const int b = kbk[p0 + q];
+      qlo = max(koff[b], p0) - p0;
+      qhi = min(koff[b + 1], p1) - p0;
+    }
     const bool win = resolve_keys<T, D>(
-        x, q, pj, cj, j,
+        x, q, pj, cj, j, qlo, qhi,
         [&](int q2, int& p2, float& c2, int& j2) {
           p2 = lp[q2];
           c2 = lc[q2];
