@@ -41,19 +41,16 @@ template <>
 struct VRow<8> {  // d = 128: 8 bf16 per lane per key
   uint4 u;
   __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
-  __device__ __forceinline__ uint32_t get(int b) const {
-    const uint32_t w = (b < 2) ? u.x : (b < 4) ? u.y : (b < 6) ? u.z : u.w;
-    return (b & 1) ? (w >> 16) : (w & 0xFFFFu);
+  // the 32-bit word holding dim b (its half: b & 1)
+  __device__ __forceinline__ uint32_t word(int b) const {
+    return (b < 2) ? u.x : (b < 4) ? u.y : (b < 6) ? u.z : u.w;
   }
 };
 template <>
 struct VRow<4> {  // d = 64: 4 bf16 per lane per key
   uint2 u;
   __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ uint32_t get(int b) const {
-    const uint32_t w = (b < 2) ? u.x : u.y;
-    return (b & 1) ? (w >> 16) : (w & 0xFFFFu);
-  }
+  __device__ __forceinline__ uint32_t word(int b) const { return (b < 2) ? u.x : u.y; }
 };
 
 __device__ __forceinline__ int wave_min_i(int v) {
@@ -276,8 +273,12 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     for (int si = 0; si < 8; ++si) vr[si].load(vbuf + (16 * (si >> 2) + 4 * g + (si & 3)) * D + NB * col);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const uint4 w = make_uint4(vr[0].get(b) | (vr[1].get(b) << 16), vr[2].get(b) | (vr[3].get(b) << 16),
-                                 vr[4].get(b) | (vr[5].get(b) << 16), vr[6].get(b) | (vr[7].get(b) << 16));
+      // (slot 2i's dim, slot 2i+1's dim) in one byte permute per dword
+      const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
+      const uint4 w = make_uint4(__builtin_amdgcn_perm(vr[1].word(b), vr[0].word(b), sel),
+                                 __builtin_amdgcn_perm(vr[3].word(b), vr[2].word(b), sel),
+                                 __builtin_amdgcn_perm(vr[5].word(b), vr[4].word(b), sel),
+                                 __builtin_amdgcn_perm(vr[7].word(b), vr[6].word(b), sel));
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[b], 0, 0, 0);
     }
     kid[0] = kid_next[0];
