@@ -141,8 +141,9 @@ class FastARLayer:
 
         With ``concurrent`` the query side runs on the second stream, forked
         after everything already queued on the caller's stream (the previous
-        step's readers of the query index included) and joined before return;
-        otherwise every stage is queued on the caller's stream in order.
+        step's readers of the query index included) and joined before the
+        self-attention; otherwise every stage is queued on the caller's stream
+        in order.
         ``timing`` (optional dict) receives (start, end) event pairs per
         stage, recorded on the stream each stage runs on."""
         cache = self.cache if cache is None else cache
@@ -155,6 +156,9 @@ class FastARLayer:
             return
         main = torch.cuda.current_stream(self.device)
         start = self._ev(None)
+        # the cache side (the longer chain) is queued first: a captured graph
+        # then starts it first
+        self._cache_side(cache, k_new, v_new, timing)
         with torch.cuda.stream(self.side):
             self.side.wait_event(start)
             self._query_hash(q, timing)
@@ -162,7 +166,6 @@ class FastARLayer:
             if prompt_k is not None:
                 self._cross(q, prompt_k, prompt_v, timing)
             side_done = self._ev(None)
-        self._cache_side(cache, k_new, v_new, timing)
         main.wait_event(q_done)
         self.self_attention(q, timing, cache)
         main.wait_event(side_done)
