@@ -497,20 +497,24 @@ __device__ __forceinline__ Top2<float> reduce_top2(Top2<float>* t) {
   return m;
 }
 
-// Step 1 for keys k0 .. k0 + 15 of the bucket-sorted key table (whole wave;
-// keys past kend are empty).  Their candidates are the candidate table's
-// positions [c_lo, c_hi), the buckets from the first key's to the last key's;
-// a (key, candidate) cosine counts only when their buckets agree.  The lane
-// with (l & 15) < 4 reports key r = 4 (l >> 4) + (l & 3): jrep (its token,
-// -1: none), p (the candidate token it proposes to, -1: none) and c (the
-// cosine).  Candidates are visited in tiles of 16, the next tile's rows
-// loading while the current one is used.
+// Step 1 for keys k0 .. k0 + 15 of a bucket-sorted key list ktok / kbk
+// (whole wave; keys past kend are empty).  Their candidates are positions
+// [c_lo, c_hi) of the bucket-sorted candidate list ctok / cbk / cg, covering
+// the buckets from the first key's to the last key's; a (key, candidate)
+// cosine counts only when their buckets agree.  The lists may be LDS copies;
+// the float64 re-evaluation reads a key's whole bucket from the candidate
+// table itself (gtok / gcg, bucket offsets coff).  The lane with
+// (l & 15) < 4 reports key r = 4 (l >> 4) + (l & 3): jrep (its token, -1:
+// none), p (the candidate token it proposes to, -1: none) and c (the cosine).
+// Candidates are visited in tiles of 16, the next tile's rows loading while
+// the current one is used.
 template <typename T, int D>
 __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t* ktok,
                                            const int32_t* kbk, int k0, int kend,
                                            const int32_t* ctok, const int32_t* cbk,
-                                           const int32_t* cg, const int32_t* coff, int c_lo,
-                                           int c_hi, int& jrep, int& p, float& c) {
+                                           const int32_t* cg, int c_lo, int c_hi,
+                                           const int32_t* gtok, const int32_t* gcg,
+                                           const int32_t* coff, int& jrep, int& p, float& c) {
   using TD = TileDot<T, D>;
   const int lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
@@ -562,8 +566,8 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
                  // the key's own bucket
                  const int b = __shfl(rb, 4 * (src >> 4) + (src & 3), FASTAR_WAVE);
                  const int s = coff[b];
-                 cl = ctok + s;
-                 gl = cg + s;
+                 cl = gtok + s;
+                 gl = gcg + s;
                  n = coff[b + 1] - s;
                },
                p, c);
@@ -617,70 +621,96 @@ __device__ __forceinline__ bool resolve_keys(const SegCtx<T, D>& x, int self, in
   return win;
 }
 
+// keys and candidates a match workgroup copies to LDS (larger ranges are read
+// from the tables directly)
+constexpr int kStageKeys = 256;
+constexpr int kStageCands = 512;
+
+// number of the first n entries of the ascending list v (LDS) that are < b
+// (below) or <= b (!below); whole wave
+__device__ __forceinline__ int count_until(const int32_t* v, int n, int b, bool below) {
+  int cnt = 0;
+  for (int i0 = 0; i0 < n; i0 += FASTAR_WAVE) {
+    const int i = i0 + lane_id();
+    const bool in = i < n && (below ? v[i] < b : v[i] <= b);
+    cnt += __popcll(ballot64(in));
+  }
+  return cnt;
+}
+
 // One workgroup per kKeysPerGroup positions of frame f's bucket-sorted keys,
 // rounded to whole buckets: a workgroup owns the buckets whose first key lies
-// in its positions.  Its waves take the tiles of 16 consecutive keys (step 1,
-// each key's best candidate and proposal), then, after one barrier, step 2
-// over all of its keys: every candidate keeps its best proposer (ties:
-// smaller j), which links to it; the other keys open groups.  A candidate's
-// proposers all share its bucket, so they are all in the workgroup.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void tc_match_kernel(
-    const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
-    const int32_t* __restrict__ frontier, float tau, MergeArgs a,
-    fastar_diag_t* __restrict__ diag) {
-  extern __shared__ int32_t lds[];  // [3][Tf] the workgroup's proposals
-  const int h = blockIdx.y;
-  const int f = blockIdx.z;
+// in its positions.  It copies its keys' ids and buckets and the candidate
+// ids, buckets and groups of its bucket range to LDS, then its waves take the
+// tiles of 16 consecutive keys (step 1, each key's best candidate and
+// proposal) and, after one barrier, step 2 over all of its keys: every
+// candidate keeps its best proposer (ties: smaller j), which links to it; the
+// other keys open groups.  A candidate's proposers all share its bucket, so
+// they are all in the workgroup.
+template <typename T, int D, bool STAGED>
+__device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeArgs& a, int h,
+                                            int p0, int p1, int c0, int c1,
+                                            const int32_t* __restrict__ frontier, int32_t* lds) {
+  const int f = x.f;
   const int lane = lane_id();
   const int col = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int nb = 1 << a.nbits;
   const int32_t* koff = a.off + off_off(a, h, f + 1);
-  const int32_t* ktok = a.tok + tok_off(a, h, f + 1);
-  const int32_t* kbk = a.tbk + tok_off(a, h, f + 1);
+  const int32_t* gktok = a.tok + tok_off(a, h, f + 1);
+  const int32_t* gkbk = a.tbk + tok_off(a, h, f + 1);
   const int32_t* coff = a.off + off_off(a, h, f);
-  const int32_t* ctok = a.tok + tok_off(a, h, f);
-  const int32_t* cbk = a.tbk + tok_off(a, h, f);
-  const int32_t* cg = a.candg + (int64_t)h * a.Tf;
-  // the owned key positions [p0, p1)
-  const int nkt = koff[nb];
-  int p0 = blockIdx.x * kKeysPerGroup;
-  if (p0 >= nkt) return;
-  int p1 = min(p0 + kKeysPerGroup, nkt);
-  if (p0 > 0 && kbk[p0 - 1] == kbk[p0]) p0 = koff[kbk[p0] + 1];
-  if (p1 < nkt && kbk[p1 - 1] == kbk[p1]) p1 = koff[kbk[p1] + 1];
-  if (p0 >= p1) return;  // the whole workgroup: no barrier is reached
+  const int32_t* gctok = a.tok + tok_off(a, h, f);
+  const int32_t* gcbk = a.tbk + tok_off(a, h, f);
+  const int32_t* gcg = a.candg + (int64_t)h * a.Tf;
   const int nk = p1 - p0;
-  const int64_t fo = frame_off(a, h, f);
-  const int32_t* fr = frontier + (int64_t)h * a.Tf;
+  const int nc = c1 - c0;
   int32_t* lp = lds;
   float* lc = reinterpret_cast<float*>(lds + a.Tf);
   int32_t* lj = lds + 2 * a.Tf;
-  SegCtx<T, D> x;
-  x.kf = knew + (int64_t)h * k_sh + (int64_t)f * a.Tf * k_st;
-  x.kp = f > 0 ? x.kf - (int64_t)a.Tf * k_st : x.kf;
-  x.rk = rep_k + (int64_t)h * a.cap * D;
-  x.k_st = k_st;
-  x.f = f;
-  x.tau = tau;
-  x.e = match_err<T, D>();
-  x.diag = diag;
-  x.nk = nk;
-  for (int k0 = p0 + wave * kKeyTile; k0 < p1; k0 += 4 * kKeyTile) {
-    const int klast = min(k0 + kKeyTile, p1) - 1;
-    const int c_lo = coff[kbk[k0]], c_hi = coff[kbk[klast] + 1];
+  // the key and candidate lists, rebased to the workgroup's ranges
+  int32_t* sk = lds + 3 * a.Tf;            // [2][kStageKeys] tokens, buckets
+  int32_t* sc = sk + 2 * kStageKeys;       // [3][kStageCands] tokens, buckets, groups
+  const int32_t* ktok = STAGED ? sk : gktok + p0;
+  const int32_t* kbk = STAGED ? sk + kStageKeys : gkbk + p0;
+  const int32_t* ctok = STAGED ? sc : gctok + c0;
+  const int32_t* cbk = STAGED ? sc + kStageCands : gcbk + c0;
+  const int32_t* cg = STAGED ? sc + 2 * kStageCands : gcg + c0;
+  if (STAGED) {
+    for (int i = threadIdx.x; i < nk; i += blockDim.x) {
+      sk[i] = gktok[p0 + i];
+      sk[kStageKeys + i] = gkbk[p0 + i];
+    }
+    for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+      sc[i] = gctok[c0 + i];
+      sc[kStageCands + i] = gcbk[c0 + i];
+      if (f == 0) sc[2 * kStageCands + i] = gcg[c0 + i];
+    }
+    __syncthreads();
+  }
+  for (int k0 = wave * kKeyTile; k0 < nk; k0 += 4 * kKeyTile) {
+    const int klast = min(k0 + kKeyTile, nk) - 1;
+    int c_lo, c_hi;
+    if (STAGED) {
+      c_lo = count_until(cbk, nc, kbk[k0], true);
+      c_hi = count_until(cbk, nc, kbk[klast], false);
+    } else {
+      c_lo = coff[kbk[k0]] - c0;
+      c_hi = coff[kbk[klast] + 1] - c0;
+    }
     int jrep, p;
     float c;
-    match_tile<T, D>(x, ktok, kbk, k0, p1, ctok, cbk, cg, coff, c_lo, c_hi, jrep, p, c);
+    match_tile<T, D>(x, ktok, kbk, k0, nk, ctok, cbk, cg, c_lo, c_hi, gctok, gcg, coff, jrep, p,
+                     c);
     if (col < 4 && jrep >= 0) {
-      const int q = k0 - p0 + 4 * (lane >> 4) + col;
+      const int q = k0 + 4 * (lane >> 4) + col;
       lp[q] = p;
       lc[q] = c;
       lj[q] = jrep;
     }
   }
   __syncthreads();
+  const int64_t fo = frame_off(a, h, f);
+  const int32_t* fr = frontier + (int64_t)h * a.Tf;
   for (int q0 = wave * FASTAR_WAVE; q0 < nk; q0 += 4 * FASTAR_WAVE) {
     const int q = q0 + lane;
     const bool v = q < nk;
@@ -690,8 +720,18 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
     // a candidate's proposers all have its bucket: the key's own bucket is
     // the only range to compare with
     int qlo = 0, qhi = 0;
-    if (v && pj >= 0) {
-      const int b = kbk[p0 + q];
+    if (STAGED && nk <= FASTAR_WAVE) {
+      // the bucket runs of the (at most 64) keys, from their starts
+      const int bq = v ? kbk[q] : -1;
+      const bool start = v && (q == 0 || kbk[q - 1] != bq);
+      // positions >= nk end a run
+      const uint64_t starts = ballot64(start) | (nk >= FASTAR_WAVE ? 0ull : (~0ull << nk));
+      const uint64_t below = starts & (lane == 63 ? ~0ull : ((2ull << lane) - 1));
+      qlo = 63 - __builtin_clzll(below);
+      const uint64_t above = starts & ~((2ull << lane) - 1);
+      qhi = above ? __builtin_ctzll(above) : FASTAR_WAVE;
+    } else if (v && pj >= 0) {
+      const int b = kbk[q];
       qlo = max(koff[b], p0) - p0;
       qhi = min(koff[b + 1], p1) - p0;
     }
@@ -712,6 +752,48 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
       a.link[fo + j] = lk;
     }
   }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void tc_match_kernel(
+    const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
+    const int32_t* __restrict__ frontier, float tau, MergeArgs a,
+    fastar_diag_t* __restrict__ diag) {
+  extern __shared__ int32_t lds[];  // [3][Tf] proposals, then the staged lists
+  const int h = blockIdx.y;
+  const int f = blockIdx.z;
+  const int nb = 1 << a.nbits;
+  const int32_t* koff = a.off + off_off(a, h, f + 1);
+  const int32_t* kbk = a.tbk + tok_off(a, h, f + 1);
+  const int32_t* coff = a.off + off_off(a, h, f);
+  // the owned key positions [p0, p1) and the candidate range [c0, c1) of
+  // their buckets (it may also hold candidates of buckets without keys)
+  const int nkt = koff[nb];
+  const int a0 = blockIdx.x * kKeysPerGroup;
+  if (a0 >= nkt) return;
+  const int a1 = min(a0 + kKeysPerGroup, nkt);
+  const int b0 = kbk[a0], b1 = kbk[a1 - 1];
+  const bool cut0 = a0 > 0 && kbk[a0 - 1] == b0;  // a0 inside a bucket owned before
+  const bool cut1 = a1 < nkt && kbk[a1] == b1;    // a1 inside a bucket owned here
+  const int p0 = cut0 ? koff[b0 + 1] : a0;
+  const int p1 = cut1 ? koff[b1 + 1] : a1;
+  if (p0 >= p1) return;  // the whole workgroup: no barrier is reached
+  const int c0 = coff[cut0 ? b0 + 1 : b0];
+  const int c1 = coff[b1 + 1];
+  SegCtx<T, D> x;
+  x.kf = knew + (int64_t)h * k_sh + (int64_t)f * a.Tf * k_st;
+  x.kp = f > 0 ? x.kf - (int64_t)a.Tf * k_st : x.kf;
+  x.rk = rep_k + (int64_t)h * a.cap * D;
+  x.k_st = k_st;
+  x.f = f;
+  x.tau = tau;
+  x.e = match_err<T, D>();
+  x.diag = diag;
+  x.nk = p1 - p0;
+  if (p1 - p0 <= kStageKeys && c1 - c0 <= kStageCands)
+    match_group<T, D, true>(x, a, h, p0, p1, c0, c1, frontier, lds);
+  else
+    match_group<T, D, false>(x, a, h, p0, p1, c0, c1, frontier, lds);
 }
 
 // One workgroup per head: the tokens that open groups, in (frame, j) order,
@@ -890,7 +972,9 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
                      c.n_groups, kb, a);
   hipLaunchKernelGGL((tc_match_kernel<T, D>),
                      dim3((unsigned)((Tf + kKeysPerGroup - 1) / kKeysPerGroup), (unsigned)H, (unsigned)F),
-                     dim3(256), (size_t)3 * Tf * sizeof(int32_t), s, (const T*)c.rep_k,
+                     dim3(256),
+                     ((size_t)3 * Tf + 2 * kStageKeys + 3 * kStageCands) * sizeof(int32_t), s,
+                     (const T*)c.rep_k,
                      (const T*)kn.data, kn.stride_head, kn.stride_token, c.frontier, tau, a, diag);
   hipLaunchKernelGGL(tc_number_kernel, dim3(H), dim3(1024), 0, s, c.n_groups, a);
   hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)F * Tf + 15) / 16), (unsigned)H),
