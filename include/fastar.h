@@ -200,6 +200,8 @@ fastar_status_t fastar_prune_prompt(const int32_t* q_bucket, int heads, int64_t 
  *   out    [H][Nq][d] contiguous, dtype of q.
  *   lse    [H][Nq] float32 natural-log normaliser, or NULL.
  *   A query with an empty key set gets out = 0 and lse = -inf.
+ *   bf16: one head's k rows (and v rows) must lie within 4 GiB of its first
+ *   row, else FASTAR_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
 fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t* q_bucket,
                                         const int32_t* q_perm, int n_probes,

@@ -279,6 +279,13 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
   if ((int64_t)q->heads * q->tokens == 0) return FASTAR_OK;
   if (!out || !aligned16(out)) return fail(FASTAR_ERR_INVALID, "out must be a non-null 16-byte aligned pointer");
   if (mode == 0 && (!q_bucket || !q_perm)) return fail(FASTAR_ERR_INVALID, "bucket mode needs q_bucket and q_perm");
+  if (q->dtype == FASTAR_BF16 && k->tokens > 0) {
+    // the bf16 kernel addresses a head's k and v rows by 32-bit byte offsets
+    const int64_t span_k = ((int64_t)(k->tokens - 1) * k->stride_token + k->dim) * 2;
+    const int64_t span_v = ((int64_t)(v->tokens - 1) * v->stride_token + v->dim) * 2;
+    if (span_k > 0xFFFFFFFFll || span_v > 0xFFFFFFFFll)
+      return fail(FASTAR_ERR_UNSUPPORTED, "a head's k or v rows span more than 4 GiB");
+  }
   fastar::AttnArgs a;
   a.q = q->data; a.q_sh = q->stride_head; a.q_st = q->stride_token; a.nq = q->tokens;
   a.q_bucket = q_bucket; a.q_perm = q_perm; a.n_probes = mode == 0 ? n_probes : 1;

@@ -53,13 +53,10 @@ struct VRow<4> {  // d = 64: 4 bf16 per lane per key
   __device__ __forceinline__ uint32_t word(int b) const { return (b < 2) ? u.x : u.y; }
 };
 
-__device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int m = 1; m < FASTAR_WAVE; m <<= 1) v = min(v, shfl_xor_i(v, m));
-  return v;
-}
 
-// MODE: 0 bucket, 1 key list, 2 dense
+// MODE: 0 bucket, 1 key list, 2 dense.  Every head's k and v rows lie within
+// 4 GiB of the head's first row (checked by the caller), so row offsets are
+// 32-bit byte offsets from the head's base.
 template <int D, int P, int MODE>
 __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_sh, int64_t q_st, int64_t Nq,
@@ -82,7 +79,7 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   if (lb >= nbx * H) return;
   const int h = (int)(lb / nbx);
   const int64_t bx = lb - (int64_t)h * nbx;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
@@ -112,8 +109,9 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
 #pragma unroll
   for (int b = 0; b < NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* kh = k + (int64_t)h * k_sh;
-  const uint16_t* vh = v + (int64_t)h * v_sh;
+  const char* kh = reinterpret_cast<const char*>(k + (int64_t)h * k_sh);
+  const char* vh = reinterpret_cast<const char*>(v + (int64_t)h * v_sh);
+  const uint32_t kst_b = (uint32_t)(k_st * 2), vst_b = (uint32_t)(v_st * 2);
   const float* bh = key_bias ? key_bias + (int64_t)h * Nk : nullptr;
   const int32_t* idx_h = nullptr;
   if (MODE == 0) idx_h = k_perm + (int64_t)h * Nk;
@@ -121,22 +119,29 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
 
   // passes: the distinct buckets of the wave's rows in ascending order (MODE
   // 0; lane i holds pass i's bucket and key range), or one pass over the list
-  // or all keys.  Every pass's key range is loaded at once.
+  // or all keys.  Every pass's key range is loaded at once.  pr0 / pr1: the
+  // passes of this row's buckets.
   int b0 = INT_MAX, b1 = INT_MAX;
   if (MODE == 0 && rvalid) {
     const int32_t* qb = q_bucket + ((int64_t)h * Nq + t) * P;
     b0 = qb[0];
     if (P == 2) b1 = qb[1];
   }
-  int npass = 0, xs = INT_MAX, pkb = 0, pke = 0;
+  int npass = 0, xs = INT_MAX, pkb = 0, pke = 0, pr0 = -1, pr1 = -1;
   if (MODE == 0) {
     int c0 = b0, c1 = b1;
     while (true) {
-      const int X = wave_min_i(min(c0, c1));
+      const int X = wave_min_dpp(min(c0, c1));
       if (X == INT_MAX) break;
       if (l == npass) xs = X;
-      if (c0 == X) c0 = INT_MAX;
-      if (c1 == X) c1 = INT_MAX;
+      if (c0 == X) {
+        c0 = INT_MAX;
+        pr0 = npass;
+      }
+      if (c1 == X) {
+        c1 = INT_MAX;
+        pr1 = npass;
+      }
       ++npass;
     }
     if (l < npass) {
@@ -152,61 +157,77 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       ke = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
     }
     pke = (int)ke;
+    if (rvalid) pr0 = 0;
   }
   // the passes' key ranges, concatenated: pass p's keys are slots
   // pre_p .. pre_p + len_p - 1 of the wave's key list
   const int len = l < npass ? pke - pkb : 0;
-  int pre = len;
-#pragma unroll
-  for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
-    const int y = __shfl_up(pre, o, FASTAR_WAVE);
-    if (l >= o) pre += y;
-  }
-  const int total = __builtin_amdgcn_readlane(pre, FASTAR_WAVE - 1);
-  pre -= len;
-  // key and bucket of list slot j (j < total), for this lane
-  auto slot_key = [&](int j, int& key, int& bucket) {
-    int pj = 0;
-    for (int q2 = 1; q2 < npass; ++q2) pj += __builtin_amdgcn_readlane(pre, q2) <= j ? 1 : 0;
-    const int kk = __shfl(pkb, pj, FASTAR_WAVE) + j - __shfl(pre, pj, FASTAR_WAVE);
-    key = (MODE == 2) ? kk : idx_h[kk];
-    bucket = __shfl(xs, pj, FASTAR_WAVE);
-  };
-  // slot `col` of each 16-slot half of the chunk at c0 (past the end: slot 0)
-  auto chunk_ids = [&](int c0, int* kid, int* kb) {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      int j = c0 + 16 * hf + col;
-      if (j >= total) j = 0;
-      slot_key(j, kid[hf], kb[hf]);
+  // lane p < npass: pre = slots of the passes before p; the rows' slot
+  // ranges, [lo0, lo0 + n0) and, with two probes, [lo1, lo1 + n1), from the
+  // same walk over the (few) passes with wave-uniform reads
+  int pre = 0, total = 0;
+  uint32_t lo0 = 0u, n0 = 0u, lo1 = 0u, n1 = 0u;
+  for (int p = 0; p < npass; ++p) {
+    const int lp = __builtin_amdgcn_readlane(len, p);
+    if (l == p) pre = total;
+    if (pr0 == p) {
+      lo0 = (uint32_t)total;
+      n0 = (uint32_t)lp;
     }
+    if (P == 2 && pr1 == p) {
+      lo1 = (uint32_t)total;
+      n1 = (uint32_t)lp;
+    }
+    total += lp;
+  }
+  // key of list slot j (past the end: the last slot's, which no row uses);
+  // the pass is found with wave-uniform reads of the pass table
+  const int kb_pre = pkb - pre;  // slot j of pass p is position j + kb_pre_p
+  auto slot_key = [&](int j) {
+    const int jc = min(j, total - 1);
+    int base = __builtin_amdgcn_readfirstlane(kb_pre);
+    for (int q2 = 1; q2 < npass; ++q2) {
+      const int pq = __builtin_amdgcn_readlane(pre, q2);
+      const int bq = __builtin_amdgcn_readlane(kb_pre, q2);
+      base = pq <= jc ? bq : base;
+    }
+    const int kk = jc + base;
+    return (MODE == 2) ? kk : idx_h[kk];
   };
-  int kid[2] = {0, 0}, kbk[2] = {0, 0};
-  if (total > 0) chunk_ids(0, kid, kbk);
+  // Chunks of 32 list slots: at chunk kc lane j < 32 holds the key of
+  // chunk slot j in ks, and the next chunk's keys load during the chunk.
+  int ks = total > 0 ? slot_key(l) : 0;
   for (int kc = 0; kc < total; kc += 32) {
-    // the next chunk's key ids load while this chunk's rows are in flight
-    int kid_next[2] = {0, 0}, kbk_next[2] = {0, 0};
-    if (kc + 32 < total) chunk_ids(kc + 32, kid_next, kbk_next);
+    const int ks_next = slot_key(kc + 32 + l);
+    const uint32_t koff_l = (uint32_t)ks * kst_b;
+    const uint32_t voff_l = (uint32_t)ks * vst_b;
     // the chunk's 32 V rows go straight to the wave's LDS buffer (slot j of
     // the chunk at row j), issued with the K gathers; V does not depend on
     // the scores, and no registers hold it until the PV product
+    // (all row offsets are fetched from their lanes before the first load)
+    uint32_t vo[32 / kVRows];
 #pragma unroll
-    for (int i = 0; i < 32 / kVRows; ++i) {
-      const int slot = kVRows * i + l / (64 / kVRows);
-      const int key = __shfl(kid[(kVRows * i) >> 4], slot & 15, FASTAR_WAVE);
+    for (int i = 0; i < 32 / kVRows; ++i)
+      vo[i] = (uint32_t)__shfl((int)voff_l, kVRows * i + l / (64 / kVRows), FASTAR_WAVE);
+    uint32_t ko[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) ko[hf] = (uint32_t)__shfl((int)koff_l, 16 * hf + col, FASTAR_WAVE);
+#pragma unroll
+    for (int i = 0; i < 32 / kVRows; ++i)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(vh + (int64_t)key * v_st + (l % (64 / kVRows)) * 8),
+          (const void*)(vh + (uint32_t)(vo[i] + (l % (64 / kVRows)) * 16)),
           (__attribute__((address_space(3))) void*)(vbuf + kVRows * i * D), 16, 0, 0);
-    }
-    // and the 32 biases (lane j < 32: chunk row j's)
+    // the 32 biases: lane j < 32 loads chunk slot j's to bbuf[j]
     if (bh && l < 32)
-      __builtin_amdgcn_global_load_lds((const void*)(bh + kid[l >> 4]), (__attribute__((address_space(3))) void*)bbuf, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(bh + ks),
+                                       (__attribute__((address_space(3))) void*)bbuf, 4, 0, 0);
+    // K rows: lane (col, g) reads slot 16 hf + col, dims 32c + 8g .. +8
     uint4 kraw[2][NC];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const uint16_t* krow = kh + (int64_t)kid[hf] * k_st;
+      const char* krow = kh + (uint32_t)(ko[hf] + 16u * g);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kraw[hf][c] = *reinterpret_cast<const uint4*>(krow + 32 * c + 8 * g);
+      for (int c = 0; c < NC; ++c) kraw[hf][c] = *reinterpret_cast<const uint4*>(krow + 64 * c);
     }
     // the MFMAs below wait for the K rows, which were issued after the V rows
     // and biases: every row load of the chunk has landed after this wait
@@ -228,42 +249,43 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
 #pragma unroll
       for (int c = 0; c < NC; ++c)
         sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kraw[hf][c]), qop[c], sacc, 0, 0, 0);
-      // sacc[i] = score(key slot 16hf + 4g + i, row col)
+      // sacc[i] = score(list slot kc + 16 hf + 4 g + i, row col)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // slot 4 hf + i is list slot kc + 16 hf + 4 g + i; its bucket:
-        const int sb = __shfl(kbk[hf], 4 * g + i, FASTAR_WAVE);
-        const bool kvalid = kc + 16 * hf + 4 * g + i < total;
-        const bool in = (MODE != 0) ? rvalid : (sb == b0 || sb == b1);
-        s[4 * hf + i] = (kvalid && in) ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
+        const uint32_t j = (uint32_t)(kc + 16 * hf + 4 * g + i);
+        bool in = j - lo0 < n0;
+        if (P == 2) in = in || j - lo1 < n1;
+        s[4 * hf + i] = in ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
       }
     }
-    float mx = s[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    mx = max_xor32(max_xor16(mx));
     const float mnew = fmaxf(m, mx);
     const float base = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = exp2f(m - base);
-    m = mnew;
     uint32_t pw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * i] - base), __builtin_amdgcn_exp2f(s[2 * i + 1] - base));
+    // the sum of the rounded weights that the PV product uses
     float psum = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = f32_to_bf16_bits(exp2f(s[2 * i] - base));
-      const uint32_t hi = f32_to_bf16_bits(exp2f(s[2 * i + 1] - base));
-      psum += bf16_bits_to_f32(lo) + bf16_bits_to_f32(hi);
-      pw[i] = lo | (hi << 16);
-    }
-    lsum = lsum * alpha + psum;
+    for (int i = 0; i < 4; ++i)
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]),
+                                              __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+    // rescale the running sums only where a row's (finite) max went up
+    if (ballot64(m != -INFINITY && mnew > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - base);
+      lsum *= alpha;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      acc[b][0] *= alpha;
-      acc[b][1] *= alpha;
-      acc[b][2] *= alpha;
-      acc[b][3] *= alpha;
+      for (int b = 0; b < NB; ++b) {
+        acc[b][0] *= alpha;
+        acc[b][1] *= alpha;
+        acc[b][2] *= alpha;
+        acc[b][3] *= alpha;
+      }
     }
+    lsum += psum;
+    m = mnew;
     const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
     // V^T operand: lane (dim-row col, group g), slot si <-> chunk row
     // 16 (si >> 2) + 4g + (si & 3), dims NB*col .. NB*col + NB - 1 (one per
@@ -281,13 +303,9 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
                                  __builtin_amdgcn_perm(vr[7].word(b), vr[6].word(b), sel));
       acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[b], 0, 0, 0);
     }
-    kid[0] = kid_next[0];
-    kid[1] = kid_next[1];
-    kbk[0] = kbk_next[0];
-    kbk[1] = kbk_next[1];
+    ks = ks_next;
   }
-  lsum += shfl_xor_f(lsum, 16);
-  lsum += shfl_xor_f(lsum, 32);
+  lsum = sum_xor32(sum_xor16(lsum));
   if (!rvalid) return;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   // acc[b][i] = O[row col][NB*(4g+i) + b]: dims 4*NB*g .. 4*NB*g + 4*NB - 1
@@ -295,11 +313,7 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int b = 0; b < NB; b += 2) {
-      const uint32_t lo = f32_to_bf16_bits(acc[b][i] * inv);
-      const uint32_t hi = f32_to_bf16_bits(acc[b + 1][i] * inv);
-      ow[(i * NB + b) / 2] = lo | (hi << 16);
-    }
+    for (int b = 0; b < NB; b += 2) ow[(i * NB + b) / 2] = pack_bf16x2(acc[b][i] * inv, acc[b + 1][i] * inv);
   uint16_t* orow = out + ((int64_t)h * Nq + t) * D + 4 * NB * g;
 #pragma unroll
   for (int j = 0; j < NB / 2; ++j)

@@ -37,6 +37,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two float32 rounded to nearest-even bf16 by one v_cvt_pk_bf16_f32; lo in
+// bits 0..15 (finite inputs: the same bits as f32_to_bf16_bits)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
@@ -58,6 +66,36 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & (FASTAR_WAVE - 1
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, FASTAR_WAVE); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, FASTAR_WAVE); }
+
+// v combined with v of lane ^ 16 (lane ^ 32) without LDS: a permlane swap
+// hands every lane both values, in an order that depends on the lane, so
+// only commutative combines are offered
+__device__ __forceinline__ f32x2_t pair_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return (f32x2_t){__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2_t pair_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return (f32x2_t){__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor16(float v) { const f32x2_t p = pair_xor16(v); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float max_xor32(float v) { const f32x2_t p = pair_xor32(v); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float sum_xor16(float v) { const f32x2_t p = pair_xor16(v); return p.x + p.y; }
+__device__ __forceinline__ float sum_xor32(float v) { const f32x2_t p = pair_xor32(v); return p.x + p.y; }
+
+// minimum over the wave without LDS: DPP pairs within quads (lane ^ 1,
+// lane ^ 2), then each half-row and row with its mirror image, then the
+// permlane swaps across rows
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = min((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return min((int)r[0], (int)r[1]);
+}
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 
