@@ -151,8 +151,10 @@ size_t fastar_tempcache_workspace(const fastar_cache_t* c, int n_frames) {
   if (c->n_bits < 0 || c->n_bits > 15) return 0;
   const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
   const size_t nb = ((size_t)1 << c->n_bits) + 1;
+  const size_t nblk = (F * T + 63) / 64;
   return align_up(4 * H * (F + 1) * nb) + 2 * align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
-         3 * align_up(4 * H * F * T) + align_up(16 * H * (size_t)c->capacity);
+         align_up(4 * H * F * T) + align_up(4 * H * (nblk + 1)) + align_up(4 * H * F * T) +
+         align_up(16 * H * (size_t)c->capacity);
 }
 
 fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
@@ -218,7 +220,7 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
   mw.tbk = take(4 * H * (F + 1) * T);
   mw.candg = take(4 * H * T);
   mw.link = take(4 * H * F * T);
-  mw.gid = take(4 * H * F * T);
+  mw.ocnt = take(4 * H * ((F * T + 63) / 64 + 1));
   mw.nextj = take(4 * H * F * T);
   mw.index_ws = take(16 * H * (size_t)c->capacity);
   return hip_status(fastar::launch_tempcache_merge(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,

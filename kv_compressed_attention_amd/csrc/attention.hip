@@ -67,30 +67,44 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     const int32_t* __restrict__ k_perm, int nbits, const int32_t* __restrict__ key_list,
     const int32_t* __restrict__ n_key_list, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, int H) {
-  constexpr int NC = D / 32;  // k-chunks of the QK^T contraction
-  constexpr int NB = D / 16;  // 16-dim output blocks
-  // rows of the V chunk one 16-byte-per-lane LDS load fills
-  constexpr int kVRows = 64 * 16 / (2 * D);
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[4][32 * D];
-  __shared__ __attribute__((aligned(16))) float blds[4][32];
-  // logical block (row block, head), XCD-grouped
+  constexpr int NC = D / 32;                      // k-chunks of the QK^T contraction
+  constexpr int NB = D / 16;                      // 16-dim output blocks
+  constexpr int kPieces = D / 8;                  // 16-byte pieces of a row
+  constexpr int kDmaRows = 64 / kPieces;          // rows one 64-lane 16-byte LDS load fills
+  constexpr int kDmaPerWave = 32 / kDmaRows / 4;  // such loads per wave, tile and chunk
+  // double-buffered chunk tiles, shared by the workgroup's waves: even
+  // chunks in the A buffers, odd chunks in the B buffers (separate arrays,
+  // so that reads of one are not held up by loads in flight to the other)
+  __shared__ __attribute__((aligned(16))) uint16_t ktA[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ktB[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vtA[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vtB[32 * D];
+  __shared__ __attribute__((aligned(16))) float btA[32];
+  __shared__ __attribute__((aligned(16))) float btB[32];
+  // logical block (64-row block, head), XCD-grouped
   const int64_t nbx = (Nq + 63) / 64;
   const int64_t lb = xcd_block(blockIdx.x, nbx * H);
-  if (lb >= nbx * H) return;
+  if (lb >= nbx * H) return;  // the whole workgroup
   const int h = (int)(lb / nbx);
-  const int64_t bx = lb - (int64_t)h * nbx;
+  const int64_t R0 = (lb - (int64_t)h * nbx) * 64;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
-  uint16_t* vbuf = vlds[wave];
-  float* bbuf = blds[wave];
-  const int64_t r0 = bx * 64 + wave * 16;
-  if (r0 >= Nq) return;
-  const int64_t r = r0 + col;
+  // this lane's MFMA row: workgroup row 16 wave + col
+  const int64_t r = R0 + 16 * wave + col;
   const bool rvalid = r < Nq;
-  int64_t t = r0;
+  int64_t t = 0;
   if (rvalid) t = (MODE == 0) ? (int64_t)q_perm[(int64_t)h * Nq + r] : r;
+  // and its row of the workgroup's bucket table: workgroup row l
+  int c0 = INT_MAX, c1 = INT_MAX;
+  const bool wvalid = R0 + l < Nq;
+  if (MODE == 0 && wvalid) {
+    const int64_t tw = q_perm[(int64_t)h * Nq + R0 + l];
+    const int32_t* qb = q_bucket + ((int64_t)h * Nq + tw) * P;
+    c0 = qb[0];
+    if (P == 2) c1 = qb[1];
+  }
 
   // B operand of S^T = K Q^T: query row `col`, dims 32c + 8g .. +8
   bf16x8_t qop[NC];
@@ -117,193 +131,214 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   if (MODE == 0) idx_h = k_perm + (int64_t)h * Nk;
   if (MODE == 1) idx_h = key_list + (int64_t)h * Nk;
 
-  // passes: the distinct buckets of the wave's rows in ascending order (MODE
-  // 0; lane i holds pass i's bucket and key range), or one pass over the list
-  // or all keys.  Every pass's key range is loaded at once.  pr0 / pr1: the
-  // passes of this row's buckets.
-  int b0 = INT_MAX, b1 = INT_MAX;
-  if (MODE == 0 && rvalid) {
-    const int32_t* qb = q_bucket + ((int64_t)h * Nq + t) * P;
-    b0 = qb[0];
-    if (P == 2) b1 = qb[1];
-  }
-  int npass = 0, xs = INT_MAX, pkb = 0, pke = 0, pr0 = -1, pr1 = -1;
-  if (MODE == 0) {
-    int c0 = b0, c1 = b1;
-    while (true) {
-      const int X = wave_min_dpp(min(c0, c1));
-      if (X == INT_MAX) break;
-      if (l == npass) xs = X;
-      if (c0 == X) {
-        c0 = INT_MAX;
-        pr0 = npass;
+  // Batches of passes.  A pass is one distinct bucket of the workgroup's 64
+  // rows (both probes), in ascending order, up to 64 per batch (lane i holds
+  // pass i); in list and dense mode one pass over the list or all keys.  The
+  // batch's key list is its passes' key ranges, concatenated.  Every wave
+  // builds the same table, so loop counts agree across the workgroup.
+  while (true) {
+    int npass = 0, xs = 0, pkb = 0, pke = 0, pr0 = -1, pr1 = -1;
+    if (MODE == 0) {
+      while (npass < FASTAR_WAVE) {
+        const int X = wave_min_dpp(min(c0, c1));
+        if (X == INT_MAX) break;
+        if (l == npass) xs = X;
+        if (c0 == X) {
+          c0 = INT_MAX;
+          pr0 = npass;
+        }
+        if (c1 == X) {
+          c1 = INT_MAX;
+          pr1 = npass;
+        }
+        ++npass;
       }
-      if (c1 == X) {
-        c1 = INT_MAX;
-        pr1 = npass;
+      if (npass == 0) break;
+      if (l < npass) {
+        const int32_t* off = k_offsets + (int64_t)h * ((1 << nbits) + 1) + xs;
+        pkb = off[0];
+        pke = off[1];
       }
-      ++npass;
-    }
-    if (l < npass) {
-      const int32_t* off = k_offsets + (int64_t)h * ((1 << nbits) + 1) + xs;
-      pkb = off[0];
-      pke = off[1];
-    }
-  } else {
-    npass = 1;
-    int64_t ke = Nk;
-    if (MODE == 1) {
-      const int64_t nl = n_key_list[h];
-      ke = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
-    }
-    pke = (int)ke;
-    if (rvalid) pr0 = 0;
-  }
-  // the passes' key ranges, concatenated: pass p's keys are slots
-  // pre_p .. pre_p + len_p - 1 of the wave's key list
-  const int len = l < npass ? pke - pkb : 0;
-  // lane p < npass: pre = slots of the passes before p; the rows' slot
-  // ranges, [lo0, lo0 + n0) and, with two probes, [lo1, lo1 + n1), from the
-  // same walk over the (few) passes with wave-uniform reads
-  int pre = 0, total = 0;
-  uint32_t lo0 = 0u, n0 = 0u, lo1 = 0u, n1 = 0u;
-  for (int p = 0; p < npass; ++p) {
-    const int lp = __builtin_amdgcn_readlane(len, p);
-    if (l == p) pre = total;
-    if (pr0 == p) {
-      lo0 = (uint32_t)total;
-      n0 = (uint32_t)lp;
-    }
-    if (P == 2 && pr1 == p) {
-      lo1 = (uint32_t)total;
-      n1 = (uint32_t)lp;
-    }
-    total += lp;
-  }
-  // key of list slot j (past the end: the last slot's, which no row uses);
-  // the pass is found with wave-uniform reads of the pass table
-  const int kb_pre = pkb - pre;  // slot j of pass p is position j + kb_pre_p
-  auto slot_key = [&](int j) {
-    const int jc = min(j, total - 1);
-    int base = __builtin_amdgcn_readfirstlane(kb_pre);
-    for (int q2 = 1; q2 < npass; ++q2) {
-      const int pq = __builtin_amdgcn_readlane(pre, q2);
-      const int bq = __builtin_amdgcn_readlane(kb_pre, q2);
-      base = pq <= jc ? bq : base;
-    }
-    const int kk = jc + base;
-    return (MODE == 2) ? kk : idx_h[kk];
-  };
-  // Chunks of 32 list slots: at chunk kc lane j < 32 holds the key of
-  // chunk slot j in ks, and the next chunk's keys load during the chunk.
-  int ks = total > 0 ? slot_key(l) : 0;
-  for (int kc = 0; kc < total; kc += 32) {
-    const int ks_next = slot_key(kc + 32 + l);
-    const uint32_t koff_l = (uint32_t)ks * kst_b;
-    const uint32_t voff_l = (uint32_t)ks * vst_b;
-    // the chunk's 32 V rows go straight to the wave's LDS buffer (slot j of
-    // the chunk at row j), issued with the K gathers; V does not depend on
-    // the scores, and no registers hold it until the PV product
-    // (all row offsets are fetched from their lanes before the first load)
-    uint32_t vo[32 / kVRows];
-#pragma unroll
-    for (int i = 0; i < 32 / kVRows; ++i)
-      vo[i] = (uint32_t)__shfl((int)voff_l, kVRows * i + l / (64 / kVRows), FASTAR_WAVE);
-    uint32_t ko[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) ko[hf] = (uint32_t)__shfl((int)koff_l, 16 * hf + col, FASTAR_WAVE);
-#pragma unroll
-    for (int i = 0; i < 32 / kVRows; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(vh + (uint32_t)(vo[i] + (l % (64 / kVRows)) * 16)),
-          (__attribute__((address_space(3))) void*)(vbuf + kVRows * i * D), 16, 0, 0);
-    // the 32 biases: lane j < 32 loads chunk slot j's to bbuf[j]
-    if (bh && l < 32)
-      __builtin_amdgcn_global_load_lds((const void*)(bh + ks),
-                                       (__attribute__((address_space(3))) void*)bbuf, 4, 0, 0);
-    // K rows: lane (col, g) reads slot 16 hf + col, dims 32c + 8g .. +8
-    uint4 kraw[2][NC];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const char* krow = kh + (uint32_t)(ko[hf] + 16u * g);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kraw[hf][c] = *reinterpret_cast<const uint4*>(krow + 64 * c);
-    }
-    // the MFMAs below wait for the K rows, which were issued after the V rows
-    // and biases: every row load of the chunk has landed after this wait
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __asm__ volatile("" ::: "memory");
-    float s[8];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      // slot 4 hf + i <-> chunk row 16 hf + 4 g + i
-      float bias[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bh) {
-        const float4 b4 = *reinterpret_cast<const float4*>(bbuf + 16 * hf + 4 * g);
-        bias[0] = b4.x * kLog2e;
-        bias[1] = b4.y * kLog2e;
-        bias[2] = b4.z * kLog2e;
-        bias[3] = b4.w * kLog2e;
+    } else {
+      npass = 1;
+      int64_t ke = Nk;
+      if (MODE == 1) {
+        const int64_t nl = n_key_list[h];
+        ke = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
       }
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kraw[hf][c]), qop[c], sacc, 0, 0, 0);
-      // sacc[i] = score(list slot kc + 16 hf + 4 g + i, row col)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t j = (uint32_t)(kc + 16 * hf + 4 * g + i);
-        bool in = j - lo0 < n0;
-        if (P == 2) in = in || j - lo1 < n1;
-        s[4 * hf + i] = in ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
+      pke = (int)ke;
+      if (wvalid) pr0 = 0;
+    }
+    const int len = l < npass ? pke - pkb : 0;
+    // lane p < npass: pre = slots of the passes before p; workgroup row l's
+    // slot ranges [lo0, lo0 + n0) and, with two probes, [lo1, lo1 + n1)
+    int pre = 0, total = 0;
+    uint32_t lo0 = 0u, n0 = 0u, lo1 = 0u, n1 = 0u;
+    for (int p = 0; p < npass; ++p) {
+      const int lp = __builtin_amdgcn_readlane(len, p);
+      if (l == p) pre = total;
+      if (pr0 == p) {
+        lo0 = (uint32_t)total;
+        n0 = (uint32_t)lp;
       }
-    }
-    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mx = max_xor32(max_xor16(mx));
-    const float mnew = fmaxf(m, mx);
-    const float base = (mnew == -INFINITY) ? 0.f : mnew;
-    uint32_t pw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * i] - base), __builtin_amdgcn_exp2f(s[2 * i + 1] - base));
-    // the sum of the rounded weights that the PV product uses
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]),
-                                              __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
-    // rescale the running sums only where a row's (finite) max went up
-    if (ballot64(m != -INFINITY && mnew > m)) {
-      const float alpha = __builtin_amdgcn_exp2f(m - base);
-      lsum *= alpha;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        acc[b][0] *= alpha;
-        acc[b][1] *= alpha;
-        acc[b][2] *= alpha;
-        acc[b][3] *= alpha;
+      if (P == 2 && pr1 == p) {
+        lo1 = (uint32_t)total;
+        n1 = (uint32_t)lp;
       }
+      total += lp;
     }
-    lsum += psum;
-    m = mnew;
-    const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-    // V^T operand: lane (dim-row col, group g), slot si <-> chunk row
-    // 16 (si >> 2) + 4g + (si & 3), dims NB*col .. NB*col + NB - 1 (one per
-    // output block), read back from LDS
-    VRow<NB> vr[8];
-#pragma unroll
-    for (int si = 0; si < 8; ++si) vr[si].load(vbuf + (16 * (si >> 2) + 4 * g + (si & 3)) * D + NB * col);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      // (slot 2i's dim, slot 2i+1's dim) in one byte permute per dword
-      const uint32_t sel = (b & 1) ? 0x07060302u : 0x05040100u;
-      const uint4 w = make_uint4(__builtin_amdgcn_perm(vr[1].word(b), vr[0].word(b), sel),
-                                 __builtin_amdgcn_perm(vr[3].word(b), vr[2].word(b), sel),
-                                 __builtin_amdgcn_perm(vr[5].word(b), vr[4].word(b), sel),
-                                 __builtin_amdgcn_perm(vr[7].word(b), vr[6].word(b), sel));
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[b], 0, 0, 0);
+    // the MFMA row's ranges
+    const int src = 16 * wave + col;
+    const uint32_t rlo0 = (uint32_t)__shfl((int)lo0, src, FASTAR_WAVE);
+    const uint32_t rn0 = (uint32_t)__shfl((int)n0, src, FASTAR_WAVE);
+    uint32_t rlo1 = 0u, rn1 = 0u;
+    if (P == 2) {
+      rlo1 = (uint32_t)__shfl((int)lo1, src, FASTAR_WAVE);
+      rn1 = (uint32_t)__shfl((int)n1, src, FASTAR_WAVE);
     }
-    ks = ks_next;
+    const int kb_pre = pkb - pre;  // slot j of pass p is position j + kb_pre_p
+    const bool is_pass = l < npass;
+    // keys this lane loads for chunk c: the rows of its 16-byte loads, then
+    // (lanes < 8) the bias of chunk row 8 wave + l
+    auto chunk_keys = [&](int c, int* key) {
+      const int j0 = 32 * c, j1 = min(32 * c + 31, total - 1);
+      // the passes that chunk c overlaps: pa .. pb
+      const int pa = __popcll(ballot64(is_pass && pre <= j0)) - 1;
+      const int pb = __popcll(ballot64(is_pass && pre <= j1)) - 1;
+      const int base_a = __builtin_amdgcn_readlane(kb_pre, pa);
+#pragma unroll
+      for (int i = 0; i <= kDmaPerWave; ++i) {
+        const int row = i < kDmaPerWave ? (wave * kDmaPerWave + i) * kDmaRows + l / kPieces
+                                        : 8 * wave + (l & 7);
+        const int j = min(j0 + row, total - 1);  // past the end: a loaded, unused key
+        int base = base_a;
+        for (int p = pa + 1; p <= pb; ++p)
+          base = __builtin_amdgcn_readlane(pre, p) <= j ? __builtin_amdgcn_readlane(kb_pre, p) : base;
+        const int kk = j + base;
+        key[i] = (MODE == 2) ? kk : idx_h[kk];
+      }
+    };
+    // chunk c's K, V rows and biases into buffer c & 1; K row `row` holds
+    // piece p ^ (row % kPieces) at position p, so that the 16 lanes reading
+    // one piece of 16 different rows hit different banks
+    auto chunk_load = [&](const int* key, uint16_t* kt, uint16_t* vt, float* bt) {
+#pragma unroll
+      for (int i = 0; i < kDmaPerWave; ++i) {
+        const int row0 = (wave * kDmaPerWave + i) * kDmaRows;
+        const int row = row0 + l / kPieces;
+        const int pc = l % kPieces;
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(kh + (uint32_t)((uint32_t)key[i] * kst_b + (uint32_t)((pc ^ (row % kPieces)) * 16))),
+            (__attribute__((address_space(3))) void*)(kt + row0 * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(vh + (uint32_t)((uint32_t)key[i] * vst_b + (uint32_t)(pc * 16))),
+            (__attribute__((address_space(3))) void*)(vt + row0 * D), 16, 0, 0);
+      }
+      if (bh && l < 8)
+        __builtin_amdgcn_global_load_lds((const void*)(bh + key[kDmaPerWave]),
+                                         (__attribute__((address_space(3))) void*)(bt + 8 * wave), 4, 0, 0);
+    };
+    const int nch = (total + 31) / 32;
+    int key[kDmaPerWave + 1];
+    // chunk c, computed from the tiles kt, vt, bt while chunk c + 1 loads
+    // into the other buffers (kn, vn, bn)
+    auto chunk = [&](int c, const uint16_t* kt, const uint16_t* vt, const float* bt, uint16_t* kn,
+                     uint16_t* vn, float* bn) {
+      // chunk c's rows (this wave's loads) and chunk c + 1's keys have landed;
+      // after the barrier every wave's loads of chunk c have, and every wave
+      // is done with chunk c - 1, whose buffers chunk c + 1 takes
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      if (c + 1 < nch) chunk_load(key, kn, vn, bn);
+      if (c + 2 < nch) chunk_keys(c + 2, key);
+      const uint32_t kc = (uint32_t)(32 * c);
+      // skip a chunk none of the wave's rows uses
+      bool use = rn0 > 0u && rlo0 < kc + 32u && rlo0 + rn0 > kc;
+      if (P == 2) use = use || (rn1 > 0u && rlo1 < kc + 32u && rlo1 + rn1 > kc);
+      if (!ballot64(use)) return;
+      float s[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        // A operand: chunk row 16 hf + col, dims 32c + 8g .. +8 (piece 4c + g)
+        const int row = 16 * hf + col;
+        bf16x8_t kop[NC];
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+          kop[cc] = *reinterpret_cast<const bf16x8_t*>(&kt[row * D + (((4 * cc + g) ^ (row % kPieces)) * 8)]);
+        const float4 b4 = bh ? *reinterpret_cast<const float4*>(&bt[16 * hf + 4 * g])
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+        const float bias[4] = {b4.x * kLog2e, b4.y * kLog2e, b4.z * kLog2e, b4.w * kLog2e};
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[cc], qop[cc], sacc, 0, 0, 0);
+        // sacc[i] = score(list slot 32c + 16 hf + 4 g + i, row col)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t j = kc + (uint32_t)(16 * hf + 4 * g + i);
+          bool in = j - rlo0 < rn0;
+          if (P == 2) in = in || j - rlo1 < rn1;
+          s[4 * hf + i] = in ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      mx = max_xor32(max_xor16(mx));
+      const float mnew = fmaxf(m, mx);
+      const float base = (mnew == -INFINITY) ? 0.f : mnew;
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(s[2 * i] - base), __builtin_amdgcn_exp2f(s[2 * i + 1] - base));
+      // the sum of the rounded weights that the PV product uses
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]),
+                                                __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+      // rescale the running sums only where a row's (finite) max went up
+      if (ballot64(m != -INFINITY && mnew > m)) {
+        const float alpha = __builtin_amdgcn_exp2f(m - base);
+        lsum *= alpha;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          acc[bb][0] *= alpha;
+          acc[bb][1] *= alpha;
+          acc[bb][2] *= alpha;
+          acc[bb][3] *= alpha;
+        }
+      }
+      lsum += psum;
+      m = mnew;
+      const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      // V^T operand: lane (dim-row col, group g), slot si <-> chunk row
+      // 16 (si >> 2) + 4g + (si & 3), dims NB*col .. NB*col + NB - 1 (one per
+      // output block)
+      VRow<NB> vr[8];
+#pragma unroll
+      for (int si = 0; si < 8; ++si) vr[si].load(&vt[(16 * (si >> 2) + 4 * g + (si & 3)) * D + NB * col]);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        // (slot 2i's dim, slot 2i+1's dim) in one byte permute per dword
+        const uint32_t sel = (bb & 1) ? 0x07060302u : 0x05040100u;
+        const uint4 w = make_uint4(__builtin_amdgcn_perm(vr[1].word(bb), vr[0].word(bb), sel),
+                                   __builtin_amdgcn_perm(vr[3].word(bb), vr[2].word(bb), sel),
+                                   __builtin_amdgcn_perm(vr[5].word(bb), vr[4].word(bb), sel),
+                                   __builtin_amdgcn_perm(vr[7].word(bb), vr[6].word(bb), sel));
+        acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[bb], 0, 0, 0);
+      }
+    };
+    if (nch > 0) {
+      chunk_keys(0, key);
+      chunk_load(key, ktA, vtA, btA);
+      if (nch > 1) chunk_keys(1, key);
+    }
+    for (int c = 0; c < nch; c += 2) {
+      chunk(c, ktA, vtA, btA, ktB, vtB, btB);
+      if (c + 1 < nch) chunk(c + 1, ktB, vtB, btB, ktA, vtA, btA);
+    }
+    if (MODE != 0 || npass < FASTAR_WAVE) break;
+    // the next batch refills both buffers: every wave is done with them
+    __syncthreads();
   }
   lsum = sum_xor32(sum_xor16(lsum));
   if (!rvalid) return;

@@ -83,18 +83,25 @@ __device__ __forceinline__ float max_xor32(float v) { const f32x2_t p = pair_xor
 __device__ __forceinline__ float sum_xor16(float v) { const f32x2_t p = pair_xor16(v); return p.x + p.y; }
 __device__ __forceinline__ float sum_xor32(float v) { const f32x2_t p = pair_xor32(v); return p.x + p.y; }
 
-// minimum over the wave without LDS: DPP pairs within quads (lane ^ 1,
-// lane ^ 2), then each half-row and row with its mirror image, then the
-// permlane swaps across rows
-__device__ __forceinline__ int wave_min_dpp(int v) {
-  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = min(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
+// a commutative, associative combine over the wave without LDS: DPP pairs
+// within quads (lane ^ 1, lane ^ 2), then each half-row and row with its
+// mirror image, then the permlane swaps across rows
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_dpp(int v, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false));  // row_mirror
   auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
-  v = min((int)r[0], (int)r[1]);
+  v = op((int)r[0], (int)r[1]);
   r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
-  return min((int)r[0], (int)r[1]);
+  return op((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  return wave_reduce_dpp(v, [](int a, int b) { return min(a, b); });
+}
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  return wave_reduce_dpp(v, [](int a, int b) { return a + b; });
 }
 
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }

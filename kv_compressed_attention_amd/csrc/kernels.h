@@ -42,7 +42,7 @@ struct MergeWs {
   int32_t* tbk;       // [H][n_frames+1][T] their buckets
   int32_t* candg;     // [H][T]
   int32_t* link;      // [H][n_frames][T]
-  int32_t* gid;       // [H][n_frames][T]
+  int32_t* ocnt;      // [H][ceil(n_frames T / 64) + 1]
   int32_t* nextj;     // [H][n_frames][T]
   int32_t* index_ws;  // bucket index scratch
 };

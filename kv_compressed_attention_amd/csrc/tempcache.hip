@@ -8,7 +8,7 @@
 // with the keys of its own bucket for a candidate, so matching and the
 // one-to-one resolution of all frames are independent per (frame, bucket)
 // and run in one launch; only the numbering of new groups is sequential.
-// Five launches per call:
+// Four launches per call:
 //   tc_index    per (table, head): the frontier and each new frame sorted by
 //               bucket (counting sort in LDS: bucket offsets, tokens, buckets);
 //   tc_match    one workgroup per 64 sorted keys of a frame, rounded to whole
@@ -17,10 +17,10 @@
 //               different buckets masked), best candidate per key, proposal if
 //               it passes tau; then per candidate the proposer of largest
 //               cosine (ties: smaller j) wins and links to it; the other keys
-//               open groups;
-//   tc_number   one workgroup per head: new groups numbered in (frame, j)
-//               order, the group count;
-//   tc_apply    16 lanes per chain of tokens (a token that opens a group or
+//               open groups and are counted per 64 tokens of (frame, j)
+//               order;
+//   tc_apply    new groups numbered in (frame, j) order from those counts,
+//               then 16 lanes per chain of tokens (a token that opens a group or
 //               extends a frontier group, then its links through the frames):
 //               float32 value sum in frame order, count, mean (rounded once
 //               to the cache dtype), last key, its bucket and ln count, the
@@ -211,7 +211,9 @@ struct MergeArgs {
   int32_t* candg;     // [H][Tf] groups of table 0's tokens
   int32_t* link;      // [H][F][Tf] f = 0: frontier group the token extends;
                       //            f > 0: frame f - 1 token it extends; -1: opens a group
-  int32_t* gid;       // [H][F][Tf] group a token opens (-1: no room left)
+  int32_t* ocnt;      // [H][nblk + 1] tokens that open groups, per 64 tokens of
+                      // (frame, j) order (nblk = ceil(F Tf / 64) blocks), then
+                      // the group count before the call
   int32_t* nextj;     // [H][F][Tf] token of frame f + 1 that extends this one, or -1
 };
 
@@ -224,9 +226,12 @@ __device__ __forceinline__ int64_t tok_off(const MergeArgs& a, int h, int t) {
 __device__ __forceinline__ int64_t frame_off(const MergeArgs& a, int h, int f) {
   return ((int64_t)h * a.F + f) * a.Tf;
 }
+__device__ __forceinline__ int ocnt_blocks(const MergeArgs& a) { return (a.F * a.Tf + 63) >> 6; }
 
 // Table 0 from the frontier (blockIdx.x == 0) or table f + 1 from new frame f.
-// One workgroup per (table, head).  Also clears new frame f's nextj links.
+// One workgroup per (table, head).  Also clears new frame f's nextj links
+// and (table 0) the head's opener counts, next to which it keeps the group
+// count before the call.
 __global__ __launch_bounds__(1024) void tc_index_kernel(
     const int32_t* __restrict__ frontier, const int32_t* __restrict__ rep_bucket,
     const int32_t* __restrict__ n_groups, const int32_t* __restrict__ kbucket, MergeArgs a) {
@@ -237,6 +242,9 @@ __global__ __launch_bounds__(1024) void tc_index_kernel(
   int32_t* tok = a.tok + tok_off(a, h, t);
   int32_t* tbk = a.tbk + tok_off(a, h, t);
   if (t == 0) {
+    const int nblk = ocnt_blocks(a);
+    int32_t* oc = a.ocnt + (int64_t)h * (nblk + 1);
+    for (int i = threadIdx.x; i <= nblk; i += blockDim.x) oc[i] = i < nblk ? 0 : n_groups[h];
     const bool empty = n_groups[h] <= 0;
     const int32_t* fr = frontier + (int64_t)h * a.Tf;
     const int32_t* rb = rep_bucket + (int64_t)h * a.cap;
@@ -750,6 +758,7 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
         if (f > 0) a.nextj[frame_off(a, h, f - 1) + pj] = j;
       }
       a.link[fo + j] = lk;
+      if (lk < 0) atomicAdd(&a.ocnt[(int64_t)h * (ocnt_blocks(a) + 1) + ((f * a.Tf + j) >> 6)], 1);
     }
   }
 }
@@ -796,63 +805,11 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
     match_group<T, D, false>(x, a, h, p0, p1, c0, c1, frontier, lds);
 }
 
-// One workgroup per head: the tokens that open groups, in (frame, j) order,
-// get the next group ids; ids from the capacity on are dropped (-1).
-__global__ __launch_bounds__(1024) void tc_number_kernel(int32_t* __restrict__ n_groups,
-                                                         MergeArgs a) {
-  constexpr int kPerThread = 8;  // links loaded up front per thread and round
-  __shared__ int wsum[16];
-  __shared__ int running;
-  const int h = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = lane_id();
-  const int nw = (int)(blockDim.x >> 6);
-  const int ng0 = n_groups[h];
-  const int total = a.F * a.Tf;
-  const int32_t* lk = a.link + frame_off(a, h, 0);
-  int32_t* gd = a.gid + frame_off(a, h, 0);
-  if (tid == 0) running = 0;
-  __syncthreads();
-  for (int base0 = 0; base0 < total; base0 += kPerThread * blockDim.x) {
-    // the links of this round, all in flight together
-    int32_t l8[kPerThread];
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int idx = base0 + u * blockDim.x + tid;
-      l8[u] = idx < total ? lk[idx] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int base = base0 + u * blockDim.x;
-      if (base >= total) break;  // uniform
-      const int idx = base + tid;
-      const bool isnew = idx < total && l8[u] < 0;
-      const uint64_t bal = ballot64(isnew);
-      if (lane == 0) wsum[wave] = __popcll(bal);
-      __syncthreads();
-      int rank = running + __popcll(bal & lanemask_lt());
-      for (int w = 0; w < wave; ++w) rank += wsum[w];
-      if (isnew) {
-        const int64_t gg = (int64_t)ng0 + rank;
-        gd[idx] = gg < a.cap ? (int32_t)gg : -1;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int sum = 0;
-        for (int w = 0; w < nw; ++w) sum += wsum[w];
-        running += sum;
-      }
-      __syncthreads();
-    }
-  }
-  if (tid == 0) {
-    const int64_t ng = (int64_t)ng0 + running;
-    n_groups[h] = ng < a.cap ? (int32_t)ng : a.cap;
-  }
-}
-
-// Group rows, 16 lanes per chain (D/16 elements each).  A chain starts at a
+// Group rows, 16 lanes per chain (D/16 elements each).  A token that opens a
+// group gets the group count before the call plus the number of tokens
+// before it in (frame, j) order that open groups (the counts of the 64-token
+// blocks before its own, then a ballot over its block's links); ids from
+// the capacity on are dropped (-1).  A chain starts at a
 // token that opens a group, or at a frame-0 token that extends a frontier
 // group; it follows nextj through the later frames.  Value sums are
 // accumulated frame by frame in float32, exactly as merging the frames one at
@@ -862,7 +819,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void tc_apply_kernel(
     T* __restrict__ rep_k, T* __restrict__ v_mean, float* __restrict__ v_sum,
     int32_t* __restrict__ count, float* __restrict__ log_count, int32_t* __restrict__ rep_bucket,
-    int32_t* __restrict__ frontier, int32_t* __restrict__ group_of_new,
+    int32_t* __restrict__ n_groups, int32_t* __restrict__ frontier, int32_t* __restrict__ group_of_new,
     const T* __restrict__ knew, int64_t k_sh, int64_t k_st, const T* __restrict__ vnew,
     int64_t v_sh, int64_t v_st, const int32_t* __restrict__ kbucket, MergeArgs a,
     fastar_diag_t* __restrict__ diag) {
@@ -870,7 +827,31 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   const int h = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
-  if (idx >= (int64_t)a.F * a.Tf) return;
+  const int total = a.F * a.Tf;
+  // the workgroup's 16 tokens lie in one 64-token block; with all lanes
+  // present: openers in the blocks before it and in it, up to each token
+  const int nblk = ocnt_blocks(a);
+  const int32_t* oc = a.ocnt + (int64_t)h * (nblk + 1);
+  const int blk = (int)((blockIdx.x * 16) >> 6);
+  const int lane = lane_id();
+  const int ng0 = oc[nblk];
+  int before = 0;
+  for (int i = lane; i < blk; i += FASTAR_WAVE) before += oc[i];
+  const int bpos = blk * 64 + lane;
+  const bool opens = bpos < total && a.link[frame_off(a, h, 0) + bpos] < 0;
+  const uint64_t openers = ballot64(opens);
+  before = wave_sum_dpp(before);
+  if (blockIdx.x == 0 && threadIdx.x < FASTAR_WAVE) {
+    // the new group count
+    int all = 0;
+    for (int i = lane; i < nblk; i += FASTAR_WAVE) all += oc[i];
+    all = wave_sum_dpp(all);
+    if (lane == 0) {
+      const int64_t ng = (int64_t)ng0 + all;
+      n_groups[h] = ng < a.cap ? (int32_t)ng : a.cap;
+    }
+  }
+  if (idx >= total) return;
   int f = (int)(idx / a.Tf);
   int j = (int)(idx - (int64_t)f * a.Tf);
   const T* kh = knew + (int64_t)h * k_sh + sub * EPL;
@@ -879,7 +860,10 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   // everything the token itself needs, in flight together: its link, the
   // group it may open, its successor, its value and key rows and its bucket
   const int lk = a.link[frame_off(a, h, f) + j];
-  const int gd = a.gid[frame_off(a, h, f) + j];  // meaningful when lk < 0
+  // meaningful when lk < 0
+  const int64_t gd64 = (int64_t)ng0 + before +
+                       __popcll(openers & ((1ull << (int)(idx - (int64_t)blk * 64)) - 1ull));
+  const int gd = gd64 < a.cap ? (int32_t)gd64 : -1;
   int nx = f + 1 < a.F ? a.nextj[frame_off(a, h, f) + j] : -1;
   float vv[EPL], kk[EPL];
   Chunk<T, EPL>::load(vh + ((int64_t)f * a.Tf + j) * v_st, vv);
@@ -965,7 +949,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   a.tbk = ws.tbk;
   a.candg = ws.candg;
   a.link = ws.link;
-  a.gid = ws.gid;
+  a.ocnt = ws.ocnt;
   a.nextj = ws.nextj;
   hipLaunchKernelGGL(tc_index_kernel, dim3(F + 1, H), dim3(1024),
                      ((size_t)1 << c.n_bits) * sizeof(int32_t), s, c.frontier, c.rep_bucket,
@@ -976,10 +960,9 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
                      ((size_t)3 * Tf + 2 * kStageKeys + 3 * kStageCands) * sizeof(int32_t), s,
                      (const T*)c.rep_k,
                      (const T*)kn.data, kn.stride_head, kn.stride_token, c.frontier, tau, a, diag);
-  hipLaunchKernelGGL(tc_number_kernel, dim3(H), dim3(1024), 0, s, c.n_groups, a);
   hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)F * Tf + 15) / 16), (unsigned)H),
                      dim3(256), 0, s, (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count,
-                     c.rep_bucket, c.frontier, group_of_new, (const T*)kn.data, kn.stride_head,
+                     c.rep_bucket, c.n_groups, c.frontier, group_of_new, (const T*)kn.data, kn.stride_head,
                      kn.stride_token, (const T*)vn.data, vn.stride_head, vn.stride_token, kb, a,
                      diag);
   hipError_t e = hipGetLastError();
