@@ -6,6 +6,7 @@
  *
  * Four operations, after the method's three modules and their shared hashing:
  *   fastar_hash             SimHash bucket ids (+ bucket-contiguous index)
+ *   fastar_hash_multi       the ids of several tensors in one launch
  *   fastar_tempcache_merge  TempCache: merge new frames into the compressed cache
  *   fastar_prune_prompt     AnnCA: drop prompt tokens no query shares a bucket with
  *   fastar_bucket_attention AnnSA / AnnCA attention, online softmax on MFMA
@@ -102,6 +103,22 @@ fastar_status_t fastar_hash(const fastar_tensor_t* x, const void* planes, int n_
                             int n_probes, int32_t* bucket, int32_t* offsets, int32_t* perm,
                             void* ws, size_t ws_bytes, fastar_diag_t* diag,
                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fastar_hash_multi -- the ids of fastar_hash (no index) for up to four
+ * tensors hashed with the same planes, in one launch for bf16 (the chunk's
+ * queries, new keys and prompt keys share one hashing: paper.rainbus.top
+ * "technical novelty").
+ *   count     1..4.
+ *   x         [count] tensors [H_i][N_i][d], one dtype and d.
+ *   n_probes  [count] host ints, 1 or 2 each.
+ *   bucket    [count] device outputs [H_i][N_i][n_probes[i]] int32.
+ *   planes, n_bits, diag: as for fastar_hash.  Build an index of any of the
+ *   ids with fastar_bucket_index.
+ * ---------------------------------------------------------------------- */
+fastar_status_t fastar_hash_multi(int count, const fastar_tensor_t* const* x, const int* n_probes,
+                                  int32_t* const* bucket, const void* planes, int n_bits,
+                                  fastar_diag_t* diag, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fastar_bucket_index -- the bucket-contiguous index of fastar_hash on its

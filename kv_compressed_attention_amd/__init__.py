@@ -12,6 +12,7 @@ from .fastar import (  # noqa: F401
     fastar_bucket_attention,
     fastar_bucket_index,
     fastar_hash,
+    fastar_hash_multi,
     fastar_prune_prompt,
     fastar_tempcache_merge,
     fastar_version,

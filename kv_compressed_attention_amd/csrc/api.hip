@@ -124,6 +124,35 @@ fastar_status_t fastar_hash(const fastar_tensor_t* x, const void* planes, int n_
 }
 
 // ---------------------------------------------------------------------------
+fastar_status_t fastar_hash_multi(int count, const fastar_tensor_t* const* x, const int* n_probes,
+                                  int32_t* const* bucket, const void* planes, int n_bits,
+                                  fastar_diag_t* diag, hipStream_t stream) {
+  if (count < 1 || count > fastar::kMaxHashJobs)
+    return fail(FASTAR_ERR_INVALID, "count %d not in [1, %d]", count, fastar::kMaxHashJobs);
+  if (!x || !n_probes || !bucket) return fail(FASTAR_ERR_INVALID, "x, n_probes and bucket must be arrays");
+  fastar::HashJobs jobs;
+  jobs.count = count;
+  bool any = false;
+  for (int i = 0; i < count; ++i) {
+    fastar_status_t st = check_tensor(x[i], "x[i]");
+    if (st != FASTAR_OK) return st;
+    if ((st = check_bits(n_bits, n_probes[i])) != FASTAR_OK) return st;
+    if (x[i]->dtype != x[0]->dtype || x[i]->dim != x[0]->dim)
+      return fail(FASTAR_ERR_INVALID, "x[%d]: dtype and dim must match x[0]", i);
+    const bool nonempty = (int64_t)x[i]->heads * x[i]->tokens > 0;
+    if (nonempty && !bucket[i]) return fail(FASTAR_ERR_INVALID, "bucket[%d] is NULL", i);
+    any = any || nonempty;
+    jobs.j[i] = fastar::HashJob{x[i]->data, x[i]->stride_head, x[i]->stride_token, x[i]->tokens,
+                                x[i]->heads, n_probes[i], bucket[i]};
+  }
+  if (!any) return FASTAR_OK;
+  if (n_bits > 0 && (!planes || !aligned16(planes)))
+    return fail(FASTAR_ERR_INVALID, "planes must be a non-null, 16-byte aligned pointer");
+  return hip_status(fastar::launch_hash_multi(jobs, x[0]->dim, x[0]->dtype, planes, n_bits, diag, stream),
+                    "hash_multi");
+}
+
+// ---------------------------------------------------------------------------
 size_t fastar_bucket_index_workspace(int heads, int64_t n) {
   if (heads < 0 || n < 0) return 0;
   return align_up(16 * (size_t)heads * (size_t)n);

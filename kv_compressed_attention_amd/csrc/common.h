@@ -82,6 +82,14 @@ __device__ __forceinline__ float max_xor16(float v) { const f32x2_t p = pair_xor
 __device__ __forceinline__ float max_xor32(float v) { const f32x2_t p = pair_xor32(v); return fmaxf(p.x, p.y); }
 __device__ __forceinline__ float sum_xor16(float v) { const f32x2_t p = pair_xor16(v); return p.x + p.y; }
 __device__ __forceinline__ float sum_xor32(float v) { const f32x2_t p = pair_xor32(v); return p.x + p.y; }
+__device__ __forceinline__ uint32_t or_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return r[0] | r[1];
+}
+__device__ __forceinline__ uint32_t or_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return r[0] | r[1];
+}
 
 // a commutative, associative combine over the wave without LDS: DPP pairs
 // within quads (lane ^ 1, lane ^ 2), then each half-row and row with its

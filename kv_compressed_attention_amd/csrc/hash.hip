@@ -62,89 +62,113 @@ __device__ __forceinline__ float kcert() {
   return (float)D * 0x1p-22f * (1.0f + 0x1p-10f);
 }
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int m = 1; m < FASTAR_WAVE; m <<= 1) v += __shfl_xor(v, m, FASTAR_WAVE);
-  return v;
+__device__ __forceinline__ double dswap16(double v) {  // the value of lane ^ 16
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  // each pair holds this lane's and the partner's word, in the same order
+  const uint32_t l0 = lo[0], l1 = lo[1], h0 = hi[0], h1 = hi[1];
+  const uint64_t a0 = ((uint64_t)h0 << 32) | l0, a1 = ((uint64_t)h1 << 32) | l1;
+  return __builtin_bit_cast(double, a0 == u ? a1 : a0);
+}
+__device__ __forceinline__ double dswap32(double v) {  // the value of lane ^ 32
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+  const uint32_t l0 = lo[0], l1 = lo[1], h0 = hi[0], h1 = hi[1];
+  const uint64_t a0 = ((uint64_t)h0 << 32) | l0, a1 = ((uint64_t)h1 << 32) | l1;
+  return __builtin_bit_cast(double, a0 == u ? a1 : a0);
+}
+// v summed over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the same value in all four)
+__device__ __forceinline__ double sum4_d(double v) {
+  const double w = v + dswap16(v);
+  return w + dswap32(w);
 }
 
-// Re-evaluates one row in float64, the whole wave (each lane holds D/64
-// dims), and writes its ids; a sign float64 cannot certify is settled
-// exactly by lane 0 with an expansion sum in E (D + 2 doubles of LDS).
-template <typename T, int D, int P>
-__device__ void hash_fixup_row(const T* __restrict__ xr, const T* __restrict__ planes, int nb,
-                               int32_t* __restrict__ o, fastar_diag_t* __restrict__ diag,
-                               double* E) {
-  constexpr int L = D / FASTAR_WAVE;
+// Re-evaluates one row in float64 and writes its ids (o: the row's output,
+// the same in every lane).  Lane 16s + p takes the dims [s D/4, (s+1) D/4)
+// of hyperplane p: serial sums of exact products, then added over the four
+// slices.  The row (xr: [D]) and the hyperplanes (ps, row stride pst) are
+// read from LDS.  A sign float64 cannot certify is settled exactly with an
+// expansion sum in E (D + 2 doubles of LDS); the second probe's distances
+// and error bounds go through DE (32 doubles of LDS).
+template <typename T, int D>
+__device__ void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t* __restrict__ o, int P,
+                               int nb, fastar_diag_t* __restrict__ diag, double* E, double* DE) {
+  constexpr int DS = D / 4;
   const int lane = lane_id();
-  double xv[L];
-#pragma unroll
-  for (int k = 0; k < L; ++k) xv[k] = (double)Elem<T>::load(xr, lane + FASTAR_WAVE * k);
-  uint32_t bits = 0;
-  double dist[16], derr[16];
-  bool unresolved = false;
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    dist[p] = 0.0;
-    derr[p] = 0.0;
-    if (p < nb) {
-      double s = 0.0, a = 0.0, n2 = 0.0;
-#pragma unroll
-      for (int k = 0; k < L; ++k) {
-        const double rv = (double)Elem<T>::load(planes, (int64_t)p * D + lane + FASTAR_WAVE * k);
-        const double pr = xv[k] * rv;  // exact: at most 48 significant bits
-        s += pr;
-        a += fabs(pr);
-        n2 += rv * rv;
-      }
-      s = wave_sum_d(s);
-      a = wave_sum_d(a);
-      n2 = wave_sum_d(n2);
-      const double bound = 2.0 * (D + 8) * 0x1p-53 * a;
-      int sg;
-      if (fabs(s) > bound) {
-        sg = s > 0.0 ? 1 : -1;
-      } else if (a == 0.0) {
-        sg = 0;
-      } else {
-        int sg0 = 0;
-        if (lane == 0) {
-          int m = 0;
-          for (int d = 0; d < D; ++d) {
-            const double xd = (double)Elem<T>::load(xr, d);
-            const double rd = (double)Elem<T>::load(planes, (int64_t)p * D + d);
-            m = grow_expansion(E, m, xd * rd);
-          }
-          sg0 = expansion_sign(E, m);
-          if (diag) atomicAdd(&diag->hash_exact_signs, 1u);
-        }
-        sg = __shfl(sg0, 0, FASTAR_WAVE);
-      }
-      if (sg > 0) bits |= 1u << p;
-      if (P == 2) {
-        const double rn = sqrt(n2);
-        dist[p] = rn > 0.0 ? fabs(s) / rn : 0.0;
-        derr[p] = (a == 0.0) ? 0.0 : (rn > 0.0 ? bound / rn : 0.0) + dist[p] * (2 * D + 8) * 0x1p-53;
-      }
+  const int sl = lane >> 4, p = lane & 15;
+  const bool active = p < nb;
+  const T* rp = ps + (active ? p : 0) * pst;
+  double s = 0.0, a = 0.0, n2 = 0.0;
+  if (active) {
+#pragma unroll 8
+    for (int d = sl * DS; d < sl * DS + DS; ++d) {
+      const double xv = (double)Elem<T>::load(xr, d);
+      const double rv = (double)Elem<T>::load(rp, d);
+      const double pr = xv * rv;  // exact: at most 48 significant bits
+      s += pr;
+      a += fabs(pr);
+      n2 += rv * rv;
     }
   }
-  int j1 = 0;
-  if (P == 2) {
-    double d1 = dist[0], e1 = derr[0];
-#pragma unroll
-    for (int p = 1; p < 16; ++p) {
-      if (p < nb && dist[p] < d1) {
-        j1 = p;
-        d1 = dist[p];
-        e1 = derr[p];
-      }
+  s = sum4_d(s);
+  a = sum4_d(a);
+  n2 = sum4_d(n2);
+  // any order of the D additions is within this bound
+  const double bound = 2.0 * (D + 8) * 0x1p-53 * a;
+  int sg = 0;
+  bool need_exact = false;
+  if (active) {
+    if (fabs(s) > bound) sg = s > 0.0 ? 1 : -1;
+    else need_exact = a != 0.0 && sl == 0;
+  }
+  uint64_t exact = ballot64(need_exact);
+  while (exact) {
+    const int src = __builtin_ctzll(exact);
+    exact &= exact - 1;
+    int sx = 0;
+    if (lane == src) {
+      int m = 0;
+      for (int d = 0; d < D; ++d)
+        m = grow_expansion(E, m, (double)Elem<T>::load(xr, d) * (double)Elem<T>::load(rp, d));
+      sx = expansion_sign(E, m);
+      if (diag) atomicAdd(&diag->hash_exact_signs, 1u);
     }
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      if (p < nb && p != j1) {
-        const double gap = dist[p] - d1;
-        const double err = derr[p] + e1;
-        if (err > 0.0 && gap <= err) unresolved = true;
+    sx = __shfl(sx, src, FASTAR_WAVE);
+    if (p == src) sg = sx;
+  }
+  const uint32_t bits = (uint32_t)(ballot64(sg > 0) & 0xFFFFu);
+  int j1 = 0;
+  bool unresolved = false;
+  if (P == 2) {
+    if (sl == 0) {
+      double dist = 0.0, derr = 0.0;
+      if (active) {
+        const double rn = sqrt(n2);
+        dist = rn > 0.0 ? fabs(s) / rn : 0.0;
+        derr = (a == 0.0) ? 0.0 : (rn > 0.0 ? bound / rn : 0.0) + dist * (2 * D + 8) * 0x1p-53;
+      }
+      DE[p] = dist;
+      DE[16 + p] = derr;
+    }
+    if (lane == 0) {
+      const double* dist = DE;
+      const double* derr = DE + 16;
+      double d1 = dist[0], e1 = derr[0];
+      for (int q = 1; q < nb; ++q) {
+        if (dist[q] < d1) {
+          j1 = q;
+          d1 = dist[q];
+          e1 = derr[q];
+        }
+      }
+      for (int q = 0; q < nb; ++q) {
+        if (q != j1) {
+          const double gap = dist[q] - d1;
+          const double err = derr[q] + e1;
+          if (err > 0.0 && gap <= err) unresolved = true;
+        }
       }
     }
   }
@@ -158,16 +182,73 @@ __device__ void hash_fixup_row(const T* __restrict__ xr, const T* __restrict__ p
   }
 }
 
-template <int D, int P>
-__global__ __launch_bounds__(256) void hash_bf16_kernel(
-    const uint16_t* __restrict__ x, int64_t sh, int64_t st, int H, int64_t N,
-    const uint16_t* __restrict__ planes, int nb, int32_t* __restrict__ bucket,
-    fastar_diag_t* __restrict__ diag) {
+// One wave per tile of 16 rows of one of the launch's tensors (tiles of
+// tensor i are numbered from jobs.tile_end[i - 1]); the first tile's rows
+// are requested before the hyperplanes are read.
+template <int D>
+__global__ __launch_bounds__(256) void hash_bf16_kernel(HashJobs jobs, const uint16_t* __restrict__ planes,
+                                                        int nb, fastar_diag_t* __restrict__ diag) {
   constexpr int NC = D / 32;
+  constexpr int kPst = D + 8;  // padded hyperplane rows: lanes reading 16 planes hit different banks
+  __shared__ __attribute__((aligned(16))) uint16_t spl[16 * kPst];
+  __shared__ __attribute__((aligned(16))) uint16_t sxr[4][D];  // per wave: the row being re-evaluated
   __shared__ double ex[4][D + 2];
+  __shared__ double de[4][32];
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
+  const int wv = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 16 * D / 8; i += blockDim.x) {
+    const int pp = i / (D / 8), c8 = i % (D / 8);
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (pp < nb) u = *reinterpret_cast<const uint4*>(planes + (int64_t)pp * D + 8 * c8);
+    *reinterpret_cast<uint4*>(&spl[pp * kPst + 8 * c8]) = u;
+  }
+  __syncthreads();
+  const int64_t total = jobs.tile_end[jobs.count - 1];
+  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t first = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  // tile -> tensor, head, first row (wave-uniform)
+  struct Where {
+    const uint16_t* x;
+    int64_t sh, st, N, r0;
+    int h, P;
+    int32_t* bucket;
+  };
+  auto where = [&](int64_t tile) {
+    int ji = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxHashJobs; ++i)
+      if (i < jobs.count && tile >= jobs.tile_end[i - 1]) ji = i;
+    Where w;
+    int64_t t0 = 0;
+    // field-wise selects: no dynamic indexing of the argument block
+#pragma unroll
+    for (int i = 0; i < kMaxHashJobs; ++i)
+      if (i == ji) {
+        w.x = (const uint16_t*)jobs.j[i].x;
+        w.sh = jobs.j[i].sh;
+        w.st = jobs.j[i].st;
+        w.N = jobs.j[i].N;
+        w.P = jobs.j[i].P;
+        w.bucket = jobs.j[i].bucket;
+        t0 = i > 0 ? jobs.tile_end[i - 1] : 0;
+      }
+    const int64_t tph = (w.N + 15) >> 4;
+    const int64_t local = tile - t0;
+    w.h = (int)(local / tph);
+    w.r0 = (local - (int64_t)w.h * tph) << 4;
+    return w;
+  };
+  auto load_rows = [&](const Where& w, uint4* u) {
+    const int64_t row = w.r0 + col;
+    const bool valid = row < w.N;
+    const uint16_t* xr = w.x + (int64_t)w.h * w.sh + (valid ? row : w.r0) * w.st;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) u[c] = *reinterpret_cast<const uint4*>(xr + 32 * c + 8 * g);
+  };
+  uint4 xu[NC];
+  if (first < total) load_rows(where(first), xu);
 
   // A operand: hyperplane `col`, dims 32c + 8g .. +8 of chunk c
   bf16x8_t aop[NC];
@@ -186,27 +267,24 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
   for (int i = 0; i < 4; ++i) rnorm[i] = sqrtf(__shfl(r2, 4 * g + i, FASTAR_WAVE));
 
   const float kc = kcert<D>();
-  const int64_t tiles_per_head = (N + 15) >> 4;
-  const int64_t total = (int64_t)H * tiles_per_head;
-  const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x >> 6);
-  for (int64_t tile = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); tile < total;
-       tile += nwaves) {
-    const int h = (int)(tile / tiles_per_head);
-    const int64_t r0 = (tile - (int64_t)h * tiles_per_head) << 4;
-    const int64_t row = r0 + col;
-    const bool valid = row < N;
-    const uint16_t* xr = x + (int64_t)h * sh + (valid ? row : r0) * st;
+  for (int64_t tile = first; tile < total; tile += nwaves) {
+    const Where w = where(tile);
+    // the next tile's rows load while this one is hashed
+    uint4 xn[NC];
+    if (tile + nwaves < total) load_rows(where(tile + nwaves), xn);
+    const int64_t row = w.r0 + col;
+    const bool valid = row < w.N;
+    const int P = w.P;
     bf16x8_t bop[NC];
     float x2 = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      uint4 u = *reinterpret_cast<const uint4*>(xr + 32 * c + 8 * g);
+      uint4 u = xu[c];
       if (!valid) u = make_uint4(0u, 0u, 0u, 0u);
       x2 += sumsq_bf16x8(u);
       bop[c] = __builtin_bit_cast(bf16x8_t, u);
     }
-    x2 += shfl_xor_f(x2, 16);
-    x2 += shfl_xor_f(x2, 32);
+    x2 = sum_xor32(sum_xor16(x2));
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[c], bop[c], acc, 0, 0, 0);
@@ -235,10 +313,8 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
         }
       }
     }
-    bits |= (uint32_t)shfl_xor_i((int)bits, 16);
-    bits |= (uint32_t)shfl_xor_i((int)bits, 32);
-    amb |= shfl_xor_i(amb, 16);
-    amb |= shfl_xor_i(amb, 32);
+    bits = or_xor32(or_xor16(bits));
+    amb = (int)or_xor32(or_xor16((uint32_t)amb));
     if (P == 2) {
       nearest_merge(nr, 16);
       nearest_merge(nr, 32);
@@ -247,20 +323,26 @@ __global__ __launch_bounds__(256) void hash_bf16_kernel(
       if (nr.d2 - nr.d1 <= err) amb = 1;
     }
     if (valid && g == 0 && !amb) {
-      int32_t* o = bucket + ((int64_t)h * N + row) * P;
+      int32_t* o = w.bucket + ((int64_t)w.h * w.N + row) * P;
       o[0] = (int32_t)bits;
       if (P == 2) o[1] = (int32_t)(bits ^ (1u << nr.j1));
     }
-    // rows float32 cannot certify: float64 by the whole wave, one at a time
-    uint64_t ab = ballot64(valid && g == 0 && amb);
+    // rows float32 cannot certify: float64 by the whole wave, one at a
+    // time, from an LDS copy
+    uint64_t ab = ballot64(valid && g == 0 && amb);  // bit = the row's column
     while (ab) {
-      const int src = __builtin_ctzll(ab);  // = the row's column (g == 0)
+      const int r = __builtin_ctzll(ab);  // wave-uniform
       ab &= ab - 1;
-      const int64_t rr = r0 + src;
-      hash_fixup_row<uint16_t, D, P>(x + (int64_t)h * sh + rr * st, planes, nb,
-                                     bucket + ((int64_t)h * N + rr) * P, diag,
-                                     ex[threadIdx.x >> 6]);
+      if (col == r) {
+        // the 4 lanes holding row r copy its dims 32c + 8g .. +8
+#pragma unroll
+        for (int c = 0; c < NC; ++c) *reinterpret_cast<uint4*>(&sxr[wv][32 * c + 8 * g]) = xu[c];
+      }
+      hash_fixup_row<uint16_t, D>(sxr[wv], spl, kPst, w.bucket + ((int64_t)w.h * w.N + w.r0 + r) * P,
+                                  P, nb, diag, ex[wv], de[wv]);
     }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) xu[c] = xn[c];
   }
 }
 
@@ -270,7 +352,9 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
     const float* __restrict__ planes, int nb, int32_t* __restrict__ bucket,
     fastar_diag_t* __restrict__ diag) {
   __shared__ float sp[16][D];
+  __shared__ float sxr[4][D];  // per wave: the row being re-evaluated
   __shared__ double ex[4][D + 2];
+  __shared__ double de[4][32];
   __shared__ float srn[16];
   for (int i = threadIdx.x; i < 16 * D; i += blockDim.x) {
     const int p = i / D;
@@ -334,50 +418,77 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
       o[0] = (int32_t)bits;
       if (P == 2) o[1] = (int32_t)(bits ^ (1u << nr.j1));
     }
+    // rows float32 cannot certify: float64 by the whole wave, one at a
+    // time, from an LDS copy
     uint64_t ab = ballot64(valid && amb);
+    const int wv = threadIdx.x >> 6;
     while (ab) {
-      const int src = __builtin_ctzll(ab);
+      const int r = __builtin_ctzll(ab);  // wave-uniform
       ab &= ab - 1;
-      const int64_t e = base + src;
-      const int hh = (int)(e / N);
-      const int64_t rr = e - (int64_t)hh * N;
-      hash_fixup_row<float, D, P>(x + (int64_t)hh * sh + rr * st, planes, nb, bucket + e * P, diag,
-                                  ex[threadIdx.x >> 6]);
+      if (lane_id() == r)
+        for (int d = 0; d < D; ++d) sxr[wv][d] = xr[d];
+      hash_fixup_row<float, D>(sxr[wv], &sp[0][0], D, bucket + (base + r) * P, P, nb, diag, ex[wv],
+                               de[wv]);
     }
   }
 }
 
 template <int D, int P>
-hipError_t launch_hash_dp(const fastar_tensor_t& x, const void* planes, int nb, int32_t* bucket,
-                          fastar_diag_t* diag, hipStream_t s) {
-  const int H = x.heads;
-  const int64_t N = x.tokens;
-  if (x.dtype == FASTAR_BF16) {
-    const int64_t tiles = (int64_t)H * ((N + 15) / 16);
-    const int64_t blocks = (tiles + 3) / 4 < 8192 ? (tiles + 3) / 4 : 8192;
-    hipLaunchKernelGGL((hash_bf16_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const uint16_t*)x.data, x.stride_head, x.stride_token, H, N,
-                       (const uint16_t*)planes, nb, bucket, diag);
-  } else {
-    const int64_t total = (int64_t)H * N;
-    const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
-    hipLaunchKernelGGL((hash_f32_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s,
-                       (const float*)x.data, x.stride_head, x.stride_token, H, N,
-                       (const float*)planes, nb, bucket, diag);
-  }
+hipError_t launch_hash_f32(const HashJob& j, const void* planes, int nb, fastar_diag_t* diag,
+                           hipStream_t s) {
+  const int64_t total = (int64_t)j.H * j.N;
+  const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
+  hipLaunchKernelGGL((hash_f32_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s,
+                     (const float*)j.x, j.sh, j.st, j.H, j.N, (const float*)planes, nb, j.bucket, diag);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_hash_multi(HashJobs jobs, int dim, int dtype, const void* planes, int n_bits,
+                             fastar_diag_t* diag, hipStream_t s) {
+  // drop empty tensors; tile ranges in launch order
+  HashJobs js;
+  js.count = 0;
+  int64_t tiles = 0;
+  for (int i = 0; i < jobs.count; ++i) {
+    const HashJob& j = jobs.j[i];
+    if ((int64_t)j.H * j.N == 0) continue;
+    js.j[js.count] = j;
+    tiles += (int64_t)j.H * ((j.N + 15) / 16);
+    js.tile_end[js.count] = tiles;
+    ++js.count;
+  }
+  if (js.count == 0) return hipSuccess;
+  if (dtype == FASTAR_BF16) {
+    // two tiles per wave: the second tile's rows load during the first
+    const int64_t blocks = (tiles + 7) / 8 < 8192 ? (tiles + 7) / 8 : 8192;
+    if (dim == 64)
+      hipLaunchKernelGGL((hash_bf16_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, s, js,
+                         (const uint16_t*)planes, n_bits, diag);
+    else
+      hipLaunchKernelGGL((hash_bf16_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, s, js,
+                         (const uint16_t*)planes, n_bits, diag);
+    return hipGetLastError();
+  }
+  for (int i = 0; i < js.count; ++i) {
+    const HashJob& j = js.j[i];
+    hipError_t e;
+    if (dim == 64)
+      e = j.P == 1 ? launch_hash_f32<64, 1>(j, planes, n_bits, diag, s) : launch_hash_f32<64, 2>(j, planes, n_bits, diag, s);
+    else
+      e = j.P == 1 ? launch_hash_f32<128, 1>(j, planes, n_bits, diag, s) : launch_hash_f32<128, 2>(j, planes, n_bits, diag, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_hash(const fastar_tensor_t& x, const void* planes, int n_bits, int n_probes,
                        int32_t* bucket, fastar_diag_t* diag, hipStream_t s) {
-  if ((int64_t)x.heads * x.tokens == 0) return hipSuccess;
-  if (x.dim == 64)
-    return n_probes == 1 ? launch_hash_dp<64, 1>(x, planes, n_bits, bucket, diag, s)
-                         : launch_hash_dp<64, 2>(x, planes, n_bits, bucket, diag, s);
-  return n_probes == 1 ? launch_hash_dp<128, 1>(x, planes, n_bits, bucket, diag, s)
-                       : launch_hash_dp<128, 2>(x, planes, n_bits, bucket, diag, s);
+  HashJobs jobs;
+  jobs.count = 1;
+  jobs.j[0] = HashJob{x.data, x.stride_head, x.stride_token, x.tokens, x.heads, n_probes, bucket};
+  return launch_hash_multi(jobs, x.dim, x.dtype, planes, n_bits, diag, s);
 }
 
 }  // namespace fastar

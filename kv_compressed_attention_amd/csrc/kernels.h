@@ -9,8 +9,23 @@
 namespace fastar {
 
 // hash.hip ------------------------------------------------------------------
+struct HashJob {  // one tensor [H][N][d] hashed into bucket [H][N][P]
+  const void* x;
+  int64_t sh, st, N;
+  int H, P;
+  int32_t* bucket;
+};
+constexpr int kMaxHashJobs = 4;
+struct HashJobs {
+  HashJob j[kMaxHashJobs];
+  int64_t tile_end[kMaxHashJobs];  // filled by launch_hash_multi
+  int count;
+};
 hipError_t launch_hash(const fastar_tensor_t& x, const void* planes, int n_bits, int n_probes,
                        int32_t* bucket, fastar_diag_t* diag, hipStream_t s);
+// all tensors share dim and dtype; one launch for bf16
+hipError_t launch_hash_multi(HashJobs jobs, int dim, int dtype, const void* planes, int n_bits,
+                             fastar_diag_t* diag, hipStream_t s);
 
 // index.hip -----------------------------------------------------------------
 hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int n_probes,

@@ -71,6 +71,7 @@ _SIGNATURES = {
     "fastar_version": (_I, []),
     "fastar_hash_workspace": (_SZ, [_I, _I64, _I, _I]),
     "fastar_hash": (_I, [_TP, _P, _I, _I, _P, _P, _P, _P, _SZ, _P, _P]),
+    "fastar_hash_multi": (_I, [_I, _P, _P, _P, _P, _I, _P, _P]),
     "fastar_bucket_index_workspace": (_SZ, [_I, _I64]),
     "fastar_bucket_index": (_I, [_P, _I, _I64, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "fastar_tempcache_workspace": (_SZ, [_CP, _I]),
@@ -111,12 +112,13 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _desc(t: torch.Tensor) -> FastarTensor:
-    if t.dim() != 3 or t.stride(2) != 1:
+    if t.dim() != 3 or (t.numel() and t.stride(2) != 1):
         raise ValueError("expected a [heads, tokens, dim] tensor with a contiguous last dim")
     if t.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {t.dtype}")
-    return FastarTensor(t.data_ptr(), _DTYPES[t.dtype], t.shape[0], t.shape[1], t.shape[2], 0,
-                        t.stride(0), t.stride(1))
+    # an empty tensor's strides are not looked at
+    sh, st = (t.stride(0), t.stride(1)) if t.numel() else (t.shape[1] * t.shape[2], t.shape[2])
+    return FastarTensor(t.data_ptr(), _DTYPES[t.dtype], t.shape[0], t.shape[1], t.shape[2], 0, sh, st)
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -166,6 +168,21 @@ def fastar_hash(x, planes, n_bits: int, n_probes: int = 1, with_index: bool = Tr
                            _ptr(offsets), _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(),
                            _ptr(diag), _stream(stream)))
     return bucket, offsets, perm
+
+
+def fastar_hash_multi(xs, planes, n_bits: int, n_probes, buckets=None, diag=None, stream=None):
+    """Bucket ids [H_i, N_i, P_i] of each x_i [H_i, N_i, d] (one launch for bf16)."""
+    lib = library()
+    n = len(xs)
+    if buckets is None:
+        buckets = [_i32((x.shape[0], x.shape[1], p), x.device) for x, p in zip(xs, n_probes)]
+    descs = [_desc(x) for x in xs]
+    xp = (ctypes.c_void_p * n)(*[ctypes.addressof(d) for d in descs])
+    npr = (ctypes.c_int * n)(*n_probes)
+    bp = (ctypes.c_void_p * n)(*[b.data_ptr() for b in buckets])
+    _check(lib.fastar_hash_multi(n, ctypes.cast(xp, _P), ctypes.cast(npr, _P), ctypes.cast(bp, _P),
+                                 _ptr(planes), n_bits, _ptr(diag), _stream(stream)))
+    return buckets
 
 
 def fastar_bucket_index(bucket, n_bits: int, n_valid=None, offsets=None, perm=None, ws=None,

@@ -3,17 +3,18 @@ buffers so that repeated steps do no allocation.
 
 Order (one hashing serves all three modules; the self-attention keys are the
 compressed cache including the chunk's own frames):
-  1. hash the chunk's queries (1 or 2 probes) and build their bucket index;
-  2. hash the chunk's new keys;
+  1. hash the chunk's queries (1 or 2 probes), new keys and prompt keys, in
+     one launch;
+  2. build the queries' bucket index;
   3. TempCache-merge the new frames, frame by frame, and index the
      representatives by bucket;
-  4. hash the prompt keys and prune them against the queries' buckets (AnnCA);
+  4. prune the prompt keys against the queries' buckets (AnnCA);
   5. AnnSA bucket attention over the cache with the + ln m bias;
   6. cross-attention over the kept prompt tokens.
 Every step is a libfastar call; this class only owns the torch buffers and
-the ordering.  The query side (1, then 4 and 6) does not touch the cache, so
-it runs on a second stream of default priority, concurrently with 2 and 3 up
-to 5's need for the query index; all streams join before step returns.
+the ordering.  The query side (2, then 4 and 6) does not touch the cache, so
+it runs on a second stream of default priority, concurrently with 3 up to
+5's need for the query index; all streams join before step returns.
 """
 
 from __future__ import annotations
@@ -105,15 +106,29 @@ class FastARLayer:
         timing.setdefault(name, []).append((a, self._ev(timing)))
         return r
 
+    def _hash_all(self, q, k_new, prompt_k, timing):
+        xs, probes, outs = [q, k_new], [self.n_probes, 1], [self.q_ids, self.k_ids]
+        if prompt_k is not None:
+            xs.append(prompt_k)
+            probes.append(1)
+            outs.append(self.p_ids)
+        self._timed(timing, "hash", lambda: fb.fastar_hash_multi(
+            xs, self.planes, self.n_bits, probes, buckets=outs, diag=self.diag))
+
+    def _query_index(self, timing):
+        self._timed(timing, "index_q", lambda: fb.fastar_bucket_index(
+            self.q_ids, self.n_bits, offsets=self.q_off, perm=self.q_perm, ws=self.ws_q))
+
     def _query_hash(self, q, timing):
         self._timed(timing, "hash_q", lambda: fb.fastar_hash(
             q, self.planes, self.n_bits, self.n_probes, bucket=self.q_ids, offsets=self.q_off,
             perm=self.q_perm, ws=self.ws_q, diag=self.diag))
 
-    def _cross(self, q, prompt_k, prompt_v, timing):
+    def _cross(self, q, prompt_k, prompt_v, timing, hashed=False):
         def run():
-            fb.fastar_hash(prompt_k, self.planes, self.n_bits, 1, with_index=False,
-                           bucket=self.p_ids, ws=self.ws_q, diag=self.diag)
+            if not hashed:
+                fb.fastar_hash(prompt_k, self.planes, self.n_bits, 1, with_index=False,
+                               bucket=self.p_ids, ws=self.ws_q, diag=self.diag)
             fb.fastar_prune_prompt(self.q_ids, self.p_ids.view(self.heads, -1), self.n_bits,
                                    keep=self.keep, kept_idx=self.kept_idx, n_kept=self.n_kept)
             fb.fastar_bucket_attention(q, prompt_k, prompt_v, key_list=self.kept_idx,
@@ -121,10 +136,9 @@ class FastARLayer:
                                        lse=self.lse_cross)
         self._timed(timing, "cross", run)
 
-    def _cache_side(self, cache, k_new, v_new, timing):
-        k_ids = self._timed(timing, "hash_k", lambda: self.hash_keys(k_new, self.k_ids))
+    def _merge(self, cache, k_new, v_new, timing):
         self._timed(timing, "merge", lambda: fb.fastar_tempcache_merge(
-            cache, k_new, v_new, k_ids.view(self.heads, -1), self.chunk_frames, self.tau,
+            cache, k_new, v_new, self.k_ids.view(self.heads, -1), self.chunk_frames, self.tau,
             group_of_new=self.group_of_new, rep_offsets=self.rep_off, rep_perm=self.rep_perm,
             ws=self.ws, diag=self.diag))
 
@@ -147,25 +161,24 @@ class FastARLayer:
         ``timing`` (optional dict) receives (start, end) event pairs per
         stage, recorded on the stream each stage runs on."""
         cache = self.cache if cache is None else cache
+        self._hash_all(q, k_new, prompt_k, timing)
         if not concurrent:
-            self._query_hash(q, timing)
-            self._cache_side(cache, k_new, v_new, timing)
+            self._query_index(timing)
+            self._merge(cache, k_new, v_new, timing)
             self.self_attention(q, timing, cache)
             if prompt_k is not None:
-                self._cross(q, prompt_k, prompt_v, timing)
+                self._cross(q, prompt_k, prompt_v, timing, hashed=True)
             return
         main = torch.cuda.current_stream(self.device)
-        start = self._ev(None)
-        # the cache side (the longer chain) is queued first: a captured graph
-        # then starts it first
-        self._cache_side(cache, k_new, v_new, timing)
+        hashed = self._ev(None)
         with torch.cuda.stream(self.side):
-            self.side.wait_event(start)
-            self._query_hash(q, timing)
+            self.side.wait_event(hashed)
+            self._query_index(timing)
             q_done = self._ev(None)
             if prompt_k is not None:
-                self._cross(q, prompt_k, prompt_v, timing)
+                self._cross(q, prompt_k, prompt_v, timing, hashed=True)
             side_done = self._ev(None)
+        self._merge(cache, k_new, v_new, timing)
         main.wait_event(q_done)
         self.self_attention(q, timing, cache)
         main.wait_event(side_done)

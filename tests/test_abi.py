@@ -89,6 +89,27 @@ def test_hash_rejects_bad_arguments_without_launching(lib):
     assert st == 1
 
 
+def test_hash_multi_rejects_bad_arguments_without_launching(lib):
+    buf = ctypes.c_void_p(1 << 20)
+
+    def call(tensors, probes, bits=12, count=None):
+        n = len(tensors)
+        xp = (ctypes.c_void_p * n)(*[ctypes.addressof(t) for t in tensors])
+        pr = (ctypes.c_int * n)(*probes)
+        bp = (ctypes.c_void_p * n)(*([buf.value] * n))
+        return lib.fastar_hash_multi(n if count is None else count, ctypes.cast(xp, ctypes.c_void_p),
+                                     ctypes.cast(pr, ctypes.c_void_p), ctypes.cast(bp, ctypes.c_void_p),
+                                     buf, bits, None, None)
+
+    a, b = _tensor(), _tensor(tokens=32)
+    assert call([a, b], [1, 1], count=0) == 1            # count < 1
+    assert call([a, b, a, b, a], [1] * 5) == 1           # count > 4
+    assert call([a, _tensor(dim=64)], [1, 1]) == 1       # dims differ
+    assert call([a, _tensor(dtype=0)], [1, 1]) == 1      # dtypes differ
+    assert call([a, b], [1, 3]) == 2                     # n_probes
+    assert call([a, b], [1, 1], bits=16) == 2            # n_bits
+
+
 def test_attention_rejects_bad_arguments_without_launching(lib):
     buf = ctypes.c_void_p(1 << 20)
     q, k = _tensor(), _tensor(tokens=32)

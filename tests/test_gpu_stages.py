@@ -94,6 +94,34 @@ def test_hash_and_index_match_oracle(fa, dtype, H, n, d, b, P):
         assert dg[1] > 0, "exactly orthogonal rows should have needed exact signs"
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_hash_multi_matches_oracle(fa, dtype, d):
+    """Queries (two probes), keys and prompt keys of different head and row
+    counts in one call: each tensor's ids equal the oracle's, and an empty
+    tensor in the list is skipped."""
+    b = 12
+    planes = gaussian((b, d), 41, dtype)
+    shapes = [(3, 1000, 2), (3, 2300, 1), (2, 77, 1), (3, 0, 1)]
+    xs = []
+    for i, (H, n, _) in enumerate(shapes):
+        x = gaussian((H, n, d), 50 + i, dtype)
+        if n:
+            for h in range(H):
+                x[h, ::4] = near_plane_rows(x[h, ::4].shape[0], d, planes, 60 + 7 * i + h, dtype)
+        xs.append(x)
+    diag = fa.new_diag()
+    outs = fa.fastar_hash_multi([dev_tensor(x, dtype) for x in xs], dev_tensor(planes, dtype), b,
+                                [P for _, _, P in shapes], diag=diag)
+    torch.cuda.synchronize()
+    for x, (H, n, P), ids in zip(xs, shapes, outs):
+        ids = ids.cpu().numpy()
+        assert ids.shape == (H, n, P)
+        for h in range(H):
+            assert np.array_equal(ids[h], oracle.simhash(x[h], planes, P)), (H, n, P, h)
+    dg = diag.cpu().numpy()
+    assert dg[3] == 0 and dg[0] > 0
+
+
 def test_hash_is_deterministic(fa):
     x = dev_tensor(gaussian((4, 3000, 128), 7, "bf16"), "bf16")
     planes = dev_tensor(gaussian((14, 128), 8, "bf16"), "bf16")
