@@ -109,7 +109,8 @@ struct Chunk<float, EPL> {
 };
 
 // running (best, second best); equal values go to the smaller index, so the
-// result does not depend on the order the candidates are visited in
+// result does not depend on the order the candidates are visited in.  Empty:
+// best = -1 and both values -inf (no finite cosine is below that).
 template <typename F>
 struct Top2 {
   F c1, c2;
@@ -119,18 +120,17 @@ struct Top2 {
     c2 = -INFINITY;
     best = -1;
   }
-  __device__ __forceinline__ void add(F c, int i) {
-    if (best < 0) {
-      c1 = c;
-      best = i;
-    } else if (c > c1 || (c == c1 && i < best)) {
-      c2 = c1 > c2 ? c1 : c2;
-      c1 = c;
-      best = i;
-    } else if (c > c2) {
-      c2 = c;
-    }
+  // the top two of this and (oc1, oc2, ob), branch-free; an empty side never
+  // wins (-1 is the largest index unsigned)
+  __device__ __forceinline__ void merge(F oc1, F oc2, int ob) {
+    const bool o = ob >= 0 && (oc1 > c1 || (oc1 == c1 && (uint32_t)ob < (uint32_t)best));
+    const F lo = o ? c1 : oc1;  // the loser's best
+    const F w2 = o ? oc2 : c2;  // the winner's second
+    c2 = lo > w2 ? lo : w2;
+    c1 = o ? oc1 : c1;
+    best = o ? ob : best;
   }
+  __device__ __forceinline__ void add(F c, int i) { merge(c, (F)-INFINITY, i); }
 };
 
 // keys are matched in tiles of this many (one wave each)
@@ -269,12 +269,13 @@ __global__ __launch_bounds__(1024) void tc_index_kernel(
   }
 }
 
-// 16 x 16 tiles of dot products, keys (rows) by candidates (columns).  Loads
-// are issued (issue_*) before they are used (finish_keys, dots), so that the
-// key rows and a tile of candidate rows are in flight together.  After
-// finish_keys, lane l (g = l >> 4) holds the squared norms of keys 4g + i in
-// kn[i]; dots gives the dots of keys 4g + i with candidate l & 15 in s[i] and
-// that candidate's squared norm in cn.
+// 16 x 16 tiles of dot products of keys with candidates.  Loads are issued
+// (issue_*) before they are used (finish_keys, dots), so that the key rows
+// and a tile of candidate rows are in flight together.  Lane l (col = l & 15,
+// g = l >> 4) fetches key col and candidate col of a tile; after finish_keys
+// it holds the squared norm of key col in kn, cand_norm gives the squared
+// norm of candidate col, and dots the dots of key col with candidates 4g + i
+// of the tile in s[i].
 template <typename T, int D>
 struct TileDot;
 
@@ -285,7 +286,7 @@ struct TileDot<uint16_t, D> {
     uint4 u[NC];  // row l & 15, dims 32c + 8g .. +8
   };
   Rows kr;
-  float kn[4];
+  float kn;
   __device__ __forceinline__ static float sumsq(const uint4& u) {
     float s = 0.f;
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -312,24 +313,19 @@ struct TileDot<uint16_t, D> {
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) s += sumsq(r.u[c]);
-    s += shfl_xor_f(s, 16);
-    s += shfl_xor_f(s, 32);
-    return s;
+    return sum_xor32(sum_xor16(s));
   }
   __device__ __forceinline__ void issue_keys(const uint16_t* row) { kr = issue(row); }
-  __device__ __forceinline__ void finish_keys() {
-    const int g = lane_id() >> 4;
-    const float s = rownorm(kr);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kn[i] = __shfl(s, 4 * g + i, FASTAR_WAVE);
-  }
-  __device__ __forceinline__ void dots(const Rows& cr, float* s, float& cn) const {
-    cn = rownorm(cr);
+  __device__ __forceinline__ void finish_keys() { kn = rownorm(kr); }
+  // the squared norm of candidate l & 15 (every lane of it)
+  __device__ __forceinline__ static float cand_norm(const Rows& cr) { return rownorm(cr); }
+  __device__ __forceinline__ void dots(const Rows& cr, float* s) const {
+    // candidates as the A operand: acc[i] = cand (4g + i) . key col
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr.u[c]),
-                                                     __builtin_bit_cast(bf16x8_t, cr.u[c]), acc,
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cr.u[c]),
+                                                     __builtin_bit_cast(bf16x8_t, kr.u[c]), acc,
                                                      0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = acc[i];
@@ -339,59 +335,47 @@ struct TileDot<uint16_t, D> {
 template <int D>
 struct TileDot<float, D> {
   struct Rows {
-    const float* p;
+    const float* p;  // candidate l & 15's row
   };
-  const float* own;    // this lane's key row (l & 15)
-  const float* kr[4];  // rows of keys 4g + i (null: none)
-  float kn[4];
+  const float* own;  // key l & 15's row
+  float kn;
   __device__ __forceinline__ static Rows issue(const float* row) { return Rows{row}; }
   __device__ __forceinline__ void issue_keys(const float* row) { own = row; }
   __device__ __forceinline__ void finish_keys() {
+    float n = 0.f;
+    if (own)
+      for (int d = 0; d < D; ++d) n = fmaf(own[d], own[d], n);
+    kn = n;
+  }
+  __device__ __forceinline__ static float cand_norm(const Rows& cr) {
+    float n = 0.f;
+    if (cr.p)
+      for (int k = 0; k < D; ++k) n = fmaf(cr.p[k], cr.p[k], n);
+    return n;
+  }
+  __device__ __forceinline__ void dots(const Rows& cr, float* s) const {
     const int g = lane_id() >> 4;
-    const uint64_t u = (uint64_t)own;
+    const uint64_t u = (uint64_t)cr.p;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)u, 4 * g + i, FASTAR_WAVE);
       const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(u >> 32), 4 * g + i, FASTAR_WAVE);
-      kr[i] = (const float*)(((uint64_t)hi << 32) | lo);
-      float n = 0.f;
-      if (kr[i])
-        for (int d = 0; d < D; ++d) n = fmaf(kr[i][d], kr[i][d], n);
-      kn[i] = n;
-    }
-  }
-  __device__ __forceinline__ void dots(const Rows& cr, float* s, float& cn) const {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s[i] = 0.f;
-    cn = 0.f;
-    if (!cr.p) return;
-    for (int d = 0; d < D; ++d) {
-      const float c = cr.p[d];
-      cn = fmaf(c, c, cn);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (kr[i]) s[i] = fmaf(kr[i][d], c, s[i]);
+      const float* c = (const float*)(((uint64_t)hi << 32) | lo);
+      float d = 0.f;
+      if (c && own)
+        for (int k = 0; k < D; ++k) d = fmaf(own[k], c[k], d);
+      s[i] = d;
     }
   }
 };
 
-template <typename F>
-__device__ __forceinline__ void top2_merge_xor(Top2<F>& t, int m) {
-  const F c1 = __shfl_xor(t.c1, m, FASTAR_WAVE);
-  const F c2 = __shfl_xor(t.c2, m, FASTAR_WAVE);
-  const int b = __shfl_xor(t.best, m, FASTAR_WAVE);
-  if (b < 0) return;
-  if (t.best < 0) {
-    t.c1 = c1;
-    t.c2 = c2;
-    t.best = b;
-  } else if (c1 > t.c1 || (c1 == t.c1 && b < t.best)) {
-    t.c2 = t.c1 > c2 ? t.c1 : c2;
-    t.c1 = c1;
-    t.best = b;
-  } else if (c1 > t.c2) {
-    t.c2 = c1;
-  }
+// t merged with the lane a DPP pattern CTRL pairs this lane with
+template <int CTRL>
+__device__ __forceinline__ void top2_merge_dpp(Top2<float>& t) {
+  const float c1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t.c1), CTRL, 0xF, 0xF, false));
+  const float c2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(t.c2), CTRL, 0xF, 0xF, false));
+  const int b = __builtin_amdgcn_update_dpp(0, t.best, CTRL, 0xF, 0xF, false);
+  t.merge(c1, c2, b);
 }
 
 // float64 cosine of two rows, the whole wave (lane l takes dims l, l + 64, ..);
@@ -483,26 +467,26 @@ __device__ __forceinline__ void decide(const SegCtx<T, D>& x, const Top2<float>&
   }
 }
 
-// the reporting lane's key (r = 4 (l >> 4) + (l & 3)) takes its float32 top
-// two out of t[] after the merge over the 16 columns
-__device__ __forceinline__ Top2<float> reduce_top2(Top2<float>* t) {
+// the lane's key's float32 top two over all 16 x 4 candidate slots: the
+// four lanes of a key (l, l ^ 16, l ^ 32, l ^ 48) merged with permlane swaps
+__device__ __forceinline__ void reduce_top2(Top2<float>& t) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    top2_merge_xor(t[i], 1);
-    top2_merge_xor(t[i], 2);
-    top2_merge_xor(t[i], 4);
-    top2_merge_xor(t[i], 8);
+  for (int step = 0; step < 2; ++step) {
+    const auto c1 = step == 0 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(t.c1), __float_as_uint(t.c1), false, false)
+                              : __builtin_amdgcn_permlane32_swap(__float_as_uint(t.c1), __float_as_uint(t.c1), false, false);
+    const auto c2 = step == 0 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(t.c2), __float_as_uint(t.c2), false, false)
+                              : __builtin_amdgcn_permlane32_swap(__float_as_uint(t.c2), __float_as_uint(t.c2), false, false);
+    const auto bb = step == 0 ? __builtin_amdgcn_permlane16_swap((uint32_t)t.best, (uint32_t)t.best, false, false)
+                              : __builtin_amdgcn_permlane32_swap((uint32_t)t.best, (uint32_t)t.best, false, false);
+    // each pair is (this lane's, the partner's) in one order or the other,
+    // the same order for all three; merging both halves is exact either way
+    Top2<float> u;
+    u.c1 = __uint_as_float(c1[0]);
+    u.c2 = __uint_as_float(c2[0]);
+    u.best = (int)bb[0];
+    u.merge(__uint_as_float(c1[1]), __uint_as_float(c2[1]), (int)bb[1]);
+    t = u;
   }
-  const int col = lane_id() & 15;
-  Top2<float> m = t[0];
-#pragma unroll
-  for (int i = 1; i < 4; ++i)
-    if ((col & 3) == i) {
-      m.c1 = t[i].c1;
-      m.c2 = t[i].c2;
-      m.best = t[i].best;
-    }
-  return m;
 }
 
 // Step 1 for keys k0 .. k0 + 15 of a bucket-sorted key list ktok / kbk
@@ -512,10 +496,10 @@ __device__ __forceinline__ Top2<float> reduce_top2(Top2<float>* t) {
 // cosine counts only when their buckets agree.  The lists may be LDS copies;
 // the float64 re-evaluation reads a key's whole bucket from the candidate
 // table itself (gtok / gcg, bucket offsets coff).  The lane with
-// (l & 15) < 4 reports key r = 4 (l >> 4) + (l & 3): jrep (its token, -1:
-// none), p (the candidate token it proposes to, -1: none) and c (the cosine).
-// Candidates are visited in tiles of 16, the next tile's rows loading while
-// the current one is used.
+// l < 16 reports key l: jrep (its token, -1: none), p (the candidate token
+// it proposes to, -1: none) and c (the cosine).  Candidates are visited in
+// tiles of 16, the next tile's rows loading while the current one is used;
+// lane l compares its key l & 15 with candidates 4 (l >> 4) .. + 3 of each.
 template <typename T, int D>
 __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t* ktok,
                                            const int32_t* kbk, int k0, int kend,
@@ -527,17 +511,21 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
   const int lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
   const bool kv = k0 + col < kend;
-  const int jr = kv ? ktok[k0 + col] : -1;  // this lane's key row
+  const int jr = kv ? ktok[k0 + col] : -1;  // this lane's key
   const int rb = kv ? kbk[k0 + col] : -1;   // and its bucket
-  jrep = __shfl(jr, 4 * g + (col & 3), FASTAR_WAVE);
+  jrep = lane < 16 ? jr : -1;
   p = -1;
   c = 0.f;
   if (c_hi <= c_lo) return;
-  const bool own = col < 4 && jrep >= 0;
-  int kb4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) kb4[i] = __shfl(rb, 4 * g + i, FASTAR_WAVE);
-  // candidate ids of the first tile, with the key rows
+  const bool own = lane < 16 && jr >= 0;
+  // per wave: the current tile's candidates (token, bucket, 1 / norm), laid
+  // out so that lane l reads its four (4 (l >> 4) ..) in one load each
+  __shared__ __attribute__((aligned(16))) int32_t tt_tok[4][16];
+  __shared__ __attribute__((aligned(16))) int32_t tt_bk[4][16];
+  __shared__ __attribute__((aligned(16))) float tt_rn[4][16];
+  const int wv = threadIdx.x >> 6;
+  // candidate ids of the first tile (the row this lane fetches), with the
+  // key rows
   bool cv = c_lo + col < c_hi;
   int ci = cv ? ctok[c_lo + col] : 0;
   int cb = cv ? cbk[c_lo + col] : -2;
@@ -546,33 +534,42 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
   td.issue_keys(jr >= 0 ? x.kf + (int64_t)jr * x.k_st : nullptr);
   typename TD::Rows cr = TD::issue(cv ? x.cand_row(0, ci, cgi) : nullptr);
   td.finish_keys();
-  Top2<float> t[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) t[i].init();
+  const float rk = td.kn > 0.f ? rsqrtf(td.kn) : 0.f;
+  Top2<float> t;
+  t.init();
   for (int c0 = c_lo; c0 < c_hi; c0 += 16) {
     // next tile's ids, then this tile's dots, then the next tile's rows
     const bool nv = c0 + 16 + col < c_hi;
     const int ni = nv ? ctok[c0 + 16 + col] : 0;
     const int nb = nv ? cbk[c0 + 16 + col] : -2;
     const int ng = (nv && x.f == 0) ? cg[c0 + 16 + col] : 0;
-    float sd[4], cn;
-    td.dots(cr, sd, cn);
-    if (cv) {
-      const float rc = cn > 0.f ? rsqrtf(cn) : 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (kb4[i] == cb) t[i].add(td.kn[i] > 0.f ? sd[i] * rsqrtf(td.kn[i]) * rc : 0.f, ci);
+    const float cn = TD::cand_norm(cr);
+    if (g == 0) {
+      tt_tok[wv][col] = ci;
+      tt_bk[wv][col] = cb;  // -2 past the end: no key's bucket
+      tt_rn[wv][col] = cn > 0.f ? rsqrtf(cn) : 0.f;
     }
+    const int4 t4 = *reinterpret_cast<const int4*>(&tt_tok[wv][4 * g]);
+    const int4 b4 = *reinterpret_cast<const int4*>(&tt_bk[wv][4 * g]);
+    const float4 r4 = *reinterpret_cast<const float4*>(&tt_rn[wv][4 * g]);
+    float sd[4];
+    td.dots(cr, sd);
+    const int ti[4] = {t4.x, t4.y, t4.z, t4.w};
+    const int bi[4] = {b4.x, b4.y, b4.z, b4.w};
+    const float ri[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (bi[i] == rb) t.add(sd[i] * rk * ri[i], ti[i]);
     if (c0 + 16 < c_hi) cr = TD::issue(nv ? x.cand_row(0, ni, ng) : nullptr);
     cv = nv;
     ci = ni;
     cb = nb;
   }
-  const Top2<float> m = reduce_top2(t);
-  decide<T, D>(x, m, own, jrep,
+  reduce_top2(t);
+  decide<T, D>(x, t, own, jrep,
                [&](int src, const int32_t*& cl, const int32_t*& gl, int& n) {
                  // the key's own bucket
-                 const int b = __shfl(rb, 4 * (src >> 4) + (src & 3), FASTAR_WAVE);
+                 const int b = __shfl(rb, src, FASTAR_WAVE);
                  const int s = coff[b];
                  cl = gtok + s;
                  gl = gcg + s;
@@ -709,8 +706,8 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
     float c;
     match_tile<T, D>(x, ktok, kbk, k0, nk, ctok, cbk, cg, c_lo, c_hi, gctok, gcg, coff, jrep, p,
                      c);
-    if (col < 4 && jrep >= 0) {
-      const int q = k0 + 4 * (lane >> 4) + col;
+    if (lane < 16 && jrep >= 0) {
+      const int q = k0 + lane;
       lp[q] = p;
       lc[q] = c;
       lj[q] = jrep;
