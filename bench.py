@@ -10,10 +10,12 @@ AnnSA bucket attention of the queries over the compressed cache with the
 into a resident copy of the pre-chunk cache of its own (made before the timed
 region); after the run the K merged caches are checked to be identical.
 
-The query hashing and index run on a second stream, concurrently with the key
-hashing and merge (--serial queues everything on one stream).  Each step is
-captured into a HIP graph and replayed (--eager launches every kernel from
-Python instead, with per-stage event times in "stages_ms").  The attention
+A step is one fastar_chunk call: the queries and the new keys hashed in one
+launch, the queries' index built by extra workgroups of the merge's first
+launch, all on one stream (--order picks the older call-by-call orders,
+on one stream or with the query side on a second one).  Each step is
+captured into a HIP graph and replayed (--eager launches from Python
+instead, with per-call event times in "stages_ms").  The attention
 kernel's duration for the roofline comes from HIP events around K launches of
 it on its stream right after the timed region (inside a graph there is no
 stream to record them on).
@@ -50,8 +52,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=1, help="synthetic workload index (1, 3 or 4)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--serial", action="store_true",
-                   help="queue every stage on one stream (no query-side stream)")
+    p.add_argument("--order", choices=["chunk", "serial", "2stream", "split"], default="chunk",
+                   help="chunk: one fastar_chunk call per step (default); serial: every call on "
+                        "one stream; 2stream: the query index (and AnnCA) on a second stream; "
+                        "split: the query hashing on the second stream as well")
     p.add_argument("--eager", action="store_true",
                    help="launch every kernel from Python each step instead of replaying the "
                         "captured HIP graphs (per-stage event times, host-launch bound)")
@@ -181,7 +185,7 @@ def main():
     del cal_src, cal_dst
 
     timing = {}
-    concurrent = not args.serial
+    concurrent = {"chunk": "chunk", "serial": False, "2stream": True, "split": "split"}[args.order]
 
     def warm_step():
         scratch.copy_from(pristine)
@@ -211,7 +215,7 @@ def main():
     t_enq = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    if not args.eager:
+    if "attention" not in timing:
         # the attention kernel's launch duration: HIP events around each of K
         # launches on the stream it is launched on, same inputs and buffers
         # as the last timed step
@@ -255,7 +259,7 @@ def main():
                       "attended_pairs": pairs,
                       "query_tokens_per_s": nq / t_att,
                       "compressed_keys_per_head": ngb_after(layer, caches[-1])},
-        "launch": ("eager" if args.eager else "hip_graph") + ("_serial" if args.serial else "_2stream"),
+        "launch": ("eager" if args.eager else "hip_graph") + "_" + args.order,
         "stages_ms": stage_ms,
         "host_enqueue_ms_per_step": t_enq * 1e3 / args.steps,
         "diag": layer.diag.tolist(),

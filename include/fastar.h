@@ -10,6 +10,7 @@
  *   fastar_tempcache_merge  TempCache: merge new frames into the compressed cache
  *   fastar_prune_prompt     AnnCA: drop prompt tokens no query shares a bucket with
  *   fastar_bucket_attention AnnSA / AnnCA attention, online softmax on MFMA
+ *   fastar_chunk            one chunk of the layer sequence, all of the above
  *
  * Conventions shared by every call
  * - All tensor and array arguments are DEVICE pointers owned by the caller.
@@ -228,6 +229,57 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
                                         const int32_t* key_list, const int32_t* n_key_list,
                                         float scale, void* out, float* lse,
                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fastar_chunk -- one chunk of the per-layer sequence in one call, the
+ * stages that do not depend on each other launched together: one hashing of
+ * the queries, new keys and prompt keys (paper.rainbus.top "technical
+ * novelty"); the TempCache merge of the new frames with the queries' bucket
+ * index built in its first launch; AnnSA over the merged cache; then, with a
+ * prompt, AnnCA pruning and cross-attention over the kept prompt tokens.
+ * Equal to fastar_hash_multi, fastar_bucket_index, fastar_tempcache_merge,
+ * fastar_bucket_attention (bucket mode, keys rep_k, values v_mean, bias
+ * log_count) and, with a prompt, fastar_prune_prompt and
+ * fastar_bucket_attention (list mode, kept_idx), called in that order on the
+ * same arguments.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  /* the chunk */
+  const fastar_tensor_t* q;         /* [H][Nq][d] queries                       */
+  int n_probes;                     /* 1 or 2                                   */
+  const fastar_tensor_t* k_new;     /* [H][n_frames * T][d] new frames' keys    */
+  const fastar_tensor_t* v_new;     /* and values                               */
+  int n_frames;                     /* > 0                                      */
+  const fastar_tensor_t* prompt_k;  /* [H][Np][d], or NULL: no cross-attention  */
+  const fastar_tensor_t* prompt_v;
+  /* parameters */
+  const void* planes;               /* [n_bits][d], as for fastar_hash          */
+  int n_bits;                       /* the cache's n_bits                       */
+  float tau;                        /* TempCache threshold                      */
+  float scale;                      /* softmax scale                            */
+  /* state: the compressed cache, merged in place */
+  const fastar_cache_t* cache;
+  /* outputs (device) */
+  int32_t* q_bucket;                /* [H][Nq][n_probes]                        */
+  int32_t* q_offsets;               /* [H][2^n_bits + 1]                        */
+  int32_t* q_perm;                  /* [H][Nq]                                  */
+  int32_t* k_bucket;                /* [H][n_frames * T]                        */
+  int32_t* group_of_new;            /* [H][n_frames * T], or NULL               */
+  int32_t* rep_offsets;             /* [H][2^n_bits + 1]                        */
+  int32_t* rep_perm;                /* [H][capacity]                            */
+  void* out;                        /* [H][Nq][d] self-attention, q's dtype     */
+  float* lse;                       /* [H][Nq] or NULL                          */
+  int32_t* p_bucket;                /* [H][Np]      (with a prompt)             */
+  uint8_t* keep;                    /* [H][Np]                                  */
+  int32_t* kept_idx;                /* [H][Np]                                  */
+  int32_t* n_kept;                  /* [H]                                      */
+  void* out_cross;                  /* [H][Nq][d]                               */
+  float* lse_cross;                 /* [H][Nq] or NULL                          */
+} fastar_chunk_t;
+
+size_t fastar_chunk_workspace(const fastar_chunk_t* args);
+fastar_status_t fastar_chunk(const fastar_chunk_t* args, void* ws, size_t ws_bytes,
+                             fastar_diag_t* diag, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -60,6 +60,170 @@ fastar_status_t check_bits(int n_bits, int n_probes) {
   return FASTAR_OK;
 }
 
+
+// ---- argument checks shared by the single calls and fastar_chunk ----------
+
+fastar_status_t hash_multi_check(int count, const fastar_tensor_t* const* x, const int* n_probes,
+                                 int32_t* const* bucket, const void* planes, int n_bits,
+                                 fastar::HashJobs* jobs, bool* any) {
+  if (count < 1 || count > fastar::kMaxHashJobs)
+    return fail(FASTAR_ERR_INVALID, "count %d not in [1, %d]", count, fastar::kMaxHashJobs);
+  if (!x || !n_probes || !bucket) return fail(FASTAR_ERR_INVALID, "x, n_probes and bucket must be arrays");
+  jobs->count = count;
+  *any = false;
+  for (int i = 0; i < count; ++i) {
+    fastar_status_t st = check_tensor(x[i], "x[i]");
+    if (st != FASTAR_OK) return st;
+    if ((st = check_bits(n_bits, n_probes[i])) != FASTAR_OK) return st;
+    if (x[i]->dtype != x[0]->dtype || x[i]->dim != x[0]->dim)
+      return fail(FASTAR_ERR_INVALID, "x[%d]: dtype and dim must match x[0]", i);
+    const bool nonempty = (int64_t)x[i]->heads * x[i]->tokens > 0;
+    if (nonempty && !bucket[i]) return fail(FASTAR_ERR_INVALID, "bucket[%d] is NULL", i);
+    *any = *any || nonempty;
+    jobs->j[i] = fastar::HashJob{x[i]->data, x[i]->stride_head, x[i]->stride_token, x[i]->tokens,
+                                 x[i]->heads, n_probes[i], bucket[i]};
+  }
+  if (*any && n_bits > 0 && (!planes || !aligned16(planes)))
+    return fail(FASTAR_ERR_INVALID, "planes must be a non-null, 16-byte aligned pointer");
+  return FASTAR_OK;
+}
+
+size_t merge_workspace(const fastar_cache_t* c, int n_frames) {
+  if (!c || n_frames < 0 || c->heads < 0 || c->tokens_per_frame < 0 || c->capacity < 0) return 0;
+  if (c->n_bits < 0 || c->n_bits > 15) return 0;
+  const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
+  const size_t nb = ((size_t)1 << c->n_bits) + 1;
+  const size_t nblk = (F * T + 63) / 64;
+  return align_up(4 * H * (F + 1) * nb) + 2 * align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
+         align_up(4 * H * F * T) + align_up(4 * H * (nblk + 1)) + align_up(4 * H * F * T) +
+         align_up(16 * H * (size_t)c->capacity);
+}
+
+// everything fastar_tempcache_merge checks for a call with n_frames > 0 and
+// heads > 0 (ws: at least merge_workspace bytes)
+fastar_status_t merge_check(const fastar_cache_t* c, const fastar_tensor_t* k_new,
+                            const fastar_tensor_t* v_new, const int32_t* k_new_bucket, int n_frames,
+                            float tau, const int32_t* rep_offsets, const int32_t* rep_perm) {
+  if (!c) return fail(FASTAR_ERR_INVALID, "cache is NULL");
+  fastar_status_t st;
+  if ((st = check_tensor(k_new, "k_new")) != FASTAR_OK) return st;
+  if ((st = check_tensor(v_new, "v_new")) != FASTAR_OK) return st;
+  if ((st = check_bits(c->n_bits, 1)) != FASTAR_OK) return st;
+  if (c->dtype != k_new->dtype || c->dtype != v_new->dtype)
+    return fail(FASTAR_ERR_INVALID, "cache, k_new and v_new must share one dtype");
+  if (c->dim != k_new->dim || c->dim != v_new->dim)
+    return fail(FASTAR_ERR_INVALID, "cache, k_new and v_new must share one dim");
+  if (c->heads != k_new->heads || c->heads != v_new->heads)
+    return fail(FASTAR_ERR_INVALID, "cache, k_new and v_new must share one head count");
+  if (n_frames < 0) return fail(FASTAR_ERR_INVALID, "n_frames < 0");
+  if (c->tokens_per_frame <= 0 || c->tokens_per_frame > 2048)
+    return fail(FASTAR_ERR_UNSUPPORTED, "tokens_per_frame %d not in [1, 2048]", c->tokens_per_frame);
+  if (k_new->tokens != (int64_t)n_frames * c->tokens_per_frame || v_new->tokens != k_new->tokens)
+    return fail(FASTAR_ERR_INVALID, "k_new/v_new must hold n_frames * tokens_per_frame tokens");
+  if (c->capacity < c->tokens_per_frame)
+    return fail(FASTAR_ERR_INVALID, "capacity %d < tokens_per_frame", c->capacity);
+  if ((int64_t)c->heads * c->capacity >= (int64_t)1 << 31)
+    return fail(FASTAR_ERR_UNSUPPORTED, "heads*capacity must be < 2^31");
+  if (!(tau == tau) || tau == INFINITY || tau == -INFINITY) return fail(FASTAR_ERR_INVALID, "tau must be finite");
+  if ((rep_offsets == nullptr) != (rep_perm == nullptr))
+    return fail(FASTAR_ERR_INVALID, "rep_offsets and rep_perm must both be given or both be NULL");
+  if (c->heads == 0 || n_frames == 0) return FASTAR_OK;
+  if (!c->rep_k || !c->v_mean || !c->v_sum || !c->count || !c->log_count || !c->rep_bucket ||
+      !c->n_groups || !c->frontier || !k_new_bucket)
+    return fail(FASTAR_ERR_INVALID, "a cache buffer or k_new_bucket is NULL");
+  if (!aligned16(c->rep_k) || !aligned16(c->v_mean) || !aligned16(c->v_sum))
+    return fail(FASTAR_ERR_INVALID, "cache rows must be 16-byte aligned");
+  return FASTAR_OK;
+}
+
+fastar::MergeWs merge_carve(const fastar_cache_t* c, int n_frames, void* ws) {
+  const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
+  const size_t nb = ((size_t)1 << c->n_bits) + 1;
+  char* w = (char*)ws;
+  auto take = [&](size_t bytes) {
+    char* p = w;
+    w += align_up(bytes);
+    return (int32_t*)p;
+  };
+  fastar::MergeWs mw;
+  mw.off = take(4 * H * (F + 1) * nb);
+  mw.tok = take(4 * H * (F + 1) * T);
+  mw.tbk = take(4 * H * (F + 1) * T);
+  mw.candg = take(4 * H * T);
+  mw.link = take(4 * H * F * T);
+  mw.ocnt = take(4 * H * ((F * T + 63) / 64 + 1));
+  mw.nextj = take(4 * H * F * T);
+  mw.index_ws = take(16 * H * (size_t)c->capacity);
+  return mw;
+}
+
+fastar_status_t prune_check(const int32_t* q_bucket, int heads, int64_t n_q, int n_probes,
+                            const int32_t* p_bucket, int64_t n_prompt, int n_bits,
+                            const uint8_t* keep, const int32_t* kept_idx, const int32_t* n_kept) {
+  fastar_status_t st = check_bits(n_bits, n_probes);
+  if (st != FASTAR_OK) return st;
+  if (heads < 0 || n_q < 0 || n_prompt < 0) return fail(FASTAR_ERR_INVALID, "negative size");
+  if (heads == 0) return FASTAR_OK;
+  if (!n_kept) return fail(FASTAR_ERR_INVALID, "n_kept is NULL");
+  if (n_q > 0 && !q_bucket) return fail(FASTAR_ERR_INVALID, "q_bucket is NULL");
+  if (n_prompt > 0 && (!p_bucket || !keep || !kept_idx))
+    return fail(FASTAR_ERR_INVALID, "p_bucket, keep or kept_idx is NULL");
+  if ((int64_t)heads * n_q * n_probes >= (int64_t)1 << 31 || (int64_t)heads * n_prompt >= (int64_t)1 << 31)
+    return fail(FASTAR_ERR_UNSUPPORTED, "sizes must be < 2^31");
+  return FASTAR_OK;
+}
+
+// checks a bucket-attention call and fills its launch arguments; *empty: no
+// query rows (nothing to launch)
+fastar_status_t attention_check(const fastar_tensor_t* q, const int32_t* q_bucket,
+                                const int32_t* q_perm, int n_probes, const fastar_tensor_t* k,
+                                const fastar_tensor_t* v, const float* key_bias,
+                                const int32_t* k_offsets, const int32_t* k_perm, int n_bits,
+                                const int32_t* key_list, const int32_t* n_key_list, float scale,
+                                void* out, float* lse, fastar::AttnArgs* a, bool* empty) {
+  fastar_status_t st;
+  if ((st = check_tensor(q, "q")) != FASTAR_OK) return st;
+  if ((st = check_tensor(k, "k")) != FASTAR_OK) return st;
+  if ((st = check_tensor(v, "v")) != FASTAR_OK) return st;
+  if (q->dtype != k->dtype || q->dtype != v->dtype) return fail(FASTAR_ERR_INVALID, "q, k, v dtypes differ");
+  if (q->dim != k->dim || q->dim != v->dim) return fail(FASTAR_ERR_INVALID, "q, k, v dims differ");
+  if (q->heads != k->heads || q->heads != v->heads) return fail(FASTAR_ERR_INVALID, "q, k, v head counts differ");
+  if (k->tokens != v->tokens) return fail(FASTAR_ERR_INVALID, "k and v token counts differ");
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return fail(FASTAR_ERR_INVALID, "scale must be finite");
+  int mode;
+  if (k_offsets || k_perm) {
+    if (!k_offsets || !k_perm) return fail(FASTAR_ERR_INVALID, "bucket mode needs k_offsets and k_perm");
+    if (key_list || n_key_list) return fail(FASTAR_ERR_INVALID, "give either bucket segments or a key list");
+    if ((st = check_bits(n_bits, n_probes)) != FASTAR_OK) return st;
+    mode = 0;
+  } else if (key_list || n_key_list) {
+    if (!key_list || !n_key_list) return fail(FASTAR_ERR_INVALID, "list mode needs key_list and n_key_list");
+    mode = 1;
+  } else {
+    mode = 2;
+  }
+  *empty = (int64_t)q->heads * q->tokens == 0;
+  if (*empty) return FASTAR_OK;
+  if (!out || !aligned16(out)) return fail(FASTAR_ERR_INVALID, "out must be a non-null 16-byte aligned pointer");
+  if (mode == 0 && (!q_bucket || !q_perm)) return fail(FASTAR_ERR_INVALID, "bucket mode needs q_bucket and q_perm");
+  if (q->dtype == FASTAR_BF16 && k->tokens > 0) {
+    // the bf16 kernel addresses a head's k and v rows by 32-bit byte offsets
+    const int64_t span_k = ((int64_t)(k->tokens - 1) * k->stride_token + k->dim) * 2;
+    const int64_t span_v = ((int64_t)(v->tokens - 1) * v->stride_token + v->dim) * 2;
+    if (span_k > 0xFFFFFFFFll || span_v > 0xFFFFFFFFll)
+      return fail(FASTAR_ERR_UNSUPPORTED, "a head's k or v rows span more than 4 GiB");
+  }
+  a->q = q->data; a->q_sh = q->stride_head; a->q_st = q->stride_token; a->nq = q->tokens;
+  a->q_bucket = q_bucket; a->q_perm = q_perm; a->n_probes = mode == 0 ? n_probes : 1;
+  a->k = k->data; a->k_sh = k->stride_head; a->k_st = k->stride_token;
+  a->v = v->data; a->v_sh = v->stride_head; a->v_st = v->stride_token; a->nk = k->tokens;
+  a->key_bias = key_bias; a->k_offsets = k_offsets; a->k_perm = k_perm; a->n_bits = n_bits;
+  a->key_list = key_list; a->n_key_list = n_key_list;
+  a->scale = scale; a->out = out; a->lse = lse;
+  a->heads = q->heads; a->dim = q->dim; a->dtype = q->dtype; a->mode = mode;
+  return FASTAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -127,27 +291,10 @@ fastar_status_t fastar_hash(const fastar_tensor_t* x, const void* planes, int n_
 fastar_status_t fastar_hash_multi(int count, const fastar_tensor_t* const* x, const int* n_probes,
                                   int32_t* const* bucket, const void* planes, int n_bits,
                                   fastar_diag_t* diag, hipStream_t stream) {
-  if (count < 1 || count > fastar::kMaxHashJobs)
-    return fail(FASTAR_ERR_INVALID, "count %d not in [1, %d]", count, fastar::kMaxHashJobs);
-  if (!x || !n_probes || !bucket) return fail(FASTAR_ERR_INVALID, "x, n_probes and bucket must be arrays");
   fastar::HashJobs jobs;
-  jobs.count = count;
-  bool any = false;
-  for (int i = 0; i < count; ++i) {
-    fastar_status_t st = check_tensor(x[i], "x[i]");
-    if (st != FASTAR_OK) return st;
-    if ((st = check_bits(n_bits, n_probes[i])) != FASTAR_OK) return st;
-    if (x[i]->dtype != x[0]->dtype || x[i]->dim != x[0]->dim)
-      return fail(FASTAR_ERR_INVALID, "x[%d]: dtype and dim must match x[0]", i);
-    const bool nonempty = (int64_t)x[i]->heads * x[i]->tokens > 0;
-    if (nonempty && !bucket[i]) return fail(FASTAR_ERR_INVALID, "bucket[%d] is NULL", i);
-    any = any || nonempty;
-    jobs.j[i] = fastar::HashJob{x[i]->data, x[i]->stride_head, x[i]->stride_token, x[i]->tokens,
-                                x[i]->heads, n_probes[i], bucket[i]};
-  }
-  if (!any) return FASTAR_OK;
-  if (n_bits > 0 && (!planes || !aligned16(planes)))
-    return fail(FASTAR_ERR_INVALID, "planes must be a non-null, 16-byte aligned pointer");
+  bool any;
+  const fastar_status_t st = hash_multi_check(count, x, n_probes, bucket, planes, n_bits, &jobs, &any);
+  if (st != FASTAR_OK || !any) return st;
   return hip_status(fastar::launch_hash_multi(jobs, x[0]->dim, x[0]->dtype, planes, n_bits, diag, stream),
                     "hash_multi");
 }
@@ -176,14 +323,7 @@ fastar_status_t fastar_bucket_index(const int32_t* bucket, int heads, int64_t n,
 
 // ---------------------------------------------------------------------------
 size_t fastar_tempcache_workspace(const fastar_cache_t* c, int n_frames) {
-  if (!c || n_frames < 0 || c->heads < 0 || c->tokens_per_frame < 0 || c->capacity < 0) return 0;
-  if (c->n_bits < 0 || c->n_bits > 15) return 0;
-  const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
-  const size_t nb = ((size_t)1 << c->n_bits) + 1;
-  const size_t nblk = (F * T + 63) / 64;
-  return align_up(4 * H * (F + 1) * nb) + 2 * align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
-         align_up(4 * H * F * T) + align_up(4 * H * (nblk + 1)) + align_up(4 * H * F * T) +
-         align_up(16 * H * (size_t)c->capacity);
+  return merge_workspace(c, n_frames);
 }
 
 fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
@@ -191,35 +331,13 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
                                        int n_frames, float tau, int32_t* group_of_new,
                                        int32_t* rep_offsets, int32_t* rep_perm, void* ws,
                                        size_t ws_bytes, fastar_diag_t* diag, hipStream_t stream) {
-  if (!c) return fail(FASTAR_ERR_INVALID, "cache is NULL");
-  fastar_status_t st;
-  if ((st = check_tensor(k_new, "k_new")) != FASTAR_OK) return st;
-  if ((st = check_tensor(v_new, "v_new")) != FASTAR_OK) return st;
-  if ((st = check_bits(c->n_bits, 1)) != FASTAR_OK) return st;
-  if (c->dtype != k_new->dtype || c->dtype != v_new->dtype)
-    return fail(FASTAR_ERR_INVALID, "cache, k_new and v_new must share one dtype");
-  if (c->dim != k_new->dim || c->dim != v_new->dim)
-    return fail(FASTAR_ERR_INVALID, "cache, k_new and v_new must share one dim");
-  if (c->heads != k_new->heads || c->heads != v_new->heads)
-    return fail(FASTAR_ERR_INVALID, "cache, k_new and v_new must share one head count");
-  if (n_frames < 0) return fail(FASTAR_ERR_INVALID, "n_frames < 0");
-  if (c->tokens_per_frame <= 0 || c->tokens_per_frame > 2048)
-    return fail(FASTAR_ERR_UNSUPPORTED, "tokens_per_frame %d not in [1, 2048]", c->tokens_per_frame);
-  if (k_new->tokens != (int64_t)n_frames * c->tokens_per_frame || v_new->tokens != k_new->tokens)
-    return fail(FASTAR_ERR_INVALID, "k_new/v_new must hold n_frames * tokens_per_frame tokens");
-  if (c->capacity < c->tokens_per_frame)
-    return fail(FASTAR_ERR_INVALID, "capacity %d < tokens_per_frame", c->capacity);
-  if ((int64_t)c->heads * c->capacity >= (int64_t)1 << 31)
-    return fail(FASTAR_ERR_UNSUPPORTED, "heads*capacity must be < 2^31");
-  if (!(tau == tau) || tau == INFINITY || tau == -INFINITY) return fail(FASTAR_ERR_INVALID, "tau must be finite");
-  if ((rep_offsets == nullptr) != (rep_perm == nullptr))
-    return fail(FASTAR_ERR_INVALID, "rep_offsets and rep_perm must both be given or both be NULL");
+  fastar_status_t st = merge_check(c, k_new, v_new, k_new_bucket, n_frames, tau, rep_offsets, rep_perm);
+  if (st != FASTAR_OK) return st;
   if (c->heads == 0 || n_frames == 0) {
     if (rep_offsets && c->heads > 0) {
-      if (!ws || ws_bytes < fastar_tempcache_workspace(c, n_frames))
+      if (!ws || ws_bytes < merge_workspace(c, n_frames))
         return fail(FASTAR_ERR_WORKSPACE, "workspace too small");
-      const size_t off = fastar_tempcache_workspace(c, n_frames) -
-                         align_up(16 * (size_t)c->heads * (size_t)c->capacity);
+      const size_t off = merge_workspace(c, n_frames) - align_up(16 * (size_t)c->heads * (size_t)c->capacity);
       return hip_status(fastar::launch_bucket_index(c->rep_bucket, c->heads, c->capacity, 1, c->n_bits,
                                                     c->n_groups, rep_offsets, rep_perm,
                                                     (int32_t*)((char*)ws + off), stream),
@@ -227,34 +345,12 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
     }
     return FASTAR_OK;
   }
-  if (!c->rep_k || !c->v_mean || !c->v_sum || !c->count || !c->log_count || !c->rep_bucket ||
-      !c->n_groups || !c->frontier || !k_new_bucket)
-    return fail(FASTAR_ERR_INVALID, "a cache buffer or k_new_bucket is NULL");
-  if (!aligned16(c->rep_k) || !aligned16(c->v_mean) || !aligned16(c->v_sum))
-    return fail(FASTAR_ERR_INVALID, "cache rows must be 16-byte aligned");
-  if (!ws || ws_bytes < fastar_tempcache_workspace(c, n_frames))
-    return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu",
-                fastar_tempcache_workspace(c, n_frames), ws_bytes);
-  const size_t H = c->heads, T = c->tokens_per_frame, F = n_frames;
-  const size_t nb = ((size_t)1 << c->n_bits) + 1;
-  char* w = (char*)ws;
-  auto take = [&](size_t bytes) {
-    char* p = w;
-    w += align_up(bytes);
-    return (int32_t*)p;
-  };
-  fastar::MergeWs mw;
-  mw.off = take(4 * H * (F + 1) * nb);
-  mw.tok = take(4 * H * (F + 1) * T);
-  mw.tbk = take(4 * H * (F + 1) * T);
-  mw.candg = take(4 * H * T);
-  mw.link = take(4 * H * F * T);
-  mw.ocnt = take(4 * H * ((F * T + 63) / 64 + 1));
-  mw.nextj = take(4 * H * F * T);
-  mw.index_ws = take(16 * H * (size_t)c->capacity);
+  if (!ws || ws_bytes < merge_workspace(c, n_frames))
+    return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", merge_workspace(c, n_frames),
+                ws_bytes);
   return hip_status(fastar::launch_tempcache_merge(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,
-                                                   group_of_new, rep_offsets, rep_perm, mw, diag,
-                                                   stream),
+                                                   group_of_new, rep_offsets, rep_perm,
+                                                   merge_carve(c, n_frames, ws), diag, stream),
                     "tempcache_merge");
 }
 
@@ -263,16 +359,9 @@ fastar_status_t fastar_prune_prompt(const int32_t* q_bucket, int heads, int64_t 
                                     const int32_t* p_bucket, int64_t n_prompt, int n_bits,
                                     uint8_t* keep, int32_t* kept_idx, int32_t* n_kept,
                                     hipStream_t stream) {
-  fastar_status_t st = check_bits(n_bits, n_probes);
-  if (st != FASTAR_OK) return st;
-  if (heads < 0 || n_q < 0 || n_prompt < 0) return fail(FASTAR_ERR_INVALID, "negative size");
-  if (heads == 0) return FASTAR_OK;
-  if (!n_kept) return fail(FASTAR_ERR_INVALID, "n_kept is NULL");
-  if (n_q > 0 && !q_bucket) return fail(FASTAR_ERR_INVALID, "q_bucket is NULL");
-  if (n_prompt > 0 && (!p_bucket || !keep || !kept_idx))
-    return fail(FASTAR_ERR_INVALID, "p_bucket, keep or kept_idx is NULL");
-  if ((int64_t)heads * n_q * n_probes >= (int64_t)1 << 31 || (int64_t)heads * n_prompt >= (int64_t)1 << 31)
-    return fail(FASTAR_ERR_UNSUPPORTED, "sizes must be < 2^31");
+  const fastar_status_t st =
+      prune_check(q_bucket, heads, n_q, n_probes, p_bucket, n_prompt, n_bits, keep, kept_idx, n_kept);
+  if (st != FASTAR_OK || heads == 0) return st;
   return hip_status(fastar::launch_prune(q_bucket, heads, n_q, n_probes, p_bucket, n_prompt, n_bits,
                                          keep, kept_idx, n_kept, stream),
                     "prune_prompt");
@@ -286,47 +375,129 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
                                         const int32_t* k_perm, int n_bits,
                                         const int32_t* key_list, const int32_t* n_key_list,
                                         float scale, void* out, float* lse, hipStream_t stream) {
-  fastar_status_t st;
-  if ((st = check_tensor(q, "q")) != FASTAR_OK) return st;
-  if ((st = check_tensor(k, "k")) != FASTAR_OK) return st;
-  if ((st = check_tensor(v, "v")) != FASTAR_OK) return st;
-  if (q->dtype != k->dtype || q->dtype != v->dtype) return fail(FASTAR_ERR_INVALID, "q, k, v dtypes differ");
-  if (q->dim != k->dim || q->dim != v->dim) return fail(FASTAR_ERR_INVALID, "q, k, v dims differ");
-  if (q->heads != k->heads || q->heads != v->heads) return fail(FASTAR_ERR_INVALID, "q, k, v head counts differ");
-  if (k->tokens != v->tokens) return fail(FASTAR_ERR_INVALID, "k and v token counts differ");
-  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return fail(FASTAR_ERR_INVALID, "scale must be finite");
-  int mode;
-  if (k_offsets || k_perm) {
-    if (!k_offsets || !k_perm) return fail(FASTAR_ERR_INVALID, "bucket mode needs k_offsets and k_perm");
-    if (key_list || n_key_list) return fail(FASTAR_ERR_INVALID, "give either bucket segments or a key list");
-    if ((st = check_bits(n_bits, n_probes)) != FASTAR_OK) return st;
-    mode = 0;
-  } else if (key_list || n_key_list) {
-    if (!key_list || !n_key_list) return fail(FASTAR_ERR_INVALID, "list mode needs key_list and n_key_list");
-    mode = 1;
-  } else {
-    mode = 2;
-  }
-  if ((int64_t)q->heads * q->tokens == 0) return FASTAR_OK;
-  if (!out || !aligned16(out)) return fail(FASTAR_ERR_INVALID, "out must be a non-null 16-byte aligned pointer");
-  if (mode == 0 && (!q_bucket || !q_perm)) return fail(FASTAR_ERR_INVALID, "bucket mode needs q_bucket and q_perm");
-  if (q->dtype == FASTAR_BF16 && k->tokens > 0) {
-    // the bf16 kernel addresses a head's k and v rows by 32-bit byte offsets
-    const int64_t span_k = ((int64_t)(k->tokens - 1) * k->stride_token + k->dim) * 2;
-    const int64_t span_v = ((int64_t)(v->tokens - 1) * v->stride_token + v->dim) * 2;
-    if (span_k > 0xFFFFFFFFll || span_v > 0xFFFFFFFFll)
-      return fail(FASTAR_ERR_UNSUPPORTED, "a head's k or v rows span more than 4 GiB");
-  }
   fastar::AttnArgs a;
-  a.q = q->data; a.q_sh = q->stride_head; a.q_st = q->stride_token; a.nq = q->tokens;
-  a.q_bucket = q_bucket; a.q_perm = q_perm; a.n_probes = mode == 0 ? n_probes : 1;
-  a.k = k->data; a.k_sh = k->stride_head; a.k_st = k->stride_token;
-  a.v = v->data; a.v_sh = v->stride_head; a.v_st = v->stride_token; a.nk = k->tokens;
-  a.key_bias = key_bias; a.k_offsets = k_offsets; a.k_perm = k_perm; a.n_bits = n_bits;
-  a.key_list = key_list; a.n_key_list = n_key_list;
-  a.scale = scale; a.out = out; a.lse = lse;
-  a.heads = q->heads; a.dim = q->dim; a.dtype = q->dtype; a.mode = mode;
+  bool empty;
+  const fastar_status_t st = attention_check(q, q_bucket, q_perm, n_probes, k, v, key_bias, k_offsets,
+                                             k_perm, n_bits, key_list, n_key_list, scale, out, lse, &a,
+                                             &empty);
+  if (st != FASTAR_OK || empty) return st;
   return hip_status(fastar::launch_attention(a, stream), "bucket_attention");
+}
+
+// ---------------------------------------------------------------------------
+namespace {
+// the cache's representatives and mean values as [H][capacity][dim] tensors
+fastar_tensor_t cache_rows(const fastar_cache_t* c, void* data) {
+  fastar_tensor_t t;
+  t.data = data;
+  t.dtype = c->dtype;
+  t.heads = c->heads;
+  t.tokens = c->capacity;
+  t.dim = c->dim;
+  t.reserved = 0;
+  t.stride_head = (int64_t)c->capacity * c->dim;
+  t.stride_token = c->dim;
+  return t;
+}
+size_t chunk_index_ws(const fastar_chunk_t* a) {
+  // the queries' index outside the merge's first launch needs scratch
+  if (fastar::direct_index_supported(a->q->tokens, a->n_probes, a->n_bits)) return 0;
+  return align_up(16 * (size_t)a->q->heads * (size_t)a->q->tokens);
+}
+}  // namespace
+
+size_t fastar_chunk_workspace(const fastar_chunk_t* a) {
+  if (!a || !a->cache || !a->q) return 0;
+  return merge_workspace(a->cache, a->n_frames) + chunk_index_ws(a);
+}
+
+fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes, fastar_diag_t* diag,
+                             hipStream_t stream) {
+  if (!a) return fail(FASTAR_ERR_INVALID, "arguments are NULL");
+  const fastar_cache_t* c = a->cache;
+  if (!c || !a->q || !a->k_new || !a->v_new) return fail(FASTAR_ERR_INVALID, "cache, q, k_new and v_new are required");
+  const bool prompt = a->prompt_k != nullptr;
+  if (prompt != (a->prompt_v != nullptr)) return fail(FASTAR_ERR_INVALID, "prompt_k and prompt_v go together");
+  if (a->q->heads != c->heads) return fail(FASTAR_ERR_INVALID, "q and the cache must share one head count");
+  if (a->n_frames <= 0) return fail(FASTAR_ERR_INVALID, "n_frames must be > 0");
+  if (!a->q_offsets || !a->q_perm || !a->rep_offsets || !a->rep_perm)
+    return fail(FASTAR_ERR_INVALID, "q_offsets, q_perm, rep_offsets and rep_perm are required");
+  fastar_status_t st;
+  // 1. one hashing: queries, new keys, prompt keys
+  const fastar_tensor_t* xs[3] = {a->q, a->k_new, a->prompt_k};
+  const int probes[3] = {a->n_probes, 1, 1};
+  int32_t* outs[3] = {a->q_bucket, a->k_bucket, a->p_bucket};
+  fastar::HashJobs jobs;
+  bool any;
+  if ((st = hash_multi_check(prompt ? 3 : 2, xs, probes, outs, a->planes, a->n_bits, &jobs, &any)) != FASTAR_OK)
+    return st;
+  if (a->q->tokens > 0 && !a->q_bucket) return fail(FASTAR_ERR_INVALID, "q_bucket is NULL");
+  // 2. the merge (and the queries' index)
+  if (c->n_bits != a->n_bits) return fail(FASTAR_ERR_INVALID, "the cache's n_bits differs from n_bits");
+  if ((st = merge_check(c, a->k_new, a->v_new, a->k_bucket, a->n_frames, a->tau, a->rep_offsets,
+                        a->rep_perm)) != FASTAR_OK)
+    return st;
+  if ((int64_t)a->q->heads * a->q->tokens * a->n_probes >= (int64_t)1 << 31)
+    return fail(FASTAR_ERR_UNSUPPORTED, "heads*tokens*n_probes must be < 2^31");
+  // 3. self-attention over the merged cache
+  const fastar_tensor_t rk = cache_rows(c, c->rep_k), vm = cache_rows(c, c->v_mean);
+  fastar::AttnArgs self, cross;
+  bool self_empty, cross_empty = true;
+  if ((st = attention_check(a->q, a->q_bucket, a->q_perm, a->n_probes, &rk, &vm, c->log_count,
+                            a->rep_offsets, a->rep_perm, a->n_bits, nullptr, nullptr, a->scale, a->out,
+                            a->lse, &self, &self_empty)) != FASTAR_OK)
+    return st;
+  // 4. AnnCA over the prompt
+  if (prompt) {
+    if (a->prompt_k->heads != c->heads) return fail(FASTAR_ERR_INVALID, "prompt and cache head counts differ");
+    if ((st = prune_check(a->q_bucket, a->q->heads, a->q->tokens, a->n_probes, a->p_bucket,
+                          a->prompt_k->tokens, a->n_bits, a->keep, a->kept_idx, a->n_kept)) != FASTAR_OK)
+      return st;
+    if ((st = attention_check(a->q, nullptr, nullptr, 1, a->prompt_k, a->prompt_v, nullptr, nullptr,
+                              nullptr, a->n_bits, a->kept_idx, a->n_kept, a->scale, a->out_cross,
+                              a->lse_cross, &cross, &cross_empty)) != FASTAR_OK)
+      return st;
+  }
+  const size_t need = fastar_chunk_workspace(a);
+  if (!ws || ws_bytes < need)
+    return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need, ws_bytes);
+
+  // launches, in order on the stream
+  if (any && (st = hip_status(fastar::launch_hash_multi(jobs, a->q->dim, a->q->dtype, a->planes, a->n_bits,
+                                                       diag, stream), "hash")) != FASTAR_OK)
+    return st;
+  fastar::MergeWs mw = merge_carve(c, a->n_frames, ws);
+  fastar::IndexJob qj{a->q_bucket, a->q->tokens, a->n_bits, a->q_offsets, a->q_perm};
+  const bool fused = chunk_index_ws(a) == 0 && a->q->tokens > 0;
+  if (fused) mw.also_index = &qj;
+  if ((st = hip_status(fastar::launch_tempcache_merge(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,
+                                                      a->tau, a->group_of_new, a->rep_offsets,
+                                                      a->rep_perm, mw, diag, stream),
+                       "tempcache_merge")) != FASTAR_OK)
+    return st;
+  if (!fused) {
+    int32_t* iws = (int32_t*)((char*)ws + merge_workspace(c, a->n_frames));
+    if ((st = hip_status(fastar::launch_bucket_index(a->q_bucket, a->q->heads, a->q->tokens, a->n_probes,
+                                                     a->n_bits, nullptr, a->q_offsets, a->q_perm, iws,
+                                                     stream),
+                         "bucket_index")) != FASTAR_OK)
+      return st;
+  }
+  if (!self_empty &&
+      (st = hip_status(fastar::launch_attention(self, stream), "bucket_attention")) != FASTAR_OK)
+    return st;
+  if (prompt) {
+    if (c->heads > 0 &&
+        (st = hip_status(fastar::launch_prune(a->q_bucket, a->q->heads, a->q->tokens, a->n_probes, a->p_bucket,
+                                              a->prompt_k->tokens, a->n_bits, a->keep, a->kept_idx,
+                                              a->n_kept, stream),
+                         "prune_prompt")) != FASTAR_OK)
+      return st;
+    if (!cross_empty &&
+        (st = hip_status(fastar::launch_attention(cross, stream), "bucket_attention")) != FASTAR_OK)
+      return st;
+  }
+  return FASTAR_OK;
 }
 
 }  // extern "C"

@@ -18,6 +18,7 @@
 // probe with at most 12 bits takes a single counting pass instead (below).
 
 #include "common.h"
+#include "index_direct.h"
 #include "kernels.h"
 
 namespace fastar {
@@ -283,171 +284,27 @@ __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
   write_offsets(off, nbk, nh, shift0, [&](int64_t p) { return kfinal[p]; }, &cnt[0][0]);
 }
 
-// One probe, 3..12 bits, at most 65535 items: a single stable counting pass.
-// Per-wave 16-bit bucket counters (kDirectWaves x 2^b) fit in LDS; one scan
-// over (bucket, wave) gives each wave's scatter bases and the offsets.  With
-// `stage`, the permutation is assembled in LDS and written out coalesced.
-constexpr int kDirectWaves = 8;
-constexpr int kDirectMinBits = 3;
-constexpr int kDirectMaxBits = 12;
-constexpr int64_t kDirectMaxItems = 65535;
-constexpr int64_t kDirectStageItems = 24000;
-
-__device__ __forceinline__ uint32_t half16(const int4& v, int e) {
-  const uint32_t w = (uint32_t)(e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w);
-  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
 template <int NBITS>
 __global__ __launch_bounds__(kDirectWaves * FASTAR_WAVE) void bucket_index_direct_kernel(
     const int32_t* __restrict__ bucket, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int stage) {
-  constexpr int nbits = NBITS;
-  // [kDirectWaves][2^nbits] uint16 counters (8 per 128-bit word), then the
-  // staged permutation (int32, n entries) when stage is set
   extern __shared__ int4 lds4[];
-  __shared__ int wtot[kDirectWaves];
-  constexpr int NT = kDirectWaves * FASTAR_WAVE;
-  static_assert((1 << kDirectMaxBits) / 8 == NT, "one 8-bucket group per thread");
-  const int h = blockIdx.x;
-  int64_t nh = n;
-  if (n_valid) {
-    const int64_t v = n_valid[h];
-    nh = v < 0 ? 0 : (v < n ? v : n);
-  }
-  const int nbk = 1 << nbits;
-  const int nb8 = nbk >> 3;
-  uint16_t* cnt = reinterpret_cast<uint16_t*>(lds4);
-  uint32_t* cnt32 = reinterpret_cast<uint32_t*>(lds4);
-  int32_t* pst = reinterpret_cast<int32_t*>(lds4 + kDirectWaves * nb8);
-  const uint32_t bmask = (uint32_t)nbk - 1u;
-  const int32_t* ids = bucket + (int64_t)h * n;
-  int32_t* ph = perm + (int64_t)h * n;
-  int32_t* off = offsets + (int64_t)h * (nbk + 1);
-  const int wave = threadIdx.x >> 6;
-  const int lane = lane_id();
-  for (int i = threadIdx.x; i < kDirectWaves * nb8; i += NT) lds4[i] = make_int4(0, 0, 0, 0);
-  __syncthreads();
-  const int64_t chunk = (nh + kDirectWaves - 1) / kDirectWaves;
-  const int64_t wbeg = (int64_t)wave * chunk < nh ? (int64_t)wave * chunk : nh;
-  const int64_t wend = wbeg + chunk < nh ? wbeg + chunk : nh;
-  const int wrow = wave * nbk;
-  // the wave's slice is handled in tiles of kTile ids per lane, loaded together
-  constexpr int kTile = 16;
-  // a slice of one tile keeps its ids in registers for the scatter
-  const bool one_tile = wend - wbeg <= kTile * FASTAR_WAVE;
-  uint32_t b[kTile];
-  for (int64_t t0 = wbeg; t0 < wend; t0 += kTile * FASTAR_WAVE) {
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-      const int64_t i = t0 + r * FASTAR_WAVE + lane;
-      b[r] = i < wend ? ((uint32_t)ids[i] & bmask) : 0xFFFFFFFFu;
-    }
-    // counts (order does not matter): the 16-bit counter in its 32-bit word
-#pragma unroll
-    for (int r = 0; r < kTile; ++r)
-      if (b[r] != 0xFFFFFFFFu)
-        atomicAdd(&cnt32[(wrow + (int)b[r]) >> 1], 1u << (16 * (b[r] & 1u)));
-  }
-  __syncthreads();
-  // exclusive scan over (bucket, wave): thread t owns buckets 8t .. 8t + 7,
-  // one 128-bit word per wave
-  const int t = threadIdx.x;
-  int4 cw[kDirectWaves];
-  uint32_t tot[8];
-  uint32_t local = 0;
-#pragma unroll
-  for (int w = 0; w < kDirectWaves; ++w) cw[w] = t < nb8 ? lds4[w * nb8 + t] : make_int4(0, 0, 0, 0);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    tot[e] = 0;
-#pragma unroll
-    for (int w = 0; w < kDirectWaves; ++w) tot[e] += half16(cw[w], e);
-    local += tot[e];
-  }
-  uint32_t incl = local;
-#pragma unroll
-  for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)incl, o, FASTAR_WAVE);
-    if (lane >= o) incl += y;
-  }
-  if (lane == FASTAR_WAVE - 1) wtot[wave] = (int)incl;
-  __syncthreads();
-  uint32_t run = incl - local;
-  for (int w = 0; w < wave; ++w) run += (uint32_t)wtot[w];
-  if (t < nb8) {
-    uint32_t base[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      base[e] = run;
-      run += tot[e];
-    }
-    // each wave's base within each bucket
-#pragma unroll
-    for (int w = 0; w < kDirectWaves; ++w) {
-      lds4[w * nb8 + t] = make_int4((int)(base[0] | (base[1] << 16)), (int)(base[2] | (base[3] << 16)),
-                                    (int)(base[4] | (base[5] << 16)), (int)(base[6] | (base[7] << 16)));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) base[e] += half16(cw[w], e);
-    }
-  }
-  __syncthreads();
-  // stable scatter: each wave walks its slice in order, 64 tokens at a time
-  for (int64_t t0 = wbeg; t0 < wend; t0 += kTile * FASTAR_WAVE) {
-    uint32_t bt[kTile];
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-      const int64_t i = t0 + r * FASTAR_WAVE + lane;
-      bt[r] = one_tile ? (b[r] & bmask) : (i < wend ? ((uint32_t)ids[i] & bmask) : 0u);
-    }
-#pragma unroll
-    for (int r = 0; r < kTile; ++r) {
-      const int64_t i = t0 + r * FASTAR_WAVE + lane;
-      if (t0 + r * FASTAR_WAVE >= wend) break;  // uniform
-      const bool valid = i < wend;
-      const uint32_t bb = bt[r];
-      // lanes of this row with the same bucket: those agreeing on every bit
-      // (lanes past the end are out of the first ballot)
-      uint64_t peers = ballot64(valid);
-#pragma unroll
-      for (int k = 0; k < NBITS; ++k) {
-        const uint32_t bit = (bb >> k) & 1u;
-        const uint64_t bk = ballot64(bit != 0u);
-        peers &= ~(bk ^ (0ull - (uint64_t)bit));
-      }
-      if (valid) {
-        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
-        const int pos = (int)cnt[wrow + (int)bb] + rank;
-        // two stores, not one through a generic pointer: an LDS store must
-        // not take the flat path that the next counter read would wait on
-        if (stage) pst[pos] = (int32_t)i;
-        else ph[pos] = (int32_t)i;
-        // the lowest peer (rank 0) advances the counter
-        if (rank == 0) cnt[wrow + (int)bb] = (uint16_t)(pos + __popcll(peers));
-      }
-    }
-  }
-  // after the scatter the last wave's counter of bucket B has reached the
-  // start of bucket B + 1: the offsets are written from it, coalesced, and so
-  // is a staged permutation
-  __syncthreads();
-  const uint16_t* last = cnt + (kDirectWaves - 1) * nbk;
-  for (int B = threadIdx.x; B <= nbk; B += NT) off[B] = B == 0 ? 0 : (int32_t)last[B - 1];
-  if (stage)
-    for (int64_t p = threadIdx.x; p < nh; p += NT) ph[p] = pst[p];
+  direct_index_body<NBITS>(blockIdx.x, bucket, n, n_valid, offsets, perm, stage, lds4);
 }
 
 }  // namespace
+
+bool direct_index_supported(int64_t n, int n_probes, int n_bits) {
+  return direct_index_fits(n, n_probes, n_bits);
+}
 
 hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int n_probes,
                                int n_bits, const int32_t* n_valid, int32_t* offsets,
                                int32_t* perm, int32_t* ws, hipStream_t s) {
   if (heads == 0) return hipSuccess;
-  if (n_probes == 1 && n_bits >= kDirectMinBits && n_bits <= kDirectMaxBits && n <= kDirectMaxItems) {
-    const int stage = n <= kDirectStageItems ? 1 : 0;
-    const size_t lds = (size_t)kDirectWaves * ((size_t)1 << n_bits) * sizeof(uint16_t) +
-                       (stage ? (size_t)n * sizeof(int32_t) : 0);
+  if (direct_index_fits(n, n_probes, n_bits)) {
+    int stage;
+    const size_t lds = direct_index_lds(n, n_bits, &stage);
     const dim3 grid(heads), block(kDirectWaves * FASTAR_WAVE);
     switch (n_bits) {
 #define FASTAR_DIRECT(B)                                                                         \

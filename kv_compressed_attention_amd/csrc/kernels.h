@@ -32,6 +32,10 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
                                int n_bits, const int32_t* n_valid, int32_t* offsets,
                                int32_t* perm, int32_t* ws, hipStream_t s);
 
+// whether launch_bucket_index uses the single counting pass (which the
+// merge's first launch can also run, IndexJob)
+bool direct_index_supported(int64_t n, int n_probes, int n_bits);
+
 // prune.hip -----------------------------------------------------------------
 hipError_t launch_prune(const int32_t* q_bucket, int heads, int64_t n_q, int n_probes,
                         const int32_t* p_bucket, int64_t n_prompt, int n_bits, uint8_t* keep,
@@ -51,6 +55,15 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // tempcache.hip -------------------------------------------------------------
+// a one-probe bucket index built by extra workgroups of the merge's first
+// launch (the chunk sequence's queries), n items per head, cache's heads
+struct IndexJob {
+  const int32_t* bucket;
+  int64_t n;
+  int n_bits;
+  int32_t* offsets;
+  int32_t* perm;
+};
 struct MergeWs {
   int32_t* off;       // [H][n_frames+1][2^b+1] bucket offsets per table (see tempcache.hip)
   int32_t* tok;       // [H][n_frames+1][T] tokens sorted by bucket
@@ -60,6 +73,7 @@ struct MergeWs {
   int32_t* ocnt;      // [H][ceil(n_frames T / 64) + 1]
   int32_t* nextj;     // [H][n_frames][T]
   int32_t* index_ws;  // bucket index scratch
+  const IndexJob* also_index = nullptr;  // direct-index job for the first launch, or none
 };
 hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
                                   const fastar_tensor_t& v_new, const int32_t* k_new_bucket,

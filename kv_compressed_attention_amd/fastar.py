@@ -50,6 +50,23 @@ class FastarCache(ctypes.Structure):
     ]
 
 
+class FastarChunk(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p), ("n_probes", ctypes.c_int),
+        ("k_new", ctypes.c_void_p), ("v_new", ctypes.c_void_p), ("n_frames", ctypes.c_int),
+        ("prompt_k", ctypes.c_void_p), ("prompt_v", ctypes.c_void_p),
+        ("planes", ctypes.c_void_p), ("n_bits", ctypes.c_int), ("tau", ctypes.c_float),
+        ("scale", ctypes.c_float),
+        ("cache", ctypes.c_void_p),
+        ("q_bucket", ctypes.c_void_p), ("q_offsets", ctypes.c_void_p), ("q_perm", ctypes.c_void_p),
+        ("k_bucket", ctypes.c_void_p), ("group_of_new", ctypes.c_void_p),
+        ("rep_offsets", ctypes.c_void_p), ("rep_perm", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("p_bucket", ctypes.c_void_p), ("keep", ctypes.c_void_p), ("kept_idx", ctypes.c_void_p),
+        ("n_kept", ctypes.c_void_p), ("out_cross", ctypes.c_void_p), ("lse_cross", ctypes.c_void_p),
+    ]
+
+
 class FastarError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"libfastar status {status}: {message}")
@@ -78,6 +95,8 @@ _SIGNATURES = {
     "fastar_tempcache_merge": (_I, [_CP, _TP, _TP, _P, _I, _F, _P, _P, _P, _P, _SZ, _P, _P]),
     "fastar_prune_prompt": (_I, [_P, _I, _I64, _I, _P, _I64, _I, _P, _P, _P, _P]),
     "fastar_bucket_attention": (_I, [_TP, _P, _P, _I, _TP, _TP, _P, _P, _P, _I, _P, _P, _F, _P, _P, _P]),
+    "fastar_chunk_workspace": (_SZ, [_P]),
+    "fastar_chunk": (_I, [_P, _P, _SZ, _P, _P]),
 }
 
 
@@ -302,3 +321,42 @@ def fastar_bucket_attention(q, k, v, scale: Optional[float] = None, q_bucket=Non
                                        _ptr(n_key_list), float(scale), _ptr(out), _ptr(lse),
                                        _stream(stream)))
     return out, lse
+
+
+class ChunkCall:
+    """fastar_chunk's argument block for fixed buffers: built once, so that a
+    call (also under HIP graph capture) only passes pointers."""
+
+    def __init__(self, q, n_probes, k_new, v_new, n_frames, planes, n_bits, tau, cache: TempCache,
+                 q_bucket, q_offsets, q_perm, k_bucket, rep_offsets, rep_perm, out, lse=None,
+                 group_of_new=None, scale=None, prompt_k=None, prompt_v=None, p_bucket=None,
+                 keep=None, kept_idx=None, n_kept=None, out_cross=None, lse_cross=None):
+        d = q.shape[-1]
+        self._keep = []  # everything the pointers below refer to
+
+        def desc(t):
+            if t is None:
+                return None
+            dd = _desc(t)
+            self._keep.append(dd)
+            return ctypes.addressof(dd)
+
+        self.cache_struct = cache.struct()
+        p = lambda t: None if t is None else _ptr(t).value
+        self.args = FastarChunk(
+            desc(q), n_probes, desc(k_new), desc(v_new), n_frames, desc(prompt_k), desc(prompt_v),
+            p(planes), n_bits, tau, float(scale if scale is not None else d ** -0.5),
+            ctypes.addressof(self.cache_struct),
+            p(q_bucket), p(q_offsets), p(q_perm), p(k_bucket), p(group_of_new), p(rep_offsets),
+            p(rep_perm), p(out), p(lse), p(p_bucket), p(keep), p(kept_idx), p(n_kept), p(out_cross),
+            p(lse_cross))
+        self._keep += [q, k_new, v_new, prompt_k, prompt_v, planes, q_bucket, q_offsets, q_perm,
+                       k_bucket, group_of_new, rep_offsets, rep_perm, out, lse, p_bucket, keep,
+                       kept_idx, n_kept, out_cross, lse_cross]
+
+    def workspace_bytes(self) -> int:
+        return library().fastar_chunk_workspace(ctypes.byref(self.args))
+
+    def __call__(self, ws, diag=None, stream=None):
+        _check(library().fastar_chunk(ctypes.byref(self.args), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _ptr(diag), _stream(stream)))

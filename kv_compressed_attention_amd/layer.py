@@ -12,9 +12,11 @@ compressed cache including the chunk's own frames):
   5. AnnSA bucket attention over the cache with the + ln m bias;
   6. cross-attention over the kept prompt tokens.
 Every step is a libfastar call; this class only owns the torch buffers and
-the ordering.  The query side (2, then 4 and 6) does not touch the cache, so
-it runs on a second stream of default priority, concurrently with 3 up to
-5's need for the query index; all streams join before step returns.
+the ordering.  By default one fastar_chunk call runs the whole sequence on
+the caller's stream (the queries' index built in the merge's first launch).
+The other orders issue the calls one by one: on one stream, or with the
+query side (2, then 4 and 6), which does not touch the cache, on a second
+stream of default priority; all streams join before step returns.
 """
 
 from __future__ import annotations
@@ -43,7 +45,9 @@ class FastARLayer:
         ws_bytes = max(lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
                        lib.fastar_hash_workspace(H, nk, n_bits, 1),
                        lib.fastar_hash_workspace(H, n_prompt, n_bits, 1),
-                       self.cache.workspace_bytes(chunk_frames),
+                       # fastar_chunk: the merge's, then (at most) the queries' index scratch
+                       self.cache.workspace_bytes(chunk_frames) +
+                       lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
                        self.cache.workspace_bytes(1))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         # the query-side stream has a workspace of its own
@@ -68,6 +72,7 @@ class FastARLayer:
             self.o_cross = torch.empty(H, n_queries, dim, dtype=dtype, device=dev)
             self.lse_cross = torch.empty(H, n_queries, dtype=torch.float32, device=dev)
         self.diag = fb.new_diag(dev)
+        self._calls = {}
 
     def set_planes(self, planes: torch.Tensor):
         if self.n_bits:
@@ -149,18 +154,64 @@ class FastARLayer:
             k_offsets=self.rep_off, k_perm=self.rep_perm, n_bits=self.n_bits, out=self.o_self,
             lse=self.lse_self))
 
-    def step(self, q, k_new, v_new, prompt_k=None, prompt_v=None, cache=None, concurrent=True,
+    def _chunk_call(self, q, k_new, v_new, prompt_k, prompt_v, cache):
+        key = tuple(0 if t is None else t.data_ptr() for t in (q, k_new, v_new, prompt_k, prompt_v)) + (
+            id(cache),)
+        call = self._calls.get(key)
+        if call is None:
+            extra = {}
+            if prompt_k is not None:
+                extra = dict(prompt_k=prompt_k, prompt_v=prompt_v, p_bucket=self.p_ids, keep=self.keep,
+                             kept_idx=self.kept_idx, n_kept=self.n_kept, out_cross=self.o_cross,
+                             lse_cross=self.lse_cross)
+            call = fb.ChunkCall(q, self.n_probes, k_new, v_new, self.chunk_frames, self.planes,
+                                self.n_bits, self.tau, cache, self.q_ids, self.q_off, self.q_perm,
+                                self.k_ids, self.rep_off, self.rep_perm, self.o_self,
+                                lse=self.lse_self, group_of_new=self.group_of_new, **extra)
+            self._calls[key] = call
+        return call
+
+    def step(self, q, k_new, v_new, prompt_k=None, prompt_v=None, cache=None, concurrent="chunk",
              timing=None):
         """One chunk, merged into ``cache`` (default: the layer's own).
 
-        With ``concurrent`` the query side runs on the second stream, forked
-        after everything already queued on the caller's stream (the previous
-        step's readers of the query index included) and joined before the
-        self-attention; otherwise every stage is queued on the caller's stream
-        in order.
+        ``concurrent``: "chunk" (default) one fastar_chunk call; False every
+        call queued on the caller's stream in order; True the query side on
+        the second stream, forked after everything already queued on the
+        caller's stream and joined before the self-attention; "split" the
+        query hashing on the second stream as well.
         ``timing`` (optional dict) receives (start, end) event pairs per
         stage, recorded on the stream each stage runs on."""
         cache = self.cache if cache is None else cache
+        if concurrent == "chunk":
+            call = self._chunk_call(q, k_new, v_new, prompt_k, prompt_v, cache)
+            self._timed(timing, "chunk", lambda: call(self.ws, diag=self.diag))
+            return
+        if concurrent == "split":
+            # the query side as its own branch from the start: its hashing
+            # and index on the second stream, queued first; the keys' hashing
+            # and the merge on this one
+            main = torch.cuda.current_stream(self.device)
+            start = self._ev(None)
+            with torch.cuda.stream(self.side):
+                self.side.wait_event(start)
+                self._timed(timing, "hash_q", lambda: fb.fastar_hash_multi(
+                    [q] + ([prompt_k] if prompt_k is not None else []), self.planes, self.n_bits,
+                    [self.n_probes] + ([1] if prompt_k is not None else []),
+                    buckets=[self.q_ids] + ([self.p_ids] if prompt_k is not None else []),
+                    diag=self.diag))
+                self._query_index(timing)
+                q_done = self._ev(None)
+                if prompt_k is not None:
+                    self._cross(q, prompt_k, prompt_v, timing, hashed=True)
+                side_done = self._ev(None)
+            self._timed(timing, "hash_k", lambda: fb.fastar_hash_multi(
+                [k_new], self.planes, self.n_bits, [1], buckets=[self.k_ids], diag=self.diag))
+            self._merge(cache, k_new, v_new, timing)
+            main.wait_event(q_done)
+            self.self_attention(q, timing, cache)
+            main.wait_event(side_done)
+            return
         self._hash_all(q, k_new, prompt_k, timing)
         if not concurrent:
             self._query_index(timing)
@@ -184,7 +235,7 @@ class FastARLayer:
         main.wait_event(side_done)
 
     def capture(self, q, k_new, v_new, prompt_k=None, prompt_v=None, cache=None,
-                concurrent=True):
+                concurrent="chunk"):
         """Capture one chunk on these buffers into a HIP graph, replayed with
         ``.replay()`` on the current stream: one graph launch instead of one
         launch per kernel.

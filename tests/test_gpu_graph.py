@@ -39,7 +39,7 @@ def _same(a, b):
     return torch.equal(a, b)
 
 
-@pytest.mark.parametrize("concurrent", [True, False])
+@pytest.mark.parametrize("concurrent", ["chunk", True, False])
 @pytest.mark.parametrize("index", [0, 1])
 def test_graph_replay_matches_eager(index, concurrent):
     if not torch.cuda.is_available():
@@ -83,7 +83,7 @@ def test_graph_replay_matches_eager(index, concurrent):
         if rep == 1:
             # an eager step in between gives the same result too
             restore()
-            layer.step(q, k_new, v_new, concurrent=not concurrent)
+            layer.step(q, k_new, v_new, concurrent=False if concurrent is not False else "chunk")
             torch.cuda.synchronize()
             for n, t in _outputs(layer).items():
                 assert _same(t, ref[n]), f"eager step after replays: {n}"
