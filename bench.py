@@ -12,13 +12,14 @@ region); after the run the K merged caches are checked to be identical.
 
 A step is one fastar_chunk call: the queries and the new keys hashed in one
 launch, the queries' index built by extra workgroups of the merge's first
-launch, all on one stream (--order picks the older call-by-call orders,
-on one stream or with the query side on a second one).  Each step is
-captured into a HIP graph and replayed (--eager launches from Python
-instead, with per-call event times in "stages_ms").  The attention
-kernel's duration for the roofline comes from HIP events around K launches of
-it on its stream right after the timed region (inside a graph there is no
-stream to record them on).
+launch, all on one stream (--order picks the older call-by-call orders, on
+one stream or with the query side on a second one).  The steps are captured
+into HIP graphs, --graph-steps of them (each on its own cache) per graph, as
+a model captures the chunks of its layers together, and replayed (--eager
+launches from Python instead, with per-call event times in "stages_ms").
+The attention kernel's duration for the roofline comes from HIP events
+around K launches of it on its stream right after the timed region (inside
+a graph there is no stream to record them on).
 
 Prints one JSON line.  --gpus N with N > 1 is refused: the library has no
 multi-GPU path (heads are independent, so a multi-GPU layer would shard them
@@ -49,6 +50,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--graph-steps", type=int, default=10,
+                   help="steps captured per HIP graph (each on its own cache, in order, as the "
+                        "chunks of a model's layers are captured together)")
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=1, help="synthetic workload index (1, 3 or 4)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -198,7 +202,9 @@ def main():
         def step(i):
             layer.step(q, k_new, v_new, cache=caches[i], concurrent=concurrent, timing=timing)
     else:
-        graphs = [layer.capture(q, k_new, v_new, cache=c, concurrent=concurrent) for c in caches]
+        G = max(1, args.graph_steps)
+        graphs = [layer.capture(q, k_new, v_new, concurrent=concurrent, caches=caches[i:i + G])
+                  for i in range(0, args.steps, G)]
         warm = layer.capture(q, k_new, v_new, cache=scratch, concurrent=concurrent)
         for _ in range(args.warmup):
             scratch.copy_from(pristine)
@@ -206,7 +212,9 @@ def main():
         torch.cuda.synchronize()
 
         def step(i):
-            graphs[i].replay()
+            # one graph launch runs steps i .. i + G - 1
+            if i % G == 0:
+                graphs[i // G].replay()
     # timed region: exactly K steps (eager: with HIP events around the
     # stages, each recorded on the stream its stage is enqueued on)
     t0 = time.perf_counter()
@@ -259,7 +267,7 @@ def main():
                       "attended_pairs": pairs,
                       "query_tokens_per_s": nq / t_att,
                       "compressed_keys_per_head": ngb_after(layer, caches[-1])},
-        "launch": ("eager" if args.eager else "hip_graph") + "_" + args.order,
+        "launch": ("eager" if args.eager else f"hip_graph{max(1, args.graph_steps)}") + "_" + args.order,
         "stages_ms": stage_ms,
         "host_enqueue_ms_per_step": t_enq * 1e3 / args.steps,
         "diag": layer.diag.tolist(),

@@ -235,10 +235,12 @@ class FastARLayer:
         main.wait_event(side_done)
 
     def capture(self, q, k_new, v_new, prompt_k=None, prompt_v=None, cache=None,
-                concurrent="chunk"):
+                concurrent="chunk", caches=None):
         """Capture one chunk on these buffers into a HIP graph, replayed with
         ``.replay()`` on the current stream: one graph launch instead of one
-        launch per kernel.
+        launch per kernel.  With ``caches``, one chunk per cache in order (as
+        a model captures the chunks of its layers together), one launch for
+        all of them.
 
         Call after at least one eager ``step`` (first use of torch's streams
         and events does one-time set-up, which capture does not allow).  Every
@@ -246,6 +248,7 @@ class FastARLayer:
         torch.cuda.synchronize(self.device)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            self.step(q, k_new, v_new, prompt_k, prompt_v, cache=cache, concurrent=concurrent)
+            for c in (caches if caches is not None else [cache]):
+                self.step(q, k_new, v_new, prompt_k, prompt_v, cache=c, concurrent=concurrent)
         torch.cuda.synchronize(self.device)
         return g
