@@ -110,6 +110,42 @@ def test_hash_multi_rejects_bad_arguments_without_launching(lib):
     assert call([a, b], [1, 1], bits=16) == 2            # n_bits
 
 
+def test_chunk_rejects_bad_arguments_without_launching(lib):
+    """fastar_chunk checks every stage's arguments before its first launch:
+    each of these calls fails on the host (no GPU here: a launch would fail
+    with a HIP status instead)."""
+    buf = 1 << 20
+    q, k = _tensor(tokens=32), _tensor(tokens=3 * 16)
+    cache = fb.FastarCache(2, 128, 64, 16, 12, 1, *([buf] * 8))
+
+    def args(**kw):
+        a = dict(q=ctypes.addressof(q), n_probes=1, k_new=ctypes.addressof(k), v_new=ctypes.addressof(k),
+                 n_frames=3, planes=buf, n_bits=12, tau=0.9, scale=0.1, cache=ctypes.addressof(cache),
+                 q_bucket=buf, q_offsets=buf, q_perm=buf, k_bucket=buf, rep_offsets=buf, rep_perm=buf,
+                 out=buf)
+        a.update(kw)
+        return fb.FastarChunk(**a)
+
+    def call(a, ws_bytes=1 << 30):
+        return lib.fastar_chunk(ctypes.byref(a), ctypes.c_void_p(buf), ws_bytes, None, None)
+
+    assert lib.fastar_chunk(None, None, 0, None, None) == 1
+    assert call(args(cache=None)) == 1                       # no cache
+    assert call(args(n_frames=2)) == 1                       # k_new holds 3 frames
+    assert call(args(n_probes=3)) == 2                       # probes
+    assert call(args(n_bits=10)) == 1                        # differs from the cache's
+    assert call(args(tau=float("inf"))) == 1                 # tau
+    assert call(args(scale=float("nan"))) == 1               # scale
+    assert call(args(q_perm=None)) == 1                      # the queries' index is required
+    assert call(args(prompt_k=ctypes.addressof(k))) == 1     # prompt_k without prompt_v
+    qh = _tensor(heads=3, tokens=32)
+    assert call(args(q=ctypes.addressof(qh))) == 1           # head counts differ
+    assert call(args(), ws_bytes=16) == 3                    # workspace
+    assert b"workspace" in lib.fastar_last_error()
+    assert lib.fastar_chunk_workspace(ctypes.byref(args())) >= lib.fastar_tempcache_workspace(
+        ctypes.byref(cache), 3)
+
+
 def test_attention_rejects_bad_arguments_without_launching(lib):
     buf = ctypes.c_void_p(1 << 20)
     q, k = _tensor(), _tensor(tokens=32)
