@@ -96,7 +96,7 @@ size_t merge_workspace(const fastar_cache_t* c, int n_frames) {
   const size_t nblk = (F * T + 63) / 64;
   return align_up(4 * H * (F + 1) * nb) + 2 * align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
          align_up(4 * H * F * T) + align_up(4 * H * (nblk + 1)) + align_up(4 * H * F * T) +
-         align_up(16 * H * (size_t)c->capacity);
+         align_up(12 * H * F * T) + align_up(16 * H * (size_t)c->capacity);
 }
 
 // everything fastar_tempcache_merge checks for a call with n_frames > 0 and
@@ -153,6 +153,7 @@ fastar::MergeWs merge_carve(const fastar_cache_t* c, int n_frames, void* ws) {
   mw.link = take(4 * H * F * T);
   mw.ocnt = take(4 * H * ((F * T + 63) / 64 + 1));
   mw.nextj = take(4 * H * F * T);
+  mw.prop = take(12 * H * F * T);
   mw.index_ws = take(16 * H * (size_t)c->capacity);
   return mw;
 }

@@ -31,8 +31,6 @@ namespace fastar {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-// s_waitcnt immediate: vector memory count 0, the other counters unconstrained
-constexpr int kWaitVm0 = 0x0F70;
 constexpr float kLn2 = 0.6931471805599453f;
 
 template <int NB>

@@ -11,6 +11,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 #define FASTAR_WAVE 64
 
+// s_waitcnt immediate: vector memory count 0, the other counters unconstrained
+constexpr int kWaitVm0 = 0x0F70;
+
 // Workgroups are handed to the 8 XCDs (each with its own L2) round-robin by
 // launch order.  xcd_block maps launch index i of a 1-D grid of
 // 8 * xcd_span(n) workgroups to logical block i % 8 * xcd_span(n) + i / 8, so
@@ -104,6 +107,19 @@ __device__ __forceinline__ int wave_reduce_dpp(int v, Op op) {
   v = op((int)r[0], (int)r[1]);
   r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
   return op((int)r[0], (int)r[1]);
+}
+// inclusive prefix sum over the wave without LDS: shifts within rows of 16
+// (lanes shifted in from outside the row add 0), then each row adds the
+// totals of the rows before it (row_bcast:15 to rows 1 and 3, row_bcast:31
+// to rows 2 and 3)
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
 }
 __device__ __forceinline__ int wave_min_dpp(int v) {
   return wave_reduce_dpp(v, [](int a, int b) { return min(a, b); });

@@ -18,11 +18,6 @@ constexpr int64_t kDirectMaxItems = 65535;
 // LDS left for the staged permutation next to the counters
 constexpr size_t kDirectLds = 152 * 1024;
 
-__device__ __forceinline__ uint32_t direct_half16(const int4& v, int e) {
-  const uint32_t w = (uint32_t)(e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w);
-  return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
-}
-
 // LDS bytes the direct index of n items needs, and whether it stages the
 // permutation there
 inline size_t direct_index_lds(int64_t n, int n_bits, int* stage) {
@@ -46,7 +41,8 @@ __device__ __forceinline__ void direct_index_body(int h, const int32_t* __restri
   // the staged permutation (int32, n entries) when stage is set
   __shared__ int wtot[kDirectWaves];
   constexpr int NT = kDirectWaves * FASTAR_WAVE;
-  static_assert((1 << kDirectMaxBits) / 8 <= NT, "at most one 8-bucket group per thread");
+  static_assert((1 << kDirectMaxBits) / 4 <= NT, "at most one 4-bucket group per thread");
+  static_assert((1 << kDirectMinBits) >= 4, "whole 4-bucket groups");
   int64_t nh = n;
   if (n_valid) {
     const int64_t v = n_valid[h];
@@ -87,46 +83,42 @@ __device__ __forceinline__ void direct_index_body(int h, const int32_t* __restri
         atomicAdd(&cnt32[(wrow + (int)b[r]) >> 1], 1u << (16 * (b[r] & 1u)));
   }
   __syncthreads();
-  // exclusive scan over (bucket, wave): thread t owns buckets 8t .. 8t + 7,
-  // one 128-bit word per wave
+  // exclusive scan over (bucket, wave): thread t owns buckets 4t .. 4t + 3,
+  // one 64-bit word per wave
   const int t = threadIdx.x;
-  uint32_t tot[8];
-  uint32_t local = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) tot[e] = 0;
-#pragma unroll 4
+  const int nb4 = nbk >> 2;
+  uint2* c64 = reinterpret_cast<uint2*>(lds4);
+  uint32_t tot[4] = {0u, 0u, 0u, 0u};
+#pragma unroll 8
   for (int w = 0; w < kDirectWaves; ++w) {
-    const int4 cw = t < nb8 ? lds4[w * nb8 + t] : make_int4(0, 0, 0, 0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) tot[e] += direct_half16(cw, e);
+    const uint2 cw = t < nb4 ? c64[w * nb4 + t] : make_uint2(0u, 0u);
+    tot[0] += cw.x & 0xFFFFu;
+    tot[1] += cw.x >> 16;
+    tot[2] += cw.y & 0xFFFFu;
+    tot[3] += cw.y >> 16;
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) local += tot[e];
-  uint32_t incl = local;
-#pragma unroll
-  for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)incl, o, FASTAR_WAVE);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t local = tot[0] + tot[1] + tot[2] + tot[3];
+  const uint32_t incl = wave_incl_scan_dpp(local);
   if (lane == FASTAR_WAVE - 1) wtot[wave] = (int)incl;
   __syncthreads();
   uint32_t run = incl - local;
   for (int w = 0; w < wave; ++w) run += (uint32_t)wtot[w];
-  if (t < nb8) {
-    uint32_t base[8];
+  if (t < nb4) {
+    uint32_t base[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       base[e] = run;
       run += tot[e];
     }
     // each wave's base within each bucket (replacing the wave's counts)
-#pragma unroll 4
+#pragma unroll 8
     for (int w = 0; w < kDirectWaves; ++w) {
-      const int4 cw = lds4[w * nb8 + t];
-      lds4[w * nb8 + t] = make_int4((int)(base[0] | (base[1] << 16)), (int)(base[2] | (base[3] << 16)),
-                                    (int)(base[4] | (base[5] << 16)), (int)(base[6] | (base[7] << 16)));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) base[e] += direct_half16(cw, e);
+      const uint2 cw = c64[w * nb4 + t];
+      c64[w * nb4 + t] = make_uint2(base[0] | (base[1] << 16), base[2] | (base[3] << 16));
+      base[0] += cw.x & 0xFFFFu;
+      base[1] += cw.x >> 16;
+      base[2] += cw.y & 0xFFFFu;
+      base[3] += cw.y >> 16;
     }
   }
   __syncthreads();

@@ -216,6 +216,7 @@ struct MergeArgs {
                       // (frame, j) order (nblk = ceil(F Tf / 64) blocks), then
                       // the group count before the call
   int32_t* nextj;     // [H][F][Tf] token of frame f + 1 that extends this one, or -1
+  int32_t* prop;      // [H][F][3][Tf] proposals of workgroups whose lists stay global
 };
 
 __device__ __forceinline__ int64_t off_off(const MergeArgs& a, int h, int t) {
@@ -323,6 +324,20 @@ struct TileDot<uint16_t, D> {
 #pragma unroll
     for (int c = 0; c < NC; ++c) s += sumsq(r.u[c]);
     return sum_xor32(sum_xor16(s));
+  }
+  // row r of an LDS tile whose row r holds 16-byte piece p at position
+  // p ^ (r % (D / 8)) (all zero for r >= n)
+  __device__ __forceinline__ static Rows from_lds(const uint16_t* rows, int r, int n) {
+    constexpr int kPieces = D / 8;
+    const int g = lane_id() >> 4;
+    Rows o;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      o.u[c] = make_uint4(0u, 0u, 0u, 0u);
+      if (r < n)
+        o.u[c] = *reinterpret_cast<const uint4*>(rows + r * D + (((4 * c + g) ^ (r % kPieces)) * 8));
+    }
+    return o;
   }
   __device__ __forceinline__ void issue_keys(const uint16_t* row) { kr = issue(row); }
   __device__ __forceinline__ void finish_keys() { kn = rownorm(kr); }
@@ -509,13 +524,14 @@ __device__ __forceinline__ void reduce_top2(Top2<float>& t) {
 // it proposes to, -1: none) and c (the cosine).  Candidates are visited in
 // tiles of 16, the next tile's rows loading while the current one is used;
 // lane l compares its key l & 15 with candidates 4 (l >> 4) .. + 3 of each.
-template <typename T, int D>
+template <typename T, int D, bool LROWS>
 __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t* ktok,
                                            const int32_t* kbk, int k0, int kend,
                                            const int32_t* ctok, const int32_t* cbk,
                                            const int32_t* cg, int c_lo, int c_hi,
                                            const int32_t* gtok, const int32_t* gcg,
-                                           const int32_t* coff, int& jrep, int& p, float& c) {
+                                           const int32_t* coff, TileDot<T, D>& td,
+                                           const uint16_t* crow, int& jrep, int& p, float& c) {
   using TD = TileDot<T, D>;
   const int lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
@@ -533,15 +549,16 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
   __shared__ __attribute__((aligned(16))) int32_t tt_bk[4][16];
   __shared__ __attribute__((aligned(16))) float tt_rn[4][16];
   const int wv = threadIdx.x >> 6;
-  // candidate ids of the first tile (the row this lane fetches), with the
-  // key rows
+  // candidate ids of the first tile (the row this lane fetches); the key
+  // rows were issued by the caller.  LROWS: the candidate rows are staged in
+  // LDS (crow, one row per candidate of the workgroup's range).
   bool cv = c_lo + col < c_hi;
   int ci = cv ? ctok[c_lo + col] : 0;
   int cb = cv ? cbk[c_lo + col] : -2;
   int cgi = (cv && x.f == 0) ? cg[c_lo + col] : 0;
-  TD td;
-  td.issue_keys(jr >= 0 ? x.kf + (int64_t)jr * x.k_st : nullptr);
-  typename TD::Rows cr = TD::issue(cv ? x.cand_row(0, ci, cgi) : nullptr);
+  typename TD::Rows cr;
+  if constexpr (LROWS) cr = TD::from_lds(crow, c_lo + col, c_hi);
+  else cr = TD::issue(cv ? x.cand_row(0, ci, cgi) : nullptr);
   td.finish_keys();
   const float rk = td.kn > 0.f ? rsqrtf(td.kn) : 0.f;
   Top2<float> t;
@@ -569,7 +586,10 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (bi[i] == rb) t.add(sd[i] * rk * ri[i], ti[i]);
-    if (c0 + 16 < c_hi) cr = TD::issue(nv ? x.cand_row(0, ni, ng) : nullptr);
+    if (c0 + 16 < c_hi) {
+      if constexpr (LROWS) cr = TD::from_lds(crow, c0 + 16 + col, c_hi);
+      else cr = TD::issue(nv ? x.cand_row(0, ni, ng) : nullptr);
+    }
     cv = nv;
     ci = ni;
     cb = nb;
@@ -652,19 +672,34 @@ __device__ __forceinline__ int count_until(const int32_t* v, int n, int b, bool 
   return cnt;
 }
 
+// candidate rows a bf16 workgroup stages in LDS
+constexpr int kRowCands = 96;
+
+// LDS int32 words of a match workgroup: proposals and lists, then (bf16)
+// the staged candidate rows
+template <typename T, int D>
+constexpr size_t match_lds_words() {
+  return 3 * kStageKeys + 2 * kStageKeys + 3 * kStageCands +
+         (sizeof(T) == 2 ? (size_t)kRowCands * D / 2 : 0);
+}
+
 // One workgroup per kKeysPerGroup positions of frame f's bucket-sorted keys,
 // rounded to whole buckets: a workgroup owns the buckets whose first key lies
-// in its positions.  It copies its keys' ids and buckets and the candidate
-// ids, buckets and groups of its bucket range to LDS, then its waves take the
-// tiles of 16 consecutive keys (step 1, each key's best candidate and
-// proposal) and, after one barrier, step 2 over all of its keys: every
-// candidate keeps its best proposer (ties: smaller j), which links to it; the
-// other keys open groups.  A candidate's proposers all share its bucket, so
-// they are all in the workgroup.
-template <typename T, int D, bool STAGED>
+// in its positions.  MODE 0: the lists and the proposals stay in global
+// memory (very large buckets); 1: the workgroup copies its keys' ids and
+// buckets and the candidate ids, buckets and groups of its bucket range to
+// LDS, and keeps the proposals there; 2 (bf16): also the candidate rows,
+// fetched once by the whole workgroup while each wave's first key rows load.
+// Then its waves take the tiles of 16 consecutive keys (step 1, each key's
+// best candidate and proposal) and, after one barrier, step 2 over all of
+// its keys: every candidate keeps its best proposer (ties: smaller j), which
+// links to it; the other keys open groups.  A candidate's proposers all
+// share its bucket, so they are all in the workgroup.
+template <typename T, int D, int MODE>
 __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeArgs& a, int h,
                                             int p0, int p1, int c0, int c1,
                                             const int32_t* __restrict__ frontier, int32_t* lds) {
+  constexpr bool STAGED = MODE >= 1;
   const int f = x.f;
   const int lane = lane_id();
   const int col = lane & 15;
@@ -678,12 +713,16 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
   const int32_t* gcg = a.candg + (int64_t)h * a.Tf;
   const int nk = p1 - p0;
   const int nc = c1 - c0;
-  int32_t* lp = lds;
-  float* lc = reinterpret_cast<float*>(lds + a.Tf);
-  int32_t* lj = lds + 2 * a.Tf;
+  // proposals of the keys by position: LDS, or the workspace's frame slice
+  int32_t* const pbase = STAGED ? lds : a.prop + frame_off(a, h, f) * 3 + p0;
+  const int pst = STAGED ? kStageKeys : a.Tf;
+  int32_t* lp = pbase;
+  float* lc = reinterpret_cast<float*>(pbase + pst);
+  int32_t* lj = pbase + 2 * pst;
   // the key and candidate lists, rebased to the workgroup's ranges
-  int32_t* sk = lds + 3 * a.Tf;            // [2][kStageKeys] tokens, buckets
+  int32_t* sk = lds + 3 * kStageKeys;      // [2][kStageKeys] tokens, buckets
   int32_t* sc = sk + 2 * kStageKeys;       // [3][kStageCands] tokens, buckets, groups
+  uint16_t* crow = reinterpret_cast<uint16_t*>(sc + 3 * kStageCands);  // [kRowCands][D]
   const int32_t* ktok = STAGED ? sk : gktok + p0;
   const int32_t* kbk = STAGED ? sk + kStageKeys : gkbk + p0;
   const int32_t* ctok = STAGED ? sc : gctok + c0;
@@ -701,7 +740,31 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
     }
     __syncthreads();
   }
+  // the key rows of this wave's first tile, in flight with the candidate rows
+  TileDot<T, D> td;
+  auto issue_tile_keys = [&](int k0) {
+    const int jr = k0 + col < nk ? ktok[k0 + col] : -1;
+    td.issue_keys(jr >= 0 ? x.kf + (int64_t)jr * x.k_st : nullptr);
+  };
+  if (wave * kKeyTile < nk) issue_tile_keys(wave * kKeyTile);
+  if constexpr (MODE == 2) {
+    // candidate row r: piece p at position p ^ (r % (D / 8)), so that the 16
+    // lanes reading one piece of 16 rows hit different banks
+    constexpr int kPieces = D / 8;
+    constexpr int kDmaRows = 64 / kPieces;
+    for (int i0 = wave * kDmaRows; i0 < nc; i0 += 4 * kDmaRows) {
+      const int r = i0 + lane / kPieces;
+      const int rr = r < nc ? r : nc - 1;  // past the end: a real row, never read
+      const T* src = x.cand_row(0, ctok[rr], f == 0 ? cg[rr] : 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src + (((lane % kPieces) ^ (r % kPieces)) * 8)),
+          (__attribute__((address_space(3))) void*)(crow + i0 * D), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
   for (int k0 = wave * kKeyTile; k0 < nk; k0 += 4 * kKeyTile) {
+    if (k0 != wave * kKeyTile) issue_tile_keys(k0);
     const int klast = min(k0 + kKeyTile, nk) - 1;
     int c_lo, c_hi;
     if (STAGED) {
@@ -713,8 +776,8 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
     }
     int jrep, p;
     float c;
-    match_tile<T, D>(x, ktok, kbk, k0, nk, ctok, cbk, cg, c_lo, c_hi, gctok, gcg, coff, jrep, p,
-                     c);
+    match_tile<T, D, MODE == 2>(x, ktok, kbk, k0, nk, ctok, cbk, cg, c_lo, c_hi, gctok, gcg, coff,
+                                td, crow, jrep, p, c);
     if (lane < 16 && jrep >= 0) {
       const int q = k0 + lane;
       lp[q] = p;
@@ -774,7 +837,7 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
     const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
     const int32_t* __restrict__ frontier, float tau, MergeArgs a,
     fastar_diag_t* __restrict__ diag) {
-  extern __shared__ int32_t lds[];  // [3][Tf] proposals, then the staged lists
+  extern __shared__ int32_t lds[];  // match_lds_words<T, D>()
   const int h = blockIdx.y;
   const int f = blockIdx.z;
   const int nb = 1 << a.nbits;
@@ -805,10 +868,12 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
   x.e = match_err<T, D>();
   x.diag = diag;
   x.nk = p1 - p0;
-  if (p1 - p0 <= kStageKeys && c1 - c0 <= kStageCands)
-    match_group<T, D, true>(x, a, h, p0, p1, c0, c1, frontier, lds);
+  if (sizeof(T) == 2 && p1 - p0 <= kStageKeys && c1 - c0 <= kRowCands) {
+    if constexpr (sizeof(T) == 2) match_group<T, D, 2>(x, a, h, p0, p1, c0, c1, frontier, lds);
+  } else if (p1 - p0 <= kStageKeys && c1 - c0 <= kStageCands)
+    match_group<T, D, 1>(x, a, h, p0, p1, c0, c1, frontier, lds);
   else
-    match_group<T, D, false>(x, a, h, p0, p1, c0, c1, frontier, lds);
+    match_group<T, D, 0>(x, a, h, p0, p1, c0, c1, frontier, lds);
 }
 
 // Group rows, 16 lanes per chain (D/16 elements each).  A token that opens a
@@ -957,6 +1022,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   a.link = ws.link;
   a.ocnt = ws.ocnt;
   a.nextj = ws.nextj;
+  a.prop = ws.prop;
   {
     const size_t tc_lds = ((size_t)1 << c.n_bits) * sizeof(int32_t);
     if (ws.also_index) {
@@ -983,7 +1049,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   hipLaunchKernelGGL((tc_match_kernel<T, D>),
                      dim3((unsigned)((Tf + kKeysPerGroup - 1) / kKeysPerGroup), (unsigned)H, (unsigned)F),
                      dim3(256),
-                     ((size_t)3 * Tf + 2 * kStageKeys + 3 * kStageCands) * sizeof(int32_t), s,
+                     (match_lds_words<T, D>() * sizeof(int32_t)), s,
                      (const T*)c.rep_k,
                      (const T*)kn.data, kn.stride_head, kn.stride_token, c.frontier, tau, a, diag);
   hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)F * Tf + 15) / 16), (unsigned)H),
