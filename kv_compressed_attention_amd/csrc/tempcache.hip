@@ -909,8 +909,10 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   int before = 0;
   for (int i = lane; i < blk; i += FASTAR_WAVE) before += oc[i];
   const int bpos = blk * 64 + lane;
-  const bool opens = bpos < total && a.link[frame_off(a, h, 0) + bpos] < 0;
-  const uint64_t openers = ballot64(opens);
+  const int lk_b = bpos < total ? a.link[frame_off(a, h, 0) + bpos] : 0;
+  const uint64_t openers = ballot64(bpos < total && lk_b < 0);
+  // this lane group's token's link, from the block's (every lane is here)
+  const int lk = __shfl(lk_b, (int)(((int64_t)blockIdx.x * 16 + (threadIdx.x >> 4)) & 63), FASTAR_WAVE);
   before = wave_sum_dpp(before);
   if (blockIdx.x == 0 && threadIdx.x < FASTAR_WAVE) {
     // the new group count
@@ -925,12 +927,12 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   if (idx >= total) return;
   int f = (int)(idx / a.Tf);
   int j = (int)(idx - (int64_t)f * a.Tf);
+  if (lk >= 0 && f > 0) return;  // continuation of a chain that starts earlier
   const T* kh = knew + (int64_t)h * k_sh + sub * EPL;
   const T* vh = vnew + (int64_t)h * v_sh + sub * EPL;
   const int32_t* kbh = kbucket + (int64_t)h * a.kb_stride;
-  // everything the token itself needs, in flight together: its link, the
-  // group it may open, its successor, its value and key rows and its bucket
-  const int lk = a.link[frame_off(a, h, f) + j];
+  // everything the chain's first token needs, in flight together: its
+  // successor, its value and key rows and its bucket
   // meaningful when lk < 0
   const int64_t gd64 = (int64_t)ng0 + before +
                        __popcll(openers & ((1ull << (int)(idx - (int64_t)blk * 64)) - 1ull));
@@ -940,7 +942,6 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   Chunk<T, EPL>::load(vh + ((int64_t)f * a.Tf + j) * v_st, vv);
   Chunk<T, EPL>::load(kh + ((int64_t)f * a.Tf + j) * k_st, kk);
   int kb = kbh[(int64_t)f * a.Tf + j];
-  if (lk >= 0 && f > 0) return;  // continuation of a chain that starts earlier
   const int g = lk < 0 ? gd : lk;
   auto member = [&](int ff, int jj) {
     if (sub != 0) return;
