@@ -96,7 +96,8 @@ size_t merge_workspace(const fastar_cache_t* c, int n_frames) {
   const size_t nblk = (F * T + 63) / 64;
   return align_up(4 * H * (F + 1) * nb) + 2 * align_up(4 * H * (F + 1) * T) + align_up(4 * H * T) +
          align_up(4 * H * F * T) + align_up(4 * H * (nblk + 1)) + align_up(4 * H * F * T) +
-         align_up(12 * H * F * T) + align_up(16 * H * (size_t)c->capacity);
+         align_up(12 * H * F * T) + align_up(16 * H * F * ((T + 63) / 64)) +
+         align_up(16 * H * (size_t)c->capacity);
 }
 
 // everything fastar_tempcache_merge checks for a call with n_frames > 0 and
@@ -154,6 +155,7 @@ fastar::MergeWs merge_carve(const fastar_cache_t* c, int n_frames, void* ws) {
   mw.ocnt = take(4 * H * ((F * T + 63) / 64 + 1));
   mw.nextj = take(4 * H * F * T);
   mw.prop = take(12 * H * F * T);
+  mw.mrange = take(16 * H * F * ((T + 63) / 64));
   mw.index_ws = take(16 * H * (size_t)c->capacity);
   return mw;
 }

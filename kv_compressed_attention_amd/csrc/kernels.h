@@ -73,6 +73,7 @@ struct MergeWs {
   int32_t* ocnt;      // [H][ceil(n_frames T / 64) + 1]
   int32_t* nextj;     // [H][n_frames][T]
   int32_t* prop;      // [H][n_frames][3][T]
+  int32_t* mrange;    // [H][n_frames][ceil(T / 64)][4]
   int32_t* index_ws;  // bucket index scratch
   const IndexJob* also_index = nullptr;  // direct-index job for the first launch, or none
 };

@@ -136,8 +136,6 @@ struct Top2 {
 
 // keys are matched in tiles of this many (one wave each)
 constexpr int kKeyTile = 16;
-// sorted keys per match workgroup (before rounding to whole buckets)
-constexpr int kKeysPerGroup = 64;
 
 // Sorts up to 2048 tokens of one head by bucket (whole workgroup of 1024
 // threads).  get(i, b, g) gives token i's bucket and group (g < 0: left out).
@@ -201,6 +199,45 @@ __device__ void csr_build(int Tf, int nbits, Get get, int32_t* lds, int32_t* off
   }
 }
 
+// The bucket starts of up to 2048 tokens (whole workgroup of 1024
+// threads): st[b] = number of kept tokens with bucket < b, st[2^nbits] = all
+// kept; get(i, b, keep) as for csr_build.  Ends with a barrier.
+template <typename Get>
+__device__ void bucket_starts(int Tf, int nbits, Get get, int32_t* st) {
+  constexpr int kPer = 2;
+  __shared__ int wtot[16];
+  const int nb = 1 << nbits;
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  for (int s = tid; s <= nb; s += nthr) st[s] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid + u * nthr;
+    int b = 0, g = -1;
+    if (i < Tf) get(i, b, g);
+    if (g >= 0) atomicAdd(&st[b], 1);
+  }
+  __syncthreads();
+  const int per = (nb + nthr - 1) / nthr;
+  const int s0 = tid * per;
+  int local = 0;
+  for (int s = s0; s < s0 + per && s < nb; ++s) local += st[s];
+  const int lane = lane_id(), wave = tid >> 6;
+  const int incl = (int)wave_incl_scan_dpp((uint32_t)local);
+  if (lane == FASTAR_WAVE - 1) wtot[wave] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w = 0; w < wave; ++w) run += wtot[w];
+  for (int s = s0; s < s0 + per && s < nb; ++s) {
+    const int c = st[s];
+    st[s] = run;
+    run += c;
+  }
+  if (tid == nthr - 1) st[nb] = run;
+  __syncthreads();
+}
+
 struct MergeArgs {
   int H, Tf, cap, F, nbits;
   int64_t kb_stride;  // F * Tf
@@ -217,6 +254,7 @@ struct MergeArgs {
                       // the group count before the call
   int32_t* nextj;     // [H][F][Tf] token of frame f + 1 that extends this one, or -1
   int32_t* prop;      // [H][F][3][Tf] proposals of workgroups whose lists stay global
+  int32_t* mrange;    // [H][F][match workgroups][4] key positions [p0, p1), candidates [c0, c1)
 };
 
 __device__ __forceinline__ int64_t off_off(const MergeArgs& a, int h, int t) {
@@ -229,6 +267,9 @@ __device__ __forceinline__ int64_t frame_off(const MergeArgs& a, int h, int f) {
   return ((int64_t)h * a.F + f) * a.Tf;
 }
 __device__ __forceinline__ int ocnt_blocks(const MergeArgs& a) { return (a.F * a.Tf + 63) >> 6; }
+// sorted keys per match workgroup (before rounding to whole buckets)
+constexpr int kKeysPerGroup = 64;
+__host__ __device__ __forceinline__ int match_groups(int Tf) { return (Tf + kKeysPerGroup - 1) / kKeysPerGroup; }
 
 // Table 0 from the frontier (blockIdx.x == 0) or table f + 1 from new frame f.
 // One workgroup per (table, head).  Also clears new frame f's nextj links
@@ -276,6 +317,45 @@ __global__ __launch_bounds__(1024) void tc_index_kernel(
           g = 0;
         },
         lds, off, tok, tbk, nullptr);
+    // The match workgroups of frame f: key positions rounded to whole
+    // buckets, and the candidate range of their buckets, from the starts of
+    // table f (recounted here: the frontier's, or frame f - 1's, buckets)
+    const int nb = 1 << a.nbits;
+    int32_t* cst = lds + nb;  // [2^b + 1]
+    if (f == 0) {
+      const bool empty = n_groups[h] <= 0;
+      const int32_t* fr = frontier + (int64_t)h * a.Tf;
+      const int32_t* rb = rep_bucket + (int64_t)h * a.cap;
+      bucket_starts(a.Tf, a.nbits, [&](int i, int& b, int& g) {
+        g = empty ? -1 : fr[i];
+        b = g >= 0 ? rb[g] : 0;
+      }, cst);
+    } else {
+      const int32_t* kp = kb - a.Tf;
+      bucket_starts(a.Tf, a.nbits, [&](int i, int& b, int& g) {
+        b = kp[i];
+        g = 0;
+      }, cst);
+    }
+    // after csr_build's fill lds[b] is the end of bucket b; tbk is this
+    // workgroup's own output, visible after the barrier above
+    const int nkt = lds[nb - 1];
+    const int nwg = match_groups(a.Tf);
+    for (int wi = threadIdx.x; wi < nwg; wi += blockDim.x) {
+      int p0 = 0, p1 = 0, c0 = 0, c1 = 0;
+      const int a0 = wi * kKeysPerGroup;
+      if (a0 < nkt) {
+        const int a1 = min(a0 + kKeysPerGroup, nkt);
+        const int b0 = tbk[a0], b1 = tbk[a1 - 1];
+        const bool cut0 = a0 > 0 && tbk[a0 - 1] == b0;  // a0 inside a bucket owned before
+        const bool cut1 = a1 < nkt && tbk[a1] == b1;    // a1 inside a bucket owned here
+        p0 = cut0 ? lds[b0] : a0;
+        p1 = cut1 ? lds[b1] : a1;
+        c0 = cst[cut0 ? b0 + 1 : b0];
+        c1 = cst[b1 + 1];
+      }
+      reinterpret_cast<int4*>(a.mrange)[((int64_t)h * a.F + f) * nwg + wi] = make_int4(p0, p1, c0, c1);
+    }
   }
 }
 
@@ -840,24 +920,12 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
   extern __shared__ int32_t lds[];  // match_lds_words<T, D>()
   const int h = blockIdx.y;
   const int f = blockIdx.z;
-  const int nb = 1 << a.nbits;
-  const int32_t* koff = a.off + off_off(a, h, f + 1);
-  const int32_t* kbk = a.tbk + tok_off(a, h, f + 1);
-  const int32_t* coff = a.off + off_off(a, h, f);
   // the owned key positions [p0, p1) and the candidate range [c0, c1) of
-  // their buckets (it may also hold candidates of buckets without keys)
-  const int nkt = koff[nb];
-  const int a0 = blockIdx.x * kKeysPerGroup;
-  if (a0 >= nkt) return;
-  const int a1 = min(a0 + kKeysPerGroup, nkt);
-  const int b0 = kbk[a0], b1 = kbk[a1 - 1];
-  const bool cut0 = a0 > 0 && kbk[a0 - 1] == b0;  // a0 inside a bucket owned before
-  const bool cut1 = a1 < nkt && kbk[a1] == b1;    // a1 inside a bucket owned here
-  const int p0 = cut0 ? koff[b0 + 1] : a0;
-  const int p1 = cut1 ? koff[b1 + 1] : a1;
+  // their buckets (it may also hold candidates of buckets without keys),
+  // worked out by the index launch
+  const int4 r = reinterpret_cast<const int4*>(a.mrange)[((int64_t)h * a.F + f) * match_groups(a.Tf) + blockIdx.x];
+  const int p0 = r.x, p1 = r.y, c0 = r.z, c1 = r.w;
   if (p0 >= p1) return;  // the whole workgroup: no barrier is reached
-  const int c0 = coff[cut0 ? b0 + 1 : b0];
-  const int c1 = coff[b1 + 1];
   SegCtx<T, D> x;
   x.kf = knew + (int64_t)h * k_sh + (int64_t)f * a.Tf * k_st;
   x.kp = f > 0 ? x.kf - (int64_t)a.Tf * k_st : x.kf;
@@ -1024,8 +1092,9 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   a.ocnt = ws.ocnt;
   a.nextj = ws.nextj;
   a.prop = ws.prop;
+  a.mrange = ws.mrange;
   {
-    const size_t tc_lds = ((size_t)1 << c.n_bits) * sizeof(int32_t);
+    const size_t tc_lds = (((size_t)2 << c.n_bits) + 1) * sizeof(int32_t);
     if (ws.also_index) {
       const IndexJob& qj = *ws.also_index;
       int stage;
@@ -1048,7 +1117,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
     }
   }
   hipLaunchKernelGGL((tc_match_kernel<T, D>),
-                     dim3((unsigned)((Tf + kKeysPerGroup - 1) / kKeysPerGroup), (unsigned)H, (unsigned)F),
+                     dim3((unsigned)match_groups(Tf), (unsigned)H, (unsigned)F),
                      dim3(256),
                      (match_lds_words<T, D>() * sizeof(int32_t)), s,
                      (const T*)c.rep_k,
