@@ -67,6 +67,14 @@ template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (FASTAR_WAVE - 1); }
 
+// A workgroup barrier that orders LDS accesses only: global loads and stores
+// still in flight stay in flight (__syncthreads waits for them too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, FASTAR_WAVE); }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, FASTAR_WAVE); }
 

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kDirectWaves * FASTAR_WAVE) void bucket_index_direc
     const int32_t* __restrict__ bucket, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int stage) {
   extern __shared__ int4 lds4[];
-  direct_index_body<NBITS>(blockIdx.x, bucket, n, n_valid, offsets, perm, stage, lds4);
+  direct_index_body<NBITS>(blockIdx.y, blockIdx.x, gridDim.x, bucket, n, n_valid, offsets, perm, stage, lds4);
 }
 
 }  // namespace
@@ -304,8 +304,9 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
   if (heads == 0) return hipSuccess;
   if (direct_index_fits(n, n_probes, n_bits)) {
     int stage;
-    const size_t lds = direct_index_lds(n, n_bits, &stage);
-    const dim3 grid(heads), block(kDirectWaves * FASTAR_WAVE);
+    const int parts = direct_index_parts(n);
+    const size_t lds = direct_index_lds(n, n_bits, parts, &stage);
+    const dim3 grid(parts, heads), block(kDirectWaves * FASTAR_WAVE);
     switch (n_bits) {
 #define FASTAR_DIRECT(B)                                                                         \
   case B:                                                                                         \

@@ -274,8 +274,9 @@ __host__ __device__ __forceinline__ int match_groups(int Tf) { return (Tf + kKey
 // Table 0 from the frontier (blockIdx.x == 0) or table f + 1 from new frame f.
 // One workgroup per (table, head).  Also clears new frame f's nextj links
 // and (table 0) the head's opener counts, next to which it keeps the group
-// count before the call.  With QBITS > 0, workgroup (F + 1, h) instead builds
-// head h of the one-probe index job (QBITS bits), which needs none of this.
+// count before the call.  With QBITS > 0, workgroups (F + 1 + p, h) instead
+// build part p of head h of the one-probe index job (QBITS bits), which needs
+// none of this.
 template <int QBITS>
 __global__ __launch_bounds__(1024) void tc_index_kernel(
     const int32_t* __restrict__ frontier, const int32_t* __restrict__ rep_bucket,
@@ -284,8 +285,9 @@ __global__ __launch_bounds__(1024) void tc_index_kernel(
   extern __shared__ int4 lds_raw[];
   const int h = blockIdx.y;
   const int t = blockIdx.x;
-  if (QBITS > 0 && t == a.F + 1) {
-    direct_index_body<(QBITS > 0 ? QBITS : 3)>(h, qj.bucket, qj.n, nullptr, qj.offsets, qj.perm, qstage, lds_raw);
+  if (QBITS > 0 && t > a.F) {
+    direct_index_body<(QBITS > 0 ? QBITS : 3)>(h, t - (a.F + 1), gridDim.x - (a.F + 1), qj.bucket, qj.n,
+                                               nullptr, qj.offsets, qj.perm, qstage, lds_raw);
     return;
   }
   int32_t* lds = reinterpret_cast<int32_t*>(lds_raw);
@@ -1098,11 +1100,12 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
     if (ws.also_index) {
       const IndexJob& qj = *ws.also_index;
       int stage;
-      const size_t lds = std::max(tc_lds, direct_index_lds(qj.n, qj.n_bits, &stage));
+      const int parts = direct_index_parts(qj.n);
+      const size_t lds = std::max(tc_lds, direct_index_lds(qj.n, qj.n_bits, parts, &stage));
       switch (qj.n_bits) {
 #define FASTAR_TC_INDEX(B)                                                                              \
   case B:                                                                                              \
-    hipLaunchKernelGGL(tc_index_kernel<B>, dim3(F + 2, H), dim3(1024), lds, s, c.frontier, c.rep_bucket, \
+    hipLaunchKernelGGL(tc_index_kernel<B>, dim3(F + 1 + parts, H), dim3(1024), lds, s, c.frontier, c.rep_bucket, \
                        c.n_groups, kb, a, qj, stage);                                                  \
     break;
         FASTAR_TC_INDEX(3) FASTAR_TC_INDEX(4) FASTAR_TC_INDEX(5) FASTAR_TC_INDEX(6) FASTAR_TC_INDEX(7)

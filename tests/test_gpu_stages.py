@@ -140,7 +140,8 @@ def test_hash_strided_input(fa):
         assert np.array_equal(ids[h].cpu().numpy(), oracle.simhash(base[h, :, 64:192], planes, 1))
 
 
-@pytest.mark.parametrize("n,b,P", [(5000, 12, 1), (4096, 14, 2), (100, 3, 1), (0, 4, 1)])
+@pytest.mark.parametrize("n,b,P", [(5000, 12, 1), (4096, 14, 2), (100, 3, 1), (0, 4, 1), (65535, 12, 1),
+                                   (3100, 3, 1), (12289, 9, 1), (1537, 12, 1)])
 def test_bucket_index_of_given_ids(fa, n, b, P):
     rng = np.random.default_rng(n + b)
     H = 3
