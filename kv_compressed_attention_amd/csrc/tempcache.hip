@@ -137,88 +137,46 @@ struct Top2 {
 // keys are matched in tiles of this many (one wave each)
 constexpr int kKeyTile = 16;
 
-// Sorts up to 2048 tokens of one head by bucket (whole workgroup of 1024
-// threads).  get(i, b, g) gives token i's bucket and group (g < 0: left out).
-// Writes off[0 .. 2^nbits] (bucket starts, then the number kept), tok (the
-// kept tokens, bucket by bucket; within a bucket in no particular order), tbk
-// (their buckets) and, if candg is given, their groups.  lds holds 2^nbits
-// int32.
-template <typename Get>
-__device__ void csr_build(int Tf, int nbits, Get get, int32_t* lds, int32_t* off, int32_t* tok,
-                          int32_t* tbk, int32_t* candg) {
-  constexpr int kPer = 2;  // tokens per thread: Tf <= 2048
-  __shared__ int wtot[16];
-  const int nb = 1 << nbits;
-  const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
-  for (int s = tid; s < nb; s += nthr) lds[s] = 0;
-  int bb[kPer], gg[kPer];
+// The tokens of one table that a thread of a 1024-thread workgroup handles
+// (i = threadIdx.x + u * blockDim.x, u < kTabPer): bucket b[u] and group g[u]
+// (g < 0: left out).  Loads are unconditional, at an index clamped into the
+// table, so that all of them go out before the first wait.
+constexpr int kTabPer = 2;  // Tf <= 2048
+struct TabTok {
+  int b[kTabPer], g[kTabPer];
+};
+// new frame tokens (all kept), buckets kb[0 .. Tf)
+__device__ __forceinline__ TabTok tab_frame(const int32_t* kb, int Tf) {
+  TabTok r;
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = tid + u * nthr;
-    bb[u] = 0;
-    gg[u] = -1;
-    if (i < Tf) get(i, bb[u], gg[u]);
+  for (int u = 0; u < kTabPer; ++u) {
+    const int i = threadIdx.x + u * blockDim.x;
+    const int v = kb[i < Tf ? i : Tf - 1];
+    r.b[u] = v;
+    r.g[u] = i < Tf ? 0 : -1;
   }
-  __syncthreads();
+  return r;
+}
+// the frontier: token i belongs to group fr[i] (< 0: none), of bucket rb[g]
+__device__ __forceinline__ TabTok tab_frontier(const int32_t* fr, const int32_t* rb, bool empty, int Tf) {
+  TabTok r;
 #pragma unroll
-  for (int u = 0; u < kPer; ++u)
-    if (gg[u] >= 0) atomicAdd(&lds[bb[u]], 1);
-  __syncthreads();
-  // exclusive scan of the counts (per consecutive buckets per thread)
-  const int per = (nb + nthr - 1) / nthr;
-  const int s0 = tid * per;
-  int local = 0;
-  for (int s = s0; s < s0 + per && s < nb; ++s) local += lds[s];
-  const int lane = lane_id(), wave = tid >> 6;
-  int incl = local;
+  for (int u = 0; u < kTabPer; ++u) {
+    const int i = threadIdx.x + u * blockDim.x;
+    const int g = fr[i < Tf ? i : Tf - 1];
+    r.g[u] = empty || i >= Tf ? -1 : g;
+  }
 #pragma unroll
-  for (int o = 1; o < FASTAR_WAVE; o <<= 1) {
-    const int y = __shfl_up(incl, o, FASTAR_WAVE);
-    if (lane >= o) incl += y;
-  }
-  if (lane == FASTAR_WAVE - 1) wtot[wave] = incl;
-  __syncthreads();
-  int run = incl - local;
-  for (int w = 0; w < wave; ++w) run += wtot[w];
-  for (int s = s0; s < s0 + per && s < nb; ++s) {
-    const int c = lds[s];
-    off[s] = run;
-    lds[s] = run;  // the bucket's cursor for the fill below
-    run += c;
-  }
-  if (tid == nthr - 1) off[nb] = run;
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    if (gg[u] < 0) continue;
-    const int k = atomicAdd(&lds[bb[u]], 1);
-    tok[k] = tid + u * nthr;
-    tbk[k] = bb[u];
-    if (candg) candg[k] = gg[u];
-  }
+  for (int u = 0; u < kTabPer; ++u) r.b[u] = rb[r.g[u] >= 0 ? r.g[u] : 0];
+  return r;
 }
 
-// The bucket starts of up to 2048 tokens (whole workgroup of 1024
-// threads): st[b] = number of kept tokens with bucket < b, st[2^nbits] = all
-// kept; get(i, b, keep) as for csr_build.  Ends with a barrier.
-template <typename Get>
-__device__ void bucket_starts(int Tf, int nbits, Get get, int32_t* st) {
-  constexpr int kPer = 2;
+// Exclusive scan of st[0 .. nb) in place (whole workgroup), st[nb] = total.
+// Ends with a barrier.
+__device__ void scan_buckets(int nb, int32_t* st, int32_t* copy) {
   __shared__ int wtot[16];
-  const int nb = 1 << nbits;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  for (int s = tid; s <= nb; s += nthr) st[s] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < kPer; ++u) {
-    const int i = tid + u * nthr;
-    int b = 0, g = -1;
-    if (i < Tf) get(i, b, g);
-    if (g >= 0) atomicAdd(&st[b], 1);
-  }
-  __syncthreads();
   const int per = (nb + nthr - 1) / nthr;
   const int s0 = tid * per;
   int local = 0;
@@ -226,17 +184,67 @@ __device__ void bucket_starts(int Tf, int nbits, Get get, int32_t* st) {
   const int lane = lane_id(), wave = tid >> 6;
   const int incl = (int)wave_incl_scan_dpp((uint32_t)local);
   if (lane == FASTAR_WAVE - 1) wtot[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   int run = incl - local;
   for (int w = 0; w < wave; ++w) run += wtot[w];
   for (int s = s0; s < s0 + per && s < nb; ++s) {
     const int c = st[s];
+    if (copy) copy[s] = run;
     st[s] = run;
     run += c;
   }
-  if (tid == nthr - 1) st[nb] = run;
-  __syncthreads();
+  if (tid == nthr - 1) {
+    if (copy) copy[nb] = run;
+    st[nb] = run;
+  }
+  lds_barrier();
 }
+
+// Sorts the tokens of one table (up to 2048, whole workgroup of 1024
+// threads) by bucket.  Writes off[0 .. 2^nbits] (bucket starts, then the
+// number kept), tok (the kept tokens, bucket by bucket; within a bucket in no
+// particular order), tbk (their buckets), if given, a copy of tbk in LDS
+// (ltbk) and their groups (candg).  lds holds 2^nbits + 1 int32; after the
+// call (and a barrier) lds[b] is the end of bucket b.
+__device__ void csr_build(int nbits, const TabTok& tt, int32_t* lds, int32_t* off, int32_t* tok,
+                          int32_t* tbk, int32_t* ltbk, int32_t* candg) {
+  const int nb = 1 << nbits;
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  for (int s = tid; s <= nb; s += nthr) lds[s] = 0;
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < kTabPer; ++u)
+    if (tt.g[u] >= 0) atomicAdd(&lds[tt.b[u]], 1);
+  lds_barrier();
+  // the bucket starts, to off and as the cursors of the fill below
+  scan_buckets(nb, lds, off);
+#pragma unroll
+  for (int u = 0; u < kTabPer; ++u) {
+    if (tt.g[u] < 0) continue;
+    const int k = atomicAdd(&lds[tt.b[u]], 1);
+    tok[k] = tid + u * nthr;
+    tbk[k] = tt.b[u];
+    if (ltbk) ltbk[k] = tt.b[u];
+    if (candg) candg[k] = tt.g[u];
+  }
+}
+
+// The bucket starts of one table (whole workgroup): st[b] = number of kept
+// tokens with bucket < b, st[2^nbits] = all kept.  Ends with a barrier.
+__device__ void bucket_starts(int nbits, const TabTok& tt, int32_t* st) {
+  const int nb = 1 << nbits;
+  for (int s = threadIdx.x; s <= nb; s += blockDim.x) st[s] = 0;
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < kTabPer; ++u)
+    if (tt.g[u] >= 0) atomicAdd(&st[tt.b[u]], 1);
+  lds_barrier();
+  scan_buckets(nb, st, nullptr);
+}
+
+// dynamic LDS the index launch may take
+constexpr size_t kTcIndexLds = 152 * 1024;
 
 struct MergeArgs {
   int H, Tf, cap, F, nbits;
@@ -294,70 +302,53 @@ __global__ __launch_bounds__(1024) void tc_index_kernel(
   int32_t* off = a.off + off_off(a, h, t);
   int32_t* tok = a.tok + tok_off(a, h, t);
   int32_t* tbk = a.tbk + tok_off(a, h, t);
+  const int nb = 1 << a.nbits;
+  const bool empty = n_groups[h] <= 0;
+  const int32_t* fr = frontier + (int64_t)h * a.Tf;
+  const int32_t* rb = rep_bucket + (int64_t)h * a.cap;
   if (t == 0) {
+    const TabTok tt = tab_frontier(fr, rb, empty, a.Tf);
     const int nblk = ocnt_blocks(a);
     int32_t* oc = a.ocnt + (int64_t)h * (nblk + 1);
     for (int i = threadIdx.x; i <= nblk; i += blockDim.x) oc[i] = i < nblk ? 0 : n_groups[h];
-    const bool empty = n_groups[h] <= 0;
-    const int32_t* fr = frontier + (int64_t)h * a.Tf;
-    const int32_t* rb = rep_bucket + (int64_t)h * a.cap;
-    csr_build(
-        a.Tf, a.nbits,
-        [&](int i, int& b, int& g) {
-          g = empty ? -1 : fr[i];
-          b = g >= 0 ? rb[g] : 0;
-        },
-        lds, off, tok, tbk, a.candg + (int64_t)h * a.Tf);
-  } else {
-    const int f = t - 1;
-    const int32_t* kb = kbucket + (int64_t)h * a.kb_stride + (int64_t)f * a.Tf;
-    for (int i = threadIdx.x; i < a.Tf; i += blockDim.x) a.nextj[frame_off(a, h, f) + i] = -1;
-    csr_build(
-        a.Tf, a.nbits,
-        [&](int i, int& b, int& g) {
-          b = kb[i];
-          g = 0;
-        },
-        lds, off, tok, tbk, nullptr);
-    // The match workgroups of frame f: key positions rounded to whole
-    // buckets, and the candidate range of their buckets, from the starts of
-    // table f (recounted here: the frontier's, or frame f - 1's, buckets)
-    const int nb = 1 << a.nbits;
-    int32_t* cst = lds + nb;  // [2^b + 1]
-    if (f == 0) {
-      const bool empty = n_groups[h] <= 0;
-      const int32_t* fr = frontier + (int64_t)h * a.Tf;
-      const int32_t* rb = rep_bucket + (int64_t)h * a.cap;
-      bucket_starts(a.Tf, a.nbits, [&](int i, int& b, int& g) {
-        g = empty ? -1 : fr[i];
-        b = g >= 0 ? rb[g] : 0;
-      }, cst);
-    } else {
-      const int32_t* kp = kb - a.Tf;
-      bucket_starts(a.Tf, a.nbits, [&](int i, int& b, int& g) {
-        b = kp[i];
-        g = 0;
-      }, cst);
+    csr_build(a.nbits, tt, lds, off, tok, tbk, nullptr, a.candg + (int64_t)h * a.Tf);
+    return;
+  }
+  const int f = t - 1;
+  const int32_t* kb = kbucket + (int64_t)h * a.kb_stride + (int64_t)f * a.Tf;
+  // this frame's buckets, and those of table f (the frontier's, or frame
+  // f - 1's), whose starts give the match workgroups' candidate ranges
+  const TabTok tt = tab_frame(kb, a.Tf);
+  for (int i = threadIdx.x; i < a.Tf; i += blockDim.x) a.nextj[frame_off(a, h, f) + i] = -1;
+  if (!a.mrange) {  // the match workgroups find their ranges themselves
+    csr_build(a.nbits, tt, lds, off, tok, tbk, nullptr, nullptr);
+    return;
+  }
+  const TabTok tc = f == 0 ? tab_frontier(fr, rb, empty, a.Tf) : tab_frame(kb - a.Tf, a.Tf);
+  // lds: [2^b + 1] cursors, [2^b + 1] starts of table f, [Tf] buckets of the
+  // sorted keys
+  int32_t* cst = lds + nb + 1;
+  int32_t* ltbk = cst + nb + 1;
+  csr_build(a.nbits, tt, lds, off, tok, tbk, ltbk, nullptr);
+  bucket_starts(a.nbits, tc, cst);
+  // The match workgroups of frame f: key positions rounded to whole buckets,
+  // and the candidate range of their buckets.  lds[b] is the end of bucket b.
+  const int nkt = lds[nb - 1];
+  const int nwg = match_groups(a.Tf);
+  for (int wi = threadIdx.x; wi < nwg; wi += blockDim.x) {
+    int p0 = 0, p1 = 0, c0 = 0, c1 = 0;
+    const int a0 = wi * kKeysPerGroup;
+    if (a0 < nkt) {
+      const int a1 = min(a0 + kKeysPerGroup, nkt);
+      const int b0 = ltbk[a0], b1 = ltbk[a1 - 1];
+      const bool cut0 = a0 > 0 && ltbk[a0 - 1] == b0;  // a0 inside a bucket owned before
+      const bool cut1 = a1 < nkt && ltbk[a1] == b1;    // a1 inside a bucket owned here
+      p0 = cut0 ? lds[b0] : a0;
+      p1 = cut1 ? lds[b1] : a1;
+      c0 = cst[cut0 ? b0 + 1 : b0];
+      c1 = cst[b1 + 1];
     }
-    // after csr_build's fill lds[b] is the end of bucket b; tbk is this
-    // workgroup's own output, visible after the barrier above
-    const int nkt = lds[nb - 1];
-    const int nwg = match_groups(a.Tf);
-    for (int wi = threadIdx.x; wi < nwg; wi += blockDim.x) {
-      int p0 = 0, p1 = 0, c0 = 0, c1 = 0;
-      const int a0 = wi * kKeysPerGroup;
-      if (a0 < nkt) {
-        const int a1 = min(a0 + kKeysPerGroup, nkt);
-        const int b0 = tbk[a0], b1 = tbk[a1 - 1];
-        const bool cut0 = a0 > 0 && tbk[a0 - 1] == b0;  // a0 inside a bucket owned before
-        const bool cut1 = a1 < nkt && tbk[a1] == b1;    // a1 inside a bucket owned here
-        p0 = cut0 ? lds[b0] : a0;
-        p1 = cut1 ? lds[b1] : a1;
-        c0 = cst[cut0 ? b0 + 1 : b0];
-        c1 = cst[b1 + 1];
-      }
-      reinterpret_cast<int4*>(a.mrange)[((int64_t)h * a.F + f) * nwg + wi] = make_int4(p0, p1, c0, c1);
-    }
+    reinterpret_cast<int4*>(a.mrange)[((int64_t)h * a.F + f) * nwg + wi] = make_int4(p0, p1, c0, c1);
   }
 }
 
@@ -924,9 +915,28 @@ __global__ __launch_bounds__(256) void tc_match_kernel(
   const int f = blockIdx.z;
   // the owned key positions [p0, p1) and the candidate range [c0, c1) of
   // their buckets (it may also hold candidates of buckets without keys),
-  // worked out by the index launch
-  const int4 r = reinterpret_cast<const int4*>(a.mrange)[((int64_t)h * a.F + f) * match_groups(a.Tf) + blockIdx.x];
-  const int p0 = r.x, p1 = r.y, c0 = r.z, c1 = r.w;
+  // worked out by the index launch, or else here
+  int p0, p1, c0, c1;
+  if (a.mrange) {
+    const int4 r = reinterpret_cast<const int4*>(a.mrange)[((int64_t)h * a.F + f) * match_groups(a.Tf) + blockIdx.x];
+    p0 = r.x, p1 = r.y, c0 = r.z, c1 = r.w;
+  } else {
+    const int nb = 1 << a.nbits;
+    const int32_t* koff = a.off + off_off(a, h, f + 1);
+    const int32_t* kbk = a.tbk + tok_off(a, h, f + 1);
+    const int32_t* coff = a.off + off_off(a, h, f);
+    const int nkt = koff[nb];
+    const int a0 = blockIdx.x * kKeysPerGroup;
+    if (a0 >= nkt) return;
+    const int a1 = min(a0 + kKeysPerGroup, nkt);
+    const int b0 = kbk[a0], b1 = kbk[a1 - 1];
+    const bool cut0 = a0 > 0 && kbk[a0 - 1] == b0;  // a0 inside a bucket owned before
+    const bool cut1 = a1 < nkt && kbk[a1] == b1;    // a1 inside a bucket owned here
+    p0 = cut0 ? koff[b0 + 1] : a0;
+    p1 = cut1 ? koff[b1 + 1] : a1;
+    c0 = coff[cut0 ? b0 + 1 : b0];
+    c1 = coff[b1 + 1];
+  }
   if (p0 >= p1) return;  // the whole workgroup: no barrier is reached
   SegCtx<T, D> x;
   x.kf = knew + (int64_t)h * k_sh + (int64_t)f * a.Tf * k_st;
@@ -1094,9 +1104,13 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   a.ocnt = ws.ocnt;
   a.nextj = ws.nextj;
   a.prop = ws.prop;
-  a.mrange = ws.mrange;
   {
-    const size_t tc_lds = (((size_t)2 << c.n_bits) + 1) * sizeof(int32_t);
+    // the index launch works out the match ranges when its LDS allows
+    const size_t nb1 = ((size_t)1 << c.n_bits) + 1;
+    const size_t full_lds = (nb1 * 2 + (size_t)Tf) * sizeof(int32_t);
+    const bool ranges = full_lds <= kTcIndexLds;
+    a.mrange = ranges ? ws.mrange : nullptr;
+    const size_t tc_lds = ranges ? full_lds : nb1 * sizeof(int32_t);
     if (ws.also_index) {
       const IndexJob& qj = *ws.also_index;
       int stage;

@@ -302,6 +302,8 @@ MERGE_CASES = [
     ("bf16", 2, 5, 300, 128, 8, 0.999, 2),
     ("bf16", 2, 4, 200, 128, 0, 0.99, 4),
     ("bf16", 1, 3, 700, 64, 10, 0.5, 3),
+    # 14 bits: the match workgroups find their own ranges
+    ("bf16", 2, 3, 300, 64, 14, 0.9, 3),
 ]
 
 
