@@ -186,7 +186,7 @@ __device__ void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t* __res
 // tensor i are numbered from jobs.tile_end[i - 1]); the first tile's rows
 // are requested before the hyperplanes are read.
 template <int D>
-__global__ __launch_bounds__(256) void hash_bf16_kernel(HashJobs jobs, const uint16_t* __restrict__ planes,
+__global__ __launch_bounds__(256, 4) void hash_bf16_kernel(HashJobs jobs, const uint16_t* __restrict__ planes,
                                                         int nb, fastar_diag_t* __restrict__ diag) {
   constexpr int NC = D / 32;
   constexpr int kPst = D + 8;  // padded hyperplane rows: lanes reading 16 planes hit different banks
