@@ -204,15 +204,24 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       const int pa = __popcll(ballot64(is_pass && pre <= j0)) - 1;
       const int pb = __popcll(ballot64(is_pass && pre <= j1)) - 1;
       const int base_a = __builtin_amdgcn_readlane(kb_pre, pa);
+      int j[kDmaPerWave + 1], base[kDmaPerWave + 1];
 #pragma unroll
       for (int i = 0; i <= kDmaPerWave; ++i) {
         const int row = i < kDmaPerWave ? (wave * kDmaPerWave + i) * kDmaRows + l / kPieces
                                         : 8 * wave + (l & 7);
-        const int j = min(j0 + row, total - 1);  // past the end: a loaded, unused key
-        int base = base_a;
-        for (int p = pa + 1; p <= pb; ++p)
-          base = __builtin_amdgcn_readlane(pre, p) <= j ? __builtin_amdgcn_readlane(kb_pre, p) : base;
-        const int kk = j + base;
+        j[i] = min(j0 + row, total - 1);  // past the end: a loaded, unused key
+        base[i] = base_a;
+      }
+      // one walk over the passes for all of the lane's keys (selects, no branches)
+      for (int p = pa + 1; p <= pb; ++p) {
+        const int pre_p = __builtin_amdgcn_readlane(pre, p);
+        const int kb_p = __builtin_amdgcn_readlane(kb_pre, p);
+#pragma unroll
+        for (int i = 0; i <= kDmaPerWave; ++i) base[i] = pre_p <= j[i] ? kb_p : base[i];
+      }
+#pragma unroll
+      for (int i = 0; i <= kDmaPerWave; ++i) {
+        const int kk = j[i] + base[i];
         key[i] = (MODE == 2) ? kk : idx_h[kk];
       }
     };
