@@ -403,7 +403,7 @@ fastar_tensor_t cache_rows(const fastar_cache_t* c, void* data) {
   return t;
 }
 size_t chunk_index_ws(const fastar_chunk_t* a) {
-  // the queries' index outside the merge's first launch needs scratch
+  // the queries' index in a launch of its own needs scratch
   if (fastar::direct_index_supported(a->q->tokens, a->n_probes, a->n_bits)) return 0;
   return align_up(16 * (size_t)a->q->heads * (size_t)a->q->tokens);
 }
@@ -471,7 +471,10 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
     return st;
   fastar::MergeWs mw = merge_carve(c, a->n_frames, ws);
   fastar::IndexJob qj{a->q_bucket, a->q->tokens, a->n_bits, a->q_offsets, a->q_perm};
-  const bool fused = chunk_index_ws(a) == 0 && a->q->tokens > 0;
+  // the queries' index rides along with the representatives' when both are
+  // built by the single counting pass
+  const bool fused = chunk_index_ws(a) == 0 && a->q->tokens > 0 &&
+                     fastar::direct_index_supported(c->capacity, 1, c->n_bits);
   if (fused) mw.also_index = &qj;
   if ((st = hip_status(fastar::launch_tempcache_merge(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,
                                                       a->tau, a->group_of_new, a->rep_offsets,

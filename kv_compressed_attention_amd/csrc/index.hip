@@ -18,6 +18,8 @@
 // probe with at most 12 bits takes a single counting pass instead (below).
 
 #include "common.h"
+#include <algorithm>
+
 #include "index_direct.h"
 #include "kernels.h"
 
@@ -284,12 +286,21 @@ __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
   write_offsets(off, nbk, nh, shift0, [&](int64_t p) { return kfinal[p]; }, &cnt[0][0]);
 }
 
+// One workgroup per part and head; the last xparts columns build the extra
+// job's index.
 template <int NBITS>
 __global__ __launch_bounds__(kDirectWaves * FASTAR_WAVE) void bucket_index_direct_kernel(
     const int32_t* __restrict__ bucket, int64_t n, const int32_t* __restrict__ n_valid,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int stage) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int stage, IndexJob xj, int xparts,
+    int xstage) {
   extern __shared__ int4 lds4[];
-  direct_index_body<NBITS>(blockIdx.y, blockIdx.x, gridDim.x, bucket, n, n_valid, offsets, perm, stage, lds4);
+  const int nparts = (int)gridDim.x - xparts;
+  if ((int)blockIdx.x >= nparts) {
+    direct_index_body<NBITS>(blockIdx.y, blockIdx.x - nparts, xparts, xj.bucket, xj.n, nullptr, xj.offsets,
+                             xj.perm, xstage, lds4);
+    return;
+  }
+  direct_index_body<NBITS>(blockIdx.y, blockIdx.x, nparts, bucket, n, n_valid, offsets, perm, stage, lds4);
 }
 
 }  // namespace
@@ -300,18 +311,25 @@ bool direct_index_supported(int64_t n, int n_probes, int n_bits) {
 
 hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int n_probes,
                                int n_bits, const int32_t* n_valid, int32_t* offsets,
-                               int32_t* perm, int32_t* ws, hipStream_t s) {
+                               int32_t* perm, int32_t* ws, hipStream_t s, const IndexJob* extra) {
   if (heads == 0) return hipSuccess;
+  const bool with_x = extra && extra->n > 0;
+  if (with_x && (!direct_index_fits(n, n_probes, n_bits) || !direct_index_fits(extra->n, 1, extra->n_bits) ||
+                 extra->n_bits != n_bits))
+    return hipErrorInvalidValue;
   if (direct_index_fits(n, n_probes, n_bits)) {
-    int stage;
+    int stage, xstage = 0;
     const int parts = direct_index_parts(n);
-    const size_t lds = direct_index_lds(n, n_bits, parts, &stage);
-    const dim3 grid(parts, heads), block(kDirectWaves * FASTAR_WAVE);
+    size_t lds = direct_index_lds(n, n_bits, parts, &stage);
+    const int xparts = with_x ? direct_index_parts(extra->n) : 0;
+    if (with_x) lds = std::max(lds, direct_index_lds(extra->n, n_bits, xparts, &xstage));
+    const IndexJob xj = with_x ? *extra : IndexJob{nullptr, 0, n_bits, nullptr, nullptr};
+    const dim3 grid(parts + xparts, heads), block(kDirectWaves * FASTAR_WAVE);
     switch (n_bits) {
 #define FASTAR_DIRECT(B)                                                                         \
   case B:                                                                                         \
     hipLaunchKernelGGL(bucket_index_direct_kernel<B>, grid, block, lds, s, bucket, n, n_valid,    \
-                       offsets, perm, stage);                                                     \
+                       offsets, perm, stage, xj, xparts, xstage);                                 \
     break;
       FASTAR_DIRECT(3) FASTAR_DIRECT(4) FASTAR_DIRECT(5) FASTAR_DIRECT(6) FASTAR_DIRECT(7)
       FASTAR_DIRECT(8) FASTAR_DIRECT(9) FASTAR_DIRECT(10) FASTAR_DIRECT(11) FASTAR_DIRECT(12)

@@ -28,12 +28,25 @@ hipError_t launch_hash_multi(HashJobs jobs, int dim, int dtype, const void* plan
                              fastar_diag_t* diag, hipStream_t s);
 
 // index.hip -----------------------------------------------------------------
+// a one-probe bucket index (n items per head) that another index launch of
+// the same heads and bits builds in extra workgroups (the chunk sequence's
+// queries, next to the representatives)
+struct IndexJob {
+  const int32_t* bucket;
+  int64_t n;
+  int n_bits;
+  int32_t* offsets;
+  int32_t* perm;
+};
+// With extra (the single counting pass only, which must apply to both), the
+// launch also builds that index.
 hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int n_probes,
                                int n_bits, const int32_t* n_valid, int32_t* offsets,
-                               int32_t* perm, int32_t* ws, hipStream_t s);
+                               int32_t* perm, int32_t* ws, hipStream_t s,
+                               const IndexJob* extra = nullptr);
 
-// whether launch_bucket_index uses the single counting pass (which the
-// merge's first launch can also run, IndexJob)
+// whether launch_bucket_index uses the single counting pass (which another
+// such launch can also run, IndexJob)
 bool direct_index_supported(int64_t n, int n_probes, int n_bits);
 
 // prune.hip -----------------------------------------------------------------
@@ -55,15 +68,6 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 // tempcache.hip -------------------------------------------------------------
-// a one-probe bucket index built by extra workgroups of the merge's first
-// launch (the chunk sequence's queries), n items per head, cache's heads
-struct IndexJob {
-  const int32_t* bucket;
-  int64_t n;
-  int n_bits;
-  int32_t* offsets;
-  int32_t* perm;
-};
 struct MergeWs {
   int32_t* off;       // [H][n_frames+1][2^b+1] bucket offsets per table (see tempcache.hip)
   int32_t* tok;       // [H][n_frames+1][T] tokens sorted by bucket
@@ -75,7 +79,7 @@ struct MergeWs {
   int32_t* prop;      // [H][n_frames][3][T]
   int32_t* mrange;    // [H][n_frames][ceil(T / 64)][4]
   int32_t* index_ws;  // bucket index scratch
-  const IndexJob* also_index = nullptr;  // direct-index job for the first launch, or none
+  const IndexJob* also_index = nullptr;  // direct-index job for the representatives' index launch, or none
 };
 hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
                                   const fastar_tensor_t& v_new, const int32_t* k_new_bucket,

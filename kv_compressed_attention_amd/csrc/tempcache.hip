@@ -33,7 +33,6 @@
 #include <algorithm>
 
 #include "common.h"
-#include "index_direct.h"
 #include "kernels.h"
 
 namespace fastar {
@@ -282,22 +281,13 @@ __host__ __device__ __forceinline__ int match_groups(int Tf) { return (Tf + kKey
 // Table 0 from the frontier (blockIdx.x == 0) or table f + 1 from new frame f.
 // One workgroup per (table, head).  Also clears new frame f's nextj links
 // and (table 0) the head's opener counts, next to which it keeps the group
-// count before the call.  With QBITS > 0, workgroups (F + 1 + p, h) instead
-// build part p of head h of the one-probe index job (QBITS bits), which needs
-// none of this.
-template <int QBITS>
+// count before the call.
 __global__ __launch_bounds__(1024) void tc_index_kernel(
     const int32_t* __restrict__ frontier, const int32_t* __restrict__ rep_bucket,
-    const int32_t* __restrict__ n_groups, const int32_t* __restrict__ kbucket, MergeArgs a,
-    IndexJob qj, int qstage) {
+    const int32_t* __restrict__ n_groups, const int32_t* __restrict__ kbucket, MergeArgs a) {
   extern __shared__ int4 lds_raw[];
   const int h = blockIdx.y;
   const int t = blockIdx.x;
-  if (QBITS > 0 && t > a.F) {
-    direct_index_body<(QBITS > 0 ? QBITS : 3)>(h, t - (a.F + 1), gridDim.x - (a.F + 1), qj.bucket, qj.n,
-                                               nullptr, qj.offsets, qj.perm, qstage, lds_raw);
-    return;
-  }
   int32_t* lds = reinterpret_cast<int32_t*>(lds_raw);
   int32_t* off = a.off + off_off(a, h, t);
   int32_t* tok = a.tok + tok_off(a, h, t);
@@ -1111,27 +1101,8 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
     const bool ranges = full_lds <= kTcIndexLds;
     a.mrange = ranges ? ws.mrange : nullptr;
     const size_t tc_lds = ranges ? full_lds : nb1 * sizeof(int32_t);
-    if (ws.also_index) {
-      const IndexJob& qj = *ws.also_index;
-      int stage;
-      const int parts = direct_index_parts(qj.n);
-      const size_t lds = std::max(tc_lds, direct_index_lds(qj.n, qj.n_bits, parts, &stage));
-      switch (qj.n_bits) {
-#define FASTAR_TC_INDEX(B)                                                                              \
-  case B:                                                                                              \
-    hipLaunchKernelGGL(tc_index_kernel<B>, dim3(F + 1 + parts, H), dim3(1024), lds, s, c.frontier, c.rep_bucket, \
-                       c.n_groups, kb, a, qj, stage);                                                  \
-    break;
-        FASTAR_TC_INDEX(3) FASTAR_TC_INDEX(4) FASTAR_TC_INDEX(5) FASTAR_TC_INDEX(6) FASTAR_TC_INDEX(7)
-        FASTAR_TC_INDEX(8) FASTAR_TC_INDEX(9) FASTAR_TC_INDEX(10) FASTAR_TC_INDEX(11) FASTAR_TC_INDEX(12)
-#undef FASTAR_TC_INDEX
-        default:
-          return hipErrorInvalidValue;
-      }
-    } else {
-      hipLaunchKernelGGL(tc_index_kernel<0>, dim3(F + 1, H), dim3(1024), tc_lds, s, c.frontier,
-                         c.rep_bucket, c.n_groups, kb, a, IndexJob{}, 0);
-    }
+    hipLaunchKernelGGL(tc_index_kernel, dim3(F + 1, H), dim3(1024), tc_lds, s, c.frontier, c.rep_bucket,
+                       c.n_groups, kb, a);
   }
   hipLaunchKernelGGL((tc_match_kernel<T, D>),
                      dim3((unsigned)match_groups(Tf), (unsigned)H, (unsigned)F),
@@ -1148,7 +1119,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   if (e != hipSuccess) return e;
   if (rep_offsets && rep_perm)
     return launch_bucket_index(c.rep_bucket, H, c.capacity, 1, c.n_bits, c.n_groups, rep_offsets,
-                               rep_perm, ws.index_ws, s);
+                               rep_perm, ws.index_ws, s, ws.also_index);
   return hipSuccess;
 }
 
