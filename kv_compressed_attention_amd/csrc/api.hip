@@ -465,11 +465,27 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   if (!ws || ws_bytes < need)
     return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need, ws_bytes);
 
-  // launches, in order on the stream
+  // launches, in order on the stream.  bf16 queries are hashed by extra
+  // workgroups of the merge's match launch (only their index, after the
+  // merge, and the attention need them); the keys first, on their own.
+  fastar::MergeWs mw = merge_carve(c, a->n_frames, ws);
+  fastar::HashJobs qjobs;
+  qjobs.count = 0;
+  if (a->q->dtype == FASTAR_BF16 && c->dtype == FASTAR_BF16 && a->q->dim == c->dim && c->heads > 0 &&
+      (int64_t)a->q->heads * a->q->tokens > 0) {
+    qjobs.count = 1;
+    qjobs.j[0] = jobs.j[0];
+    for (int i = 1; i < jobs.count; ++i) jobs.j[i - 1] = jobs.j[i];
+    --jobs.count;
+    mw.also_hash = &qjobs;
+    mw.hash_planes = a->planes;
+    mw.hash_bits = a->n_bits;
+  }
+  any = false;
+  for (int i = 0; i < jobs.count; ++i) any = any || (int64_t)jobs.j[i].H * jobs.j[i].N > 0;
   if (any && (st = hip_status(fastar::launch_hash_multi(jobs, a->q->dim, a->q->dtype, a->planes, a->n_bits,
                                                        diag, stream), "hash")) != FASTAR_OK)
     return st;
-  fastar::MergeWs mw = merge_carve(c, a->n_frames, ws);
   fastar::IndexJob qj{a->q_bucket, a->q->tokens, a->n_bits, a->q_offsets, a->q_perm};
   // the queries' index rides along with the representatives' when both are
   // built by the single counting pass

@@ -33,6 +33,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "hash_body.h"
 #include "kernels.h"
 
 namespace fastar {
@@ -244,6 +245,10 @@ __device__ void bucket_starts(int nbits, const TabTok& tt, int32_t* st) {
 
 // dynamic LDS the index launch may take
 constexpr size_t kTcIndexLds = 152 * 1024;
+// hashing that rides along with the match launch: tiles per wave, and at most
+// this many planes of the match grid
+constexpr int kMatchHashTiles = 2;
+constexpr int kMatchHashPlanes = 2;
 
 struct MergeArgs {
   int H, Tf, cap, F, nbits;
@@ -895,14 +900,27 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
   }
 }
 
+// The workgroups of the planes past the frames (blockIdx.z >= F, dispatched
+// last; bf16 only) hash the jobs qh instead: flat index ((z - F) * gridDim.y
+// + y) * gridDim.x + x < qblocks is hashing block that index.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void tc_match_kernel(
+__global__ __launch_bounds__(256, 4) void tc_match_kernel(
     const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
     const int32_t* __restrict__ frontier, float tau, MergeArgs a,
-    fastar_diag_t* __restrict__ diag) {
+    fastar_diag_t* __restrict__ diag, HashJobs qh, const uint16_t* __restrict__ qplanes, int qnb,
+    int qblocks) {
   extern __shared__ int32_t lds[];  // match_lds_words<T, D>()
   const int h = blockIdx.y;
   const int f = blockIdx.z;
+  if (f >= a.F) {
+    if constexpr (sizeof(T) == 2) {
+      static_assert(hash_bf16_lds<D>() <= match_lds_words<T, D>() * sizeof(int32_t), "hashing fits the LDS");
+      const int qb = (int)(((blockIdx.z - a.F) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x);
+      if (qb < qblocks)
+        hash_bf16_body<D>(qh, qplanes, qnb, diag, qb, qblocks, reinterpret_cast<char*>(lds));
+    }
+    return;  // the whole workgroup
+  }
   // the owned key positions [p0, p1) and the candidate range [c0, c1) of
   // their buckets (it may also hold candidates of buckets without keys),
   // worked out by the index launch, or else here
@@ -1104,12 +1122,26 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
     hipLaunchKernelGGL(tc_index_kernel, dim3(F + 1, H), dim3(1024), tc_lds, s, c.frontier, c.rep_bucket,
                        c.n_groups, kb, a);
   }
+  // extra workgroups (planes after the frames', dispatched last) hash the
+  // jobs that come with the merge: about kMatchHashTiles tiles per wave, at
+  // most kMatchHashPlanes planes
+  HashJobs qh;
+  qh.count = 0;
+  int qblocks = 0, qz = 0;
+  if (ws.also_hash && sizeof(T) == 2) {
+    const int64_t tiles = hash_tiles(*ws.also_hash, &qh);
+    const int64_t plane = (int64_t)match_groups(Tf) * H;
+    const int64_t want = (tiles + 4 * kMatchHashTiles - 1) / (4 * kMatchHashTiles);
+    qblocks = (int)(want < kMatchHashPlanes * plane ? want : kMatchHashPlanes * plane);
+    qz = (int)((qblocks + plane - 1) / plane);
+  }
   hipLaunchKernelGGL((tc_match_kernel<T, D>),
-                     dim3((unsigned)match_groups(Tf), (unsigned)H, (unsigned)F),
+                     dim3((unsigned)match_groups(Tf), (unsigned)H, (unsigned)(F + qz)),
                      dim3(256),
                      (match_lds_words<T, D>() * sizeof(int32_t)), s,
                      (const T*)c.rep_k,
-                     (const T*)kn.data, kn.stride_head, kn.stride_token, c.frontier, tau, a, diag);
+                     (const T*)kn.data, kn.stride_head, kn.stride_token, c.frontier, tau, a, diag, qh,
+                     (const uint16_t*)ws.hash_planes, ws.hash_bits, qblocks);
   hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)F * Tf + 15) / 16), (unsigned)H),
                      dim3(256), 0, s, (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count,
                      c.rep_bucket, c.n_groups, c.frontier, group_of_new, (const T*)kn.data, kn.stride_head,
