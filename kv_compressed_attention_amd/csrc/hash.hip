@@ -140,8 +140,9 @@ hipError_t launch_hash_multi(HashJobs jobs, int dim, int dtype, const void* plan
   const int64_t tiles = hash_tiles(jobs, &js);
   if (js.count == 0) return hipSuccess;
   if (dtype == FASTAR_BF16) {
-    // two tiles per wave: the second tile's rows load during the first
-    const int64_t blocks = (tiles + 7) / 8 < 8192 ? (tiles + 7) / 8 : 8192;
+    // one tile per wave (a wave with more loads the next tile's rows while
+    // it hashes one): the loads are spread over as many waves as possible
+    const int64_t blocks = (tiles + 3) / 4 < 8192 ? (tiles + 3) / 4 : 8192;
     if (dim == 64)
       hipLaunchKernelGGL((hash_bf16_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, s, js,
                          (const uint16_t*)planes, n_bits, diag);
