@@ -176,8 +176,9 @@ __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
   const uint32_t incl = wave_incl_scan_dpp(local);
   if (lane == FASTAR_WAVE - 1) wtot[wave] = (int)incl;
   lds_barrier();
-  uint32_t run = incl - local;
-  for (int w = 0; w < wave; ++w) run += (uint32_t)wtot[w];
+  // plus the totals of the waves before (one load per lane, then a sum)
+  const int wt = lane < kDirectWaves ? wtot[lane] : 0;
+  uint32_t run = incl - local + (uint32_t)wave_sum_dpp(lane < wave ? wt : 0);
   if (t < nb4) {
     uint32_t base[4];
 #pragma unroll

@@ -171,31 +171,77 @@ __device__ __forceinline__ TabTok tab_frontier(const int32_t* fr, const int32_t*
   return r;
 }
 
-// Exclusive scan of st[0 .. nb) in place (whole workgroup), st[nb] = total.
-// Ends with a barrier.
-__device__ void scan_buckets(int nb, int32_t* st, int32_t* copy) {
-  __shared__ int wtot[16];
+// Exclusive scans of st[0 .. nb) and, if given, st2[0 .. nb) in place (whole
+// workgroup, one set of barriers for both); st[nb] = total (st2 likewise);
+// copy (if given) gets st's starts too.  st and st2 16-byte aligned.  Ends
+// with a barrier.
+__device__ void scan_buckets(int nb, int32_t* st, int32_t* copy, int32_t* st2 = nullptr) {
+  __shared__ int wtot[2][16];
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int per = (nb + nthr - 1) / nthr;
   const int s0 = tid * per;
-  int local = 0;
-  for (int s = s0; s < s0 + per && s < nb; ++s) local += st[s];
+  // four buckets per thread exactly: one 16-byte access each way
+  const bool quad = nb == 4 * nthr;
+  int4 q = make_int4(0, 0, 0, 0), q2 = make_int4(0, 0, 0, 0);
+  int local = 0, local2 = 0;
+  if (quad) {
+    q = *reinterpret_cast<const int4*>(st + s0);
+    local = q.x + q.y + q.z + q.w;
+    if (st2) {
+      q2 = *reinterpret_cast<const int4*>(st2 + s0);
+      local2 = q2.x + q2.y + q2.z + q2.w;
+    }
+  } else {
+    for (int s = s0; s < s0 + per && s < nb; ++s) {
+      local += st[s];
+      if (st2) local2 += st2[s];
+    }
+  }
   const int lane = lane_id(), wave = tid >> 6;
   const int incl = (int)wave_incl_scan_dpp((uint32_t)local);
-  if (lane == FASTAR_WAVE - 1) wtot[wave] = incl;
+  const int incl2 = (int)wave_incl_scan_dpp((uint32_t)local2);
+  if (lane == FASTAR_WAVE - 1) {
+    wtot[0][wave] = incl;
+    wtot[1][wave] = incl2;
+  }
   lds_barrier();
-  int run = incl - local;
-  for (int w = 0; w < wave; ++w) run += wtot[w];
-  for (int s = s0; s < s0 + per && s < nb; ++s) {
+  // plus the totals of the waves before (one load per lane, then a sum)
+  const int nw = nthr >> 6;
+  const int wt = lane < nw ? wtot[0][lane] : 0, wt2 = lane < nw ? wtot[1][lane] : 0;
+  int run = incl - local + wave_sum_dpp(lane < wave ? wt : 0);
+  int run2 = incl2 - local2 + wave_sum_dpp(lane < wave ? wt2 : 0);
+  if (quad) {
+    const int4 o = make_int4(run, run + q.x, run + q.x + q.y, run + q.x + q.y + q.z);
+    *reinterpret_cast<int4*>(st + s0) = o;
+    if (copy) {
+      copy[s0] = o.x;
+      copy[s0 + 1] = o.y;
+      copy[s0 + 2] = o.z;
+      copy[s0 + 3] = o.w;
+    }
+    run += local;
+    if (st2) {
+      *reinterpret_cast<int4*>(st2 + s0) =
+          make_int4(run2, run2 + q2.x, run2 + q2.x + q2.y, run2 + q2.x + q2.y + q2.z);
+      run2 += local2;
+    }
+  }
+  for (int s = s0; !quad && s < s0 + per && s < nb; ++s) {
     const int c = st[s];
     if (copy) copy[s] = run;
     st[s] = run;
     run += c;
+    if (st2) {
+      const int c2 = st2[s];
+      st2[s] = run2;
+      run2 += c2;
+    }
   }
   if (tid == nthr - 1) {
     if (copy) copy[nb] = run;
     st[nb] = run;
+    if (st2) st2[nb] = run2;
   }
   lds_barrier();
 }
@@ -205,20 +251,29 @@ __device__ void scan_buckets(int nb, int32_t* st, int32_t* copy) {
 // number kept), tok (the kept tokens, bucket by bucket; within a bucket in no
 // particular order), tbk (their buckets), if given, a copy of tbk in LDS
 // (ltbk) and their groups (candg).  lds holds 2^nbits + 1 int32; after the
-// call (and a barrier) lds[b] is the end of bucket b.
+// call (and a barrier) lds[b] is the end of bucket b.  With a second table
+// tc, its bucket starts go to st (2^nbits + 1 int32 of LDS: st[b] = kept
+// tokens of buckets < b, st[2^nbits] = all kept), counted and scanned
+// together with the first table's.
 __device__ void csr_build(int nbits, const TabTok& tt, int32_t* lds, int32_t* off, int32_t* tok,
-                          int32_t* tbk, int32_t* ltbk, int32_t* candg) {
+                          int32_t* tbk, int32_t* ltbk, int32_t* candg, const TabTok* tc = nullptr,
+                          int32_t* st = nullptr) {
   const int nb = 1 << nbits;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  for (int s = tid; s <= nb; s += nthr) lds[s] = 0;
+  for (int s = tid; s <= nb; s += nthr) {
+    lds[s] = 0;
+    if (tc) st[s] = 0;
+  }
   lds_barrier();
 #pragma unroll
-  for (int u = 0; u < kTabPer; ++u)
+  for (int u = 0; u < kTabPer; ++u) {
     if (tt.g[u] >= 0) atomicAdd(&lds[tt.b[u]], 1);
+    if (tc && tc->g[u] >= 0) atomicAdd(&st[tc->b[u]], 1);
+  }
   lds_barrier();
   // the bucket starts, to off and as the cursors of the fill below
-  scan_buckets(nb, lds, off);
+  scan_buckets(nb, lds, off, tc ? st : nullptr);
 #pragma unroll
   for (int u = 0; u < kTabPer; ++u) {
     if (tt.g[u] < 0) continue;
@@ -228,19 +283,6 @@ __device__ void csr_build(int nbits, const TabTok& tt, int32_t* lds, int32_t* of
     if (ltbk) ltbk[k] = tt.b[u];
     if (candg) candg[k] = tt.g[u];
   }
-}
-
-// The bucket starts of one table (whole workgroup): st[b] = number of kept
-// tokens with bucket < b, st[2^nbits] = all kept.  Ends with a barrier.
-__device__ void bucket_starts(int nbits, const TabTok& tt, int32_t* st) {
-  const int nb = 1 << nbits;
-  for (int s = threadIdx.x; s <= nb; s += blockDim.x) st[s] = 0;
-  lds_barrier();
-#pragma unroll
-  for (int u = 0; u < kTabPer; ++u)
-    if (tt.g[u] >= 0) atomicAdd(&st[tt.b[u]], 1);
-  lds_barrier();
-  scan_buckets(nb, st, nullptr);
 }
 
 // dynamic LDS the index launch may take
@@ -321,11 +363,12 @@ __global__ __launch_bounds__(1024) void tc_index_kernel(
   }
   const TabTok tc = f == 0 ? tab_frontier(fr, rb, empty, a.Tf) : tab_frame(kb - a.Tf, a.Tf);
   // lds: [2^b + 1] cursors, [2^b + 1] starts of table f, [Tf] buckets of the
-  // sorted keys
-  int32_t* cst = lds + nb + 1;
-  int32_t* ltbk = cst + nb + 1;
-  csr_build(a.nbits, tt, lds, off, tok, tbk, ltbk, nullptr);
-  bucket_starts(a.nbits, tc, cst);
+  // sorted keys (each array from a 16-byte boundary)
+  const int nb1 = (nb + 1 + 3) & ~3;
+  int32_t* cst = lds + nb1;
+  int32_t* ltbk = cst + nb1;
+  csr_build(a.nbits, tt, lds, off, tok, tbk, ltbk, nullptr, &tc, cst);
+  lds_barrier();
   // The match workgroups of frame f: key positions rounded to whole buckets,
   // and the candidate range of their buckets.  lds[b] is the end of bucket b.
   const int nkt = lds[nb - 1];
@@ -1114,7 +1157,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   a.prop = ws.prop;
   {
     // the index launch works out the match ranges when its LDS allows
-    const size_t nb1 = ((size_t)1 << c.n_bits) + 1;
+    const size_t nb1 = ((((size_t)1 << c.n_bits) + 1) + 3) & ~(size_t)3;
     const size_t full_lds = (nb1 * 2 + (size_t)Tf) * sizeof(int32_t);
     const bool ranges = full_lds <= kTcIndexLds;
     a.mrange = ranges ? ws.mrange : nullptr;
