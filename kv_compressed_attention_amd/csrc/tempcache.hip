@@ -642,7 +642,8 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
                                            const int32_t* cg, int c_lo, int c_hi,
                                            const int32_t* gtok, const int32_t* gcg,
                                            const int32_t* coff, TileDot<T, D>& td,
-                                           const uint16_t* crow, int& jrep, int& p, float& c) {
+                                           const uint16_t* crow, const float* crn, int& jrep, int& p,
+                                           float& c) {
   using TD = TileDot<T, D>;
   const int lane = lane_id();
   const int g = lane >> 4, col = lane & 15;
@@ -662,7 +663,8 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
   const int wv = threadIdx.x >> 6;
   // candidate ids of the first tile (the row this lane fetches); the key
   // rows were issued by the caller.  LROWS: the candidate rows are staged in
-  // LDS (crow, one row per candidate of the workgroup's range).
+  // LDS (crow, one row per candidate of the workgroup's range) and so are
+  // their 1 / norms (crn).
   bool cv = c_lo + col < c_hi;
   int ci = cv ? ctok[c_lo + col] : 0;
   int cb = cv ? cbk[c_lo + col] : -2;
@@ -680,11 +682,17 @@ __device__ __forceinline__ void match_tile(const SegCtx<T, D>& x, const int32_t*
     const int ni = nv ? ctok[c0 + 16 + col] : 0;
     const int nb = nv ? cbk[c0 + 16 + col] : -2;
     const int ng = (nv && x.f == 0) ? cg[c0 + 16 + col] : 0;
-    const float cn = TD::cand_norm(cr);
+    float rn;
+    if constexpr (LROWS) {
+      rn = crn[c0 + col];
+    } else {
+      const float cn = TD::cand_norm(cr);
+      rn = cn > 0.f ? rsqrtf(cn) : 0.f;
+    }
     if (g == 0) {
       tt_tok[wv][col] = ci;
       tt_bk[wv][col] = cb;  // -2 past the end: no key's bucket
-      tt_rn[wv][col] = cn > 0.f ? rsqrtf(cn) : 0.f;
+      tt_rn[wv][col] = rn;
     }
     const int4 t4 = *reinterpret_cast<const int4*>(&tt_tok[wv][4 * g]);
     const int4 b4 = *reinterpret_cast<const int4*>(&tt_bk[wv][4 * g]);
@@ -787,11 +795,11 @@ __device__ __forceinline__ int count_until(const int32_t* v, int n, int b, bool 
 constexpr int kRowCands = 96;
 
 // LDS int32 words of a match workgroup: proposals and lists, then (bf16)
-// the staged candidate rows
+// the staged candidate rows and their 1 / norms
 template <typename T, int D>
 constexpr size_t match_lds_words() {
   return 3 * kStageKeys + 2 * kStageKeys + 3 * kStageCands +
-         (sizeof(T) == 2 ? (size_t)kRowCands * D / 2 : 0);
+         (sizeof(T) == 2 ? (size_t)kRowCands * D / 2 + kRowCands : 0);
 }
 
 // One workgroup per kKeysPerGroup positions of frame f's bucket-sorted keys,
@@ -834,6 +842,7 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
   int32_t* sk = lds + 3 * kStageKeys;      // [2][kStageKeys] tokens, buckets
   int32_t* sc = sk + 2 * kStageKeys;       // [3][kStageCands] tokens, buckets, groups
   uint16_t* crow = reinterpret_cast<uint16_t*>(sc + 3 * kStageCands);  // [kRowCands][D]
+  float* crn = reinterpret_cast<float*>(crow + kRowCands * D);          // [kRowCands]
   const int32_t* ktok = STAGED ? sk : gktok + p0;
   const int32_t* kbk = STAGED ? sk + kStageKeys : gkbk + p0;
   const int32_t* ctok = STAGED ? sc : gctok + c0;
@@ -873,6 +882,13 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
     }
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
+    // each candidate's 1 / norm, once for the workgroup (16 rows per wave at
+    // a time, exactly as a tile would compute them)
+    for (int r0 = wave * 16; r0 < nc; r0 += 64) {
+      const float cn = TileDot<T, D>::cand_norm(TileDot<T, D>::from_lds(crow, r0 + col, nc));
+      if (lane < 16 && r0 + col < nc) crn[r0 + col] = cn > 0.f ? rsqrtf(cn) : 0.f;
+    }
+    lds_barrier();  // (the first key rows stay in flight)
   }
   for (int k0 = wave * kKeyTile; k0 < nk; k0 += 4 * kKeyTile) {
     if (k0 != wave * kKeyTile) issue_tile_keys(k0);
@@ -888,7 +904,7 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
     int jrep, p;
     float c;
     match_tile<T, D, MODE == 2>(x, ktok, kbk, k0, nk, ctok, cbk, cg, c_lo, c_hi, gctok, gcg, coff,
-                                td, crow, jrep, p, c);
+                                td, crow, crn, jrep, p, c);
     if (lane < 16 && jrep >= 0) {
       const int q = k0 + lane;
       lp[q] = p;
