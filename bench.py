@@ -10,10 +10,11 @@ AnnSA bucket attention of the queries over the compressed cache with the
 into a resident copy of the pre-chunk cache of its own (made before the timed
 region); after the run the K merged caches are checked to be identical.
 
-A step is one fastar_chunk call: the queries and the new keys hashed in one
-launch, the queries' index built by extra workgroups of the merge's first
-launch, all on one stream (--order picks the older call-by-call orders, on
-one stream or with the query side on a second one).  The steps are captured
+A step is one fastar_chunk call, six launches on one stream: the new keys
+hashed; the merge's index, match (whose extra workgroups hash the queries)
+and apply launches; the representatives' index (whose extra workgroups build
+the queries' index); the attention.  --order picks the older call-by-call
+orders, on one stream or with the query side on a second one.  The steps are captured
 into HIP graphs, --graph-steps of them (each on its own cache) per graph, as
 a model captures the chunks of its layers together, and replayed (--eager
 launches from Python instead, with per-call event times in "stages_ms").

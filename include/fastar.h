@@ -231,13 +231,15 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
                                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * fastar_chunk -- one chunk of the per-layer sequence in one call, the
- * stages that do not depend on each other launched together: one hashing of
- * the queries, new keys and prompt keys (paper.rainbus.top "technical
- * novelty"); the TempCache merge of the new frames, the queries' bucket
- * index built in the launch that indexes the representatives (when both use
- * the single counting pass); AnnSA over the merged cache; then, with a
- * prompt, AnnCA pruning and cross-attention over the kept prompt tokens.
+ * fastar_chunk -- one chunk of the per-layer sequence in one call, on one
+ * stream, work that does not depend on a launch's own work carried by extra
+ * workgroups of it: the new keys (and prompt keys) hashed; the TempCache
+ * merge of the new frames, whose match launch also hashes bf16 queries (one
+ * hashing serves every module: paper.rainbus.top "technical novelty"); the
+ * representatives' bucket index, whose launch also builds the queries' index
+ * (when both use the single counting pass); AnnSA over the merged cache;
+ * then, with a prompt, AnnCA pruning and cross-attention over the kept prompt
+ * tokens.
  * Equal to fastar_hash_multi, fastar_bucket_index, fastar_tempcache_merge,
  * fastar_bucket_attention (bucket mode, keys rep_k, values v_mean, bias
  * log_count) and, with a prompt, fastar_prune_prompt and
