@@ -266,6 +266,15 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       float s[8];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
+        // a half of the chunk none of the wave's rows uses: no scores
+        const uint32_t ka = kc + (uint32_t)(16 * hf);
+        bool uh = rn0 > 0u && rlo0 < ka + 16u && rlo0 + rn0 > ka;
+        if (P == 2) uh = uh || (rn1 > 0u && rlo1 < ka + 16u && rlo1 + rn1 > ka);
+        if (!ballot64(uh)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[4 * hf + i] = -INFINITY;
+          continue;
+        }
         // A operand: chunk row 16 hf + col, dims 32c + 8g .. +8 (piece 4c + g)
         const int row = 16 * hf + col;
         bf16x8_t kop[NC];
