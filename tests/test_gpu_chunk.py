@@ -1,14 +1,16 @@
 """fastar_chunk against the same calls made one by one.
 
-The chunk entry point launches the stages that do not depend on each other
-together (one hashing launch for queries, keys and prompt keys; the queries'
-index inside the merge's first launch).  Its outputs must equal, bit for bit,
-those of fastar_hash_multi, fastar_bucket_index, fastar_tempcache_merge,
+The chunk entry point puts work that does not depend on a launch into extra
+workgroups of it: bf16 queries are hashed by the merge's match launch, and
+their one-probe index is built by the launch that indexes the
+representatives.  Its outputs must equal, bit for bit, those of
+fastar_hash_multi, fastar_bucket_index, fastar_tempcache_merge,
 fastar_bucket_attention and (with a prompt) fastar_prune_prompt plus the
 list-mode attention, called in order on the same inputs: every kernel on the
-path is deterministic.  Workload 0 (fp32, prompt, one probe) and 4 (bf16,
-prompt, two probes: the index outside the merge launch) cover both index
-paths and the AnnCA tail; workload 1 is the layer workload itself.
+path is deterministic.  Workload 0 (fp32, prompt, one probe: every hashing in
+the hash launch) and 4 (bf16, prompt, two probes: the queries' index in a
+launch of its own) cover the other paths and the AnnCA tail; workload 1 is
+the layer workload itself.
 """
 
 import numpy as np
