@@ -73,10 +73,11 @@ __device__ __forceinline__ double sum4_d(double v) {
 // Re-evaluates one row in float64 and writes its ids (o: the row's output,
 // the same in every lane).  Lane 16s + p takes the dims [s D/4, (s+1) D/4)
 // of hyperplane p: serial sums of exact products, then added over the four
-// slices.  The row (xr: [D]) and the hyperplanes (ps, row stride pst) are
-// read from LDS.  A sign float64 cannot certify is settled exactly with an
-// expansion sum in E (D + 2 doubles of LDS); the second probe's distances
-// and error bounds go through DE (32 doubles of LDS).
+// slices.  The row (xr: [D], LDS) and the hyperplanes (ps, row stride pst;
+// LDS or global memory) are read through generic pointers.  A sign float64
+// cannot certify is settled exactly with an expansion sum in E (D + 2
+// doubles of LDS); the second probe's distances and error bounds go through
+// DE (32 doubles of LDS).
 template <typename T, int D>
 __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t* __restrict__ o, int P,
                                int nb, fastar_diag_t* __restrict__ diag, double* E, double* DE) {
@@ -170,7 +171,7 @@ __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t
 // LDS bytes of hash_bf16_body<D>
 template <int D>
 constexpr size_t hash_bf16_lds() {
-  return 4 * (D + 2 + 32) * sizeof(double) + 16 * (D + 8) * sizeof(uint16_t) + 4 * D * sizeof(uint16_t);
+  return 4 * (D + 2 + 32) * sizeof(double) + 4 * D * sizeof(uint16_t);
 }
 
 // The jobs with rows, with tile_end filled in (16-row tiles in job order);
@@ -192,31 +193,23 @@ inline int64_t hash_tiles(const HashJobs& jobs, HashJobs* js) {
 // Workgroup `block` of nblocks (256 threads) of a bf16 hashing: one wave per
 // tile of 16 rows of one of the jobs' tensors (tiles of tensor i are numbered
 // from jobs.tile_end[i - 1]; tile_end filled by hash_tiles); the first tile's
-// rows are requested before the hyperplanes are read.  lds: hash_bf16_lds<D>()
+// rows and the hyperplanes are requested together.  lds: hash_bf16_lds<D>()
 // bytes, 16-byte aligned.
 template <int D>
 __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint16_t* __restrict__ planes, int nb,
                                                fastar_diag_t* __restrict__ diag, int block, int nblocks,
                                                char* lds) {
   constexpr int NC = D / 32;
-  constexpr int kPst = D + 8;  // padded hyperplane rows: lanes reading 16 planes hit different banks
   // lds: [4][D + 2] doubles (exact sums), [4][32] doubles (second probe),
-  // [16][kPst] hyperplanes, [4][D] per wave the row being re-evaluated
+  // [4][D] per wave the row being re-evaluated (each wave uses only its own
+  // parts: no barrier).  The hyperplanes are read from global memory.
   double (*ex)[D + 2] = reinterpret_cast<double (*)[D + 2]>(lds);
   double (*de)[32] = reinterpret_cast<double (*)[32]>(lds + 4 * (D + 2) * sizeof(double));
-  uint16_t* spl = reinterpret_cast<uint16_t*>(lds + 4 * (D + 2 + 32) * sizeof(double));
-  uint16_t (*sxr)[D] = reinterpret_cast<uint16_t (*)[D]>(spl + 16 * kPst);
+  uint16_t (*sxr)[D] = reinterpret_cast<uint16_t (*)[D]>(lds + 4 * (D + 2 + 32) * sizeof(double));
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
   const int wv = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < 16 * D / 8; i += blockDim.x) {
-    const int pp = i / (D / 8), c8 = i % (D / 8);
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (pp < nb) u = *reinterpret_cast<const uint4*>(planes + (int64_t)pp * D + 8 * c8);
-    *reinterpret_cast<uint4*>(&spl[pp * kPst + 8 * c8]) = u;
-  }
-  __syncthreads();
   const int64_t total = jobs.tile_end[jobs.count - 1];
   const int64_t nwaves = (int64_t)nblocks * (blockDim.x >> 6);
   const int64_t first = (int64_t)block * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -350,7 +343,7 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
 #pragma unroll
         for (int c = 0; c < NC; ++c) *reinterpret_cast<uint4*>(&sxr[wv][32 * c + 8 * g]) = xu[c];
       }
-      hash_fixup_row<uint16_t, D>(sxr[wv], spl, kPst, w.bucket + ((int64_t)w.h * w.N + w.r0 + r) * P,
+      hash_fixup_row<uint16_t, D>(sxr[wv], planes, D, w.bucket + ((int64_t)w.h * w.N + w.r0 + r) * P,
                                   P, nb, diag, ex[wv], de[wv]);
     }
 #pragma unroll
