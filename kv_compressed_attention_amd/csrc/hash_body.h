@@ -171,7 +171,7 @@ __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t
 // LDS bytes of hash_bf16_body<D>
 template <int D>
 constexpr size_t hash_bf16_lds() {
-  return 4 * (D + 2 + 32) * sizeof(double) + 4 * D * sizeof(uint16_t);
+  return 4 * (D + 2 + 32) * sizeof(double) + 16 * (D + 8) * sizeof(uint16_t) + 4 * D * sizeof(uint16_t);
 }
 
 // The jobs with rows, with tile_end filled in (16-row tiles in job order);
@@ -193,19 +193,22 @@ inline int64_t hash_tiles(const HashJobs& jobs, HashJobs* js) {
 // Workgroup `block` of nblocks (256 threads) of a bf16 hashing: one wave per
 // tile of 16 rows of one of the jobs' tensors (tiles of tensor i are numbered
 // from jobs.tile_end[i - 1]; tile_end filled by hash_tiles); the first tile's
-// rows and the hyperplanes are requested together.  lds: hash_bf16_lds<D>()
+// rows and the hyperplanes are requested together.  256 threads.  lds:
+// hash_bf16_lds<D>()
 // bytes, 16-byte aligned.
 template <int D>
 __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint16_t* __restrict__ planes, int nb,
                                                fastar_diag_t* __restrict__ diag, int block, int nblocks,
                                                char* lds) {
   constexpr int NC = D / 32;
+  constexpr int kPst = D + 8;  // padded hyperplane rows: lanes reading 16 planes hit different banks
   // lds: [4][D + 2] doubles (exact sums), [4][32] doubles (second probe),
-  // [4][D] per wave the row being re-evaluated (each wave uses only its own
-  // parts: no barrier).  The hyperplanes are read from global memory.
+  // [16][kPst] hyperplanes (for rows float32 cannot certify), [4][D] per
+  // wave the row being re-evaluated
   double (*ex)[D + 2] = reinterpret_cast<double (*)[D + 2]>(lds);
   double (*de)[32] = reinterpret_cast<double (*)[32]>(lds + 4 * (D + 2) * sizeof(double));
-  uint16_t (*sxr)[D] = reinterpret_cast<uint16_t (*)[D]>(lds + 4 * (D + 2 + 32) * sizeof(double));
+  uint16_t* spl = reinterpret_cast<uint16_t*>(lds + 4 * (D + 2 + 32) * sizeof(double));
+  uint16_t (*sxr)[D] = reinterpret_cast<uint16_t (*)[D]>(spl + 16 * kPst);
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
@@ -252,19 +255,32 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
 #pragma unroll
     for (int c = 0; c < NC; ++c) u[c] = *reinterpret_cast<const uint4*>(xr + 32 * c + 8 * g);
   };
+  // The first tile's rows, the A operand and this thread's share of the
+  // hyperplanes for the LDS copy are all in flight together; the copy is
+  // written once the A operand has landed (its barrier orders LDS only).
   uint4 xu[NC];
   if (first < total) load_rows(where(first), xu);
 
   // A operand: hyperplane `col`, dims 32c + 8g .. +8 of chunk c
+  uint4 au[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    au[c] = make_uint4(0u, 0u, 0u, 0u);
+    if (col < nb) au[c] = *reinterpret_cast<const uint4*>(planes + (int64_t)col * D + 32 * c + 8 * g);
+  }
+  static_assert(16 * D / 8 <= 256, "one 16-byte piece of the hyperplanes per thread");
+  const int pi = threadIdx.x, pp = pi / (D / 8), p8 = pi % (D / 8);
+  uint4 pu = make_uint4(0u, 0u, 0u, 0u);
+  if (pi < 16 * D / 8 && pp < nb) pu = *reinterpret_cast<const uint4*>(planes + (int64_t)pp * D + 8 * p8);
   bf16x8_t aop[NC];
   float r2 = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (col < nb) u = *reinterpret_cast<const uint4*>(planes + (int64_t)col * D + 32 * c + 8 * g);
-    r2 += sumsq_bf16x8(u);
-    aop[c] = __builtin_bit_cast(bf16x8_t, u);
+    r2 += sumsq_bf16x8(au[c]);
+    aop[c] = __builtin_bit_cast(bf16x8_t, au[c]);
   }
+  if (pi < 16 * D / 8) *reinterpret_cast<uint4*>(&spl[pp * kPst + 8 * p8]) = pu;
+  lds_barrier();
   r2 += shfl_xor_f(r2, 16);
   r2 += shfl_xor_f(r2, 32);
   float rnorm[4];
@@ -343,7 +359,7 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
 #pragma unroll
         for (int c = 0; c < NC; ++c) *reinterpret_cast<uint4*>(&sxr[wv][32 * c + 8 * g]) = xu[c];
       }
-      hash_fixup_row<uint16_t, D>(sxr[wv], planes, D, w.bucket + ((int64_t)w.h * w.N + w.r0 + r) * P,
+      hash_fixup_row<uint16_t, D>(sxr[wv], spl, kPst, w.bucket + ((int64_t)w.h * w.N + w.r0 + r) * P,
                                   P, nb, diag, ex[wv], de[wv]);
     }
 #pragma unroll
