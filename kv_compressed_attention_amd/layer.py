@@ -13,10 +13,12 @@ compressed cache including the chunk's own frames):
   6. cross-attention over the kept prompt tokens.
 Every step is a libfastar call; this class only owns the torch buffers and
 the ordering.  By default one fastar_chunk call runs the whole sequence on
-the caller's stream (the queries' index built in the merge's first launch).
-The other orders issue the calls one by one: on one stream, or with the
-query side (2, then 4 and 6), which does not touch the cache, on a second
-stream of default priority; all streams join before step returns.
+the caller's stream (bf16 queries hashed by extra workgroups of the merge's
+match launch, their index by extra workgroups of the launch that indexes the
+representatives).  The other orders issue the calls one by one: on one
+stream, or with the query side (2, then 4 and 6), which does not touch the
+cache, on a second stream of default priority; all streams join before step
+returns.
 """
 
 from __future__ import annotations
