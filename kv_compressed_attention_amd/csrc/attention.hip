@@ -6,20 +6,25 @@
 // ln m_j for a TempCache group of m_j merged keys (Lemma 5.1, paperlayer.ai
 // appendix A).
 //
-// bf16 kernel layout.  A wave owns 16 query rows, taken in index (bucket)
-// order, so a wave's rows usually share one or a few buckets.  It walks the
-// distinct buckets of its rows (both probes) in ascending order; for each it
-// streams that bucket's keys in chunks of 32 with rows outside the bucket
-// masked.  Per chunk:
-//   S^T[32 keys x 16 rows] = K Q^T   two v_mfma_f32_16x16x32_bf16 groups,
-//                                      K gathered straight from HBM (each lane
-//                                      reads 64 contiguous bytes of one key);
-//   online softmax in float32 with exp2, row max shared by the 4 lanes of a row;
-//   O^T[d x 16 rows] += V^T P^T         d/16 MFMAs.  P^T comes out of S^T's
+// bf16 kernel layout.  A workgroup of 4 waves owns 64 query rows, taken in
+// index (bucket) order; each wave's MFMA rows are 16 of them.  The key list
+// of the workgroup is the key ranges of its rows' distinct buckets (both
+// probes), concatenated, and is streamed in chunks of 32 slots shared by the
+// four waves; a (slot, row) score counts only where the slot lies in one of
+// the row's own ranges, so small buckets share chunks.  Per chunk:
+//   the chunk's 32 K and V rows and 32 biases go from HBM to LDS with the
+//   16-byte direct loads (double-buffered: chunk c + 1 loads while chunk c
+//   is computed), K rows stored with their 16-byte pieces XOR-swizzled;
+//   S^T[32 slots x 16 rows] = K Q^T   two groups of d/32
+//                                      v_mfma_f32_16x16x32_bf16 (a half-chunk
+//                                      no row of the wave uses is skipped);
+//   online softmax in float32 with exp2, row max shared by the 4 lanes of a
+//   row;
+//   O^T[d x 16 rows] += V^T P^T       d/16 MFMAs.  P^T comes out of S^T's
 //                                      accumulator layout with no shuffles; V^T
-//                                      is built in registers: each lane loads 16
-//                                      contiguous bytes of 8 keys and transposes
-//                                      8x8 16-bit values, so V needs no LDS.
+//                                      is built from LDS reads of 16 bytes of
+//                                      8 keys per lane and 8x8 16-bit
+//                                      transposes in registers.
 // The dims of O^T are interleaved (row r of block b is dim (d/16) r + b) so
 // that every lane finally holds 32 (d=128) contiguous output dims.
 
@@ -129,14 +134,46 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   if (MODE == 0) idx_h = k_perm + (int64_t)h * Nk;
   if (MODE == 1) idx_h = key_list + (int64_t)h * Nk;
 
-  // Batches of passes.  A pass is one distinct bucket of the workgroup's 64
-  // rows (both probes), in ascending order, up to 64 per batch (lane i holds
-  // pass i); in list and dense mode one pass over the list or all keys.  The
-  // batch's key list is its passes' key ranges, concatenated.  Every wave
-  // builds the same table, so loop counts agree across the workgroup.
+  // Batches of passes.  With two probes a pass is one distinct bucket of the
+  // workgroup's 64 rows (either probe), in ascending order, up to 64 per
+  // batch (lane i holds pass i); with one probe, one per run of equal
+  // buckets in row order (one per distinct bucket when the rows come in
+  // bucket order; any order is still correct, as a bucket seen twice is then
+  // just loaded twice); in list and dense mode one pass over the list or all
+  // keys.  The batch's key list is its passes' key ranges, concatenated.
+  // Every wave builds the same table, so loop counts agree across the
+  // workgroup.
   while (true) {
     int npass = 0, xs = 0, pkb = 0, pke = 0, pr0 = -1, pr1 = -1;
-    if (MODE == 0) {
+    if (MODE == 0 && P == 1) {
+      // one probe: the rows come in bucket order (rows past the end hold
+      // INT_MAX, last), so a pass opens wherever a row's bucket differs from
+      // the previous row's, and the 64 rows' passes fit one batch
+      const int cprev = __shfl(c0, l > 0 ? l - 1 : 0, FASTAR_WAVE);
+      const uint64_t opens = ballot64(c0 != INT_MAX && (l == 0 || cprev != c0));
+      npass = __popcll(opens);
+      if (npass == 0) break;
+      if (c0 != INT_MAX) pr0 = __popcll(opens & (lanemask_lt() | (1ull << l))) - 1;
+      // lane p: the row that opens pass p (the (p+1)-th set bit of opens)
+      int pos = 0, kth = l;
+      uint64_t mk = opens;
+#pragma unroll
+      for (int w = 32; w >= 1; w >>= 1) {
+        const int cnt = __popcll(mk & ((1ull << w) - 1ull));
+        if (kth >= cnt) {
+          kth -= cnt;
+          mk >>= w;
+          pos += w;
+        }
+      }
+      xs = __shfl(c0, pos & (FASTAR_WAVE - 1), FASTAR_WAVE);
+      c0 = INT_MAX;
+      if (l < npass) {
+        const int32_t* off = k_offsets + (int64_t)h * ((1 << nbits) + 1) + xs;
+        pkb = off[0];
+        pke = off[1];
+      }
+    } else if (MODE == 0) {
       while (npass < FASTAR_WAVE) {
         const int X = wave_min_dpp(min(c0, c1));
         if (X == INT_MAX) break;
@@ -172,18 +209,31 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     // slot ranges [lo0, lo0 + n0) and, with two probes, [lo1, lo1 + n1)
     int pre = 0, total = 0;
     uint32_t lo0 = 0u, n0 = 0u, lo1 = 0u, n1 = 0u;
-    for (int p = 0; p < npass; ++p) {
-      const int lp = __builtin_amdgcn_readlane(len, p);
-      if (l == p) pre = total;
-      if (pr0 == p) {
-        lo0 = (uint32_t)total;
-        n0 = (uint32_t)lp;
+    if (MODE == 0 && P == 1) {
+      // a prefix sum over the passes; row l's range is its pass's
+      const int incl = (int)wave_incl_scan_dpp((uint32_t)len);
+      pre = incl - len;
+      total = __builtin_amdgcn_readlane(incl, FASTAR_WAVE - 1);
+      const int pl = pr0 < 0 ? 0 : pr0;
+      const int lo = __shfl(pre, pl, FASTAR_WAVE), n = __shfl(len, pl, FASTAR_WAVE);
+      if (pr0 >= 0) {
+        lo0 = (uint32_t)lo;
+        n0 = (uint32_t)n;
       }
-      if (P == 2 && pr1 == p) {
-        lo1 = (uint32_t)total;
-        n1 = (uint32_t)lp;
+    } else {
+      for (int p = 0; p < npass; ++p) {
+        const int lp = __builtin_amdgcn_readlane(len, p);
+        if (l == p) pre = total;
+        if (pr0 == p) {
+          lo0 = (uint32_t)total;
+          n0 = (uint32_t)lp;
+        }
+        if (P == 2 && pr1 == p) {
+          lo1 = (uint32_t)total;
+          n1 = (uint32_t)lp;
+        }
+        total += lp;
       }
-      total += lp;
     }
     // the MFMA row's ranges
     const int src = 16 * wave + col;
@@ -352,7 +402,7 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       chunk(c, ktA, vtA, btA, ktB, vtB, btB);
       if (c + 1 < nch) chunk(c + 1, ktB, vtB, btB, ktA, vtA, btA);
     }
-    if (MODE != 0 || npass < FASTAR_WAVE) break;
+    if (MODE != 0 || P == 1 || npass < FASTAR_WAVE) break;
     // the next batch refills both buffers: every wave is done with them
     __syncthreads();
   }

@@ -235,6 +235,27 @@ def test_bucket_attention_matches_oracle(fa, dtype, H, nq, nk, d, b, P):
         assert np.max(np.abs(lse[h][fin] - lse_ref[fin]), initial=0) <= 10 * TOL[dtype]
 
 
+@pytest.mark.parametrize("P", [1, 2])
+def test_bucket_attention_any_row_order(fa, P):
+    # q_perm in a random order instead of the index's bucket order: a
+    # workgroup then meets a bucket in several runs of rows; every row must
+    # still see exactly its own bucket's keys
+    H, nq, nk, d, b = 2, 700, 1500, 128, 5
+    q, k, v, q_ids, k_ids, kb = _attn_case("bf16", H, nq, nk, d, b, P, seed=77)
+    rng = np.random.default_rng(78)
+    perm = np.stack([rng.permutation(nq) for _ in range(H)]).astype(np.int32)
+    k_off, k_perm = fa.fastar_bucket_index(i32(k_ids[:, :, None]), b)
+    out, lse = fa.fastar_bucket_attention(dev_tensor(q, "bf16"), dev_tensor(k, "bf16"),
+                                          dev_tensor(v, "bf16"), q_bucket=i32(q_ids),
+                                          q_perm=i32(perm), key_bias=torch.tensor(kb, device="cuda"),
+                                          k_offsets=k_off, k_perm=k_perm, n_bits=b)
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    for h in range(H):
+        o_ref, _ = oracle.bucket_attention(q[h], q_ids[h], k[h], v[h], k_ids[h], bias=kb[h])
+        assert np.max(np.abs(out[h] - o_ref)) <= TOL["bf16"], f"head {h}"
+
+
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
 def test_list_and_dense_modes_match_oracle(fa, dtype, d):
     H, nq, nk = 2, 333, 512
