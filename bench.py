@@ -128,9 +128,10 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=20):
     return total / reps, reps
 
 
-def recorded_traffic():
+def recorded_traffic(workload: str):
     """HBM bytes per attention launch from the committed counter passes, if
-    they were taken with the current attention sources (else None)."""
+    they were taken on this workload with the current attention sources
+    (else None)."""
     import glob
     import hashlib
     import re
@@ -138,9 +139,10 @@ def recorded_traffic():
     src = b"".join(open(os.path.join(ROOT, "kv_compressed_attention_amd", "csrc", f), "rb").read()
                    for f in ("attention.hip", "common.h"))
     digest = hashlib.sha256(src).hexdigest()[:16]
-    for path in glob.glob(os.path.join(ROOT, "profiles", "attn_bf16_bucket_layer_*.md")):
-        m = re.search(r"traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]+)", open(path).read())
-        if m and m.group(2) == digest:
+    for path in glob.glob(os.path.join(ROOT, "profiles", "attn_bf16_*.md")):
+        m = re.search(r"traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]+) workload=(\S+)",
+                      open(path).read())
+        if m and m.group(2) == digest and m.group(3) == workload:
             return int(m.group(1))
     return None
 
@@ -271,7 +273,7 @@ def main():
                    "cache_frames": F, "tokens_per_frame": T, "new_frames": w.chunk_frames,
                    "n_bits": w.n_bits, "n_probes": w.n_probes, "tau": w.tau},
         "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": recorded_traffic(),
+                     "unit": "GB/s", "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": recorded_traffic(w.name),
                      "kernel": "attn_bf16_kernel (fastar_bucket_attention, bucket mode)",
                      "bytes_per_launch": nbytes, "launch_ms": stage_ms["attention"]},
         "attention": {"tflops": tflops, "frac_bf16_mfma_peak": tflops / PEAK_BF16_TFLOPS,
