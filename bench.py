@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=1, help="synthetic workload index (1, 3 or 4)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense", action="store_true",
+                   help="skip the one-bucket (dense, MFMA-bound) attention measurement")
     p.add_argument("--order", choices=["chunk", "serial", "2stream", "split"], default="chunk",
                    help="chunk: one fastar_chunk call per step (default); serial: every call on "
                         "one stream; 2stream: the query index (and AnnCA) on a second stream; "
@@ -126,6 +128,43 @@ def cpu_baseline(w, min_seconds=10.0, max_reps=20):
             total += time.perf_counter() - t0
             reps += 1
     return total / reps, reps
+
+
+def dense_one_bucket(dev, reps: int = 5):
+    """The attention kernel with all keys in one bucket (dense mode) at the
+    rollout size: 12 heads, 4680 queries, 23,400 keys, d = 128, bf16, seeded
+    normal inputs.  Every query meets every key, so the kernel is bound by
+    its MFMA work and its fraction of the bf16 peak measures MFMA quality.
+    reps launches in one HIP graph, replayed between two events."""
+    import kv_compressed_attention_amd as fa
+    from synth import gaussian
+
+    H, nq, nk, d = 12, 4680, 23400, 128
+
+    def up(a):
+        return torch.tensor(a, dtype=torch.float32, device=dev).to(torch.bfloat16)
+
+    q, k, v = up(gaussian((H, nq, d), 501, "bf16")), up(gaussian((H, nk, d), 502, "bf16")), \
+        up(gaussian((H, nk, d), 503, "bf16"))
+    out = torch.empty(H, nq, d, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(H, nq, dtype=torch.float32, device=dev)
+    fa.fastar_bucket_attention(q, k, v, out=out, lse=lse)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fa.fastar_bucket_attention(q, k, v, out=out, lse=lse)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    tflops = 4.0 * d * nq * nk * H / (ms * 1e-3) / 1e12
+    return {"workload": f"one_bucket_bf16_h{H}_d{d}_q{nq}_k{nk}", "bound": "mfma", "launch_ms": ms,
+            "tflops": tflops, "frac_bf16_mfma_peak": tflops / PEAK_BF16_TFLOPS}
 
 
 def recorded_traffic(workload: str):
@@ -287,6 +326,8 @@ def main():
         "host_enqueue_ms_per_step": t_enq * 1e3 / args.steps,
         "diag": layer.diag.tolist(),
     }
+    if not args.no_dense:
+        out["dense_one_bucket"] = dense_one_bucket(dev)
     if not args.no_cpu_baseline:
         per_step, reps = cpu_baseline(w)
         out["cpu_baseline"] = {"value": nq / per_step, "unit": "query tokens/s", "cores": 1,

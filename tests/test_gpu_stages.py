@@ -389,3 +389,20 @@ def test_tempcache_capacity_overflow_is_reported(fa):
     assert diag[4].item() == T - 10
     g = gon[0].cpu().numpy()
     assert np.array_equal(g[:10], T + np.arange(10)) and np.all(g[10:] == -1)
+
+
+def test_dense_one_bucket_full_size_sampled(fa):
+    # the one-bucket measurement's size and launch (12 heads, 4680 queries,
+    # 23,400 keys, d = 128, bf16, dense mode): sampled rows against the oracle
+    H, nq, nk, d = 12, 4680, 23400, 128
+    q, k, v = gaussian((H, nq, d), 501, "bf16"), gaussian((H, nk, d), 502, "bf16"), \
+        gaussian((H, nk, d), 503, "bf16")
+    out, lse = fa.fastar_bucket_attention(dev_tensor(q, "bf16"), dev_tensor(k, "bf16"),
+                                          dev_tensor(v, "bf16"))
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    rows = np.array([0, 1, 63, 64, 2047, 4095, 4616, 4679])
+    for h in (0, 5, 11):
+        o_ref, lse_ref = oracle.dense_attention(q[h][rows], k[h], v[h])
+        assert np.max(np.abs(out[h][rows] - o_ref)) <= TOL["bf16"], f"head {h}"
+        assert np.max(np.abs(lse[h][rows] - lse_ref)) <= 10 * TOL["bf16"], f"head {h}"
