@@ -22,11 +22,9 @@
 //   row;
 //   O^T[d x 16 rows] += V^T P^T       d/16 MFMAs.  P^T comes out of S^T's
 //                                      accumulator layout with no shuffles; V^T
-//                                      is built from LDS reads of 16 bytes of
-//                                      8 keys per lane and 8x8 16-bit
-//                                      transposes in registers.
-// The dims of O^T are interleaved (row r of block b is dim (d/16) r + b) so
-// that every lane finally holds 32 (d=128) contiguous output dims.
+//                                      comes from gfx950's transposing LDS
+//                                      reads (ds_read_b64_tr_b16), two per
+//                                      16-dim block.
 
 #include "common.h"
 #include "kernels.h"
@@ -38,24 +36,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int NB>
-struct VRow;
-template <>
-struct VRow<8> {  // d = 128: 8 bf16 per lane per key
-  uint4 u;
-  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
-  // the 32-bit word holding dim b (its half: b & 1)
-  __device__ __forceinline__ uint32_t word(int b) const {
-    return (b < 2) ? u.x : (b < 4) ? u.y : (b < 6) ? u.z : u.w;
-  }
-};
-template <>
-struct VRow<4> {  // d = 64: 4 bf16 per lane per key
-  uint2 u;
-  __device__ __forceinline__ void load(const uint16_t* p) { u = *reinterpret_cast<const uint2*>(p); }
-  __device__ __forceinline__ uint32_t word(int b) const { return (b < 2) ? u.x : u.y; }
-};
-
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 // MODE: 0 bucket, 1 key list, 2 dense.  Every head's k and v rows lie within
 // 4 GiB of the head's first row (checked by the caller), so row offsets are
@@ -94,6 +75,8 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
+  // the chunk row this lane addresses for the V^T operand's transposing reads
+  const int vrow = 4 * g + ((l >> 2) & 3);
   // this lane's MFMA row: workgroup row 16 wave + col
   const int64_t r = R0 + 16 * wave + col;
   const bool rvalid = r < Nq;
@@ -275,9 +258,9 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
         key[i] = (MODE == 2) ? kk : idx_h[kk];
       }
     };
-    // chunk c's K, V rows and biases into buffer c & 1; K row `row` holds
-    // piece p ^ (row % kPieces) at position p, so that the 16 lanes reading
-    // one piece of 16 different rows hit different banks
+    // chunk c's K, V rows and biases into buffer c & 1; K and V row `row`
+    // hold piece p ^ (row % kPieces) at position p, so that lanes reading one
+    // piece of 16 different rows hit different banks
     auto chunk_load = [&](const int* key, uint16_t* kt, uint16_t* vt, float* bt) {
 #pragma unroll
       for (int i = 0; i < kDmaPerWave; ++i) {
@@ -288,7 +271,7 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
             (const void*)(kh + (uint32_t)((uint32_t)key[i] * kst_b + (uint32_t)((pc ^ (row % kPieces)) * 16))),
             (__attribute__((address_space(3))) void*)(kt + row0 * D), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(
-            (const void*)(vh + (uint32_t)((uint32_t)key[i] * vst_b + (uint32_t)(pc * 16))),
+            (const void*)(vh + (uint32_t)((uint32_t)key[i] * vst_b + (uint32_t)((pc ^ (row % kPieces)) * 16))),
             (__attribute__((address_space(3))) void*)(vt + row0 * D), 16, 0, 0);
       }
       if (bh && l < 8)
@@ -376,20 +359,21 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       lsum += psum;
       m = mnew;
       const bf16x8_t pop = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-      // V^T operand: lane (dim-row col, group g), slot si <-> chunk row
-      // 16 (si >> 2) + 4g + (si & 3), dims NB*col .. NB*col + NB - 1 (one per
-      // output block)
-      VRow<NB> vr[8];
-#pragma unroll
-      for (int si = 0; si < 8; ++si) vr[si].load(&vt[(16 * (si >> 2) + 4 * g + (si & 3)) * D + NB * col]);
+      // V^T operand of block bb: lane (dim 16 bb + col, group g), slot si <->
+      // chunk row 16 (si >> 2) + 4g + (si & 3), by two transposing LDS reads
+      // (slots 0..3, then 4..7).  Such a read hands lane 16g + a element
+      // a % 4 of the 8 bytes that lane 16g + 4e + a / 4 addresses, as its
+      // element e; so this lane addresses row 4 (l >> 4) + ((l >> 2) & 3)
+      // (plus 16), dims 16 bb + 4 (l & 3) .. + 3.
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
-        // (slot 2i's dim, slot 2i+1's dim) in one byte permute per dword
-        const uint32_t sel = (bb & 1) ? 0x07060302u : 0x05040100u;
-        const uint4 w = make_uint4(__builtin_amdgcn_perm(vr[1].word(bb), vr[0].word(bb), sel),
-                                   __builtin_amdgcn_perm(vr[3].word(bb), vr[2].word(bb), sel),
-                                   __builtin_amdgcn_perm(vr[5].word(bb), vr[4].word(bb), sel),
-                                   __builtin_amdgcn_perm(vr[7].word(bb), vr[6].word(bb), sel));
+        const int piece = 2 * bb + ((l & 3) >> 1);
+        const uint16_t* src = vt + vrow * D + ((piece ^ (vrow % kPieces)) * 8) + (l & 1) * 4;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)src);
+        const v4i16_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(src + 16 * D));
+        const uint2 wl = __builtin_bit_cast(uint2, lo), wh = __builtin_bit_cast(uint2, hi);
+        const uint4 w = make_uint4(wl.x, wl.y, wh.x, wh.y);
         acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), pop, acc[bb], 0, 0, 0);
       }
     };
@@ -409,16 +393,23 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   lsum = sum_xor32(sum_xor16(lsum));
   if (!rvalid) return;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  // acc[b][i] = O[row col][NB*(4g+i) + b]: dims 4*NB*g .. 4*NB*g + 4*NB - 1
-  uint32_t ow[2 * NB];
+  // acc[b][i] = O[row col][16 b + 4 g + i].  Lanes g and g ^ 1 (l ^ 16, the
+  // same row) trade halves of each block pair, so that each stores 16
+  // contiguous bytes: even g dims 16 b0 + 4g .. + 7, odd g dims 16 b1 +
+  // 4 (g - 1) .. + 7
+  uint16_t* orow = out + ((int64_t)h * Nq + t) * D;
+  const bool odd = (g & 1) != 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int b = 0; b < NB; b += 2) ow[(i * NB + b) / 2] = pack_bf16x2(acc[b][i] * inv, acc[b + 1][i] * inv);
-  uint16_t* orow = out + ((int64_t)h * Nq + t) * D + 4 * NB * g;
-#pragma unroll
-  for (int j = 0; j < NB / 2; ++j)
-    reinterpret_cast<uint4*>(orow)[j] = make_uint4(ow[4 * j], ow[4 * j + 1], ow[4 * j + 2], ow[4 * j + 3]);
+  for (int m = 0; m < NB / 2; ++m) {
+    const uint2 w0 = make_uint2(pack_bf16x2(acc[2 * m][0] * inv, acc[2 * m][1] * inv),
+                                pack_bf16x2(acc[2 * m][2] * inv, acc[2 * m][3] * inv));
+    const uint2 w1 = make_uint2(pack_bf16x2(acc[2 * m + 1][0] * inv, acc[2 * m + 1][1] * inv),
+                                pack_bf16x2(acc[2 * m + 1][2] * inv, acc[2 * m + 1][3] * inv));
+    const uint2 snd = odd ? w0 : w1;
+    const uint2 rcv = make_uint2(xor16_word(snd.x), xor16_word(snd.y));
+    const uint4 o = odd ? make_uint4(rcv.x, rcv.y, w1.x, w1.y) : make_uint4(w0.x, w0.y, rcv.x, rcv.y);
+    *reinterpret_cast<uint4*>(orow + (odd ? 16 * (2 * m + 1) + 4 * (g - 1) : 32 * m + 4 * g)) = o;
+  }
   if (lse && g == 0) lse[(int64_t)h * Nq + t] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
 }
 

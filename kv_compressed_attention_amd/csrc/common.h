@@ -89,6 +89,12 @@ __device__ __forceinline__ f32x2_t pair_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return (f32x2_t){__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
+// the value of lane l ^ 16 (either word of the swap may be this lane's own
+// value; where both words are equal, they are the partner's as well)
+__device__ __forceinline__ uint32_t xor16_word(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return r[0] == v ? r[1] : r[0];
+}
 __device__ __forceinline__ float max_xor16(float v) { const f32x2_t p = pair_xor16(v); return fmaxf(p.x, p.y); }
 __device__ __forceinline__ float max_xor32(float v) { const f32x2_t p = pair_xor32(v); return fmaxf(p.x, p.y); }
 __device__ __forceinline__ float sum_xor16(float v) { const f32x2_t p = pair_xor16(v); return p.x + p.y; }
