@@ -296,6 +296,11 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       bool use = rn0 > 0u && rlo0 < kc + 32u && rlo0 + rn0 > kc;
       if (P == 2) use = use || (rn1 > 0u && rlo1 < kc + 32u && rlo1 + rn1 > kc);
       if (!ballot64(use)) return;
+      // list and dense mode (every row's range is the whole list): a chunk
+      // with all its slots inside every row's range needs no per-score masks
+      // (in bucket mode the test costs more than it saves)
+      bool whole = false;
+      if (MODE != 0) whole = ballot64(!(kc - rlo0 < rn0 && kc + 31u - rlo0 < rn0)) == 0ull;
       float s[8];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -322,12 +327,17 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
         for (int cc = 0; cc < NC; ++cc)
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[cc], qop[cc], sacc, 0, 0, 0);
         // sacc[i] = score(list slot 32c + 16 hf + 4 g + i, row col)
+        if (whole) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t j = kc + (uint32_t)(16 * hf + 4 * g + i);
-          bool in = j - rlo0 < rn0;
-          if (P == 2) in = in || j - rlo1 < rn1;
-          s[4 * hf + i] = in ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
+          for (int i = 0; i < 4; ++i) s[4 * hf + i] = sacc[i] * scale_log2 + bias[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t j = kc + (uint32_t)(16 * hf + 4 * g + i);
+            bool in = j - rlo0 < rn0;
+            if (P == 2) in = in || j - rlo1 < rn1;
+            s[4 * hf + i] = in ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
+          }
         }
       }
       float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
