@@ -374,7 +374,8 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       // (slots 0..3, then 4..7).  Such a read hands lane 16g + a element
       // a % 4 of the 8 bytes that lane 16g + 4e + a / 4 addresses, as its
       // element e; so this lane addresses row 4 (l >> 4) + ((l >> 2) & 3)
-      // (plus 16), dims 16 bb + 4 (l & 3) .. + 3.
+      // (plus 16, which has the same swizzle), dims 16 bb + 4 (l & 3) .. + 3.
+      static_assert(16 % kPieces == 0, "rows r and r + 16 share their piece swizzle");
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
         const int piece = 2 * bb + ((l & 3) >> 1);
