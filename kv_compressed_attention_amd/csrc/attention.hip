@@ -14,10 +14,12 @@
 // the row's own ranges, so small buckets share chunks.  Per chunk:
 //   the chunk's 32 K and V rows and 32 biases go from HBM to LDS with the
 //   16-byte direct loads (double-buffered: chunk c + 1 loads while chunk c
-//   is computed), K rows stored with their 16-byte pieces XOR-swizzled;
+//   is computed), K and V rows stored with their 16-byte pieces
+//   XOR-swizzled;
 //   S^T[32 slots x 16 rows] = K Q^T   two groups of d/32
-//                                      v_mfma_f32_16x16x32_bf16 (a half-chunk
-//                                      no row of the wave uses is skipped);
+//                                      v_mfma_f32_16x16x32_bf16 (a chunk no
+//                                      row of the wave uses is skipped; in
+//                                      list and dense mode also such a half);
 //   online softmax in float32 with exp2, row max shared by the 4 lanes of a
 //   row;
 //   O^T[d x 16 rows] += V^T P^T       d/16 MFMAs.  P^T comes out of S^T's
@@ -304,11 +306,13 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       float s[8];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        // a half of the chunk none of the wave's rows uses: no scores
+        // list and dense mode: a half of the chunk none of the wave's rows
+        // uses gets no scores (in bucket mode the test costs more than the
+        // MFMAs it saves; the masks below leave such a half at -inf)
         const uint32_t ka = kc + (uint32_t)(16 * hf);
         bool uh = rn0 > 0u && rlo0 < ka + 16u && rlo0 + rn0 > ka;
         if (P == 2) uh = uh || (rn1 > 0u && rlo1 < ka + 16u && rlo1 + rn1 > ka);
-        if (!ballot64(uh)) {
+        if (MODE != 0 && !ballot64(uh)) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[4 * hf + i] = -INFINITY;
           continue;
