@@ -281,18 +281,29 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
                                          (__attribute__((address_space(3))) void*)(bt + 8 * wave), 4, 0, 0);
     };
     const int nch = (total + 31) / 32;
-    int key[kDmaPerWave + 1];
+    int key[kDmaPerWave + 1], key1[kDmaPerWave + 1];
     // chunk c, computed from the tiles kt, vt, bt while chunk c + 1 loads
     // into the other buffers (kn, vn, bn)
     auto chunk = [&](int c, const uint16_t* kt, const uint16_t* vt, const float* bt, uint16_t* kn,
                      uint16_t* vn, float* bn) {
-      // chunk c's rows (this wave's loads) and chunk c + 1's keys have landed;
-      // after the barrier every wave's loads of chunk c have, and every wave
-      // is done with chunk c - 1, whose buffers chunk c + 1 takes
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __syncthreads();
-      if (c + 1 < nch) chunk_load(key, kn, vn, bn);
-      if (c + 2 < nch) chunk_keys(c + 2, key);
+      if (c == 0) {
+        // chunk 0's rows have landed (chunk 1's, requested right behind them
+        // while both buffers were free, and chunk 2's keys may still be in
+        // flight: at least 2 kDmaPerWave requests were issued after them)
+        static_assert(2 * kDmaPerWave < 16, "vmcnt immediate");
+        if (nch > 1) __builtin_amdgcn_s_waitcnt(kWaitVm0 | (2 * kDmaPerWave));
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      } else {
+        // chunk c's rows (this wave's loads) and chunk c + 1's keys have
+        // landed; after the barrier every wave's loads of chunk c have, and
+        // every wave is done with chunk c - 1, whose buffers chunk c + 1 takes
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __syncthreads();
+        if (c + 1 < nch) chunk_load(key, kn, vn, bn);
+        if (c + 2 < nch) chunk_keys(c + 2, key);
+      }
       const uint32_t kc = (uint32_t)(32 * c);
       // skip a chunk none of the wave's rows uses
       bool use = rn0 > 0u && rlo0 < kc + 32u && rlo0 + rn0 > kc;
@@ -393,9 +404,16 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       }
     };
     if (nch > 0) {
+      // chunks 0 and 1 into the two (free) buffers back to back, then chunk
+      // 2's keys; chunk 1's keys are requested before chunk 0's rows so that
+      // waiting for them does not wait for those rows
       chunk_keys(0, key);
+      if (nch > 1) chunk_keys(1, key1);
       chunk_load(key, ktA, vtA, btA);
-      if (nch > 1) chunk_keys(1, key);
+      if (nch > 1) {
+        chunk_load(key1, ktB, vtB, btB);
+        if (nch > 2) chunk_keys(2, key);
+      }
     }
     for (int c = 0; c < nch; c += 2) {
       chunk(c, ktA, vtA, btA, ktB, vtB, btB);
