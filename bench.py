@@ -1,37 +1,43 @@
 """Benchmark of one attention layer's FAST-AR hot path on one MI355X.
 
-A step is one chunk of the per-layer sequence on the layer workload (12 heads,
-d=128, 4680 queries = 3 frames x 1560 tokens, a 6-frame KV cache, 12 hash
-bits, one probe, bf16): hash the queries and build their bucket index, hash
-the chunk's 3 new frames of keys, TempCache-merge them frame by frame into the
-compressed cache of the first 3 frames and index the representatives, then
-AnnSA bucket attention of the queries over the compressed cache with the
-+ ln m bias.  The merge works in place, so each of the K timed steps merges
-into a resident copy of the pre-chunk cache of its own (made before the timed
-region); after the run the K merged caches are checked to be identical.
+Default workload: the wide world-model shape (24 heads, d = 128, a chunk of
+4 frames x 2048 tokens = 8192 queries, a 16-frame KV cache, 14 hash bits,
+two probes per query, a 512-token prompt, bf16).  A step is one chunk of the
+whole per-layer sequence, one fastar_chunk call: hash the queries, the 4 new
+frames' keys and the prompt keys; TempCache-merge the new frames into the
+compressed cache of the first 12 frames and index the representatives;
+index the queries; AnnSA bucket self-attention with the + ln m bias; AnnCA
+prune of the prompt and cross-attention over the kept prompt tokens.
 
-A step is one fastar_chunk call, six launches on one stream: the new keys
-hashed; the merge's index, match (whose extra workgroups hash the queries)
-and apply launches; the representatives' index (whose extra workgroups build
-the queries' index); the attention.  --order picks the older call-by-call
-orders, on one stream or with the query side on a second one.  The steps are captured
-into HIP graphs, --graph-steps of them (each on its own cache) per graph, as
-a model captures the chunks of its layers together, and replayed (--eager
-launches from Python instead, with per-call event times in "stages_ms").
-The attention kernel's duration for the roofline comes from two HIP events
-around K launches of it right after the timed region, captured into one
-graph and replayed on the stream the events are recorded on (so host
-enqueue time stays out of it).
+Cold and hot.  The merge works in place, so every timed step merges into a
+resident copy of the pre-chunk cache of its own (made before the timed
+region; afterwards the K merged caches are checked to be identical, so every
+step did the same work).  In the cold run (the headline) every step also has
+its own copy of the queries, new frames and prompt: one step touches more
+bytes than the 256 MB Infinity Cache holds, so each step starts on inputs no
+recent step has read.  The hot run shares one copy of the inputs between the
+steps.  Steps are captured into HIP graphs, --graph-steps per graph, and
+replayed; the timed region brackets exactly K steps with synchronisation.
 
-Prints one JSON line.  --gpus N with N > 1 is refused: the library has no
-multi-GPU path (heads are independent, so a multi-GPU layer would shard them
-with no collective).
+Kernel durations.  Each stage of the chunk is also captured on its own, K
+launches on the K steps' buffers in one HIP graph, and replayed between two
+HIP events on the stream it runs on; duration = elapsed / K.  Algorithmic
+bytes per launch (from the actual bucket occupancy and merge outcome) over
+that duration give each kernel's fraction of the HBM peak; the roofline
+object is the stage with the largest duration.
+
+Also reported: the oracle on the host's cores (one thread, then one process
+per core over heads; taken before the GPU is first used), the other
+workloads (the layer, AnnCA and rollout shapes; --no-extra skips them), the
+one-bucket (dense, MFMA-bound) attention, and the pages' own end-to-end
+figures for context.  Prints one JSON line.  --gpus N with N > 1 is refused:
+the library has no multi-GPU path (heads are independent, so a multi-GPU
+layer would shard them with no collective).
 """
 
 from __future__ import annotations
 
 import argparse
-import copy
 import json
 import os
 import sys
@@ -46,30 +52,43 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-attention query tokens/s per layer; achieved TFLOP/s vs bf16 MFMA peak"
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+FLUSH_BYTES = 512 << 20   # > the 256 MB Infinity Cache
+
+# The pages' end-to-end figures (another system, other hardware): context only
+PAGES = {
+    "end_to_end_speedup_vs_dense_flashattention3":
+        "up to 5-10x (paperlayer.ai summary, abstract and introduction; the introduction "
+        "states a single H100; precision not stated)",
+    "dense_flashattention3_3000_frames":
+        "about 11 minutes, memory growing throughout (paper.rainbus.top, motivation; "
+        "hardware not stated there)",
+}
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--graph-steps", type=int, default=10,
-                   help="steps captured per HIP graph (each on its own cache, in order, as the "
-                        "chunks of a model's layers are captured together)")
-    p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", type=int, default=1, help="synthetic workload index (1, 3 or 4)")
+                   help="steps captured per HIP graph (each on its own buffers, in order, as "
+                        "the chunks of a model's layers are captured together)")
+    p.add_argument("--workload", type=int, default=4,
+                   help="synthetic workload of the headline (1, 3 or 4; 4 = wide)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true",
                    help="skip the one-bucket (dense, MFMA-bound) attention measurement")
-    p.add_argument("--order", choices=["chunk", "serial", "2stream", "split"], default="chunk",
-                   help="chunk: one fastar_chunk call per step (default); serial: every call on "
-                        "one stream; 2stream: the query index (and AnnCA) on a second stream; "
-                        "split: the query hashing on the second stream as well")
-    p.add_argument("--eager", action="store_true",
-                   help="launch every kernel from Python each step instead of replaying the "
-                        "captured HIP graphs (per-stage event times, host-launch bound)")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the layer, AnnCA and rollout workloads")
+    p.add_argument("--no-hot", action="store_true", help="skip the hot (shared inputs) run")
+    p.add_argument("--cpu-sample-heads", type=int, default=0,
+                   help="heads of the one-thread oracle sample (0: enough for about 10 s)")
     return p.parse_args()
 
 
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
 def attention_work(q_ids, rep_off, n_bits, H, nq, d, P):
     """Algorithmic bytes and flops of one self-attention launch.
 
@@ -86,56 +105,332 @@ def attention_work(q_ids, rep_off, n_bits, H, nq, d, P):
         occ = np.zeros(nb, dtype=bool)
         occ[q_ids[h].reshape(-1)] = True
         kv_keys += int(seg[h][occ].sum())
-        pairs += int(seg[h][q_ids[h]].sum())
+        ids = q_ids[h].reshape(nq, -1)
+        # keys of the distinct probe buckets of each query
+        same = ids[:, 1:] == ids[:, :1] if ids.shape[1] > 1 else np.zeros((nq, 0), bool)
+        pairs += int(seg[h][ids[:, 0]].sum())
+        if ids.shape[1] > 1:
+            pairs += int(seg[h][ids[:, 1]][~same[:, 0]].sum())
     qo = H * nq * (2 * d * 2 + 4 + 4 * P + 4)
     kv = kv_keys * (2 * d * 2 + 4 + 4)
     return qo + kv, 4 * d * pairs, pairs
 
 
-def cpu_baseline(w, min_seconds=10.0, max_reps=20):
-    """Time the oracle on the whole chunk (all heads), repeated to >= min_seconds.
+def cross_work(n_kept, H, nq, npr, d):
+    """Bytes and flops of the cross-attention over the kept prompt tokens
+    (Q, O and lse per query; the kept keys' K and V rows and list entries
+    once per head) and of the prune (query ids, prompt ids, mask, list)."""
+    kept = int(np.sum(n_kept))
+    att_bytes = H * nq * (2 * d * 2 + 4) + kept * (2 * d * 2 + 4)
+    flops = 4 * d * nq * kept
+    return att_bytes, flops
 
-    The set-up merges that build the pre-chunk cache are not timed.
-    Returns (seconds per chunk, repetitions).
-    """
+
+def merge_work(n_before, n_after, group_of_new, H, F, T, d, s=2):
+    """Algorithmic bytes of one merge call of F frames (all heads), from its
+    outcome: the new frames' keys and values read; the previous frame's
+    keys (the candidates of frame 0) read once; per group the call touches
+    (every frontier group a chunk token extends, and every new group) its
+    float32 value sum read (if it existed) and written, its mean value and
+    key written, its count, ln count and bucket; each token's bucket read and
+    group written, and the frontier written."""
+    total = 0
+    for h in range(H):
+        g = group_of_new[h]
+        ext = np.unique(g[(g >= 0) & (g < n_before[h])]).size
+        new = int(n_after[h] - n_before[h])
+        total += F * T * (2 * d * s + 8) + T * d * s + T * 4
+        total += ext * (2 * 4 * d + 2 * d * s + 12) + new * (4 * d + 2 * d * s + 12)
+    return total
+
+
+def hash_work(rows, d, P, s=2):
+    return rows * (d * s + 4 * P)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host's cores (before the GPU is touched)
+# ---------------------------------------------------------------------------
+_CPU_W = None
+
+
+def _oracle_chunk_head(h):
+    """The chunk's sequence for head h: set-up merges untimed, then hash,
+    merge, index, self-attention, prune and cross-attention timed.
+    Returns seconds."""
     import oracle
     from threadpoolctl import threadpool_limits
 
+    w = _CPU_W
     with threadpool_limits(limits=1):
-        setup = []
-        for h in range(w.heads):
-            tc = oracle.TempCacheOracle(w.dim, w.dtype)
-            for f in range(w.setup_frames):
-                kf = w.k_frames[h, f].astype(np.float64)
-                tc.merge_frame(kf, w.v_frames[h, f], oracle.simhash(kf, w.planes, 1)[:, 0], w.tau)
-            setup.append(tc)
-        total, reps = 0.0, 0
-        while reps < max_reps and (total < min_seconds or reps == 0):
-            states = [copy.deepcopy(tc) for tc in setup]
-            t0 = time.perf_counter()
-            for h in range(w.heads):
-                tc = states[h]
-                q = w.q[h].astype(np.float64)
-                q_ids = oracle.simhash(q, w.planes, w.n_probes)
-                oracle.bucket_index(q_ids, w.n_bits)
-                for f in range(w.setup_frames, w.n_frames):
-                    kf = w.k_frames[h, f].astype(np.float64)
-                    tc.merge_frame(kf, w.v_frames[h, f], oracle.simhash(kf, w.planes, 1)[:, 0],
-                                   w.tau)
-                oracle.bucket_index(tc.rep_bucket, w.n_bits)
-                oracle.bucket_attention(q, q_ids, tc.rep_k, tc.v_mean, tc.rep_bucket,
-                                        bias=tc.log_count)
-            total += time.perf_counter() - t0
-            reps += 1
-    return total / reps, reps
+        tc = oracle.TempCacheOracle(w.dim, w.dtype)
+        for f in range(w.setup_frames):
+            kf = w.k_frames[h, f].astype(np.float64)
+            tc.merge_frame(kf, w.v_frames[h, f], oracle.simhash(kf, w.planes, 1)[:, 0], w.tau)
+        t0 = time.perf_counter()
+        q = w.q[h].astype(np.float64)
+        q_ids = oracle.simhash(q, w.planes, w.n_probes)
+        oracle.bucket_index(q_ids, w.n_bits)
+        for f in range(w.setup_frames, w.n_frames):
+            kf = w.k_frames[h, f].astype(np.float64)
+            tc.merge_frame(kf, w.v_frames[h, f], oracle.simhash(kf, w.planes, 1)[:, 0], w.tau)
+        oracle.bucket_index(tc.rep_bucket, w.n_bits)
+        oracle.bucket_attention(q, q_ids, tc.rep_k, tc.v_mean, tc.rep_bucket, bias=tc.log_count)
+        if w.prompt_k is not None:
+            pk = w.prompt_k[h].astype(np.float64)
+            p_ids = oracle.simhash(pk, w.planes, 1)[:, 0]
+            _, kept = oracle.prune_prompt(q_ids, p_ids)
+            oracle.cross_attention(q, pk, w.prompt_v[h], kept)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, sample_heads=0):
+    """Oracle time per chunk (all heads), one thread and all cores.
+
+    One thread: `sample_heads` heads in this process (default: as many as
+    take about 10 s, at least one), scaled to all heads.  All cores: one
+    process per core (fork, at most 16: the host share of one GPU), each
+    running one head; the slowest head's time, scaled by heads / processes.
+    """
+    import multiprocessing as mp
+
+    global _CPU_W
+    _CPU_W = w
+    H = w.heads
+    t1 = [_oracle_chunk_head(0)]
+    n1 = sample_heads or max(1, min(H, int(10.0 / max(t1[0], 1e-3))))
+    for h in range(1, n1):
+        t1.append(_oracle_chunk_head(h))
+    one = float(np.mean(t1)) * H
+    host = os.cpu_count() or 1
+    procs = max(1, min(host, 16, H))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs) as pool:
+        tp = pool.map(_oracle_chunk_head, list(range(procs)))
+    allc = max(tp) * H / procs
+    return {"one_thread_s_per_chunk": one, "one_thread_heads": n1,
+            "all_cores_s_per_chunk": allc, "processes": procs, "host_cpus": host}
+
+
+# ---------------------------------------------------------------------------
+# GPU helpers
+# ---------------------------------------------------------------------------
+def graph_time(fns, before=None, reps=1):
+    """Capture the callables fns (in order) into one HIP graph, replay it once
+    (warm-up), then time `reps` replays between two events on the current
+    stream; returns ms per callable.  before(): untimed work before each
+    replay (e.g. restoring in-place state)."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fns:
+            fn()
+    if before:
+        before()
+    g.replay()
+    torch.cuda.synchronize()
+    total = 0.0
+    for _ in range(reps):
+        if before:
+            before()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    del g
+    return total / reps / len(fns)
+
+
+class Setup:
+    """A workload's layer, its pre-chunk cache, and per-step copies."""
+
+    def __init__(self, w, dev, steps, rotate):
+        import kv_compressed_attention_amd as fa
+        from kv_compressed_attention_amd.layer import FastARLayer
+
+        self.w, self.dev = w, dev
+        H, F, T, d = w.k_frames.shape
+        self.H, self.F, self.T, self.d = H, F, T, d
+        self.tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        npr = 0 if w.prompt_k is None else w.prompt_k.shape[1]
+        self.npr = npr
+        self.layer = FastARLayer(H, d, w.n_bits, w.n_probes, w.tau, T, F * T, w.n_queries,
+                                 w.chunk_frames, n_prompt=npr, dtype=self.tdt, device=dev)
+        self.layer.set_planes(self.up(w.planes))
+        for f in range(w.setup_frames):
+            self.layer.merge(self.up(w.k_frames[:, f]), self.up(w.v_frames[:, f]), 1,
+                             with_index=False)
+        q = self.up(w.q)
+        k_new, v_new = (self.up(a) for a in w.frames(w.setup_frames, F))
+        pk = self.up(w.prompt_k) if npr else None
+        pv = self.up(w.prompt_v) if npr else None
+        torch.cuda.synchronize()
+        self.pristine = self.layer.cache
+        self.caches = []
+        for _ in range(steps):
+            c = fa.TempCache(H, d, F * T, T, w.n_bits, self.tdt, dev)
+            c.copy_from(self.pristine)
+            self.caches.append(c)
+        self.scratch = fa.TempCache(H, d, F * T, T, w.n_bits, self.tdt, dev)
+
+        def clone(t):
+            return None if t is None else t.clone()
+        n_in = steps if rotate else 1
+        self.inputs = [(q, k_new, v_new, pk, pv)] + [
+            tuple(clone(t) for t in (q, k_new, v_new, pk, pv)) for _ in range(n_in - 1)]
+        torch.cuda.synchronize()
+
+    def up(self, a):
+        return torch.tensor(np.ascontiguousarray(a), dtype=torch.float32,
+                            device=self.dev).to(self.tdt)
+
+    def inp(self, i):
+        return self.inputs[i % len(self.inputs)]
+
+    def restore(self):
+        for c in self.caches:
+            c.copy_from(self.pristine)
+
+    def step(self, i, cache=None):
+        q, k, v, pk, pv = self.inp(i)
+        self.layer.step(q, k, v, pk, pv, cache=self.caches[i] if cache is None else cache)
+
+    def check_steps_agree(self):
+        """Every timed step did the same work: the caches it merged into agree."""
+        ref = self.caches[0]
+        for c in self.caches[1:]:
+            for n, t in c.buffers().items():
+                if not torch.equal(t, ref.buffers()[n]):
+                    raise RuntimeError(f"timed steps disagree on the merged cache ({n})")
+
+
+def timed_steps(st, steps, warmup, graph_steps):
+    """Warm up, capture the K steps into graphs of graph_steps, then the timed
+    region: exactly K steps (graph replays) bracketed by synchronisation.
+    Returns wall seconds of the timed region."""
+    for i in range(warmup):
+        st.scratch.copy_from(st.pristine)
+        st.step(i, cache=st.scratch)
+    torch.cuda.synchronize()
+    G = max(1, graph_steps)
+    graphs = []
+    for i0 in range(0, steps, G):
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(i0, min(steps, i0 + G)):
+                st.step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    # the captures merged nothing; the caches are still pristine
+    t0 = time.perf_counter()
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st.check_steps_agree()
+    del graphs
+    return wall
+
+
+def stage_times(st, steps):
+    """Each stage of the chunk on its own (cold: step i's buffers), K
+    launches per graph; ms per launch, plus the algorithmic work."""
+    import kv_compressed_attention_amd.fastar as fb
+
+    L, w = st.layer, st.w
+    H, d = st.H, st.d
+    idx = list(range(steps))
+    out = {}
+
+    def run(name, make, before=None):
+        out[name] = graph_time([make(i) for i in idx], before=before)
+
+    run("hash_keys_prompt", lambda i: (lambda: fb.fastar_hash_multi(
+        [st.inp(i)[1]] + ([st.inp(i)[3]] if st.npr else []), L.planes, w.n_bits,
+        [1] + ([1] if st.npr else []), buckets=[L.k_ids] + ([L.p_ids] if st.npr else []),
+        diag=L.diag)))
+    run("hash_queries", lambda i: (lambda: fb.fastar_hash_multi(
+        [st.inp(i)[0]], L.planes, w.n_bits, [w.n_probes], buckets=[L.q_ids], diag=L.diag)))
+    run("index_queries", lambda i: (lambda: fb.fastar_bucket_index(
+        L.q_ids, w.n_bits, offsets=L.q_off, perm=L.q_perm, ws=L.ws_q)))
+    # the merge is in place: the caches are restored before each replay
+    run("merge", lambda i: (lambda: fb.fastar_tempcache_merge(
+        st.caches[i], st.inp(i)[1], st.inp(i)[2], L.k_ids.view(H, -1), w.chunk_frames, w.tau,
+        group_of_new=L.group_of_new, rep_offsets=L.rep_off, rep_perm=L.rep_perm, ws=L.ws,
+        diag=L.diag)), before=st.restore)
+    n_before = st.pristine.n_groups.cpu().numpy()
+    n_after = st.caches[-1].n_groups.cpu().numpy()
+    gon = L.group_of_new.cpu().numpy()
+    run("attention_self", lambda i: (lambda: fb.fastar_bucket_attention(
+        st.inp(i)[0], st.caches[i].rep_k, st.caches[i].v_mean, q_bucket=L.q_ids, q_perm=L.q_perm,
+        key_bias=st.caches[i].log_count, k_offsets=L.rep_off, k_perm=L.rep_perm,
+        n_bits=w.n_bits, out=L.o_self, lse=L.lse_self)))
+    if st.npr:
+        run("prune", lambda i: (lambda: fb.fastar_prune_prompt(
+            L.q_ids, L.p_ids.view(H, -1), w.n_bits, keep=L.keep, kept_idx=L.kept_idx,
+            n_kept=L.n_kept)))
+        run("attention_cross", lambda i: (lambda: fb.fastar_bucket_attention(
+            st.inp(i)[0], st.inp(i)[3], st.inp(i)[4], key_list=L.kept_idx, n_key_list=L.n_kept,
+            out=L.o_cross, lse=L.lse_cross)))
+    torch.cuda.synchronize()
+
+    nq, P, T, Fc = w.n_queries, w.n_probes, st.T, w.chunk_frames
+    q_ids = L.q_ids.cpu().numpy()
+    rep_off = L.rep_off.cpu().numpy()
+    a_bytes, a_flops, pairs = attention_work(q_ids, rep_off, w.n_bits, H, nq, d, P)
+    kern = {}
+
+    def put(name, nbytes, flops=None, kernel=""):
+        ms = out[name]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        e = {"kernel": kernel, "launch_ms": ms, "bytes_per_launch": int(nbytes), "achieved_gbs": gbs,
+             "frac_hbm": gbs / PEAK_HBM_GBS}
+        if flops is not None:
+            e["tflops"] = flops / (ms * 1e-3) / 1e12
+        kern[name] = e
+
+    put("attention_self", a_bytes, a_flops, "attn_bf16_kernel<128, P, 0> (bucket mode)")
+    put("hash_keys_prompt", hash_work(H * (Fc * T + st.npr), d, 1), None, "hash_bf16_kernel<128>")
+    put("hash_queries", hash_work(H * nq, d, P), None, "hash_bf16_kernel<128>")
+    put("index_queries", H * nq * (4 * P + 4) + H * ((1 << w.n_bits) + 1) * 4, None,
+        "bucket index of the queries")
+    m_bytes = merge_work(n_before, n_after, gon, H, Fc, T, d)
+    m_bytes += int(n_after.sum()) * 8 + H * ((1 << w.n_bits) + 1) * 4   # the representatives' index
+    put("merge", m_bytes, None, "tc_index + tc_match + tc_apply + representatives' index")
+    extra = {"attended_pairs": pairs, "compressed_keys_per_head_max": int(n_after.max()),
+             "compressed_keys_per_head_mean": float(n_after.mean())}
+    if st.npr:
+        n_kept = L.n_kept.cpu().numpy()
+        c_bytes, c_flops = cross_work(n_kept, H, nq, st.npr, d)
+        put("attention_cross", c_bytes, c_flops, "attn_bf16_kernel<128, 1, 1> (key-list mode)")
+        put("prune", H * nq * 4 * P + H * st.npr * (4 + 1 + 4) + H * 4, None, "prune")
+        extra["prompt_kept_per_head_mean"] = float(n_kept.mean())
+        extra["prompt_prune_ratio"] = 1.0 - float(n_kept.mean()) / st.npr
+    return kern, extra
+
+
+def flushed_chunk_ms(st, flush, i):
+    """One eager chunk on step i's buffers after a 512 MB write (the
+    Infinity Cache flushed, and the GPU busy while the host enqueues), timed
+    between two events."""
+    flush.zero_()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    st.step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
 
 
 def dense_one_bucket(dev, reps: int = 5):
     """The attention kernel with all keys in one bucket (dense mode) at the
     rollout size: 12 heads, 4680 queries, 23,400 keys, d = 128, bf16, seeded
     normal inputs.  Every query meets every key, so the kernel is bound by
-    its MFMA work and its fraction of the bf16 peak measures MFMA quality.
-    reps launches in one HIP graph, replayed between two events."""
+    its MFMA work and its fraction of the bf16 peak measures MFMA quality."""
     import kv_compressed_attention_amd as fa
     from synth import gaussian
 
@@ -148,42 +443,154 @@ def dense_one_bucket(dev, reps: int = 5):
         up(gaussian((H, nk, d), 503, "bf16"))
     out = torch.empty(H, nq, d, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(H, nq, dtype=torch.float32, device=dev)
-    fa.fastar_bucket_attention(q, k, v, out=out, lse=lse)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for _ in range(reps):
-            fa.fastar_bucket_attention(q, k, v, out=out, lse=lse)
-    graph.replay()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record()
-    graph.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / reps
+    ms = graph_time([lambda: fa.fastar_bucket_attention(q, k, v, out=out, lse=lse)] * reps)
     tflops = 4.0 * d * nq * nk * H / (ms * 1e-3) / 1e12
     return {"workload": f"one_bucket_bf16_h{H}_d{d}_q{nq}_k{nk}", "bound": "mfma", "launch_ms": ms,
             "tflops": tflops, "frac_bf16_mfma_peak": tflops / PEAK_BF16_TFLOPS}
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per attention launch from the committed counter passes, if
-    they were taken on this workload with the current attention sources
-    (else None)."""
+def recorded_traffic(workload: str, kernel_file: str):
+    """HBM bytes per launch of the roofline kernel from the committed counter
+    passes, if they were taken on this workload with the current sources of
+    that kernel (else None)."""
     import glob
     import hashlib
     import re
 
     src = b"".join(open(os.path.join(ROOT, "kv_compressed_attention_amd", "csrc", f), "rb").read()
-                   for f in ("attention.hip", "common.h"))
+                   for f in (kernel_file, "common.h"))
     digest = hashlib.sha256(src).hexdigest()[:16]
-    for path in glob.glob(os.path.join(ROOT, "profiles", "attn_bf16_*.md")):
-        m = re.search(r"traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]+) workload=(\S+)",
-                      open(path).read())
-        if m and m.group(2) == digest and m.group(3) == workload:
-            return int(m.group(1))
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        for m in re.finditer(r"traffic_bytes_per_launch=(\d+) source_sha256=([0-9a-f]+) workload=(\S+)",
+                             open(path).read()):
+            if m.group(2) == digest and m.group(3) == workload:
+                return int(m.group(1))
     return None
+
+
+KERNEL_FILES = {"attention_self": "attention.hip", "attention_cross": "attention.hip",
+                "hash_keys_prompt": "hash.hip", "hash_queries": "hash.hip",
+                "merge": "tempcache.hip", "index_queries": "index.hip", "prune": "prune.hip"}
+
+
+def measure_workload(w, dev, steps, warmup, graph_steps, hot=True):
+    """Cold (rotated inputs) and, optionally, hot chunk steps plus per-stage
+    kernel times of workload w."""
+    st = Setup(w, dev, steps, rotate=True)
+    res = {"cold_s": timed_steps(st, steps, warmup, graph_steps)}
+    if hot:
+        st_hot_inputs = st.inputs
+        st.inputs = st.inputs[:1]
+        st.restore()
+        res["hot_s"] = timed_steps(st, steps, warmup, graph_steps)
+        st.inputs = st_hot_inputs
+    st.restore()
+    res["kernels"], res["extra"] = stage_times(st, steps)
+    res["diag"] = st.layer.diag.tolist()
+    res["setup"] = st
+    return res
+
+
+def rollout(w, dev, flush):
+    """The rollout workload as a stream of chunks from an empty cache: every
+    3 frames one fastar_chunk (queries: the workload's 4680, the chunk
+    sequence's shape), each timed cold (after a 512 MB write) between two
+    events; per chunk the time, the compressed keys per head, the density
+    (compressed keys / raw keys so far) and the compressed cache's bytes."""
+    from kv_compressed_attention_amd.layer import FastARLayer
+
+    H, F, T, d = w.k_frames.shape
+    tdt = torch.bfloat16
+    layer = FastARLayer(H, d, w.n_bits, w.n_probes, w.tau, T, F * T, w.n_queries, 3,
+                        dtype=tdt, device=dev)
+
+    def up(a):
+        return torch.tensor(np.ascontiguousarray(a), dtype=torch.float32, device=dev).to(tdt)
+    layer.set_planes(up(w.planes))
+    q = up(w.q)
+    chunks = [tuple(up(a) for a in w.frames(3 * c, 3 * c + 3)) for c in range(F // 3)]
+    # the calls' argument blocks are built before the timed calls
+    for k, v in chunks:
+        layer._chunk_call(q, k, v, None, None, layer.cache)
+    torch.cuda.synchronize()
+    group_bytes = 2 * d * 2 + 4 * d + 4 + 4 + 4      # key, mean, float32 sum, count, ln m, bucket
+    out = []
+    for c, (k, v) in enumerate(chunks):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.step(q, k, v)
+        e1.record()
+        torch.cuda.synchronize()
+        ng = layer.cache.n_groups.cpu().numpy()
+        out.append({"chunk": c, "frames": 3 * c + 3, "ms": e0.elapsed_time(e1),
+                    "keys_per_head": float(ng.mean()),
+                    "density": float(ng.mean()) / (3 * (c + 1) * T),
+                    "cache_mb": float(ng.sum()) * group_bytes / 1e6})
+    if layer.cache.status_code() != 0:
+        raise RuntimeError("rollout cache overflowed")
+    return out
+
+
+def annca(w, dev, steps):
+    """The AnnCA workload: hash the queries and the prompt, prune, and
+    cross-attention over the kept prompt keys; per-call times (cold: one
+    copy of the inputs per step) and the prune ratio."""
+    import kv_compressed_attention_amd.fastar as fb
+
+    H, nq, d = w.q.shape
+    npr = w.prompt_k.shape[1]
+    tdt = torch.bfloat16
+
+    def up(a):
+        return torch.tensor(np.ascontiguousarray(a), dtype=torch.float32, device=dev).to(tdt)
+    planes = up(w.planes)
+    ins = [(up(w.q), up(w.prompt_k), up(w.prompt_v))]
+    ins += [tuple(t.clone() for t in ins[0]) for _ in range(steps - 1)]
+    i32 = dict(dtype=torch.int32, device=dev)
+    q_ids, p_ids = torch.empty(H, nq, 1, **i32), torch.empty(H, npr, 1, **i32)
+    keep = torch.empty(H, npr, dtype=torch.uint8, device=dev)
+    kept, n_kept = torch.empty(H, npr, **i32), torch.empty(H, **i32)
+    o, lse = torch.empty(H, nq, d, dtype=tdt, device=dev), torch.empty(H, nq, device=dev)
+
+    def hash_(i):
+        return lambda: fb.fastar_hash_multi([ins[i][0], ins[i][1]], planes, w.n_bits, [1, 1],
+                                            buckets=[q_ids, p_ids])
+
+    def prune(i):
+        return lambda: fb.fastar_prune_prompt(q_ids, p_ids.view(H, -1), w.n_bits, keep=keep,
+                                              kept_idx=kept, n_kept=n_kept)
+
+    def cross(i):
+        return lambda: fb.fastar_bucket_attention(ins[i][0], ins[i][1], ins[i][2], key_list=kept,
+                                                  n_key_list=n_kept, out=o, lse=lse)
+    t_hash = graph_time([hash_(i) for i in range(steps)])
+    t_prune = graph_time([prune(i) for i in range(steps)])
+    t_cross = graph_time([cross(i) for i in range(steps)])
+    t_all = graph_time([f for i in range(steps) for f in (hash_(i), prune(i), cross(i))]) * 3
+    nk = n_kept.cpu().numpy()
+    c_bytes, c_flops = cross_work(nk, H, nq, npr, d)
+    return {"workload": w.name, "prompt_tokens": npr, "kept_per_head_mean": float(nk.mean()),
+            "kept_per_head_min": int(nk.min()), "kept_per_head_max": int(nk.max()),
+            "prune_ratio": 1.0 - float(nk.mean()) / npr,
+            "ms": {"hash_queries_prompt": t_hash, "prune": t_prune, "attention_cross": t_cross,
+                   "all": t_all},
+            "query_tokens_per_s": nq / (t_all * 1e-3),
+            "cross_attention_gbs": c_bytes / (t_cross * 1e-3) / 1e9,
+            "cross_attention_tflops": c_flops / (t_cross * 1e-3) / 1e12}
+
+
+def summarize(w, res, steps):
+    nq = w.n_queries
+    cold_ms = res["cold_s"] * 1e3 / steps
+    d = {"ms_per_step": cold_ms, "query_tokens_per_s": nq / (cold_ms * 1e-3)}
+    if "hot_s" in res:
+        hot_ms = res["hot_s"] * 1e3 / steps
+        d["hot"] = {"ms_per_step": hot_ms, "query_tokens_per_s": nq / (hot_ms * 1e-3)}
+    d["kernels_ms"] = {k: v["launch_ms"] for k, v in res["kernels"].items()}
+    a = res["kernels"]["attention_self"]
+    d["attention_frac_hbm"] = a["frac_hbm"]
+    return d
 
 
 def main():
@@ -192,38 +599,18 @@ def main():
         print("bench.py runs on one GPU only: libfastar has no multi-GPU path (heads are "
               "independent and would shard across GPUs with no collective)", file=sys.stderr)
         sys.exit(2)
-    import kv_compressed_attention_amd as fa
-    from kv_compressed_attention_amd.layer import FastARLayer
     from synth import make_workload
 
-    dev = torch.device("cuda:0")
     w = make_workload(args.workload)
-    H, F, T, d = w.k_frames.shape
-    nq = w.n_queries
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    # the oracle first: its worker processes are forked before this process
+    # touches the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_sample_heads)
 
-    def up(a):
-        return torch.tensor(np.ascontiguousarray(a), dtype=torch.float32, device=dev).to(tdt)
-
-    layer = FastARLayer(H, d, w.n_bits, w.n_probes, w.tau, T, F * T, nq, w.chunk_frames,
-                        dtype=tdt, device=dev)
-    layer.set_planes(up(w.planes))
-    q = up(w.q)
-    for f in range(w.setup_frames):
-        layer.merge(up(w.k_frames[:, f]), up(w.v_frames[:, f]), 1, with_index=False)
-    k_new, v_new = (up(a) for a in w.frames(w.setup_frames, F))
-    torch.cuda.synchronize()
-    # the merge is in place: every timed step gets a resident copy of the
-    # pre-chunk cache of its own, so the K steps are identical work and the
-    # timed region holds only the hot path
-    pristine = layer.cache
-    caches = []
-    for _ in range(args.steps):
-        c = fa.TempCache(H, d, F * T, T, w.n_bits, tdt, dev)
-        c.copy_from(pristine)
-        caches.append(c)
-    scratch = fa.TempCache(H, d, F * T, T, w.n_bits, tdt, dev)
-
+    import kv_compressed_attention_amd as fa
+    dev = torch.device("cuda:0")
+    fa.library()
     # a plain 64 MiB device copy before the timed region: the calibration
     # kernel for the FETCH_SIZE / WRITE_SIZE counter passes
     cal_src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
@@ -231,70 +618,17 @@ def main():
     cal_dst.copy_(cal_src)
     del cal_src, cal_dst
 
-    timing = {}
-    concurrent = {"chunk": "chunk", "serial": False, "2stream": True, "split": "split"}[args.order]
-
-    def warm_step():
-        scratch.copy_from(pristine)
-        layer.step(q, k_new, v_new, cache=scratch, concurrent=concurrent)
-
-    for _ in range(args.warmup):
-        warm_step()
-    torch.cuda.synchronize()
-    if args.eager:
-        def step(i):
-            layer.step(q, k_new, v_new, cache=caches[i], concurrent=concurrent, timing=timing)
-    else:
-        G = max(1, args.graph_steps)
-        graphs = [layer.capture(q, k_new, v_new, concurrent=concurrent, caches=caches[i:i + G])
-                  for i in range(0, args.steps, G)]
-        warm = layer.capture(q, k_new, v_new, cache=scratch, concurrent=concurrent)
-        for _ in range(args.warmup):
-            scratch.copy_from(pristine)
-            warm.replay()
-        torch.cuda.synchronize()
-
-        def step(i):
-            # one graph launch runs steps i .. i + G - 1
-            if i % G == 0:
-                graphs[i // G].replay()
-    # timed region: exactly K steps (eager: with HIP events around the
-    # stages, each recorded on the stream its stage is enqueued on)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    t_enq = time.perf_counter() - t0
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stage_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in v])) for s, v in timing.items()}
-    if "attention" not in stage_ms:
-        # the attention kernel's average launch duration: K launches on the
-        # inputs and buffers of the last timed step, captured in one HIP graph
-        # and replayed between two events on the stream they run on (host
-        # enqueue time, which a per-launch event pair can include, stays out)
-        torch.cuda.synchronize()
-        g_attn = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_attn):
-            for _ in range(args.steps):
-                layer.self_attention(q, None, caches[-1])
-        g_attn.replay()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        g_attn.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        stage_ms["attention"] = ev0.elapsed_time(ev1) / args.steps
-    check_steps_agree(layer, caches)
-
-    ms = wall * 1e3 / args.steps
-    q_ids = layer.q_ids.cpu().numpy()
-    rep_off = layer.rep_off.cpu().numpy()
-    nbytes, flops, pairs = attention_work(q_ids, rep_off, w.n_bits, H, nq, d, w.n_probes)
-    t_att = stage_ms["attention"] * 1e-3
-    achieved_gbs = nbytes / t_att / 1e9
-    tflops = flops / t_att / 1e12
-    ai = flops / nbytes
+    res = measure_workload(w, dev, args.steps, args.warmup, args.graph_steps, hot=not args.no_hot)
+    H, F, T, d = w.k_frames.shape
+    nq = w.n_queries
+    ms = res["cold_s"] * 1e3 / args.steps
+    kern = res["kernels"]
+    dom = max(kern, key=lambda k: kern[k]["launch_ms"])
+    a = kern["attention_self"]
+    t_att = a["launch_ms"] * 1e-3
+    a_bytes = a["bytes_per_launch"]
+    flops = a["tflops"] * 1e12 * t_att
+    ai = flops / a_bytes
     out = {
         "metric": METRIC,
         "value": nq / (ms * 1e-3),
@@ -310,46 +644,75 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "heads": H, "head_dim": d, "queries": nq,
                    "cache_frames": F, "tokens_per_frame": T, "new_frames": w.chunk_frames,
-                   "n_bits": w.n_bits, "n_probes": w.n_probes, "tau": w.tau},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved_gbs / PEAK_HBM_GBS, "traffic": recorded_traffic(w.name),
-                     "kernel": "attn_bf16_kernel (fastar_bucket_attention, bucket mode)",
-                     "bytes_per_launch": nbytes, "launch_ms": stage_ms["attention"]},
-        "attention": {"tflops": tflops, "frac_bf16_mfma_peak": tflops / PEAK_BF16_TFLOPS,
+                   "n_bits": w.n_bits, "n_probes": w.n_probes, "tau": w.tau,
+                   "prompt_tokens": 0 if w.prompt_k is None else int(w.prompt_k.shape[1]),
+                   "inputs": "cold: every step on its own copy of the inputs and cache"},
+        "roofline": {"bound": "hbm", "achieved": kern[dom]["achieved_gbs"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": kern[dom]["frac_hbm"],
+                     "traffic": recorded_traffic(w.name + ":" + dom, KERNEL_FILES[dom]),
+                     "kernel": f"{dom}: {kern[dom]['kernel']}",
+                     "bytes_per_launch": kern[dom]["bytes_per_launch"],
+                     "launch_ms": kern[dom]["launch_ms"]},
+        "kernels": kern,
+        "attention": {"tflops": a["tflops"], "frac_bf16_mfma_peak": a["tflops"] / PEAK_BF16_TFLOPS,
                       "arith_intensity_flop_per_byte": ai,
                       "roofline_tflops": min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3),
-                      "attended_pairs": pairs,
-                      "query_tokens_per_s": nq / t_att,
-                      "compressed_keys_per_head": ngb_after(layer, caches[-1])},
-        "launch": ("eager" if args.eager else f"hip_graph{max(1, args.graph_steps)}") + "_" + args.order,
-        "stages_ms": stage_ms,
-        "host_enqueue_ms_per_step": t_enq * 1e3 / args.steps,
-        "diag": layer.diag.tolist(),
+                      "frac_of_roofline": a["tflops"] / min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3),
+                      "query_tokens_per_s": nq / t_att, **res["extra"]},
+        "launch": f"hip_graph{max(1, args.graph_steps)}_chunk",
+        "diag": res["diag"],
+        "pages": PAGES,
     }
+    if "hot_s" in res:
+        hms = res["hot_s"] * 1e3 / args.steps
+        out["hot"] = {"ms_per_step": hms, "value": nq / (hms * 1e-3),
+                      "inputs": "one copy of the inputs shared by every step (each still merges "
+                                "into its own cache)"}
+    st = res.pop("setup")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flushed = []
+    for i in range(min(5, args.steps)):
+        st.caches[i].copy_from(st.pristine)
+        flushed.append(flushed_chunk_ms(st, flush, i))
+    out["flushed_chunk_ms"] = float(np.median(flushed))
+    del st, res
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra = {}
+        if args.workload != 1:
+            w1 = make_workload(1)
+            r1 = measure_workload(w1, dev, args.steps, args.warmup, args.graph_steps,
+                                  hot=not args.no_hot)
+            r1.pop("setup")
+            extra[w1.name] = summarize(w1, r1, args.steps)
+            del r1
+            torch.cuda.empty_cache()
+        extra["annca"] = annca(make_workload(2), dev, args.steps)
+        w3 = make_workload(3)
+        roll = rollout(w3, dev, flush)
+        extra["rollout"] = {"workload": w3.name, "chunks": roll,
+                            "first_last_ms": [roll[0]["ms"], roll[-1]["ms"]],
+                            "last_chunk_density": roll[-1]["density"]}
+        del w3
+        torch.cuda.empty_cache()
+        out["extra_workloads"] = extra
     if not args.no_dense:
         out["dense_one_bucket"] = dense_one_bucket(dev)
-    if not args.no_cpu_baseline:
-        per_step, reps = cpu_baseline(w)
-        out["cpu_baseline"] = {"value": nq / per_step, "unit": "query tokens/s", "cores": 1,
-                               "kind": "oracle",
-                               "sample": f"the whole chunk, all {H} heads (hash queries, hash and "
-                                         f"merge {w.chunk_frames} frames, index, bucket "
-                                         f"attention; cache restore not needed), {reps} "
-                                         f"repetitions of {per_step:.2f} s, one thread"}
+    if cpu is not None:
+        out["cpu_baseline"] = {
+            "value": nq / cpu["all_cores_s_per_chunk"], "unit": "query tokens/s",
+            "cores": cpu["processes"], "kind": "oracle",
+            "sample": (f"the whole chunk (hash, merge {w.chunk_frames} frames, index, bucket "
+                       f"self-attention, prune, cross-attention) of {cpu['processes']} heads, "
+                       f"one process per head and core, scaled to all {H} heads; set-up "
+                       f"merges untimed"),
+            "host_cpus": cpu["host_cpus"],
+            "one_thread": {"value": nq / cpu["one_thread_s_per_chunk"], "cores": 1,
+                           "sample": f"{cpu['one_thread_heads']} head(s) in one thread, "
+                                     f"scaled to all {H} heads"},
+        }
     print(json.dumps(out))
-
-
-def ngb_after(layer, cache):
-    return int(cache.n_groups.max().item())
-
-
-def check_steps_agree(layer, caches):
-    """Every timed step did the same work: the caches it merged into agree."""
-    ref = caches[0]
-    for c in caches[1:]:
-        for n, t in c.buffers().items():
-            if not torch.equal(t, ref.buffers()[n]):
-                raise RuntimeError(f"timed steps disagree on the merged cache ({n})")
 
 
 if __name__ == "__main__":

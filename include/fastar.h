@@ -45,7 +45,9 @@ typedef enum {
   FASTAR_ERR_INVALID = 1,      /* bad pointer, size or combination of arguments */
   FASTAR_ERR_UNSUPPORTED = 2,  /* valid request outside what the kernels cover   */
   FASTAR_ERR_WORKSPACE = 3,    /* ws_bytes below what the *_workspace query says */
-  FASTAR_ERR_HIP = 4           /* a HIP launch failed                            */
+  FASTAR_ERR_HIP = 4,          /* a HIP launch failed                            */
+  FASTAR_ERR_CAPACITY = 5      /* a merge dropped groups: the cache was full
+                                  (reported by fastar_cache_status only)          */
 } fastar_status_t;
 
 typedef enum { FASTAR_F32 = 0, FASTAR_BF16 = 1 } fastar_dtype_t;
@@ -149,9 +151,24 @@ fastar_status_t fastar_bucket_index(const int32_t* bucket, int heads, int64_t n,
  *   n_groups   [H]                 int32 groups in use (0 = empty cache)
  *   frontier   [H][tokens_per_frame] int32 group of each token of the last
  *                                  merged frame
- * An empty cache is one with n_groups all 0; nothing else needs clearing.
- * tokens_per_frame must be in [1, 2048]; capacity >= tokens_per_frame.
+ *   status     [1]                 int32 device status word: a merge that has
+ *                                  to drop groups for lack of capacity sets
+ *                                  bit 0 (FASTAR_CACHE_OVERFLOW), whether or
+ *                                  not the call had a diag buffer; nothing
+ *                                  clears it but fastar_cache_status(clear)
+ * An empty cache is one with n_groups all 0 and status 0; nothing else needs
+ * clearing.  tokens_per_frame must be in [1, 2048]; capacity >=
+ * tokens_per_frame.
+ *
+ * Capacity overflow is an error state, not a supported mode: the groups that
+ * do not fit are dropped (group_of_new = -1, and n_groups stays at
+ * capacity), and which groups survive can then depend on how the frames were
+ * split into calls (within one call a dropped frame f - 1 token is still a
+ * candidate of frame f; across calls it is not).  Size the capacity for the
+ * worst case (frames merged times tokens per frame) or check
+ * fastar_cache_status.
  * ---------------------------------------------------------------------- */
+#define FASTAR_CACHE_OVERFLOW 1
 typedef struct {
   int32_t heads, dim, capacity, tokens_per_frame, n_bits, dtype;
   void* rep_k;
@@ -162,7 +179,16 @@ typedef struct {
   int32_t* rep_bucket;
   int32_t* n_groups;
   int32_t* frontier;
+  int32_t* status;
 } fastar_cache_t;
+
+/* fastar_cache_status -- the one call that synchronises: waits for `stream`,
+ * reads the cache's status word and returns FASTAR_ERR_CAPACITY if a merge
+ * since it was last cleared dropped groups, FASTAR_OK otherwise (or
+ * FASTAR_ERR_INVALID / FASTAR_ERR_HIP).  With clear != 0 the word is then
+ * reset to 0 (stream-ordered, also waited for).  Not for use under graph
+ * capture. */
+fastar_status_t fastar_cache_status(const fastar_cache_t* cache, int clear, hipStream_t stream);
 
 /* fastar_tempcache_merge -- merge n_frames new frames, in order.
  *   k_new, v_new  [H][n_frames * tokens_per_frame][dim], cache dtype.

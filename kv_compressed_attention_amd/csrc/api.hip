@@ -1,5 +1,6 @@
 // extern "C" entry points of libfastar: host-side validation, workspace
-// carving and kernel launches.  Nothing here allocates or synchronises.
+// carving and kernel launches.  Nothing here allocates; only
+// fastar_cache_status synchronises.
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -130,7 +131,7 @@ fastar_status_t merge_check(const fastar_cache_t* c, const fastar_tensor_t* k_ne
     return fail(FASTAR_ERR_INVALID, "rep_offsets and rep_perm must both be given or both be NULL");
   if (c->heads == 0 || n_frames == 0) return FASTAR_OK;
   if (!c->rep_k || !c->v_mean || !c->v_sum || !c->count || !c->log_count || !c->rep_bucket ||
-      !c->n_groups || !c->frontier || !k_new_bucket)
+      !c->n_groups || !c->frontier || !c->status || !k_new_bucket)
     return fail(FASTAR_ERR_INVALID, "a cache buffer or k_new_bucket is NULL");
   if (!aligned16(c->rep_k) || !aligned16(c->v_mean) || !aligned16(c->v_sum))
     return fail(FASTAR_ERR_INVALID, "cache rows must be 16-byte aligned");
@@ -238,13 +239,14 @@ const char* fastar_status_string(int status) {
     case FASTAR_ERR_UNSUPPORTED: return "unsupported argument";
     case FASTAR_ERR_WORKSPACE: return "workspace too small";
     case FASTAR_ERR_HIP: return "HIP error";
+    case FASTAR_ERR_CAPACITY: return "cache capacity exceeded";
     default: return "unknown status";
   }
 }
 
 const char* fastar_last_error(void) { return g_err; }
 
-int fastar_version(void) { return 100; }
+int fastar_version(void) { return 200; }
 
 // ---------------------------------------------------------------------------
 size_t fastar_hash_workspace(int heads, int64_t n, int n_bits, int n_probes) {
@@ -355,6 +357,25 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
                                                    group_of_new, rep_offsets, rep_perm,
                                                    merge_carve(c, n_frames, ws), diag, stream),
                     "tempcache_merge");
+}
+
+fastar_status_t fastar_cache_status(const fastar_cache_t* c, int clear, hipStream_t stream) {
+  if (!c || !c->status) return fail(FASTAR_ERR_INVALID, "cache or its status word is NULL");
+  int32_t word = 0;
+  fastar_status_t st = hip_status(hipMemcpyAsync(&word, c->status, sizeof(word), hipMemcpyDeviceToHost, stream),
+                                  "cache_status read");
+  if (st == FASTAR_OK) st = hip_status(hipStreamSynchronize(stream), "cache_status sync");
+  if (st != FASTAR_OK) return st;
+  if (clear) {
+    static const int32_t kZero = 0;
+    st = hip_status(hipMemcpyAsync(c->status, &kZero, sizeof(kZero), hipMemcpyHostToDevice, stream),
+                    "cache_status clear");
+    if (st == FASTAR_OK) st = hip_status(hipStreamSynchronize(stream), "cache_status sync");
+    if (st != FASTAR_OK) return st;
+  }
+  if (word & FASTAR_CACHE_OVERFLOW)
+    return fail(FASTAR_ERR_CAPACITY, "a merge dropped groups: the cache's capacity was exceeded");
+  return FASTAR_OK;
 }
 
 // ---------------------------------------------------------------------------

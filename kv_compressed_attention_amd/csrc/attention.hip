@@ -477,7 +477,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   if (MODE == 0) {
     const int32_t* qb = q_bucket + ((int64_t)h * Nq + t) * P;
     buckets[0] = qb[0];
-    if (P == 2) {
+    // two equal probes name one key set, walked once
+    if (P == 2 && qb[1] != qb[0]) {
       buckets[1] = qb[1];
       nseg = 2;
     }

@@ -1040,7 +1040,7 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
     int32_t* __restrict__ n_groups, int32_t* __restrict__ frontier, int32_t* __restrict__ group_of_new,
     const T* __restrict__ knew, int64_t k_sh, int64_t k_st, const T* __restrict__ vnew,
     int64_t v_sh, int64_t v_st, const int32_t* __restrict__ kbucket, MergeArgs a,
-    fastar_diag_t* __restrict__ diag) {
+    int32_t* __restrict__ status, fastar_diag_t* __restrict__ diag) {
   constexpr int EPL = D / 16;
   const int h = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -1094,7 +1094,11 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
     if (sub != 0) return;
     if (group_of_new) group_of_new[(int64_t)h * a.kb_stride + (int64_t)ff * a.Tf + jj] = g;
     if (ff == a.F - 1) frontier[(int64_t)h * a.Tf + jj] = g;
-    if (g < 0 && diag) atomicAdd(&diag->capacity_overflow, 1u);
+    if (g < 0) {
+      // the cache's status word (benign race: every writer stores the same bit)
+      *status = FASTAR_CACHE_OVERFLOW;
+      if (diag) atomicAdd(&diag->capacity_overflow, 1u);
+    }
   };
   member(f, j);
   if (g < 0) {
@@ -1205,7 +1209,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
                      dim3(256), 0, s, (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count,
                      c.rep_bucket, c.n_groups, c.frontier, group_of_new, (const T*)kn.data, kn.stride_head,
                      kn.stride_token, (const T*)vn.data, vn.stride_head, vn.stride_token, kb, a,
-                     diag);
+                     c.status, diag);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (rep_offsets && rep_perm)

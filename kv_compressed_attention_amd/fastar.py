@@ -47,6 +47,7 @@ class FastarCache(ctypes.Structure):
         ("rep_bucket", ctypes.c_void_p),
         ("n_groups", ctypes.c_void_p),
         ("frontier", ctypes.c_void_p),
+        ("status", ctypes.c_void_p),
     ]
 
 
@@ -92,6 +93,7 @@ _SIGNATURES = {
     "fastar_bucket_index_workspace": (_SZ, [_I, _I64]),
     "fastar_bucket_index": (_I, [_P, _I, _I64, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "fastar_tempcache_workspace": (_SZ, [_CP, _I]),
+    "fastar_cache_status": (_I, [_CP, _I, _P]),
     "fastar_tempcache_merge": (_I, [_CP, _TP, _TP, _P, _I, _F, _P, _P, _P, _P, _SZ, _P, _P]),
     "fastar_prune_prompt": (_I, [_P, _I, _I64, _I, _P, _I64, _I, _P, _P, _P, _P]),
     "fastar_bucket_attention": (_I, [_TP, _P, _P, _I, _TP, _TP, _P, _P, _P, _I, _P, _P, _F, _P, _P, _P]),
@@ -236,11 +238,12 @@ class TempCache:
         self.rep_bucket = torch.zeros(heads, capacity, dtype=torch.int32, **z)
         self.n_groups = torch.zeros(heads, dtype=torch.int32, **z)
         self.frontier = torch.full((heads, tokens_per_frame), -1, dtype=torch.int32, **z)
+        self.status = torch.zeros(1, dtype=torch.int32, **z)
 
     def buffers(self):
         return dict(rep_k=self.rep_k, v_mean=self.v_mean, v_sum=self.v_sum, count=self.count,
                     log_count=self.log_count, rep_bucket=self.rep_bucket,
-                    n_groups=self.n_groups, frontier=self.frontier)
+                    n_groups=self.n_groups, frontier=self.frontier, status=self.status)
 
     def copy_from(self, other: "TempCache"):
         for name, t in self.buffers().items():
@@ -251,11 +254,21 @@ class TempCache:
                            _DTYPES[self.dtype], self.rep_k.data_ptr(), self.v_mean.data_ptr(),
                            self.v_sum.data_ptr(), self.count.data_ptr(),
                            self.log_count.data_ptr(), self.rep_bucket.data_ptr(),
-                           self.n_groups.data_ptr(), self.frontier.data_ptr())
+                           self.n_groups.data_ptr(), self.frontier.data_ptr(),
+                           self.status.data_ptr())
 
     def workspace_bytes(self, n_frames: int) -> int:
         c = self.struct()
         return library().fastar_tempcache_workspace(ctypes.byref(c), n_frames)
+
+    def status_code(self, clear: bool = False, stream=None) -> int:
+        """fastar_cache_status: 0 (ok) or 5 (FASTAR_ERR_CAPACITY: a merge since the
+        last clear dropped groups).  Synchronises the stream."""
+        c = self.struct()
+        st = library().fastar_cache_status(ctypes.byref(c), int(clear), _stream(stream))
+        if st not in (0, 5):
+            _check(st)
+        return st
 
 
 def fastar_tempcache_merge(cache: TempCache, k_new, v_new, k_new_bucket, n_frames: int,

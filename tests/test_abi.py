@@ -52,14 +52,29 @@ def test_binding_covers_every_declared_symbol():
 
 def test_struct_layouts_match_header(lib):
     assert ctypes.sizeof(fb.FastarTensor) == 48
-    assert ctypes.sizeof(fb.FastarCache) == 24 + 8 * 8
+    assert ctypes.sizeof(fb.FastarCache) == 24 + 9 * 8
 
 
 def test_status_strings(lib):
     assert lib.fastar_status_string(0) == b"ok"
     assert lib.fastar_status_string(1) == b"invalid argument"
     assert lib.fastar_status_string(3) == b"workspace too small"
-    assert lib.fastar_version() >= 100
+    assert lib.fastar_status_string(5) == b"cache capacity exceeded"
+    assert lib.fastar_version() >= 200
+
+
+def test_cache_status_rejects_missing_status_word(lib):
+    # fastar_cache_status needs the cache and its device status word; the
+    # merge needs the status word too (overflow is always reported)
+    assert lib.fastar_cache_status(None, 0, None) == 1
+    buf = 1 << 20
+    c = fb.FastarCache(2, 128, 64, 16, 12, 1, *([buf] * 8), 0)
+    assert lib.fastar_cache_status(ctypes.byref(c), 1, None) == 1
+    k = _tensor(tokens=16)
+    st = lib.fastar_tempcache_merge(ctypes.byref(c), ctypes.byref(k), ctypes.byref(k),
+                                    ctypes.c_void_p(buf), 1, 0.9, None, None, None,
+                                    ctypes.c_void_p(buf), 1 << 30, None, None)
+    assert st == 1 and b"NULL" in lib.fastar_last_error()
 
 
 def _tensor(dtype=1, heads=2, tokens=16, dim=128, data=1 << 20):
@@ -116,7 +131,7 @@ def test_chunk_rejects_bad_arguments_without_launching(lib):
     with a HIP status instead)."""
     buf = 1 << 20
     q, k = _tensor(tokens=32), _tensor(tokens=3 * 16)
-    cache = fb.FastarCache(2, 128, 64, 16, 12, 1, *([buf] * 8))
+    cache = fb.FastarCache(2, 128, 64, 16, 12, 1, *([buf] * 9))
 
     def args(**kw):
         a = dict(q=ctypes.addressof(q), n_probes=1, k_new=ctypes.addressof(k), v_new=ctypes.addressof(k),
@@ -171,7 +186,7 @@ def test_attention_rejects_bad_arguments_without_launching(lib):
 
 def test_merge_and_prune_reject_bad_arguments(lib):
     buf = 1 << 20
-    c = fb.FastarCache(2, 128, 64, 16, 12, 1, *([buf] * 8))
+    c = fb.FastarCache(2, 128, 64, 16, 12, 1, *([buf] * 9))
     k = _tensor(tokens=32)
     # k_new must hold n_frames * tokens_per_frame tokens
     st = lib.fastar_tempcache_merge(ctypes.byref(c), ctypes.byref(k), ctypes.byref(k), ctypes.c_void_p(buf),
@@ -182,7 +197,7 @@ def test_merge_and_prune_reject_bad_arguments(lib):
                                     2, float("inf"), None, None, None, ctypes.c_void_p(buf), 1 << 30, None, None)
     assert st == 1
     # capacity below one frame
-    c2 = fb.FastarCache(2, 128, 8, 16, 12, 1, *([buf] * 8))
+    c2 = fb.FastarCache(2, 128, 8, 16, 12, 1, *([buf] * 9))
     st = lib.fastar_tempcache_merge(ctypes.byref(c2), ctypes.byref(k), ctypes.byref(k), ctypes.c_void_p(buf),
                                     2, 0.9, None, None, None, ctypes.c_void_p(buf), 1 << 30, None, None)
     assert st == 1
@@ -203,5 +218,5 @@ def test_workspace_queries_scale_with_size(lib):
     b = lib.fastar_hash_workspace(24, 8192, 14, 2)
     assert 0 < a < b
     assert lib.fastar_bucket_index_workspace(12, 1000) >= 16 * 12 * 1000
-    c = fb.FastarCache(12, 128, 20000, 1560, 12, 1, *([0] * 8))
+    c = fb.FastarCache(12, 128, 20000, 1560, 12, 1, *([0] * 9))
     assert lib.fastar_tempcache_workspace(ctypes.byref(c), 3) >= 16 * 12 * 20000

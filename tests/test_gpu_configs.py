@@ -115,8 +115,7 @@ def check_head(w, g, r, h, setup_groups_ref):
         assert np.array_equal(i(g["rep_perm"])[:G], r["rep_perm"]), "representative index perm"
         err = np.max(np.abs(g["o_self"][h].float().numpy() - r["o_self"]))
         assert err <= tol, f"self-attention max|err| {err}"
-        fin = np.isfinite(r["lse_self"])
-        assert np.array_equal(np.isfinite(g["lse_self"][h].numpy()), fin)
+        check_lse(g["lse_self"][h].numpy(), r["lse_self"], tol, "self-attention lse")
     if w.prompt_k is not None:
         assert np.array_equal(i(g["p_ids"]), r["p_ids"]), "prompt bucket ids"
         assert np.array_equal(g["keep"][h].numpy().astype(bool), r["keep"]), "prune mask"
@@ -125,6 +124,33 @@ def check_head(w, g, r, h, setup_groups_ref):
         assert np.array_equal(i(g["kept"])[:nk], r["kept_idx"]), "kept prompt indices"
         err = np.max(np.abs(g["o_cross"][h].float().numpy() - r["o_cross"]))
         assert err <= tol, f"cross-attention max|err| {err}"
+        check_lse(g["lse_cross"][h].numpy(), r["lse_cross"], tol, "cross-attention lse")
+
+
+def check_lse(got, ref, tol, what):
+    """Element-wise: the same rows are empty (-inf), the rest within tol."""
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: empty rows differ"
+    assert np.all(got[~fin] == -np.inf), f"{what}: empty rows must be -inf"
+    err = np.max(np.abs(got[fin] - ref[fin]), initial=0.0)
+    assert err <= tol, f"{what} max|err| {err}"
+
+
+def check_all_heads_integers(w, g):
+    """Hash ids (and the prune mask) of every head, not just the sampled
+    ones: the oracle's hashing and pruning are cheap."""
+    for h in range(w.heads):
+        q_ids = oracle.simhash(w.q[h], w.planes, w.n_probes)
+        assert np.array_equal(g["q_ids"][h].numpy(), q_ids), f"query ids, head {h}"
+        if w.k_frames is not None:
+            kf = w.k_frames[h, w.setup_frames:].reshape(-1, w.dim)
+            assert np.array_equal(g["k_ids"][h].numpy(), oracle.simhash(kf, w.planes, 1)[:, 0]), \
+                f"new key ids, head {h}"
+        if w.prompt_k is not None:
+            p_ids = oracle.simhash(w.prompt_k[h], w.planes, 1)[:, 0]
+            assert np.array_equal(g["p_ids"][h].numpy(), p_ids), f"prompt ids, head {h}"
+            keep, kept = oracle.prune_prompt(q_ids, p_ids)
+            assert np.array_equal(g["keep"][h].numpy().astype(bool), keep), f"prune mask, head {h}"
 
 
 @pytest.mark.parametrize("index", [0, 1, 2, 3, 4])
@@ -138,6 +164,7 @@ def test_workload_end_to_end(fa, index):
     t3 = time.time()
     for h in SAMPLE[index]:
         check_head(w, g, ref[h], h, ref[h].get("setup_groups"))
+    check_all_heads_integers(w, g)
     if "diag" in g:
         d = g["diag"].numpy()
         assert d[3] == 0, f"unresolved decisions {d}"

@@ -411,3 +411,198 @@ def test_prune_single_bucket_keeps_all_and_equals_dense():
 def test_cross_attention_nothing_kept_is_zero():
     o, lse = cross_attention(np.ones((3, 4)), np.ones((5, 4)), np.ones((5, 4)), np.zeros(0, int))
     assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# --------------------------------------------------------------------------
+# The per-chunk sequence (oracle.run_chunk)
+# --------------------------------------------------------------------------
+
+def _seq_workload(k_frames, v_frames, q, setup_frames, tau, n_bits=0, planes=None,
+                  prompt_k=None, prompt_v=None, n_probes=1, dtype="f32"):
+    """A Workload holding given arrays (k/v frames [H, F, T, d], q [H, N, d])."""
+    from synth import Workload
+    H, _, _, d = k_frames.shape
+    if planes is None:
+        planes = np.zeros((n_bits, d), np.float32)
+    return Workload(-1, "pin", dtype, H, d, n_bits, n_probes, tau, planes, q, k_frames,
+                    v_frames, setup_frames=setup_frames, prompt_k=prompt_k, prompt_v=prompt_v)
+
+
+def test_sequence_no_merge_one_bucket_is_dense_over_raw_frames():
+    # tau > 1 merges nothing and b = 0 puts every key in one bucket: the
+    # self-attention of the chunk is dense attention over every raw key of
+    # every frame, the chunk's own frames included (the merge runs before the
+    # attention), with no bias
+    H, F, T, d = 1, 4, 40, 64
+    k = gaussian((H, F, T, d), 201)
+    v = gaussian((H, F, T, d), 202)
+    q = gaussian((H, 30, d), 203)
+    r = oracle_run_chunk(_seq_workload(k, v, q, setup_frames=2, tau=1.5))[0]
+    assert r["cache"].n_groups == F * T
+    ref = sdpa64(q[0], k[0].reshape(-1, d), v[0].reshape(-1, d))
+    assert np.max(np.abs(r["o_self"] - ref)) < 1e-12
+    # the lse is the log of the softmax normaliser over the same keys
+    logits = (q[0].astype(np.float64) @ k[0].reshape(-1, d).T.astype(np.float64)) / math.sqrt(d)
+    lse = np.log(np.exp(logits - logits.max(1, keepdims=True)).sum(1)) + logits.max(1)
+    assert np.max(np.abs(r["lse_self"] - lse)) < 1e-12
+
+
+def test_sequence_exact_duplicates_is_lemma_exact_over_raw_cache():
+    # Frames whose carried tokens are exact copies of the previous frame's
+    # (the rest fresh): groups of unequal size m form, and with b = 0 the
+    # chunk's self-attention over the compressed cache (mean values, + ln m)
+    # equals dense attention over the raw, uncompressed frames (Lemma 5.1,
+    # paperlayer.ai appendix A).  Unequal m makes the bias matter, so a
+    # dropped bias, attention before the chunk's merge, or an unrounded
+    # mean of the wrong frames fails.
+    H, F, T, d = 1, 5, 48, 64
+    rng = np.random.default_rng(204)
+    k = np.empty((H, F, T, d), np.float32)
+    k[:, 0] = gaussian((H, T, d), 205)
+    for f in range(1, F):
+        carry = rng.random((H, T)) < 0.6
+        fresh = gaussian((H, T, d), 206 + f)
+        k[:, f] = np.where(carry[..., None], k[:, f - 1], fresh)
+    v = gaussian((H, F, T, d), 211)
+    q = gaussian((H, 25, d), 212)
+    for tau in (0.5, 0.999, 1.0):
+        r = oracle_run_chunk(_seq_workload(k, v, q, setup_frames=3, tau=tau))[0]
+        tc = r["cache"]
+        assert tc.count.max() > 1 and tc.count.min() == 1       # unequal group sizes
+        assert tc.count.sum() == F * T
+        ref = sdpa64(q[0], k[0].reshape(-1, d), v[0].reshape(-1, d))
+        # only the float32 rounding of the stored means separates the two
+        assert np.max(np.abs(r["o_self"] - ref)) < 1e-6
+    # dropping the bias breaks the identity
+    o_nobias, _ = bucket_attention(q[0], r["q_ids"], tc.rep_k, tc.v_mean, tc.rep_bucket)
+    assert np.max(np.abs(o_nobias - ref)) > 1e-3
+
+
+def test_sequence_unpruned_prompt_is_dense_cross_attention():
+    # b = 0: every prompt key shares the queries' one bucket, so AnnCA keeps
+    # all of them and the cross-attention is dense attention over the prompt
+    H, T, d = 1, 16, 64
+    k = gaussian((H, 2, T, d), 220)
+    v = gaussian((H, 2, T, d), 221)
+    q = gaussian((H, 20, d), 222)
+    pk, pv = gaussian((H, 33, d), 223), gaussian((H, 33, d), 224)
+    r = oracle_run_chunk(_seq_workload(k, v, q, 1, 0.9, prompt_k=pk, prompt_v=pv))[0]
+    assert r["keep"].all() and r["kept_idx"].tolist() == list(range(33))
+    assert np.max(np.abs(r["o_cross"] - sdpa64(q[0], pk[0], pv[0]))) < 1e-12
+
+
+def test_sequence_buckets_restrict_attention_to_probe_sets():
+    # with hashing on, the sequence's self-attention equals masked SDPA over
+    # the compressed cache, the mask being "representative bucket is one of
+    # the query's probe buckets" (two probes), computed from the sequence's
+    # own ids: a wrong probe's ids or an unmasked key fails
+    H, F, T, d = 1, 3, 64, 64
+    k = gaussian((H, F, T, d), 230)
+    v = gaussian((H, F, T, d), 231)
+    q = gaussian((H, 50, d), 232)
+    planes = gaussian((3, d), 233)
+    r = oracle_run_chunk(_seq_workload(k, v, q, 1, 1.5, n_bits=3, planes=planes, n_probes=2))[0]
+    tc = r["cache"]
+    ids = simhash(q[0], planes, 2)
+    assert np.array_equal(r["q_ids"], ids)
+    mask = (tc.rep_bucket[None, :] == ids[:, :1]) | (tc.rep_bucket[None, :] == ids[:, 1:2])
+    rows = mask.any(axis=1)
+    ref = sdpa64(q[0][rows], tc.rep_k, tc.v_mean, mask=mask[rows], bias=tc.log_count)
+    assert np.max(np.abs(r["o_self"][rows] - ref)) < 1e-12
+    assert np.all(r["o_self"][~rows] == 0)
+
+
+def oracle_run_chunk(w):
+    from oracle import run_chunk
+    return run_chunk(w)
+
+
+# --------------------------------------------------------------------------
+# Decisions whose true gap float64 cannot resolve
+# --------------------------------------------------------------------------
+
+def test_tempcache_argmax_below_float64_resolution():
+    # key a = (1, 0); candidates b0 = (1, 3 e), b1 = (1, e) with e = 2^-30:
+    # cos(a, b_i) = 1 / sqrt(1 + (c e)^2), which float64 rounds to exactly 1
+    # for both, but b1 is strictly closer.  The smaller-index tie rule would
+    # pick b0; the exact comparison picks b1.
+    e = 2.0 ** -30
+    tc = TempCacheOracle(2, "f32")
+    tc.merge_frame(np.array([[1.0, 3 * e], [1.0, e]]), np.ones((2, 2)), np.zeros(2, int), 0.5)
+    cos_f64 = [np.float64(1.0) / np.sqrt(1.0 + (c * e) ** 2) for c in (3, 1)]
+    assert cos_f64[0] == cos_f64[1] == 1.0
+    g = tc.merge_frame(np.array([[1.0, 0.0]]), np.ones((1, 2)), np.zeros(1, int), 0.5)
+    assert g.tolist() == [1]
+    assert tc.exact_evals > 0
+
+
+def test_tempcache_conflict_below_float64_resolution():
+    # two new keys propose to one candidate (1, 0); their cosines 1 / sqrt(1
+    # + (c e)^2) are both 1.0 in float64, the second is strictly larger and
+    # wins the candidate; the first opens a new group
+    e = 2.0 ** -30
+    tc = TempCacheOracle(2, "f32")
+    tc.merge_frame(np.array([[1.0, 0.0]]), np.ones((1, 2)), np.zeros(1, int), 0.5)
+    g = tc.merge_frame(np.array([[1.0, 3 * e], [1.0, e]]), np.ones((2, 2)), np.zeros(2, int), 0.5)
+    assert g.tolist() == [1, 0]
+
+
+def test_tempcache_threshold_below_float64_resolution():
+    # cos(a, b) = 1 / sqrt(1 + e^2) with e = 2^-30 is 1.0 in float64 but is
+    # strictly below tau = 1: no merge.  With b = a exactly it merges.
+    e = 2.0 ** -30
+    tc = TempCacheOracle(2, "f32")
+    tc.merge_frame(np.array([[1.0, e]]), np.ones((1, 2)), np.zeros(1, int), 1.0)
+    g = tc.merge_frame(np.array([[1.0, 0.0]]), np.ones((1, 2)), np.zeros(1, int), 1.0)
+    assert g.tolist() == [1]
+    g = tc.merge_frame(np.array([[1.0, 0.0]]), np.ones((1, 2)), np.zeros(1, int), 1.0)
+    assert g.tolist() == [1]
+
+
+def test_second_probe_below_float64_resolution():
+    # planes r0 = (1, 0, 0), r1 = (0, 1, e) with e = 2^-30 and x = (1, 1, 0):
+    # both projections are 1, so the distances are 1 / |r_j|; |r1| =
+    # sqrt(1 + e^2) is 1.0 in float64, but x is strictly nearer plane 1.  The
+    # smaller-index tie rule would flip bit 0; the exact comparison flips bit 1.
+    e = 2.0 ** -30
+    planes = np.array([[1.0, 0.0, 0.0], [0.0, 1.0, e]])
+    assert np.sqrt(1.0 + e * e) == 1.0
+    ids = simhash(np.array([[1.0, 1.0, 0.0]]), planes, 2)
+    assert ids.tolist() == [[3, 1]]
+
+
+def test_stored_mean_is_rounded_once_to_bf16_by_hand():
+    # two identical keys merge; values 1 and 1 + 2^-7 average to 1 + 2^-8,
+    # halfway between the bf16 neighbours 1 and 1 + 2^-7: ties to even give
+    # 1.  Values 1 + 2^-7 and 1 + 2^-6 average to 1 + 3 2^-8, halfway
+    # between 1 + 2^-7 (odd) and 1 + 2^-6 (even): 1 + 2^-6.
+    for (v0, v1), mean in [((1.0, 1.0 + 2.0 ** -7), 1.0),
+                           ((1.0 + 2.0 ** -7, 1.0 + 2.0 ** -6), 1.0 + 2.0 ** -6)]:
+        tc = TempCacheOracle(2, "bf16")
+        tc.merge_frame(np.array([[1.0, 0.0]]), np.array([[v0, v0]]), np.zeros(1, int), 0.9)
+        tc.merge_frame(np.array([[1.0, 0.0]]), np.array([[v1, v1]]), np.zeros(1, int), 0.9)
+        assert tc.count.tolist() == [2]
+        assert tc.v_mean.tolist() == [[mean, mean]]
+        assert tc.v_sum.tolist() == [[v0 + v1, v0 + v1]]
+
+
+def test_sequence_bookkeeping_invariants():
+    # the set-up frames' and the chunk's groups together account for every
+    # token exactly once: per-group member counts equal the stored counts,
+    # the chunk's ids and groups cover exactly its frames, and the group
+    # count before the chunk is what the set-up frames opened
+    from synth import make_workload
+    w = make_workload(0)
+    r = oracle_run_chunk(w)[0]
+    tc = r["cache"]
+    T = w.tokens_per_frame
+    assert r["k_ids"].shape == (w.chunk_frames * T,)
+    assert r["group_of_new"].shape == (w.chunk_frames * T,)
+    assert r["setup_groups"].shape == (w.setup_frames * T,)
+    allg = np.concatenate([r["setup_groups"], r["group_of_new"]])
+    assert np.array_equal(np.bincount(allg, minlength=tc.n_groups), tc.count)
+    assert r["n_groups_before"] == r["setup_groups"].max() + 1
+    assert r["group_of_new"].max() == tc.n_groups - 1
+    # chunk keys' ids are the hash of the chunk's own frames (not a set-up frame)
+    k_last = w.k_frames[0, -1].astype(np.float64)
+    assert np.array_equal(r["k_ids"][-T:], simhash(k_last, w.planes, 1)[:, 0])
