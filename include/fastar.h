@@ -310,6 +310,28 @@ size_t fastar_chunk_workspace(const fastar_chunk_t* args);
 fastar_status_t fastar_chunk(const fastar_chunk_t* args, void* ws, size_t ws_bytes,
                              fastar_diag_t* diag, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * fastar_chunk_noalloc -- fastar_chunk for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation): the same launches on the same arguments, with the
+ * workspace taken from a scratch array the library holds on each GPU it runs
+ * on (FASTAR_NOALLOC_SCRATCH_BYTES, held until the process ends) instead of
+ * a caller buffer.  The caller still passes every input and output.
+ * - Returns FASTAR_ERR_WORKSPACE, launching nothing, when the call needs more
+ *   than FASTAR_NOALLOC_SCRATCH_BYTES (fastar_chunk_workspace(args) says how
+ *   much it needs).
+ * - Allocates nothing: no hipMalloc, no allocating library routine.  The
+ *   first call on a device looks up that device's scratch address once.
+ * - Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *   one GPU (different streams, or different host threads) race and must be
+ *   ordered by the caller.  The scratch keeps the last call's contents; the
+ *   kernels write every scratch word before they read it, so nothing needs
+ *   clearing between calls.
+ * ---------------------------------------------------------------------- */
+#define FASTAR_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
+fastar_status_t fastar_chunk_noalloc(const fastar_chunk_t* args, fastar_diag_t* diag,
+                                     hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

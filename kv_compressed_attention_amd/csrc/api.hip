@@ -6,7 +6,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
+
+// The workspace of fastar_chunk_noalloc: one copy on every GPU the library
+// runs on, 256-byte aligned like the workspace carve.  Host code never uses
+// this name as an address: each device's address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[FASTAR_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -408,6 +416,8 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
   return hip_status(fastar::launch_attention(a, stream), "bucket_attention");
 }
 
+}  // extern "C"
+
 // ---------------------------------------------------------------------------
 namespace {
 // the cache's representatives and mean values as [H][capacity][dim] tensors
@@ -429,6 +439,8 @@ size_t chunk_index_ws(const fastar_chunk_t* a) {
   return align_up(16 * (size_t)a->q->heads * (size_t)a->q->tokens);
 }
 }  // namespace
+
+extern "C" {
 
 size_t fastar_chunk_workspace(const fastar_chunk_t* a) {
   if (!a || !a->cache || !a->q) return 0;
@@ -541,6 +553,48 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
       return st;
   }
   return FASTAR_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices] = {};
+
+// the current device's scratch address, looked up once per device with that
+// device current
+fastar_status_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  fastar_status_t st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != FASTAR_OK) return st;
+  if (dev < 0 || dev >= kMaxDevices) return fail(FASTAR_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != FASTAR_OK) return st;
+    if (!p) return fail(FASTAR_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return FASTAR_OK;
+}
+}  // namespace
+
+extern "C" {
+
+fastar_status_t fastar_chunk_noalloc(const fastar_chunk_t* a, fastar_diag_t* diag, hipStream_t stream) {
+  if (!a || !a->cache || !a->q) return fail(FASTAR_ERR_INVALID, "arguments, cache and q are required");
+  const size_t need = fastar_chunk_workspace(a);
+  if (need > FASTAR_NOALLOC_SCRATCH_BYTES)
+    return fail(FASTAR_ERR_WORKSPACE, "the call needs %zu bytes of workspace, more than the %zu bytes "
+                "of the allocation-free scratch", need, (size_t)FASTAR_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const fastar_status_t st = noalloc_scratch(&ws);
+  if (st != FASTAR_OK) return st;
+  return fastar_chunk(a, ws, FASTAR_NOALLOC_SCRATCH_BYTES, diag, stream);
 }
 
 }  // extern "C"

@@ -99,7 +99,11 @@ _SIGNATURES = {
     "fastar_bucket_attention": (_I, [_TP, _P, _P, _I, _TP, _TP, _P, _P, _P, _I, _P, _P, _F, _P, _P, _P]),
     "fastar_chunk_workspace": (_SZ, [_P]),
     "fastar_chunk": (_I, [_P, _P, _SZ, _P, _P]),
+    "fastar_chunk_noalloc": (_I, [_P, _P, _P]),
 }
+
+# FASTAR_NOALLOC_SCRATCH_BYTES in include/fastar.h
+NOALLOC_SCRATCH_BYTES = 48 << 20
 
 
 def library():
@@ -373,3 +377,8 @@ class ChunkCall:
     def __call__(self, ws, diag=None, stream=None):
         _check(library().fastar_chunk(ctypes.byref(self.args), _ptr(ws), ws.numel() * ws.element_size(),
                                       _ptr(diag), _stream(stream)))
+
+    def noalloc(self, diag=None, stream=None):
+        """fastar_chunk_noalloc: the same call with the library's scratch as
+        workspace (nothing allocated, by torch or the library)."""
+        _check(library().fastar_chunk_noalloc(ctypes.byref(self.args), _ptr(diag), _stream(stream)))

@@ -220,3 +220,24 @@ def test_workspace_queries_scale_with_size(lib):
     assert lib.fastar_bucket_index_workspace(12, 1000) >= 16 * 12 * 1000
     c = fb.FastarCache(12, 128, 20000, 1560, 12, 1, *([0] * 9))
     assert lib.fastar_tempcache_workspace(ctypes.byref(c), 3) >= 16 * 12 * 20000
+
+
+def test_noalloc_chunk_rejects_oversized_workspace_without_launching(lib):
+    # a chunk whose workspace exceeds the allocation-free scratch is refused
+    # on the host, before any HIP call
+    buf = 1 << 20
+    H, T, cap = 24, 2048, 1 << 20
+    c = fb.FastarCache(H, 128, cap, T, 14, 1, *([buf] * 9))
+    q = fb.FastarTensor(buf, 1, H, 8192, 128, 0, 8192 * 128, 128)
+    k = fb.FastarTensor(buf, 1, H, 4 * T, 128, 0, 4 * T * 128, 128)
+    a = fb.FastarChunk(ctypes.addressof(q), 2, ctypes.addressof(k), ctypes.addressof(k), 4, None,
+                       None, buf, 14, 0.999, 0.088, ctypes.addressof(c), *([buf] * 9))
+    need = lib.fastar_chunk_workspace(ctypes.byref(a))
+    assert need > fb.NOALLOC_SCRATCH_BYTES
+    assert lib.fastar_chunk_noalloc(ctypes.byref(a), None, None) == 3
+    assert b"scratch" in lib.fastar_last_error()
+
+
+def test_noalloc_scratch_size_matches_header():
+    m = re.search(r"#define FASTAR_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fb.NOALLOC_SCRATCH_BYTES
