@@ -93,10 +93,10 @@ int fastar_version(void);
  *   bucket   out [H][N][n_probes] int32.
  *   offsets  out [H][2^n_bits + 1] int32, or NULL (no index).
  *   perm     out [H][N] int32, or NULL (together with offsets).
- *            One probe: perm lists token indices sorted by bucket, ascending
- *            token within a bucket; offsets[B] = number of tokens with
- *            bucket < B.  Two probes: each token once, sorted by (first
- *            bucket, flipped bit, token); offsets count first buckets.
+ *            perm lists token indices sorted by bucket (with two probes,
+ *            the first probe's bucket; each token once), ascending token
+ *            within a bucket; offsets[B] = number of tokens whose (first)
+ *            bucket is < B.
  *   ws       device workspace of at least fastar_hash_workspace() bytes,
  *            used by the index only (may be NULL when offsets is NULL).
  *   diag     optional device counters (may be NULL).

@@ -519,11 +519,11 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   if (any && (st = hip_status(fastar::launch_hash_multi(jobs, a->q->dim, a->q->dtype, a->planes, a->n_bits,
                                                        diag, stream), "hash")) != FASTAR_OK)
     return st;
-  fastar::IndexJob qj{a->q_bucket, a->q->tokens, a->n_bits, a->q_offsets, a->q_perm};
+  fastar::IndexJob qj{a->q_bucket, a->q->tokens, a->n_bits, a->n_probes, a->q_offsets, a->q_perm};
   // the queries' index rides along with the representatives' when both are
   // built by the single counting pass
-  const bool fused = chunk_index_ws(a) == 0 && a->q->tokens > 0 &&
-                     fastar::direct_index_supported(c->capacity, 1, c->n_bits);
+  const bool fused = a->q->tokens > 0 &&
+                     fastar::direct_index_supported(c->capacity, 1, c->n_bits, a->q->tokens, a->n_probes);
   if (fused) mw.also_index = &qj;
   if ((st = hip_status(fastar::launch_tempcache_merge(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,
                                                       a->tau, a->group_of_new, a->rep_offsets,

@@ -2,11 +2,13 @@
 //
 // Block-sparse bucket attention needs each bucket's members contiguous
 // (gist.science technical summary, AnnSA: attention is restricted to the keys
-// of the query's bucket(s) and run block-sparse).  With one probe the sort key
-// is the bucket id; with two probes it is (first bucket, flipped bit), so that
-// queries sharing their second bucket sit together.
+// of the query's bucket(s) and run block-sparse).  The sort key is the bucket
+// id (with two probes, the first probe's), ties in token order.
 //
-// One workgroup (16 waves) per head runs an LSD radix sort with 8-bit digits.
+// 3..14 bits take a single stable counting pass (index_direct.h), a head
+// split over up to 8 workgroups.  Anything else (0..2 or 15 bits, or 14 bits
+// past 65535 items) falls back to one workgroup (16 waves) per head running
+// an LSD radix sort with 8-bit digits.
 // Each wave owns a contiguous slice of the input and walks it 64 items at a
 // time in order; items with equal digits in a 64-item group are matched with
 // 8 ballots, so ranks come from popcounts and the sort is stable without
@@ -14,8 +16,7 @@
 // most kLdsItems items is sorted entirely in LDS (keys and 16-bit token
 // indices, double-buffered); larger heads go through the workspace.
 // offsets[B] is the number of items whose first bucket is < B: every run of
-// equal buckets writes its start and a suffix minimum fills the gaps.  One
-// probe with at most 12 bits takes a single counting pass instead (below).
+// equal buckets writes its start and a suffix minimum fills the gaps.
 
 #include "common.h"
 #include <algorithm>
@@ -31,11 +32,6 @@ constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * FASTAR_WAVE;
 constexpr int U = 4;               // groups of 64 keys loaded before they are ranked
 constexpr int kLdsItems = 11264;   // 2 x (4 + 2) bytes per item in LDS
-
-__device__ __forceinline__ int32_t flip_bit(int32_t a, int32_t b) {
-  const uint32_t x = (uint32_t)(a ^ b);
-  return x ? (int32_t)__builtin_ctz(x) : 0;
-}
 
 // peers: lanes of this wave holding the same 8-bit digit (valid lanes only)
 __device__ __forceinline__ uint64_t match_digit(uint32_t digit, bool valid) {
@@ -207,8 +203,8 @@ __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
   }
   const int32_t* ids = bucket + (int64_t)h * n * P;
   int32_t* ph = perm + (int64_t)h * n;
-  const int shift0 = (P == 2) ? 4 : 0;
-  const int passes = (nbits + shift0 + 7) / 8;
+  const int shift0 = 0;
+  const int passes = (nbits + 7) / 8;
   const int nbk = 1 << nbits;
   int32_t* off = offsets + (int64_t)h * (nbk + 1);
   if (passes == 0) {  // one bucket: identity
@@ -220,9 +216,8 @@ __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
   const int64_t chunk = (nh + kWaves - 1) / kWaves;
   const int64_t wbeg = (int64_t)wave * chunk < nh ? (int64_t)wave * chunk : nh;
   const int64_t wend = wbeg + chunk < nh ? wbeg + chunk : nh;
-  auto key_of = [&](int64_t i) -> int32_t {
-    return P == 2 ? ((ids[2 * i] << 4) | flip_bit(ids[2 * i], ids[2 * i + 1])) : ids[i];
-  };
+  // the sort key: the first probe's bucket
+  auto key_of = [&](int64_t i) -> int32_t { return ids[(int64_t)P * i]; };
   if (use_lds && nh <= kLdsItems) {
     int32_t* ka = lds;
     int32_t* kb = ka + kLdsItems;
@@ -287,26 +282,32 @@ __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
 }
 
 // One workgroup per part and head; the last xparts columns build the extra
-// job's index.
-template <int NBITS>
-__global__ __launch_bounds__(kDirectWaves * FASTAR_WAVE) void bucket_index_direct_kernel(
-    const int32_t* __restrict__ bucket, int64_t n, const int32_t* __restrict__ n_valid,
+// job's index (same heads and bits).
+template <int NBITS, bool WIDE>
+__global__ __launch_bounds__(kDirectThreads) void bucket_index_direct_kernel(
+    const int32_t* __restrict__ bucket, int P, int64_t n, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int stage, IndexJob xj, int xparts,
     int xstage) {
   extern __shared__ int4 lds4[];
   const int nparts = (int)gridDim.x - xparts;
   if ((int)blockIdx.x >= nparts) {
-    direct_index_body<NBITS>(blockIdx.y, blockIdx.x - nparts, xparts, xj.bucket, xj.n, nullptr, xj.offsets,
-                             xj.perm, xstage, lds4);
+    direct_index_body<NBITS, WIDE>(blockIdx.y, blockIdx.x - nparts, xparts, xj.bucket, xj.P, xj.n,
+                                   nullptr, xj.offsets, xj.perm, xstage, lds4);
     return;
   }
-  direct_index_body<NBITS>(blockIdx.y, blockIdx.x, nparts, bucket, n, n_valid, offsets, perm, stage, lds4);
+  direct_index_body<NBITS, WIDE>(blockIdx.y, blockIdx.x, nparts, bucket, P, n, n_valid, offsets, perm,
+                                 stage, lds4);
 }
+
+// counter width of a direct launch of n items (and an extra job's n_extra)
+bool direct_wide(int64_t n, int64_t n_extra) { return direct_index_wide(n) || direct_index_wide(n_extra); }
 
 }  // namespace
 
-bool direct_index_supported(int64_t n, int n_probes, int n_bits) {
-  return direct_index_fits(n, n_probes, n_bits);
+bool direct_index_supported(int64_t n, int n_probes, int n_bits, int64_t n_extra, int extra_probes) {
+  const bool wide = direct_wide(n, n_extra);
+  return direct_index_fits_wide(n, n_probes, n_bits, wide) &&
+         (n_extra <= 0 || direct_index_fits_wide(n_extra, extra_probes, n_bits, wide));
 }
 
 hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int n_probes,
@@ -314,27 +315,36 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
                                int32_t* perm, int32_t* ws, hipStream_t s, const IndexJob* extra) {
   if (heads == 0) return hipSuccess;
   const bool with_x = extra && extra->n > 0;
-  if (with_x && (!direct_index_fits(n, n_probes, n_bits) || !direct_index_fits(extra->n, 1, extra->n_bits) ||
-                 extra->n_bits != n_bits))
+  if (with_x && (extra->n_bits != n_bits ||
+                 !direct_index_supported(n, n_probes, n_bits, extra->n, extra->P)))
     return hipErrorInvalidValue;
-  if (direct_index_fits(n, n_probes, n_bits)) {
+  if (direct_index_supported(n, n_probes, n_bits, with_x ? extra->n : 0, with_x ? extra->P : 1)) {
+    const bool wide = direct_wide(n, with_x ? extra->n : 0);
     int stage, xstage = 0;
     const int parts = direct_index_parts(n);
-    size_t lds = direct_index_lds(n, n_bits, parts, &stage);
+    size_t lds = direct_index_lds(n, n_bits, wide, parts, &stage);
     const int xparts = with_x ? direct_index_parts(extra->n) : 0;
-    if (with_x) lds = std::max(lds, direct_index_lds(extra->n, n_bits, xparts, &xstage));
-    const IndexJob xj = with_x ? *extra : IndexJob{nullptr, 0, n_bits, nullptr, nullptr};
-    const dim3 grid(parts + xparts, heads), block(kDirectWaves * FASTAR_WAVE);
-    switch (n_bits) {
-#define FASTAR_DIRECT(B)                                                                         \
-  case B:                                                                                         \
-    hipLaunchKernelGGL(bucket_index_direct_kernel<B>, grid, block, lds, s, bucket, n, n_valid,    \
-                       offsets, perm, stage, xj, xparts, xstage);                                 \
+    if (with_x) lds = std::max(lds, direct_index_lds(extra->n, n_bits, wide, xparts, &xstage));
+    const IndexJob xj = with_x ? *extra : IndexJob{nullptr, 0, n_bits, 1, nullptr, nullptr};
+    const dim3 grid(parts + xparts, heads), block(kDirectThreads);
+#define FASTAR_DIRECT_W(B, W)                                                                       \
+  hipLaunchKernelGGL((bucket_index_direct_kernel<B, W>), grid, block, lds, s, bucket, n_probes, n,  \
+                     n_valid, offsets, perm, stage, xj, xparts, xstage)
+#define FASTAR_DIRECT(B)                      \
+  case B:                                     \
+    if (wide) FASTAR_DIRECT_W(B, true);       \
+    else FASTAR_DIRECT_W(B, false);           \
     break;
+    switch (n_bits) {
       FASTAR_DIRECT(3) FASTAR_DIRECT(4) FASTAR_DIRECT(5) FASTAR_DIRECT(6) FASTAR_DIRECT(7)
       FASTAR_DIRECT(8) FASTAR_DIRECT(9) FASTAR_DIRECT(10) FASTAR_DIRECT(11) FASTAR_DIRECT(12)
-#undef FASTAR_DIRECT
+      FASTAR_DIRECT(13)
+      case 14:  // 32-bit counters do not fit at 14 bits (never chosen)
+        FASTAR_DIRECT_W(14, false);
+        break;
     }
+#undef FASTAR_DIRECT
+#undef FASTAR_DIRECT_W
     return hipGetLastError();
   }
   // LDS staging whenever a head can fit (n, or a device count, at most kLdsItems)

@@ -1,95 +1,132 @@
-// Stable counting-sort bucket index for one probe, 3..12 bits and at most
-// 65535 items per head (see index.hip), as a workgroup-level body, so that
-// other launches can run it in workgroups of their own.
+// Stable counting-sort bucket index (see index.hip) as a workgroup-level
+// body, so that other launches can run it in workgroups of their own.
 #pragma once
+
+#include <type_traits>
 
 #include "common.h"
 
 namespace fastar {
 
-// One probe, 3..12 bits, at most 65535 items: a single stable counting pass.
-// Per-wave 16-bit bucket counters (one row of 2^b per scattering wave) fit in
-// LDS; one scan over (bucket, row) gives each wave's scatter bases and the
-// offsets.  A head may be split into parts, one workgroup each: a part
+// A single stable counting pass for 3..14 bits, one or two probes (the sort
+// key is the first probe's bucket), any item count below 2^31 that the
+// counters allow.  Per-wave bucket counters (one row of 2^b per scattering
+// wave) sit in LDS: 16-bit while a head has at most 65535 items, 32-bit
+// above.  One scan over (bucket, row) gives each wave its scatter bases and
+// the offsets.  A head may be split into parts, one workgroup each: a part
 // scatters its own slice of the items and counts the others (those before
 // the slice and those after it, per bucket, in two more rows) to place it,
-// so the parts need no exchange.  With `stage` (one part), the permutation is
-// assembled in LDS and written out coalesced.
+// so the parts need no exchange.  With `stage` (one part, room left in LDS)
+// the permutation is assembled in LDS and written out coalesced.
 constexpr int kDirectWaves = 16;
-// waves that scatter a part's slice when a head has several parts (fewer
-// counter rows to clear and scan)
+constexpr int kDirectThreads = kDirectWaves * FASTAR_WAVE;
+// waves that scatter a part's slice when a head has several parts, at most
 constexpr int kDirectPartWaves = 8;
 constexpr int kDirectMinBits = 3;
-constexpr int kDirectMaxBits = 12;
-constexpr int64_t kDirectMaxItems = 65535;
+constexpr int kDirectMaxBits = 14;
+// 16-bit counters up to this many items per head
+constexpr int64_t kDirectNarrowItems = 65535;
 // parts per head: about this many items each, at most kDirectMaxParts
 constexpr int64_t kDirectPartItems = 1536;
 constexpr int kDirectMaxParts = 8;
-// LDS left for the staged permutation next to the counters
+// LDS for the counter rows, and for counters plus a staged permutation
+constexpr size_t kDirectCounterLds = 128 * 1024;
 constexpr size_t kDirectLds = 152 * 1024;
 
+// scattering waves and counter rows of a part
+struct DirectShape {
+  int sw, rows;
+};
+__host__ __device__ inline DirectShape direct_shape(int n_bits, bool wide, int nparts) {
+  const size_t row = ((size_t)1 << n_bits) * (wide ? 4u : 2u);
+  const int fit = (int)(kDirectCounterLds / row);
+  DirectShape s;
+  if (nparts == 1) {
+    s.sw = fit < kDirectWaves ? fit : kDirectWaves;
+    s.rows = s.sw;
+  } else {
+    s.sw = fit - 2 < kDirectPartWaves ? fit - 2 : kDirectPartWaves;
+    s.rows = s.sw + 2;
+  }
+  return s;
+}
+// 32-bit counters for n items
+inline bool direct_index_wide(int64_t n) { return n > kDirectNarrowItems; }
 // The parts (workgroups) per head for n items
 inline int direct_index_parts(int64_t n) {
   const int64_t p = (n + kDirectPartItems - 1) / kDirectPartItems;
   return p < 1 ? 1 : (p > kDirectMaxParts ? kDirectMaxParts : (int)p);
 }
-// counter rows: one per scattering wave, and two more with several parts
-__host__ __device__ inline int direct_index_rows(int nparts) {
-  return nparts > 1 ? kDirectPartWaves + 2 : kDirectWaves;
+// whether the direct pass covers n items of n_bits bits with counters of the
+// given width
+inline bool direct_index_fits_wide(int64_t n, int n_probes, int n_bits, bool wide) {
+  if (n_probes < 1 || n_probes > 2 || n_bits < kDirectMinBits || n_bits > kDirectMaxBits) return false;
+  if (n >= ((int64_t)1 << 31) || (!wide && direct_index_wide(n))) return false;
+  return direct_shape(n_bits, wide, direct_index_parts(n)).sw >= 1;
+}
+inline bool direct_index_fits(int64_t n, int n_probes, int n_bits) {
+  return direct_index_fits_wide(n, n_probes, n_bits, direct_index_wide(n));
 }
 // LDS bytes the direct index of n items in nparts parts needs, and whether it
 // stages the permutation there
-inline size_t direct_index_lds(int64_t n, int n_bits, int nparts, int* stage) {
-  const size_t counters = (size_t)direct_index_rows(nparts) * ((size_t)1 << n_bits) * sizeof(uint16_t);
+inline size_t direct_index_lds(int64_t n, int n_bits, bool wide, int nparts, int* stage) {
+  const DirectShape sh = direct_shape(n_bits, wide, nparts);
+  const size_t counters = (size_t)sh.rows * ((size_t)1 << n_bits) * (wide ? 4u : 2u);
   *stage = nparts == 1 && counters + (size_t)n * sizeof(int32_t) <= kDirectLds ? 1 : 0;
   return counters + (*stage ? (size_t)n * sizeof(int32_t) : 0);
 }
-inline bool direct_index_fits(int64_t n, int n_probes, int n_bits) {
-  return n_probes == 1 && n_bits >= kDirectMinBits && n_bits <= kDirectMaxBits && n <= kDirectMaxItems;
-}
 
-// Part `part` of nparts of the index of head h, by one workgroup of
-// kDirectWaves waves.  lds4: the dynamic LDS of direct_index_lds bytes.
-template <int NBITS>
+// Part `part` of nparts of the index of head h (ids [H][n][P], sorted by
+// their first probe), by one workgroup of kDirectWaves waves.  lds4: the
+// dynamic LDS of direct_index_lds bytes.
+template <int NBITS, bool WIDE>
 __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
-                                                  const int32_t* __restrict__ bucket, int64_t n,
+                                                  const int32_t* __restrict__ bucket, int P, int64_t n,
                                                   const int32_t* __restrict__ n_valid,
                                                   int32_t* __restrict__ offsets,
                                                   int32_t* __restrict__ perm, int stage, int4* lds4) {
   constexpr int nbits = NBITS;
-  // lds4: [sw][2^nbits] uint16 counters of the scattering waves (8 per
-  // 128-bit word), then with several parts [2][2^nbits] uint16 counts of the
-  // items before and after this part's slice, then the staged permutation
-  // (int32, n entries) when stage is set
+  constexpr int nbk = 1 << nbits;
+  // buckets per thread in the scan, in groups of 4
+  constexpr int BPT = nbk / kDirectThreads > 4 ? nbk / kDirectThreads : 4;
+  constexpr int NG = BPT / 4;
+  using CT = typename std::conditional<WIDE, uint32_t, uint16_t>::type;
+  using CT4 = typename std::conditional<WIDE, uint4, uint2>::type;  // 4 counters
+  static_assert(nbk % 4 == 0, "whole 4-bucket groups");
+  // lds4: [rows][2^nbits] counters (the scattering waves' rows, then with
+  // several parts the counts of the items before and after this part's
+  // slice), then the staged permutation (int32, n entries) when stage is set
   __shared__ int wtot[kDirectWaves];
-  constexpr int NT = kDirectWaves * FASTAR_WAVE;
-  static_assert((1 << kDirectMaxBits) / 4 <= NT, "at most one 4-bucket group per thread");
-  static_assert((1 << kDirectMinBits) >= 4, "whole 4-bucket groups");
-  // item indices fit in 32 bits (at most kDirectMaxItems)
   int nh = (int)n;
   if (n_valid) {
     const int v = n_valid[h];
     nh = v < 0 ? 0 : (v < nh ? v : nh);
   }
   const bool split = nparts > 1;
-  const int sw = split ? kDirectPartWaves : kDirectWaves;
-  const int rows = direct_index_rows(nparts);
-  const int nbk = 1 << nbits;
-  const int nb8 = nbk >> 3;
-  uint16_t* cnt = reinterpret_cast<uint16_t*>(lds4);
+  const DirectShape shape = direct_shape(nbits, WIDE, nparts);
+  const int sw = shape.sw, rows = shape.rows;
+  CT* cnt = reinterpret_cast<CT*>(lds4);
   uint32_t* cnt32 = reinterpret_cast<uint32_t*>(lds4);
-  int32_t* pst = reinterpret_cast<int32_t*>(lds4 + rows * nb8);
+  CT4* cnt4 = reinterpret_cast<CT4*>(lds4);
+  constexpr int kPerInt4 = 16 / sizeof(CT);
+  int32_t* pst = reinterpret_cast<int32_t*>(lds4 + rows * (nbk / kPerInt4));
   const uint32_t bmask = (uint32_t)nbk - 1u;
-  const int32_t* ids = bucket + (int64_t)h * n;
+  const int32_t* ids = bucket + (int64_t)h * n * P;
   int32_t* ph = perm + (int64_t)h * n;
   int32_t* off = offsets + (int64_t)h * (nbk + 1);
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   if (nh == 0) {  // the whole workgroup: every bucket is empty
     if (part == 0)
-      for (int B = threadIdx.x; B <= nbk; B += NT) off[B] = 0;
+      for (int B = threadIdx.x; B <= nbk; B += kDirectThreads) off[B] = 0;
     return;
   }
+  // one counter up by one (LDS atomics; 16-bit counters in their 32-bit word)
+  auto inc = [&](int row, uint32_t b) {
+    const int i = row * nbk + (int)b;
+    if (WIDE) atomicAdd(&cnt32[i], 1u);
+    else atomicAdd(&cnt32[i >> 1], 1u << (16 * (b & 1u)));
+  };
   // this part's slice [sb, se), and the share [wbeg, wend) of wave w < sw
   const int pchunk = (nh + nparts - 1) / nparts;
   const int sb = part * pchunk < nh ? part * pchunk : nh;
@@ -114,16 +151,16 @@ __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
 #pragma unroll
     for (int r = 0; r < kTile; ++r) {
       const int i = t0 + r * FASTAR_WAVE + lane;
-      const uint32_t v = (uint32_t)ids[i < last ? i : last];
+      const uint32_t v = (uint32_t)ids[(int64_t)(i < last ? i : last) * P];
       b[r] = i < wend ? (v & bmask) : 0xFFFFFFFFu;
     }
   };
   auto load_batch = [&](int j0) {
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
-      const int j = j0 + r * NT + (int)threadIdx.x;
+      const int j = j0 + r * kDirectThreads + (int)threadIdx.x;
       const int i = j < sb ? j : j + (se - sb);
-      const uint32_t v = (uint32_t)ids[i < last ? i : last];
+      const uint32_t v = (uint32_t)ids[(int64_t)(i < last ? i : last) * P];
       ob[r] = j < nother ? (v & bmask) : 0xFFFFFFFFu;
     }
   };
@@ -132,13 +169,13 @@ __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
   // it writes)
   load_tile(wbeg);
   load_batch(0);
-  for (int i = threadIdx.x; i < rows * nb8; i += NT) lds4[i] = make_int4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < rows * (nbk / kPerInt4); i += kDirectThreads) lds4[i] = make_int4(0, 0, 0, 0);
   lds_barrier();
-  // counts (order does not matter): the 16-bit counter in its 32-bit word
-  for (int t0 = wbeg;;) {
+  // counts (order does not matter)
+  for (int t0 = wbeg; t0 < wend;) {
 #pragma unroll
     for (int r = 0; r < kTile; ++r)
-      if (b[r] != 0xFFFFFFFFu) atomicAdd(&cnt32[(wrow + (int)b[r]) >> 1], 1u << (16 * (b[r] & 1u)));
+      if (b[r] != 0xFFFFFFFFu) inc(wave, b[r]);
     t0 += kTile * FASTAR_WAVE;
     if (t0 >= wend) break;
     load_tile(t0);
@@ -147,68 +184,87 @@ __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
   for (int j0 = 0; j0 < nother;) {
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
-      const int j = j0 + r * NT + (int)threadIdx.x;
-      if (ob[r] != 0xFFFFFFFFu) {
-        const int row = j < sb ? sw : sw + 1;
-        atomicAdd(&cnt32[(row * nbk + (int)ob[r]) >> 1], 1u << (16 * (ob[r] & 1u)));
-      }
+      const int j = j0 + r * kDirectThreads + (int)threadIdx.x;
+      if (ob[r] != 0xFFFFFFFFu) inc(j < sb ? sw : sw + 1, ob[r]);
     }
-    j0 += kBatch * NT;
+    j0 += kBatch * kDirectThreads;
     if (j0 >= nother) break;
     load_batch(j0);
   }
   lds_barrier();
-  // exclusive scan over (bucket, row): thread t owns buckets 4t .. 4t + 3,
-  // one 64-bit word per row
+  // exclusive scan over (bucket, row): thread t owns buckets BPT t .. + BPT,
+  // four counters per LDS access
   const int t = threadIdx.x;
-  const int nb4 = nbk >> 2;
-  uint2* c64 = reinterpret_cast<uint2*>(lds4);
-  uint32_t tot[4] = {0u, 0u, 0u, 0u};
-#pragma unroll 2
-  for (int w = 0; w < rows; ++w) {
-    const uint2 cw = t < nb4 ? c64[w * nb4 + t] : make_uint2(0u, 0u);
-    tot[0] += cw.x & 0xFFFFu;
-    tot[1] += cw.x >> 16;
-    tot[2] += cw.y & 0xFFFFu;
-    tot[3] += cw.y >> 16;
+  const bool owner = t < nbk / BPT;
+  const int g0 = t * NG;  // its first 4-bucket group
+  auto get4 = [&](int w, int gi, uint32_t* o) {
+    const CT4 c = cnt4[w * (nbk / 4) + g0 + gi];
+    if constexpr (WIDE) {
+      o[0] = c.x; o[1] = c.y; o[2] = c.z; o[3] = c.w;
+    } else {
+      o[0] = c.x & 0xFFFFu; o[1] = c.x >> 16; o[2] = c.y & 0xFFFFu; o[3] = c.y >> 16;
+    }
+  };
+  auto put4 = [&](int w, int gi, const uint32_t* v) {
+    if constexpr (WIDE) cnt4[w * (nbk / 4) + g0 + gi] = make_uint4(v[0], v[1], v[2], v[3]);
+    else cnt4[w * (nbk / 4) + g0 + gi] = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
+  };
+  uint32_t tot[BPT];
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) tot[e] = 0u;
+  if (owner) {
+    for (int w = 0; w < rows; ++w) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        uint32_t c[4];
+        get4(w, gi, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tot[4 * gi + e] += c[e];
+      }
+    }
   }
-  const uint32_t local = tot[0] + tot[1] + tot[2] + tot[3];
+  uint32_t local = 0u;
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) local += tot[e];
   const uint32_t incl = wave_incl_scan_dpp(local);
   if (lane == FASTAR_WAVE - 1) wtot[wave] = (int)incl;
   lds_barrier();
   // plus the totals of the waves before (one load per lane, then a sum)
   const int wt = lane < kDirectWaves ? wtot[lane] : 0;
   uint32_t run = incl - local + (uint32_t)wave_sum_dpp(lane < wave ? wt : 0);
-  if (t < nb4) {
-    uint32_t base[4];
+  if (owner) {
+    uint32_t base[BPT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < BPT; ++e) {
       base[e] = run;
       run += tot[e];
     }
     // the bucket starts; part 0 writes the offsets
     if (part == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) off[4 * t + e] = (int)base[e];
-      if (t == nb4 - 1) off[nbk] = (int)run;
+      for (int e = 0; e < BPT; ++e) off[t * BPT + e] = (int)base[e];
+      if (t == nbk / BPT - 1) off[nbk] = (int)run;
     }
     if (split) {
       // this part's items follow those before its slice
-      const uint2 pw = c64[sw * nb4 + t];
-      base[0] += pw.x & 0xFFFFu;
-      base[1] += pw.x >> 16;
-      base[2] += pw.y & 0xFFFFu;
-      base[3] += pw.y >> 16;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        uint32_t c[4];
+        get4(sw, gi, c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) base[4 * gi + e] += c[e];
+      }
     }
     // each wave's base within each bucket (replacing the wave's counts)
-#pragma unroll 8
     for (int w = 0; w < sw; ++w) {
-      const uint2 cw = c64[w * nb4 + t];
-      c64[w * nb4 + t] = make_uint2(base[0] | (base[1] << 16), base[2] | (base[3] << 16));
-      base[0] += cw.x & 0xFFFFu;
-      base[1] += cw.x >> 16;
-      base[2] += cw.y & 0xFFFFu;
-      base[3] += cw.y >> 16;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        uint32_t c[4];
+        get4(w, gi, c);
+        put4(w, gi, &base[4 * gi]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) base[4 * gi + e] += c[e];
+      }
     }
   }
   lds_barrier();
@@ -239,14 +295,14 @@ __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
         if (stage) pst[pos] = (int32_t)i;
         else ph[pos] = (int32_t)i;
         // the lowest peer (rank 0) advances the counter
-        if (rank == 0) cnt[wrow + (int)bb] = (uint16_t)(pos + __popcll(peers));
+        if (rank == 0) cnt[wrow + (int)bb] = (CT)(pos + __popcll(peers));
       }
     }
   }
   // a staged permutation is written out coalesced
   if (stage) {
     lds_barrier();
-    for (int p = threadIdx.x; p < nh; p += NT) ph[p] = pst[p];
+    for (int p = threadIdx.x; p < nh; p += kDirectThreads) ph[p] = pst[p];
   }
 }
 

@@ -28,13 +28,15 @@ hipError_t launch_hash_multi(HashJobs jobs, int dim, int dtype, const void* plan
                              fastar_diag_t* diag, hipStream_t s);
 
 // index.hip -----------------------------------------------------------------
-// a one-probe bucket index (n items per head) that another index launch of
-// the same heads and bits builds in extra workgroups (the chunk sequence's
-// queries, next to the representatives)
+// a bucket index (n items per head, ids [H][n][P] sorted by their first
+// probe) that another index launch of the same heads and bits builds in
+// extra workgroups (the chunk sequence's queries, next to the
+// representatives)
 struct IndexJob {
   const int32_t* bucket;
   int64_t n;
   int n_bits;
+  int P;
   int32_t* offsets;
   int32_t* perm;
 };
@@ -45,9 +47,10 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
                                int32_t* perm, int32_t* ws, hipStream_t s,
                                const IndexJob* extra = nullptr);
 
-// whether launch_bucket_index uses the single counting pass (which another
-// such launch can also run, IndexJob)
-bool direct_index_supported(int64_t n, int n_probes, int n_bits);
+// whether launch_bucket_index uses the single counting pass for n items (and,
+// with n_extra > 0, can build an IndexJob of n_extra items in the same launch)
+bool direct_index_supported(int64_t n, int n_probes, int n_bits, int64_t n_extra = 0,
+                            int extra_probes = 1);
 
 // prune.hip -----------------------------------------------------------------
 hipError_t launch_prune(const int32_t* q_bucket, int heads, int64_t n_q, int n_probes,

@@ -141,7 +141,13 @@ def test_hash_strided_input(fa):
 
 
 @pytest.mark.parametrize("n,b,P", [(5000, 12, 1), (4096, 14, 2), (100, 3, 1), (0, 4, 1), (65535, 12, 1),
-                                   (3100, 3, 1), (12289, 9, 1), (1537, 12, 1)])
+                                   (3100, 3, 1), (12289, 9, 1), (1537, 12, 1),
+                                   # the counting pass at 13-14 bits, two probes, and
+                                   # 32-bit counters past 65535 items
+                                   (8192, 14, 2), (32768, 14, 1), (1000, 14, 1), (1, 14, 2),
+                                   (20000, 13, 2), (70000, 13, 1), (93600, 12, 1), (66000, 3, 1),
+                                   # the radix fallback
+                                   (5000, 15, 1), (3000, 2, 2), (70000, 14, 1)])
 def test_bucket_index_of_given_ids(fa, n, b, P):
     rng = np.random.default_rng(n + b)
     H = 3
@@ -160,6 +166,21 @@ def test_bucket_index_of_given_ids(fa, n, b, P):
         r_off, r_perm = oracle.bucket_index(ids[h, :nv], b)
         assert np.array_equal(off[h], r_off)
         assert np.array_equal(perm[h, :nv], r_perm)
+
+
+@pytest.mark.parametrize("n,b", [(70000, 12), (65535, 14), (9000, 13)])
+def test_bucket_index_one_full_bucket(fa, n, b):
+    # every item in one bucket: its count reaches n (past 16 bits for 70000)
+    H = 2
+    ids = np.full((H, n, 1), 5, dtype=np.int64)
+    ids[1, ::2, 0] = 7
+    off, perm = fa.fastar_bucket_index(i32(ids), b)
+    torch.cuda.synchronize()
+    off, perm = off.cpu().numpy(), perm.cpu().numpy()
+    for h in range(H):
+        r_off, r_perm = oracle.bucket_index(ids[h], b)
+        assert np.array_equal(off[h], r_off)
+        assert np.array_equal(perm[h], r_perm)
 
 
 # ---------------------------------------------------------------------------

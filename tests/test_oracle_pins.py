@@ -142,10 +142,10 @@ def test_index_by_hand_one_probe():
 
 
 def test_index_by_hand_two_probes():
+    # two probes: each query once, stably by its first bucket
     ids = np.array([[1, 0], [1, 3], [1, 0], [0, 2]])
     off, perm = bucket_index(ids, 2)
-    # keys (first, flipped bit): (1,0) (1,1) (1,0) (0,1)
-    assert perm.tolist() == [3, 0, 2, 1]
+    assert perm.tolist() == [3, 0, 1, 2]
     assert off.tolist() == [0, 1, 4, 4, 4]
 
 
