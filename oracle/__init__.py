@@ -27,6 +27,9 @@ arg-max, a threshold) settled on the exact real value of its operands:
                      attention formulation, section 5 "AnnSA", appendix A).
 * ``sequence``    -- one layer's per-chunk call sequence: hash, merge, prune,
                      self-attention, cross-attention.
+* ``recall``      -- attention recall (dense mass kept by the retained
+                     entries) and density, and the top-k reference
+                     (paperlayer.ai section 4, attention sparsity).
 
 Pins (tests marked ``not gpu``) tie each function to something other than
 itself: Lemma 5.1, dense attention in the one-bucket case, a library SDPA,
@@ -43,3 +46,4 @@ from .tempcache import TempCacheOracle  # noqa: F401
 from .annca import prune_prompt, cross_attention  # noqa: F401
 from .attention import dense_attention, bucket_attention  # noqa: F401
 from .sequence import run_chunk  # noqa: F401
+from .recall import attention_recall, bucket_retained, topk_recall  # noqa: F401

@@ -606,3 +606,56 @@ def test_sequence_bookkeeping_invariants():
     # chunk keys' ids are the hash of the chunk's own frames (not a set-up frame)
     k_last = w.k_frames[0, -1].astype(np.float64)
     assert np.array_equal(r["k_ids"][-T:], simhash(k_last, w.planes, 1)[:, 0])
+
+
+# --------------------------------------------------------------------------
+# Attention recall and density
+# --------------------------------------------------------------------------
+
+def test_recall_by_hand():
+    # two keys with logits 0 and ln 3 (scale 1): p = (1/4, 3/4)
+    from oracle import attention_recall
+    q = np.array([[1.0]])
+    k = np.array([[0.0], [math.log(3.0)]])
+    rec, den = attention_recall(q, k, np.array([[False, True]]), scale=1.0)
+    assert abs(rec[0] - 0.75) < 1e-15 and den[0] == 0.5
+    rec, den = attention_recall(q, k, np.array([[True, False]]), scale=1.0)
+    assert abs(rec[0] - 0.25) < 1e-15
+    # a bias of ln 3 on key 0 evens them out
+    rec, _ = attention_recall(q, k, np.array([[True, False]]), scale=1.0, bias=np.array([math.log(3.0), 0]))
+    assert abs(rec[0] - 0.5) < 1e-15
+
+
+def test_recall_one_bucket_is_one():
+    # b = 0: every key shares the query's bucket, nothing is dropped
+    from oracle import attention_recall, bucket_retained
+    rng = np.random.default_rng(40)
+    q, k = rng.standard_normal((20, 32)), rng.standard_normal((70, 32))
+    ids = simhash(q, np.zeros((0, 32)))
+    mask = bucket_retained(ids, simhash(k, np.zeros((0, 32)))[:, 0])
+    rec, den = attention_recall(q, k, mask)
+    assert np.allclose(rec, 1.0, atol=1e-14, rtol=0) and np.all(den == 1.0)
+
+
+def test_recall_is_lse_difference_and_topk_bounds_it():
+    # recall = exp(lse over the retained keys - lse over all keys) (the
+    # softmax normalisers), and the top-k reference at the same count keeps
+    # at least as much mass as any retained set of that size
+    from oracle import attention_recall, bucket_retained, topk_recall
+    rng = np.random.default_rng(41)
+    q, k = rng.standard_normal((30, 64)), rng.standard_normal((200, 64))
+    bias = np.log(rng.integers(1, 4, 200).astype(float))
+    planes = rng.standard_normal((3, 64))
+    q_ids, k_b = simhash(q, planes, 2), simhash(k, planes)[:, 0]
+    mask = bucket_retained(q_ids, k_b)
+    rec, den = attention_recall(q, k, mask, bias=bias)
+    _, lse_all = dense_attention(q, k, np.zeros((200, 1)), bias=bias)
+    _, lse_a = bucket_attention(q, q_ids, k, np.zeros((200, 1)), k_b, bias=bias)
+    assert np.max(np.abs(rec - np.exp(lse_a - lse_all))) < 1e-12
+    for i in range(30):
+        top = topk_recall(q[i:i + 1], k, den[i], bias=bias)[0]
+        assert top >= rec[i] - 1e-12
+    # the reference curve: 0 at density 0, 1 at density 1, nondecreasing
+    curve = [topk_recall(q, k, r, bias=bias).mean() for r in (0.0, 0.1, 0.3, 0.5, 1.0)]
+    assert curve[0] == 0.0 and abs(curve[-1] - 1.0) < 1e-12
+    assert all(a <= b + 1e-15 for a, b in zip(curve, curve[1:]))
