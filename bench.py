@@ -413,6 +413,38 @@ def stage_times(st, steps):
     return kern, extra
 
 
+def recall_stats(st, i=0):
+    """AnnSA's (and with a prompt AnnCA's) attention recall and density on
+    step i's merged cache: recall(q) = exp(lse_sparse - lse_dense), the dense
+    attention over the same keys and bias, both from the attention kernel
+    (the pages' measure of sparsity: the dense mass the retained entries
+    keep).  Means over queries and heads."""
+    import kv_compressed_attention_amd.fastar as fb
+
+    L, w, c = st.layer, st.w, st.caches[i]
+    q = st.inp(i)[0]
+    _, lse_s = fb.fastar_bucket_attention(q, c.rep_k, c.v_mean, q_bucket=L.q_ids, q_perm=L.q_perm,
+                                          key_bias=c.log_count, k_offsets=L.rep_off, k_perm=L.rep_perm,
+                                          n_bits=w.n_bits)
+    _, lse_d = fb.fastar_bucket_attention(q, c.rep_k, c.v_mean, key_bias=c.log_count,
+                                          n_key_list=c.n_groups)
+    _, stats = fb.fastar_attention_recall(lse_s, lse_d, c.n_groups, q_bucket=L.q_ids, k_offsets=L.rep_off,
+                                          n_bits=w.n_bits, want_recall=False)
+    s = stats.cpu().numpy()
+    out = {"annsa": {"recall": float(s[:, 0].mean()), "density": float(s[:, 1].mean()),
+                     "over": "the compressed cache with its + ln m bias"}}
+    if st.npr:
+        pk, pv = st.inp(i)[3], st.inp(i)[4]
+        _, lse_cs = fb.fastar_bucket_attention(q, pk, pv, key_list=L.kept_idx, n_key_list=L.n_kept)
+        _, lse_cd = fb.fastar_bucket_attention(q, pk, pv)
+        n_all = torch.full((st.H,), st.npr, dtype=torch.int32, device=q.device)
+        _, cs = fb.fastar_attention_recall(lse_cs, lse_cd, n_all, n_retained=L.n_kept, want_recall=False)
+        cs = cs.cpu().numpy()
+        out["annca"] = {"recall": float(cs[:, 0].mean()), "density": float(cs[:, 1].mean()),
+                        "over": "the prompt"}
+    return out
+
+
 def flushed_chunk_ms(st, flush, i):
     """One eager chunk on step i's buffers after a 512 MB write (the
     Infinity Cache flushed, and the GPU busy while the host enqueues), timed
@@ -486,6 +518,7 @@ def measure_workload(w, dev, steps, warmup, graph_steps, hot=True):
         st.inputs = st_hot_inputs
     st.restore()
     res["kernels"], res["extra"] = stage_times(st, steps)
+    res["recall"] = recall_stats(st)
     res["diag"] = st.layer.diag.tolist()
     res["setup"] = st
     return res
@@ -529,6 +562,14 @@ def rollout(w, dev, flush):
                     "cache_mb": float(ng.sum()) * group_bytes / 1e6})
     if layer.cache.status_code() != 0:
         raise RuntimeError("rollout cache overflowed")
+    import kv_compressed_attention_amd.fastar as fb
+    c = layer.cache
+    _, lse_d = fb.fastar_bucket_attention(q, c.rep_k, c.v_mean, key_bias=c.log_count, n_key_list=c.n_groups)
+    _, stats = fb.fastar_attention_recall(layer.lse_self, lse_d, c.n_groups, q_bucket=layer.q_ids,
+                                          k_offsets=layer.rep_off, n_bits=w.n_bits, want_recall=False)
+    s = stats.cpu().numpy()
+    out[-1]["annsa_recall"] = float(s[:, 0].mean())
+    out[-1]["annsa_density"] = float(s[:, 1].mean())
     return out
 
 
@@ -568,11 +609,16 @@ def annca(w, dev, steps):
     t_prune = graph_time([prune(i) for i in range(steps)])
     t_cross = graph_time([cross(i) for i in range(steps)])
     t_all = graph_time([f for i in range(steps) for f in (hash_(i), prune(i), cross(i))]) * 3
+    _, lse_d = fb.fastar_bucket_attention(ins[0][0], ins[0][1], ins[0][2])
+    _, rstats = fb.fastar_attention_recall(lse, lse_d, torch.full((H,), npr, dtype=torch.int32, device=dev),
+                                           n_retained=n_kept, want_recall=False)
+    rs = rstats.cpu().numpy()
     nk = n_kept.cpu().numpy()
     c_bytes, c_flops = cross_work(nk, H, nq, npr, d)
     return {"workload": w.name, "prompt_tokens": npr, "kept_per_head_mean": float(nk.mean()),
             "kept_per_head_min": int(nk.min()), "kept_per_head_max": int(nk.max()),
             "prune_ratio": 1.0 - float(nk.mean()) / npr,
+            "annca_recall": float(rs[:, 0].mean()), "annca_density": float(rs[:, 1].mean()),
             "ms": {"hash_queries_prompt": t_hash, "prune": t_prune, "attention_cross": t_cross,
                    "all": t_all},
             "query_tokens_per_s": nq / (t_all * 1e-3),
@@ -588,6 +634,7 @@ def summarize(w, res, steps):
         hot_ms = res["hot_s"] * 1e3 / steps
         d["hot"] = {"ms_per_step": hot_ms, "query_tokens_per_s": nq / (hot_ms * 1e-3)}
     d["kernels_ms"] = {k: v["launch_ms"] for k, v in res["kernels"].items()}
+    d["recall"] = res["recall"]
     a = res["kernels"]["attention_self"]
     d["attention_frac_hbm"] = a["frac_hbm"]
     return d
@@ -662,6 +709,7 @@ def main():
                       "frac_of_roofline": a["tflops"] / min(PEAK_BF16_TFLOPS, ai * PEAK_HBM_GBS / 1e3),
                       "query_tokens_per_s": nq / t_att, **res["extra"]},
         "launch": f"hip_graph{max(1, args.graph_steps)}_chunk",
+        "recall": res["recall"],
         "diag": res["diag"],
         "pages": PAGES,
     }
@@ -695,7 +743,9 @@ def main():
         roll = rollout(w3, dev, flush)
         extra["rollout"] = {"workload": w3.name, "chunks": roll,
                             "first_last_ms": [roll[0]["ms"], roll[-1]["ms"]],
-                            "last_chunk_density": roll[-1]["density"]}
+                            "last_chunk_density": roll[-1]["density"],
+                            "last_chunk_annsa": {"recall": roll[-1]["annsa_recall"],
+                                                 "density": roll[-1]["annsa_density"]}}
         del w3
         torch.cuda.empty_cache()
         out["extra_workloads"] = extra

@@ -237,7 +237,9 @@ fastar_status_t fastar_prune_prompt(const int32_t* q_bucket, int heads, int64_t 
  *           are visited in q_perm order (the index from fastar_hash).
  *   list    key_list and n_key_list given: every query attends to
  *           key_list[h][0 .. n_key_list[h]) (AnnCA over the kept prompt).
- *   dense   neither: every query attends to all k->tokens keys.
+ *   dense   neither: every query attends to all k->tokens keys; with
+ *           n_key_list alone, to keys 0 .. n_key_list[h] of head h (e.g. the
+ *           n_groups of a compressed cache).
  *   q      [H][Nq][d]; k, v [H][Nk][d], all the same dtype.
  *   key_bias [H][Nk] float32 or NULL (k's head stride is not used for it:
  *           the bias row of head h starts at h * k->tokens).
@@ -255,6 +257,33 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
                                         const int32_t* key_list, const int32_t* n_key_list,
                                         float scale, void* out, float* lse,
                                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * fastar_attention_recall -- attention recall and density of a sparse
+ * attention against the dense one over the same keys (paperlayer.ai section 4
+ * "Motivation", attention sparsity: the dense-attention mass the retained
+ * entries keep; section 3: about 85% at 30% density).  For query q with
+ * retained key set A(q):
+ *   recall(q)  = sum_{j in A(q)} softmax_j(logits over all keys)
+ *              = exp(lse_sparse(q) - lse_dense(q))
+ *   density(q) = |A(q)| / n_keys[h]
+ * lse_sparse, lse_dense [H][n_q] float32: the lse outputs of
+ * fastar_bucket_attention over A(q) and over all keys (same scale and bias).
+ * |A(q)| comes from
+ *   bucket mode  q_bucket [H][n_q][n_probes] and k_offsets [H][2^n_bits + 1]
+ *                (the keys of q's distinct probe buckets), or
+ *   list mode    n_retained [H] (q_bucket and k_offsets NULL): the same list
+ *                for every query of the head (AnnCA's kept prompt).
+ * n_keys [H] int32 device: keys the dense attention ran over.
+ * recall out [H][n_q] float32, or NULL; stats out [H][2] float32: the mean
+ * recall and the mean density over the head's queries.  An empty retained
+ * set has recall 0.  One launch; nothing synchronises.
+ * ---------------------------------------------------------------------- */
+fastar_status_t fastar_attention_recall(const float* lse_sparse, const float* lse_dense, int heads,
+                                        int64_t n_q, const int32_t* q_bucket, int n_probes,
+                                        const int32_t* k_offsets, int n_bits,
+                                        const int32_t* n_retained, const int32_t* n_keys,
+                                        float* recall, float* stats, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fastar_chunk -- one chunk of the per-layer sequence in one call, on one

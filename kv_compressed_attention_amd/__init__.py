@@ -9,6 +9,7 @@ load the library; the first call does, and fails loudly if it is missing.
 from .fastar import (  # noqa: F401
     FastarError,
     TempCache,
+    fastar_attention_recall,
     fastar_bucket_attention,
     fastar_bucket_index,
     fastar_hash,

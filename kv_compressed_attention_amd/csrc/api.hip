@@ -208,11 +208,11 @@ fastar_status_t attention_check(const fastar_tensor_t* q, const int32_t* q_bucke
     if (key_list || n_key_list) return fail(FASTAR_ERR_INVALID, "give either bucket segments or a key list");
     if ((st = check_bits(n_bits, n_probes)) != FASTAR_OK) return st;
     mode = 0;
-  } else if (key_list || n_key_list) {
-    if (!key_list || !n_key_list) return fail(FASTAR_ERR_INVALID, "list mode needs key_list and n_key_list");
+  } else if (key_list) {
+    if (!n_key_list) return fail(FASTAR_ERR_INVALID, "list mode needs key_list and n_key_list");
     mode = 1;
   } else {
-    mode = 2;
+    mode = 2;  // dense: all keys, or with n_key_list a head's first n_key_list[h]
   }
   *empty = (int64_t)q->heads * q->tokens == 0;
   if (*empty) return FASTAR_OK;
@@ -414,6 +414,32 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
                                              &empty);
   if (st != FASTAR_OK || empty) return st;
   return hip_status(fastar::launch_attention(a, stream), "bucket_attention");
+}
+
+// ---------------------------------------------------------------------------
+fastar_status_t fastar_attention_recall(const float* lse_sparse, const float* lse_dense, int heads,
+                                        int64_t n_q, const int32_t* q_bucket, int n_probes,
+                                        const int32_t* k_offsets, int n_bits,
+                                        const int32_t* n_retained, const int32_t* n_keys,
+                                        float* recall, float* stats, hipStream_t stream) {
+  if (heads < 0 || n_q < 0) return fail(FASTAR_ERR_INVALID, "negative size");
+  if ((int64_t)heads * n_q >= (int64_t)1 << 31) return fail(FASTAR_ERR_UNSUPPORTED, "heads*n_q must be < 2^31");
+  if (heads == 0) return FASTAR_OK;
+  if (!stats || !n_keys) return fail(FASTAR_ERR_INVALID, "stats and n_keys are required");
+  const bool bucket = k_offsets != nullptr;
+  if (bucket) {
+    fastar_status_t st = check_bits(n_bits, n_probes);
+    if (st != FASTAR_OK) return st;
+    if (n_q > 0 && !q_bucket) return fail(FASTAR_ERR_INVALID, "bucket mode needs q_bucket");
+    if (n_retained) return fail(FASTAR_ERR_INVALID, "give either k_offsets or n_retained");
+  } else if (!n_retained) {
+    return fail(FASTAR_ERR_INVALID, "give k_offsets (bucket mode) or n_retained (list mode)");
+  }
+  if (n_q > 0 && (!lse_sparse || !lse_dense)) return fail(FASTAR_ERR_INVALID, "lse arrays are NULL");
+  return hip_status(fastar::launch_recall(lse_sparse, lse_dense, heads, n_q, bucket ? q_bucket : nullptr,
+                                          n_probes, k_offsets, n_bits, n_retained, n_keys, recall, stats,
+                                          stream),
+                    "attention_recall");
 }
 
 }  // extern "C"

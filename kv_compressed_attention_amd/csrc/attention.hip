@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     } else {
       npass = 1;
       int64_t ke = Nk;
-      if (MODE == 1) {
+      if (n_key_list) {  // list mode, or dense over a head's first n keys
         const int64_t nl = n_key_list[h];
         ke = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
       }
@@ -491,10 +491,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
       kbeg = off[0];
       kend = off[1];
       idx = k_perm + (int64_t)h * Nk;
-    } else if (MODE == 1) {
+    } else if (n_key_list) {  // list mode, or dense over a head's first n keys
       const int64_t nl = n_key_list[h];
       kend = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
-      idx = key_list + (int64_t)h * Nk;
+      if (MODE == 1) idx = key_list + (int64_t)h * Nk;
     }
     for (int64_t kk = kbeg; kk < kend; ++kk) {
       const int64_t key = idx ? idx[kk] : kk;

@@ -70,6 +70,12 @@ struct AttnArgs {
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
+// recall.hip ----------------------------------------------------------------
+hipError_t launch_recall(const float* lse_s, const float* lse_d, int heads, int64_t nq,
+                         const int32_t* q_bucket, int P, const int32_t* k_offsets, int nbits,
+                         const int32_t* n_retained, const int32_t* n_keys, float* recall, float* stats,
+                         hipStream_t s);
+
 // tempcache.hip -------------------------------------------------------------
 struct MergeWs {
   int32_t* off;       // [H][n_frames+1][2^b+1] bucket offsets per table (see tempcache.hip)

@@ -97,6 +97,7 @@ _SIGNATURES = {
     "fastar_tempcache_merge": (_I, [_CP, _TP, _TP, _P, _I, _F, _P, _P, _P, _P, _SZ, _P, _P]),
     "fastar_prune_prompt": (_I, [_P, _I, _I64, _I, _P, _I64, _I, _P, _P, _P, _P]),
     "fastar_bucket_attention": (_I, [_TP, _P, _P, _I, _TP, _TP, _P, _P, _P, _I, _P, _P, _F, _P, _P, _P]),
+    "fastar_attention_recall": (_I, [_P, _P, _I, _I64, _P, _I, _P, _I, _P, _P, _P, _P, _P]),
     "fastar_chunk_workspace": (_SZ, [_P]),
     "fastar_chunk": (_I, [_P, _P, _SZ, _P, _P]),
     "fastar_chunk_noalloc": (_I, [_P, _P, _P]),
@@ -338,6 +339,25 @@ def fastar_bucket_attention(q, k, v, scale: Optional[float] = None, q_bucket=Non
                                        _ptr(n_key_list), float(scale), _ptr(out), _ptr(lse),
                                        _stream(stream)))
     return out, lse
+
+
+def fastar_attention_recall(lse_sparse, lse_dense, n_keys, q_bucket=None, k_offsets=None,
+                            n_bits: int = 0, n_retained=None, recall=None, stats=None,
+                            want_recall: bool = True, stream=None):
+    """Recall [H, n_q] (exp(lse_sparse - lse_dense)) and stats [H, 2] (mean
+    recall, mean density) of a sparse attention against the dense one."""
+    lib = library()
+    H, nq = lse_sparse.shape
+    dev = lse_sparse.device
+    if recall is None and want_recall:
+        recall = torch.empty(H, nq, dtype=torch.float32, device=dev)
+    if stats is None:
+        stats = torch.empty(H, 2, dtype=torch.float32, device=dev)
+    P = 1 if q_bucket is None else q_bucket.shape[2]
+    _check(lib.fastar_attention_recall(_ptr(lse_sparse), _ptr(lse_dense), H, nq, _ptr(q_bucket), P,
+                                       _ptr(k_offsets), n_bits, _ptr(n_retained), _ptr(n_keys),
+                                       _ptr(recall), _ptr(stats), _stream(stream)))
+    return recall, stats
 
 
 class ChunkCall:

@@ -241,3 +241,14 @@ def test_noalloc_chunk_rejects_oversized_workspace_without_launching(lib):
 def test_noalloc_scratch_size_matches_header():
     m = re.search(r"#define FASTAR_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
     assert m and int(m.group(1)) << int(m.group(2)) == fb.NOALLOC_SCRATCH_BYTES
+
+
+def test_recall_rejects_bad_arguments_without_launching(lib):
+    buf = ctypes.c_void_p(1 << 20)
+    # stats and n_keys are required; exactly one of k_offsets / n_retained
+    assert lib.fastar_attention_recall(buf, buf, 2, 10, buf, 1, buf, 4, None, buf, None, None, None) == 1
+    assert lib.fastar_attention_recall(buf, buf, 2, 10, buf, 1, buf, 4, buf, buf, None, buf, None) == 1
+    assert lib.fastar_attention_recall(buf, buf, 2, 10, None, 1, None, 4, None, buf, None, buf, None) == 1
+    assert lib.fastar_attention_recall(buf, buf, 2, 10, buf, 3, buf, 4, None, buf, None, buf, None) == 2
+    assert lib.fastar_attention_recall(None, buf, 2, 10, None, 1, None, 0, buf, buf, None, buf, None) == 1
+    assert lib.fastar_attention_recall(None, None, 0, 10, None, 1, None, 0, None, None, None, None, None) == 0
