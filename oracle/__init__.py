@@ -20,6 +20,10 @@ arg-max, a threshold) settled on the exact real value of its operands:
                      last key as representative, value mean and log-count
                      bias (paperlayer.ai section 5 "TempCache", appendix A,
                      Lemma 5.1; appendix C ablations).
+* ``tempcache_quant`` -- TempCache's quantized-ANN variant: the top-1 match
+                     compares b-bit scalar codes against every previous-frame
+                     token (paperlayer.ai section 5 "ANN Attention", appendix
+                     C quantization precision).
 * ``annca``       -- AnnCA prompt pruning and cross-attention over the kept
                      prompt tokens (gist.science technical summary, AnnCA).
 * ``attention``   -- dense softmax attention and AnnSA bucket-restricted
@@ -43,6 +47,7 @@ from .exact import exact_dot, exact_sqnorm, cos_compare, cos_at_least  # noqa: F
 from .simhash import simhash  # noqa: F401
 from .index import bucket_index  # noqa: F401
 from .tempcache import TempCacheOracle  # noqa: F401
+from .tempcache_quant import TempCacheQuantOracle, scalar_codes  # noqa: F401
 from .annca import prune_prompt, cross_attention  # noqa: F401
 from .attention import dense_attention, bucket_attention  # noqa: F401
 from .sequence import run_chunk  # noqa: F401

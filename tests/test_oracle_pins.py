@@ -659,3 +659,89 @@ def test_recall_is_lse_difference_and_topk_bounds_it():
     curve = [topk_recall(q, k, r, bias=bias).mean() for r in (0.0, 0.1, 0.3, 0.5, 1.0)]
     assert curve[0] == 0.0 and abs(curve[-1] - 1.0) < 1e-12
     assert all(a <= b + 1e-15 for a, b in zip(curve, curve[1:]))
+
+
+# --------------------------------------------------------------------------
+# TempCache with quantized matching
+# --------------------------------------------------------------------------
+
+def test_scalar_codes_by_hand():
+    from oracle import scalar_codes
+    x = np.array([[1.0, -0.5, 0.25, 0.0], [2.0, 1.0, -3.0, 0.5], [0.0, 0.0, 0.0, 0.0]])
+    # 8 bits, Q = 127, row scale max|x|: -63.5 ties to the even -64; 84.67 -> 85
+    assert scalar_codes(x, 8).tolist() == [[127, -64, 32, 0], [85, 42, -127, 21], [0, 0, 0, 0]]
+    # 2 bits, Q = 1: -0.5 ties to the even 0
+    assert scalar_codes(x, 2).tolist() == [[1, 0, 0, 0], [1, 0, -1, 0], [0, 0, 0, 0]]
+    # a positive power-of-two rescaling is exact and leaves the codes unchanged
+    assert np.array_equal(scalar_codes(x * 8.0, 5), scalar_codes(x, 5))
+
+
+@pytest.mark.parametrize("tau", [0.5, 1.0])
+def test_quant_exact_duplicates_merge_one_to_one(tau):
+    from oracle import TempCacheQuantOracle
+    T, d, F = 40, 32, 4
+    k0 = gaussian((T, d), 240, "bf16")
+    vs = gaussian((F, T, d), 241, "bf16")
+    tc = TempCacheQuantOracle(d, "bf16", 8)
+    for f in range(F):
+        g = tc.merge_frame(k0, vs[f], np.zeros(T, int), tau)
+        assert g.tolist() == list(range(T))
+    assert np.all(tc.count == F)
+    assert np.array_equal(tc.v_sum, vs.astype(np.float64).sum(axis=0))
+
+
+def test_quant_threshold_above_one_merges_nothing():
+    from oracle import TempCacheQuantOracle
+    T, d = 20, 16
+    k0 = gaussian((T, d), 242)
+    tc = TempCacheQuantOracle(d, "f32", 8)
+    for f in range(3):
+        g = tc.merge_frame(k0, np.ones((T, d)), np.zeros(T, int), 1.5)
+    assert tc.n_groups == 3 * T and g.tolist() == list(range(2 * T, 3 * T))
+
+
+def test_quant_matches_across_buckets_and_by_codes_by_hand():
+    # the quantized search sees every previous-frame token, whatever its
+    # bucket: key (1, 0.3) of bucket 7 finds (1, 0.29) of bucket 2.  At 2
+    # bits both code to (1, 0) (0.3 and 0.29 round to 0), cos 1; at 8 bits
+    # the codes (127, 38) and (127, 37) differ but pass tau = 0.999.
+    from oracle import TempCacheQuantOracle
+    for bits in (2, 8):
+        tc = TempCacheQuantOracle(2, "f32", bits)
+        tc.merge_frame(np.array([[0.0, 1.0], [1.0, 0.29]]), np.ones((2, 2)), np.array([5, 2]), 0.999)
+        g = tc.merge_frame(np.array([[1.0, 0.3]]), np.ones((1, 2)), np.array([7]), 0.999)
+        assert g.tolist() == [1] and tc.rep_bucket.tolist() == [5, 7]
+    # at 2 bits two different new keys code alike and tie on the candidate:
+    # the smaller index wins, the other opens a group
+    tc = TempCacheQuantOracle(2, "f32", 2)
+    tc.merge_frame(np.array([[1.0, 0.0]]), np.ones((1, 2)), np.zeros(1, int), 1.0)
+    g = tc.merge_frame(np.array([[1.0, 0.3], [1.0, 0.1]]), np.ones((2, 2)), np.zeros(2, int), 1.0)
+    assert g.tolist() == [0, 1]
+    # at 8 bits the second (closer) key wins instead
+    tc = TempCacheQuantOracle(2, "f32", 8)
+    tc.merge_frame(np.array([[1.0, 0.0]]), np.ones((1, 2)), np.zeros(1, int), 0.9)
+    g = tc.merge_frame(np.array([[1.0, 0.3], [1.0, 0.1]]), np.ones((2, 2)), np.zeros(2, int), 0.9)
+    assert g.tolist() == [1, 0]
+
+
+def test_quant_rescaled_keys_give_the_same_groups_and_conserve_mass():
+    from oracle import TempCacheQuantOracle
+    T, d, F = 64, 32, 5
+    rng = np.random.default_rng(243)
+    k = np.empty((F, T, d))
+    k[0] = rng.standard_normal((T, d))
+    for f in range(1, F):
+        keep = rng.random(T) < 0.7
+        k[f] = np.where(keep[:, None], k[f - 1] + 0.02 * rng.standard_normal((T, d)), rng.standard_normal((T, d)))
+    k = round_to_dtype(k, "bf16")
+    v = gaussian((F, T, d), 244, "bf16")
+    scale = 2.0 ** rng.integers(-3, 4, (F, T, 1))            # exact in bf16
+    a, b = TempCacheQuantOracle(d, "bf16", 8), TempCacheQuantOracle(d, "bf16", 8)
+    ga = [a.merge_frame(k[f], v[f], np.zeros(T, int), 0.99) for f in range(F)]
+    gb = [b.merge_frame(k[f] * scale[f], v[f], np.zeros(T, int), 0.99) for f in range(F)]
+    assert all(np.array_equal(x, y) for x, y in zip(ga, gb))
+    assert a.count.sum() == F * T and 0 < a.n_groups < F * T
+    assert np.array_equal(a.v_sum.sum(axis=0), v.astype(np.float64).reshape(-1, d).sum(axis=0))
+    assert np.array_equal(np.bincount(np.concatenate(ga), minlength=a.n_groups), a.count)
+    for g in ga:
+        assert len(set(g.tolist())) == T
