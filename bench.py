@@ -247,7 +247,7 @@ def graph_time(fns, before=None, reps=1):
 class Setup:
     """A workload's layer, its pre-chunk cache, and per-step copies."""
 
-    def __init__(self, w, dev, steps, rotate):
+    def __init__(self, w, dev, steps, rotate, match="lsh"):
         import kv_compressed_attention_amd as fa
         from kv_compressed_attention_amd.layer import FastARLayer
 
@@ -258,7 +258,7 @@ class Setup:
         npr = 0 if w.prompt_k is None else w.prompt_k.shape[1]
         self.npr = npr
         self.layer = FastARLayer(H, d, w.n_bits, w.n_probes, w.tau, T, F * T, w.n_queries,
-                                 w.chunk_frames, n_prompt=npr, dtype=self.tdt, device=dev)
+                                 w.chunk_frames, n_prompt=npr, dtype=self.tdt, device=dev, match=match)
         self.layer.set_planes(self.up(w.planes))
         for f in range(w.setup_frames):
             self.layer.merge(self.up(w.k_frames[:, f]), self.up(w.v_frames[:, f]), 1,
@@ -361,7 +361,7 @@ def stage_times(st, steps):
     run("merge", lambda i: (lambda: fb.fastar_tempcache_merge(
         st.caches[i], st.inp(i)[1], st.inp(i)[2], L.k_ids.view(H, -1), w.chunk_frames, w.tau,
         group_of_new=L.group_of_new, rep_offsets=L.rep_off, rep_perm=L.rep_perm, ws=L.ws,
-        diag=L.diag)), before=st.restore)
+        diag=L.diag, opts=L.opts)), before=st.restore)
     n_before = st.pristine.n_groups.cpu().numpy()
     n_after = st.caches[-1].n_groups.cpu().numpy()
     gon = L.group_of_new.cpu().numpy()
@@ -505,10 +505,10 @@ KERNEL_FILES = {"attention_self": "attention.hip", "attention_cross": "attention
                 "merge": "tempcache.hip", "index_queries": "index.hip", "prune": "prune.hip"}
 
 
-def measure_workload(w, dev, steps, warmup, graph_steps, hot=True):
+def measure_workload(w, dev, steps, warmup, graph_steps, hot=True, match="lsh"):
     """Cold (rotated inputs) and, optionally, hot chunk steps plus per-stage
-    kernel times of workload w."""
-    st = Setup(w, dev, steps, rotate=True)
+    kernel times of workload w (TempCache's match: "lsh" or "quant")."""
+    st = Setup(w, dev, steps, rotate=True, match=match)
     res = {"cold_s": timed_steps(st, steps, warmup, graph_steps)}
     if hot:
         st_hot_inputs = st.inputs
@@ -519,6 +519,8 @@ def measure_workload(w, dev, steps, warmup, graph_steps, hot=True):
     st.restore()
     res["kernels"], res["extra"] = stage_times(st, steps)
     res["recall"] = recall_stats(st)
+    ng = st.caches[0].n_groups.cpu().numpy()
+    res["cache_density"] = float(ng.mean()) / (w.n_frames * st.T)
     res["diag"] = st.layer.diag.tolist()
     res["setup"] = st
     return res
@@ -635,6 +637,7 @@ def summarize(w, res, steps):
         d["hot"] = {"ms_per_step": hot_ms, "query_tokens_per_s": nq / (hot_ms * 1e-3)}
     d["kernels_ms"] = {k: v["launch_ms"] for k, v in res["kernels"].items()}
     d["recall"] = res["recall"]
+    d["cache_density"] = res["cache_density"]
     a = res["kernels"]["attention_self"]
     d["attention_frac_hbm"] = a["frac_hbm"]
     return d
@@ -710,6 +713,7 @@ def main():
                       "query_tokens_per_s": nq / t_att, **res["extra"]},
         "launch": f"hip_graph{max(1, args.graph_steps)}_chunk",
         "recall": res["recall"],
+        "cache_density": res["cache_density"],
         "diag": res["diag"],
         "pages": PAGES,
     }
@@ -729,6 +733,13 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extra:
+        # TempCache's quantized match (8-bit codes, every previous-frame token a
+        # candidate) on the same workload
+        rq = measure_workload(w, dev, args.steps, args.warmup, args.graph_steps, hot=False, match="quant")
+        rq.pop("setup")
+        out["tempcache_quant8"] = summarize(w, rq, args.steps)
+        del rq
+        torch.cuda.empty_cache()
         extra = {}
         if args.workload != 1:
             w1 = make_workload(1)

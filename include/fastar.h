@@ -190,6 +190,26 @@ typedef struct {
  * capture. */
 fastar_status_t fastar_cache_status(const fastar_cache_t* cache, int clear, hipStream_t stream);
 
+/* TempCache variants (paperlayer.ai section 5 "ANN Attention" and appendix C).
+ *   match           FASTAR_MATCH_LSH (default): a new key's candidates are
+ *                   the previous frame's tokens with its bucket; similarity is
+ *                   the exact cosine.
+ *                   FASTAR_MATCH_QUANT: every previous-frame token is a
+ *                   candidate; similarity is the cosine of per-row
+ *                   symmetric code_bits-bit scalar codes of the two keys
+ *                   (c_i = round_half_even(Q x_i / max|x|), Q = 2^(bits-1) - 1:
+ *                   the pages' quantized ANN, 8 bits by default), decided
+ *                   exactly on the integer codes.
+ *   code_bits       2..8 with FASTAR_MATCH_QUANT (0 means 8).
+ * Everything else (threshold, one-to-one rule, last-key representative,
+ * value means, ln m bias) is the same for every match. */
+typedef enum { FASTAR_MATCH_LSH = 0, FASTAR_MATCH_QUANT = 1 } fastar_match_t;
+typedef struct {
+  int32_t match;
+  int32_t code_bits;
+  int32_t reserved[6];
+} fastar_merge_opts_t;
+
 /* fastar_tempcache_merge -- merge n_frames new frames, in order.
  *   k_new, v_new  [H][n_frames * tokens_per_frame][dim], cache dtype.
  *   k_new_bucket  [H][n_frames * tokens_per_frame] int32 (fastar_hash, one
@@ -207,6 +227,21 @@ fastar_status_t fastar_cache_status(const fastar_cache_t* cache, int clear, hipS
  *                 NULL: bucket index of the representatives after the merge.
  */
 size_t fastar_tempcache_workspace(const fastar_cache_t* cache, int n_frames);
+/* the same with options (opts NULL: the defaults, as fastar_tempcache_merge) */
+size_t fastar_tempcache_workspace_ex(const fastar_cache_t* cache, int n_frames,
+                                     const fastar_merge_opts_t* opts);
+fastar_status_t fastar_tempcache_merge_ex(const fastar_cache_t* cache, const fastar_tensor_t* k_new,
+                                          const fastar_tensor_t* v_new, const int32_t* k_new_bucket,
+                                          int n_frames, float tau, const fastar_merge_opts_t* opts,
+                                          int32_t* group_of_new, int32_t* rep_offsets,
+                                          int32_t* rep_perm, void* ws, size_t ws_bytes,
+                                          fastar_diag_t* diag, hipStream_t stream);
+
+/* fastar_scalar_codes -- the per-row symmetric b-bit codes of FASTAR_MATCH_QUANT
+ * (bits 2..8) of x [H][N][d]: codes out [H][N][d] int8 (contiguous),
+ * norm2 out [H][N] int32, the sum of squared codes. */
+fastar_status_t fastar_scalar_codes(const fastar_tensor_t* x, int bits, int8_t* codes, int32_t* norm2,
+                                    hipStream_t stream);
 fastar_status_t fastar_tempcache_merge(const fastar_cache_t* cache, const fastar_tensor_t* k_new,
                                        const fastar_tensor_t* v_new,
                                        const int32_t* k_new_bucket, int n_frames, float tau,
@@ -333,6 +368,8 @@ typedef struct {
   int32_t* n_kept;                  /* [H]                                      */
   void* out_cross;                  /* [H][Nq][d]                               */
   float* lse_cross;                 /* [H][Nq] or NULL                          */
+  /* TempCache variant (NULL: the defaults) */
+  const fastar_merge_opts_t* merge_opts;
 } fastar_chunk_t;
 
 size_t fastar_chunk_workspace(const fastar_chunk_t* args);

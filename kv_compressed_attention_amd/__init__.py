@@ -15,8 +15,10 @@ from .fastar import (  # noqa: F401
     fastar_hash,
     fastar_hash_multi,
     fastar_prune_prompt,
+    fastar_scalar_codes,
     fastar_tempcache_merge,
     fastar_version,
     library,
+    merge_opts,
     new_diag,
 )

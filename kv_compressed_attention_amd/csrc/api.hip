@@ -109,6 +109,30 @@ size_t merge_workspace(const fastar_cache_t* c, int n_frames) {
          align_up(16 * H * (size_t)c->capacity);
 }
 
+// the match kind and code bits of opts (NULL: defaults)
+fastar_status_t merge_opts(const fastar_merge_opts_t* o, int* match, int* bits) {
+  *match = FASTAR_MATCH_LSH;
+  *bits = 8;
+  if (!o) return FASTAR_OK;
+  if (o->match != FASTAR_MATCH_LSH && o->match != FASTAR_MATCH_QUANT)
+    return fail(FASTAR_ERR_UNSUPPORTED, "merge option match %d unknown", o->match);
+  *match = o->match;
+  if (o->match == FASTAR_MATCH_QUANT && o->code_bits != 0) {
+    if (o->code_bits < 2 || o->code_bits > 8)
+      return fail(FASTAR_ERR_UNSUPPORTED, "code_bits %d not in [2, 8]", o->code_bits);
+    *bits = o->code_bits;
+  }
+  return FASTAR_OK;
+}
+
+size_t merge_workspace_ex(const fastar_cache_t* c, int n_frames, const fastar_merge_opts_t* o) {
+  int match, bits;
+  if (merge_opts(o, &match, &bits) != FASTAR_OK) return 0;
+  const size_t base = merge_workspace(c, n_frames);
+  if (match != FASTAR_MATCH_QUANT || base == 0) return base;
+  return base + fastar::quant_workspace_bytes(c->heads, c->tokens_per_frame, n_frames, c->dim);
+}
+
 // everything fastar_tempcache_merge checks for a call with n_frames > 0 and
 // heads > 0 (ws: at least merge_workspace bytes)
 fastar_status_t merge_check(const fastar_cache_t* c, const fastar_tensor_t* k_new,
@@ -339,17 +363,24 @@ size_t fastar_tempcache_workspace(const fastar_cache_t* c, int n_frames) {
   return merge_workspace(c, n_frames);
 }
 
-fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
-                                       const fastar_tensor_t* v_new, const int32_t* k_new_bucket,
-                                       int n_frames, float tau, int32_t* group_of_new,
-                                       int32_t* rep_offsets, int32_t* rep_perm, void* ws,
-                                       size_t ws_bytes, fastar_diag_t* diag, hipStream_t stream) {
-  fastar_status_t st = merge_check(c, k_new, v_new, k_new_bucket, n_frames, tau, rep_offsets, rep_perm);
+size_t fastar_tempcache_workspace_ex(const fastar_cache_t* c, int n_frames, const fastar_merge_opts_t* opts) {
+  return merge_workspace_ex(c, n_frames, opts);
+}
+
+fastar_status_t fastar_tempcache_merge_ex(const fastar_cache_t* c, const fastar_tensor_t* k_new,
+                                          const fastar_tensor_t* v_new, const int32_t* k_new_bucket,
+                                          int n_frames, float tau, const fastar_merge_opts_t* opts,
+                                          int32_t* group_of_new, int32_t* rep_offsets, int32_t* rep_perm,
+                                          void* ws, size_t ws_bytes, fastar_diag_t* diag, hipStream_t stream) {
+  int match, bits;
+  fastar_status_t st = merge_opts(opts, &match, &bits);
   if (st != FASTAR_OK) return st;
+  if ((st = merge_check(c, k_new, v_new, k_new_bucket, n_frames, tau, rep_offsets, rep_perm)) != FASTAR_OK)
+    return st;
+  const size_t need = merge_workspace_ex(c, n_frames, opts);
   if (c->heads == 0 || n_frames == 0) {
     if (rep_offsets && c->heads > 0) {
-      if (!ws || ws_bytes < merge_workspace(c, n_frames))
-        return fail(FASTAR_ERR_WORKSPACE, "workspace too small");
+      if (!ws || ws_bytes < need) return fail(FASTAR_ERR_WORKSPACE, "workspace too small");
       const size_t off = merge_workspace(c, n_frames) - align_up(16 * (size_t)c->heads * (size_t)c->capacity);
       return hip_status(fastar::launch_bucket_index(c->rep_bucket, c->heads, c->capacity, 1, c->n_bits,
                                                     c->n_groups, rep_offsets, rep_perm,
@@ -358,13 +389,40 @@ fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_ten
     }
     return FASTAR_OK;
   }
-  if (!ws || ws_bytes < merge_workspace(c, n_frames))
-    return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", merge_workspace(c, n_frames),
-                ws_bytes);
+  if (!ws || ws_bytes < need)
+    return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need, ws_bytes);
+  const fastar::MergeWs mw = merge_carve(c, n_frames, ws);
+  if (match == FASTAR_MATCH_QUANT) {
+    const fastar::QuantWs q = fastar::quant_carve(c->heads, c->tokens_per_frame, n_frames, c->dim,
+                                                  (char*)ws + merge_workspace(c, n_frames));
+    return hip_status(fastar::launch_tempcache_merge_quant(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,
+                                                           bits, group_of_new, rep_offsets, rep_perm, mw, q,
+                                                           diag, stream),
+                      "tempcache_merge (quantized match)");
+  }
   return hip_status(fastar::launch_tempcache_merge(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,
-                                                   group_of_new, rep_offsets, rep_perm,
-                                                   merge_carve(c, n_frames, ws), diag, stream),
+                                                   group_of_new, rep_offsets, rep_perm, mw, diag, stream),
                     "tempcache_merge");
+}
+
+fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
+                                       const fastar_tensor_t* v_new, const int32_t* k_new_bucket,
+                                       int n_frames, float tau, int32_t* group_of_new,
+                                       int32_t* rep_offsets, int32_t* rep_perm, void* ws,
+                                       size_t ws_bytes, fastar_diag_t* diag, hipStream_t stream) {
+  return fastar_tempcache_merge_ex(c, k_new, v_new, k_new_bucket, n_frames, tau, nullptr, group_of_new,
+                                   rep_offsets, rep_perm, ws, ws_bytes, diag, stream);
+}
+
+fastar_status_t fastar_scalar_codes(const fastar_tensor_t* x, int bits, int8_t* codes, int32_t* norm2,
+                                    hipStream_t stream) {
+  fastar_status_t st = check_tensor(x, "x");
+  if (st != FASTAR_OK) return st;
+  if (bits < 2 || bits > 8) return fail(FASTAR_ERR_UNSUPPORTED, "bits %d not in [2, 8]", bits);
+  if ((int64_t)x->heads * x->tokens == 0) return FASTAR_OK;
+  if (!codes || !norm2) return fail(FASTAR_ERR_INVALID, "codes and norm2 are required");
+  if (((uintptr_t)codes & 7u) != 0) return fail(FASTAR_ERR_INVALID, "codes must be 8-byte aligned");
+  return hip_status(fastar::launch_scalar_codes(*x, bits, codes, norm2, stream), "scalar_codes");
 }
 
 fastar_status_t fastar_cache_status(const fastar_cache_t* c, int clear, hipStream_t stream) {
@@ -470,7 +528,7 @@ extern "C" {
 
 size_t fastar_chunk_workspace(const fastar_chunk_t* a) {
   if (!a || !a->cache || !a->q) return 0;
-  return merge_workspace(a->cache, a->n_frames) + chunk_index_ws(a);
+  return merge_workspace_ex(a->cache, a->n_frames, a->merge_opts) + chunk_index_ws(a);
 }
 
 fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes, fastar_diag_t* diag,
@@ -496,6 +554,8 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   if (a->q->tokens > 0 && !a->q_bucket) return fail(FASTAR_ERR_INVALID, "q_bucket is NULL");
   // 2. the merge (and the queries' index)
   if (c->n_bits != a->n_bits) return fail(FASTAR_ERR_INVALID, "the cache's n_bits differs from n_bits");
+  int match, bits;
+  if ((st = merge_opts(a->merge_opts, &match, &bits)) != FASTAR_OK) return st;
   if ((st = merge_check(c, a->k_new, a->v_new, a->k_bucket, a->n_frames, a->tau, a->rep_offsets,
                         a->rep_perm)) != FASTAR_OK)
     return st;
@@ -530,8 +590,8 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   fastar::MergeWs mw = merge_carve(c, a->n_frames, ws);
   fastar::HashJobs qjobs;
   qjobs.count = 0;
-  if (a->q->dtype == FASTAR_BF16 && c->dtype == FASTAR_BF16 && a->q->dim == c->dim && c->heads > 0 &&
-      (int64_t)a->q->heads * a->q->tokens > 0) {
+  if (match == FASTAR_MATCH_LSH && a->q->dtype == FASTAR_BF16 && c->dtype == FASTAR_BF16 &&
+      a->q->dim == c->dim && c->heads > 0 && (int64_t)a->q->heads * a->q->tokens > 0) {
     qjobs.count = 1;
     qjobs.j[0] = jobs.j[0];
     for (int i = 1; i < jobs.count; ++i) jobs.j[i - 1] = jobs.j[i];
@@ -551,13 +611,22 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   const bool fused = a->q->tokens > 0 &&
                      fastar::direct_index_supported(c->capacity, 1, c->n_bits, a->q->tokens, a->n_probes);
   if (fused) mw.also_index = &qj;
-  if ((st = hip_status(fastar::launch_tempcache_merge(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,
-                                                      a->tau, a->group_of_new, a->rep_offsets,
-                                                      a->rep_perm, mw, diag, stream),
-                       "tempcache_merge")) != FASTAR_OK)
+  if (match == FASTAR_MATCH_QUANT) {
+    const fastar::QuantWs q = fastar::quant_carve(c->heads, c->tokens_per_frame, a->n_frames, c->dim,
+                                                  (char*)ws + merge_workspace(c, a->n_frames));
+    if ((st = hip_status(fastar::launch_tempcache_merge_quant(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,
+                                                              a->tau, bits, a->group_of_new, a->rep_offsets,
+                                                              a->rep_perm, mw, q, diag, stream),
+                         "tempcache_merge (quantized match)")) != FASTAR_OK)
+      return st;
+  } else if ((st = hip_status(fastar::launch_tempcache_merge(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,
+                                                             a->tau, a->group_of_new, a->rep_offsets,
+                                                             a->rep_perm, mw, diag, stream),
+                              "tempcache_merge")) != FASTAR_OK) {
     return st;
+  }
   if (!fused) {
-    int32_t* iws = (int32_t*)((char*)ws + merge_workspace(c, a->n_frames));
+    int32_t* iws = (int32_t*)((char*)ws + merge_workspace_ex(c, a->n_frames, a->merge_opts));
     if ((st = hip_status(fastar::launch_bucket_index(a->q_bucket, a->q->heads, a->q->tokens, a->n_probes,
                                                      a->n_bits, nullptr, a->q_offsets, a->q_perm, iws,
                                                      stream),

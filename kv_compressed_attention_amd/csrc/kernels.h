@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "../../include/fastar.h"
+#include "merge_args.h"
 
 namespace fastar {
 
@@ -95,6 +96,36 @@ struct MergeWs {
   const void* hash_planes = nullptr;
   int hash_bits = 0;
 };
+// the merge's last launches for any match kind: the group updates (from the
+// links, successors and opener counts in a) and the representatives' index
+hipError_t launch_merge_apply(const fastar_cache_t& c, const fastar_tensor_t& kn, const fastar_tensor_t& vn,
+                              const int32_t* kb, const MergeArgs& a, int32_t* group_of_new,
+                              int32_t* rep_offsets, int32_t* rep_perm, const MergeWs& ws,
+                              fastar_diag_t* diag, hipStream_t s);
+
+// tempcache_quant.hip ---------------------------------------------------------
+// per-row symmetric b-bit codes of x's rows: codes [rows][dim] int8, norm2
+// [rows] int32 (sum of squared codes)
+hipError_t launch_scalar_codes(const fastar_tensor_t& x, int bits, int8_t* codes, int32_t* norm2,
+                               hipStream_t s);
+// the quantized match's workspace (beyond MergeWs's link / nextj / ocnt)
+struct QuantWs {
+  int8_t* codes;   // [H][F+1][T][dim]
+  int32_t* norm2;  // [H][F+1][T]
+  float* rn;       // [H][F+1][T]   1 / sqrt(norm2) (0 for a zero code)
+  float* bias;     // [H][F+1][T]   0, or -inf for a token that is no candidate
+  int32_t* ptgt;   // [H][F][T]     proposed candidate, or -1
+  int32_t* pdot;   // [H][F][T]     exact code dot product with it
+  float* pcos;     // [H][F][T]     float32 cosine estimate
+};
+size_t quant_workspace_bytes(int heads, int T, int F, int dim);
+QuantWs quant_carve(int heads, int T, int F, int dim, void* ws);
+hipError_t launch_tempcache_merge_quant(const fastar_cache_t& c, const fastar_tensor_t& k_new,
+                                        const fastar_tensor_t& v_new, const int32_t* k_new_bucket,
+                                        int n_frames, float tau, int bits, int32_t* group_of_new,
+                                        int32_t* rep_offsets, int32_t* rep_perm, const MergeWs& ws,
+                                        const QuantWs& qws, fastar_diag_t* diag, hipStream_t s);
+
 hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
                                   const fastar_tensor_t& v_new, const int32_t* k_new_bucket,
                                   int n_frames, float tau, int32_t* group_of_new,

@@ -35,6 +35,7 @@
 #include "common.h"
 #include "hash_body.h"
 #include "kernels.h"
+#include "merge_args.h"
 
 namespace fastar {
 
@@ -292,35 +293,6 @@ constexpr size_t kTcIndexLds = 152 * 1024;
 constexpr int kMatchHashTiles = 2;
 constexpr int kMatchHashPlanes = 2;
 
-struct MergeArgs {
-  int H, Tf, cap, F, nbits;
-  int64_t kb_stride;  // F * Tf
-  // per head, tables t = 0..F sorted by bucket: table 0 holds the cache's
-  // last frame (the frontier), table f + 1 new frame f
-  int32_t* off;       // [H][F+1][2^b + 1] bucket starts, then the number kept
-  int32_t* tok;       // [H][F+1][Tf] tokens, bucket by bucket
-  int32_t* tbk;       // [H][F+1][Tf] their buckets
-  int32_t* candg;     // [H][Tf] groups of table 0's tokens
-  int32_t* link;      // [H][F][Tf] f = 0: frontier group the token extends;
-                      //            f > 0: frame f - 1 token it extends; -1: opens a group
-  int32_t* ocnt;      // [H][nblk + 1] tokens that open groups, per 64 tokens of
-                      // (frame, j) order (nblk = ceil(F Tf / 64) blocks), then
-                      // the group count before the call
-  int32_t* nextj;     // [H][F][Tf] token of frame f + 1 that extends this one, or -1
-  int32_t* prop;      // [H][F][3][Tf] proposals of workgroups whose lists stay global
-  int32_t* mrange;    // [H][F][match workgroups][4] key positions [p0, p1), candidates [c0, c1)
-};
-
-__device__ __forceinline__ int64_t off_off(const MergeArgs& a, int h, int t) {
-  return ((int64_t)h * (a.F + 1) + t) * ((1 << a.nbits) + 1);
-}
-__device__ __forceinline__ int64_t tok_off(const MergeArgs& a, int h, int t) {
-  return ((int64_t)h * (a.F + 1) + t) * a.Tf;
-}
-__device__ __forceinline__ int64_t frame_off(const MergeArgs& a, int h, int f) {
-  return ((int64_t)h * a.F + f) * a.Tf;
-}
-__device__ __forceinline__ int ocnt_blocks(const MergeArgs& a) { return (a.F * a.Tf + 63) >> 6; }
 // sorted keys per match workgroup (before rounding to whole buckets)
 constexpr int kKeysPerGroup = 64;
 __host__ __device__ __forceinline__ int match_groups(int Tf) { return (Tf + kKeysPerGroup - 1) / kKeysPerGroup; }
@@ -1218,7 +1190,35 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   return hipSuccess;
 }
 
+template <typename T, int D>
+hipError_t apply_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fastar_tensor_t& vn,
+                    const int32_t* kb, const MergeArgs& a, int32_t* group_of_new, int32_t* rep_offsets,
+                    int32_t* rep_perm, const MergeWs& ws, fastar_diag_t* diag, hipStream_t s) {
+  hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)a.F * a.Tf + 15) / 16), (unsigned)a.H),
+                     dim3(256), 0, s, (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count,
+                     c.rep_bucket, c.n_groups, c.frontier, group_of_new, (const T*)kn.data, kn.stride_head,
+                     kn.stride_token, (const T*)vn.data, vn.stride_head, vn.stride_token, kb, a,
+                     c.status, diag);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (rep_offsets && rep_perm)
+    return launch_bucket_index(c.rep_bucket, a.H, c.capacity, 1, c.n_bits, c.n_groups, rep_offsets,
+                               rep_perm, ws.index_ws, s, ws.also_index);
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_merge_apply(const fastar_cache_t& c, const fastar_tensor_t& kn, const fastar_tensor_t& vn,
+                              const int32_t* kb, const MergeArgs& a, int32_t* group_of_new,
+                              int32_t* rep_offsets, int32_t* rep_perm, const MergeWs& ws,
+                              fastar_diag_t* diag, hipStream_t s) {
+  if (c.dtype == FASTAR_BF16)
+    return c.dim == 64 ? apply_td<uint16_t, 64>(c, kn, vn, kb, a, group_of_new, rep_offsets, rep_perm, ws, diag, s)
+                       : apply_td<uint16_t, 128>(c, kn, vn, kb, a, group_of_new, rep_offsets, rep_perm, ws, diag, s);
+  return c.dim == 64 ? apply_td<float, 64>(c, kn, vn, kb, a, group_of_new, rep_offsets, rep_perm, ws, diag, s)
+                     : apply_td<float, 128>(c, kn, vn, kb, a, group_of_new, rep_offsets, rep_perm, ws, diag, s);
+}
 
 hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
                                   const fastar_tensor_t& v_new, const int32_t* k_new_bucket,

@@ -51,6 +51,19 @@ class FastarCache(ctypes.Structure):
     ]
 
 
+class FastarMergeOpts(ctypes.Structure):
+    _fields_ = [("match", ctypes.c_int32), ("code_bits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
+
+
+MATCH = {"lsh": 0, "quant": 1}
+
+
+def merge_opts(match: str = "lsh", code_bits: int = 8) -> FastarMergeOpts:
+    """fastar_merge_opts_t for a TempCache variant ("lsh" or "quant")."""
+    return FastarMergeOpts(MATCH[match], code_bits)
+
+
 class FastarChunk(ctypes.Structure):
     _fields_ = [
         ("q", ctypes.c_void_p), ("n_probes", ctypes.c_int),
@@ -65,6 +78,7 @@ class FastarChunk(ctypes.Structure):
         ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("p_bucket", ctypes.c_void_p), ("keep", ctypes.c_void_p), ("kept_idx", ctypes.c_void_p),
         ("n_kept", ctypes.c_void_p), ("out_cross", ctypes.c_void_p), ("lse_cross", ctypes.c_void_p),
+        ("merge_opts", ctypes.c_void_p),
     ]
 
 
@@ -93,6 +107,9 @@ _SIGNATURES = {
     "fastar_bucket_index_workspace": (_SZ, [_I, _I64]),
     "fastar_bucket_index": (_I, [_P, _I, _I64, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "fastar_tempcache_workspace": (_SZ, [_CP, _I]),
+    "fastar_tempcache_workspace_ex": (_SZ, [_CP, _I, _P]),
+    "fastar_tempcache_merge_ex": (_I, [_CP, _TP, _TP, _P, _I, _F, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "fastar_scalar_codes": (_I, [_TP, _I, _P, _P, _P]),
     "fastar_cache_status": (_I, [_CP, _I, _P]),
     "fastar_tempcache_merge": (_I, [_CP, _TP, _TP, _P, _I, _F, _P, _P, _P, _P, _SZ, _P, _P]),
     "fastar_prune_prompt": (_I, [_P, _I, _I64, _I, _P, _I64, _I, _P, _P, _P, _P]),
@@ -262,9 +279,10 @@ class TempCache:
                            self.n_groups.data_ptr(), self.frontier.data_ptr(),
                            self.status.data_ptr())
 
-    def workspace_bytes(self, n_frames: int) -> int:
+    def workspace_bytes(self, n_frames: int, opts: Optional[FastarMergeOpts] = None) -> int:
         c = self.struct()
-        return library().fastar_tempcache_workspace(ctypes.byref(c), n_frames)
+        return library().fastar_tempcache_workspace_ex(ctypes.byref(c), n_frames,
+                                                       None if opts is None else ctypes.byref(opts))
 
     def status_code(self, clear: bool = False, stream=None) -> int:
         """fastar_cache_status: 0 (ok) or 5 (FASTAR_ERR_CAPACITY: a merge since the
@@ -278,8 +296,10 @@ class TempCache:
 
 def fastar_tempcache_merge(cache: TempCache, k_new, v_new, k_new_bucket, n_frames: int,
                            tau: float, group_of_new=None, with_index: bool = True,
-                           rep_offsets=None, rep_perm=None, ws=None, diag=None, stream=None):
-    """Merge n_frames frames (k_new, v_new [H, n_frames*T, d]) into the cache."""
+                           rep_offsets=None, rep_perm=None, ws=None, diag=None, stream=None,
+                           opts: Optional[FastarMergeOpts] = None):
+    """Merge n_frames frames (k_new, v_new [H, n_frames*T, d]) into the cache
+    (opts: the TempCache variant, merge_opts(); None: the defaults)."""
     lib = library()
     H = cache.heads
     dev = k_new.device
@@ -291,13 +311,27 @@ def fastar_tempcache_merge(cache: TempCache, k_new, v_new, k_new_bucket, n_frame
     else:
         rep_offsets = rep_perm = None
     c = cache.struct()
-    ws = _ws(lib.fastar_tempcache_workspace(ctypes.byref(c), n_frames), dev, ws)
+    o = None if opts is None else ctypes.byref(opts)
+    ws = _ws(lib.fastar_tempcache_workspace_ex(ctypes.byref(c), n_frames, o), dev, ws)
     dk, dv = _desc(k_new), _desc(v_new)
-    _check(lib.fastar_tempcache_merge(ctypes.byref(c), ctypes.byref(dk), ctypes.byref(dv),
-                                      _ptr(k_new_bucket), n_frames, float(tau), _ptr(group_of_new),
-                                      _ptr(rep_offsets), _ptr(rep_perm), _ptr(ws),
-                                      ws.numel() * ws.element_size(), _ptr(diag), _stream(stream)))
+    _check(lib.fastar_tempcache_merge_ex(ctypes.byref(c), ctypes.byref(dk), ctypes.byref(dv),
+                                         _ptr(k_new_bucket), n_frames, float(tau), o, _ptr(group_of_new),
+                                         _ptr(rep_offsets), _ptr(rep_perm), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _ptr(diag), _stream(stream)))
     return rep_offsets, rep_perm
+
+
+def fastar_scalar_codes(x, bits: int = 8, codes=None, norm2=None, stream=None):
+    """Per-row symmetric b-bit codes [H, N, d] (int8) and squared norms [H, N] of x."""
+    lib = library()
+    H, N, d = x.shape
+    if codes is None:
+        codes = torch.empty(H, N, d, dtype=torch.int8, device=x.device)
+    if norm2 is None:
+        norm2 = torch.empty(H, N, dtype=torch.int32, device=x.device)
+    dx = _desc(x)
+    _check(lib.fastar_scalar_codes(ctypes.byref(dx), bits, _ptr(codes), _ptr(norm2), _stream(stream)))
+    return codes, norm2
 
 
 def fastar_prune_prompt(q_bucket, p_bucket, n_bits: int, keep=None, kept_idx=None, n_kept=None,
@@ -367,7 +401,8 @@ class ChunkCall:
     def __init__(self, q, n_probes, k_new, v_new, n_frames, planes, n_bits, tau, cache: TempCache,
                  q_bucket, q_offsets, q_perm, k_bucket, rep_offsets, rep_perm, out, lse=None,
                  group_of_new=None, scale=None, prompt_k=None, prompt_v=None, p_bucket=None,
-                 keep=None, kept_idx=None, n_kept=None, out_cross=None, lse_cross=None):
+                 keep=None, kept_idx=None, n_kept=None, out_cross=None, lse_cross=None,
+                 opts: Optional[FastarMergeOpts] = None):
         d = q.shape[-1]
         self._keep = []  # everything the pointers below refer to
 
@@ -386,7 +421,8 @@ class ChunkCall:
             ctypes.addressof(self.cache_struct),
             p(q_bucket), p(q_offsets), p(q_perm), p(k_bucket), p(group_of_new), p(rep_offsets),
             p(rep_perm), p(out), p(lse), p(p_bucket), p(keep), p(kept_idx), p(n_kept), p(out_cross),
-            p(lse_cross))
+            p(lse_cross), None if opts is None else ctypes.addressof(opts))
+        self._keep.append(opts)
         self._keep += [q, k_new, v_new, prompt_k, prompt_v, planes, q_bucket, q_offsets, q_perm,
                        k_bucket, group_of_new, rep_offsets, rep_perm, out, lse, p_bucket, keep,
                        kept_idx, n_kept, out_cross, lse_cross]

@@ -33,11 +33,14 @@ from . import fastar as fb
 class FastARLayer:
     def __init__(self, heads: int, dim: int, n_bits: int, n_probes: int, tau: float,
                  tokens_per_frame: int, capacity: int, n_queries: int, chunk_frames: int,
-                 n_prompt: int = 0, dtype=torch.bfloat16, device="cuda"):
+                 n_prompt: int = 0, dtype=torch.bfloat16, device="cuda", match: str = "lsh",
+                 code_bits: int = 8):
         self.heads, self.dim, self.n_bits, self.n_probes = heads, dim, n_bits, n_probes
         self.tau, self.T, self.capacity = tau, tokens_per_frame, capacity
         self.nq, self.chunk_frames, self.n_prompt = n_queries, chunk_frames, n_prompt
         self.dtype, self.device = dtype, torch.device(device)
+        # the TempCache variant (None: the library's defaults)
+        self.opts = None if match == "lsh" else fb.merge_opts(match, code_bits)
         H, dev = heads, self.device
         i32 = dict(dtype=torch.int32, device=dev)
         self.cache = fb.TempCache(H, dim, capacity, tokens_per_frame, n_bits, dtype, dev)
@@ -48,9 +51,9 @@ class FastARLayer:
                        lib.fastar_hash_workspace(H, nk, n_bits, 1),
                        lib.fastar_hash_workspace(H, n_prompt, n_bits, 1),
                        # fastar_chunk: the merge's, then (at most) the queries' index scratch
-                       self.cache.workspace_bytes(chunk_frames) +
+                       self.cache.workspace_bytes(chunk_frames, self.opts) +
                        lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
-                       self.cache.workspace_bytes(1))
+                       self.cache.workspace_bytes(1, self.opts))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         # the query-side stream has a workspace of its own
         ws_q = max(lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
@@ -97,7 +100,7 @@ class FastARLayer:
         return fb.fastar_tempcache_merge(
             self.cache, k, v, ids.view(self.heads, -1), n_frames, self.tau,
             group_of_new=group_of_new, with_index=with_index, rep_offsets=self.rep_off,
-            rep_perm=self.rep_perm, ws=self.ws, diag=self.diag)
+            rep_perm=self.rep_perm, ws=self.ws, diag=self.diag, opts=self.opts)
 
     # -- one chunk ----------------------------------------------------------
     def _ev(self, timing):
@@ -147,7 +150,7 @@ class FastARLayer:
         self._timed(timing, "merge", lambda: fb.fastar_tempcache_merge(
             cache, k_new, v_new, self.k_ids.view(self.heads, -1), self.chunk_frames, self.tau,
             group_of_new=self.group_of_new, rep_offsets=self.rep_off, rep_perm=self.rep_perm,
-            ws=self.ws, diag=self.diag))
+            ws=self.ws, diag=self.diag, opts=self.opts))
 
     def self_attention(self, q, timing=None, cache=None):
         c = self.cache if cache is None else cache
@@ -169,7 +172,8 @@ class FastARLayer:
             call = fb.ChunkCall(q, self.n_probes, k_new, v_new, self.chunk_frames, self.planes,
                                 self.n_bits, self.tau, cache, self.q_ids, self.q_off, self.q_perm,
                                 self.k_ids, self.rep_off, self.rep_perm, self.o_self,
-                                lse=self.lse_self, group_of_new=self.group_of_new, **extra)
+                                lse=self.lse_self, group_of_new=self.group_of_new, opts=self.opts,
+                                **extra)
             self._calls[key] = call
         return call
 

@@ -23,16 +23,19 @@ import numpy as np
 from .simhash import simhash
 from .index import bucket_index
 from .tempcache import TempCacheOracle
+from .tempcache_quant import TempCacheQuantOracle
 from .annca import prune_prompt, cross_attention
 from .attention import bucket_attention
 
 
-def run_chunk(w, heads=None, attention=True):
+def run_chunk(w, heads=None, attention=True, match="lsh", code_bits=8):
     """Run the sequence for workload-like object ``w`` on the given heads.
 
     ``w`` provides dtype, dim, n_bits, n_probes, tau, planes [b, d], q [H, N, d],
     and optionally k_frames/v_frames [H, F, T, d] with setup_frames, and
-    prompt_k/prompt_v [H, Np, d].  Returns a dict of per-head result dicts.
+    prompt_k/prompt_v [H, Np, d].  ``match``: TempCache's LSH match ("lsh") or
+    its quantized match ("quant", ``code_bits`` bits).  Returns a dict of
+    per-head result dicts.
     """
     heads = range(w.heads) if heads is None else heads
     scale = 1.0 / np.sqrt(w.dim)
@@ -43,7 +46,8 @@ def run_chunk(w, heads=None, attention=True):
         r["q_ids"] = simhash(q, w.planes, w.n_probes)
         r["q_offsets"], r["q_perm"] = bucket_index(r["q_ids"], w.n_bits)
         if w.k_frames is not None:
-            tc = TempCacheOracle(w.dim, w.dtype)
+            tc = (TempCacheQuantOracle(w.dim, w.dtype, code_bits) if match == "quant"
+                  else TempCacheOracle(w.dim, w.dtype))
             F = w.k_frames.shape[1]
             groups = []
             setup_groups = []

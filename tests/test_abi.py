@@ -252,3 +252,19 @@ def test_recall_rejects_bad_arguments_without_launching(lib):
     assert lib.fastar_attention_recall(buf, buf, 2, 10, buf, 3, buf, 4, None, buf, None, buf, None) == 2
     assert lib.fastar_attention_recall(None, buf, 2, 10, None, 1, None, 0, buf, buf, None, buf, None) == 1
     assert lib.fastar_attention_recall(None, None, 0, 10, None, 1, None, 0, None, None, None, None, None) == 0
+
+
+def test_merge_options_rejected_without_launching(lib):
+    buf = 1 << 20
+    c = fb.FastarCache(2, 128, 64, 16, 12, 1, *([buf] * 9))
+    k = _tensor(tokens=16)
+    for match, bits, want in [(7, 8, 2), (1, 9, 2), (1, 1, 2)]:
+        o = fb.FastarMergeOpts(match, bits)
+        st = lib.fastar_tempcache_merge_ex(ctypes.byref(c), ctypes.byref(k), ctypes.byref(k),
+                                           ctypes.c_void_p(buf), 1, 0.9, ctypes.byref(o), None, None,
+                                           None, ctypes.c_void_p(buf), 1 << 30, None, None)
+        assert st == want, (match, bits)
+    assert lib.fastar_tempcache_workspace_ex(ctypes.byref(c), 1, ctypes.byref(fb.FastarMergeOpts(1, 8))) > \
+        lib.fastar_tempcache_workspace(ctypes.byref(c), 1)
+    assert lib.fastar_scalar_codes(ctypes.byref(k), 1, ctypes.c_void_p(buf), ctypes.c_void_p(buf), None) == 2
+    assert lib.fastar_scalar_codes(ctypes.byref(k), 8, None, ctypes.c_void_p(buf), None) == 1
