@@ -575,6 +575,59 @@ def rollout(w, dev, flush):
     return out
 
 
+def tau_sweep(w, dev, taus, match="lsh"):
+    """TempCache's threshold swept on workload w (paperlayer.ai appendix C,
+    tau 0.9 -> 0.5): per tau the chunk time (cold, after a 512 MB write), the
+    compressed cache's density (groups / raw keys), AnnSA's recall, and the
+    merging's error: dense attention over the compressed cache (+ ln m, all
+    groups) against dense attention over the raw frames, as the mean relative
+    L2 error of the outputs and of the normalisers' ratio (exp(lse_comp -
+    lse_raw), 1 when the merged groups keep every raw key's mass)."""
+    import kv_compressed_attention_amd.fastar as fb
+    from kv_compressed_attention_amd.layer import FastARLayer
+
+    H, F, T, d = w.k_frames.shape
+    tdt = torch.bfloat16
+
+    def up(a):
+        return torch.tensor(np.ascontiguousarray(a), dtype=torch.float32, device=dev).to(tdt)
+    q = up(w.q)
+    raw_k = up(w.k_frames.reshape(H, F * T, d))
+    raw_v = up(w.v_frames.reshape(H, F * T, d))
+    o_raw, lse_raw = fb.fastar_bucket_attention(q, raw_k, raw_v)
+    k_new, v_new = (up(a) for a in w.frames(w.setup_frames, F))
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    out = []
+    for tau in taus:
+        layer = FastARLayer(H, d, w.n_bits, w.n_probes, tau, T, F * T, w.n_queries, w.chunk_frames,
+                            dtype=tdt, device=dev, match=match)
+        layer.set_planes(up(w.planes))
+        for f in range(w.setup_frames):
+            layer.merge(up(w.k_frames[:, f]), up(w.v_frames[:, f]), 1, with_index=False)
+        layer._chunk_call(q, k_new, v_new, None, None, layer.cache)
+        torch.cuda.synchronize()
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        layer.step(q, k_new, v_new)
+        e1.record()
+        torch.cuda.synchronize()
+        c = layer.cache
+        o_c, lse_c = fb.fastar_bucket_attention(q, c.rep_k, c.v_mean, key_bias=c.log_count,
+                                                n_key_list=c.n_groups)
+        _, rs = fb.fastar_attention_recall(layer.lse_self, lse_c, c.n_groups, q_bucket=layer.q_ids,
+                                           k_offsets=layer.rep_off, n_bits=w.n_bits, want_recall=False)
+        rel = ((o_c.float() - o_raw.float()).norm(dim=2) / o_raw.float().norm(dim=2).clamp_min(1e-30))
+        ng = c.n_groups.cpu().numpy()
+        out.append({"tau": tau, "chunk_ms": e0.elapsed_time(e1),
+                    "cache_density": float(ng.mean()) / (F * T),
+                    "annsa_recall": float(rs[:, 0].mean().item()),
+                    "merge_rel_l2_error": float(rel.mean().item()),
+                    "mass_ratio": float(torch.exp(lse_c - lse_raw).mean().item())})
+        del layer
+    return out
+
+
 def annca(w, dev, steps):
     """The AnnCA workload: hash the queries and the prompt, prune, and
     cross-attention over the kept prompt keys; per-call times (cold: one
@@ -749,6 +802,9 @@ def main():
             extra[w1.name] = summarize(w1, r1, args.steps)
             del r1
             torch.cuda.empty_cache()
+        w1 = make_workload(1)
+        extra["tau_sweep"] = {"workload": w1.name, "lsh": tau_sweep(w1, dev, [0.999, 0.99, 0.95, 0.9, 0.7, 0.5]),
+                              "quant8": tau_sweep(w1, dev, [0.999, 0.99, 0.9, 0.5], match="quant")}
         extra["annca"] = annca(make_workload(2), dev, args.steps)
         w3 = make_workload(3)
         roll = rollout(w3, dev, flush)

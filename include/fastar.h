@@ -190,7 +190,8 @@ typedef struct {
  * capture. */
 fastar_status_t fastar_cache_status(const fastar_cache_t* cache, int clear, hipStream_t stream);
 
-/* TempCache variants (paperlayer.ai section 5 "ANN Attention" and appendix C).
+/* TempCache variants (paperlayer.ai section 5 "ANN Attention" and appendix C;
+ * gist.science and paper.rainbus.top on the query-driven correspondence).
  *   match           FASTAR_MATCH_LSH (default): a new key's candidates are
  *                   the previous frame's tokens with its bucket; similarity is
  *                   the exact cosine.
@@ -201,13 +202,29 @@ fastar_status_t fastar_cache_status(const fastar_cache_t* cache, int clear, hipS
  *                   the pages' quantized ANN, 8 bits by default), decided
  *                   exactly on the integer codes.
  *   code_bits       2..8 with FASTAR_MATCH_QUANT (0 means 8).
- * Everything else (threshold, one-to-one rule, last-key representative,
- * value means, ln m bias) is the same for every match. */
+ *   representative  FASTAR_REP_LAST (default): a group keeps its most recent
+ *                   key.  FASTAR_REP_MEAN: the mean of its keys, rounded once
+ *                   to the cache dtype.  FASTAR_REP_MEDOID: of the previous
+ *                   representative and the new key, the one of larger cosine
+ *                   with the group's key sum (an online medoid; ties keep the
+ *                   previous one).  Mean and medoid need cache->k_sum, and
+ *                   merge the frames of a call one at a time.
+ *   match_queries   NULL (key-driven), or [H][n_frames * T][d] queries of the
+ *                   new frames' tokens, cache dtype: the new side of the
+ *                   similarity is the token's query (query-driven
+ *                   correspondence); the token joins with its key and value.
+ *                   FASTAR_MATCH_QUANT only.
+ * Everything else (threshold, one-to-one rule, value means, ln m bias) is
+ * the same for every variant. */
 typedef enum { FASTAR_MATCH_LSH = 0, FASTAR_MATCH_QUANT = 1 } fastar_match_t;
+typedef enum { FASTAR_REP_LAST = 0, FASTAR_REP_MEAN = 1, FASTAR_REP_MEDOID = 2 } fastar_rep_t;
 typedef struct {
   int32_t match;
   int32_t code_bits;
-  int32_t reserved[6];
+  int32_t representative;
+  int32_t reserved;
+  const fastar_tensor_t* match_queries;
+  void* reserved_ptr;
 } fastar_merge_opts_t;
 
 /* fastar_tempcache_merge -- merge n_frames new frames, in order.

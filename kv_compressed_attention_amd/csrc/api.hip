@@ -109,28 +109,50 @@ size_t merge_workspace(const fastar_cache_t* c, int n_frames) {
          align_up(16 * H * (size_t)c->capacity);
 }
 
-// the match kind and code bits of opts (NULL: defaults)
-fastar_status_t merge_opts(const fastar_merge_opts_t* o, int* match, int* bits) {
-  *match = FASTAR_MATCH_LSH;
-  *bits = 8;
+// a merge's options, checked (NULL: the defaults)
+struct MergeOpt {
+  int match = FASTAR_MATCH_LSH, bits = 8, rep = FASTAR_REP_LAST;
+  const fastar_tensor_t* q = nullptr;
+};
+fastar_status_t merge_opts(const fastar_merge_opts_t* o, MergeOpt* m) {
+  *m = MergeOpt();
   if (!o) return FASTAR_OK;
   if (o->match != FASTAR_MATCH_LSH && o->match != FASTAR_MATCH_QUANT)
     return fail(FASTAR_ERR_UNSUPPORTED, "merge option match %d unknown", o->match);
-  *match = o->match;
+  m->match = o->match;
   if (o->match == FASTAR_MATCH_QUANT && o->code_bits != 0) {
     if (o->code_bits < 2 || o->code_bits > 8)
       return fail(FASTAR_ERR_UNSUPPORTED, "code_bits %d not in [2, 8]", o->code_bits);
-    *bits = o->code_bits;
+    m->bits = o->code_bits;
+  }
+  if (o->representative != FASTAR_REP_LAST)
+    return fail(FASTAR_ERR_UNSUPPORTED, "representative %d not supported", o->representative);
+  m->rep = o->representative;
+  if (o->match_queries) {
+    if (o->match != FASTAR_MATCH_QUANT)
+      return fail(FASTAR_ERR_UNSUPPORTED, "query-driven matching needs FASTAR_MATCH_QUANT");
+    m->q = o->match_queries;
   }
   return FASTAR_OK;
 }
 
 size_t merge_workspace_ex(const fastar_cache_t* c, int n_frames, const fastar_merge_opts_t* o) {
-  int match, bits;
-  if (merge_opts(o, &match, &bits) != FASTAR_OK) return 0;
+  MergeOpt m;
+  if (merge_opts(o, &m) != FASTAR_OK) return 0;
   const size_t base = merge_workspace(c, n_frames);
-  if (match != FASTAR_MATCH_QUANT || base == 0) return base;
-  return base + fastar::quant_workspace_bytes(c->heads, c->tokens_per_frame, n_frames, c->dim);
+  if (m.match != FASTAR_MATCH_QUANT || base == 0) return base;
+  return base + fastar::quant_workspace_bytes(c->heads, c->tokens_per_frame, n_frames, c->dim, m.q != nullptr);
+}
+
+// the query tensor of query-driven matching against the new keys
+fastar_status_t check_match_queries(const MergeOpt& m, const fastar_tensor_t* k_new) {
+  if (!m.q) return FASTAR_OK;
+  fastar_status_t st = check_tensor(m.q, "match_queries");
+  if (st != FASTAR_OK) return st;
+  if (m.q->dtype != k_new->dtype || m.q->dim != k_new->dim || m.q->heads != k_new->heads ||
+      m.q->tokens != k_new->tokens)
+    return fail(FASTAR_ERR_INVALID, "match_queries must have k_new's dtype, heads, tokens and dim");
+  return FASTAR_OK;
 }
 
 // everything fastar_tempcache_merge checks for a call with n_frames > 0 and
@@ -372,11 +394,12 @@ fastar_status_t fastar_tempcache_merge_ex(const fastar_cache_t* c, const fastar_
                                           int n_frames, float tau, const fastar_merge_opts_t* opts,
                                           int32_t* group_of_new, int32_t* rep_offsets, int32_t* rep_perm,
                                           void* ws, size_t ws_bytes, fastar_diag_t* diag, hipStream_t stream) {
-  int match, bits;
-  fastar_status_t st = merge_opts(opts, &match, &bits);
+  MergeOpt mo;
+  fastar_status_t st = merge_opts(opts, &mo);
   if (st != FASTAR_OK) return st;
   if ((st = merge_check(c, k_new, v_new, k_new_bucket, n_frames, tau, rep_offsets, rep_perm)) != FASTAR_OK)
     return st;
+  if ((st = check_match_queries(mo, k_new)) != FASTAR_OK) return st;
   const size_t need = merge_workspace_ex(c, n_frames, opts);
   if (c->heads == 0 || n_frames == 0) {
     if (rep_offsets && c->heads > 0) {
@@ -392,12 +415,12 @@ fastar_status_t fastar_tempcache_merge_ex(const fastar_cache_t* c, const fastar_
   if (!ws || ws_bytes < need)
     return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need, ws_bytes);
   const fastar::MergeWs mw = merge_carve(c, n_frames, ws);
-  if (match == FASTAR_MATCH_QUANT) {
+  if (mo.match == FASTAR_MATCH_QUANT) {
     const fastar::QuantWs q = fastar::quant_carve(c->heads, c->tokens_per_frame, n_frames, c->dim,
-                                                  (char*)ws + merge_workspace(c, n_frames));
-    return hip_status(fastar::launch_tempcache_merge_quant(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,
-                                                           bits, group_of_new, rep_offsets, rep_perm, mw, q,
-                                                           diag, stream),
+                                                  mo.q != nullptr, (char*)ws + merge_workspace(c, n_frames));
+    return hip_status(fastar::launch_tempcache_merge_quant(*c, *k_new, *v_new, mo.q, k_new_bucket, n_frames,
+                                                           tau, mo.bits, group_of_new, rep_offsets, rep_perm,
+                                                           mw, q, diag, stream),
                       "tempcache_merge (quantized match)");
   }
   return hip_status(fastar::launch_tempcache_merge(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,
@@ -554,8 +577,10 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   if (a->q->tokens > 0 && !a->q_bucket) return fail(FASTAR_ERR_INVALID, "q_bucket is NULL");
   // 2. the merge (and the queries' index)
   if (c->n_bits != a->n_bits) return fail(FASTAR_ERR_INVALID, "the cache's n_bits differs from n_bits");
-  int match, bits;
-  if ((st = merge_opts(a->merge_opts, &match, &bits)) != FASTAR_OK) return st;
+  MergeOpt mo;
+  if ((st = merge_opts(a->merge_opts, &mo)) != FASTAR_OK) return st;
+  if ((st = check_match_queries(mo, a->k_new)) != FASTAR_OK) return st;
+  const int match = mo.match;
   if ((st = merge_check(c, a->k_new, a->v_new, a->k_bucket, a->n_frames, a->tau, a->rep_offsets,
                         a->rep_perm)) != FASTAR_OK)
     return st;
@@ -613,10 +638,10 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   if (fused) mw.also_index = &qj;
   if (match == FASTAR_MATCH_QUANT) {
     const fastar::QuantWs q = fastar::quant_carve(c->heads, c->tokens_per_frame, a->n_frames, c->dim,
-                                                  (char*)ws + merge_workspace(c, a->n_frames));
-    if ((st = hip_status(fastar::launch_tempcache_merge_quant(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,
-                                                              a->tau, bits, a->group_of_new, a->rep_offsets,
-                                                              a->rep_perm, mw, q, diag, stream),
+                                                  mo.q != nullptr, (char*)ws + merge_workspace(c, a->n_frames));
+    if ((st = hip_status(fastar::launch_tempcache_merge_quant(*c, *a->k_new, *a->v_new, mo.q, a->k_bucket,
+                                                              a->n_frames, a->tau, mo.bits, a->group_of_new,
+                                                              a->rep_offsets, a->rep_perm, mw, q, diag, stream),
                          "tempcache_merge (quantized match)")) != FASTAR_OK)
       return st;
   } else if ((st = hip_status(fastar::launch_tempcache_merge(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,

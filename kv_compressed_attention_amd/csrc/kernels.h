@@ -110,21 +110,24 @@ hipError_t launch_scalar_codes(const fastar_tensor_t& x, int bits, int8_t* codes
                                hipStream_t s);
 // the quantized match's workspace (beyond MergeWs's link / nextj / ocnt)
 struct QuantWs {
-  int8_t* codes;   // [H][F+1][T][dim]
-  int32_t* norm2;  // [H][F+1][T]
-  float* rn;       // [H][F+1][T]   1 / sqrt(norm2) (0 for a zero code)
-  float* bias;     // [H][F+1][T]   0, or -inf for a token that is no candidate
+  int8_t* codes;   // [H][tables][T][dim]
+  int32_t* norm2;  // [H][tables][T]
+  float* rn;       // [H][tables][T]   1 / sqrt(norm2) (0 for a zero code)
+  float* bias;     // [H][tables][T]   0, or -inf for a token that is no candidate
   int32_t* ptgt;   // [H][F][T]     proposed candidate, or -1
   int32_t* pdot;   // [H][F][T]     exact code dot product with it
   float* pcos;     // [H][F][T]     float32 cosine estimate
+  // codes etc. hold F + 1 tables, or 2F + 1 with query-driven matching (tables F + 1 .. 2F: queries)
 };
-size_t quant_workspace_bytes(int heads, int T, int F, int dim);
-QuantWs quant_carve(int heads, int T, int F, int dim, void* ws);
+size_t quant_workspace_bytes(int heads, int T, int F, int dim, bool query_driven);
+QuantWs quant_carve(int heads, int T, int F, int dim, bool query_driven, void* ws);
+// q_new: the new frames' queries (query-driven matching), or NULL
 hipError_t launch_tempcache_merge_quant(const fastar_cache_t& c, const fastar_tensor_t& k_new,
-                                        const fastar_tensor_t& v_new, const int32_t* k_new_bucket,
-                                        int n_frames, float tau, int bits, int32_t* group_of_new,
-                                        int32_t* rep_offsets, int32_t* rep_perm, const MergeWs& ws,
-                                        const QuantWs& qws, fastar_diag_t* diag, hipStream_t s);
+                                        const fastar_tensor_t& v_new, const fastar_tensor_t* q_new,
+                                        const int32_t* k_new_bucket, int n_frames, float tau, int bits,
+                                        int32_t* group_of_new, int32_t* rep_offsets, int32_t* rep_perm,
+                                        const MergeWs& ws, const QuantWs& qws, fastar_diag_t* diag,
+                                        hipStream_t s);
 
 hipError_t launch_tempcache_merge(const fastar_cache_t& c, const fastar_tensor_t& k_new,
                                   const fastar_tensor_t& v_new, const int32_t* k_new_bucket,

@@ -58,6 +58,10 @@ struct EncArgs {
   int32_t* nextj;           // [H][F][T], cleared to -1
   int32_t* ocnt;            // [H][nblk + 1], cleared; [nblk] = n_groups
   int nblk;
+  // query-driven: tables F + 1 .. 2F are the new frames' queries
+  const void* q;
+  int64_t qsh, qst;
+  int qd;
   // outputs
   int8_t* codes;
   int32_t* norm2;
@@ -82,7 +86,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void tcq_encode_kernel(EncArgs e) {
   constexpr int EPL = D / 16;
   const int sub = threadIdx.x & 15;
-  const int64_t total = e.mode == 0 ? (int64_t)e.H * e.N : (int64_t)e.H * (e.F + 1) * e.T;
+  const int ntab = e.F + 1 + (e.qd ? e.F : 0);
+  const int64_t total = e.mode == 0 ? (int64_t)e.H * e.N : (int64_t)e.H * ntab * e.T;
   const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (e.mode == 1) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -102,7 +107,7 @@ __global__ __launch_bounds__(256) void tcq_encode_kernel(EncArgs e) {
     const int64_t i = r - (int64_t)h * e.N;
     src = (const T*)e.x + (int64_t)h * e.sh + i * e.st;
   } else {
-    const int64_t per = (int64_t)(e.F + 1) * e.T;
+    const int64_t per = (int64_t)ntab * e.T;
     const int h = (int)(r / per);
     const int t = (int)((r - (int64_t)h * per) / e.T);
     const int i = (int)(r - (int64_t)h * per - (int64_t)t * e.T);
@@ -110,8 +115,10 @@ __global__ __launch_bounds__(256) void tcq_encode_kernel(EncArgs e) {
       const int g = e.frontier[(int64_t)h * e.T + i];
       valid = e.n_groups[h] > 0 && g >= 0 && g < e.cap;
       src = (const T*)e.rep_k + ((int64_t)h * e.cap + (valid ? g : 0)) * D;
-    } else {
+    } else if (t <= e.F) {
       src = (const T*)e.x + (int64_t)h * e.sh + ((int64_t)(t - 1) * e.T + i) * e.st;
+    } else {
+      src = (const T*)e.q + (int64_t)h * e.qsh + ((int64_t)(t - 1 - e.F) * e.T + i) * e.qst;
     }
   }
   float v[EPL];
@@ -218,6 +225,7 @@ __device__ __forceinline__ int code_dot(const int8_t* a, const int8_t* b) {
 // ---------------------------------------------------------------------------
 struct QMatchArgs {
   int H, T, F;
+  int ntab, moff;  // tables per head; the matcher table of frame f is f + 1 + moff
   Tau tau;
   const int8_t* codes;
   const int32_t* norm2;
@@ -260,8 +268,8 @@ __global__ __launch_bounds__(256) void tcq_match_kernel(QMatchArgs a) {
   const int k0 = blockIdx.x * 64 + wave * 16;
   if (k0 >= a.T) return;  // the whole wave (no workgroup barriers here)
   const int T = a.T;
-  const int64_t tk = ((int64_t)h * (a.F + 1) + f + 1) * T;  // key table rows
-  const int64_t tc = ((int64_t)h * (a.F + 1) + f) * T;      // candidate table rows
+  const int64_t tk = ((int64_t)h * a.ntab + f + 1 + a.moff) * T;  // matcher table rows (keys or queries)
+  const int64_t tc = ((int64_t)h * a.ntab + f) * T;                // candidate table rows
   const int8_t* kc = a.codes + tk * D;
   const int8_t* cc = a.codes + tc * D;
   const float* crn = a.rn + tc;
@@ -379,6 +387,7 @@ __global__ __launch_bounds__(256) void tcq_match_kernel(QMatchArgs a) {
 // ---------------------------------------------------------------------------
 struct QResolveArgs {
   int H, T, F;
+  int ntab, moff;
   const int32_t* norm2;     // key norms: tables 1..F
   const int32_t* ptgt;
   const int32_t* pdot;
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(kResThreads) void tcq_resolve_kernel(QResolveArgs a
   __shared__ int32_t wsum[kResThreads / FASTAR_WAVE];
   const int f = blockIdx.x, h = blockIdx.y, T = a.T;
   const int64_t po = ((int64_t)h * a.F + f) * T;
-  const int64_t kn = ((int64_t)h * (a.F + 1) + f + 1) * T;
+  const int64_t kn = ((int64_t)h * a.ntab + f + 1 + a.moff) * T;
   int tg[kResPer], dj[kResPer], nj[kResPer];
   float cj[kResPer];
 #pragma unroll
@@ -480,7 +489,8 @@ __global__ __launch_bounds__(kResThreads) void tcq_resolve_kernel(QResolveArgs a
 
 template <typename T, int D>
 hipError_t merge_quant_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fastar_tensor_t& vn,
-                          const int32_t* kb, int F, float tau, int bits, int32_t* group_of_new,
+                          const fastar_tensor_t* qn, const int32_t* kb, int F, float tau, int bits,
+                          int32_t* group_of_new,
                           int32_t* rep_offsets, int32_t* rep_perm, const MergeWs& ws, const QuantWs& q,
                           fastar_diag_t* diag, hipStream_t s) {
   const int H = c.heads, Tf = c.tokens_per_frame;
@@ -515,12 +525,21 @@ hipError_t merge_quant_td(const fastar_cache_t& c, const fastar_tensor_t& kn, co
   e.norm2 = q.norm2;
   e.rn = q.rn;
   e.bias = q.bias;
-  const int64_t rows = (int64_t)H * (F + 1) * Tf;
+  e.qd = qn != nullptr;
+  if (qn) {
+    e.q = qn->data;
+    e.qsh = qn->stride_head;
+    e.qst = qn->stride_token;
+  }
+  const int ntab = F + 1 + (qn ? F : 0);
+  const int64_t rows = (int64_t)H * ntab * Tf;
   hipLaunchKernelGGL((tcq_encode_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, e);
   QMatchArgs ma{};
   ma.H = H;
   ma.T = Tf;
   ma.F = F;
+  ma.ntab = ntab;
+  ma.moff = qn ? F : 0;
   {
     Tau t;
     t.f = tau;
@@ -551,6 +570,8 @@ hipError_t merge_quant_td(const fastar_cache_t& c, const fastar_tensor_t& kn, co
   ra.H = H;
   ra.T = Tf;
   ra.F = F;
+  ra.ntab = ntab;
+  ra.moff = qn ? F : 0;
   ra.norm2 = q.norm2;
   ra.ptgt = q.ptgt;
   ra.pdot = q.pdot;
@@ -568,15 +589,15 @@ hipError_t merge_quant_td(const fastar_cache_t& c, const fastar_tensor_t& kn, co
 
 }  // namespace
 
-size_t quant_workspace_bytes(int heads, int T, int F, int dim) {
+size_t quant_workspace_bytes(int heads, int T, int F, int dim, bool query_driven) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t rows = (size_t)heads * (F + 1) * T, props = (size_t)heads * F * T;
+  const size_t rows = (size_t)heads * (F + 1 + (query_driven ? F : 0)) * T, props = (size_t)heads * F * T;
   return al(rows * dim) + 3 * al(4 * rows) + 3 * al(4 * props);
 }
 
-QuantWs quant_carve(int heads, int T, int F, int dim, void* ws) {
+QuantWs quant_carve(int heads, int T, int F, int dim, bool query_driven, void* ws) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t rows = (size_t)heads * (F + 1) * T, props = (size_t)heads * F * T;
+  const size_t rows = (size_t)heads * (F + 1 + (query_driven ? F : 0)) * T, props = (size_t)heads * F * T;
   char* w = (char*)ws;
   QuantWs q;
   q.codes = (int8_t*)w;
@@ -621,19 +642,20 @@ hipError_t launch_scalar_codes(const fastar_tensor_t& x, int bits, int8_t* codes
 }
 
 hipError_t launch_tempcache_merge_quant(const fastar_cache_t& c, const fastar_tensor_t& k_new,
-                                        const fastar_tensor_t& v_new, const int32_t* k_new_bucket,
-                                        int n_frames, float tau, int bits, int32_t* group_of_new,
-                                        int32_t* rep_offsets, int32_t* rep_perm, const MergeWs& ws,
-                                        const QuantWs& qws, fastar_diag_t* diag, hipStream_t s) {
+                                        const fastar_tensor_t& v_new, const fastar_tensor_t* q_new,
+                                        const int32_t* k_new_bucket, int n_frames, float tau, int bits,
+                                        int32_t* group_of_new, int32_t* rep_offsets, int32_t* rep_perm,
+                                        const MergeWs& ws, const QuantWs& qws, fastar_diag_t* diag,
+                                        hipStream_t s) {
   if (c.heads == 0 || n_frames == 0) return hipSuccess;
   if (c.dtype == FASTAR_BF16)
-    return c.dim == 64 ? merge_quant_td<uint16_t, 64>(c, k_new, v_new, k_new_bucket, n_frames, tau, bits,
+    return c.dim == 64 ? merge_quant_td<uint16_t, 64>(c, k_new, v_new, q_new, k_new_bucket, n_frames, tau, bits,
                                                       group_of_new, rep_offsets, rep_perm, ws, qws, diag, s)
-                       : merge_quant_td<uint16_t, 128>(c, k_new, v_new, k_new_bucket, n_frames, tau, bits,
+                       : merge_quant_td<uint16_t, 128>(c, k_new, v_new, q_new, k_new_bucket, n_frames, tau, bits,
                                                        group_of_new, rep_offsets, rep_perm, ws, qws, diag, s);
-  return c.dim == 64 ? merge_quant_td<float, 64>(c, k_new, v_new, k_new_bucket, n_frames, tau, bits,
+  return c.dim == 64 ? merge_quant_td<float, 64>(c, k_new, v_new, q_new, k_new_bucket, n_frames, tau, bits,
                                                  group_of_new, rep_offsets, rep_perm, ws, qws, diag, s)
-                     : merge_quant_td<float, 128>(c, k_new, v_new, k_new_bucket, n_frames, tau, bits,
+                     : merge_quant_td<float, 128>(c, k_new, v_new, q_new, k_new_bucket, n_frames, tau, bits,
                                                   group_of_new, rep_offsets, rep_perm, ws, qws, diag, s);
 }
 

@@ -53,15 +53,26 @@ class FastarCache(ctypes.Structure):
 
 class FastarMergeOpts(ctypes.Structure):
     _fields_ = [("match", ctypes.c_int32), ("code_bits", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("representative", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("match_queries", ctypes.c_void_p), ("reserved_ptr", ctypes.c_void_p)]
 
 
 MATCH = {"lsh": 0, "quant": 1}
+REPRESENTATIVE = {"last": 0, "mean": 1, "medoid": 2}
 
 
-def merge_opts(match: str = "lsh", code_bits: int = 8) -> FastarMergeOpts:
-    """fastar_merge_opts_t for a TempCache variant ("lsh" or "quant")."""
-    return FastarMergeOpts(MATCH[match], code_bits)
+def merge_opts(match: str = "lsh", code_bits: int = 8, representative: str = "last",
+               match_queries=None) -> FastarMergeOpts:
+    """fastar_merge_opts_t for a TempCache variant: match "lsh" or "quant";
+    representative "last", "mean" or "medoid"; match_queries (a [H, n, d]
+    tensor of the new frames' queries): query-driven matching.  The returned
+    struct keeps the query descriptor alive."""
+    o = FastarMergeOpts(MATCH[match], code_bits, REPRESENTATIVE[representative], 0, None, None)
+    if match_queries is not None:
+        o._qdesc = _desc(match_queries)
+        o._qtensor = match_queries
+        o.match_queries = ctypes.addressof(o._qdesc)
+    return o
 
 
 class FastarChunk(ctypes.Structure):

@@ -23,6 +23,7 @@ returns.
 
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
@@ -34,24 +35,34 @@ class FastARLayer:
     def __init__(self, heads: int, dim: int, n_bits: int, n_probes: int, tau: float,
                  tokens_per_frame: int, capacity: int, n_queries: int, chunk_frames: int,
                  n_prompt: int = 0, dtype=torch.bfloat16, device="cuda", match: str = "lsh",
-                 code_bits: int = 8):
+                 code_bits: int = 8, query_driven: bool = False):
         self.heads, self.dim, self.n_bits, self.n_probes = heads, dim, n_bits, n_probes
         self.tau, self.T, self.capacity = tau, tokens_per_frame, capacity
         self.nq, self.chunk_frames, self.n_prompt = n_queries, chunk_frames, n_prompt
         self.dtype, self.device = dtype, torch.device(device)
         # the TempCache variant (None: the library's defaults)
         self.opts = None if match == "lsh" else fb.merge_opts(match, code_bits)
+        # query-driven matching of a chunk's frames (by the chunk's queries,
+        # which are then the new frames' tokens); set-up merges stay key-driven
+        self.match, self.code_bits, self.query_driven = match, code_bits, query_driven
         H, dev = heads, self.device
         i32 = dict(dtype=torch.int32, device=dev)
         self.cache = fb.TempCache(H, dim, capacity, tokens_per_frame, n_bits, dtype, dev)
         self.planes = torch.zeros(max(n_bits, 1), dim, dtype=dtype, device=dev)
         nk = chunk_frames * tokens_per_frame
         lib = fb.library()
+        size_opts = self.opts
+        if query_driven:
+            # the workspace of query-driven matching (only the presence of the
+            # query tensor matters for its size)
+            self._qd_desc = fb.FastarTensor(0, fb._DTYPES[dtype], H, nk, dim, 0, nk * dim, dim)
+            size_opts = fb.merge_opts(match, code_bits)
+            size_opts.match_queries = ctypes.addressof(self._qd_desc)
         ws_bytes = max(lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
                        lib.fastar_hash_workspace(H, nk, n_bits, 1),
                        lib.fastar_hash_workspace(H, n_prompt, n_bits, 1),
                        # fastar_chunk: the merge's, then (at most) the queries' index scratch
-                       self.cache.workspace_bytes(chunk_frames, self.opts) +
+                       self.cache.workspace_bytes(chunk_frames, size_opts) +
                        lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
                        self.cache.workspace_bytes(1, self.opts))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -146,11 +157,14 @@ class FastARLayer:
                                        lse=self.lse_cross)
         self._timed(timing, "cross", run)
 
-    def _merge(self, cache, k_new, v_new, timing):
+    def _merge(self, cache, k_new, v_new, timing, q=None):
+        opts = self.opts
+        if self.query_driven:
+            opts = fb.merge_opts(self.match, self.code_bits, match_queries=q)
         self._timed(timing, "merge", lambda: fb.fastar_tempcache_merge(
             cache, k_new, v_new, self.k_ids.view(self.heads, -1), self.chunk_frames, self.tau,
             group_of_new=self.group_of_new, rep_offsets=self.rep_off, rep_perm=self.rep_perm,
-            ws=self.ws, diag=self.diag, opts=self.opts))
+            ws=self.ws, diag=self.diag, opts=opts))
 
     def self_attention(self, q, timing=None, cache=None):
         c = self.cache if cache is None else cache
@@ -169,10 +183,13 @@ class FastARLayer:
                 extra = dict(prompt_k=prompt_k, prompt_v=prompt_v, p_bucket=self.p_ids, keep=self.keep,
                              kept_idx=self.kept_idx, n_kept=self.n_kept, out_cross=self.o_cross,
                              lse_cross=self.lse_cross)
+            opts = self.opts
+            if self.query_driven:
+                opts = fb.merge_opts(self.match, self.code_bits, match_queries=q)
             call = fb.ChunkCall(q, self.n_probes, k_new, v_new, self.chunk_frames, self.planes,
                                 self.n_bits, self.tau, cache, self.q_ids, self.q_off, self.q_perm,
                                 self.k_ids, self.rep_off, self.rep_perm, self.o_self,
-                                lse=self.lse_self, group_of_new=self.group_of_new, opts=self.opts,
+                                lse=self.lse_self, group_of_new=self.group_of_new, opts=opts,
                                 **extra)
             self._calls[key] = call
         return call
@@ -213,7 +230,7 @@ class FastARLayer:
                 side_done = self._ev(None)
             self._timed(timing, "hash_k", lambda: fb.fastar_hash_multi(
                 [k_new], self.planes, self.n_bits, [1], buckets=[self.k_ids], diag=self.diag))
-            self._merge(cache, k_new, v_new, timing)
+            self._merge(cache, k_new, v_new, timing, q)
             main.wait_event(q_done)
             self.self_attention(q, timing, cache)
             main.wait_event(side_done)
@@ -221,7 +238,7 @@ class FastARLayer:
         self._hash_all(q, k_new, prompt_k, timing)
         if not concurrent:
             self._query_index(timing)
-            self._merge(cache, k_new, v_new, timing)
+            self._merge(cache, k_new, v_new, timing, q)
             self.self_attention(q, timing, cache)
             if prompt_k is not None:
                 self._cross(q, prompt_k, prompt_v, timing, hashed=True)
@@ -235,7 +252,7 @@ class FastARLayer:
             if prompt_k is not None:
                 self._cross(q, prompt_k, prompt_v, timing, hashed=True)
             side_done = self._ev(None)
-        self._merge(cache, k_new, v_new, timing)
+        self._merge(cache, k_new, v_new, timing, q)
         main.wait_event(q_done)
         self.self_attention(q, timing, cache)
         main.wait_event(side_done)

@@ -28,14 +28,15 @@ from .annca import prune_prompt, cross_attention
 from .attention import bucket_attention
 
 
-def run_chunk(w, heads=None, attention=True, match="lsh", code_bits=8):
+def run_chunk(w, heads=None, attention=True, match="lsh", code_bits=8, query_driven=False):
     """Run the sequence for workload-like object ``w`` on the given heads.
 
     ``w`` provides dtype, dim, n_bits, n_probes, tau, planes [b, d], q [H, N, d],
     and optionally k_frames/v_frames [H, F, T, d] with setup_frames, and
     prompt_k/prompt_v [H, Np, d].  ``match``: TempCache's LSH match ("lsh") or
-    its quantized match ("quant", ``code_bits`` bits).  Returns a dict of
-    per-head result dicts.
+    its quantized match ("quant", ``code_bits`` bits; ``query_driven``: the
+    chunk's frames are matched by their queries, ``w.q`` being the chunk
+    frames' tokens).  Returns a dict of per-head result dicts.
     """
     heads = range(w.heads) if heads is None else heads
     scale = 1.0 / np.sqrt(w.dim)
@@ -59,7 +60,13 @@ def run_chunk(w, heads=None, attention=True, match="lsh", code_bits=8):
                     k_ids.append(ids)
                 if f == w.setup_frames:
                     r["n_groups_before"] = tc.n_groups
-                g = tc.merge_frame(kf, w.v_frames[h, f], ids, w.tau)
+                if query_driven and f >= w.setup_frames:
+                    T = w.k_frames.shape[2]
+                    qf = np.asarray(w.q[h, (f - w.setup_frames) * T:(f - w.setup_frames + 1) * T],
+                                    dtype=np.float64)
+                    g = tc.merge_frame(kf, w.v_frames[h, f], ids, w.tau, match_vec=qf)
+                else:
+                    g = tc.merge_frame(kf, w.v_frames[h, f], ids, w.tau)
                 (groups if f >= w.setup_frames else setup_groups).append(g)
             r["k_ids"] = np.concatenate(k_ids) if k_ids else np.zeros(0, np.int64)
             r["group_of_new"] = np.concatenate(groups) if groups else np.zeros(0, np.int64)

@@ -16,6 +16,11 @@ Readings where the pages are silent:
 * candidates: every token of the previous frame (no buckets: the quantized
   search replaces the hash-table lookup), i.e. the representatives of the
   frontier groups;
+* query-driven correspondence (gist.science technical summary and
+  paper.rainbus.top method steps: each current-frame token's QUERY finds its
+  top-1 key in the previous frame): with ``match_vec`` the new side of the
+  similarity is that token's query code instead of its key code; the token
+  still joins the group with its key and value;
 * everything else is TempCache's rule set unchanged (the LSH oracle's
   readings): the best candidate by similarity, ties to the smaller index;
   propose if similarity >= tau (tau as its float32 value); one-to-one, the
@@ -62,9 +67,19 @@ class TempCacheQuantOracle(TempCacheOracle):
     def __init__(self, dim: int, dtype: str, bits: int = 8):
         super().__init__(dim, dtype)
         self.bits = bits
+        self._match_vec = None
+
+    def merge_frame(self, k, v, bucket, tau: float, match_vec=None) -> np.ndarray:
+        """As TempCacheOracle.merge_frame; match_vec [T, d] (the tokens'
+        queries): query-driven matching."""
+        self._match_vec = None if match_vec is None else np.asarray(match_vec, dtype=np.float64)
+        try:
+            return super().merge_frame(k, v, bucket, tau)
+        finally:
+            self._match_vec = None
 
     def _match(self, k, bucket, prev_k, prev_b, tau_f, tau_q, target, tcos):
-        ck = scalar_codes(k, self.bits)
+        ck = scalar_codes(k if self._match_vec is None else self._match_vec, self.bits)
         cp = scalar_codes(prev_k, self.bits)
         dots = ck @ cp.T                                  # exact (small integers)
         nk = (ck * ck).sum(axis=1)

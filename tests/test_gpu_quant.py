@@ -181,3 +181,56 @@ def test_quant_chunk_equals_calls_one_by_one(fa):
         assert torch.equal(getattr(layers[0], n), getattr(layers[1], n)), n
     for n, t in layers[0].cache.buffers().items():
         assert torch.equal(t, layers[1].cache.buffers()[n]), n
+
+
+def test_quant_query_driven_merge_matches_oracle(fa):
+    # each new token matched by its query (a noisy copy of its key, so that
+    # the query and key sometimes pick different candidates)
+    H, F, T, d, b, tau, bits = 2, 4, 400, 128, 6, 0.99, 8
+    k, v = _frames(H, F, T, d, seed=91, dtype="bf16")
+    rng = np.random.default_rng(92)
+    qv = round_to_dtype(k + 0.05 * rng.standard_normal(k.shape), "bf16")
+    planes = gaussian((b, d), 93, "bf16")
+    cache = fa.TempCache(H, d, F * T, T, b, torch.bfloat16, "cuda")
+    refs = [oracle.TempCacheQuantOracle(d, "bf16", bits) for _ in range(H)]
+    for f0, f1 in [(0, 1), (1, 3), (3, 4)]:
+        kk = dev_tensor(np.ascontiguousarray(k[:, f0:f1].reshape(H, -1, d)), "bf16")
+        qq = dev_tensor(np.ascontiguousarray(qv[:, f0:f1].reshape(H, -1, d)), "bf16")
+        vv = dev_tensor(np.ascontiguousarray(v[:, f0:f1].reshape(H, -1, d)), "bf16")
+        ids, _, _ = fa.fastar_hash(kk, dev_tensor(planes, "bf16"), b, 1, with_index=False)
+        gon = torch.empty(H, kk.shape[1], dtype=torch.int32, device="cuda")
+        opts = fa.merge_opts("quant", bits, match_queries=qq)
+        fa.fastar_tempcache_merge(cache, kk, vv, ids[:, :, 0].contiguous(), f1 - f0, tau,
+                                  group_of_new=gon, opts=opts)
+        torch.cuda.synchronize()
+        for h in range(H):
+            want = np.concatenate([refs[h].merge_frame(k[h, f], v[h, f], oracle.simhash(k[h, f], planes, 1)[:, 0],
+                                                       tau, match_vec=qv[h, f]) for f in range(f0, f1)])
+            assert np.array_equal(gon[h].cpu().numpy(), want), f"frames {f0}-{f1} head {h}"
+    for h in range(H):
+        G = refs[h].n_groups
+        assert int(cache.n_groups[h]) == G
+        assert np.array_equal(cache.rep_k[h, :G].float().cpu().numpy(), refs[h].rep_k)
+
+
+def test_quant_query_driven_chunk_matches_oracle(fa):
+    from kv_compressed_attention_amd.layer import FastARLayer
+
+    w = make_workload(1)
+    H, F, T, d = w.k_frames.shape
+    layer = FastARLayer(H, d, w.n_bits, w.n_probes, w.tau, T, F * T, w.n_queries, w.chunk_frames,
+                        dtype=torch.bfloat16, device="cuda", match="quant", query_driven=True)
+    layer.set_planes(dev_tensor(w.planes, "bf16"))
+    for f in range(w.setup_frames):
+        layer.merge(dev_tensor(w.k_frames[:, f], "bf16"), dev_tensor(w.v_frames[:, f], "bf16"), 1,
+                    with_index=False)
+    q = dev_tensor(w.q, "bf16")
+    k_new, v_new = (dev_tensor(a, "bf16") for a in w.frames(w.setup_frames, F))
+    layer.step(q, k_new, v_new)
+    torch.cuda.synchronize()
+    ref = oracle.run_chunk(w, heads=[3], match="quant", query_driven=True)
+    r = ref[3]
+    assert np.array_equal(layer.group_of_new[3].cpu().numpy(), r["group_of_new"])
+    assert int(layer.cache.n_groups[3]) == r["cache"].n_groups
+    err = np.max(np.abs(layer.o_self[3].float().cpu().numpy() - r["o_self"]))
+    assert err <= TOL["bf16"]

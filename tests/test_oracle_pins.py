@@ -745,3 +745,26 @@ def test_quant_rescaled_keys_give_the_same_groups_and_conserve_mass():
     assert np.array_equal(np.bincount(np.concatenate(ga), minlength=a.n_groups), a.count)
     for g in ga:
         assert len(set(g.tolist())) == T
+
+
+def test_quant_query_driven_by_hand():
+    # the new token's query (0, 1) finds the previous key (0.1, 1) although its
+    # own key (1, 0) would have matched the other previous key (1, 0.05): the
+    # token joins group 0 with its key and value
+    from oracle import TempCacheQuantOracle
+    prev = np.array([[0.1, 1.0], [1.0, 0.05]])
+    for qd, want in [(True, [0]), (False, [1])]:
+        tc = TempCacheQuantOracle(2, "f32", 8)
+        tc.merge_frame(prev, np.ones((2, 2)), np.zeros(2, int), 0.99)
+        g = tc.merge_frame(np.array([[1.0, 0.0]]), np.array([[3.0, 3.0]]), np.zeros(1, int), 0.99,
+                           match_vec=np.array([[0.0, 1.0]]) if qd else None)
+        assert g.tolist() == want
+        assert tc.rep_k[want[0]].tolist() == [1.0, 0.0] and tc.count[want[0]] == 2
+    # a query equal to its key gives the key-driven result
+    rng = np.random.default_rng(250)
+    k = round_to_dtype(rng.standard_normal((3, 30, 16)), "bf16")
+    a, b = TempCacheQuantOracle(16, "bf16"), TempCacheQuantOracle(16, "bf16")
+    for f in range(3):
+        ga = a.merge_frame(k[f], np.ones((30, 16)), np.zeros(30, int), 0.3)
+        gb = b.merge_frame(k[f], np.ones((30, 16)), np.zeros(30, int), 0.3, match_vec=k[f])
+        assert np.array_equal(ga, gb)
