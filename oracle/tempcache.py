@@ -28,6 +28,18 @@ Readings where the pages are silent:
   rounded once to the storage dtype, the bias is ln(count);
 * every decision in a frame uses the cache as it stood after frame f-1.
 
+Representative variants (paperlayer.ai appendix C compares last-key,
+mean-key and medoid-key representatives); readings:
+* mean: the exact mean of the group's keys, rounded once to the storage
+  dtype;
+* medoid: kept online, since the members are not stored: after a merge the
+  representative is whichever of the previous representative and the new key
+  has the larger cosine with the group's key sum (exactly; ties keep the
+  previous one);
+* with either, a frame's candidates are the current representatives of the
+  previous frame's groups, and a group's bucket is its newest key's bucket
+  (the one the next frame's lookup uses).
+
 Parity unpinned by the pages beyond Lemma 5.1: the selection rules above are
 the definition; they are pinned by exact-duplicate and no-merge closed cases,
 mass conservation and hand-worked tiny examples.
@@ -42,6 +54,22 @@ import numpy as np
 from .exact import exact_dot, exact_sqnorm, cos_compare, cos_at_least
 
 _U64 = 2.0 ** -53
+
+
+def round_fraction_to_storage(fr: Fraction, dtype: str) -> float:
+    """The exact rational fr rounded once (to nearest, ties to even) to the
+    storage dtype's precision (8 significant bits for bf16, 24 for f32)."""
+    if fr == 0:
+        return 0.0
+    bits = 8 if dtype == "bf16" else 24
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    # a = m 2^e with 1 <= m < 2: scale so that the integer part has `bits` bits
+    scaled = a / (Fraction(2) ** (e - bits + 1))
+    return sign * float(round(scaled)) * 2.0 ** (e - bits + 1)
 
 
 def round_to_storage(x, dtype: str) -> np.ndarray:
@@ -59,9 +87,13 @@ def round_to_storage(x, dtype: str) -> np.ndarray:
 class TempCacheOracle:
     """Compressed cache of one head, merged frame by frame."""
 
-    def __init__(self, dim: int, dtype: str):
+    def __init__(self, dim: int, dtype: str, representative: str = "last"):
+        if representative not in ("last", "mean", "medoid"):
+            raise ValueError(representative)
         self.dim = dim
         self.dtype = dtype
+        self.representative = representative
+        self.k_sum = []               # per group: exact key sum (Fractions), mean/medoid
         self.rep_k = np.zeros((0, dim))
         self.v_sum = np.zeros((0, dim))
         self.count = np.zeros(0, dtype=np.int64)
@@ -112,14 +144,37 @@ class TempCacheOracle:
         mj = np.nonzero(merged)[0]
         self.count[mg] += 1
         self.v_sum[mg] += v[mj]
-        self.rep_k[mg] = k[mj]
+        if self.representative == "last":
+            self.rep_k[mg] = k[mj]
+        else:
+            for g, j in zip(mg.tolist(), mj.tolist()):
+                self._update_rep(g, k[j])
         self.rep_bucket[mg] = bucket[mj]
+        if self.representative != "last":
+            self.k_sum += [[Fraction(float(x)) for x in k[j]] for j in fresh.tolist()]
         self.rep_k = np.concatenate([self.rep_k, k[fresh]])
         self.v_sum = np.concatenate([self.v_sum, v[fresh]])
         self.count = np.concatenate([self.count, np.ones(fresh.size, dtype=np.int64)])
         self.rep_bucket = np.concatenate([self.rep_bucket, bucket[fresh]])
         self.frontier = group.copy()
         return group
+
+    # -- representative of a group that key kj joins -------------------------
+    def _update_rep(self, g, kj):
+        s = self.k_sum[g]
+        for i, x in enumerate(kj.tolist()):
+            s[i] += Fraction(x)
+        if self.representative == "mean":
+            n = int(self.count[g])
+            self.rep_k[g] = [round_fraction_to_storage(x / n, self.dtype) for x in s]
+            return
+        # medoid: the previous representative or kj, by cosine with the sum
+        r = self.rep_k[g]
+        dot = lambda a: sum((Fraction(float(u)) * w for u, w in zip(a, s)), Fraction(0))  # noqa: E731
+        sq = lambda a: sum((Fraction(float(u)) ** 2 for u in a), Fraction(0))  # noqa: E731
+        ss = sum((w * w for w in s), Fraction(0))
+        if cos_compare(dot(kj), sq(kj) * ss, dot(r), sq(r) * ss) > 0:
+            self.rep_k[g] = kj
 
     # -- step 1: each new key's best previous-frame candidate ---------------
     def _match(self, k, bucket, prev_k, prev_b, tau_f, tau_q, target, tcos):

@@ -64,8 +64,8 @@ class TempCacheQuantOracle(TempCacheOracle):
     """TempCache whose top-1 match compares b-bit scalar codes of the keys
     against every previous-frame token."""
 
-    def __init__(self, dim: int, dtype: str, bits: int = 8):
-        super().__init__(dim, dtype)
+    def __init__(self, dim: int, dtype: str, bits: int = 8, representative: str = "last"):
+        super().__init__(dim, dtype, representative)
         self.bits = bits
         self._match_vec = None
 

@@ -768,3 +768,60 @@ def test_quant_query_driven_by_hand():
         ga = a.merge_frame(k[f], np.ones((30, 16)), np.zeros(30, int), 0.3)
         gb = b.merge_frame(k[f], np.ones((30, 16)), np.zeros(30, int), 0.3, match_vec=k[f])
         assert np.array_equal(ga, gb)
+
+
+# --------------------------------------------------------------------------
+# Representative variants
+# --------------------------------------------------------------------------
+
+def test_round_fraction_to_storage_by_hand():
+    from fractions import Fraction
+    from oracle.tempcache import round_fraction_to_storage as rf
+    assert rf(Fraction(1), "bf16") == 1.0
+    assert rf(Fraction(1) + Fraction(1, 512), "bf16") == 1.0                 # tie to even
+    assert rf(Fraction(1) + Fraction(3, 512), "bf16") == 1.0 + 2.0 ** -7     # tie to even (up)
+    assert rf(Fraction(1, 3), "bf16") == 171 / 512    # 1.0101010|1010.. x 2^-2 rounds up to 1.0101011
+    assert rf(Fraction(1, 3), "f32") == float(np.float32(1.0) / np.float32(3.0))
+    assert rf(Fraction(-5, 2), "bf16") == -2.5
+    # a mean of three keys rounded once: (1 + 1 + 1 + 2^-7) / 3 sits just above 1
+    assert rf((Fraction(3) + Fraction(1, 128)) / 3, "bf16") == 1.0
+
+
+def test_mean_and_medoid_representatives_by_hand():
+    # keys (1, 1) then (3, 1) merge (cos 0.894 >= 0.5); sum (4, 2).  Mean: (2, 1).
+    # Medoid: cos((1,1), (4,2)) = 0.949 < cos((3,1), (4,2)) = 0.990: the new key.
+    for rep, want in [("mean", [[2.0, 1.0]]), ("medoid", [[3.0, 1.0]]), ("last", [[3.0, 1.0]])]:
+        tc = TempCacheOracle(2, "f32", rep)
+        tc.merge_frame(np.array([[1.0, 1.0]]), np.ones((1, 2)), np.zeros(1, int), 0.5)
+        g = tc.merge_frame(np.array([[3.0, 1.0]]), np.ones((1, 2)), np.zeros(1, int), 0.5)
+        assert g.tolist() == [0] and tc.rep_k.tolist() == want, rep
+    # medoid over four frames: (1,0); (1,.5): sum (2,.5), cos .970 < .976, moves;
+    # (1,-.5): sum (3,0), cos .894 = .894 exactly, a tie keeps (1,.5); (1,0):
+    # sum (4,0), cos .894 < 1, moves.  The candidate each frame is matched
+    # against is the current representative (cos .6 and .894 pass 0.5).
+    tc = TempCacheOracle(2, "f32", "medoid")
+    steps = [([1.0, 0.0], [1.0, 0.0]), ([1.0, 0.5], [1.0, 0.5]), ([1.0, -0.5], [1.0, 0.5]),
+             ([1.0, 0.0], [1.0, 0.0])]
+    for key, rep in steps:
+        g = tc.merge_frame(np.array([key]), np.ones((1, 2)), np.zeros(1, int), 0.5)
+        assert g.tolist() == [0] and tc.rep_k.tolist() == [rep], (key, rep)
+    # the mean after the same four keys: (4, 0) / 4
+    tc = TempCacheOracle(2, "f32", "mean")
+    for key, _ in steps:
+        tc.merge_frame(np.array([key]), np.ones((1, 2)), np.zeros(1, int), 0.5)
+    assert tc.rep_k.tolist() == [[1.0, 0.0]] and tc.count.tolist() == [4]
+
+
+def test_representatives_on_exact_duplicates_agree():
+    # exact duplicates: every representative rule gives the same key, and the
+    # groups are the same
+    T, d, F = 30, 16, 4
+    k0 = gaussian((T, d), 260, "bf16")
+    vs = gaussian((F, T, d), 261, "bf16")
+    outs = []
+    for rep in ("last", "mean", "medoid"):
+        tc = TempCacheOracle(d, "bf16", rep)
+        gs = [tc.merge_frame(k0, vs[f], np.zeros(T, int), 0.9) for f in range(F)]
+        outs.append((tc.rep_k.copy(), np.concatenate(gs)))
+    for rk, g in outs[1:]:
+        assert np.array_equal(rk, outs[0][0]) and np.array_equal(g, outs[0][1])
