@@ -575,14 +575,15 @@ def rollout(w, dev, flush):
     return out
 
 
-def tau_sweep(w, dev, taus, match="lsh"):
+def tau_sweep(w, dev, taus, match="lsh", representative="last"):
     """TempCache's threshold swept on workload w (paperlayer.ai appendix C,
     tau 0.9 -> 0.5): per tau the chunk time (cold, after a 512 MB write), the
     compressed cache's density (groups / raw keys), AnnSA's recall, and the
     merging's error: dense attention over the compressed cache (+ ln m, all
     groups) against dense attention over the raw frames, as the mean relative
     L2 error of the outputs and of the normalisers' ratio (exp(lse_comp -
-    lse_raw), 1 when the merged groups keep every raw key's mass)."""
+    lse_raw), 1 when the merged groups keep every raw key's mass).
+    representative: the groups' representative key (last, mean or medoid)."""
     import kv_compressed_attention_amd.fastar as fb
     from kv_compressed_attention_amd.layer import FastARLayer
 
@@ -600,7 +601,7 @@ def tau_sweep(w, dev, taus, match="lsh"):
     out = []
     for tau in taus:
         layer = FastARLayer(H, d, w.n_bits, w.n_probes, tau, T, F * T, w.n_queries, w.chunk_frames,
-                            dtype=tdt, device=dev, match=match)
+                            dtype=tdt, device=dev, match=match, representative=representative)
         layer.set_planes(up(w.planes))
         for f in range(w.setup_frames):
             layer.merge(up(w.k_frames[:, f]), up(w.v_frames[:, f]), 1, with_index=False)
@@ -805,6 +806,10 @@ def main():
         w1 = make_workload(1)
         extra["tau_sweep"] = {"workload": w1.name, "lsh": tau_sweep(w1, dev, [0.999, 0.99, 0.95, 0.9, 0.7, 0.5]),
                               "quant8": tau_sweep(w1, dev, [0.999, 0.99, 0.9, 0.5], match="quant")}
+        # the group representative (paperlayer.ai appendix C: last, mean and
+        # medoid keys) at two thresholds
+        extra["representatives"] = {"workload": w1.name, **{
+            rep: tau_sweep(w1, dev, [0.9, 0.7], representative=rep) for rep in ("last", "mean", "medoid")}}
         extra["annca"] = annca(make_workload(2), dev, args.steps)
         w3 = make_workload(3)
         roll = rollout(w3, dev, flush)

@@ -156,6 +156,14 @@ fastar_status_t fastar_bucket_index(const int32_t* bucket, int heads, int64_t n,
  *                                  bit 0 (FASTAR_CACHE_OVERFLOW), whether or
  *                                  not the call had a diag buffer; nothing
  *                                  clears it but fastar_cache_status(clear)
+ *   k_sum      [H][capacity][dim]  float64 running key sum, 8-byte aligned:
+ *                                  read and written only by merges with the
+ *                                  mean or medoid representative (NULL
+ *                                  otherwise allowed).  A sum that leaves
+ *                                  float64's exact range (keys of one group
+ *                                  whose magnitudes span more than about 50
+ *                                  binary orders) is counted in
+ *                                  diag->unresolved
  * An empty cache is one with n_groups all 0 and status 0; nothing else needs
  * clearing.  tokens_per_frame must be in [1, 2048]; capacity >=
  * tokens_per_frame.
@@ -180,6 +188,7 @@ typedef struct {
   int32_t* n_groups;
   int32_t* frontier;
   int32_t* status;
+  double* k_sum;
 } fastar_cache_t;
 
 /* fastar_cache_status -- the one call that synchronises: waits for `stream`,
@@ -208,7 +217,13 @@ fastar_status_t fastar_cache_status(const fastar_cache_t* cache, int clear, hipS
  *                   representative and the new key, the one of larger cosine
  *                   with the group's key sum (an online medoid; ties keep the
  *                   previous one).  Mean and medoid need cache->k_sum, and
- *                   merge the frames of a call one at a time.
+ *                   merge the frames of a call one at a time (a frame's
+ *                   candidates are the representatives of the previous
+ *                   frame's groups); a group's bucket is its newest key's.
+ *                   The mean is rounded exactly from the float64 sum; the
+ *                   medoid's cosine comparison is certified in float64, and
+ *                   one it cannot certify (other than identical keys, a tie)
+ *                   takes the float64 answer and counts in diag->unresolved.
  *   match_queries   NULL (key-driven), or [H][n_frames * T][d] queries of the
  *                   new frames' tokens, cache dtype: the new side of the
  *                   similarity is the token's query (query-driven

@@ -125,8 +125,9 @@ fastar_status_t merge_opts(const fastar_merge_opts_t* o, MergeOpt* m) {
       return fail(FASTAR_ERR_UNSUPPORTED, "code_bits %d not in [2, 8]", o->code_bits);
     m->bits = o->code_bits;
   }
-  if (o->representative != FASTAR_REP_LAST)
-    return fail(FASTAR_ERR_UNSUPPORTED, "representative %d not supported", o->representative);
+  if (o->representative != FASTAR_REP_LAST && o->representative != FASTAR_REP_MEAN &&
+      o->representative != FASTAR_REP_MEDOID)
+    return fail(FASTAR_ERR_UNSUPPORTED, "representative %d unknown", o->representative);
   m->rep = o->representative;
   if (o->match_queries) {
     if (o->match != FASTAR_MATCH_QUANT)
@@ -213,6 +214,82 @@ fastar::MergeWs merge_carve(const fastar_cache_t* c, int n_frames, void* ws) {
   mw.mrange = take(16 * H * F * ((T + 63) / 64));
   mw.index_ws = take(16 * H * (size_t)c->capacity);
   return mw;
+}
+
+// the key sum that mean and medoid representatives keep
+fastar_status_t check_rep(const fastar_cache_t* c, const MergeOpt& m) {
+  if (m.rep == FASTAR_REP_LAST) return FASTAR_OK;
+  if (!c->k_sum || !aligned16(c->k_sum))
+    return fail(FASTAR_ERR_INVALID, "mean and medoid representatives need a 16-byte aligned cache->k_sum");
+  return FASTAR_OK;
+}
+
+// frame f of a [H][n_frames * T][d] tensor
+fastar_tensor_t frame_slice(const fastar_tensor_t& t, int T, int f) {
+  fastar_tensor_t r = t;
+  const size_t es = t.dtype == FASTAR_BF16 ? 2 : 4;
+  r.data = (const char*)t.data + (size_t)f * T * (size_t)t.stride_token * es;
+  r.tokens = T;
+  return r;
+}
+
+// The merge's launches, in stream order.  With the last-key representative
+// all frames go at once; mean and medoid representatives change what the
+// next frame is matched against, so each frame is merged by its own launch
+// sequence (workspace carved for one frame, rows strided as the whole call's;
+// the hashing that rides on the match only with the first frame, the
+// representatives' index and what rides on it only after the last).
+fastar_status_t run_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new, const fastar_tensor_t* v_new,
+                          const int32_t* kb, int F, float tau, const MergeOpt& mo, int32_t* group_of_new,
+                          int32_t* rep_offsets, int32_t* rep_perm, const fastar::MergeWs& mw, void* ws,
+                          fastar_diag_t* diag, hipStream_t stream) {
+  const int H = c->heads, T = c->tokens_per_frame;
+  if (mo.rep == FASTAR_REP_LAST) {
+    if (mo.match == FASTAR_MATCH_QUANT) {
+      const fastar::QuantWs q =
+          fastar::quant_carve(H, T, F, c->dim, mo.q != nullptr, (char*)ws + merge_workspace(c, F));
+      return hip_status(fastar::launch_tempcache_merge_quant(*c, *k_new, *v_new, mo.q, kb, F, tau, mo.bits,
+                                                             group_of_new, rep_offsets, rep_perm, mw, q, diag,
+                                                             stream),
+                        "tempcache_merge (quantized match)");
+    }
+    return hip_status(fastar::launch_tempcache_merge(*c, *k_new, *v_new, kb, F, tau, group_of_new, rep_offsets,
+                                                     rep_perm, mw, diag, stream),
+                      "tempcache_merge");
+  }
+  fastar::MergeWs one = merge_carve(c, 1, ws);
+  one.rep = mo.rep;
+  one.kb_stride = (int64_t)F * T;
+  one.hash_planes = mw.hash_planes;
+  one.hash_bits = mw.hash_bits;
+  const fastar::QuantWs q1 =
+      mo.match == FASTAR_MATCH_QUANT
+          ? fastar::quant_carve(H, T, 1, c->dim, mo.q != nullptr, (char*)ws + merge_workspace(c, 1))
+          : fastar::QuantWs{};
+  for (int f = 0; f < F; ++f) {
+    const bool last = f == F - 1;
+    fastar::MergeWs wf = one;
+    wf.also_hash = f == 0 ? mw.also_hash : nullptr;
+    wf.also_index = last ? mw.also_index : nullptr;
+    const fastar_tensor_t kf = frame_slice(*k_new, T, f), vf = frame_slice(*v_new, T, f);
+    int32_t* gf = group_of_new ? group_of_new + (int64_t)f * T : nullptr;
+    int32_t* ro = last ? rep_offsets : nullptr;
+    int32_t* rp = last ? rep_perm : nullptr;
+    fastar_status_t st;
+    if (mo.match == FASTAR_MATCH_QUANT) {
+      fastar_tensor_t qf;
+      if (mo.q) qf = frame_slice(*mo.q, T, f);
+      st = hip_status(fastar::launch_tempcache_merge_quant(*c, kf, vf, mo.q ? &qf : nullptr, kb + (int64_t)f * T, 1,
+                                                           tau, mo.bits, gf, ro, rp, wf, q1, diag, stream),
+                      "tempcache_merge (quantized match)");
+    } else {
+      st = hip_status(fastar::launch_tempcache_merge(*c, kf, vf, kb + (int64_t)f * T, 1, tau, gf, ro, rp, wf,
+                                                     diag, stream),
+                      "tempcache_merge");
+    }
+    if (st != FASTAR_OK) return st;
+  }
+  return FASTAR_OK;
 }
 
 fastar_status_t prune_check(const int32_t* q_bucket, int heads, int64_t n_q, int n_probes,
@@ -412,20 +489,11 @@ fastar_status_t fastar_tempcache_merge_ex(const fastar_cache_t* c, const fastar_
     }
     return FASTAR_OK;
   }
+  if ((st = check_rep(c, mo)) != FASTAR_OK) return st;
   if (!ws || ws_bytes < need)
     return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need, ws_bytes);
-  const fastar::MergeWs mw = merge_carve(c, n_frames, ws);
-  if (mo.match == FASTAR_MATCH_QUANT) {
-    const fastar::QuantWs q = fastar::quant_carve(c->heads, c->tokens_per_frame, n_frames, c->dim,
-                                                  mo.q != nullptr, (char*)ws + merge_workspace(c, n_frames));
-    return hip_status(fastar::launch_tempcache_merge_quant(*c, *k_new, *v_new, mo.q, k_new_bucket, n_frames,
-                                                           tau, mo.bits, group_of_new, rep_offsets, rep_perm,
-                                                           mw, q, diag, stream),
-                      "tempcache_merge (quantized match)");
-  }
-  return hip_status(fastar::launch_tempcache_merge(*c, *k_new, *v_new, k_new_bucket, n_frames, tau,
-                                                   group_of_new, rep_offsets, rep_perm, mw, diag, stream),
-                    "tempcache_merge");
+  return run_merge(c, k_new, v_new, k_new_bucket, n_frames, tau, mo, group_of_new, rep_offsets, rep_perm,
+                   merge_carve(c, n_frames, ws), ws, diag, stream);
 }
 
 fastar_status_t fastar_tempcache_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
@@ -580,6 +648,7 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   MergeOpt mo;
   if ((st = merge_opts(a->merge_opts, &mo)) != FASTAR_OK) return st;
   if ((st = check_match_queries(mo, a->k_new)) != FASTAR_OK) return st;
+  if ((st = check_rep(c, mo)) != FASTAR_OK) return st;
   const int match = mo.match;
   if ((st = merge_check(c, a->k_new, a->v_new, a->k_bucket, a->n_frames, a->tau, a->rep_offsets,
                         a->rep_perm)) != FASTAR_OK)
@@ -636,20 +705,9 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   const bool fused = a->q->tokens > 0 &&
                      fastar::direct_index_supported(c->capacity, 1, c->n_bits, a->q->tokens, a->n_probes);
   if (fused) mw.also_index = &qj;
-  if (match == FASTAR_MATCH_QUANT) {
-    const fastar::QuantWs q = fastar::quant_carve(c->heads, c->tokens_per_frame, a->n_frames, c->dim,
-                                                  mo.q != nullptr, (char*)ws + merge_workspace(c, a->n_frames));
-    if ((st = hip_status(fastar::launch_tempcache_merge_quant(*c, *a->k_new, *a->v_new, mo.q, a->k_bucket,
-                                                              a->n_frames, a->tau, mo.bits, a->group_of_new,
-                                                              a->rep_offsets, a->rep_perm, mw, q, diag, stream),
-                         "tempcache_merge (quantized match)")) != FASTAR_OK)
-      return st;
-  } else if ((st = hip_status(fastar::launch_tempcache_merge(*c, *a->k_new, *a->v_new, a->k_bucket, a->n_frames,
-                                                             a->tau, a->group_of_new, a->rep_offsets,
-                                                             a->rep_perm, mw, diag, stream),
-                              "tempcache_merge")) != FASTAR_OK) {
+  if ((st = run_merge(c, a->k_new, a->v_new, a->k_bucket, a->n_frames, a->tau, mo, a->group_of_new,
+                      a->rep_offsets, a->rep_perm, mw, ws, diag, stream)) != FASTAR_OK)
     return st;
-  }
   if (!fused) {
     int32_t* iws = (int32_t*)((char*)ws + merge_workspace_ex(c, a->n_frames, a->merge_opts));
     if ((st = hip_status(fastar::launch_bucket_index(a->q_bucket, a->q->heads, a->q->tokens, a->n_probes,

@@ -95,6 +95,8 @@ struct MergeWs {
   const HashJobs* also_hash = nullptr;
   const void* hash_planes = nullptr;
   int hash_bits = 0;
+  int rep = FASTAR_REP_LAST;  // representative kind (mean and medoid: one frame per call)
+  int64_t kb_stride = 0;      // row stride of k_new_bucket and group_of_new (0: n_frames * T)
 };
 // the merge's last launches for any match kind: the group updates (from the
 // links, successors and opener counts in a) and the representatives' index

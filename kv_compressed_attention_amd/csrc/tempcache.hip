@@ -487,12 +487,21 @@ __device__ __forceinline__ void top2_merge_dpp(Top2<float>& t) {
 
 // float64 cosine of two rows, the whole wave (lane l takes dims l, l + 64, ..);
 // every lane returns it.  Products of the stored values are exact in float64.
+// exact: the value is the cosine itself, not an estimate: 0 for a zero row,
+// 1 for two bitwise-identical nonzero rows.
+struct Cos64 {
+  double c;
+  bool exact;
+};
 template <typename T, int D>
-__device__ double wave_cos64(const T* x, const T* y) {
+__device__ Cos64 wave_cos64(const T* x, const T* y) {
   double s = 0.0, na = 0.0, nb = 0.0;
+  bool differ = false;
   for (int d = lane_id(); d < D; d += FASTAR_WAVE) {
-    const double u = (double)Elem<T>::load(x, d);
-    const double v = (double)Elem<T>::load(y, d);
+    const float uf = Elem<T>::load(x, d), vf = Elem<T>::load(y, d);
+    differ = differ || __float_as_uint(uf) != __float_as_uint(vf);
+    const double u = (double)uf;
+    const double v = (double)vf;
     s += u * v;
     na += u * u;
     nb += v * v;
@@ -503,8 +512,9 @@ __device__ double wave_cos64(const T* x, const T* y) {
     na += __shfl_xor(na, m, FASTAR_WAVE);
     nb += __shfl_xor(nb, m, FASTAR_WAVE);
   }
-  if (na == 0.0 || nb == 0.0) return 0.0;
-  return s / sqrt(na * nb);
+  if (na == 0.0 || nb == 0.0) return Cos64{0.0, true};
+  if (ballot64(differ) == 0) return Cos64{1.0, true};
+  return Cos64{s / sqrt(na * nb), false};
 }
 
 // What one wave needs to match keys of new frame f.
@@ -551,15 +561,29 @@ __device__ __forceinline__ void decide(const SegCtx<T, D>& x, const Top2<float>&
     const int32_t* gl;
     int n;
     cand_of(src, cl, gl, n);
+    const T* key = x.kf + (int64_t)js * x.k_st;
     Top2<double> u;
     u.init();
-    for (int k = 0; k < n; ++k)
-      u.add(wave_cos64<T, D>(x.kf + (int64_t)js * x.k_st, x.cand_row(k, cl[k], x.f == 0 ? gl[k] : 0)),
-            cl[k]);
+    for (int k = 0; k < n; ++k) u.add(wave_cos64<T, D>(key, x.cand_row(k, cl[k], x.f == 0 ? gl[k] : 0)).c, cl[k]);
+    // certified: the threshold test (an exact best value decides it exactly)
+    // and, with a proposal, the winner (every candidate within the bound of
+    // the best has an exact value: equal values go to the smaller index)
+    bool ex1 = false;
+    int near = 0, near_exact = 0;
+    if (u.c1 >= (double)x.tau - e64) {
+      for (int k = 0; k < n; ++k) {
+        const Cos64 r = wave_cos64<T, D>(key, x.cand_row(k, cl[k], x.f == 0 ? gl[k] : 0));
+        if (cl[k] == u.best) ex1 = r.exact;
+        if (r.c >= u.c1 - 2.0 * e64) {
+          ++near;
+          near_exact += r.exact ? 1 : 0;
+        }
+      }
+    }
     if (lane == src) {
       if (x.diag) atomicAdd(&x.diag->merge_fallbacks, 1u);
-      const bool sure = (u.c1 < (double)x.tau - e64) ||
-                        (u.c1 >= (double)x.tau + e64 && u.c1 - u.c2 > 2.0 * e64);
+      const bool thr_sure = ex1 || fabs(u.c1 - (double)x.tau) > e64;
+      const bool sure = thr_sure && (u.c1 < (double)x.tau || near <= 1 || near == near_exact);
       if (!sure && x.diag) atomicAdd(&x.diag->unresolved, 1u);
       best = u.best;
       prop = u.c1 >= (double)x.tau;
@@ -726,15 +750,18 @@ __device__ __forceinline__ bool resolve_keys(const SegCtx<T, D>& x, int self, in
     const int js = __shfl(j, src, FASTAR_WAVE);
     const int qs = __shfl(self, src, FASTAR_WAVE);
     const T* prev = x.f == 0 ? x.rk + (int64_t)fr[ps] * D : x.kp + (int64_t)ps * x.k_st;
-    const double dj = wave_cos64<T, D>(x.kf + (int64_t)js * x.k_st, prev);
+    const Cos64 cj = wave_cos64<T, D>(x.kf + (int64_t)js * x.k_st, prev);
+    const double dj = cj.c;
     bool w = true, unres = false;
     for (int q2 = 0; q2 < x.nk; ++q2) {
       int p2, j2;
       float c2;
       other(q2, p2, c2, j2);
       if (q2 == qs || p2 != ps) continue;
-      const double dd = wave_cos64<T, D>(x.kf + (int64_t)j2 * x.k_st, prev);
-      if (fabs(dd - dj) <= 2.0 * e64) unres = true;
+      const Cos64 cd = wave_cos64<T, D>(x.kf + (int64_t)j2 * x.k_st, prev);
+      const double dd = cd.c;
+      // two exact values compare exactly (equal ones go to the smaller j)
+      if (fabs(dd - dj) <= 2.0 * e64 && !(cd.exact && cj.exact)) unres = true;
       if (dd > dj || (dd == dj && j2 < js)) w = false;
     }
     if (lane == src) {
@@ -995,6 +1022,133 @@ __global__ __launch_bounds__(256, 4) void tc_match_kernel(
     match_group<T, D, 0>(x, a, h, p0, p1, c0, c1, frontier, lds);
 }
 
+// The float64 quotient s / n rounded once to the storage dtype T (to nearest,
+// ties to even).  q = fl(s / n) is on the same side of every rounding
+// midpoint of T as s / n unless q is itself a midpoint; then the sign of
+// s - n q, exact from one fma, tells which side s / n lies on.
+template <typename T>
+__device__ __forceinline__ float mean_round(double s, int n) {
+  constexpr int kDrop = sizeof(T) == 2 ? 45 : 29;  // float64 fraction bits T lacks
+  const double q = s / (double)n;
+  const uint64_t b = (uint64_t)__double_as_longlong(q);
+  const uint64_t low = b & ((1ull << kDrop) - 1), base = b - low;
+  const uint64_t half = 1ull << (kDrop - 1);
+  bool away;  // round the magnitude up
+  if (low != half) {
+    away = low > half;
+  } else {
+    const double r = fma(-(double)n, q, s);
+    away = r == 0.0 ? ((base >> kDrop) & 1) != 0 : ((r > 0.0) == (q > 0.0));
+  }
+  return (float)__longlong_as_double((long long)(base + (away ? (1ull << kDrop) : 0ull)));
+}
+
+// A mean- or medoid-key group's representative state, held by the 16 lanes
+// of its token (D/16 elements each): the group's float64 key sum and the
+// current representative.  Adding a key to the sum is checked with an exact
+// two-sum; a rounded addition is counted as unresolved.  Mean: the sum over
+// the count, rounded once (mean_round).  Medoid: of the previous
+// representative r and the new key k, the one of larger cosine with the sum
+// S; both cosines are evaluated in float64 with a bound (products and sums of
+// D terms: (D + 2) u sum|x_i S_i| on the dot, (D + 8) u |dot| for the norm
+// and the square root, doubled); a difference inside the bound keeps r if the
+// two are an exact tie (identical keys, or both cosines exactly computed) and
+// otherwise takes the float64 answer and counts as unresolved.
+template <typename T, int D, int REP>
+struct RepState {
+  static constexpr int EPL = D / 16;
+  double ks[EPL];
+  float rk[EPL];
+  bool inexact = false;
+  int unres = 0;
+
+  __device__ __forceinline__ void open(const float* k) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      ks[e] = (double)k[e];
+      rk[e] = k[e];
+    }
+  }
+  __device__ __forceinline__ void load(const T* rep, const double* sum) {
+    Chunk<T, EPL>::load(rep, rk);
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2) {
+      const double2 u = *reinterpret_cast<const double2*>(sum + e);
+      ks[e] = u.x;
+      ks[e + 1] = u.y;
+    }
+  }
+  __device__ __forceinline__ void join(const float* k, int) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const double x = (double)k[e];
+      const double t = ks[e] + x;
+      const double bb = t - ks[e];
+      const double err = (ks[e] - (t - bb)) + (x - bb);
+      inexact = inexact || err != 0.0;
+      ks[e] = t;
+    }
+    if (REP != FASTAR_REP_MEDOID) return;
+    double dk = 0.0, dr = 0.0, nk = 0.0, nr = 0.0, ak = 0.0, ar = 0.0;
+    bool differ = false;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const double x = (double)k[e], r = (double)rk[e], sv = ks[e];
+      dk = fma(x, sv, dk);
+      dr = fma(r, sv, dr);
+      nk = fma(x, x, nk);
+      nr = fma(r, r, nr);
+      ak += fabs(x * sv);
+      ar += fabs(r * sv);
+      differ = differ || __float_as_uint(k[e]) != __float_as_uint(rk[e]);
+    }
+    dk = sum16d(dk);
+    dr = sum16d(dr);
+    nk = sum16d(nk);
+    nr = sum16d(nr);
+    ak = sum16d(ak);
+    ar = sum16d(ar);
+    constexpr double u = 0x1p-53;
+    const double sk = sqrt(nk), sr = sqrt(nr);
+    const double ck = nk > 0.0 ? dk / sk : 0.0, cr = nr > 0.0 ? dr / sr : 0.0;
+    const double ek = nk > 0.0 ? 2.0 * ((D + 2) * u * ak + (D + 8) * u * fabs(dk)) / sk : 0.0;
+    const double er = nr > 0.0 ? 2.0 * ((D + 2) * u * ar + (D + 8) * u * fabs(dr)) / sr : 0.0;
+    const double diff = ck - cr, bound = ek + er;
+    bool take;
+    if (diff > bound) {
+      take = true;
+    } else if (-diff > bound) {
+      take = false;
+    } else {
+      const int lane = lane_id();
+      const bool same = ((ballot64(differ) >> (lane & 48)) & 0xFFFFull) == 0;
+      if (same || (bound == 0.0 && diff == 0.0)) {
+        take = false;  // a tie keeps the previous representative
+      } else {
+        take = diff > 0.0;
+        ++unres;
+      }
+    }
+    if (take) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) rk[e] = k[e];
+    }
+  }
+  __device__ __forceinline__ void store(T* rep, double* sum, int n, fastar_diag_t* diag) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float r = REP == FASTAR_REP_MEAN ? mean_round<T>(ks[e], n) : rk[e];
+      Elem<T>::store(rep, e, r);  // r is a value of T: stored exactly
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2) *reinterpret_cast<double2*>(sum + e) = make_double2(ks[e], ks[e + 1]);
+    const int lane = lane_id();
+    const bool any_inexact = ((ballot64(inexact) >> (lane & 48)) & 0xFFFFull) != 0;
+    const int total = unres + (any_inexact ? 1 : 0);
+    if ((lane & 15) == 0 && total && diag) atomicAdd(&diag->unresolved, (unsigned)total);
+  }
+};
+
 // Group rows, 16 lanes per chain (D/16 elements each).  A token that opens a
 // group gets the group count before the call plus the number of tokens
 // before it in (frame, j) order that open groups (the counts of the 64-token
@@ -1003,16 +1157,18 @@ __global__ __launch_bounds__(256, 4) void tc_match_kernel(
 // token that opens a group, or at a frame-0 token that extends a frontier
 // group; it follows nextj through the later frames.  Value sums are
 // accumulated frame by frame in float32, exactly as merging the frames one at
-// a time would; the representative is the chain's last key.  Every member's
-// group goes to group_of_new, last-frame members' to the frontier.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void tc_apply_kernel(
+// a time would; the representative is the chain's last key (REP =
+// FASTAR_REP_LAST), or is updated at every member from the group's float64
+// key sum (RepState).  Every member's group goes to group_of_new, last-frame
+// members' to the frontier.
+template <typename T, int D, int REP>
+__device__ __forceinline__ void tc_apply_body(
     T* __restrict__ rep_k, T* __restrict__ v_mean, float* __restrict__ v_sum,
     int32_t* __restrict__ count, float* __restrict__ log_count, int32_t* __restrict__ rep_bucket,
     int32_t* __restrict__ n_groups, int32_t* __restrict__ frontier, int32_t* __restrict__ group_of_new,
     const T* __restrict__ knew, int64_t k_sh, int64_t k_st, const T* __restrict__ vnew,
     int64_t v_sh, int64_t v_st, const int32_t* __restrict__ kbucket, MergeArgs a,
-    int32_t* __restrict__ status, fastar_diag_t* __restrict__ diag) {
+    int32_t* __restrict__ status, fastar_diag_t* __restrict__ diag, double* __restrict__ k_sum) {
   constexpr int EPL = D / 16;
   const int h = blockIdx.y;
   const int64_t idx = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -1086,15 +1242,21 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
   const int64_t gi = (int64_t)h * a.cap + g;
   float sum[EPL];
   int cnt;
+  RepState<T, D, REP> rs;
   if (lk < 0) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) sum[e] = vv[e];
     cnt = 1;
+    if (REP != FASTAR_REP_LAST) rs.open(kk);
   } else {
     const float* vs = v_sum + gi * D + sub * EPL;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) sum[e] = vs[e] + vv[e];
     cnt = count[gi] + 1;
+    if (REP != FASTAR_REP_LAST) {
+      rs.load(rep_k + gi * D + sub * EPL, k_sum + gi * D + sub * EPL);
+      rs.join(kk, cnt);
+    }
   }
   // the successors: each hop loads the member's rows, bucket and successor at once
   while (nx >= 0) {
@@ -1108,15 +1270,18 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) sum[e] += vv[e];
     ++cnt;
+    if (REP != FASTAR_REP_LAST) rs.join(kk, cnt);
   }
   T* rkr = rep_k + gi * D + sub * EPL;
   T* vmr = v_mean + gi * D + sub * EPL;
   float* vsr = v_sum + gi * D + sub * EPL;
   const float fc = (float)cnt;
+  if (REP != FASTAR_REP_LAST) rs.store(rkr, k_sum + gi * D + sub * EPL, cnt, diag);
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     vsr[e] = sum[e];
-    Elem<T>::store(rkr, e, kk[e]);  // the last key, exactly (stored values round-trip)
+    // the last key, exactly (stored values round-trip)
+    if (REP == FASTAR_REP_LAST) Elem<T>::store(rkr, e, kk[e]);
     if (cnt == 1) Elem<T>::store(vmr, e, sum[e]);  // exact copy of the value
     else Elem<T>::store(vmr, e, sum[e] / fc);
   }
@@ -1125,6 +1290,32 @@ __global__ __launch_bounds__(256) void tc_apply_kernel(
     log_count[gi] = logf(fc);
     rep_bucket[gi] = kb;
   }
+}
+
+template <typename T, int D, int REP>
+__global__ __launch_bounds__(256) void tc_apply_kernel(
+    T* __restrict__ rep_k, T* __restrict__ v_mean, float* __restrict__ v_sum,
+    int32_t* __restrict__ count, float* __restrict__ log_count, int32_t* __restrict__ rep_bucket,
+    int32_t* __restrict__ n_groups, int32_t* __restrict__ frontier, int32_t* __restrict__ group_of_new,
+    const T* __restrict__ knew, int64_t k_sh, int64_t k_st, const T* __restrict__ vnew,
+    int64_t v_sh, int64_t v_st, const int32_t* __restrict__ kbucket, MergeArgs a,
+    int32_t* __restrict__ status, fastar_diag_t* __restrict__ diag, double* __restrict__ k_sum) {
+  tc_apply_body<T, D, REP>(rep_k, v_mean, v_sum, count, log_count, rep_bucket, n_groups, frontier, group_of_new,
+                           knew, k_sh, k_st, vnew, v_sh, v_st, kbucket, a, status, diag, k_sum);
+}
+
+// the group updates of a merge, for the representative kind rep
+template <typename T, int D>
+void apply_launch(const fastar_cache_t& c, const fastar_tensor_t& kn, const fastar_tensor_t& vn,
+                  const int32_t* kb, const MergeArgs& a, int32_t* group_of_new, int rep,
+                  fastar_diag_t* diag, hipStream_t s) {
+  auto kern = rep == FASTAR_REP_MEAN     ? tc_apply_kernel<T, D, FASTAR_REP_MEAN>
+              : rep == FASTAR_REP_MEDOID ? tc_apply_kernel<T, D, FASTAR_REP_MEDOID>
+                                         : tc_apply_kernel<T, D, FASTAR_REP_LAST>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(((int64_t)a.F * a.Tf + 15) / 16), (unsigned)a.H), dim3(256), 0, s,
+                     (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count, c.rep_bucket, c.n_groups,
+                     c.frontier, group_of_new, (const T*)kn.data, kn.stride_head, kn.stride_token,
+                     (const T*)vn.data, vn.stride_head, vn.stride_token, kb, a, c.status, diag, c.k_sum);
 }
 
 template <typename T, int D>
@@ -1138,7 +1329,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   a.cap = c.capacity;
   a.F = F;
   a.nbits = c.n_bits;
-  a.kb_stride = (int64_t)F * Tf;
+  a.kb_stride = ws.kb_stride > 0 ? ws.kb_stride : (int64_t)F * Tf;
   a.off = ws.off;
   a.tok = ws.tok;
   a.tbk = ws.tbk;
@@ -1177,11 +1368,7 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
                      (const T*)c.rep_k,
                      (const T*)kn.data, kn.stride_head, kn.stride_token, c.frontier, tau, a, diag, qh,
                      (const uint16_t*)ws.hash_planes, ws.hash_bits, qblocks);
-  hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)F * Tf + 15) / 16), (unsigned)H),
-                     dim3(256), 0, s, (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count,
-                     c.rep_bucket, c.n_groups, c.frontier, group_of_new, (const T*)kn.data, kn.stride_head,
-                     kn.stride_token, (const T*)vn.data, vn.stride_head, vn.stride_token, kb, a,
-                     c.status, diag);
+  apply_launch<T, D>(c, kn, vn, kb, a, group_of_new, ws.rep, diag, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (rep_offsets && rep_perm)
@@ -1194,11 +1381,7 @@ template <typename T, int D>
 hipError_t apply_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fastar_tensor_t& vn,
                     const int32_t* kb, const MergeArgs& a, int32_t* group_of_new, int32_t* rep_offsets,
                     int32_t* rep_perm, const MergeWs& ws, fastar_diag_t* diag, hipStream_t s) {
-  hipLaunchKernelGGL((tc_apply_kernel<T, D>), dim3((unsigned)(((int64_t)a.F * a.Tf + 15) / 16), (unsigned)a.H),
-                     dim3(256), 0, s, (T*)c.rep_k, (T*)c.v_mean, c.v_sum, c.count, c.log_count,
-                     c.rep_bucket, c.n_groups, c.frontier, group_of_new, (const T*)kn.data, kn.stride_head,
-                     kn.stride_token, (const T*)vn.data, vn.stride_head, vn.stride_token, kb, a,
-                     c.status, diag);
+  apply_launch<T, D>(c, kn, vn, kb, a, group_of_new, ws.rep, diag, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (rep_offsets && rep_perm)

@@ -500,7 +500,7 @@ hipError_t merge_quant_td(const fastar_cache_t& c, const fastar_tensor_t& kn, co
   m.cap = c.capacity;
   m.F = F;
   m.nbits = c.n_bits;
-  m.kb_stride = (int64_t)F * Tf;
+  m.kb_stride = ws.kb_stride > 0 ? ws.kb_stride : (int64_t)F * Tf;
   m.link = ws.link;
   m.ocnt = ws.ocnt;
   m.nextj = ws.nextj;

@@ -48,6 +48,7 @@ class FastarCache(ctypes.Structure):
         ("n_groups", ctypes.c_void_p),
         ("frontier", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+        ("k_sum", ctypes.c_void_p),
     ]
 
 
@@ -259,7 +260,9 @@ class TempCache:
     """Device buffers of one layer's compressed cache (fastar_cache_t)."""
 
     def __init__(self, heads, dim, capacity, tokens_per_frame, n_bits, dtype=torch.bfloat16,
-                 device="cuda"):
+                 device="cuda", key_sums: bool = False):
+        """key_sums: also keep the float64 key sums that merges with the mean or
+        medoid representative need."""
         self.heads, self.dim, self.capacity = heads, dim, capacity
         self.tokens_per_frame, self.n_bits, self.dtype = tokens_per_frame, n_bits, dtype
         z = dict(device=device)
@@ -272,11 +275,16 @@ class TempCache:
         self.n_groups = torch.zeros(heads, dtype=torch.int32, **z)
         self.frontier = torch.full((heads, tokens_per_frame), -1, dtype=torch.int32, **z)
         self.status = torch.zeros(1, dtype=torch.int32, **z)
+        self.k_sum = (torch.zeros(heads, capacity, dim, dtype=torch.float64, **z) if key_sums
+                      else None)
 
     def buffers(self):
-        return dict(rep_k=self.rep_k, v_mean=self.v_mean, v_sum=self.v_sum, count=self.count,
-                    log_count=self.log_count, rep_bucket=self.rep_bucket,
-                    n_groups=self.n_groups, frontier=self.frontier, status=self.status)
+        b = dict(rep_k=self.rep_k, v_mean=self.v_mean, v_sum=self.v_sum, count=self.count,
+                 log_count=self.log_count, rep_bucket=self.rep_bucket,
+                 n_groups=self.n_groups, frontier=self.frontier, status=self.status)
+        if self.k_sum is not None:
+            b["k_sum"] = self.k_sum
+        return b
 
     def copy_from(self, other: "TempCache"):
         for name, t in self.buffers().items():
@@ -288,7 +296,8 @@ class TempCache:
                            self.v_sum.data_ptr(), self.count.data_ptr(),
                            self.log_count.data_ptr(), self.rep_bucket.data_ptr(),
                            self.n_groups.data_ptr(), self.frontier.data_ptr(),
-                           self.status.data_ptr())
+                           self.status.data_ptr(),
+                           None if self.k_sum is None else self.k_sum.data_ptr())
 
     def workspace_bytes(self, n_frames: int, opts: Optional[FastarMergeOpts] = None) -> int:
         c = self.struct()

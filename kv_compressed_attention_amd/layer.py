@@ -35,19 +35,22 @@ class FastARLayer:
     def __init__(self, heads: int, dim: int, n_bits: int, n_probes: int, tau: float,
                  tokens_per_frame: int, capacity: int, n_queries: int, chunk_frames: int,
                  n_prompt: int = 0, dtype=torch.bfloat16, device="cuda", match: str = "lsh",
-                 code_bits: int = 8, query_driven: bool = False):
+                 code_bits: int = 8, query_driven: bool = False, representative: str = "last"):
         self.heads, self.dim, self.n_bits, self.n_probes = heads, dim, n_bits, n_probes
         self.tau, self.T, self.capacity = tau, tokens_per_frame, capacity
         self.nq, self.chunk_frames, self.n_prompt = n_queries, chunk_frames, n_prompt
         self.dtype, self.device = dtype, torch.device(device)
         # the TempCache variant (None: the library's defaults)
-        self.opts = None if match == "lsh" else fb.merge_opts(match, code_bits)
+        self.opts = (None if match == "lsh" and representative == "last"
+                     else fb.merge_opts(match, code_bits, representative))
+        self.representative = representative
         # query-driven matching of a chunk's frames (by the chunk's queries,
         # which are then the new frames' tokens); set-up merges stay key-driven
         self.match, self.code_bits, self.query_driven = match, code_bits, query_driven
         H, dev = heads, self.device
         i32 = dict(dtype=torch.int32, device=dev)
-        self.cache = fb.TempCache(H, dim, capacity, tokens_per_frame, n_bits, dtype, dev)
+        self.cache = fb.TempCache(H, dim, capacity, tokens_per_frame, n_bits, dtype, dev,
+                                  key_sums=representative != "last")
         self.planes = torch.zeros(max(n_bits, 1), dim, dtype=dtype, device=dev)
         nk = chunk_frames * tokens_per_frame
         lib = fb.library()
@@ -56,7 +59,7 @@ class FastARLayer:
             # the workspace of query-driven matching (only the presence of the
             # query tensor matters for its size)
             self._qd_desc = fb.FastarTensor(0, fb._DTYPES[dtype], H, nk, dim, 0, nk * dim, dim)
-            size_opts = fb.merge_opts(match, code_bits)
+            size_opts = fb.merge_opts(match, code_bits, representative)
             size_opts.match_queries = ctypes.addressof(self._qd_desc)
         ws_bytes = max(lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
                        lib.fastar_hash_workspace(H, nk, n_bits, 1),
@@ -160,7 +163,7 @@ class FastARLayer:
     def _merge(self, cache, k_new, v_new, timing, q=None):
         opts = self.opts
         if self.query_driven:
-            opts = fb.merge_opts(self.match, self.code_bits, match_queries=q)
+            opts = fb.merge_opts(self.match, self.code_bits, self.representative, match_queries=q)
         self._timed(timing, "merge", lambda: fb.fastar_tempcache_merge(
             cache, k_new, v_new, self.k_ids.view(self.heads, -1), self.chunk_frames, self.tau,
             group_of_new=self.group_of_new, rep_offsets=self.rep_off, rep_perm=self.rep_perm,
@@ -185,7 +188,7 @@ class FastARLayer:
                              lse_cross=self.lse_cross)
             opts = self.opts
             if self.query_driven:
-                opts = fb.merge_opts(self.match, self.code_bits, match_queries=q)
+                opts = fb.merge_opts(self.match, self.code_bits, self.representative, match_queries=q)
             call = fb.ChunkCall(q, self.n_probes, k_new, v_new, self.chunk_frames, self.planes,
                                 self.n_bits, self.tau, cache, self.q_ids, self.q_off, self.q_perm,
                                 self.k_ids, self.rep_off, self.rep_perm, self.o_self,

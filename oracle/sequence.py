@@ -28,7 +28,8 @@ from .annca import prune_prompt, cross_attention
 from .attention import bucket_attention
 
 
-def run_chunk(w, heads=None, attention=True, match="lsh", code_bits=8, query_driven=False):
+def run_chunk(w, heads=None, attention=True, match="lsh", code_bits=8, query_driven=False,
+              representative="last"):
     """Run the sequence for workload-like object ``w`` on the given heads.
 
     ``w`` provides dtype, dim, n_bits, n_probes, tau, planes [b, d], q [H, N, d],
@@ -36,7 +37,8 @@ def run_chunk(w, heads=None, attention=True, match="lsh", code_bits=8, query_dri
     prompt_k/prompt_v [H, Np, d].  ``match``: TempCache's LSH match ("lsh") or
     its quantized match ("quant", ``code_bits`` bits; ``query_driven``: the
     chunk's frames are matched by their queries, ``w.q`` being the chunk
-    frames' tokens).  Returns a dict of per-head result dicts.
+    frames' tokens).  ``representative``: TempCache's group representative
+    ("last", "mean" or "medoid").  Returns a dict of per-head result dicts.
     """
     heads = range(w.heads) if heads is None else heads
     scale = 1.0 / np.sqrt(w.dim)
@@ -47,8 +49,8 @@ def run_chunk(w, heads=None, attention=True, match="lsh", code_bits=8, query_dri
         r["q_ids"] = simhash(q, w.planes, w.n_probes)
         r["q_offsets"], r["q_perm"] = bucket_index(r["q_ids"], w.n_bits)
         if w.k_frames is not None:
-            tc = (TempCacheQuantOracle(w.dim, w.dtype, code_bits) if match == "quant"
-                  else TempCacheOracle(w.dim, w.dtype))
+            tc = (TempCacheQuantOracle(w.dim, w.dtype, code_bits, representative) if match == "quant"
+                  else TempCacheOracle(w.dim, w.dtype, representative))
             F = w.k_frames.shape[1]
             groups = []
             setup_groups = []

@@ -52,7 +52,7 @@ def test_binding_covers_every_declared_symbol():
 
 def test_struct_layouts_match_header(lib):
     assert ctypes.sizeof(fb.FastarTensor) == 48
-    assert ctypes.sizeof(fb.FastarCache) == 24 + 9 * 8
+    assert ctypes.sizeof(fb.FastarCache) == 24 + 10 * 8
 
 
 def test_status_strings(lib):
@@ -264,6 +264,16 @@ def test_merge_options_rejected_without_launching(lib):
                                            ctypes.c_void_p(buf), 1, 0.9, ctypes.byref(o), None, None,
                                            None, ctypes.c_void_p(buf), 1 << 30, None, None)
         assert st == want, (match, bits)
+    # an unknown representative; mean and medoid without (or with a
+    # misaligned) key-sum buffer
+    for rep, k_sum, want in [(3, None, 2), (1, None, 1), (2, None, 1), (1, buf + 8, 1)]:
+        c.k_sum = k_sum
+        o = fb.FastarMergeOpts(0, 8, rep)
+        st = lib.fastar_tempcache_merge_ex(ctypes.byref(c), ctypes.byref(k), ctypes.byref(k),
+                                           ctypes.c_void_p(buf), 1, 0.9, ctypes.byref(o), None, None,
+                                           None, ctypes.c_void_p(buf), 1 << 30, None, None)
+        assert st == want, (rep, k_sum)
+    c.k_sum = None
     assert lib.fastar_tempcache_workspace_ex(ctypes.byref(c), 1, ctypes.byref(fb.FastarMergeOpts(1, 8))) > \
         lib.fastar_tempcache_workspace(ctypes.byref(c), 1)
     assert lib.fastar_scalar_codes(ctypes.byref(k), 1, ctypes.c_void_p(buf), ctypes.c_void_p(buf), None) == 2
