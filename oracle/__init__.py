@@ -9,7 +9,7 @@ every integer decision that depends on a float comparison (a hash sign, an
 arg-max, a threshold) settled on the exact real value of its operands:
 
 * ``simhash``     -- random-hyperplane hashing of queries and keys into
-                     bucket ids, optionally with a second probe (paper page
+                     bucket ids, optionally with more probes (paper page
                      "paperlayer.ai", section 5 Method, "ANN Attention";
                      paper.rainbus.top, prerequisites, ANN).
 * ``index``       -- the bucket-contiguous index (stable counting sort) that
@@ -31,6 +31,10 @@ arg-max, a threshold) settled on the exact real value of its operands:
                      attention formulation, section 5 "AnnSA", appendix A).
 * ``sequence``    -- one layer's per-chunk call sequence: hash, merge, prune,
                      self-attention, cross-attention.
+* ``multitable``  -- several LSH tables (and more probes per table): AnnSA
+                     over the union of the tables' buckets, AnnCA keeping a
+                     prompt token that any table keeps (paperlayer.ai
+                     section 2, approximate nearest neighbor search).
 * ``recall``      -- attention recall (dense mass kept by the retained
                      entries) and density, and the top-k reference
                      (paperlayer.ai section 4, attention sparsity).
@@ -52,3 +56,5 @@ from .annca import prune_prompt, cross_attention  # noqa: F401
 from .attention import dense_attention, bucket_attention  # noqa: F401
 from .sequence import run_chunk  # noqa: F401
 from .recall import attention_recall, bucket_retained, topk_recall  # noqa: F401
+from .multitable import (simhash_tables, retained_tables, bucket_attention_tables,  # noqa: F401
+                         prune_prompt_tables)

@@ -14,7 +14,12 @@ Readings where the pages are silent:
 * with two probes ("one or more buckets" per query, paper.rainbus.top method
   steps, AnnSA), the second bucket is the Hamming-1 neighbour across the
   hyperplane nearest to x: flip bit j* = argmin_j |x . r_j| / |r_j|, ties to
-  the smaller j.
+  the smaller j;
+* with P > 2 probes (multi-probe LSH, the bucket probing of paperlayer.ai
+  section 2 "Approximate nearest neighbor search"), probe p >= 1 flips the
+  bit of the p-th nearest hyperplane (the same distance, ascending, ties to
+  the smaller j): the Hamming-1 neighbours in order of how close x lies to
+  their boundary.  P <= n_bits + 1.
 """
 
 from __future__ import annotations
@@ -41,10 +46,8 @@ def simhash(x, planes, n_probes: int = 1) -> np.ndarray:
     planes = np.asarray(planes, dtype=np.float64).reshape(-1, x.shape[1])
     n, d = x.shape
     b = planes.shape[0]
-    if n_probes not in (1, 2):
-        raise ValueError("n_probes must be 1 or 2")
-    if n_probes == 2 and b == 0:
-        raise ValueError("a second probe needs at least one hyperplane")
+    if n_probes < 1 or n_probes > b + 1:
+        raise ValueError("n_probes must be in [1, n_bits + 1]")
     ids = np.zeros((n, n_probes), dtype=np.int64)
     if b == 0 or n == 0:
         return ids
@@ -66,19 +69,25 @@ def simhash(x, planes, n_probes: int = 1) -> np.ndarray:
     err = bound / rn + dist * (2 * d + 8) * _U64
     lo, hi = dist - err, dist + err
     sqn = None
+    k = n_probes - 1                                   # flipped bits wanted
     for r in range(n):
-        j0 = int(np.argmin(dist[r]))
-        cand = np.nonzero(lo[r] <= hi[r, j0])[0]
-        if cand.size > 1:
+        order = np.argsort(dist[r], kind="stable")     # ascending, ties to the smaller j
+        # planes that may be among the k nearest: any whose interval reaches
+        # below the upper end of the k-th nearest's
+        cand = np.nonzero(lo[r] <= hi[r, order[k - 1]])[0]
+        first = order[:k]
+        ivl = sorted(zip(lo[r, cand].tolist(), hi[r, cand].tolist()))
+        disjoint = all(ivl[i][1] < ivl[i + 1][0] for i in range(len(ivl) - 1))
+        if cand.size > k or not disjoint:
             if sqn is None:
                 sqn = [exact_sqnorm(planes[j]) for j in range(b)]
-            # compare s_j^2 / |r_j|^2 exactly; ties go to the smaller j
-            best, best_key = None, None
+            # order them by s_j^2 / |r_j|^2 exactly, ties to the smaller j
+            keyed = []
             for j in cand.tolist():
                 sj = exact_dot(x[r], planes[j])
-                key = sj * sj / sqn[j]
-                if best_key is None or key < best_key:
-                    best, best_key = j, key
-            j0 = best
-        ids[r, 1] = ids[r, 0] ^ (1 << j0)
+                keyed.append((sj * sj / sqn[j], j))
+            keyed.sort()
+            first = [j for _, j in keyed[:k]]
+        for p, j in enumerate(first):
+            ids[r, p + 1] = ids[r, 0] ^ (1 << int(j))
     return ids
