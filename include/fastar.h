@@ -11,6 +11,11 @@
  *   fastar_prune_prompt     AnnCA: drop prompt tokens no query shares a bucket with
  *   fastar_bucket_attention AnnSA / AnnCA attention, online softmax on MFMA
  *   fastar_chunk            one chunk of the layer sequence, all of the above
+ * and around them: several LSH tables (fastar_bucket_attention_tables,
+ * fastar_prune_prompt_tables), TempCache variants (fastar_tempcache_merge_ex),
+ * attention recall (fastar_attention_recall[_counts]), the cache's status
+ * word (fastar_cache_status) and an allocation-free chunk
+ * (fastar_chunk_noalloc).
  *
  * Conventions shared by every call
  * - All tensor and array arguments are DEVICE pointers owned by the caller.
@@ -23,8 +28,8 @@
  *   message for the last failure in the calling thread.
  * - Float inputs must be finite.  bf16 and fp32 are the supported dtypes;
  *   the head dimension must be 64 or 128.
- * - Integer decisions taken from float comparisons (hash signs, the second
- *   probe, TempCache's arg-max, threshold and conflict tests) follow the exact
+ * - Integer decisions taken from float comparisons (hash signs, the probes'
+ *   order, TempCache's arg-max, threshold and conflict tests) follow the exact
  *   real value of the stored inputs: a decision the fast float32 evaluation
  *   cannot certify is re-evaluated in float64 (and for hash signs, exactly).
  *   Counters of these events accumulate in an optional fastar_diag_t.
@@ -74,6 +79,10 @@ typedef struct {
   uint32_t reserved[3];
 } fastar_diag_t;
 
+/* Limits: probes per LSH table and tables of the multi-table calls. */
+#define FASTAR_MAX_PROBES 8
+#define FASTAR_MAX_TABLES 4
+
 const char* fastar_status_string(int status);
 const char* fastar_last_error(void);
 int fastar_version(void);
@@ -87,14 +96,17 @@ int fastar_version(void);
  *   x        [H][N][d], bf16 or fp32.
  *   planes   [n_bits][d], same dtype as x, contiguous: hyperplane normals r_j.
  *   n_bits   0..15.  Bit j of an id is 1 iff x . r_j > 0 (exact value).
- *   n_probes 1 or 2.  The second probe flips the bit of the hyperplane
- *            nearest to x: argmin_j |x . r_j| / |r_j|, ties to smaller j
- *            (requires n_bits >= 1).
+ *   n_probes 1 .. min(FASTAR_MAX_PROBES, n_bits + 1).  Probe p >= 1 flips
+ *            the bit of the p-th nearest hyperplane to x by distance
+ *            |x . r_j| / |r_j| (ascending, ties to the smaller j): the second
+ *            probe is the Hamming-1 neighbour across the nearest hyperplane,
+ *            later ones are multi-probe LSH's next neighbours (paperlayer.ai
+ *            section 2, approximate nearest neighbor search: bucket probing).
  *   bucket   out [H][N][n_probes] int32.
  *   offsets  out [H][2^n_bits + 1] int32, or NULL (no index).
  *   perm     out [H][N] int32, or NULL (together with offsets).
- *            perm lists token indices sorted by bucket (with two probes,
- *            the first probe's bucket; each token once), ascending token
+ *            perm lists token indices sorted by bucket (with several
+ *            probes, the first probe's bucket; each token once), ascending token
  *            within a bucket; offsets[B] = number of tokens whose (first)
  *            bucket is < B.
  *   ws       device workspace of at least fastar_hash_workspace() bytes,
@@ -114,7 +126,7 @@ fastar_status_t fastar_hash(const fastar_tensor_t* x, const void* planes, int n_
  * "technical novelty").
  *   count     1..4.
  *   x         [count] tensors [H_i][N_i][d], one dtype and d.
- *   n_probes  [count] host ints, 1 or 2 each.
+ *   n_probes  [count] host ints, each as for fastar_hash.
  *   bucket    [count] device outputs [H_i][N_i][n_probes[i]] int32.
  *   planes, n_bits, diag: as for fastar_hash.  Build an index of any of the
  *   ids with fastar_bucket_index.
@@ -326,6 +338,44 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
                                         hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * fastar_bucket_attention_tables -- AnnSA with n_tables LSH tables of
+ * n_probes probes each (hash-based retrieval probing buckets in several
+ * tables: paperlayer.ai section 2, approximate nearest neighbor search).
+ * Query t attends to A(t) = the union over tables u of the keys whose
+ * table-u bucket is one of t's table-u probes; a key in several tables'
+ * sets is attended once.  With n_tables = 1 this is fastar_bucket_attention's
+ * bucket mode (any n_probes).
+ *   n_tables   1 .. FASTAR_MAX_TABLES; n_tables * n_probes <= FASTAR_MAX_PROBES.
+ *   q_bucket   [n_tables][H][Nq][n_probes] int32 (fastar_hash with each
+ *              table's planes); q_perm [H][Nq] the rows' visit order (e.g.
+ *              table 0's index; any permutation is correct).
+ *   k_bucket   [n_tables][H][Nk] int32: every key's bucket in each table
+ *              (read for tables 0 .. n_tables - 2; may be NULL with one).
+ *   k_offsets  [n_tables][H][2^n_bits + 1], k_perm [n_tables][H][Nk]: each
+ *              table's key index (fastar_bucket_index; a compressed cache's
+ *              with n_valid = n_groups).
+ *   q, k, v, key_bias, scale, out, lse: as for fastar_bucket_attention.
+ *   n_attended out [H][Nq] int32 |A(t)|, or NULL.
+ *   n_tables * H * Nk must be < 2^31.
+ * ---------------------------------------------------------------------- */
+fastar_status_t fastar_bucket_attention_tables(const fastar_tensor_t* q, int n_tables, const int32_t* q_bucket,
+                                               const int32_t* q_perm, int n_probes, const fastar_tensor_t* k,
+                                               const fastar_tensor_t* v, const float* key_bias,
+                                               const int32_t* k_bucket, const int32_t* k_offsets,
+                                               const int32_t* k_perm, int n_bits, float scale, void* out,
+                                               float* lse, int32_t* n_attended, hipStream_t stream);
+
+/* fastar_prune_prompt_tables -- AnnCA with n_tables LSH tables: a prompt
+ * token is kept if, in some table u, its table-u bucket is one of the
+ * table-u probes of any query.  q_bucket [n_tables][H][n_q][n_probes],
+ * p_bucket [n_tables][H][n_prompt]; keep, kept_idx, n_kept as for
+ * fastar_prune_prompt (which this is with n_tables = 1). */
+fastar_status_t fastar_prune_prompt_tables(const int32_t* q_bucket, int n_tables, int heads, int64_t n_q,
+                                           int n_probes, const int32_t* p_bucket, int64_t n_prompt, int n_bits,
+                                           uint8_t* keep, int32_t* kept_idx, int32_t* n_kept,
+                                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * fastar_attention_recall -- attention recall and density of a sparse
  * attention against the dense one over the same keys (paperlayer.ai section 4
  * "Motivation", attention sparsity: the dense-attention mass the retained
@@ -351,6 +401,13 @@ fastar_status_t fastar_attention_recall(const float* lse_sparse, const float* ls
                                         const int32_t* k_offsets, int n_bits,
                                         const int32_t* n_retained, const int32_t* n_keys,
                                         float* recall, float* stats, hipStream_t stream);
+
+/* fastar_attention_recall_counts -- the same with |A(q)| given per query:
+ * n_attended [H][n_q] int32 device (e.g. fastar_bucket_attention_tables'
+ * n_attended).  Every other argument as for fastar_attention_recall. */
+fastar_status_t fastar_attention_recall_counts(const float* lse_sparse, const float* lse_dense, int heads,
+                                               int64_t n_q, const int32_t* n_attended, const int32_t* n_keys,
+                                               float* recall, float* stats, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * fastar_chunk -- one chunk of the per-layer sequence in one call, on one

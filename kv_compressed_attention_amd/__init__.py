@@ -10,11 +10,14 @@ from .fastar import (  # noqa: F401
     FastarError,
     TempCache,
     fastar_attention_recall,
+    fastar_attention_recall_counts,
     fastar_bucket_attention,
+    fastar_bucket_attention_tables,
     fastar_bucket_index,
     fastar_hash,
     fastar_hash_multi,
     fastar_prune_prompt,
+    fastar_prune_prompt_tables,
     fastar_scalar_codes,
     fastar_tempcache_merge,
     fastar_version,

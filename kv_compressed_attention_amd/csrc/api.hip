@@ -64,8 +64,9 @@ fastar_status_t check_tensor(const fastar_tensor_t* t, const char* name) {
 
 fastar_status_t check_bits(int n_bits, int n_probes) {
   if (n_bits < 0 || n_bits > 15) return fail(FASTAR_ERR_UNSUPPORTED, "n_bits %d not in [0, 15]", n_bits);
-  if (n_probes != 1 && n_probes != 2) return fail(FASTAR_ERR_UNSUPPORTED, "n_probes %d not 1 or 2", n_probes);
-  if (n_probes == 2 && n_bits < 1) return fail(FASTAR_ERR_INVALID, "two probes need n_bits >= 1");
+  if (n_probes < 1 || n_probes > FASTAR_MAX_PROBES)
+    return fail(FASTAR_ERR_UNSUPPORTED, "n_probes %d not in [1, %d]", n_probes, FASTAR_MAX_PROBES);
+  if (n_probes > n_bits + 1) return fail(FASTAR_ERR_INVALID, "%d probes need n_bits >= %d", n_probes, n_probes - 1);
   return FASTAR_OK;
 }
 
@@ -330,7 +331,7 @@ fastar_status_t attention_check(const fastar_tensor_t* q, const int32_t* q_bucke
     if (!k_offsets || !k_perm) return fail(FASTAR_ERR_INVALID, "bucket mode needs k_offsets and k_perm");
     if (key_list || n_key_list) return fail(FASTAR_ERR_INVALID, "give either bucket segments or a key list");
     if ((st = check_bits(n_bits, n_probes)) != FASTAR_OK) return st;
-    mode = 0;
+    mode = n_probes > 2 ? 3 : 0;  // more probes: the general (table, probe) mode
   } else if (key_list) {
     if (!n_key_list) return fail(FASTAR_ERR_INVALID, "list mode needs key_list and n_key_list");
     mode = 1;
@@ -340,7 +341,10 @@ fastar_status_t attention_check(const fastar_tensor_t* q, const int32_t* q_bucke
   *empty = (int64_t)q->heads * q->tokens == 0;
   if (*empty) return FASTAR_OK;
   if (!out || !aligned16(out)) return fail(FASTAR_ERR_INVALID, "out must be a non-null 16-byte aligned pointer");
-  if (mode == 0 && (!q_bucket || !q_perm)) return fail(FASTAR_ERR_INVALID, "bucket mode needs q_bucket and q_perm");
+  if ((mode == 0 || mode == 3) && (!q_bucket || !q_perm))
+    return fail(FASTAR_ERR_INVALID, "bucket mode needs q_bucket and q_perm");
+  if (mode == 3 && (int64_t)q->heads * k->tokens >= (int64_t)1 << 31)
+    return fail(FASTAR_ERR_UNSUPPORTED, "heads * keys must be < 2^31");
   if (q->dtype == FASTAR_BF16 && k->tokens > 0) {
     // the bf16 kernel addresses a head's k and v rows by 32-bit byte offsets
     const int64_t span_k = ((int64_t)(k->tokens - 1) * k->stride_token + k->dim) * 2;
@@ -349,7 +353,8 @@ fastar_status_t attention_check(const fastar_tensor_t* q, const int32_t* q_bucke
       return fail(FASTAR_ERR_UNSUPPORTED, "a head's k or v rows span more than 4 GiB");
   }
   a->q = q->data; a->q_sh = q->stride_head; a->q_st = q->stride_token; a->nq = q->tokens;
-  a->q_bucket = q_bucket; a->q_perm = q_perm; a->n_probes = mode == 0 ? n_probes : 1;
+  a->q_bucket = q_bucket; a->q_perm = q_perm; a->n_probes = (mode == 0 || mode == 3) ? n_probes : 1;
+  a->n_tables = 1; a->k_bucket = nullptr; a->n_attended = nullptr;
   a->k = k->data; a->k_sh = k->stride_head; a->k_st = k->stride_token;
   a->v = v->data; a->v_sh = v->stride_head; a->v_st = v->stride_token; a->nk = k->tokens;
   a->key_bias = key_bias; a->k_offsets = k_offsets; a->k_perm = k_perm; a->n_bits = n_bits;
@@ -548,6 +553,23 @@ fastar_status_t fastar_prune_prompt(const int32_t* q_bucket, int heads, int64_t 
                     "prune_prompt");
 }
 
+fastar_status_t fastar_prune_prompt_tables(const int32_t* q_bucket, int n_tables, int heads, int64_t n_q,
+                                           int n_probes, const int32_t* p_bucket, int64_t n_prompt, int n_bits,
+                                           uint8_t* keep, int32_t* kept_idx, int32_t* n_kept,
+                                           hipStream_t stream) {
+  if (n_tables < 1 || n_tables > FASTAR_MAX_TABLES)
+    return fail(FASTAR_ERR_UNSUPPORTED, "n_tables %d not in [1, %d]", n_tables, FASTAR_MAX_TABLES);
+  const fastar_status_t st =
+      prune_check(q_bucket, heads, n_q, n_probes, p_bucket, n_prompt, n_bits, keep, kept_idx, n_kept);
+  if (st != FASTAR_OK || heads == 0) return st;
+  if ((int64_t)n_tables * heads * n_q * n_probes >= (int64_t)1 << 31 ||
+      (int64_t)n_tables * heads * n_prompt >= (int64_t)1 << 31)
+    return fail(FASTAR_ERR_UNSUPPORTED, "sizes times n_tables must be < 2^31");
+  return hip_status(fastar::launch_prune(q_bucket, heads, n_q, n_probes, p_bucket, n_prompt, n_bits,
+                                         keep, kept_idx, n_kept, stream, n_tables),
+                    "prune_prompt_tables");
+}
+
 // ---------------------------------------------------------------------------
 fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t* q_bucket,
                                         const int32_t* q_perm, int n_probes,
@@ -563,6 +585,32 @@ fastar_status_t fastar_bucket_attention(const fastar_tensor_t* q, const int32_t*
                                              &empty);
   if (st != FASTAR_OK || empty) return st;
   return hip_status(fastar::launch_attention(a, stream), "bucket_attention");
+}
+
+fastar_status_t fastar_bucket_attention_tables(const fastar_tensor_t* q, int n_tables, const int32_t* q_bucket,
+                                               const int32_t* q_perm, int n_probes, const fastar_tensor_t* k,
+                                               const fastar_tensor_t* v, const float* key_bias,
+                                               const int32_t* k_bucket, const int32_t* k_offsets,
+                                               const int32_t* k_perm, int n_bits, float scale, void* out,
+                                               float* lse, int32_t* n_attended, hipStream_t stream) {
+  if (n_tables < 1 || n_tables > FASTAR_MAX_TABLES)
+    return fail(FASTAR_ERR_UNSUPPORTED, "n_tables %d not in [1, %d]", n_tables, FASTAR_MAX_TABLES);
+  if (n_probes < 1 || n_tables * n_probes > FASTAR_MAX_PROBES)
+    return fail(FASTAR_ERR_UNSUPPORTED, "n_tables * n_probes must be in [1, %d]", FASTAR_MAX_PROBES);
+  if (!k_offsets || !k_perm) return fail(FASTAR_ERR_INVALID, "k_offsets and k_perm are required");
+  if (n_tables > 1 && !k_bucket) return fail(FASTAR_ERR_INVALID, "k_bucket is required with several tables");
+  fastar::AttnArgs a;
+  bool empty;
+  fastar_status_t st = attention_check(q, q_bucket, q_perm, n_probes, k, v, key_bias, k_offsets, k_perm, n_bits,
+                                       nullptr, nullptr, scale, out, lse, &a, &empty);
+  if (st != FASTAR_OK || empty) return st;
+  if ((int64_t)n_tables * q->heads * k->tokens >= (int64_t)1 << 31)
+    return fail(FASTAR_ERR_UNSUPPORTED, "n_tables * heads * keys must be < 2^31");
+  a.mode = 3;
+  a.n_tables = n_tables;
+  a.k_bucket = k_bucket;
+  a.n_attended = n_attended;
+  return hip_status(fastar::launch_attention(a, stream), "bucket_attention_tables");
 }
 
 // ---------------------------------------------------------------------------
@@ -589,6 +637,20 @@ fastar_status_t fastar_attention_recall(const float* lse_sparse, const float* ls
                                           n_probes, k_offsets, n_bits, n_retained, n_keys, recall, stats,
                                           stream),
                     "attention_recall");
+}
+
+fastar_status_t fastar_attention_recall_counts(const float* lse_sparse, const float* lse_dense, int heads,
+                                               int64_t n_q, const int32_t* n_attended, const int32_t* n_keys,
+                                               float* recall, float* stats, hipStream_t stream) {
+  if (heads < 0 || n_q < 0) return fail(FASTAR_ERR_INVALID, "negative size");
+  if ((int64_t)heads * n_q >= (int64_t)1 << 31) return fail(FASTAR_ERR_UNSUPPORTED, "heads*n_q must be < 2^31");
+  if (heads == 0) return FASTAR_OK;
+  if (!stats || !n_keys) return fail(FASTAR_ERR_INVALID, "stats and n_keys are required");
+  if (n_q > 0 && (!lse_sparse || !lse_dense || !n_attended))
+    return fail(FASTAR_ERR_INVALID, "lse arrays and n_attended are required");
+  return hip_status(fastar::launch_recall(lse_sparse, lse_dense, heads, n_q, nullptr, 1, nullptr, 0, nullptr,
+                                          n_keys, recall, stats, stream, n_attended),
+                    "attention_recall_counts");
 }
 
 }  // extern "C"

@@ -40,11 +40,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
-// MODE: 0 bucket, 1 key list, 2 dense.  Every head's k and v rows lie within
-// 4 GiB of the head's first row (checked by the caller), so row offsets are
-// 32-bit byte offsets from the head's base.
+// MODE: 0 bucket, 1 key list, 2 dense, 3 tables (several LSH tables and/or
+// more than two probes: P is then the capacity of a row's (table, probe)
+// list, ntab * ppt of it used).  Every head's k and v rows lie within 4 GiB
+// of the head's first row (checked by the caller), so row offsets are 32-bit
+// byte offsets from the head's base.
 template <int D, int P, int MODE>
-__global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
+__global__ __launch_bounds__(256, MODE == 3 ? 2 : 4) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_sh, int64_t q_st, int64_t Nq,
     const int32_t* __restrict__ q_bucket, const int32_t* __restrict__ q_perm,
     const uint16_t* __restrict__ k, int64_t k_sh, int64_t k_st,
@@ -52,7 +54,10 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     const float* __restrict__ key_bias, const int32_t* __restrict__ k_offsets,
     const int32_t* __restrict__ k_perm, int nbits, const int32_t* __restrict__ key_list,
     const int32_t* __restrict__ n_key_list, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int H) {
+    float* __restrict__ lse, int H, const int32_t* __restrict__ k_bucket, int ntab, int ppt,
+    int32_t* __restrict__ n_att) {
+  constexpr bool kList = MODE == 1 || MODE == 2;  // every row's keys are one list
+  constexpr int E = MODE == 3 ? P : 1;            // (table, probe) entries of a row
   constexpr int NC = D / 32;                      // k-chunks of the QK^T contraction
   constexpr int NB = D / 16;                      // 16-dim output blocks
   constexpr int kPieces = D / 8;                  // 16-byte pieces of a row
@@ -67,6 +72,9 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t vtB[32 * D];
   __shared__ __attribute__((aligned(16))) float btA[32];
   __shared__ __attribute__((aligned(16))) float btB[32];
+  // MODE 3: the chunk's keys' buckets in tables 0 .. ntab - 2 (the dedup test)
+  __shared__ __attribute__((aligned(16))) int32_t kdA[MODE == 3 ? 3 * 32 : 4];
+  __shared__ __attribute__((aligned(16))) int32_t kdB[MODE == 3 ? 3 * 32 : 4];
   // logical block (64-row block, head), XCD-grouped
   const int64_t nbx = (Nq + 63) / 64;
   const int64_t lb = xcd_block(blockIdx.x, nbx * H);
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   const int64_t r = R0 + 16 * wave + col;
   const bool rvalid = r < Nq;
   int64_t t = 0;
-  if (rvalid) t = (MODE == 0) ? (int64_t)q_perm[(int64_t)h * Nq + r] : r;
+  if (rvalid) t = (MODE == 0 || MODE == 3) ? (int64_t)q_perm[(int64_t)h * Nq + r] : r;
   // and its row of the workgroup's bucket table: workgroup row l
   int c0 = INT_MAX, c1 = INT_MAX;
   const bool wvalid = R0 + l < Nq;
@@ -92,6 +100,27 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     const int32_t* qb = q_bucket + ((int64_t)h * Nq + tw) * P;
     c0 = qb[0];
     if (P == 2) c1 = qb[1];
+  }
+  // MODE 3: workgroup row l's entries as t << nbits | bucket (ce, INT_MAX
+  // when absent; the pass loop consumes them), each entry's table (te), and
+  // the MFMA row's buckets per entry (rq) for the dedup test: a key counts
+  // in the first table that retains it
+  int ce[E], te[E], rq[E];
+  if (MODE == 3) {
+    int64_t tw = 0;
+    if (wvalid) tw = q_perm[(int64_t)h * Nq + R0 + l];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      te[e] = e / ppt;
+      ce[e] = INT_MAX;
+      rq[e] = -1;
+      if (e < ntab * ppt) {
+        const int64_t row0 = ((int64_t)te[e] * H + h) * Nq;
+        const int pp = e - te[e] * ppt;
+        if (wvalid) ce[e] = (te[e] << nbits) | (q_bucket[(row0 + tw) * ppt + pp] & ((1 << nbits) - 1));
+        if (rvalid) rq[e] = q_bucket[(row0 + t) * ppt + pp];
+      }
+    }
   }
 
   // B operand of S^T = K Q^T: query row `col`, dims 32c + 8g .. +8
@@ -118,6 +147,8 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   const int32_t* idx_h = nullptr;
   if (MODE == 0) idx_h = k_perm + (int64_t)h * Nk;
   if (MODE == 1) idx_h = key_list + (int64_t)h * Nk;
+  if (MODE == 3) idx_h = k_perm;  // positions include the (table, head) row
+  int cnt = 0;                    // MODE 3: the row's attended keys (this lane's share)
 
   // Batches of passes.  With two probes a pass is one distinct bucket of the
   // workgroup's 64 rows (either probe), in ascending order, up to 64 per
@@ -130,6 +161,9 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
   // workgroup.
   while (true) {
     int npass = 0, xs = 0, pkb = 0, pke = 0, pr0 = -1, pr1 = -1;
+    int pr[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) pr[e] = -1;
     if (MODE == 0 && P == 1) {
       // one probe: the rows come in bucket order (rows past the end hold
       // INT_MAX, last), so a pass opens wherever a row's bucket differs from
@@ -157,6 +191,31 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
         const int32_t* off = k_offsets + (int64_t)h * ((1 << nbits) + 1) + xs;
         pkb = off[0];
         pke = off[1];
+      }
+    } else if (MODE == 3) {
+      // a pass per distinct (table, bucket) of the rows' entries, ascending
+      while (npass < FASTAR_WAVE) {
+        int mn = INT_MAX;
+#pragma unroll
+        for (int e = 0; e < E; ++e) mn = min(mn, ce[e]);
+        const int X = wave_min_dpp(mn);
+        if (X == INT_MAX) break;
+        if (l == npass) xs = X;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (ce[e] == X) {
+            ce[e] = INT_MAX;
+            pr[e] = npass;
+          }
+        ++npass;
+      }
+      if (npass == 0) break;
+      if (l < npass) {
+        // positions in the tables' perms [ntab][H][Nk]
+        const int64_t hb = (int64_t)(xs >> nbits) * H + h;
+        const int32_t* off = k_offsets + hb * ((1 << nbits) + 1) + (xs & ((1 << nbits) - 1));
+        pkb = (int)(hb * Nk) + off[0];
+        pke = (int)(hb * Nk) + off[1];
       }
     } else if (MODE == 0) {
       while (npass < FASTAR_WAVE) {
@@ -194,6 +253,9 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     // slot ranges [lo0, lo0 + n0) and, with two probes, [lo1, lo1 + n1)
     int pre = 0, total = 0;
     uint32_t lo0 = 0u, n0 = 0u, lo1 = 0u, n1 = 0u;
+    uint32_t loe[E], ne[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) loe[e] = ne[e] = 0u;
     if (MODE == 0 && P == 1) {
       // a prefix sum over the passes; row l's range is its pass's
       const int incl = (int)wave_incl_scan_dpp((uint32_t)len);
@@ -217,6 +279,14 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
           lo1 = (uint32_t)total;
           n1 = (uint32_t)lp;
         }
+        if (MODE == 3) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (pr[e] == p) {
+              loe[e] = (uint32_t)total;
+              ne[e] = (uint32_t)lp;
+            }
+        }
         total += lp;
       }
     }
@@ -225,10 +295,28 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     const uint32_t rlo0 = (uint32_t)__shfl((int)lo0, src, FASTAR_WAVE);
     const uint32_t rn0 = (uint32_t)__shfl((int)n0, src, FASTAR_WAVE);
     uint32_t rlo1 = 0u, rn1 = 0u;
-    if (P == 2) {
+    if (P == 2 && MODE == 0) {
       rlo1 = (uint32_t)__shfl((int)lo1, src, FASTAR_WAVE);
       rn1 = (uint32_t)__shfl((int)n1, src, FASTAR_WAVE);
     }
+    uint32_t rloe[E], rne[E];
+    if (MODE == 3) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        rloe[e] = (uint32_t)__shfl((int)loe[e], src, FASTAR_WAVE);
+        rne[e] = (uint32_t)__shfl((int)ne[e], src, FASTAR_WAVE);
+      }
+    }
+    // does any of the MFMA row's ranges meet slots [a, a + w)?
+    auto meets = [&](uint32_t a, uint32_t w) {
+      bool u = rn0 > 0u && rlo0 < a + w && rlo0 + rn0 > a;
+      if (P == 2 && MODE == 0) u = u || (rn1 > 0u && rlo1 < a + w && rlo1 + rn1 > a);
+      if (MODE == 3) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) u = u || (rne[e] > 0u && rloe[e] < a + w && rloe[e] + rne[e] > a);
+      }
+      return u;
+    };
     const int kb_pre = pkb - pre;  // slot j of pass p is position j + kb_pre_p
     const bool is_pass = l < npass;
     // keys this lane loads for chunk c: the rows of its 16-byte loads, then
@@ -263,7 +351,7 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
     // chunk c's K, V rows and biases into buffer c & 1; K and V row `row`
     // hold piece p ^ (row % kPieces) at position p, so that lanes reading one
     // piece of 16 different rows hit different banks
-    auto chunk_load = [&](const int* key, uint16_t* kt, uint16_t* vt, float* bt) {
+    auto chunk_load = [&](const int* key, uint16_t* kt, uint16_t* vt, float* bt, int32_t* kd) {
 #pragma unroll
       for (int i = 0; i < kDmaPerWave; ++i) {
         const int row0 = (wave * kDmaPerWave + i) * kDmaRows;
@@ -279,13 +367,19 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       if (bh && l < 8)
         __builtin_amdgcn_global_load_lds((const void*)(bh + key[kDmaPerWave]),
                                          (__attribute__((address_space(3))) void*)(bt + 8 * wave), 4, 0, 0);
+      if (MODE == 3 && l < 8) {
+        for (int tb = 0; tb + 1 < ntab; ++tb)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(k_bucket + ((int64_t)tb * H + h) * Nk + key[kDmaPerWave]),
+              (__attribute__((address_space(3))) void*)(kd + 32 * tb + 8 * wave), 4, 0, 0);
+      }
     };
     const int nch = (total + 31) / 32;
     int key[kDmaPerWave + 1], key1[kDmaPerWave + 1];
     // chunk c, computed from the tiles kt, vt, bt while chunk c + 1 loads
     // into the other buffers (kn, vn, bn)
-    auto chunk = [&](int c, const uint16_t* kt, const uint16_t* vt, const float* bt, uint16_t* kn,
-                     uint16_t* vn, float* bn) {
+    auto chunk = [&](int c, const uint16_t* kt, const uint16_t* vt, const float* bt, const int32_t* kd,
+                     uint16_t* kn, uint16_t* vn, float* bn, int32_t* kdn) {
       if (c == 0) {
         // chunk 0's rows have landed (chunk 1's, requested right behind them
         // while both buffers were free, and chunk 2's keys may still be in
@@ -301,19 +395,17 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
         // every wave is done with chunk c - 1, whose buffers chunk c + 1 takes
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
-        if (c + 1 < nch) chunk_load(key, kn, vn, bn);
+        if (c + 1 < nch) chunk_load(key, kn, vn, bn, kdn);
         if (c + 2 < nch) chunk_keys(c + 2, key);
       }
       const uint32_t kc = (uint32_t)(32 * c);
       // skip a chunk none of the wave's rows uses
-      bool use = rn0 > 0u && rlo0 < kc + 32u && rlo0 + rn0 > kc;
-      if (P == 2) use = use || (rn1 > 0u && rlo1 < kc + 32u && rlo1 + rn1 > kc);
-      if (!ballot64(use)) return;
+      if (!ballot64(meets(kc, 32u))) return;
       // list and dense mode (every row's range is the whole list): a chunk
       // with all its slots inside every row's range needs no per-score masks
       // (in bucket mode the test costs more than it saves)
       bool whole = false;
-      if (MODE != 0) whole = ballot64(!(kc - rlo0 < rn0 && kc + 31u - rlo0 < rn0)) == 0ull;
+      if (kList) whole = ballot64(!(kc - rlo0 < rn0 && kc + 31u - rlo0 < rn0)) == 0ull;
       float s[8];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -321,9 +413,7 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
         // uses gets no scores (in bucket mode the test costs more than the
         // MFMAs it saves; the masks below leave such a half at -inf)
         const uint32_t ka = kc + (uint32_t)(16 * hf);
-        bool uh = rn0 > 0u && rlo0 < ka + 16u && rlo0 + rn0 > ka;
-        if (P == 2) uh = uh || (rn1 > 0u && rlo1 < ka + 16u && rlo1 + rn1 > ka);
-        if (MODE != 0 && !ballot64(uh)) {
+        if (kList && !ballot64(meets(ka, 16u))) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[4 * hf + i] = -INFINITY;
           continue;
@@ -345,6 +435,35 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
         if (whole) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) s[4 * hf + i] = sacc[i] * scale_log2 + bias[i];
+        } else if (MODE == 3) {
+          // the slot's table is its range's; it counts unless an earlier
+          // table already retains the key for this row
+          int kb[3][4];
+#pragma unroll
+          for (int tb = 0; tb < 3; ++tb) {
+            const int4 w4 = tb + 1 < ntab ? *reinterpret_cast<const int4*>(&kd[32 * tb + 16 * hf + 4 * g])
+                                          : make_int4(-1, -1, -1, -1);
+            kb[tb][0] = w4.x;
+            kb[tb][1] = w4.y;
+            kb[tb][2] = w4.z;
+            kb[tb][3] = w4.w;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t j = kc + (uint32_t)(16 * hf + 4 * g + i);
+            int tm = INT_MAX;
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if (j - rloe[e] < rne[e]) tm = min(tm, te[e]);
+            bool keep = tm != INT_MAX;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const int tb = te[e];
+              if (tb < tm && tb < 3) keep = keep && kb[tb][i] != rq[e];
+            }
+            cnt += keep ? 1 : 0;
+            s[4 * hf + i] = keep ? sacc[i] * scale_log2 + bias[i] : -INFINITY;
+          }
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -409,21 +528,26 @@ __global__ __launch_bounds__(256, 4) void attn_bf16_kernel(
       // waiting for them does not wait for those rows
       chunk_keys(0, key);
       if (nch > 1) chunk_keys(1, key1);
-      chunk_load(key, ktA, vtA, btA);
+      chunk_load(key, ktA, vtA, btA, kdA);
       if (nch > 1) {
-        chunk_load(key1, ktB, vtB, btB);
+        chunk_load(key1, ktB, vtB, btB, kdB);
         if (nch > 2) chunk_keys(2, key);
       }
     }
     for (int c = 0; c < nch; c += 2) {
-      chunk(c, ktA, vtA, btA, ktB, vtB, btB);
-      if (c + 1 < nch) chunk(c + 1, ktB, vtB, btB, ktA, vtA, btA);
+      chunk(c, ktA, vtA, btA, kdA, ktB, vtB, btB, kdB);
+      if (c + 1 < nch) chunk(c + 1, ktB, vtB, btB, kdB, ktA, vtA, btA, kdA);
     }
-    if (MODE != 0 || P == 1 || npass < FASTAR_WAVE) break;
+    if (kList || (MODE == 0 && P == 1) || npass < FASTAR_WAVE) break;
     // the next batch refills both buffers: every wave is done with them
     __syncthreads();
   }
   lsum = sum_xor32(sum_xor16(lsum));
+  if (MODE == 3 && n_att) {
+    cnt += __shfl_xor(cnt, 16, FASTAR_WAVE);
+    cnt += __shfl_xor(cnt, 32, FASTAR_WAVE);
+    if (rvalid && g == 0) n_att[(int64_t)h * Nq + t] = cnt;
+  }
   if (!rvalid) return;
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   // acc[b][i] = O[row col][16 b + 4 g + i].  Lanes g and g ^ 1 (l ^ 16, the
@@ -456,11 +580,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
     int64_t v_sh, int64_t v_st, int64_t Nk, const float* __restrict__ key_bias,
     const int32_t* __restrict__ k_offsets, const int32_t* __restrict__ k_perm, int nbits,
     const int32_t* __restrict__ key_list, const int32_t* __restrict__ n_key_list, float scale,
-    float* __restrict__ out, float* __restrict__ lse) {
+    float* __restrict__ out, float* __restrict__ lse, int H, const int32_t* __restrict__ k_bucket, int ntab,
+    int ppt, int32_t* __restrict__ n_att) {
   const int h = blockIdx.y;
   const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= Nq) return;
-  const int64_t t = (MODE == 0) ? (int64_t)q_perm[(int64_t)h * Nq + r] : r;
+  const int64_t t = (MODE == 0 || MODE == 3) ? (int64_t)q_perm[(int64_t)h * Nq + r] : r;
   float qr[D], acc[D];
   const float* qrow = q + (int64_t)h * q_sh + t * q_st;
 #pragma unroll
@@ -472,8 +597,53 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
   const float* kh = k + (int64_t)h * k_sh;
   const float* vh = v + (int64_t)h * v_sh;
   const float* bh = key_bias ? key_bias + (int64_t)h * Nk : nullptr;
+  auto attend = [&](int64_t key) {
+    const float* krow = kh + key * k_st;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = fmaf(qr[d], krow[d], s);
+    s = s * scale + (bh ? bh[key] : 0.f);
+    const float mnew = fmaxf(m, s);
+    const float alpha = expf(m - mnew);
+    const float p = expf(s - mnew);
+    m = mnew;
+    lsum = lsum * alpha + p;
+    const float* vrow = vh + key * v_st;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vrow[d], acc[d] * alpha);
+  };
   int buckets[2] = {0, -1};
   int nseg = 1;
+  if (MODE == 3) {
+    // the row's (table, bucket) entries, each distinct one walked once; a key
+    // counts in the first table that retains it
+    nseg = 0;
+    int cnt = 0;
+    auto probe = [&](int e) {
+      const int tb = e / ppt;
+      return q_bucket[(((int64_t)tb * H + h) * Nq + t) * ppt + (e - tb * ppt)];
+    };
+    const int ne = ntab * ppt;
+    for (int e = 0; e < ne; ++e) {
+      const int tb = e / ppt, b = probe(e);
+      bool dup = false;
+      for (int e2 = tb * ppt; e2 < e; ++e2) dup = dup || probe(e2) == b;
+      if (dup) continue;
+      const int64_t hb = (int64_t)tb * H + h;
+      const int32_t* off = k_offsets + hb * ((1 << nbits) + 1) + (b & ((1 << nbits) - 1));
+      const int32_t* idx = k_perm + hb * Nk;
+      for (int64_t kk = off[0]; kk < off[1]; ++kk) {
+        const int64_t key = idx[kk];
+        bool earlier = false;
+        for (int e2 = 0; e2 < tb * ppt; ++e2)
+          earlier = earlier || k_bucket[((int64_t)(e2 / ppt) * H + h) * Nk + key] == probe(e2);
+        if (earlier) continue;
+        attend(key);
+        ++cnt;
+      }
+    }
+    if (n_att) n_att[(int64_t)h * Nq + t] = cnt;
+  }
   if (MODE == 0) {
     const int32_t* qb = q_bucket + ((int64_t)h * Nq + t) * P;
     buckets[0] = qb[0];
@@ -496,22 +666,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
       kend = nl < 0 ? 0 : (nl < Nk ? nl : Nk);
       if (MODE == 1) idx = key_list + (int64_t)h * Nk;
     }
-    for (int64_t kk = kbeg; kk < kend; ++kk) {
-      const int64_t key = idx ? idx[kk] : kk;
-      const float* krow = kh + key * k_st;
-      float s = 0.f;
-#pragma unroll
-      for (int d = 0; d < D; ++d) s = fmaf(qr[d], krow[d], s);
-      s = s * scale + (bh ? bh[key] : 0.f);
-      const float mnew = fmaxf(m, s);
-      const float alpha = expf(m - mnew);
-      const float p = expf(s - mnew);
-      m = mnew;
-      lsum = lsum * alpha + p;
-      const float* vrow = vh + key * v_st;
-#pragma unroll
-      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vrow[d], acc[d] * alpha);
-    }
+    for (int64_t kk = kbeg; kk < kend; ++kk) attend(idx ? idx[kk] : kk);
   }
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   float* orow = out + ((int64_t)h * Nq + t) * D;
@@ -529,20 +684,23 @@ hipError_t launch3(const AttnArgs& a, hipStream_t s) {
                        (const uint16_t*)a.q, a.q_sh, a.q_st, a.nq, a.q_bucket, a.q_perm,
                        (const uint16_t*)a.k, a.k_sh, a.k_st, (const uint16_t*)a.v, a.v_sh, a.v_st,
                        a.nk, a.key_bias, a.k_offsets, a.k_perm, a.n_bits, a.key_list,
-                       a.n_key_list, a.scale * kLog2e, (uint16_t*)a.out, a.lse, a.heads);
+                       a.n_key_list, a.scale * kLog2e, (uint16_t*)a.out, a.lse, a.heads, a.k_bucket,
+                       a.n_tables, a.n_probes, a.n_attended);
   } else {
     dim3 grid((unsigned)((a.nq + 63) / 64), (unsigned)a.heads);
     hipLaunchKernelGGL((attn_f32_kernel<D, P, MODE>), grid, dim3(64), 0, s,
                        (const float*)a.q, a.q_sh, a.q_st, a.nq, a.q_bucket, a.q_perm,
                        (const float*)a.k, a.k_sh, a.k_st, (const float*)a.v, a.v_sh, a.v_st,
                        a.nk, a.key_bias, a.k_offsets, a.k_perm, a.n_bits, a.key_list,
-                       a.n_key_list, a.scale, (float*)a.out, a.lse);
+                       a.n_key_list, a.scale, (float*)a.out, a.lse, a.heads, a.k_bucket, a.n_tables,
+                       a.n_probes, a.n_attended);
   }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, hipStream_t s) {
+  if (a.mode == 3) return a.n_tables * a.n_probes <= 4 ? launch3<D, 4, 3>(a, s) : launch3<D, 8, 3>(a, s);
   if (a.mode == 0) return a.n_probes == 2 ? launch3<D, 2, 0>(a, s) : launch3<D, 1, 0>(a, s);
   if (a.mode == 1) return launch3<D, 1, 1>(a, s);
   return launch3<D, 1, 2>(a, s);

@@ -21,6 +21,9 @@ constexpr int kWaitVm0 = 0x0F70;
 // blocks, which tend to read the same rows, share an L2.  Logical blocks >= n
 // are empty.
 #define FASTAR_XCDS 8
+
+// probes per LSH table (FASTAR_MAX_PROBES)
+constexpr int kMaxProbes = FASTAR_MAX_PROBES;
 __host__ __device__ __forceinline__ int64_t xcd_span(int64_t n) {
   return (n + FASTAR_XCDS - 1) / FASTAR_XCDS;
 }

@@ -34,11 +34,12 @@ __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(HashJobs jobs, const 
   hash_bf16_body<D>(jobs, planes, nb, diag, blockIdx.x, gridDim.x, lds);
 }
 
-template <int D, int P>
+// PT: 1, 2, or 3 for any P >= 3 (given by P)
+template <int D, int PT>
 __global__ __launch_bounds__(256) void hash_f32_kernel(
     const float* __restrict__ x, int64_t sh, int64_t st, int H, int64_t N,
     const float* __restrict__ planes, int nb, int32_t* __restrict__ bucket,
-    fastar_diag_t* __restrict__ diag) {
+    fastar_diag_t* __restrict__ diag, int P) {
   __shared__ float sp[16][D];
   __shared__ float sxr[4][D];  // per wave: the row being re-evaluated
   __shared__ double ex[4][D + 2];
@@ -101,10 +102,25 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
       const float err = 2.f * kc * xnorm + (nr.d1 + nr.d2) * 0x1p-20f + 0x1p-90f;
       if (nr.d2 - nr.d1 <= err) amb = true;
     }
+    // more probes: rank the row's distances, four planes at a time
+    int rk[16];
+    if (P > 2) {
+      float da[16];
+#pragma unroll
+      for (int p = 0; p < 16; ++p) da[p] = p < nb ? (srn[p] > 0.f ? fabsf(s[p]) / srn[p] : 0.f) : INFINITY;
+#pragma unroll
+      for (int p0 = 0; p0 < 16; p0 += 4)
+        amb = probe_ranks(da + p0, da, p0, nb, P, 2.f * kc * xnorm + 0x1p-90f, rk + p0) || amb;
+    }
     if (valid && !amb) {
       int32_t* o = bucket + idx * P;
       o[0] = (int32_t)bits;
       if (P == 2) o[1] = (int32_t)(bits ^ (1u << nr.j1));
+      if (P > 2) {
+#pragma unroll
+        for (int p = 0; p < 16; ++p)
+          if (p < nb && rk[p] < P - 1) o[1 + rk[p]] = (int32_t)(bits ^ (1u << p));
+      }
     }
     // rows float32 cannot certify: float64 by the whole wave, one at a
     // time, from an LDS copy
@@ -121,13 +137,14 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
   }
 }
 
-template <int D, int P>
+template <int D>
 hipError_t launch_hash_f32(const HashJob& j, const void* planes, int nb, fastar_diag_t* diag,
                            hipStream_t s) {
   const int64_t total = (int64_t)j.H * j.N;
   const int64_t blocks = (total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192;
-  hipLaunchKernelGGL((hash_f32_kernel<D, P>), dim3((unsigned)blocks), dim3(256), 0, s,
-                     (const float*)j.x, j.sh, j.st, j.H, j.N, (const float*)planes, nb, j.bucket, diag);
+  auto kern = j.P == 1 ? hash_f32_kernel<D, 1> : j.P == 2 ? hash_f32_kernel<D, 2> : hash_f32_kernel<D, 3>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, (const float*)j.x, j.sh, j.st, j.H, j.N,
+                     (const float*)planes, nb, j.bucket, diag, j.P);
   return hipGetLastError();
 }
 
@@ -153,11 +170,8 @@ hipError_t launch_hash_multi(HashJobs jobs, int dim, int dtype, const void* plan
   }
   for (int i = 0; i < js.count; ++i) {
     const HashJob& j = js.j[i];
-    hipError_t e;
-    if (dim == 64)
-      e = j.P == 1 ? launch_hash_f32<64, 1>(j, planes, n_bits, diag, s) : launch_hash_f32<64, 2>(j, planes, n_bits, diag, s);
-    else
-      e = j.P == 1 ? launch_hash_f32<128, 1>(j, planes, n_bits, diag, s) : launch_hash_f32<128, 2>(j, planes, n_bits, diag, s);
+    const hipError_t e = dim == 64 ? launch_hash_f32<64>(j, planes, n_bits, diag, s)
+                                   : launch_hash_f32<128>(j, planes, n_bits, diag, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

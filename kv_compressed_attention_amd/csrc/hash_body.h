@@ -125,9 +125,8 @@ __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t
     if (p == src) sg = sx;
   }
   const uint32_t bits = (uint32_t)(ballot64(sg > 0) & 0xFFFFu);
-  int j1 = 0;
   bool unresolved = false;
-  if (P == 2) {
+  if (P >= 2) {
     if (sl == 0) {
       double dist = 0.0, derr = 0.0;
       if (active) {
@@ -138,34 +137,55 @@ __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t
       DE[p] = dist;
       DE[16 + p] = derr;
     }
-    if (lane == 0) {
-      const double* dist = DE;
-      const double* derr = DE + 16;
-      double d1 = dist[0], e1 = derr[0];
-      for (int q = 1; q < nb; ++q) {
-        if (dist[q] < d1) {
-          j1 = q;
-          d1 = dist[q];
-          e1 = derr[q];
-        }
-      }
-      for (int q = 0; q < nb; ++q) {
-        if (q != j1) {
-          const double gap = dist[q] - d1;
-          const double err = derr[q] + e1;
-          if (err > 0.0 && gap <= err) unresolved = true;
-        }
-      }
-    }
   }
   if (lane == 0) {
     o[0] = (int32_t)bits;
-    if (P == 2) o[1] = (int32_t)(bits ^ (1u << j1));
+    // probes 1 .. P - 1: the P - 1 nearest hyperplanes in ascending distance
+    // (ties to the smaller index), each certified apart from every other
+    const double* dist = DE;
+    const double* derr = DE + 16;
+    uint32_t used = 0u;
+    for (int r = 0; r + 1 < P; ++r) {
+      int jb = -1;
+      for (int q = 0; q < nb; ++q)
+        if (!((used >> q) & 1u) && (jb < 0 || dist[q] < dist[jb])) jb = q;
+      used |= 1u << jb;
+      for (int q = 0; q < nb; ++q) {
+        const double err = derr[q] + derr[jb];
+        if (q != jb && err > 0.0 && fabs(dist[q] - dist[jb]) <= err) unresolved = true;
+      }
+      o[r + 1] = (int32_t)(bits ^ (1u << jb));
+    }
     if (diag) {
       atomicAdd(&diag->hash_fallback_rows, 1u);
       if (unresolved) atomicAdd(&diag->unresolved, 1u);
     }
   }
+}
+
+// Ranks of a row's hyperplane distances (ascending, ties to the smaller
+// index) for probes beyond the second: dl[i] is this lane's plane p0 + i
+// distance (INFINITY past nb), da[16] all of the row's.  Returns in rk[i] the
+// rank of plane p0 + i and whether a plane of rank < P - 1 lies within err
+// of another plane (err: the float32 distances' bound, e0 + (d + d') 2^-20).
+__device__ __forceinline__ bool probe_ranks(const float* dl, const float* da, int p0, int nb, int P, float e0,
+                                            int* rk) {
+  bool amb = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int r = 0;
+    bool near = false;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (q < nb && q != p0 + i) {
+        r += (da[q] < dl[i] || (da[q] == dl[i] && q < p0 + i)) ? 1 : 0;
+        near = near || fabsf(da[q] - dl[i]) <= e0 + (da[q] + dl[i]) * 0x1p-20f;
+      }
+    }
+    rk[i] = r;
+    amb = amb || (p0 + i < nb && r < P - 1 && near);
+  }
+  return amb;
 }
 
 // LDS bytes of hash_bf16_body<D>
@@ -343,10 +363,31 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
       const float err = 2.f * kc * xnorm + (nr.d1 + nr.d2) * 0x1p-20f + 0x1p-90f;
       if (nr.d2 - nr.d1 <= err) amb = 1;
     }
+    // more probes: every lane of the row gathers the row's 16 distances and
+    // ranks its own 4 planes
+    int rk[4] = {0, 0, 0, 0};
+    if (P > 2) {
+      float dl[4], da[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dl[i] = (4 * g + i < nb) ? (rnorm[i] > 0.f ? fabsf(acc[i]) / rnorm[i] : 0.f) : INFINITY;
+#pragma unroll
+      for (int g2 = 0; g2 < 4; ++g2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) da[4 * g2 + i] = __shfl(dl[i], 16 * g2 + col, FASTAR_WAVE);
+      const bool a2 = probe_ranks(dl, da, 4 * g, nb, P, 2.f * kc * xnorm + 0x1p-90f, rk);
+      amb = (int)or_xor32(or_xor16((uint32_t)(amb | (a2 ? 1 : 0))));
+    }
     if (valid && g == 0 && !amb) {
       int32_t* o = w.bucket + ((int64_t)w.h * w.N + row) * P;
       o[0] = (int32_t)bits;
       if (P == 2) o[1] = (int32_t)(bits ^ (1u << nr.j1));
+    }
+    if (P > 2 && valid && !amb) {
+      int32_t* o = w.bucket + ((int64_t)w.h * w.N + row) * P;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * g + i < nb && rk[i] < P - 1) o[1 + rk[i]] = (int32_t)(bits ^ (1u << (4 * g + i)));
     }
     // rows float32 cannot certify: float64 by the whole wave, one at a
     // time, from an LDS copy

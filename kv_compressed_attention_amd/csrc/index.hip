@@ -187,9 +187,9 @@ __device__ __forceinline__ void write_offsets(int32_t* off, int nbk, int64_t nh,
   }
 }
 
-template <int P>
+// P: the ids' row stride (probes per item); the first probe is the key
 __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
-    const int32_t* __restrict__ bucket, int64_t n, int nbits, const int32_t* __restrict__ n_valid,
+    const int32_t* __restrict__ bucket, int P, int64_t n, int nbits, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ ws,
     int use_lds) {
   extern __shared__ int32_t lds[];  // kLdsItems x (key, key, u16 val, u16 val)
@@ -350,12 +350,8 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
   // LDS staging whenever a head can fit (n, or a device count, at most kLdsItems)
   const int use_lds = (n <= kLdsItems || n_valid) ? 1 : 0;
   const size_t lds = use_lds ? (size_t)kLdsItems * 12 : 0;
-  if (n_probes == 2)
-    hipLaunchKernelGGL(bucket_index_kernel<2>, dim3(heads), dim3(kThreads), lds, s, bucket, n,
-                       n_bits, n_valid, offsets, perm, ws, use_lds);
-  else
-    hipLaunchKernelGGL(bucket_index_kernel<1>, dim3(heads), dim3(kThreads), lds, s, bucket, n,
-                       n_bits, n_valid, offsets, perm, ws, use_lds);
+  hipLaunchKernelGGL(bucket_index_kernel, dim3(heads), dim3(kThreads), lds, s, bucket, n_probes, n, n_bits,
+                     n_valid, offsets, perm, ws, use_lds);
   return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ inline int direct_index_parts(int64_t n) {
 // whether the direct pass covers n items of n_bits bits with counters of the
 // given width
 inline bool direct_index_fits_wide(int64_t n, int n_probes, int n_bits, bool wide) {
-  if (n_probes < 1 || n_probes > 2 || n_bits < kDirectMinBits || n_bits > kDirectMaxBits) return false;
+  if (n_probes < 1 || n_probes > kMaxProbes || n_bits < kDirectMinBits || n_bits > kDirectMaxBits) return false;
   if (n >= ((int64_t)1 << 31) || (!wide && direct_index_wide(n))) return false;
   return direct_shape(n_bits, wide, direct_index_parts(n)).sw >= 1;
 }

@@ -56,7 +56,7 @@ bool direct_index_supported(int64_t n, int n_probes, int n_bits, int64_t n_extra
 // prune.hip -----------------------------------------------------------------
 hipError_t launch_prune(const int32_t* q_bucket, int heads, int64_t n_q, int n_probes,
                         const int32_t* p_bucket, int64_t n_prompt, int n_bits, uint8_t* keep,
-                        int32_t* kept_idx, int32_t* n_kept, hipStream_t s);
+                        int32_t* kept_idx, int32_t* n_kept, hipStream_t s, int n_tables = 1);
 
 // attention.hip -------------------------------------------------------------
 struct AttnArgs {
@@ -67,7 +67,13 @@ struct AttnArgs {
   const float* key_bias; const int32_t* k_offsets; const int32_t* k_perm; int n_bits;
   const int32_t* key_list; const int32_t* n_key_list;
   float scale; void* out; float* lse;
-  int heads, dim, dtype, mode;  // mode: 0 bucket, 1 list, 2 dense
+  int heads, dim, dtype, mode;  // mode: 0 bucket, 1 list, 2 dense, 3 tables
+  // mode 3: n_tables LSH tables of n_probes probes each; q_bucket
+  // [n_tables][H][nq][n_probes], k_offsets / k_perm / k_bucket per table
+  // ([n_tables][H][...]), n_attended [H][nq] out or NULL
+  int n_tables = 1;
+  const int32_t* k_bucket = nullptr;
+  int32_t* n_attended = nullptr;
 };
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
@@ -75,7 +81,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 hipError_t launch_recall(const float* lse_s, const float* lse_d, int heads, int64_t nq,
                          const int32_t* q_bucket, int P, const int32_t* k_offsets, int nbits,
                          const int32_t* n_retained, const int32_t* n_keys, float* recall, float* stats,
-                         hipStream_t s);
+                         hipStream_t s, const int32_t* n_per_query = nullptr);
 
 // tempcache.hip -------------------------------------------------------------
 struct MergeWs {

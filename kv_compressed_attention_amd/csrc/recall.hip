@@ -19,6 +19,7 @@ __global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ l
                                                      const int32_t* __restrict__ q_bucket, int P,
                                                      const int32_t* __restrict__ k_offsets, int nbits,
                                                      const int32_t* __restrict__ n_retained,
+                                                     const int32_t* __restrict__ n_per_query,
                                                      const int32_t* __restrict__ n_keys,
                                                      float* __restrict__ recall, float* __restrict__ stats) {
   __shared__ double red[2][256];
@@ -31,12 +32,17 @@ __global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ l
     const float a = lse_s[r], b = lse_d[r];
     const float rc = (a == -INFINITY || b == -INFINITY) ? 0.f : expf(a - b);
     if (recall) recall[r] = rc;
-    int cnt;
-    if (off) {
+    int cnt = 0;
+    if (n_per_query) {
+      cnt = n_per_query[r];
+    } else if (off) {
+      // the keys of the query's distinct probe buckets
       const int32_t* qb = q_bucket + r * P;
-      const int b0 = qb[0];
-      cnt = off[b0 + 1] - off[b0];
-      if (P == 2 && qb[1] != b0) cnt += off[qb[1] + 1] - off[qb[1]];
+      for (int p = 0; p < P; ++p) {
+        bool dup = false;
+        for (int p2 = 0; p2 < p; ++p2) dup = dup || qb[p2] == qb[p];
+        if (!dup) cnt += off[qb[p] + 1] - off[qb[p]];
+      }
     } else {
       cnt = n_retained[h];
     }
@@ -64,9 +70,9 @@ __global__ __launch_bounds__(256) void recall_kernel(const float* __restrict__ l
 hipError_t launch_recall(const float* lse_s, const float* lse_d, int heads, int64_t nq,
                          const int32_t* q_bucket, int P, const int32_t* k_offsets, int nbits,
                          const int32_t* n_retained, const int32_t* n_keys, float* recall, float* stats,
-                         hipStream_t s) {
+                         hipStream_t s, const int32_t* n_per_query) {
   hipLaunchKernelGGL(recall_kernel, dim3(heads), dim3(256), 0, s, lse_s, lse_d, nq, q_bucket, P, k_offsets,
-                     nbits, n_retained, n_keys, recall, stats);
+                     nbits, n_retained, n_per_query, n_keys, recall, stats);
   return hipGetLastError();
 }
 

@@ -127,13 +127,19 @@ _SIGNATURES = {
     "fastar_prune_prompt": (_I, [_P, _I, _I64, _I, _P, _I64, _I, _P, _P, _P, _P]),
     "fastar_bucket_attention": (_I, [_TP, _P, _P, _I, _TP, _TP, _P, _P, _P, _I, _P, _P, _F, _P, _P, _P]),
     "fastar_attention_recall": (_I, [_P, _P, _I, _I64, _P, _I, _P, _I, _P, _P, _P, _P, _P]),
+    "fastar_bucket_attention_tables": (_I, [_TP, _I, _P, _P, _I, _TP, _TP, _P, _P, _P, _P, _I, _F, _P, _P,
+                                            _P, _P]),
+    "fastar_prune_prompt_tables": (_I, [_P, _I, _I, _I64, _I, _P, _I64, _I, _P, _P, _P, _P]),
+    "fastar_attention_recall_counts": (_I, [_P, _P, _I, _I64, _P, _P, _P, _P, _P]),
     "fastar_chunk_workspace": (_SZ, [_P]),
     "fastar_chunk": (_I, [_P, _P, _SZ, _P, _P]),
     "fastar_chunk_noalloc": (_I, [_P, _P, _P]),
 }
 
-# FASTAR_NOALLOC_SCRATCH_BYTES in include/fastar.h
+# FASTAR_NOALLOC_SCRATCH_BYTES, FASTAR_MAX_PROBES, FASTAR_MAX_TABLES in include/fastar.h
 NOALLOC_SCRATCH_BYTES = 48 << 20
+MAX_PROBES = 8
+MAX_TABLES = 4
 
 
 def library():
@@ -393,6 +399,68 @@ def fastar_bucket_attention(q, k, v, scale: Optional[float] = None, q_bucket=Non
                                        _ptr(n_key_list), float(scale), _ptr(out), _ptr(lse),
                                        _stream(stream)))
     return out, lse
+
+
+def fastar_bucket_attention_tables(q, k, v, q_bucket, q_perm, k_offsets, k_perm, n_bits: int,
+                                   k_bucket=None, scale: Optional[float] = None, key_bias=None,
+                                   out=None, lse=None, n_attended=None, want_lse: bool = True,
+                                   want_count: bool = False, stream=None):
+    """AnnSA over several LSH tables (q_bucket [L, H, nq, P], k_offsets
+    [L, H, 2^b + 1], k_perm and k_bucket [L, H, nk]); returns (out, lse,
+    n_attended)."""
+    lib = library()
+    H, nq, d = q.shape
+    L, P = q_bucket.shape[0], q_bucket.shape[3]
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty(H, nq, d, dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty(H, nq, dtype=torch.float32, device=q.device)
+    if n_attended is None and want_count:
+        n_attended = _i32((H, nq), q.device)
+    dq, dk, dv = _desc(q), _desc(k), _desc(v)
+    _check(lib.fastar_bucket_attention_tables(ctypes.byref(dq), L, _ptr(q_bucket), _ptr(q_perm), P,
+                                              ctypes.byref(dk), ctypes.byref(dv), _ptr(key_bias),
+                                              _ptr(k_bucket), _ptr(k_offsets), _ptr(k_perm), n_bits,
+                                              float(scale), _ptr(out), _ptr(lse), _ptr(n_attended),
+                                              _stream(stream)))
+    return out, lse, n_attended
+
+
+def fastar_prune_prompt_tables(q_bucket, p_bucket, n_bits: int, keep=None, kept_idx=None, n_kept=None,
+                               stream=None):
+    """AnnCA over several LSH tables: q_bucket [L, H, nq, P], p_bucket
+    [L, H, Np]; returns keep [H, Np], kept indices [H, Np], counts [H]."""
+    lib = library()
+    L, H, nq, P = q_bucket.shape
+    npr = p_bucket.shape[2]
+    dev = q_bucket.device
+    if keep is None:
+        keep = torch.empty(H, npr, dtype=torch.uint8, device=dev)
+    if kept_idx is None:
+        kept_idx = _i32((H, npr), dev)
+    if n_kept is None:
+        n_kept = _i32((H,), dev)
+    _check(lib.fastar_prune_prompt_tables(_ptr(q_bucket), L, H, nq, P, _ptr(p_bucket), npr, n_bits,
+                                          _ptr(keep), _ptr(kept_idx), _ptr(n_kept), _stream(stream)))
+    return keep, kept_idx, n_kept
+
+
+def fastar_attention_recall_counts(lse_sparse, lse_dense, n_keys, n_attended, recall=None, stats=None,
+                                   want_recall: bool = True, stream=None):
+    """fastar_attention_recall with the retained counts given per query
+    (n_attended [H, n_q])."""
+    lib = library()
+    H, nq = lse_sparse.shape
+    dev = lse_sparse.device
+    if recall is None and want_recall:
+        recall = torch.empty(H, nq, dtype=torch.float32, device=dev)
+    if stats is None:
+        stats = torch.empty(H, 2, dtype=torch.float32, device=dev)
+    _check(lib.fastar_attention_recall_counts(_ptr(lse_sparse), _ptr(lse_dense), H, nq, _ptr(n_attended),
+                                              _ptr(n_keys), _ptr(recall), _ptr(stats), _stream(stream)))
+    return recall, stats
 
 
 def fastar_attention_recall(lse_sparse, lse_dense, n_keys, q_bucket=None, k_offsets=None,

@@ -87,8 +87,10 @@ def test_hash_rejects_bad_arguments_without_launching(lib):
         (_tensor(dtype=7), 12, 1, 2),           # dtype
         (_tensor(dim=96), 12, 1, 2),            # head dim
         (_tensor(), 16, 1, 2),                  # n_bits > 15
-        (_tensor(), 12, 3, 2),                  # n_probes
+        (_tensor(), 12, 9, 2),                  # n_probes > FASTAR_MAX_PROBES
+        (_tensor(), 12, 0, 2),                  # n_probes < 1
         (_tensor(), 0, 2, 1),                   # two probes need a bit
+        (_tensor(), 3, 5, 1),                   # five probes need four bits
         (_tensor(data=(1 << 20) + 2), 12, 1, 1),  # misaligned data
     ]
     for t, bits, probes, want in cases:
@@ -121,7 +123,7 @@ def test_hash_multi_rejects_bad_arguments_without_launching(lib):
     assert call([a, b, a, b, a], [1] * 5) == 1           # count > 4
     assert call([a, _tensor(dim=64)], [1, 1]) == 1       # dims differ
     assert call([a, _tensor(dtype=0)], [1, 1]) == 1      # dtypes differ
-    assert call([a, b], [1, 3]) == 2                     # n_probes
+    assert call([a, b], [1, 9]) == 2                     # n_probes
     assert call([a, b], [1, 1], bits=16) == 2            # n_bits
 
 
@@ -147,7 +149,7 @@ def test_chunk_rejects_bad_arguments_without_launching(lib):
     assert lib.fastar_chunk(None, None, 0, None, None) == 1
     assert call(args(cache=None)) == 1                       # no cache
     assert call(args(n_frames=2)) == 1                       # k_new holds 3 frames
-    assert call(args(n_probes=3)) == 2                       # probes
+    assert call(args(n_probes=9)) == 2                       # probes
     assert call(args(n_bits=10)) == 1                        # differs from the cache's
     assert call(args(tau=float("inf"))) == 1                 # tau
     assert call(args(scale=float("nan"))) == 1               # scale
@@ -249,7 +251,7 @@ def test_recall_rejects_bad_arguments_without_launching(lib):
     assert lib.fastar_attention_recall(buf, buf, 2, 10, buf, 1, buf, 4, None, buf, None, None, None) == 1
     assert lib.fastar_attention_recall(buf, buf, 2, 10, buf, 1, buf, 4, buf, buf, None, buf, None) == 1
     assert lib.fastar_attention_recall(buf, buf, 2, 10, None, 1, None, 4, None, buf, None, buf, None) == 1
-    assert lib.fastar_attention_recall(buf, buf, 2, 10, buf, 3, buf, 4, None, buf, None, buf, None) == 2
+    assert lib.fastar_attention_recall(buf, buf, 2, 10, buf, 9, buf, 4, None, buf, None, buf, None) == 2
     assert lib.fastar_attention_recall(None, buf, 2, 10, None, 1, None, 0, buf, buf, None, buf, None) == 1
     assert lib.fastar_attention_recall(None, None, 0, 10, None, 1, None, 0, None, None, None, None, None) == 0
 
@@ -278,3 +280,23 @@ def test_merge_options_rejected_without_launching(lib):
         lib.fastar_tempcache_workspace(ctypes.byref(c), 1)
     assert lib.fastar_scalar_codes(ctypes.byref(k), 1, ctypes.c_void_p(buf), ctypes.c_void_p(buf), None) == 2
     assert lib.fastar_scalar_codes(ctypes.byref(k), 8, None, ctypes.c_void_p(buf), None) == 1
+
+
+def test_tables_calls_reject_bad_arguments_without_launching(lib):
+    buf = ctypes.c_void_p(1 << 20)
+    q, k = _tensor(), _tensor(tokens=32)
+
+    def attn(n_tables, probes, k_bucket=buf, bits=6):
+        return lib.fastar_bucket_attention_tables(ctypes.byref(q), n_tables, buf, buf, probes, ctypes.byref(k),
+                                                  ctypes.byref(k), None, k_bucket, buf, buf, bits, 0.1, buf,
+                                                  None, None, None)
+    assert attn(0, 1) == 2 and attn(5, 1) == 2           # tables outside [1, FASTAR_MAX_TABLES]
+    assert attn(3, 3) == 2                               # 9 (table, probe) entries
+    assert attn(2, 2, k_bucket=None) == 1                # several tables need the keys' buckets
+    assert attn(1, 4, bits=2) == 1                       # four probes need three bits
+
+    def prune(n_tables, probes=1):
+        return lib.fastar_prune_prompt_tables(buf, n_tables, 2, 16, probes, buf, 32, 6, buf, buf, buf, None)
+    assert prune(0) == 2 and prune(5) == 2 and prune(2, 9) == 2
+    assert lib.fastar_attention_recall_counts(buf, buf, 2, 16, None, buf, None, buf, None) == 1
+    assert lib.fastar_attention_recall_counts(buf, buf, 2, 16, buf, None, None, buf, None) == 1
