@@ -177,3 +177,42 @@ def test_multi_table_collision_rate():
     p = 1 - (1 - (1 - theta / math.pi) ** b) ** L
     sd = math.sqrt(p * (1 - p) / trials)
     assert abs(hits / trials - p) < 5 * sd
+
+
+def test_sequence_with_repeated_tables_is_the_single_table_sequence():
+    # further tables with table 0's planes retain exactly table 0's keys
+    from dataclasses import replace
+    from oracle import run_chunk
+    from synth import make_workload
+    w = make_workload(0)
+    one = run_chunk(w)[0]
+    rep = run_chunk(w, extra_planes=np.stack([w.planes, w.planes]))[0]
+    assert np.array_equal(rep["group_of_new"], one["group_of_new"])
+    assert np.allclose(rep["o_self"], one["o_self"], rtol=0, atol=1e-12)
+    assert np.array_equal(rep["kept_idx"], one["kept_idx"])
+    # and a second table that retains more can only add keys
+    w2 = replace(w, n_probes=1)
+    other = np.random.default_rng(5).standard_normal(w.planes.shape)
+    more = run_chunk(w2, extra_planes=other[None])[0]
+    single = np.array([np.isin(one["cache"].rep_bucket, row).sum() for row in one["q_ids"]])
+    assert np.all(more["n_attended"] >= single)
+    assert set(one["kept_idx"].tolist()) <= set(more["kept_idx"].tolist())
+
+
+def test_sequence_dense_warmup_is_the_one_bucket_sequence():
+    # with no hyperplanes every key shares the one bucket: sparse = dense
+    from dataclasses import replace
+    from oracle import run_chunk
+    from synth import make_workload
+    w = make_workload(0)
+    w0 = replace(w, n_bits=0, planes=w.planes[:0])
+    sparse = run_chunk(w0)[0]
+    dense = run_chunk(w, sparse=False)[0]
+    dense0 = run_chunk(w0, sparse=False)[0]
+    assert np.allclose(sparse["o_self"], dense0["o_self"], rtol=0, atol=1e-12)
+    assert np.allclose(sparse["o_cross"], dense0["o_cross"], rtol=0, atol=1e-12)
+    # the warm-up keeps the sparse run's merge (the cache does not depend on
+    # whether attention is sparse), and attends to every group and prompt token
+    ref = run_chunk(w)[0]
+    assert np.array_equal(dense["group_of_new"], ref["group_of_new"])
+    assert dense["kept_idx"].size == w.prompt_k.shape[1]
