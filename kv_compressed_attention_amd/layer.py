@@ -35,7 +35,8 @@ class FastARLayer:
     def __init__(self, heads: int, dim: int, n_bits: int, n_probes: int, tau: float,
                  tokens_per_frame: int, capacity: int, n_queries: int, chunk_frames: int,
                  n_prompt: int = 0, dtype=torch.bfloat16, device="cuda", match: str = "lsh",
-                 code_bits: int = 8, query_driven: bool = False, representative: str = "last"):
+                 code_bits: int = 8, query_driven: bool = False, representative: str = "last",
+                 n_tables: int = 1):
         self.heads, self.dim, self.n_bits, self.n_probes = heads, dim, n_bits, n_probes
         self.tau, self.T, self.capacity = tau, tokens_per_frame, capacity
         self.nq, self.chunk_frames, self.n_prompt = n_queries, chunk_frames, n_prompt
@@ -51,7 +52,11 @@ class FastARLayer:
         i32 = dict(dtype=torch.int32, device=dev)
         self.cache = fb.TempCache(H, dim, capacity, tokens_per_frame, n_bits, dtype, dev,
                                   key_sums=representative != "last")
-        self.planes = torch.zeros(max(n_bits, 1), dim, dtype=dtype, device=dev)
+        # several LSH tables: planes [n_tables, n_bits, dim]; table 0's also
+        # drive TempCache's match and the fused chunk
+        self.n_tables = n_tables
+        self.planes_t = torch.zeros(n_tables, max(n_bits, 1), dim, dtype=dtype, device=dev)
+        self.planes = self.planes_t[0]
         nk = chunk_frames * tokens_per_frame
         lib = fb.library()
         size_opts = self.opts
@@ -67,7 +72,9 @@ class FastARLayer:
                        # fastar_chunk: the merge's, then (at most) the queries' index scratch
                        self.cache.workspace_bytes(chunk_frames, size_opts) +
                        lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
-                       self.cache.workspace_bytes(1, self.opts))
+                       self.cache.workspace_bytes(1, self.opts),
+                       # several tables: the representatives' index per table
+                       lib.fastar_hash_workspace(H, capacity, n_bits, 1))
         self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         # the query-side stream has a workspace of its own
         ws_q = max(lib.fastar_hash_workspace(H, n_queries, n_bits, n_probes),
@@ -90,12 +97,22 @@ class FastARLayer:
             self.n_kept = torch.empty(H, **i32)
             self.o_cross = torch.empty(H, n_queries, dim, dtype=dtype, device=dev)
             self.lse_cross = torch.empty(H, n_queries, dtype=torch.float32, device=dev)
+        if n_tables > 1:
+            L = n_tables
+            self.q_ids_t = torch.empty(L, H, n_queries, n_probes, **i32)
+            self.rep_ids_t = torch.empty(L, H, capacity, **i32)
+            self.rep_off_t = torch.empty(L, H, (1 << n_bits) + 1, **i32)
+            self.rep_perm_t = torch.empty(L, H, capacity, **i32)
+            self.n_attended = torch.empty(H, n_queries, **i32)
+            if n_prompt:
+                self.p_ids_t = torch.empty(L, H, n_prompt, 1, **i32)
         self.diag = fb.new_diag(dev)
         self._calls = {}
 
     def set_planes(self, planes: torch.Tensor):
+        """planes [n_bits, dim] (one table) or [n_tables, n_bits, dim]."""
         if self.n_bits:
-            self.planes.copy_(planes)
+            self.planes_t.copy_(planes.view(self.n_tables, self.n_bits, self.dim))
 
     # -- building blocks ----------------------------------------------------
     def hash_keys(self, k: torch.Tensor, out: Optional[torch.Tensor] = None):
@@ -209,6 +226,9 @@ class FastARLayer:
         ``timing`` (optional dict) receives (start, end) event pairs per
         stage, recorded on the stream each stage runs on."""
         cache = self.cache if cache is None else cache
+        if self.n_tables > 1:
+            self._step_tables(q, k_new, v_new, prompt_k, prompt_v, cache, timing)
+            return
         if concurrent == "chunk":
             call = self._chunk_call(q, k_new, v_new, prompt_k, prompt_v, cache)
             self._timed(timing, "chunk", lambda: call(self.ws, diag=self.diag))
@@ -259,6 +279,73 @@ class FastARLayer:
         main.wait_event(q_done)
         self.self_attention(q, timing, cache)
         main.wait_event(side_done)
+
+    def _step_tables(self, q, k_new, v_new, prompt_k, prompt_v, cache, timing):
+        """One chunk with several LSH tables, call by call on the caller's
+        stream: the chunk's queries and prompt keys hashed with every table's
+        planes, the new keys with table 0's (TempCache's match); the merge and
+        table 0's index of the representatives; tables 1.. hash the
+        representatives themselves and index them (the groups in use); AnnSA
+        over the union of the tables' buckets; AnnCA keeps a prompt token any
+        table keeps."""
+        L, H = self.n_tables, self.heads
+
+        def hashes():
+            for u in range(L):
+                xs, probes, outs = [q], [self.n_probes], [self.q_ids_t[u]]
+                if u == 0:
+                    xs.append(k_new)
+                    probes.append(1)
+                    outs.append(self.k_ids)
+                if prompt_k is not None:
+                    xs.append(prompt_k)
+                    probes.append(1)
+                    outs.append(self.p_ids_t[u])
+                fb.fastar_hash_multi(xs, self.planes_t[u], self.n_bits, probes, buckets=outs,
+                                     diag=self.diag)
+            fb.fastar_bucket_index(self.q_ids_t[0], self.n_bits, offsets=self.q_off, perm=self.q_perm,
+                                   ws=self.ws_q)
+        self._timed(timing, "hash", hashes)
+        self._merge(cache, k_new, v_new, timing, q)
+
+        def rep_index():
+            self.rep_ids_t[0].copy_(cache.rep_bucket)
+            self.rep_off_t[0].copy_(self.rep_off)
+            self.rep_perm_t[0].copy_(self.rep_perm)
+            for u in range(1, L):
+                fb.fastar_hash(cache.rep_k, self.planes_t[u], self.n_bits, 1, with_index=False,
+                               bucket=self.rep_ids_t[u].view(H, -1, 1), diag=self.diag)
+                fb.fastar_bucket_index(self.rep_ids_t[u].view(H, -1, 1), self.n_bits,
+                                       n_valid=cache.n_groups, offsets=self.rep_off_t[u],
+                                       perm=self.rep_perm_t[u], ws=self.ws)
+        self._timed(timing, "rep_index", rep_index)
+        self._timed(timing, "attention", lambda: fb.fastar_bucket_attention_tables(
+            q, cache.rep_k, cache.v_mean, self.q_ids_t, self.q_perm, self.rep_off_t, self.rep_perm_t,
+            self.n_bits, k_bucket=self.rep_ids_t, key_bias=cache.log_count, out=self.o_self,
+            lse=self.lse_self, n_attended=self.n_attended))
+        if prompt_k is not None:
+            def cross():
+                fb.fastar_prune_prompt_tables(self.q_ids_t, self.p_ids_t.view(L, H, -1), self.n_bits,
+                                              keep=self.keep, kept_idx=self.kept_idx, n_kept=self.n_kept)
+                fb.fastar_bucket_attention(q, prompt_k, prompt_v, key_list=self.kept_idx,
+                                           n_key_list=self.n_kept, out=self.o_cross, lse=self.lse_cross)
+            self._timed(timing, "cross", cross)
+
+    def step_dense(self, q, k_new, v_new, prompt_k=None, prompt_v=None, cache=None, timing=None):
+        """One chunk with the sparse attention switched off (the denoising
+        warm-up): the same merge, then dense self-attention over every group of
+        the compressed cache (with the + ln m bias) and dense cross-attention
+        over the whole prompt."""
+        cache = self.cache if cache is None else cache
+        self._timed(timing, "hash_k", lambda: fb.fastar_hash(
+            k_new, self.planes, self.n_bits, 1, with_index=False, bucket=self.k_ids, diag=self.diag))
+        self._merge(cache, k_new, v_new, timing, q)
+        self._timed(timing, "attention", lambda: fb.fastar_bucket_attention(
+            q, cache.rep_k, cache.v_mean, key_bias=cache.log_count, n_key_list=cache.n_groups,
+            out=self.o_self, lse=self.lse_self))
+        if prompt_k is not None:
+            self._timed(timing, "cross", lambda: fb.fastar_bucket_attention(
+                q, prompt_k, prompt_v, out=self.o_cross, lse=self.lse_cross))
 
     def capture(self, q, k_new, v_new, prompt_k=None, prompt_v=None, cache=None,
                 concurrent="chunk", caches=None):
