@@ -629,6 +629,143 @@ def tau_sweep(w, dev, taus, match="lsh", representative="last"):
     return out
 
 
+def lsh_tables_sweep(w, dev, configs, reps=5):
+    """Several LSH tables and more probes per table for AnnSA and AnnCA
+    (paperlayer.ai section 2: LSH probes buckets in several tables) on
+    workload w: per (tables, probes per table) the chunk time (cold: a 512 MB
+    write before each of reps chunks, each merging into its own copy of the
+    pre-chunk cache; median), the self-attention launch alone (hot, median of
+    reps), and AnnSA's mean recall and density against dense attention over
+    the compressed cache.  Table 0 is the workload's planes; further tables
+    draw their own."""
+    from dataclasses import replace
+    import kv_compressed_attention_amd.fastar as fb
+    from kv_compressed_attention_amd.layer import FastARLayer
+
+    H, F, T, d = w.k_frames.shape
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    npr = 0 if w.prompt_k is None else w.prompt_k.shape[1]
+
+    def up(a):
+        return torch.tensor(np.ascontiguousarray(a), dtype=torch.float32, device=dev).to(tdt)
+    q = up(w.q)
+    k_new, v_new = (up(a) for a in w.frames(w.setup_frames, F))
+    pk = up(w.prompt_k) if npr else None
+    pv = up(w.prompt_v) if npr else None
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    out = []
+    for L, P in configs:
+        if P > w.n_bits + 1:
+            continue
+        extra = np.random.default_rng(900 + L).standard_normal((max(L - 1, 0), w.n_bits, d))
+        planes = np.concatenate([w.planes[None], extra]) if L > 1 else w.planes[None]
+        layer = FastARLayer(H, d, w.n_bits, P, w.tau, T, F * T, w.n_queries, w.chunk_frames, n_prompt=npr,
+                            dtype=tdt, device=dev, n_tables=L)
+        layer.set_planes(up(planes))
+        for f in range(w.setup_frames):
+            layer.merge(up(w.k_frames[:, f]), up(w.v_frames[:, f]), 1, with_index=False)
+        pristine = layer.cache
+        work = fb.TempCache(H, d, F * T, T, w.n_bits, tdt, dev)
+        work.copy_from(pristine)
+        layer.step(q, k_new, v_new, pk, pv, cache=work)   # first use: set-up outside the timing
+        ms = []
+        for _ in range(reps):
+            work.copy_from(pristine)
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            layer.step(q, k_new, v_new, pk, pv, cache=work)
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        c = work
+        if L > 1:
+            def attn():
+                fb.fastar_bucket_attention_tables(
+                    q, c.rep_k, c.v_mean, layer.q_ids_t, layer.q_perm, layer.rep_off_t, layer.rep_perm_t,
+                    w.n_bits, k_bucket=layer.rep_ids_t, key_bias=c.log_count, out=layer.o_self,
+                    lse=layer.lse_self, n_attended=layer.n_attended)
+        else:
+            def attn():
+                fb.fastar_bucket_attention(q, c.rep_k, c.v_mean, q_bucket=layer.q_ids, q_perm=layer.q_perm,
+                                           key_bias=c.log_count, k_offsets=layer.rep_off,
+                                           k_perm=layer.rep_perm, n_bits=w.n_bits, out=layer.o_self,
+                                           lse=layer.lse_self)
+        at = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            attn()
+            e1.record()
+            torch.cuda.synchronize()
+            at.append(e0.elapsed_time(e1))
+        _, lse_d = fb.fastar_bucket_attention(q, c.rep_k, c.v_mean, key_bias=c.log_count, n_key_list=c.n_groups)
+        if L > 1:
+            _, st = fb.fastar_attention_recall_counts(layer.lse_self, lse_d, c.n_groups, layer.n_attended,
+                                                      want_recall=False)
+        else:
+            _, st = fb.fastar_attention_recall(layer.lse_self, lse_d, c.n_groups, q_bucket=layer.q_ids,
+                                               k_offsets=layer.rep_off, n_bits=w.n_bits, want_recall=False)
+        st = st.cpu().numpy()
+        row = {"tables": L, "probes_per_table": P, "chunk_ms": float(np.median(ms)),
+               "attention_ms": float(np.median(at)), "annsa_recall": float(st[:, 0].mean()),
+               "annsa_density": float(st[:, 1].mean())}
+        if npr:
+            row["annca_kept_frac"] = float(layer.n_kept.float().mean().item()) / npr
+        out.append(row)
+        del layer, work
+        torch.cuda.empty_cache()
+    return out
+
+
+def denoise_loop(w, dev, n_steps=10, warmup=0.3, reps=3):
+    """One chunk's denoising loop around the layer (paper.rainbus.top,
+    limitations: the sparse attention is off in the first 30% of the steps):
+    the loop's time with that warm-up, with every step sparse and with every
+    step dense (the same merge per step, dense attention over every group and
+    the whole prompt).  Hot inputs (each step reuses the chunk's tensors);
+    median over reps loops."""
+    from kv_compressed_attention_amd.denoise import DenoisingDriver, warmup_steps
+    from kv_compressed_attention_amd.layer import FastARLayer
+
+    H, F, T, d = w.k_frames.shape
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    npr = 0 if w.prompt_k is None else w.prompt_k.shape[1]
+
+    def up(a):
+        return torch.tensor(np.ascontiguousarray(a), dtype=torch.float32, device=dev).to(tdt)
+    q = up(w.q)
+    k_new, v_new = (up(a) for a in w.frames(w.setup_frames, F))
+    pk = up(w.prompt_k) if npr else None
+    pv = up(w.prompt_v) if npr else None
+    layer = FastARLayer(H, d, w.n_bits, w.n_probes, w.tau, T, F * T, w.n_queries, w.chunk_frames,
+                        n_prompt=npr, dtype=tdt, device=dev)
+    layer.set_planes(up(w.planes))
+    for f in range(w.setup_frames):
+        layer.merge(up(w.k_frames[:, f]), up(w.v_frames[:, f]), 1, with_index=False)
+    import kv_compressed_attention_amd.fastar as fb
+    start = fb.TempCache(H, d, F * T, T, w.n_bits, tdt, dev)
+    start.copy_from(layer.cache)
+    res = {"steps": n_steps, "warmup": warmup, "dense_steps": warmup_steps(n_steps, warmup)}
+    for name, frac in (("warmup", warmup), ("all_sparse", 0.0), ("all_dense", 1.0)):
+        drv = DenoisingDriver(layer, n_steps, frac)
+        times = []
+        for r in range(reps + 1):
+            layer.cache.copy_from(start)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            drv.run(lambda s: (q, k_new, v_new, pk, pv))
+            e1.record()
+            torch.cuda.synchronize()
+            if r:
+                times.append(e0.elapsed_time(e1))
+        res[name + "_ms"] = float(np.median(times))
+    res["speedup_vs_all_dense"] = res["all_dense_ms"] / res["warmup_ms"]
+    res["speedup_all_sparse_vs_all_dense"] = res["all_dense_ms"] / res["all_sparse_ms"]
+    return res
+
+
 def annca(w, dev, steps):
     """The AnnCA workload: hash the queries and the prompt, prune, and
     cross-attention over the kept prompt keys; per-call times (cold: one
@@ -811,6 +948,14 @@ def main():
         extra["representatives"] = {"workload": w1.name, **{
             rep: tau_sweep(w1, dev, [0.9, 0.7], representative=rep) for rep in ("last", "mean", "medoid")}}
         extra["annca"] = annca(make_workload(2), dev, args.steps)
+        # several LSH tables and more probes (AnnSA recall / density / time)
+        extra["lsh_tables"] = {
+            "workload": w1.name,
+            "configs": lsh_tables_sweep(w1, dev, [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (4, 1), (4, 2)])}
+        if args.workload != 1:
+            extra["lsh_tables_" + w.name] = lsh_tables_sweep(w, dev, [(1, 2), (2, 2), (1, 4)])
+        # the denoising loop with the 30% dense warm-up
+        extra["denoise"] = {"workload": w.name, **denoise_loop(w, dev)}
         w3 = make_workload(3)
         roll = rollout(w3, dev, flush)
         extra["rollout"] = {"workload": w3.name, "chunks": roll,

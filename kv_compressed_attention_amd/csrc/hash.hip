@@ -70,8 +70,10 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
 #pragma unroll
     for (int p = 0; p < 16; ++p) s[p] = 0.f;
     float x2 = 0.f;
+    uint32_t nzb = 0u;  // any element nonzero (from the bits)
     for (int d = 0; d < D; ++d) {
       const float xv = xr[d];
+      nzb |= __float_as_uint(xv) & 0x7FFFFFFFu;
       x2 = fmaf(xv, xv, x2);
 #pragma unroll
       for (int p = 0; p < 16; ++p) s[p] = fmaf(xv, sp[p][d], s[p]);
@@ -111,6 +113,13 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
 #pragma unroll
       for (int p0 = 0; p0 < 16; p0 += 4)
         amb = probe_ranks(da + p0, da, p0, nb, P, 2.f * kc * xnorm + 0x1p-90f, rk + p0) || amb;
+    }
+    // a zero row: id 0, probes flip bits 0, 1, .. in order (every distance 0)
+    if (nzb == 0u) {
+      amb = false;
+      nr.j1 = 0;
+#pragma unroll
+      for (int p = 0; p < 16; ++p) rk[p] = p;
     }
     if (valid && !amb) {
       int32_t* o = bucket + idx * P;

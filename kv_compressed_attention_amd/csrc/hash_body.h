@@ -356,12 +356,24 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
     }
     bits = or_xor32(or_xor16(bits));
     amb = (int)or_xor32(or_xor16((uint32_t)amb));
+    // a zero row (every element +-0, from the bits: no underflow question):
+    // every projection is exactly 0 (id 0) and every distance 0, so the
+    // probes flip bits 0, 1, .. in order (ties to the smaller index);
+    // nothing to certify
+    uint32_t nzb = 0u;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) nzb |= (xu[c].x | xu[c].y | xu[c].z | xu[c].w) & 0x7FFF7FFFu;
+    const bool zero = valid && or_xor32(or_xor16(nzb)) == 0u;
     if (P == 2) {
       nearest_merge(nr, 16);
       nearest_merge(nr, 32);
       // each distance is known to within kc*|x| (plus division rounding)
       const float err = 2.f * kc * xnorm + (nr.d1 + nr.d2) * 0x1p-20f + 0x1p-90f;
       if (nr.d2 - nr.d1 <= err) amb = 1;
+    }
+    if (zero) {
+      amb = 0;
+      nr.j1 = 0;
     }
     // more probes: every lane of the row gathers the row's 16 distances and
     // ranks its own 4 planes
@@ -377,6 +389,11 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
         for (int i = 0; i < 4; ++i) da[4 * g2 + i] = __shfl(dl[i], 16 * g2 + col, FASTAR_WAVE);
       const bool a2 = probe_ranks(dl, da, 4 * g, nb, P, 2.f * kc * xnorm + 0x1p-90f, rk);
       amb = (int)or_xor32(or_xor16((uint32_t)(amb | (a2 ? 1 : 0))));
+      if (zero) {
+        amb = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rk[i] = 4 * g + i;
+      }
     }
     if (valid && g == 0 && !amb) {
       int32_t* o = w.bucket + ((int64_t)w.h * w.N + row) * P;

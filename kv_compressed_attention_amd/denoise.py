@@ -12,7 +12,8 @@ the denoising steps, so that early generation runs full attention
 * every step attends from the cache as it stood before the chunk (the chunk's
   frames change from step to step); after the last step its merged state is
   kept: the chunk's frames enter the cache once, as generated.
-All compute is libfastar's; this module only orders calls and swaps caches.
+All compute is libfastar's; this module only orders calls and restores the
+cache between steps.
 """
 
 from __future__ import annotations
@@ -20,7 +21,6 @@ from __future__ import annotations
 from fractions import Fraction
 from typing import Callable, List, Optional
 
-from . import fastar as fb
 
 
 def is_warmup_step(step: int, n_steps: int, warmup: float = 0.3) -> bool:
@@ -45,7 +45,10 @@ class DenoisingDriver:
     prompt_k, prompt_v) (prompt may be None); on_step(s, dense), if given, is
     called after each step is queued (the layer's o_self, lse_self, o_cross
     hold that step's results until the next step runs).  The layer's cache
-    is the cache before the chunk and, when run returns, the cache after it.
+    is the cache before the chunk and, when run returns, the cache after it:
+    each step merges into it, and the next step first undoes that merge
+    (TempCache.checkpoint / restore: only the last frame's groups and the
+    counts are restored, not the whole cache).
     """
 
     def __init__(self, layer, n_steps: int, warmup: float = 0.3):
@@ -53,27 +56,23 @@ class DenoisingDriver:
             raise ValueError("n_steps must be >= 1")
         self.layer, self.n_steps, self.warmup = layer, n_steps, warmup
         self.dense = [is_warmup_step(s, n_steps, warmup) for s in range(n_steps)]
-        c = layer.cache
-        # the step's working cache: each step merges into a copy of the
-        # chunk's starting cache
-        self.work = fb.TempCache(c.heads, c.dim, c.capacity, c.tokens_per_frame, c.n_bits, c.dtype,
-                                 c.rep_k.device, key_sums=c.k_sum is not None)
 
     def run(self, inputs: Callable[[int], tuple], on_step: Optional[Callable[[int, bool], None]] = None,
             timing: Optional[dict] = None) -> List[bool]:
         layer = self.layer
-        start = layer.cache
+        cache = layer.cache
+        ck = cache.checkpoint()
         for s in range(self.n_steps):
             q, k_new, v_new, prompt_k, prompt_v = inputs(s)
-            self.work.copy_from(start)
+            if s:
+                cache.restore(ck)
             if self.dense[s]:
-                layer.step_dense(q, k_new, v_new, prompt_k, prompt_v, cache=self.work, timing=timing)
+                layer.step_dense(q, k_new, v_new, prompt_k, prompt_v, cache=cache, timing=timing)
             else:
-                layer.step(q, k_new, v_new, prompt_k, prompt_v, cache=self.work, timing=timing)
+                layer.step(q, k_new, v_new, prompt_k, prompt_v, cache=cache, timing=timing)
             if on_step is not None:
                 on_step(s, self.dense[s])
-        # the last step's merge is the chunk's: keep it
-        start.copy_from(self.work)
+        # the last step's merge is the chunk's: it stays
         return list(self.dense)
 
 

@@ -296,6 +296,36 @@ class TempCache:
         for name, t in self.buffers().items():
             t.copy_(getattr(other, name))
 
+    _GROUP_ROWS = ("rep_k", "v_mean", "v_sum", "count", "log_count", "rep_bucket", "k_sum")
+
+    def checkpoint(self) -> dict:
+        """What later merges can change, saved for restore(): the rows of the
+        last frame's groups (the only existing groups a merge extends: frame
+        f's candidates are frame f - 1's groups, so every chain of later
+        frames starts at one of them), the group count, the frontier and the
+        status word.  Groups opened later lie past the saved count; a merge
+        that opens them again rewrites every field of their rows.  Device
+        copies only (stream-ordered)."""
+        H, cap = self.heads, self.capacity
+        heads = torch.arange(H, device=self.frontier.device)[:, None] * cap
+        idx = (heads + self.frontier.clamp_min(0)).reshape(-1).long()
+        rows = {}
+        for name in self._GROUP_ROWS:
+            t = getattr(self, name)
+            if t is not None:
+                rows[name] = t.view(H * cap, -1).index_select(0, idx)
+        return {"idx": idx, "rows": rows, "n_groups": self.n_groups.clone(),
+                "frontier": self.frontier.clone(), "status": self.status.clone()}
+
+    def restore(self, ck: dict):
+        """Undo the merges since checkpoint() returned ck."""
+        H, cap = self.heads, self.capacity
+        for name, saved in ck["rows"].items():
+            getattr(self, name).view(H * cap, -1).index_copy_(0, ck["idx"], saved)
+        self.n_groups.copy_(ck["n_groups"])
+        self.frontier.copy_(ck["frontier"])
+        self.status.copy_(ck["status"])
+
     def struct(self) -> FastarCache:
         return FastarCache(self.heads, self.dim, self.capacity, self.tokens_per_frame, self.n_bits,
                            _DTYPES[self.dtype], self.rep_k.data_ptr(), self.v_mean.data_ptr(),

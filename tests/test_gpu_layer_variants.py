@@ -150,3 +150,36 @@ def test_denoising_driver_matches_oracle(fa):
     assert int(layer.cache.n_groups[0]) == G
     assert np.array_equal(layer.cache.count[0, :G].cpu().numpy(), tc.count)
     assert np.array_equal(layer.cache.rep_k[0, :G].float().cpu().numpy(), tc.rep_k)
+
+
+@pytest.mark.parametrize("rep", ["last", "medoid"])
+def test_cache_checkpoint_restore(fa, rep):
+    """restore() undoes the merges since checkpoint(): the next merge then
+    gives what it gives on a full copy of the checkpointed cache."""
+    w = make_workload(1)
+    H, F, T, d = w.k_frames.shape
+    layer = _layer(w, representative=rep)
+    layer.set_planes(dev_tensor(w.planes, w.dtype))
+    _setup(layer, w)
+    c = layer.cache
+    copy = fa.TempCache(H, d, F * T, T, w.n_bits, TDT[w.dtype], "cuda", key_sums=rep != "last")
+    copy.copy_from(c)
+    ck = c.checkpoint()
+    rng = np.random.default_rng(31)
+    k_new, v_new = w.frames(w.setup_frames, F)
+    other_k = round_to_dtype(k_new + 0.2 * rng.standard_normal(k_new.shape), w.dtype)
+    layer.merge(dev_tensor(other_k, w.dtype), dev_tensor(v_new, w.dtype), w.chunk_frames)
+    c.restore(ck)
+    layer.merge(dev_tensor(k_new, w.dtype), dev_tensor(v_new, w.dtype), w.chunk_frames)
+    g1 = layer.group_of_new.clone()
+    layer.cache = copy
+    layer.merge(dev_tensor(k_new, w.dtype), dev_tensor(v_new, w.dtype), w.chunk_frames)
+    torch.cuda.synchronize()
+    assert torch.equal(g1, layer.group_of_new)
+    for h in range(H):
+        G = int(copy.n_groups[h])
+        assert int(c.n_groups[h]) == G
+        for name in ("rep_k", "v_mean", "v_sum", "count", "log_count", "rep_bucket") + (
+                ("k_sum",) if rep != "last" else ()):
+            assert torch.equal(getattr(c, name)[h, :G], getattr(copy, name)[h, :G]), name
+    assert torch.equal(c.frontier, copy.frontier)
