@@ -40,13 +40,15 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
+// Occupancy: 4 workgroups per CU, 3 with two probes (its 128-register
+// budget at 4 spilled), 2 in table mode (up to 8 ranges per row).
 // MODE: 0 bucket, 1 key list, 2 dense, 3 tables (several LSH tables and/or
 // more than two probes: P is then the capacity of a row's (table, probe)
 // list, ntab * ppt of it used).  Every head's k and v rows lie within 4 GiB
 // of the head's first row (checked by the caller), so row offsets are 32-bit
 // byte offsets from the head's base.
 template <int D, int P, int MODE>
-__global__ __launch_bounds__(256, MODE == 3 ? 2 : 4) void attn_bf16_kernel(
+__global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t q_sh, int64_t q_st, int64_t Nq,
     const int32_t* __restrict__ q_bucket, const int32_t* __restrict__ q_perm,
     const uint16_t* __restrict__ k, int64_t k_sh, int64_t k_st,

@@ -186,6 +186,48 @@ __device__ void scan_buckets(int nb, int32_t* st, int32_t* copy, int32_t* st2 = 
   const bool quad = nb == 4 * nthr;
   int4 q = make_int4(0, 0, 0, 0), q2 = make_int4(0, 0, 0, 0);
   int local = 0, local2 = 0;
+  const int nwv = nthr >> 6;
+  if (!quad && nb >= 64 * nwv && nb % (64 * nwv) == 0) {
+    const int lane = lane_id(), wave = tid >> 6;
+    // each wave scans a contiguous segment, 64 buckets per step (lane l:
+    // bucket base + l: no bank conflicts, contiguous stores)
+    const int seg = nb / nwv, b0 = wave * seg;
+    int sum = 0, sum2 = 0;
+    for (int i = lane; i < seg; i += FASTAR_WAVE) {
+      sum += st[b0 + i];
+      if (st2) sum2 += st2[b0 + i];
+    }
+    sum = wave_sum_dpp(sum);
+    sum2 = wave_sum_dpp(sum2);
+    if (lane == 0) {
+      wtot[0][wave] = sum;
+      wtot[1][wave] = sum2;
+    }
+    lds_barrier();
+    const int wt = lane < nwv ? wtot[0][lane] : 0, wt2 = lane < nwv ? wtot[1][lane] : 0;
+    int carry = wave_sum_dpp(lane < wave ? wt : 0), carry2 = wave_sum_dpp(lane < wave ? wt2 : 0);
+    for (int i = 0; i < seg; i += FASTAR_WAVE) {
+      const int b = b0 + i + lane;
+      const int v = st[b];
+      const int inc = (int)wave_incl_scan_dpp((uint32_t)v);
+      st[b] = carry + inc - v;
+      if (copy) copy[b] = carry + inc - v;
+      carry += __builtin_amdgcn_readlane(inc, FASTAR_WAVE - 1);
+      if (st2) {
+        const int v2 = st2[b];
+        const int inc2 = (int)wave_incl_scan_dpp((uint32_t)v2);
+        st2[b] = carry2 + inc2 - v2;
+        carry2 += __builtin_amdgcn_readlane(inc2, FASTAR_WAVE - 1);
+      }
+    }
+    if (wave == nwv - 1 && lane == 0) {
+      if (copy) copy[nb] = carry;
+      st[nb] = carry;
+      if (st2) st2[nb] = carry2;
+    }
+    lds_barrier();
+    return;
+  }
   if (quad) {
     q = *reinterpret_cast<const int4*>(st + s0);
     local = q.x + q.y + q.z + q.w;
