@@ -20,7 +20,9 @@
  * Conventions shared by every call
  * - All tensor and array arguments are DEVICE pointers owned by the caller.
  *   The library allocates nothing and keeps no state between calls.
- * - Every call is enqueued on `stream` and returns without synchronising.
+ * - Every call is enqueued on `stream` and returns without synchronising
+ *   (fastar_chunk forks part of its work to a second stream and joins it
+ *   back on `stream`).
  *   Counts produced on the device (groups, kept tokens) stay on the device.
  * - Arguments are validated on the host before any launch; a failed check
  *   returns FASTAR_ERR_INVALID or FASTAR_ERR_UNSUPPORTED and launches nothing.
@@ -410,15 +412,22 @@ fastar_status_t fastar_attention_recall_counts(const float* lse_sparse, const fl
                                                float* recall, float* stats, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * fastar_chunk -- one chunk of the per-layer sequence in one call, on one
- * stream, work that does not depend on a launch's own work carried by extra
- * workgroups of it: the new keys (and prompt keys) hashed; the TempCache
- * merge of the new frames, whose match launch also hashes bf16 queries (one
- * hashing serves every module: paper.rainbus.top "technical novelty"); the
- * representatives' bucket index, whose launch also builds the queries' index
- * (when both use the single counting pass); AnnSA over the merged cache;
- * then, with a prompt, AnnCA pruning and cross-attention over the kept prompt
- * tokens.
+ * fastar_chunk -- one chunk of the per-layer sequence in one call, work
+ * that does not depend on a launch's own work carried by extra workgroups of
+ * it: the new keys (and prompt keys) hashed; the TempCache merge of the new
+ * frames, whose match launch also hashes bf16 queries (one hashing serves
+ * every module: paper.rainbus.top "technical novelty"); the representatives'
+ * bucket index, whose launch also builds the queries' index (when both use
+ * the single counting pass); AnnSA over the merged cache; then, with a
+ * prompt, AnnCA pruning and cross-attention over the kept prompt tokens.
+ * The part that does not touch the cache (prune, cross-attention, and the
+ * queries' hashing when it does not ride on the match) runs on a second
+ * stream of the library's own (one per device, default priority, created on
+ * the device's first chunk call that is not under stream capture), forked
+ * from `stream` with an event after the work it needs and joined back before
+ * the call's last launch: in stream order of `stream` the call is one unit,
+ * also under graph capture.  Calls on one device share that stream, so
+ * concurrent calls on different streams serialise their second branches.
  * Equal to fastar_hash_multi, fastar_bucket_index, fastar_tempcache_merge,
  * fastar_bucket_attention (bucket mode, keys rep_k, values v_mean, bias
  * log_count) and, with a prompt, fastar_prune_prompt and
@@ -428,7 +437,7 @@ fastar_status_t fastar_attention_recall_counts(const float* lse_sparse, const fl
 typedef struct {
   /* the chunk */
   const fastar_tensor_t* q;         /* [H][Nq][d] queries                       */
-  int n_probes;                     /* 1 or 2                                   */
+  int n_probes;                     /* 1 .. FASTAR_MAX_PROBES                   */
   const fastar_tensor_t* k_new;     /* [H][n_frames * T][d] new frames' keys    */
   const fastar_tensor_t* v_new;     /* and values                               */
   int n_frames;                     /* > 0                                      */

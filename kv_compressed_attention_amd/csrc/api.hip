@@ -272,6 +272,8 @@ fastar_status_t run_merge(const fastar_cache_t* c, const fastar_tensor_t* k_new,
     fastar::MergeWs wf = one;
     wf.also_hash = f == 0 ? mw.also_hash : nullptr;
     wf.also_index = last ? mw.also_index : nullptr;
+    wf.index_after = last ? mw.index_after : nullptr;
+    wf.after_match = f == 0 ? mw.after_match : nullptr;
     const fastar_tensor_t kf = frame_slice(*k_new, T, f), vf = frame_slice(*v_new, T, f);
     int32_t* gf = group_of_new ? group_of_new + (int64_t)f * T : nullptr;
     int32_t* ro = last ? rep_offsets : nullptr;
@@ -670,6 +672,42 @@ fastar_tensor_t cache_rows(const fastar_cache_t* c, void* data) {
   t.stride_token = c->dim;
   return t;
 }
+// The chunk's second branch: a stream of the library's per device (default
+// priority, non-blocking) and the events that fork it from and join it to
+// the caller's stream.  Created on the first chunk call of the device that
+// is not under stream capture; a call that finds none runs on one stream.
+struct AuxBranch {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, q_done = nullptr, done = nullptr;
+};
+constexpr int kAuxDevices = 64;
+std::mutex g_aux_mutex;
+AuxBranch g_aux[kAuxDevices];
+bool g_aux_failed[kAuxDevices] = {};
+
+bool aux_branch(hipStream_t stream, AuxBranch* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kAuxDevices) return false;
+  std::lock_guard<std::mutex> lock(g_aux_mutex);
+  AuxBranch& b = g_aux[dev];
+  if (!b.s) {
+    if (g_aux_failed[dev]) return false;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return false;
+    AuxBranch n;
+    if (hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.q_done, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.done, hipEventDisableTiming) != hipSuccess) {
+      g_aux_failed[dev] = true;  // (what was created stays: this is rare and once)
+      return false;
+    }
+    b = n;
+  }
+  *out = b;
+  return true;
+}
+
 size_t chunk_index_ws(const fastar_chunk_t* a) {
   // the queries' index in a launch of its own needs scratch
   if (fastar::direct_index_supported(a->q->tokens, a->n_probes, a->n_bits)) return 0;
@@ -740,10 +778,110 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   if (!ws || ws_bytes < need)
     return fail(FASTAR_ERR_WORKSPACE, "workspace: need %zu bytes, got %zu", need, ws_bytes);
 
-  // launches, in order on the stream.  bf16 queries are hashed by extra
-  // workgroups of the merge's match launch (only their index, after the
-  // merge, and the attention need them); the keys first, on their own.
+  fastar::IndexJob qj{a->q_bucket, a->q->tokens, a->n_bits, a->n_probes, a->q_offsets, a->q_perm};
+  // the queries' index rides along with the representatives' when both are
+  // built by the single counting pass
+  const bool fused = a->q->tokens > 0 &&
+                     fastar::direct_index_supported(c->capacity, 1, c->n_bits, a->q->tokens, a->n_probes);
   fastar::MergeWs mw = merge_carve(c, a->n_frames, ws);
+  if (fused) mw.also_index = &qj;
+  // bf16 queries with the LSH match are hashed by extra workgroups of the
+  // merge's match launch (only their index, after the merge, and the
+  // attention need them)
+  const bool ride = match == FASTAR_MATCH_LSH && a->q->dtype == FASTAR_BF16 && c->dtype == FASTAR_BF16 &&
+                    a->q->dim == c->dim && c->heads > 0 && (int64_t)a->q->heads * a->q->tokens > 0;
+  AuxBranch ab;
+  if (c->heads > 0 && (int64_t)a->q->heads * a->q->tokens > 0 && (prompt || !ride) && aux_branch(stream, &ab)) {
+    // Two branches.  The library's second stream prunes the prompt and runs
+    // the cross-attention (neither touches the cache), and hashes the
+    // queries when they do not ride on the match; the caller's stream hashes
+    // the new keys (and with riding queries the prompt keys), merges them,
+    // indexes the queries with the representatives, runs the
+    // self-attention and joins the second branch.
+    fastar::HashJobs side, mainj;
+    side.count = mainj.count = 0;
+    fastar::HashJobs qjobs;
+    qjobs.count = 0;
+    if (ride) {
+      qjobs.count = 1;
+      qjobs.j[0] = jobs.j[0];
+      mw.also_hash = &qjobs;
+      mw.hash_planes = a->planes;
+      mw.hash_bits = a->n_bits;
+      mw.after_match = ab.q_done;
+      for (int i = 1; i < jobs.count; ++i) mainj.j[mainj.count++] = jobs.j[i];
+    } else {
+      side.j[side.count++] = jobs.j[0];
+      if (prompt) side.j[side.count++] = jobs.j[2];
+      mainj.j[mainj.count++] = jobs.j[1];
+      mw.index_after = ab.q_done;
+    }
+    bool main_any = false;
+    for (int i = 0; i < mainj.count; ++i) main_any = main_any || (int64_t)mainj.j[i].H * mainj.j[i].N > 0;
+    if (main_any && (st = hip_status(fastar::launch_hash_multi(mainj, a->q->dim, a->q->dtype, a->planes, a->n_bits,
+                                                               diag, stream),
+                                     "hash")) != FASTAR_OK)
+      return st;
+    if (!ride) {
+      if ((st = hip_status(hipEventRecord(ab.fork, stream), "hipEventRecord")) != FASTAR_OK) return st;
+      if ((st = hip_status(hipStreamWaitEvent(ab.s, ab.fork, 0), "hipStreamWaitEvent")) != FASTAR_OK) return st;
+      if ((st = hip_status(fastar::launch_hash_multi(side, a->q->dim, a->q->dtype, a->planes, a->n_bits, diag,
+                                                     ab.s),
+                           "hash")) != FASTAR_OK)
+        return st;
+      if ((st = hip_status(hipEventRecord(ab.q_done, ab.s), "hipEventRecord")) != FASTAR_OK) return st;
+    }
+    // the merge: with riding queries it records q_done right after its match
+    // launch, and the second branch starts from there
+    const bool side_first = !ride;
+    if (side_first && prompt) {
+      if ((st = hip_status(fastar::launch_prune(a->q_bucket, a->q->heads, a->q->tokens, a->n_probes, a->p_bucket,
+                                                a->prompt_k->tokens, a->n_bits, a->keep, a->kept_idx, a->n_kept,
+                                                ab.s),
+                           "prune_prompt")) != FASTAR_OK)
+        return st;
+      if (!cross_empty &&
+          (st = hip_status(fastar::launch_attention(cross, ab.s), "bucket_attention")) != FASTAR_OK)
+        return st;
+    }
+    if (side_first && (st = hip_status(hipEventRecord(ab.done, ab.s), "hipEventRecord")) != FASTAR_OK) return st;
+    if ((st = run_merge(c, a->k_new, a->v_new, a->k_bucket, a->n_frames, a->tau, mo, a->group_of_new,
+                        a->rep_offsets, a->rep_perm, mw, ws, diag, stream)) != FASTAR_OK)
+      return st;
+    if (ride) {
+      // the queries and prompt keys are hashed: prune and cross-attention
+      if ((st = hip_status(hipStreamWaitEvent(ab.s, ab.q_done, 0), "hipStreamWaitEvent")) != FASTAR_OK) return st;
+      if ((st = hip_status(fastar::launch_prune(a->q_bucket, a->q->heads, a->q->tokens, a->n_probes, a->p_bucket,
+                                                a->prompt_k->tokens, a->n_bits, a->keep, a->kept_idx, a->n_kept,
+                                                ab.s),
+                           "prune_prompt")) != FASTAR_OK)
+        return st;
+      if (!cross_empty &&
+          (st = hip_status(fastar::launch_attention(cross, ab.s), "bucket_attention")) != FASTAR_OK)
+        return st;
+      if ((st = hip_status(hipEventRecord(ab.done, ab.s), "hipEventRecord")) != FASTAR_OK) return st;
+    }
+    if (!fused) {
+      if (!ride &&
+          (st = hip_status(hipStreamWaitEvent(stream, ab.q_done, 0), "hipStreamWaitEvent")) != FASTAR_OK)
+        return st;
+      int32_t* iws = (int32_t*)((char*)ws + merge_workspace_ex(c, a->n_frames, a->merge_opts));
+      if ((st = hip_status(fastar::launch_bucket_index(a->q_bucket, a->q->heads, a->q->tokens, a->n_probes,
+                                                       a->n_bits, nullptr, a->q_offsets, a->q_perm, iws,
+                                                       stream),
+                           "bucket_index")) != FASTAR_OK)
+        return st;
+    }
+    if (!self_empty &&
+        (st = hip_status(fastar::launch_attention(self, stream), "bucket_attention")) != FASTAR_OK)
+      return st;
+    return hip_status(hipStreamWaitEvent(stream, ab.done, 0), "hipStreamWaitEvent");
+  }
+
+  // One stream (the second branch unavailable): launches in order.  bf16
+  // queries are hashed by extra workgroups of the merge's match launch (only
+  // their index, after the merge, and the attention need them); the keys
+  // first, on their own.
   fastar::HashJobs qjobs;
   qjobs.count = 0;
   if (match == FASTAR_MATCH_LSH && a->q->dtype == FASTAR_BF16 && c->dtype == FASTAR_BF16 &&
@@ -761,12 +899,6 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   if (any && (st = hip_status(fastar::launch_hash_multi(jobs, a->q->dim, a->q->dtype, a->planes, a->n_bits,
                                                        diag, stream), "hash")) != FASTAR_OK)
     return st;
-  fastar::IndexJob qj{a->q_bucket, a->q->tokens, a->n_bits, a->n_probes, a->q_offsets, a->q_perm};
-  // the queries' index rides along with the representatives' when both are
-  // built by the single counting pass
-  const bool fused = a->q->tokens > 0 &&
-                     fastar::direct_index_supported(c->capacity, 1, c->n_bits, a->q->tokens, a->n_probes);
-  if (fused) mw.also_index = &qj;
   if ((st = run_merge(c, a->k_new, a->v_new, a->k_bucket, a->n_frames, a->tau, mo, a->group_of_new,
                       a->rep_offsets, a->rep_perm, mw, ws, diag, stream)) != FASTAR_OK)
     return st;

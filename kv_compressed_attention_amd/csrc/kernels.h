@@ -103,6 +103,12 @@ struct MergeWs {
   int hash_bits = 0;
   int rep = FASTAR_REP_LAST;  // representative kind (mean and medoid: one frame per call)
   int64_t kb_stride = 0;      // row stride of k_new_bucket and group_of_new (0: n_frames * T)
+  // an event the stream waits for before the representatives' index launch
+  // (the job in also_index is written on another stream), or none
+  hipEvent_t index_after = nullptr;
+  // an event recorded right after the match launch (the jobs in also_hash
+  // are then hashed), or none
+  hipEvent_t after_match = nullptr;
 };
 // the merge's last launches for any match kind: the group updates (from the
 // links, successors and opener counts in a) and the representatives' index

@@ -1410,9 +1410,17 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
                      (const T*)c.rep_k,
                      (const T*)kn.data, kn.stride_head, kn.stride_token, c.frontier, tau, a, diag, qh,
                      (const uint16_t*)ws.hash_planes, ws.hash_bits, qblocks);
-  apply_launch<T, D>(c, kn, vn, kb, a, group_of_new, ws.rep, diag, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ws.after_match && (e = hipEventRecord(ws.after_match, s)) != hipSuccess) return e;
+  apply_launch<T, D>(c, kn, vn, kb, a, group_of_new, ws.rep, diag, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (ws.index_after) {
+    // the job riding on the index launch is produced on another stream
+    e = hipStreamWaitEvent(s, ws.index_after, 0);
+    if (e != hipSuccess) return e;
+  }
   if (rep_offsets && rep_perm)
     return launch_bucket_index(c.rep_bucket, H, c.capacity, 1, c.n_bits, c.n_groups, rep_offsets,
                                rep_perm, ws.index_ws, s, ws.also_index);
@@ -1426,6 +1434,10 @@ hipError_t apply_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   apply_launch<T, D>(c, kn, vn, kb, a, group_of_new, ws.rep, diag, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ws.index_after) {
+    e = hipStreamWaitEvent(s, ws.index_after, 0);
+    if (e != hipSuccess) return e;
+  }
   if (rep_offsets && rep_perm)
     return launch_bucket_index(c.rep_bucket, a.H, c.capacity, 1, c.n_bits, c.n_groups, rep_offsets,
                                rep_perm, ws.index_ws, s, ws.also_index);
