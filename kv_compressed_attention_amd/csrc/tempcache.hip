@@ -559,6 +559,35 @@ __device__ Cos64 wave_cos64(const T* x, const T* y) {
   return Cos64{s / sqrt(na * nb), false};
 }
 
+// The same with 16 lanes per pair of rows (the lane's group of 16 takes the
+// pair, D/16 elements per lane): four cosines per wave at once.  Every lane
+// of the group returns its pair's.
+template <typename T, int D>
+__device__ __forceinline__ Cos64 group_cos64(const T* x, const T* y) {
+  constexpr int EPL = D / 16;
+  const int sub = threadIdx.x & 15;
+  float xv[EPL], yv[EPL];
+  Chunk<T, EPL>::load(x + sub * EPL, xv);
+  Chunk<T, EPL>::load(y + sub * EPL, yv);
+  double s = 0.0, na = 0.0, nb = 0.0;
+  bool differ = false;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    differ = differ || __float_as_uint(xv[e]) != __float_as_uint(yv[e]);
+    const double u = (double)xv[e], v = (double)yv[e];
+    s += u * v;
+    na += u * u;
+    nb += v * v;
+  }
+  s = sum16d(s);
+  na = sum16d(na);
+  nb = sum16d(nb);
+  const bool dif = ((ballot64(differ) >> (lane_id() & 48)) & 0xFFFFull) != 0ull;
+  if (na == 0.0 || nb == 0.0) return Cos64{0.0, true};
+  if (!dif) return Cos64{1.0, true};
+  return Cos64{s / sqrt(na * nb), false};
+}
+
 // What one wave needs to match keys of new frame f.
 template <typename T, int D>
 struct SegCtx {
@@ -604,21 +633,46 @@ __device__ __forceinline__ void decide(const SegCtx<T, D>& x, const Top2<float>&
     int n;
     cand_of(src, cl, gl, n);
     const T* key = x.kf + (int64_t)js * x.k_st;
+    // four candidates at a time, one per 16-lane group
+    const int grp = lane >> 4;
+    auto cand_cos = [&](int k0) {
+      const int k = k0 + grp < n ? k0 + grp : n - 1;
+      return group_cos64<T, D>(key, x.cand_row(k, cl[k], x.f == 0 ? gl[k] : 0));
+    };
     Top2<double> u;
     u.init();
-    for (int k = 0; k < n; ++k) u.add(wave_cos64<T, D>(key, x.cand_row(k, cl[k], x.f == 0 ? gl[k] : 0)).c, cl[k]);
+    for (int k0 = 0; k0 < n; k0 += 4) {
+      const Cos64 r = cand_cos(k0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double cq = __shfl(r.c, 16 * q, FASTAR_WAVE);
+        if (k0 + q < n) u.add(cq, cl[k0 + q]);
+      }
+    }
     // certified: the threshold test (an exact best value decides it exactly)
     // and, with a proposal, the winner (every candidate within the bound of
-    // the best has an exact value: equal values go to the smaller index)
+    // the best has an exact value: equal values go to the smaller index).
+    // The exactness of values is only looked at when float64 alone leaves
+    // either in doubt.
     bool ex1 = false;
-    int near = 0, near_exact = 0;
-    if (u.c1 >= (double)x.tau - e64) {
-      for (int k = 0; k < n; ++k) {
-        const Cos64 r = wave_cos64<T, D>(key, x.cand_row(k, cl[k], x.f == 0 ? gl[k] : 0));
-        if (cl[k] == u.best) ex1 = r.exact;
-        if (r.c >= u.c1 - 2.0 * e64) {
-          ++near;
-          near_exact += r.exact ? 1 : 0;
+    int near = 1, near_exact = 0;
+    const bool thr_doubt = fabs(u.c1 - (double)x.tau) <= e64;
+    const bool win_doubt = u.c1 >= (double)x.tau - e64 && u.c1 - u.c2 <= 2.0 * e64;
+    if (thr_doubt || win_doubt) {
+      near = 0;
+      for (int k0 = 0; k0 < n; k0 += 4) {
+        const Cos64 r = cand_cos(k0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const double cq = __shfl(r.c, 16 * q, FASTAR_WAVE);
+          const bool xq = __shfl((int)r.exact, 16 * q, FASTAR_WAVE) != 0;
+          if (k0 + q < n) {
+            if (cl[k0 + q] == u.best) ex1 = xq;
+            if (cq >= u.c1 - 2.0 * e64) {
+              ++near;
+              near_exact += xq ? 1 : 0;
+            }
+          }
         }
       }
     }
