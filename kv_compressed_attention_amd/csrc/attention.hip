@@ -77,6 +77,12 @@ __global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf
   // MODE 3: the chunk's keys' buckets in tables 0 .. ntab - 2 (the dedup test)
   __shared__ __attribute__((aligned(16))) int32_t kdA[MODE == 3 ? 3 * 32 : 4];
   __shared__ __attribute__((aligned(16))) int32_t kdB[MODE == 3 ? 3 * 32 : 4];
+  // per wave: the key ids of the chunk after next (lane l's ids at [i][l]),
+  // gathered by 4-byte direct loads so that no register load stays in
+  // flight across the chunk loop (the compiler would wait for such a load
+  // before the first reuse of its register, which fell before the LDS
+  // reads of the current chunk and stalled them on the next chunk's rows)
+  __shared__ __attribute__((aligned(16))) int32_t kid[4][kDmaPerWave + 1][FASTAR_WAVE];
   // logical block (64-row block, head), XCD-grouped
   const int64_t nbx = (Nq + 63) / 64;
   const int64_t lb = xcd_block(blockIdx.x, nbx * H);
@@ -321,9 +327,10 @@ __global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf
     };
     const int kb_pre = pkb - pre;  // slot j of pass p is position j + kb_pre_p
     const bool is_pass = l < npass;
-    // keys this lane loads for chunk c: the rows of its 16-byte loads, then
-    // (lanes < 8) the bias of chunk row 8 wave + l
-    auto chunk_keys = [&](int c, int* key) {
+    // positions (in the index's permutation) of the keys this lane loads
+    // for chunk c: the rows of its 16-byte loads, then (lanes < 8) the bias
+    // of chunk row 8 wave + l
+    auto chunk_pos = [&](int c, int* key) {
       const int j0 = 32 * c, j1 = min(32 * c + 31, total - 1);
       // the passes that chunk c overlaps: pa .. pb
       const int pa = __popcll(ballot64(is_pass && pre <= j0)) - 1;
@@ -345,9 +352,34 @@ __global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf
         for (int i = 0; i <= kDmaPerWave; ++i) base[i] = pre_p <= j[i] ? kb_p : base[i];
       }
 #pragma unroll
-      for (int i = 0; i <= kDmaPerWave; ++i) {
-        const int kk = j[i] + base[i];
-        key[i] = (MODE == 2) ? kk : idx_h[kk];
+      for (int i = 0; i <= kDmaPerWave; ++i) key[i] = j[i] + base[i];
+    };
+    // the keys themselves, now (dense mode: the positions are the keys)
+    auto chunk_keys = [&](int c, int* key) {
+      chunk_pos(c, key);
+      if (MODE != 2) {
+#pragma unroll
+        for (int i = 0; i <= kDmaPerWave; ++i) key[i] = idx_h[key[i]];
+      }
+    };
+    // ... or requested into this wave's kid slots, to be read after the next
+    // wait for all of the wave's loads
+    auto chunk_keys_async = [&](int c, int* key) {
+      if (MODE == 2) {
+        chunk_pos(c, key);
+        return;
+      }
+      int pos[kDmaPerWave + 1];
+      chunk_pos(c, pos);
+#pragma unroll
+      for (int i = 0; i <= kDmaPerWave; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(idx_h + pos[i]),
+                                         (__attribute__((address_space(3))) void*)&kid[wave][i][0], 4, 0, 0);
+    };
+    auto keys_landed = [&](int* key) {
+      if (MODE != 2) {
+#pragma unroll
+        for (int i = 0; i <= kDmaPerWave; ++i) key[i] = kid[wave][i][l];
       }
     };
     // chunk c's K, V rows and biases into buffer c & 1; K and V row `row`
@@ -397,8 +429,11 @@ __global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf
         // every wave is done with chunk c - 1, whose buffers chunk c + 1 takes
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __syncthreads();
-        if (c + 1 < nch) chunk_load(key, kn, vn, bn, kdn);
-        if (c + 2 < nch) chunk_keys(c + 2, key);
+        if (c + 1 < nch) {
+          keys_landed(key);
+          chunk_load(key, kn, vn, bn, kdn);
+        }
+        if (c + 2 < nch) chunk_keys_async(c + 2, key);
       }
       const uint32_t kc = (uint32_t)(32 * c);
       // skip a chunk none of the wave's rows uses
@@ -533,7 +568,7 @@ __global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf
       chunk_load(key, ktA, vtA, btA, kdA);
       if (nch > 1) {
         chunk_load(key1, ktB, vtB, btB, kdB);
-        if (nch > 2) chunk_keys(2, key);
+        if (nch > 2) chunk_keys_async(2, key);
       }
     }
     for (int c = 0; c < nch; c += 2) {
