@@ -834,6 +834,14 @@ def summarize(w, res, steps):
     return d
 
 
+def progress(msg: str) -> None:
+    """One line per finished stage on stderr (the JSON line alone goes to stdout)."""
+    print(f"[bench {time.monotonic() - _T0:7.1f} s] {msg}", file=sys.stderr, flush=True)
+
+
+_T0 = time.monotonic()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -848,6 +856,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_sample_heads)
+        progress("cpu baseline")
 
     import kv_compressed_attention_amd as fa
     dev = torch.device("cuda:0")
@@ -860,6 +869,7 @@ def main():
     del cal_src, cal_dst
 
     res = measure_workload(w, dev, args.steps, args.warmup, args.graph_steps, hot=not args.no_hot)
+    progress(f"{w.name}: timed steps and stages")
     H, F, T, d = w.k_frames.shape
     nq = w.n_queries
     ms = res["cold_s"] * 1e3 / args.steps
@@ -929,6 +939,7 @@ def main():
         rq = measure_workload(w, dev, args.steps, args.warmup, args.graph_steps, hot=False, match="quant")
         rq.pop("setup")
         out["tempcache_quant8"] = summarize(w, rq, args.steps)
+        progress("quantized match")
         del rq
         torch.cuda.empty_cache()
         extra = {}
@@ -938,6 +949,7 @@ def main():
                                   hot=not args.no_hot)
             r1.pop("setup")
             extra[w1.name] = summarize(w1, r1, args.steps)
+            progress(w1.name)
             del r1
             torch.cuda.empty_cache()
         w1 = make_workload(1)
@@ -947,17 +959,22 @@ def main():
         # medoid keys) at two thresholds
         extra["representatives"] = {"workload": w1.name, **{
             rep: tau_sweep(w1, dev, [0.9, 0.7], representative=rep) for rep in ("last", "mean", "medoid")}}
+        progress("tau sweep and representatives")
         extra["annca"] = annca(make_workload(2), dev, args.steps)
+        progress("annca")
         # several LSH tables and more probes (AnnSA recall / density / time)
         extra["lsh_tables"] = {
             "workload": w1.name,
             "configs": lsh_tables_sweep(w1, dev, [(1, 1), (1, 2), (1, 4), (2, 1), (2, 2), (4, 1), (4, 2)])}
         if args.workload != 1:
             extra["lsh_tables_" + w.name] = lsh_tables_sweep(w, dev, [(1, 2), (2, 2), (1, 4)])
+        progress("lsh tables")
         # the denoising loop with the 30% dense warm-up
         extra["denoise"] = {"workload": w.name, **denoise_loop(w, dev)}
+        progress("denoising loop")
         w3 = make_workload(3)
         roll = rollout(w3, dev, flush)
+        progress("rollout")
         extra["rollout"] = {"workload": w3.name, "chunks": roll,
                             "first_last_ms": [roll[0]["ms"], roll[-1]["ms"]],
                             "last_chunk_density": roll[-1]["density"],
@@ -968,6 +985,7 @@ def main():
         out["extra_workloads"] = extra
     if not args.no_dense:
         out["dense_one_bucket"] = dense_one_bucket(dev)
+        progress("one-bucket attention")
     if cpu is not None:
         out["cpu_baseline"] = {
             "value": nq / cpu["all_cores_s_per_chunk"], "unit": "query tokens/s",

@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf
   // flight across the chunk loop (the compiler would wait for such a load
   // before the first reuse of its register, which fell before the LDS
   // reads of the current chunk and stalled them on the next chunk's rows)
-  __shared__ __attribute__((aligned(16))) int32_t kid[4][kDmaPerWave + 1][FASTAR_WAVE];
+  __shared__ __attribute__((aligned(16))) int32_t kid[MODE == 2 ? 1 : 4][kDmaPerWave + 1][FASTAR_WAVE];
   // logical block (64-row block, head), XCD-grouped
   const int64_t nbx = (Nq + 63) / 64;
   const int64_t lb = xcd_block(blockIdx.x, nbx * H);
@@ -365,19 +365,19 @@ __global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf
     // ... or requested into this wave's kid slots, to be read after the next
     // wait for all of the wave's loads
     auto chunk_keys_async = [&](int c, int* key) {
-      if (MODE == 2) {
+      if constexpr (MODE == 2) {
         chunk_pos(c, key);
-        return;
-      }
-      int pos[kDmaPerWave + 1];
-      chunk_pos(c, pos);
+      } else {
+        int pos[kDmaPerWave + 1];
+        chunk_pos(c, pos);
 #pragma unroll
-      for (int i = 0; i <= kDmaPerWave; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(idx_h + pos[i]),
-                                         (__attribute__((address_space(3))) void*)&kid[wave][i][0], 4, 0, 0);
+        for (int i = 0; i <= kDmaPerWave; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(idx_h + pos[i]),
+                                           (__attribute__((address_space(3))) void*)&kid[wave][i][0], 4, 0, 0);
+      }
     };
     auto keys_landed = [&](int* key) {
-      if (MODE != 2) {
+      if constexpr (MODE != 2) {
 #pragma unroll
         for (int i = 0; i <= kDmaPerWave; ++i) key[i] = kid[wave][i][l];
       }
