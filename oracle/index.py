@@ -5,14 +5,16 @@ bucket stored contiguously (gist.science technical summary, AnnSA: attention
 restricted to keys of the same bucket(s), run as a block-sparse operation).
 
 Definition used here:
-* members are sorted by bucket id (with two probes, by the first probe's
-  bucket), ties in ascending token order (a stable sort); each query appears
-  once; offsets[B] is the number of members with (first) bucket < B, so
-  offsets has 2**n_bits + 1 entries and offsets[-1] = N.
+* members are sorted by bucket id (with several probes, by the smallest of
+  the query's probe buckets), ties in ascending token order (a stable sort);
+  each query appears once; offsets[B] is the number of members whose (smallest)
+  bucket is < B, so offsets has 2**n_bits + 1 entries and offsets[-1] = N.
 
 Reading: the pages only ask that a bucket's members be contiguous for the
-block-sparse kernel; with two probes the query's keys come from both of its
-buckets, and the index groups the queries by the first one.
+block-sparse kernel; with several probes a query's keys come from all of its
+buckets, and any grouping key is a valid index.  The smallest probe bucket
+is taken: two queries probing the same pair {X, X ^ 2^j} share it whichever
+of the two is their own bucket, so they sit side by side.
 """
 
 from __future__ import annotations
@@ -25,9 +27,9 @@ def bucket_index(ids, n_bits: int):
     ids = np.asarray(ids, dtype=np.int64)
     if ids.ndim == 1:
         ids = ids[:, None]
-    first = ids[:, 0]
-    perm = np.argsort(first, kind="stable")
-    counts = np.bincount(first, minlength=1 << n_bits)
+    key = ids.min(axis=1)
+    perm = np.argsort(key, kind="stable")
+    counts = np.bincount(key, minlength=1 << n_bits)
     offsets = np.zeros((1 << n_bits) + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
     return offsets, perm.astype(np.int64)

@@ -142,11 +142,15 @@ def test_index_by_hand_one_probe():
 
 
 def test_index_by_hand_two_probes():
-    # two probes: each query once, stably by its first bucket
-    ids = np.array([[1, 0], [1, 3], [1, 0], [0, 2]])
+    # several probes: each query once, stably by its smallest probe bucket
+    # (keys 0, 1, 0, 0 and 2)
+    ids = np.array([[1, 0], [1, 3], [1, 0], [0, 2], [3, 2]])
     off, perm = bucket_index(ids, 2)
-    assert perm.tolist() == [3, 0, 1, 2]
-    assert off.tolist() == [0, 1, 4, 4, 4]
+    assert perm.tolist() == [0, 2, 3, 1, 4]
+    assert off.tolist() == [0, 3, 4, 5, 5]
+    # with three probes the smallest of all three
+    off, perm = bucket_index(np.array([[3, 2, 1], [2, 3, 0], [1, 0, 3]]), 2)
+    assert perm.tolist() == [1, 2, 0] and off.tolist() == [0, 2, 3, 3, 3]
 
 
 def test_index_invariants():
