@@ -108,9 +108,9 @@ int fastar_version(void);
  *   offsets  out [H][2^n_bits + 1] int32, or NULL (no index).
  *   perm     out [H][N] int32, or NULL (together with offsets).
  *            perm lists token indices sorted by bucket (with several
- *            probes, the first probe's bucket; each token once), ascending token
- *            within a bucket; offsets[B] = number of tokens whose (first)
- *            bucket is < B.
+ *            probes, the smallest of the token's probe buckets; each token
+ *            once), ascending token within a bucket; offsets[B] = number of
+ *            tokens whose (smallest) bucket is < B.
  *   ws       device workspace of at least fastar_hash_workspace() bytes,
  *            used by the index only (may be NULL when offsets is NULL).
  *   diag     optional device counters (may be NULL).

@@ -3,7 +3,8 @@
 // Block-sparse bucket attention needs each bucket's members contiguous
 // (gist.science technical summary, AnnSA: attention is restricted to the keys
 // of the query's bucket(s) and run block-sparse).  The sort key is the bucket
-// id (with two probes, the first probe's), ties in token order.
+// id (with several probes, the smallest of the item's probe buckets), ties in
+// token order.
 //
 // 3..14 bits take a single stable counting pass (index_direct.h), a head
 // split over up to 8 workgroups.  Anything else (0..2 or 15 bits, or 14 bits
@@ -15,7 +16,7 @@
 // atomics.  Per-wave digit counters live in LDS (16 x 256 ints).  A head of at
 // most kLdsItems items is sorted entirely in LDS (keys and 16-bit token
 // indices, double-buffered); larger heads go through the workspace.
-// offsets[B] is the number of items whose first bucket is < B: every run of
+// offsets[B] is the number of items whose key is < B: every run of
 // equal buckets writes its start and a suffix minimum fills the gaps.
 
 #include "common.h"
@@ -137,7 +138,7 @@ __device__ __forceinline__ void radix_pass(int64_t wbeg, int64_t wend, int shift
   __syncthreads();
 }
 
-// offsets[B] = number of sorted items whose first bucket (key >> shift0) < B.
+// offsets[B] = number of sorted items whose key (>> shift0) is < B.
 template <typename KeyAt>
 __device__ __forceinline__ void write_offsets(int32_t* off, int nbk, int64_t nh, int shift0,
                                               KeyAt key_at, int* cmin) {
@@ -187,7 +188,7 @@ __device__ __forceinline__ void write_offsets(int32_t* off, int nbk, int64_t nh,
   }
 }
 
-// P: the ids' row stride (probes per item); the first probe is the key
+// P: the ids' row stride (probes per item); the smallest probe is the key
 __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
     const int32_t* __restrict__ bucket, int P, int64_t n, int nbits, const int32_t* __restrict__ n_valid,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ ws,
@@ -216,8 +217,8 @@ __global__ __launch_bounds__(kThreads) void bucket_index_kernel(
   const int64_t chunk = (nh + kWaves - 1) / kWaves;
   const int64_t wbeg = (int64_t)wave * chunk < nh ? (int64_t)wave * chunk : nh;
   const int64_t wend = wbeg + chunk < nh ? wbeg + chunk : nh;
-  // the sort key: the first probe's bucket
-  auto key_of = [&](int64_t i) -> int32_t { return ids[(int64_t)P * i]; };
+  // the sort key: the smallest probe bucket
+  auto key_of = [&](int64_t i) -> int32_t { return (int32_t)index_key(ids, i, P); };
   if (use_lds && nh <= kLdsItems) {
     int32_t* ka = lds;
     int32_t* kb = ka + kLdsItems;

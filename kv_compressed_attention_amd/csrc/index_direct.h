@@ -8,8 +8,8 @@
 
 namespace fastar {
 
-// A single stable counting pass for 3..14 bits, one or two probes (the sort
-// key is the first probe's bucket), any item count below 2^31 that the
+// A single stable counting pass for 3..14 bits, any probe count (the sort
+// key is the smallest of an item's probe buckets), any item count below 2^31 that the
 // counters allow.  Per-wave bucket counters (one row of 2^b per scattering
 // wave) sit in LDS: 16-bit while a head has at most 65535 items, 32-bit
 // above.  One scan over (bucket, row) gives each wave its scatter bases and
@@ -18,6 +18,19 @@ namespace fastar {
 // the slice and those after it, per bucket, in two more rows) to place it,
 // so the parts need no exchange.  With `stage` (one part, room left in LDS)
 // the permutation is assembled in LDS and written out coalesced.
+// the sort key of item i of ids [n][P]: the smallest of its P probe buckets
+// (queries probing the same bucket pair then sit together)
+__device__ __forceinline__ uint32_t index_key(const int32_t* ids, int64_t i, int P) {
+  const int32_t* r = ids + i * P;
+  int m = r[0];
+  if (P == 2) {
+    m = min(m, r[1]);
+  } else {
+    for (int p = 1; p < P; ++p) m = min(m, r[p]);
+  }
+  return (uint32_t)m;
+}
+
 constexpr int kDirectWaves = 16;
 constexpr int kDirectThreads = kDirectWaves * FASTAR_WAVE;
 // waves that scatter a part's slice when a head has several parts, at most
@@ -77,7 +90,7 @@ inline size_t direct_index_lds(int64_t n, int n_bits, bool wide, int nparts, int
 }
 
 // Part `part` of nparts of the index of head h (ids [H][n][P], sorted by
-// their first probe), by one workgroup of kDirectWaves waves.  lds4: the
+// their smallest probe), by one workgroup of kDirectWaves waves.  lds4: the
 // dynamic LDS of direct_index_lds bytes.
 template <int NBITS, bool WIDE>
 __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
@@ -151,7 +164,7 @@ __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
 #pragma unroll
     for (int r = 0; r < kTile; ++r) {
       const int i = t0 + r * FASTAR_WAVE + lane;
-      const uint32_t v = (uint32_t)ids[(int64_t)(i < last ? i : last) * P];
+      const uint32_t v = index_key(ids, i < last ? i : last, P);
       b[r] = i < wend ? (v & bmask) : 0xFFFFFFFFu;
     }
   };
@@ -160,7 +173,7 @@ __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
     for (int r = 0; r < kBatch; ++r) {
       const int j = j0 + r * kDirectThreads + (int)threadIdx.x;
       const int i = j < sb ? j : j + (se - sb);
-      const uint32_t v = (uint32_t)ids[(int64_t)(i < last ? i : last) * P];
+      const uint32_t v = index_key(ids, i < last ? i : last, P);
       ob[r] = j < nother ? (v & bmask) : 0xFFFFFFFFu;
     }
   };
