@@ -33,6 +33,8 @@
 // even) gives the exact rounding.  float32 x: the same argument in float64
 // (Q x exact in 31 bits; at least 2^52 / (Q a) half-ulps).
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -259,15 +261,29 @@ struct QTop {
   }
 };
 
+// Candidates go through LDS in tiles of 64 shared by the workgroup's four
+// waves (16-byte direct loads, double-buffered, each row's 16-byte pieces
+// XOR-swizzled by the row so that the 8 rows one read touches hit distinct
+// banks), with their 1 / norms and biases.
 template <int D>
 __global__ __launch_bounds__(256) void tcq_match_kernel(QMatchArgs a) {
-  constexpr int KB = D / 64;  // 64-byte k-blocks of a row
+  constexpr int KB = D / 64;          // 64-byte k-blocks of a row
+  constexpr int kPieces = D / 16;     // 16-byte pieces of a row
+  constexpr int kRowsPer = 64 / kPieces;  // rows one 64-lane 16-byte load fills
+  constexpr int kLoadsPerWave = kPieces / 4;
+  __shared__ __attribute__((aligned(16))) int8_t ctA[64 * D];
+  __shared__ __attribute__((aligned(16))) int8_t ctB[64 * D];
+  __shared__ __attribute__((aligned(16))) float rtA[64];
+  __shared__ __attribute__((aligned(16))) float rtB[64];
+  __shared__ __attribute__((aligned(16))) float btA[64];
+  __shared__ __attribute__((aligned(16))) float btB[64];
   const int h = blockIdx.y, f = blockIdx.z;
   const int lane = lane_id(), col = lane & 15, g = lane >> 4;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int k0 = blockIdx.x * 64 + wave * 16;
-  if (k0 >= a.T) return;  // the whole wave (no workgroup barriers here)
   const int T = a.T;
+  // a wave past the last key still loads its share of the tiles
+  const bool wact = k0 < T;
   const int64_t tk = ((int64_t)h * a.ntab + f + 1 + a.moff) * T;  // matcher table rows (keys or queries)
   const int64_t tc = ((int64_t)h * a.ntab + f) * T;                // candidate table rows
   const int8_t* kc = a.codes + tk * D;
@@ -275,39 +291,101 @@ __global__ __launch_bounds__(256) void tcq_match_kernel(QMatchArgs a) {
   const float* crn = a.rn + tc;
   const float* cbias = a.bias + tc;
   // B operand: key k0 + col, bytes 16 g .. + 16 of each k-block
-  const int key = k0 + col < T ? k0 + col : T - 1;
+  const int key = wact && k0 + col < T ? k0 + col : T - 1;
   v4i32_t kb[KB];
 #pragma unroll
   for (int b = 0; b < KB; ++b) kb[b] = *reinterpret_cast<const v4i32_t*>(kc + (int64_t)key * D + 64 * b + 16 * g);
-  auto load_cands = [&](int c0, v4i32_t* ca) {
-    const int c = c0 + col < T ? c0 + col : T - 1;
+  // tile t's rows (row r's piece p at position p ^ (r % kPieces)), 1 / norms
+  // and biases; rows past the end repeat the last (masked when scored)
+  auto load_tile = [&](int t, int8_t* ct, float* rt, float* bt) {
+    const int c0 = t * 64;
 #pragma unroll
-    for (int b = 0; b < KB; ++b) ca[b] = *reinterpret_cast<const v4i32_t*>(cc + (int64_t)c * D + 64 * b + 16 * g);
-  };
-  QTop t{-INFINITY, -INFINITY, -1};
-  v4i32_t ca[KB], cn[KB];
-  load_cands(0, ca);
-  for (int c0 = 0; c0 < T; c0 += 16) {
-    if (c0 + 16 < T) load_cands(c0 + 16, cn);
-    v4i32_t acc = {0, 0, 0, 0};
-#pragma unroll
-    for (int b = 0; b < KB; ++b) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ca[b], kb[b], acc, 0, 0, 0);
-    // acc[i] = code dot of candidate c0 + 4 g + i with key k0 + col
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = c0 + 4 * g + i;
-      const bool cv = ci < T;
-      const int cl = cv ? ci : T - 1;  // in bounds; past the end masked below
-      const float rv = crn[cl], bv = cbias[cl];
-      const float s = fmaf((float)acc[i], cv ? rv : 0.f, cv ? bv : -INFINITY);
-      const float c1o = t.c1;
-      t.c2 = __builtin_amdgcn_fmed3f(s, c1o, t.c2);
-      t.best = s > c1o ? ci : t.best;
-      t.c1 = fmaxf(c1o, s);
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+      const int blk = wave * kLoadsPerWave + i;
+      const int row = blk * kRowsPer + lane / kPieces;
+      const int pc = lane % kPieces;
+      const int c = min(c0 + row, T - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(cc + (int64_t)c * D + 16 * (pc ^ (row % kPieces))),
+                                       (__attribute__((address_space(3))) void*)(ct + blk * 1024), 16, 0, 0);
     }
+    const int c = min(c0 + lane, T - 1);
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds((const void*)(crn + c), (__attribute__((address_space(3))) void*)rt, 4, 0,
+                                       0);
+    if (wave == 1)
+      __builtin_amdgcn_global_load_lds((const void*)(cbias + c), (__attribute__((address_space(3))) void*)bt, 4,
+                                       0, 0);
+  };
+  // running top two of the lane's scores; best holds the candidate minus
+  // 4 g (the lane's offset within a block) until the tiles are done
+  QTop t{-INFINITY, -INFINITY, -1};
+  // the wave's 16 keys against tile ti's candidates.  BIASED: the frontier
+  // (f == 0) may hold candidates without a group (bias -inf); TAIL: the last
+  // tile's rows past the end
+  auto compute = [&](auto biased_c, auto tail_c, int ti, const int8_t* ct, const float* rt, const float* bt) {
+    constexpr bool BIASED = decltype(biased_c)::value, TAIL = decltype(tail_c)::value;
+    const int c0 = ti * 64;
 #pragma unroll
-    for (int b = 0; b < KB; ++b) ca[b] = cn[b];
+    for (int cb = 0; cb < 4; ++cb) {
+      if (TAIL && c0 + 16 * cb >= T) break;
+      const int row = 16 * cb + col;
+      v4i32_t acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        const v4i32_t ca = *reinterpret_cast<const v4i32_t*>(ct + row * D + 16 * ((4 * b + g) ^ (row % kPieces)));
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(ca, kb[b], acc, 0, 0, 0);
+      }
+      // acc[i] = code dot of candidate c0 + 16 cb + 4 g + i with key k0 + col
+      const float4 r4 = *reinterpret_cast<const float4*>(rt + 16 * cb + 4 * g);
+      const float rv[4] = {r4.x, r4.y, r4.z, r4.w};
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BIASED) {
+        const float4 b4 = *reinterpret_cast<const float4*>(bt + 16 * cb + 4 * g);
+        bv[0] = b4.x;
+        bv[1] = b4.y;
+        bv[2] = b4.z;
+        bv[3] = b4.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int cr = c0 + 16 * cb + i;  // the candidate less 4 g (uniform)
+        float s = BIASED ? fmaf((float)acc[i], rv[i], bv[i]) : (float)acc[i] * rv[i];
+        if (TAIL) s = cr + 4 * g < T ? s : -INFINITY;
+        const float c1o = t.c1;
+        t.c2 = __builtin_amdgcn_fmed3f(s, c1o, t.c2);
+        t.best = s > c1o ? cr : t.best;
+        t.c1 = __builtin_amdgcn_fmed3f(s, c1o, INFINITY);  // the larger (no NaN here)
+      }
+    }
+  };
+  using yes = std::true_type;
+  using no = std::false_type;
+  const int ntile = (T + 63) / 64;
+  // tile t + 1 loads while tile t is scored; before the barrier each wave
+  // waits for its own loads of tile t, after it every wave's have landed and
+  // every wave is done with tile t - 1, whose buffers tile t + 1 takes
+  auto step = [&](int ti, const int8_t* ct, const float* rt, const float* bt, int8_t* cn, float* rn2,
+                  float* bn) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (ti + 1 < ntile) load_tile(ti + 1, cn, rn2, bn);
+    if (!wact) return;
+    const bool tail = ti * 64 + 64 > T;
+    if (f == 0) {
+      if (tail) compute(yes{}, yes{}, ti, ct, rt, bt);
+      else compute(yes{}, no{}, ti, ct, rt, bt);
+    } else {
+      if (tail) compute(no{}, yes{}, ti, ct, rt, bt);
+      else compute(no{}, no{}, ti, ct, rt, bt);
+    }
+  };
+  load_tile(0, ctA, rtA, btA);
+  for (int ti = 0; ti < ntile; ti += 2) {
+    step(ti, ctA, rtA, btA, ctB, rtB, btB);
+    if (ti + 1 < ntile) step(ti + 1, ctB, rtB, btB, ctA, rtA, btA);
   }
+  if (!wact) return;  // the whole wave; no barrier follows
+  if (t.best >= 0) t.best += 4 * g;
   // the four lanes of a key (l, l ^ 16, l ^ 32, l ^ 48)
 #pragma unroll
   for (int m = 16; m <= 32; m <<= 1) {
