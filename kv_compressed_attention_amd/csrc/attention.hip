@@ -607,6 +607,228 @@ __global__ __launch_bounds__(256, MODE == 3 ? 2 : (P == 2 ? 3 : 4)) void attn_bf
   if (lse && g == 0) lse[(int64_t)h * Nq + t] = lsum > 0.f ? (m + log2f(lsum)) * kLn2 : -INFINITY;
 }
 
+// Dense attention in bf16 (every query of a head against the head's first n
+// keys: all of them, or n_key_list[h]): one workgroup of 4 waves owns 128
+// query rows, each wave two 16-row MFMA groups that share every LDS read of a
+// chunk's K and V^T operands (half the LDS reads per score of the kernel
+// above, whose one group per wave left the dense case bound by LDS
+// bandwidth).  Chunks of 32 keys, their rows and biases staged in LDS as
+// above (double-buffered 16-byte direct loads, swizzled rows).
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_dense_bf16_kernel(
+    const uint16_t* __restrict__ q, int64_t q_sh, int64_t q_st, int64_t Nq,
+    const uint16_t* __restrict__ k, int64_t k_sh, int64_t k_st,
+    const uint16_t* __restrict__ v, int64_t v_sh, int64_t v_st, int64_t Nk,
+    const float* __restrict__ key_bias, const int32_t* __restrict__ n_key_list, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int H) {
+  constexpr int RG = 2;                           // 16-row MFMA groups per wave
+  constexpr int NC = D / 32;                      // k-chunks of the QK^T contraction
+  constexpr int NB = D / 16;                      // 16-dim output blocks
+  constexpr int kPieces = D / 8;                  // 16-byte pieces of a row
+  constexpr int kDmaRows = 64 / kPieces;          // rows one 64-lane 16-byte LDS load fills
+  constexpr int kDmaPerWave = 32 / kDmaRows / 4;  // such loads per wave, tile and chunk
+  __shared__ __attribute__((aligned(16))) uint16_t ktA[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t ktB[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vtA[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vtB[32 * D];
+  __shared__ __attribute__((aligned(16))) float btA[32];
+  __shared__ __attribute__((aligned(16))) float btB[32];
+  const int64_t nbx = (Nq + 127) / 128;
+  const int64_t lb = xcd_block(blockIdx.x, nbx * H);
+  if (lb >= nbx * H) return;  // the whole workgroup
+  const int h = (int)(lb / nbx);
+  const int64_t R0 = (lb - (int64_t)h * nbx) * 128;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int l = lane_id();
+  const int col = l & 15;
+  const int g = l >> 4;
+  const int vrow = 4 * g + ((l >> 2) & 3);
+  // group gi's MFMA row of this lane: workgroup row 32 wave + 16 gi + col
+  int64_t r[RG];
+  bool rvalid[RG];
+  bf16x8_t qop[RG][NC];
+#pragma unroll
+  for (int gi = 0; gi < RG; ++gi) {
+    r[gi] = R0 + 32 * wave + 16 * gi + col;
+    rvalid[gi] = r[gi] < Nq;
+    const uint16_t* qrow = q + (int64_t)h * q_sh + (rvalid[gi] ? r[gi] : 0) * q_st;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * c + 8 * g);
+      if (!rvalid[gi]) u = make_uint4(0u, 0u, 0u, 0u);
+      qop[gi][c] = __builtin_bit_cast(bf16x8_t, u);
+    }
+  }
+  float m[RG], lsum[RG];
+  f32x4_t acc[RG][NB];
+#pragma unroll
+  for (int gi = 0; gi < RG; ++gi) {
+    m[gi] = -INFINITY;
+    lsum[gi] = 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[gi][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const char* kh = reinterpret_cast<const char*>(k + (int64_t)h * k_sh);
+  const char* vh = reinterpret_cast<const char*>(v + (int64_t)h * v_sh);
+  const uint32_t kst_b = (uint32_t)(k_st * 2), vst_b = (uint32_t)(v_st * 2);
+  const float* bh = key_bias ? key_bias + (int64_t)h * Nk : nullptr;
+  int total = (int)Nk;
+  if (n_key_list) {
+    const int64_t nl = n_key_list[h];
+    total = (int)(nl < 0 ? 0 : (nl < Nk ? nl : Nk));
+  }
+  const int nch = (total + 31) / 32;
+  // chunk c's K, V rows and biases (the keys are the positions; past the end
+  // the last key, loaded and masked)
+  auto chunk_load = [&](int c, uint16_t* kt, uint16_t* vt, float* bt) {
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int row0 = (wave * kDmaPerWave + i) * kDmaRows;
+      const int row = row0 + l / kPieces;
+      const int pc = l % kPieces;
+      const uint32_t key = (uint32_t)min(32 * c + row, total - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(kh + (uint32_t)(key * kst_b + (uint32_t)((pc ^ (row % kPieces)) * 16))),
+          (__attribute__((address_space(3))) void*)(kt + row0 * D), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(vh + (uint32_t)(key * vst_b + (uint32_t)((pc ^ (row % kPieces)) * 16))),
+          (__attribute__((address_space(3))) void*)(vt + row0 * D), 16, 0, 0);
+    }
+    if (bh && l < 8)
+      __builtin_amdgcn_global_load_lds((const void*)(bh + min(32 * c + 8 * wave + l, total - 1)),
+                                       (__attribute__((address_space(3))) void*)(bt + 8 * wave), 4, 0, 0);
+  };
+  auto compute = [&](int c, const uint16_t* kt, const uint16_t* vt, const float* bt) {
+    const int kc = 32 * c;
+    const bool whole = kc + 32 <= total;  // no slot past the end
+    float s[RG][8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      // A operand: chunk row 16 hf + col, dims 32 cc + 8 g .. +8 (piece 4 cc + g)
+      const int row = 16 * hf + col;
+      bf16x8_t kop[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+        kop[cc] = *reinterpret_cast<const bf16x8_t*>(&kt[row * D + (((4 * cc + g) ^ (row % kPieces)) * 8)]);
+      const float4 b4 = bh ? *reinterpret_cast<const float4*>(&bt[16 * hf + 4 * g])
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float bias[4] = {b4.x * kLog2e, b4.y * kLog2e, b4.z * kLog2e, b4.w * kLog2e};
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi) {
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[cc], qop[gi][cc], sacc, 0, 0, 0);
+        // sacc[i] = score(chunk slot 16 hf + 4 g + i, row col)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sv = sacc[i] * scale_log2 + bias[i];
+          s[gi][4 * hf + i] = (whole || kc + 16 * hf + 4 * g + i < total) ? sv : -INFINITY;
+        }
+      }
+    }
+    bf16x8_t pop[RG];
+#pragma unroll
+    for (int gi = 0; gi < RG; ++gi) {
+      float mx = fmaxf(fmaxf(fmaxf(s[gi][0], s[gi][1]), fmaxf(s[gi][2], s[gi][3])),
+                       fmaxf(fmaxf(s[gi][4], s[gi][5]), fmaxf(s[gi][6], s[gi][7])));
+      mx = max_xor32(max_xor16(mx));
+      const float mnew = fmaxf(m[gi], mx);
+      const float base = (mnew == -INFINITY) ? 0.f : mnew;
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pw[i] = pack_bf16x2(__builtin_amdgcn_exp2f(s[gi][2 * i] - base),
+                            __builtin_amdgcn_exp2f(s[gi][2 * i + 1] - base));
+      // the sum of the rounded weights that the PV product uses
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw[i]),
+                                                __builtin_bit_cast(bf16x2_t, 0x3F803F80u), psum, false);
+      // rescale the running sums only where a row's (finite) max went up
+      if (ballot64(m[gi] != -INFINITY && mnew > m[gi])) {
+        const float alpha = __builtin_amdgcn_exp2f(m[gi] - base);
+        lsum[gi] *= alpha;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+          acc[gi][bb][0] *= alpha;
+          acc[gi][bb][1] *= alpha;
+          acc[gi][bb][2] *= alpha;
+          acc[gi][bb][3] *= alpha;
+        }
+      }
+      lsum[gi] += psum;
+      m[gi] = mnew;
+      pop[gi] = __builtin_bit_cast(bf16x8_t, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    }
+    // V^T operand of block bb, as in the kernel above, shared by both groups
+    static_assert(16 % kPieces == 0 || kPieces == 16, "rows r and r + 16 share their piece swizzle");
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int piece = 2 * bb + ((l & 3) >> 1);
+      const uint16_t* src = vt + vrow * D + ((piece ^ (vrow % kPieces)) * 8) + (l & 1) * 4;
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)src);
+      const v4i16_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(src + 16 * D));
+      const uint2 wl = __builtin_bit_cast(uint2, lo), wh = __builtin_bit_cast(uint2, hi);
+      const bf16x8_t vop = __builtin_bit_cast(bf16x8_t, make_uint4(wl.x, wl.y, wh.x, wh.y));
+#pragma unroll
+      for (int gi = 0; gi < RG; ++gi)
+        acc[gi][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pop[gi], acc[gi][bb], 0, 0, 0);
+    }
+  };
+  auto chunk = [&](int c, const uint16_t* kt, const uint16_t* vt, const float* bt, uint16_t* kn, uint16_t* vn,
+                   float* bn) {
+    if (c == 0) {
+      // chunk 0's rows have landed (chunk 1's, requested right behind them,
+      // may still be in flight: at least 2 kDmaPerWave requests)
+      static_assert(2 * kDmaPerWave < 16, "vmcnt immediate");
+      if (nch > 1) __builtin_amdgcn_s_waitcnt(kWaitVm0 | (2 * kDmaPerWave));
+      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    } else {
+      // chunk c's rows have landed; after the barrier every wave's have, and
+      // every wave is done with chunk c - 1, whose buffers chunk c + 1 takes
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      if (c + 1 < nch) chunk_load(c + 1, kn, vn, bn);
+    }
+    compute(c, kt, vt, bt);
+  };
+  if (nch > 0) {
+    chunk_load(0, ktA, vtA, btA);
+    if (nch > 1) chunk_load(1, ktB, vtB, btB);
+  }
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, ktA, vtA, btA, ktB, vtB, btB);
+    if (c + 1 < nch) chunk(c + 1, ktB, vtB, btB, ktA, vtA, btA);
+  }
+  const bool odd = (g & 1) != 0;
+#pragma unroll
+  for (int gi = 0; gi < RG; ++gi) {
+    const float ls = sum_xor32(sum_xor16(lsum[gi]));
+    if (!rvalid[gi]) continue;
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    // as in the kernel above: lanes g and g ^ 1 trade halves of each block
+    // pair so that each stores 16 contiguous bytes
+    uint16_t* orow = out + ((int64_t)h * Nq + r[gi]) * D;
+#pragma unroll
+    for (int mb = 0; mb < NB / 2; ++mb) {
+      const uint2 w0 = make_uint2(pack_bf16x2(acc[gi][2 * mb][0] * inv, acc[gi][2 * mb][1] * inv),
+                                  pack_bf16x2(acc[gi][2 * mb][2] * inv, acc[gi][2 * mb][3] * inv));
+      const uint2 w1 = make_uint2(pack_bf16x2(acc[gi][2 * mb + 1][0] * inv, acc[gi][2 * mb + 1][1] * inv),
+                                  pack_bf16x2(acc[gi][2 * mb + 1][2] * inv, acc[gi][2 * mb + 1][3] * inv));
+      const uint2 snd = odd ? w0 : w1;
+      const uint2 rcv = make_uint2(xor16_word(snd.x), xor16_word(snd.y));
+      const uint4 o = odd ? make_uint4(rcv.x, rcv.y, w1.x, w1.y) : make_uint4(w0.x, w0.y, rcv.x, rcv.y);
+      *reinterpret_cast<uint4*>(orow + (odd ? 16 * (2 * mb + 1) + 4 * (g - 1) : 32 * mb + 4 * g)) = o;
+    }
+    if (lse && g == 0) lse[(int64_t)h * Nq + r[gi]] = ls > 0.f ? (m[gi] + log2f(ls)) * kLn2 : -INFINITY;
+  }
+}
+
 // fp32: one query row per lane on the vector ALUs (no fp32 MFMA rounding
 // concerns; the fp32 workloads are small).
 template <int D, int P, int MODE>
@@ -714,6 +936,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(
 
 template <int D, int P, int MODE>
 hipError_t launch3(const AttnArgs& a, hipStream_t s) {
+  if (MODE == 2 && a.dtype == FASTAR_BF16) {
+    const int64_t nb = (a.nq + 127) / 128 * a.heads;
+    dim3 grid((unsigned)(FASTAR_XCDS * xcd_span(nb)));
+    hipLaunchKernelGGL((attn_dense_bf16_kernel<D>), grid, dim3(256), 0, s, (const uint16_t*)a.q, a.q_sh, a.q_st,
+                       a.nq, (const uint16_t*)a.k, a.k_sh, a.k_st, (const uint16_t*)a.v, a.v_sh, a.v_st, a.nk,
+                       a.key_bias, a.n_key_list, a.scale * kLog2e, (uint16_t*)a.out, a.lse, a.heads);
+    return hipGetLastError();
+  }
   if (a.dtype == FASTAR_BF16) {
     const int64_t nb = (a.nq + 63) / 64 * a.heads;
     dim3 grid((unsigned)(FASTAR_XCDS * xcd_span(nb)));
