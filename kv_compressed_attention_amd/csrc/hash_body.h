@@ -10,16 +10,15 @@
 namespace fastar {
 
 
+// the sum of squares of 8 bf16 values (two per dot step; it only feeds the
+// error bounds, which allow for its rounding)
 __device__ __forceinline__ float sumsq_bf16x8(uint4 u) {
   float s = 0.f;
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = __uint_as_float(w[i] << 16);
-    const float hi = __uint_as_float(w[i] & 0xFFFF0000u);
-    s = fmaf(lo, lo, s);
-    s = fmaf(hi, hi, s);
-  }
+  for (int i = 0; i < 4; ++i)
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]), __builtin_bit_cast(bf16x2_t, w[i]),
+                                        s, false);
   return s;
 }
 
@@ -303,9 +302,12 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
   lds_barrier();
   r2 += shfl_xor_f(r2, 16);
   r2 += shfl_xor_f(r2, 32);
-  float rnorm[4];
+  float rnorm[4], irn[4];  // the lane's four hyperplanes' norms and their reciprocals
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rnorm[i] = sqrtf(__shfl(r2, 4 * g + i, FASTAR_WAVE));
+  for (int i = 0; i < 4; ++i) {
+    rnorm[i] = sqrtf(__shfl(r2, 4 * g + i, FASTAR_WAVE));
+    irn[i] = rnorm[i] > 0.f ? 1.f / rnorm[i] : 0.f;
+  }
 
   const float kc = kcert<D>();
   for (int64_t tile = first; tile < total; tile += nwaves) {
@@ -343,7 +345,7 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
         amb |= fabsf(s) <= bound;
         if (s > 0.f) bits |= 1u << p;
         if (P == 2) {
-          const float dist = rnorm[i] > 0.f ? fabsf(s) / rnorm[i] : 0.f;
+          const float dist = fabsf(s) * irn[i];  // within 2^-22 relative of the quotient
           if (dist < nr.d1) {
             nr.d2 = nr.d1;
             nr.d1 = dist;
@@ -367,7 +369,8 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
     if (P == 2) {
       nearest_merge(nr, 16);
       nearest_merge(nr, 32);
-      // each distance is known to within kc*|x| (plus division rounding)
+      // each distance is known to within kc*|x| (plus the rounding of the
+      // reciprocal norm and of the product)
       const float err = 2.f * kc * xnorm + (nr.d1 + nr.d2) * 0x1p-20f + 0x1p-90f;
       if (nr.d2 - nr.d1 <= err) amb = 1;
     }
@@ -382,7 +385,7 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
       float dl[4], da[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dl[i] = (4 * g + i < nb) ? (rnorm[i] > 0.f ? fabsf(acc[i]) / rnorm[i] : 0.f) : INFINITY;
+        dl[i] = (4 * g + i < nb) ? fabsf(acc[i]) * irn[i] : INFINITY;
 #pragma unroll
       for (int g2 = 0; g2 < 4; ++g2)
 #pragma unroll
