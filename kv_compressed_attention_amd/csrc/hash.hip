@@ -166,9 +166,17 @@ hipError_t launch_hash_multi(HashJobs jobs, int dim, int dtype, const void* plan
   const int64_t tiles = hash_tiles(jobs, &js);
   if (js.count == 0) return hipSuccess;
   if (dtype == FASTAR_BF16) {
-    // one tile per wave (a wave with more loads the next tile's rows while
-    // it hashes one): the loads are spread over as many waves as possible
-    const int64_t blocks = (tiles + 3) / 4 < 8192 ? (tiles + 3) / 4 : 8192;
+    // tiles per wave: a wave with more loads the next tile's rows while it
+    // hashes one, and amortises its hyperplane set-up; but at least about
+    // 800 workgroups (three per CU) keep the loads spread.  Measured best:
+    // up to 4 with one probe, 2 with more (their per-row work is larger)
+    int max_p = 1;
+    for (int i = 0; i < js.count; ++i) max_p = js.j[i].P > max_p ? js.j[i].P : max_p;
+    int64_t tpw = tiles / (4 * 800);
+    const int64_t tpw_cap = max_p == 1 ? 4 : 2;
+    tpw = tpw < 1 ? 1 : (tpw > tpw_cap ? tpw_cap : tpw);
+    const int64_t want = (tiles + 4 * tpw - 1) / (4 * tpw);
+    const int64_t blocks = want < 8192 ? want : 8192;
     if (dim == 64)
       hipLaunchKernelGGL((hash_bf16_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, s, js,
                          (const uint16_t*)planes, n_bits, diag);
