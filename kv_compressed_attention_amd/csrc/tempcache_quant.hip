@@ -82,37 +82,37 @@ __device__ __forceinline__ int quant_elem<float>(float x, float m, int q) {
   return (int)__builtin_rint(((double)q * (double)x) / (double)m);
 }
 
-// 16 lanes per row (D / 16 elements each), 16 rows per workgroup; the
-// threads also clear the successor links and opener counts (mode 1)
+// 16 lanes per row (D / 16 elements each), 16 rows per workgroup; grid (row
+// blocks, tables, heads) (mode 0: one table of N rows), so that no thread
+// divides to find its row; the threads also clear the successor links and
+// opener counts (mode 1)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void tcq_encode_kernel(EncArgs e) {
   constexpr int EPL = D / 16;
   const int sub = threadIdx.x & 15;
   const int ntab = e.F + 1 + (e.qd ? e.F : 0);
-  const int64_t total = e.mode == 0 ? (int64_t)e.H * e.N : (int64_t)e.H * ntab * e.T;
-  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int h = blockIdx.z, t = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // the row within its table
   if (e.mode == 1) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = gid; i < (int64_t)e.H * e.F * e.T; i += stride) e.nextj[i] = -1;
-    for (int64_t i = gid; i < (int64_t)e.H * (e.nblk + 1); i += stride) {
-      const int h = (int)(i / (e.nblk + 1));
-      const int b = (int)(i - (int64_t)h * (e.nblk + 1));
-      e.ocnt[i] = b < e.nblk ? 0 : e.n_groups[h];
+    const int64_t blk = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int64_t gid = blk * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * gridDim.y * gridDim.z * blockDim.x;
+    for (int64_t j = gid; j < (int64_t)e.H * e.F * e.T; j += stride) e.nextj[j] = -1;
+    const int nob = e.H * (e.nblk + 1);
+    for (int64_t j = gid; j < nob; j += stride) {
+      const int hh = (int)j / (e.nblk + 1);
+      const int b = (int)j - hh * (e.nblk + 1);
+      e.ocnt[j] = b < e.nblk ? 0 : e.n_groups[hh];
     }
   }
-  if (r >= total) return;  // 16 whole lanes of a row
+  if (i >= (e.mode == 0 ? e.N : (int64_t)e.T)) return;  // 16 whole lanes of a row
+  // the row's index in the code table [H][tables][rows]
+  const int64_t r = e.mode == 0 ? (int64_t)h * e.N + i : ((int64_t)h * ntab + t) * e.T + i;
   const T* src = nullptr;
   bool valid = true;
   if (e.mode == 0) {
-    const int h = (int)(r / e.N);
-    const int64_t i = r - (int64_t)h * e.N;
     src = (const T*)e.x + (int64_t)h * e.sh + i * e.st;
   } else {
-    const int64_t per = (int64_t)ntab * e.T;
-    const int h = (int)(r / per);
-    const int t = (int)((r - (int64_t)h * per) / e.T);
-    const int i = (int)(r - (int64_t)h * per - (int64_t)t * e.T);
     if (t == 0) {
       const int g = e.frontier[(int64_t)h * e.T + i];
       valid = e.n_groups[h] > 0 && g >= 0 && g < e.cap;
@@ -610,8 +610,8 @@ hipError_t merge_quant_td(const fastar_cache_t& c, const fastar_tensor_t& kn, co
     e.qst = qn->stride_token;
   }
   const int ntab = F + 1 + (qn ? F : 0);
-  const int64_t rows = (int64_t)H * ntab * Tf;
-  hipLaunchKernelGGL((tcq_encode_kernel<T, D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, e);
+  hipLaunchKernelGGL((tcq_encode_kernel<T, D>), dim3((unsigned)((Tf + 15) / 16), (unsigned)ntab, (unsigned)H),
+                     dim3(256), 0, s, e);
   QMatchArgs ma{};
   ma.H = H;
   ma.T = Tf;
@@ -708,7 +708,7 @@ hipError_t launch_scalar_codes(const fastar_tensor_t& x, int bits, int8_t* codes
   e.N = x.tokens;
   e.codes = codes;
   e.norm2 = norm2;
-  const dim3 grid((unsigned)((rows + 15) / 16)), block(256);
+  const dim3 grid((unsigned)((x.tokens + 15) / 16), 1u, (unsigned)x.heads), block(256);
   if (x.dtype == FASTAR_BF16) {
     if (x.dim == 64) hipLaunchKernelGGL((tcq_encode_kernel<uint16_t, 64>), grid, block, 0, s, e);
     else hipLaunchKernelGGL((tcq_encode_kernel<uint16_t, 128>), grid, block, 0, s, e);
