@@ -59,6 +59,7 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
   const float kc = kcert<D>();
   const int64_t total = (int64_t)H * N;
   // the loop is uniform per wave so that the wave can settle rows together
+  HashCounts hc;
   for (int64_t base = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63); base < total;
        base += (int64_t)gridDim.x * blockDim.x) {
     const int64_t idx = base + lane_id();
@@ -140,10 +141,11 @@ __global__ __launch_bounds__(256) void hash_f32_kernel(
       ab &= ab - 1;
       if (lane_id() == r)
         for (int d = 0; d < D; ++d) sxr[wv][d] = xr[d];
-      hash_fixup_row<float, D>(sxr[wv], &sp[0][0], D, bucket + (base + r) * P, P, nb, diag, ex[wv],
+      hash_fixup_row<float, D>(sxr[wv], &sp[0][0], D, bucket + (base + r) * P, P, nb, hc, ex[wv],
                                de[wv]);
     }
   }
+  hash_counts_flush(hc, diag);
 }
 
 template <int D>

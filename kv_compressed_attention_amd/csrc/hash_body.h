@@ -22,6 +22,20 @@ __device__ __forceinline__ float sumsq_bf16x8(uint4 u) {
   return s;
 }
 
+// a wave's counts of the diag events (wave-uniform), added to the device
+// counters once when its rows are done (one atomic per counter, not one per
+// event: a wave that waited for such an atomic before its next tile's rows
+// stalled)
+struct HashCounts {
+  uint32_t rows = 0u, signs = 0u, unresolved = 0u;
+};
+__device__ __forceinline__ void hash_counts_flush(const HashCounts& c, fastar_diag_t* __restrict__ diag) {
+  if (!diag || lane_id() != 0) return;
+  if (c.rows) atomicAdd(&diag->hash_fallback_rows, c.rows);
+  if (c.signs) atomicAdd(&diag->hash_exact_signs, c.signs);
+  if (c.unresolved) atomicAdd(&diag->unresolved, c.unresolved);
+}
+
 // best / second-best hyperplane distance, merged across lanes
 struct Nearest {
   float d1, d2;
@@ -79,7 +93,7 @@ __device__ __forceinline__ double sum4_d(double v) {
 // DE (32 doubles of LDS).
 template <typename T, int D>
 __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t* __restrict__ o, int P,
-                               int nb, fastar_diag_t* __restrict__ diag, double* E, double* DE) {
+                               int nb, HashCounts& hc, double* E, double* DE) {
   constexpr int DS = D / 4;
   const int lane = lane_id();
   const int sl = lane >> 4, p = lane & 15;
@@ -118,8 +132,8 @@ __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t
       for (int d = 0; d < D; ++d)
         m = grow_expansion(E, m, (double)Elem<T>::load(xr, d) * (double)Elem<T>::load(rp, d));
       sx = expansion_sign(E, m);
-      if (diag) atomicAdd(&diag->hash_exact_signs, 1u);
     }
+    ++hc.signs;
     sx = __shfl(sx, src, FASTAR_WAVE);
     if (p == src) sg = sx;
   }
@@ -155,11 +169,9 @@ __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t
       }
       o[r + 1] = (int32_t)(bits ^ (1u << jb));
     }
-    if (diag) {
-      atomicAdd(&diag->hash_fallback_rows, 1u);
-      if (unresolved) atomicAdd(&diag->unresolved, 1u);
-    }
   }
+  ++hc.rows;
+  if (ballot64(unresolved) != 0ull) ++hc.unresolved;
 }
 
 // Ranks of a row's hyperplane distances (ascending, ties to the smaller
@@ -310,6 +322,7 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
   }
 
   const float kc = kcert<D>();
+  HashCounts hc;
   for (int64_t tile = first; tile < total; tile += nwaves) {
     const Where w = where(tile);
     // the next tile's rows load while this one is hashed
@@ -421,11 +434,12 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
         for (int c = 0; c < NC; ++c) *reinterpret_cast<uint4*>(&sxr[wv][32 * c + 8 * g]) = xu[c];
       }
       hash_fixup_row<uint16_t, D>(sxr[wv], spl, kPst, w.bucket + ((int64_t)w.h * w.N + w.r0 + r) * P,
-                                  P, nb, diag, ex[wv], de[wv]);
+                                  P, nb, hc, ex[wv], de[wv]);
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) xu[c] = xn[c];
   }
+  hash_counts_flush(hc, diag);
 }
 
 
