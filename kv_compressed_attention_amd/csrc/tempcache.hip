@@ -598,6 +598,10 @@ struct SegCtx {
   int nk, f;            // keys that step 2 compares; the frame
   float tau, e;
   fastar_diag_t* diag;
+  // the wave's float64 decisions and the ones float64 could not certify
+  // (wave-uniform), added to diag once at the end: an atomic per event that
+  // the wave then waits for stalls it
+  mutable uint32_t nfb = 0u, nunres = 0u;
   // candidate row: the frontier group's representative (f == 0), else the
   // frame f - 1 key
   __device__ __forceinline__ const T* cand_row(int, int i, int gr) const {
@@ -676,11 +680,11 @@ __device__ __forceinline__ void decide(const SegCtx<T, D>& x, const Top2<float>&
         }
       }
     }
+    ++x.nfb;
+    const bool thr_sure = ex1 || fabs(u.c1 - (double)x.tau) > e64;
+    const bool sure = thr_sure && (u.c1 < (double)x.tau || near <= 1 || near == near_exact);
+    if (!sure) ++x.nunres;
     if (lane == src) {
-      if (x.diag) atomicAdd(&x.diag->merge_fallbacks, 1u);
-      const bool thr_sure = ex1 || fabs(u.c1 - (double)x.tau) > e64;
-      const bool sure = thr_sure && (u.c1 < (double)x.tau || near <= 1 || near == near_exact);
-      if (!sure && x.diag) atomicAdd(&x.diag->unresolved, 1u);
       best = u.best;
       prop = u.c1 >= (double)x.tau;
       c1 = (float)u.c1;
@@ -860,11 +864,9 @@ __device__ __forceinline__ bool resolve_keys(const SegCtx<T, D>& x, int self, in
       if (fabs(dd - dj) <= 2.0 * e64 && !(cd.exact && cj.exact)) unres = true;
       if (dd > dj || (dd == dj && j2 < js)) w = false;
     }
-    if (lane == src) {
-      if (x.diag) atomicAdd(&x.diag->merge_fallbacks, 1u);
-      if (unres && x.diag) atomicAdd(&x.diag->unresolved, 1u);
-      win = w;
-    }
+    ++x.nfb;
+    if (unres) ++x.nunres;
+    if (lane == src) win = w;
   }
   return win;
 }
@@ -1116,6 +1118,10 @@ __global__ __launch_bounds__(256, 4) void tc_match_kernel(
     match_group<T, D, 1>(x, a, h, p0, p1, c0, c1, frontier, lds);
   else
     match_group<T, D, 0>(x, a, h, p0, p1, c0, c1, frontier, lds);
+  if (diag && lane_id() == 0) {
+    if (x.nfb) atomicAdd(&diag->merge_fallbacks, x.nfb);
+    if (x.nunres) atomicAdd(&diag->unresolved, x.nunres);
+  }
 }
 
 // The float64 quotient s / n rounded once to the storage dtype T (to nearest,
