@@ -411,8 +411,10 @@ __global__ __launch_bounds__(256) void tcq_match_kernel(QMatchArgs a) {
       amb = true;
     }
   }
-  // keys the float32 bound cannot decide: the whole wave, exactly
+  // keys the float32 bound cannot decide: the whole wave, exactly (counted
+  // per wave and added to diag once)
   uint64_t ab = ballot64(amb);
+  const unsigned nfb = (unsigned)__popcll(ab);
   while (ab) {
     const int src = __builtin_ctzll(ab);
     ab &= ab - 1;
@@ -444,13 +446,13 @@ __global__ __launch_bounds__(256) void tcq_match_kernel(QMatchArgs a) {
       }
     }
     if (lane == src) {
-      if (a.diag) atomicAdd(&a.diag->merge_fallbacks, 1u);
       const bool ok = bi >= 0 && cos_at_least(bd, (uint64_t)ns * (uint64_t)bn, a.tau);
       prop = ok ? bi : -1;
       dot = bd;
       pc = (bn > 0 && ns > 0) ? (float)((double)bd / sqrt((double)ns * (double)bn)) : 0.f;
     }
   }
+  if (a.diag && lane == 0 && nfb) atomicAdd(&a.diag->merge_fallbacks, nfb);
   if (own) {
     if (prop >= 0 && !amb) dot = code_dot<D>(kc + (int64_t)key * D, cc + (int64_t)prop * D);
     const int64_t o = ((int64_t)h * a.F + f) * T + key;
