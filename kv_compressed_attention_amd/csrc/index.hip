@@ -6,9 +6,9 @@
 // id (with several probes, the smallest of the item's probe buckets), ties in
 // token order.
 //
-// 3..14 bits take a single stable counting pass (index_direct.h), a head
-// split over up to 8 workgroups.  Anything else (0..2 or 15 bits, or 14 bits
-// past 65535 items) falls back to one workgroup (16 waves) per head running
+// 3..15 bits take a single stable counting pass (index_direct.h): up to 12
+// bits a head split by items over up to 8 workgroups, from 13 bits by bucket
+// ranges.  0..2 bits fall back to one workgroup (16 waves) per head running
 // an LSD radix sort with 8-bit digits.
 // Each wave owns a contiguous slice of the input and walks it 64 items at a
 // time in order; items with equal digits in a 64-item group are matched with
@@ -291,13 +291,22 @@ __global__ __launch_bounds__(kDirectThreads) void bucket_index_direct_kernel(
     int xstage) {
   extern __shared__ int4 lds4[];
   const int nparts = (int)gridDim.x - xparts;
-  if ((int)blockIdx.x >= nparts) {
-    direct_index_body<NBITS, WIDE>(blockIdx.y, blockIdx.x - nparts, xparts, xj.bucket, xj.P, xj.n,
-                                   nullptr, xj.offsets, xj.perm, xstage, lds4);
-    return;
+  if constexpr (NBITS >= kRangeMinBits) {
+    if ((int)blockIdx.x >= nparts) {
+      range_index_body<NBITS, WIDE>(blockIdx.y, blockIdx.x - nparts, xparts, xj.bucket, xj.P, xj.n, nullptr,
+                                    xj.offsets, xj.perm, lds4);
+      return;
+    }
+    range_index_body<NBITS, WIDE>(blockIdx.y, blockIdx.x, nparts, bucket, P, n, n_valid, offsets, perm, lds4);
+  } else {
+    if ((int)blockIdx.x >= nparts) {
+      direct_index_body<NBITS, WIDE>(blockIdx.y, blockIdx.x - nparts, xparts, xj.bucket, xj.P, xj.n,
+                                     nullptr, xj.offsets, xj.perm, xstage, lds4);
+      return;
+    }
+    direct_index_body<NBITS, WIDE>(blockIdx.y, blockIdx.x, nparts, bucket, P, n, n_valid, offsets, perm,
+                                   stage, lds4);
   }
-  direct_index_body<NBITS, WIDE>(blockIdx.y, blockIdx.x, nparts, bucket, P, n, n_valid, offsets, perm,
-                                 stage, lds4);
 }
 
 // counter width of a direct launch of n items (and an extra job's n_extra)
@@ -322,9 +331,9 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
   if (direct_index_supported(n, n_probes, n_bits, with_x ? extra->n : 0, with_x ? extra->P : 1)) {
     const bool wide = direct_wide(n, with_x ? extra->n : 0);
     int stage, xstage = 0;
-    const int parts = direct_index_parts(n);
+    const int parts = direct_index_parts(n, n_bits, wide);
     size_t lds = direct_index_lds(n, n_bits, wide, parts, &stage);
-    const int xparts = with_x ? direct_index_parts(extra->n) : 0;
+    const int xparts = with_x ? direct_index_parts(extra->n, n_bits, wide) : 0;
     if (with_x) lds = std::max(lds, direct_index_lds(extra->n, n_bits, wide, xparts, &xstage));
     const IndexJob xj = with_x ? *extra : IndexJob{nullptr, 0, n_bits, 1, nullptr, nullptr};
     const dim3 grid(parts + xparts, heads), block(kDirectThreads);
@@ -339,10 +348,7 @@ hipError_t launch_bucket_index(const int32_t* bucket, int heads, int64_t n, int 
     switch (n_bits) {
       FASTAR_DIRECT(3) FASTAR_DIRECT(4) FASTAR_DIRECT(5) FASTAR_DIRECT(6) FASTAR_DIRECT(7)
       FASTAR_DIRECT(8) FASTAR_DIRECT(9) FASTAR_DIRECT(10) FASTAR_DIRECT(11) FASTAR_DIRECT(12)
-      FASTAR_DIRECT(13)
-      case 14:  // 32-bit counters do not fit at 14 bits (never chosen)
-        FASTAR_DIRECT_W(14, false);
-        break;
+      FASTAR_DIRECT(13) FASTAR_DIRECT(14) FASTAR_DIRECT(15)
     }
 #undef FASTAR_DIRECT
 #undef FASTAR_DIRECT_W

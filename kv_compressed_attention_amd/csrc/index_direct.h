@@ -8,7 +8,7 @@
 
 namespace fastar {
 
-// A single stable counting pass for 3..14 bits, any probe count (the sort
+// A single stable counting pass for 3..12 bits, any probe count (the sort
 // key is the smallest of an item's probe buckets), any item count below 2^31 that the
 // counters allow.  Per-wave bucket counters (one row of 2^b per scattering
 // wave) sit in LDS: 16-bit while a head has at most 65535 items, 32-bit
@@ -36,7 +36,12 @@ constexpr int kDirectThreads = kDirectWaves * FASTAR_WAVE;
 // waves that scatter a part's slice when a head has several parts, at most
 constexpr int kDirectPartWaves = 8;
 constexpr int kDirectMinBits = 3;
-constexpr int kDirectMaxBits = 14;
+constexpr int kDirectMaxBits = 15;
+// 13 bits and more: the parts of a head split its buckets, not its items
+// (range_index_body); the counter rows of a part then take 64 KB of LDS, so
+// that an index workgroup fits on a CU beside other launches' workgroups
+constexpr int kRangeMinBits = 13;
+constexpr int kRangeRowBytes = 64 * 1024 / 16;  // per scattering wave
 // 16-bit counters up to this many items per head
 constexpr int64_t kDirectNarrowItems = 65535;
 // parts per head: about this many items each, at most kDirectMaxParts
@@ -65,8 +70,11 @@ __host__ __device__ inline DirectShape direct_shape(int n_bits, bool wide, int n
 }
 // 32-bit counters for n items
 inline bool direct_index_wide(int64_t n) { return n > kDirectNarrowItems; }
+// buckets of one part of a head in range mode
+__host__ __device__ constexpr int range_part_buckets(bool wide) { return kRangeRowBytes / (wide ? 4 : 2); }
 // The parts (workgroups) per head for n items
-inline int direct_index_parts(int64_t n) {
+inline int direct_index_parts(int64_t n, int n_bits, bool wide) {
+  if (n_bits >= kRangeMinBits) return (1 << n_bits) / range_part_buckets(wide);
   const int64_t p = (n + kDirectPartItems - 1) / kDirectPartItems;
   return p < 1 ? 1 : (p > kDirectMaxParts ? kDirectMaxParts : (int)p);
 }
@@ -75,7 +83,8 @@ inline int direct_index_parts(int64_t n) {
 inline bool direct_index_fits_wide(int64_t n, int n_probes, int n_bits, bool wide) {
   if (n_probes < 1 || n_probes > kMaxProbes || n_bits < kDirectMinBits || n_bits > kDirectMaxBits) return false;
   if (n >= ((int64_t)1 << 31) || (!wide && direct_index_wide(n))) return false;
-  return direct_shape(n_bits, wide, direct_index_parts(n)).sw >= 1;
+  if (n_bits >= kRangeMinBits) return true;
+  return direct_shape(n_bits, wide, direct_index_parts(n, n_bits, wide)).sw >= 1;
 }
 inline bool direct_index_fits(int64_t n, int n_probes, int n_bits) {
   return direct_index_fits_wide(n, n_probes, n_bits, direct_index_wide(n));
@@ -83,6 +92,10 @@ inline bool direct_index_fits(int64_t n, int n_probes, int n_bits) {
 // LDS bytes the direct index of n items in nparts parts needs, and whether it
 // stages the permutation there
 inline size_t direct_index_lds(int64_t n, int n_bits, bool wide, int nparts, int* stage) {
+  if (n_bits >= kRangeMinBits) {
+    *stage = 0;
+    return (size_t)kDirectWaves * kRangeRowBytes;
+  }
   const DirectShape sh = direct_shape(n_bits, wide, nparts);
   const size_t counters = (size_t)sh.rows * ((size_t)1 << n_bits) * (wide ? 4u : 2u);
   *stage = nparts == 1 && counters + (size_t)n * sizeof(int32_t) <= kDirectLds ? 1 : 0;
@@ -316,6 +329,155 @@ __device__ __forceinline__ void direct_index_body(int h, int part, int nparts,
   if (stage) {
     lds_barrier();
     for (int p = threadIdx.x; p < nh; p += kDirectThreads) ph[p] = pst[p];
+  }
+}
+
+// Range mode (13..15 bits): part `part` of nparts of head h owns the buckets
+// [part R, part R + R), R = range_part_buckets(WIDE), and reads all of the
+// head's items: every wave counts the items of its contiguous slice that fall
+// in the range (one LDS counter row per wave) and the ones below it; a scan
+// over (bucket, wave) from the count below gives each wave its base in each
+// bucket and the range's offsets; then each wave walks its slice in order
+// and places its in-range items (ballot ranks among equal buckets), so the
+// sort is stable.  No exchange between the parts.
+template <int NBITS, bool WIDE>
+__device__ __forceinline__ void range_index_body(int h, int part, int nparts,
+                                                 const int32_t* __restrict__ bucket, int P, int64_t n,
+                                                 const int32_t* __restrict__ n_valid,
+                                                 int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ perm, int4* lds4) {
+  constexpr int nbk = 1 << NBITS;
+  constexpr int R = range_part_buckets(WIDE);
+  constexpr int RB = NBITS - (WIDE ? 10 : 11);  // bits of the part index
+  static_assert(R * (1 << RB) == nbk && R % kDirectThreads == 0 || R < kDirectThreads, "range split");
+  constexpr int BPT = R / kDirectThreads > 0 ? R / kDirectThreads : 1;  // buckets per thread
+  using CT = typename std::conditional<WIDE, uint32_t, uint16_t>::type;
+  __shared__ int wtot[kDirectWaves];
+  __shared__ int wbelow[kDirectWaves];
+  int nh = (int)n;
+  if (n_valid) {
+    const int v = n_valid[h];
+    nh = v < 0 ? 0 : (v < nh ? v : nh);
+  }
+  CT* cnt = reinterpret_cast<CT*>(lds4);  // [kDirectWaves][R]
+  uint32_t* cnt32 = reinterpret_cast<uint32_t*>(lds4);
+  const uint32_t bmask = (uint32_t)nbk - 1u;
+  const uint32_t lo = (uint32_t)part * R;
+  const int32_t* ids = bucket + (int64_t)h * n * P;
+  int32_t* ph = perm + (int64_t)h * n;
+  int32_t* off = offsets + (int64_t)h * (nbk + 1);
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  if (nh == 0) {  // the whole workgroup: every bucket is empty
+    for (int B = threadIdx.x; B < R; B += kDirectThreads) off[lo + B] = 0;
+    if (part == nparts - 1 && threadIdx.x == 0) off[nbk] = 0;
+    return;
+  }
+  auto inc = [&](int row, uint32_t b) {
+    const int i = row * R + (int)b;
+    if (WIDE) atomicAdd(&cnt32[i], 1u);
+    else atomicAdd(&cnt32[i >> 1], 1u << (16 * (b & 1u)));
+  };
+  // the wave's slice [wbeg, wend), walked in tiles of kTile ids per lane
+  const int chunk = (nh + kDirectWaves - 1) / kDirectWaves;
+  const int wbeg = wave * chunk < nh ? wave * chunk : nh;
+  const int wend = wbeg + chunk < nh ? wbeg + chunk : nh;
+  constexpr int kTile = 8;
+  const int last = nh - 1;
+  uint32_t b[kTile];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      const int i = t0 + r * FASTAR_WAVE + lane;
+      const uint32_t v = index_key(ids, i < last ? i : last, P) & bmask;
+      b[r] = i < wend ? v : 0xFFFFFFFFu;
+    }
+  };
+  load_tile(wbeg);
+  for (int i = threadIdx.x; i < kDirectWaves * R * (int)sizeof(CT) / 16; i += kDirectThreads)
+    lds4[i] = make_int4(0, 0, 0, 0);
+  lds_barrier();
+  int below = 0;  // this lane's items below the range
+  for (int t0 = wbeg; t0 < wend;) {
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      if (b[r] == 0xFFFFFFFFu) continue;
+      const uint32_t d = b[r] - lo;
+      if (d < (uint32_t)R) inc(wave, d);
+      else if (b[r] < lo) ++below;
+    }
+    t0 += kTile * FASTAR_WAVE;
+    if (t0 >= wend) break;
+    load_tile(t0);
+  }
+  below = wave_sum_dpp(below);
+  if (lane == 0) wbelow[wave] = below;
+  lds_barrier();
+  // the items below the range, all waves
+  int base0 = lane < kDirectWaves ? wbelow[lane] : 0;
+  base0 = wave_sum_dpp(base0);
+  // exclusive scan over (bucket, wave): thread t owns buckets BPT t .. + BPT
+  const int t = threadIdx.x;
+  const bool owner = t * BPT < R;
+  uint32_t tot[BPT];
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    tot[e] = 0u;
+    if (owner)
+      for (int w = 0; w < kDirectWaves; ++w) tot[e] += (uint32_t)cnt[w * R + t * BPT + e];
+  }
+  uint32_t local = 0u;
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) local += tot[e];
+  const uint32_t incl = wave_incl_scan_dpp(local);
+  if (lane == FASTAR_WAVE - 1) wtot[wave] = (int)incl;
+  lds_barrier();
+  const int wt = lane < kDirectWaves ? wtot[lane] : 0;
+  uint32_t run = (uint32_t)base0 + incl - local + (uint32_t)wave_sum_dpp(lane < wave ? wt : 0);
+  if (owner) {
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      off[lo + t * BPT + e] = (int)run;
+      // each wave's base within the bucket (replacing the wave's count)
+      uint32_t bw = run;
+      for (int w = 0; w < kDirectWaves; ++w) {
+        const uint32_t c = (uint32_t)cnt[w * R + t * BPT + e];
+        cnt[w * R + t * BPT + e] = (CT)bw;
+        bw += c;
+      }
+      run += tot[e];
+    }
+    if (part == nparts - 1 && t * BPT + BPT == R) off[nbk] = (int)run;
+  }
+  lds_barrier();
+  // stable scatter of the in-range items: each wave walks its slice in order
+  for (int t0 = wbeg; t0 < wend; t0 += kTile * FASTAR_WAVE) {
+    load_tile(t0);
+#pragma unroll
+    for (int r = 0; r < kTile; ++r) {
+      if (t0 + r * FASTAR_WAVE >= wend) break;  // uniform
+      const int i = t0 + r * FASTAR_WAVE + lane;
+      const uint32_t d = b[r] - lo;  // past the end: 0xFFFFFFFF - lo, not in range
+      const bool inr = d < (uint32_t)R;
+      // lanes of this row with the same bucket: in range, and agreeing on the
+      // bits of d
+      uint64_t peers = ballot64(inr);
+      if (peers == 0ull) continue;  // uniform
+#pragma unroll
+      for (int k = 0; k < NBITS - RB; ++k) {
+        const uint32_t bit = (d >> k) & 1u;
+        const uint64_t bk = ballot64(bit != 0u);
+        peers &= ~(bk ^ (0ull - (uint64_t)bit));
+      }
+      if (inr) {
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+        const int pos = (int)cnt[wave * R + (int)d] + rank;
+        ph[pos] = (int32_t)i;
+        // the lowest peer (rank 0) advances the counter
+        if (rank == 0) cnt[wave * R + (int)d] = (CT)(pos + __popcll(peers));
+      }
+    }
   }
 }
 

@@ -143,12 +143,14 @@ def test_hash_strided_input(fa):
 
 @pytest.mark.parametrize("n,b,P", [(5000, 12, 1), (4096, 14, 2), (100, 3, 1), (0, 4, 1), (65535, 12, 1),
                                    (3100, 3, 1), (12289, 9, 1), (1537, 12, 1),
-                                   # the counting pass at 13-14 bits, two probes, and
-                                   # 32-bit counters past 65535 items
+                                   # the counting pass by bucket ranges at 13-15 bits, two
+                                   # probes, and 32-bit counters past 65535 items
                                    (8192, 14, 2), (32768, 14, 1), (1000, 14, 1), (1, 14, 2),
                                    (20000, 13, 2), (70000, 13, 1), (93600, 12, 1), (66000, 3, 1),
+                                   (5000, 15, 1), (70000, 14, 1), (65535, 15, 2), (70000, 15, 1),
+                                   (40, 13, 1),
                                    # the radix fallback
-                                   (5000, 15, 1), (3000, 2, 2), (70000, 14, 1)])
+                                   (3000, 2, 2)])
 def test_bucket_index_of_given_ids(fa, n, b, P):
     rng = np.random.default_rng(n + b)
     H = 3
@@ -169,7 +171,7 @@ def test_bucket_index_of_given_ids(fa, n, b, P):
         assert np.array_equal(perm[h, :nv], r_perm)
 
 
-@pytest.mark.parametrize("n,b", [(70000, 12), (65535, 14), (9000, 13)])
+@pytest.mark.parametrize("n,b", [(70000, 12), (65535, 14), (9000, 13), (66000, 15)])
 def test_bucket_index_one_full_bucket(fa, n, b):
     # every item in one bucket: its count reaches n (past 16 bits for 70000)
     H = 2
