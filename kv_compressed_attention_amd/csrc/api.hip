@@ -95,6 +95,11 @@ fastar_status_t hash_multi_check(int count, const fastar_tensor_t* const* x, con
   }
   if (*any && n_bits > 0 && (!planes || !aligned16(planes)))
     return fail(FASTAR_ERR_INVALID, "planes must be a non-null, 16-byte aligned pointer");
+  // the bf16 launch numbers its 16-row tiles with 32-bit integers
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) tiles += (int64_t)x[i]->heads * ((x[i]->tokens + 15) / 16);
+  if (tiles >= (int64_t)1 << 31)
+    return fail(FASTAR_ERR_UNSUPPORTED, "more than 2^31 tiles of 16 rows in one call");
   return FASTAR_OK;
 }
 
@@ -785,11 +790,12 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
                      fastar::direct_index_supported(c->capacity, 1, c->n_bits, a->q->tokens, a->n_probes);
   fastar::MergeWs mw = merge_carve(c, a->n_frames, ws);
   if (fused) mw.also_index = &qj;
-  // bf16 queries with the LSH match are hashed by extra workgroups of the
-  // merge's match launch (only their index, after the merge, and the
-  // attention need them)
+  // bf16 queries with the LSH match and at most two probes are hashed by
+  // extra workgroups of the merge's match launch (only their index, after
+  // the merge, and the attention need them)
   const bool ride = match == FASTAR_MATCH_LSH && a->q->dtype == FASTAR_BF16 && c->dtype == FASTAR_BF16 &&
-                    a->q->dim == c->dim && c->heads > 0 && (int64_t)a->q->heads * a->q->tokens > 0;
+                    a->q->dim == c->dim && a->n_probes <= 2 && c->heads > 0 &&
+                    (int64_t)a->q->heads * a->q->tokens > 0;
   AuxBranch ab;
   if (c->heads > 0 && (int64_t)a->q->heads * a->q->tokens > 0 && (prompt || !ride) && aux_branch(stream, &ab)) {
     // Two branches.  The library's second stream prunes the prompt and runs
@@ -879,13 +885,13 @@ fastar_status_t fastar_chunk(const fastar_chunk_t* a, void* ws, size_t ws_bytes,
   }
 
   // One stream (the second branch unavailable): launches in order.  bf16
-  // queries are hashed by extra workgroups of the merge's match launch (only
-  // their index, after the merge, and the attention need them); the keys
-  // first, on their own.
+  // queries with at most two probes are hashed by extra workgroups of the
+  // merge's match launch (only their index, after the merge, and the
+  // attention need them); the keys first, on their own.
   fastar::HashJobs qjobs;
   qjobs.count = 0;
   if (match == FASTAR_MATCH_LSH && a->q->dtype == FASTAR_BF16 && c->dtype == FASTAR_BF16 &&
-      a->q->dim == c->dim && c->heads > 0 && (int64_t)a->q->heads * a->q->tokens > 0) {
+      a->q->dim == c->dim && a->n_probes <= 2 && c->heads > 0 && (int64_t)a->q->heads * a->q->tokens > 0) {
     qjobs.count = 1;
     qjobs.j[0] = jobs.j[0];
     for (int i = 1; i < jobs.count; ++i) jobs.j[i - 1] = jobs.j[i];

@@ -12,11 +12,14 @@
 //
 // A float32 projection is trusted only when its magnitude exceeds an a-priori
 // bound on its rounding error, Kd * |x| * |r_j| with Kd = d * 2^-22 (four times
-// the worst case of a d-term float32 accumulation of exact products).  A row
-// with any untrusted sign or second-probe choice is re-evaluated on the spot
-// by its whole wave in float64 (products of bf16/fp32 values are exact there),
-// and a sign float64 still cannot certify is settled exactly with an
-// error-free expansion sum.
+// the worst case of a d-term float32 accumulation of exact products).  With
+// bf16 inputs and one or two probes, the untrusted projections of a tile (a
+// sign, or the distances that may be a row's smallest) are re-evaluated in
+// float64 together (products of bf16 values are exact there); a row that
+// still cannot be certified, every uncertain row with more probes and every
+// uncertain fp32 row are re-evaluated whole by their wave in float64, and a
+// sign float64 still cannot certify is settled exactly with an error-free
+// expansion sum.
 
 #include "common.h"
 #include "hash_body.h"
@@ -27,11 +30,11 @@ namespace fastar {
 namespace {
 
 // One workgroup of 256 threads per hash_bf16_body block.
-template <int D>
+template <int D, int PT>
 __global__ __launch_bounds__(256, 4) void hash_bf16_kernel(HashJobs jobs, const uint16_t* __restrict__ planes,
                                                         int nb, fastar_diag_t* __restrict__ diag) {
   __shared__ __attribute__((aligned(16))) char lds[hash_bf16_lds<D>()];
-  hash_bf16_body<D>(jobs, planes, nb, diag, blockIdx.x, gridDim.x, lds);
+  hash_bf16_body<D, PT>(jobs, planes, nb, diag, blockIdx.x, gridDim.x, lds);
 }
 
 // PT: 1, 2, or 3 for any P >= 3 (given by P)
@@ -171,20 +174,16 @@ hipError_t launch_hash_multi(HashJobs jobs, int dim, int dtype, const void* plan
     // tiles per wave: a wave with more loads the next tile's rows while it
     // hashes one, and amortises its hyperplane set-up; but at least about
     // 800 workgroups (three per CU) keep the loads spread.  Measured best:
-    // up to 4 with one probe, 2 with more (their per-row work is larger)
-    int max_p = 1;
-    for (int i = 0; i < js.count; ++i) max_p = js.j[i].P > max_p ? js.j[i].P : max_p;
+    // up to 4
     int64_t tpw = tiles / (4 * 800);
-    const int64_t tpw_cap = max_p == 1 ? 4 : 2;
-    tpw = tpw < 1 ? 1 : (tpw > tpw_cap ? tpw_cap : tpw);
+    tpw = tpw < 1 ? 1 : (tpw > 4 ? 4 : tpw);
     const int64_t want = (tiles + 4 * tpw - 1) / (4 * tpw);
     const int64_t blocks = want < 8192 ? want : 8192;
-    if (dim == 64)
-      hipLaunchKernelGGL((hash_bf16_kernel<64>), dim3((unsigned)blocks), dim3(256), 0, s, js,
-                         (const uint16_t*)planes, n_bits, diag);
-    else
-      hipLaunchKernelGGL((hash_bf16_kernel<128>), dim3((unsigned)blocks), dim3(256), 0, s, js,
-                         (const uint16_t*)planes, n_bits, diag);
+    if (tiles >= (int64_t)1 << 31) return hipErrorInvalidValue;  // tiles are numbered in 32 bits
+    const bool two = hash_probe_class(js) == 2;
+    auto kern = dim == 64 ? (two ? hash_bf16_kernel<64, 2> : hash_bf16_kernel<64, 3>)
+                          : (two ? hash_bf16_kernel<128, 2> : hash_bf16_kernel<128, 3>);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, js, (const uint16_t*)planes, n_bits, diag);
     return hipGetLastError();
   }
   for (int i = 0; i < js.count; ++i) {

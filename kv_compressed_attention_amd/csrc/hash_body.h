@@ -199,10 +199,17 @@ __device__ __forceinline__ bool probe_ranks(const float* dl, const float* da, in
   return amb;
 }
 
-// LDS bytes of hash_bf16_body<D>
+// (row, hyperplane) projections a wave re-evaluates together in float64
+// for one tile (hash_bf16_body, one and two probes)
+constexpr int kRefinePairs = 64;
+// a row with more uncertain hyperplanes than this takes the whole-row pass
+constexpr int kRefineRowMax = 8;
+
+// LDS bytes of hash_bf16_body<D, PT>
 template <int D>
 constexpr size_t hash_bf16_lds() {
-  return 4 * (D + 2 + 32) * sizeof(double) + 16 * (D + 8) * sizeof(uint16_t) + 4 * D * sizeof(uint16_t);
+  return 4 * (D + 2 + 32 + 2 * kRefinePairs + 16) * sizeof(double) + 16 * (D + 8) * sizeof(uint16_t) +
+         4 * 16 * D * sizeof(uint16_t) + 4 * kRefinePairs + 4 * sizeof(uint32_t);
 }
 
 // The jobs with rows, with tile_end filled in (16-row tiles in job order);
@@ -221,32 +228,95 @@ inline int64_t hash_tiles(const HashJobs& jobs, HashJobs* js) {
   return tiles;
 }
 
+// the probe class of a launch's jobs: 2 when every job has at most two
+// probes, else 3 (the template argument PT of hash_bf16_body)
+__host__ __device__ inline int hash_probe_class(const HashJobs& js) {
+  int pt = 2;
+  for (int i = 0; i < js.count; ++i) pt = js.j[i].P > 2 ? 3 : pt;
+  return pt;
+}
+
+// v summed over the 16 lanes of its DPP row (the same value in all of them:
+// every step adds a lane's value and its partner's, which commutes)
+__device__ __forceinline__ double row16_sum_d(double v) {
+  auto step = [](double x, auto dpp) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)dpp((int)(uint32_t)u), hi = (uint32_t)dpp((int)(uint32_t)(u >> 32));
+    return x + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+  };
+  v = step(v, [](int w) { return __builtin_amdgcn_update_dpp(w, w, 0xB1, 0xF, 0xF, false); });   // quad_perm [1,0,3,2]
+  v = step(v, [](int w) { return __builtin_amdgcn_update_dpp(w, w, 0x4E, 0xF, 0xF, false); });   // quad_perm [2,3,0,1]
+  v = step(v, [](int w) { return __builtin_amdgcn_update_dpp(w, w, 0x141, 0xF, 0xF, false); });  // row_half_mirror
+  v = step(v, [](int w) { return __builtin_amdgcn_update_dpp(w, w, 0x140, 0xF, 0xF, false); });  // row_mirror
+  return v;
+}
+
+// the value of lane l ^ 32 (as xor16_word)
+__device__ __forceinline__ uint32_t xor32_word(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return r[0] == v ? r[1] : r[0];
+}
+// Nearest of lane ^ 16 (X = 16) or lane ^ 32 (X = 32) merged in, without
+// LDS: the same (d1, d2, j1) in both lanes of a pair
+template <int X>
+__device__ __forceinline__ void nearest_merge_pl(Nearest& a) {
+  auto other = [](uint32_t w) { return X == 16 ? xor16_word(w) : xor32_word(w); };
+  const float pd1 = __uint_as_float(other(__float_as_uint(a.d1)));
+  const float pd2 = __uint_as_float(other(__float_as_uint(a.d2)));
+  const int pj1 = (int)other((uint32_t)a.j1);
+  const bool take = (pd1 < a.d1) | ((pd1 == a.d1) & (pj1 < a.j1));
+  const float nd2 = take ? (pd2 < a.d1 ? pd2 : a.d1) : (pd1 < a.d2 ? pd1 : a.d2);
+  a.d1 = take ? pd1 : a.d1;
+  a.j1 = take ? pj1 : a.j1;
+  a.d2 = nd2;
+}
+
 // Workgroup `block` of nblocks (256 threads) of a bf16 hashing: one wave per
 // tile of 16 rows of one of the jobs' tensors (tiles of tensor i are numbered
-// from jobs.tile_end[i - 1]; tile_end filled by hash_tiles); the first tile's
-// rows and the hyperplanes are requested together.  256 threads.  lds:
-// hash_bf16_lds<D>()
-// bytes, 16-byte aligned.
-template <int D>
+// from jobs.tile_end[i - 1]; tile_end filled by hash_tiles, fewer than 2^31
+// tiles); the first tile's rows and the hyperplanes are requested together.
+// PT: hash_probe_class of the jobs (2: every job has one or two probes).
+// lds: hash_bf16_lds<D>() bytes, 16-byte aligned.
+//
+// Rows float32 cannot certify.  With one or two probes a tile's uncertain
+// (row, hyperplane) pairs -- the signs within the float32 bound, and for a
+// second probe the hyperplanes whose distance may be the row's smallest --
+// are re-evaluated in float64 together, 16 lanes per pair and four pairs at
+// a time; a row those cannot settle (a float64 sign within its bound, a
+// nearest hyperplane float64 cannot separate, too many uncertain pairs) and
+// every uncertain row with more probes take the whole-row float64 / exact
+// pass of hash_fixup_row, one row at a time.
+template <int D, int PT>
 __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint16_t* __restrict__ planes, int nb,
                                                fastar_diag_t* __restrict__ diag, int block, int nblocks,
                                                char* lds) {
+  static_assert(PT == 2 || PT == 3, "probe class 2 (one or two probes) or 3");
   constexpr int NC = D / 32;
   constexpr int kPst = D + 8;  // padded hyperplane rows: lanes reading 16 planes hit different banks
-  // lds: [4][D + 2] doubles (exact sums), [4][32] doubles (second probe),
-  // [16][kPst] hyperplanes (for rows float32 cannot certify), [4][D] per
-  // wave the row being re-evaluated
+  constexpr int EPL = D / 16;  // dims per lane when 16 lanes share one projection
+  // lds, per wave: [4][D + 2] doubles (exact sums), [4][32] doubles (second
+  // probe), [4][2][kRefinePairs] doubles (refined sums and absolute sums),
+  // [4][16] doubles (the hyperplanes' norms); then [16][kPst] hyperplanes,
+  // [4][16][D] the waves' tiles' rows, [4][kRefinePairs] bytes (row | plane
+  // << 4), and the workgroup's 3 diag counts
   double (*ex)[D + 2] = reinterpret_cast<double (*)[D + 2]>(lds);
   double (*de)[32] = reinterpret_cast<double (*)[32]>(lds + 4 * (D + 2) * sizeof(double));
-  uint16_t* spl = reinterpret_cast<uint16_t*>(lds + 4 * (D + 2 + 32) * sizeof(double));
-  uint16_t (*sxr)[D] = reinterpret_cast<uint16_t (*)[D]>(spl + 16 * kPst);
+  double (*rs)[2][kRefinePairs] =
+      reinterpret_cast<double (*)[2][kRefinePairs]>(lds + 4 * (D + 2 + 32) * sizeof(double));
+  double (*rn64)[16] =
+      reinterpret_cast<double (*)[16]>(lds + 4 * (D + 2 + 32 + 2 * kRefinePairs) * sizeof(double));
+  uint16_t* spl = reinterpret_cast<uint16_t*>(rn64 + 4);
+  uint16_t (*trow)[16][D] = reinterpret_cast<uint16_t (*)[16][D]>(spl + 16 * kPst);
+  uint8_t (*pairs)[kRefinePairs] = reinterpret_cast<uint8_t (*)[kRefinePairs]>(trow + 4);
+  uint32_t* wgcount = reinterpret_cast<uint32_t*>(pairs + 4);
   const int l = lane_id();
   const int col = l & 15;
   const int g = l >> 4;
   const int wv = threadIdx.x >> 6;
-  const int64_t total = jobs.tile_end[jobs.count - 1];
-  const int64_t nwaves = (int64_t)nblocks * (blockDim.x >> 6);
-  const int64_t first = (int64_t)block * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int total = (int)jobs.tile_end[jobs.count - 1];
+  const int nwaves = nblocks * (int)(blockDim.x >> 6);
+  // wave-uniform (scalar tile bookkeeping)
+  const int first = __builtin_amdgcn_readfirstlane(block * (int)(blockDim.x >> 6) + (int)(threadIdx.x >> 6));
   // tile -> tensor, head, first row (wave-uniform)
   struct Where {
     const uint16_t* x;
@@ -254,13 +324,13 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
     int h, P;
     int32_t* bucket;
   };
-  auto where = [&](int64_t tile) {
+  auto where = [&](int tile) {
     int ji = 0;
 #pragma unroll
     for (int i = 1; i < kMaxHashJobs; ++i)
       if (i < jobs.count && tile >= jobs.tile_end[i - 1]) ji = i;
     Where w;
-    int64_t t0 = 0;
+    int t0 = 0;
     // field-wise selects: no dynamic indexing of the argument block
 #pragma unroll
     for (int i = 0; i < kMaxHashJobs; ++i)
@@ -271,12 +341,12 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
         w.N = jobs.j[i].N;
         w.P = jobs.j[i].P;
         w.bucket = jobs.j[i].bucket;
-        t0 = i > 0 ? jobs.tile_end[i - 1] : 0;
+        t0 = i > 0 ? (int)jobs.tile_end[i - 1] : 0;
       }
-    const int64_t tph = (w.N + 15) >> 4;
-    const int64_t local = tile - t0;
+    const uint32_t tph = (uint32_t)((w.N + 15) >> 4);
+    const uint32_t local = (uint32_t)(tile - t0);
     w.h = (int)(local / tph);
-    w.r0 = (local - (int64_t)w.h * tph) << 4;
+    w.r0 = (int64_t)(local - (uint32_t)w.h * tph) << 4;
     return w;
   };
   auto load_rows = [&](const Where& w, uint4* u) {
@@ -290,7 +360,11 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
   // hyperplanes for the LDS copy are all in flight together; the copy is
   // written once the A operand has landed (its barrier orders LDS only).
   uint4 xu[NC];
-  if (first < total) load_rows(where(first), xu);
+  Where w{};
+  if (first < total) {
+    w = where(first);
+    load_rows(w, xu);
+  }
 
   // A operand: hyperplane `col`, dims 32c + 8g .. +8 of chunk c
   uint4 au[NC];
@@ -311,135 +385,276 @@ __device__ __forceinline__ void hash_bf16_body(const HashJobs& jobs, const uint1
     aop[c] = __builtin_bit_cast(bf16x8_t, au[c]);
   }
   if (pi < 16 * D / 8) *reinterpret_cast<uint4*>(&spl[pp * kPst + 8 * p8]) = pu;
+  if (threadIdx.x < 3) wgcount[threadIdx.x] = 0u;
   lds_barrier();
+  bool have_rn64 = false;  // this wave's copy of the hyperplanes' float64 norms
   r2 += shfl_xor_f(r2, 16);
   r2 += shfl_xor_f(r2, 32);
-  float rnorm[4], irn[4];  // the lane's four hyperplanes' norms and their reciprocals
+  // the lane's four hyperplanes 4g + i: reciprocal norms and the factor of
+  // |x| in their sign bounds; for hyperplanes past nb (projections 0) NaN and
+  // -inf, which no comparison below takes: such a hyperplane is never
+  // uncertain and never nearest
+  const float kc = kcert<D>();
+  float irn[4], kb[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    rnorm[i] = sqrtf(__shfl(r2, 4 * g + i, FASTAR_WAVE));
-    irn[i] = rnorm[i] > 0.f ? 1.f / rnorm[i] : 0.f;
+    const float rnorm = sqrtf(__shfl(r2, 4 * g + i, FASTAR_WAVE));
+    const bool pv = 4 * g + i < nb;
+    irn[i] = pv ? (rnorm > 0.f ? 1.f / rnorm : 0.f) : __builtin_nanf("");
+    kb[i] = pv ? kc * rnorm : -INFINITY;
   }
-
-  const float kc = kcert<D>();
   HashCounts hc;
-  for (int64_t tile = first; tile < total; tile += nwaves) {
-    const Where w = where(tile);
+  for (int tile = first; tile < total; tile += nwaves) {
     // the next tile's rows load while this one is hashed
     uint4 xn[NC];
-    if (tile + nwaves < total) load_rows(where(tile + nwaves), xn);
+    Where wn = w;
+    if (tile + nwaves < total) {
+      wn = where(tile + nwaves);
+      load_rows(wn, xn);
+    }
     const int64_t row = w.r0 + col;
     const bool valid = row < w.N;
     const int P = w.P;
     bf16x8_t bop[NC];
     float x2 = 0.f;
+    uint32_t nzb = 0u;  // any element nonzero (from the bits)
+    // (a row past N holds row r0's values: hashed, never written)
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      uint4 u = xu[c];
-      if (!valid) u = make_uint4(0u, 0u, 0u, 0u);
+      const uint4 u = xu[c];
       x2 += sumsq_bf16x8(u);
+      nzb |= (u.x | u.y | u.z | u.w) & 0x7FFF7FFFu;
       bop[c] = __builtin_bit_cast(bf16x8_t, u);
     }
     x2 = sum_xor32(sum_xor16(x2));
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[c], bop[c], acc, 0, 0, 0);
-    // acc[i] = x_row(col) . r_(4g+i)
-    const float xnorm = sqrtf(x2);
-    uint32_t bits = 0;
-    int amb = 0;
-    Nearest nr{INFINITY, INFINITY, 0};
+    // acc[i] = x_row(col) . r_(4g+i) (0 for hyperplanes past nb: their A rows are 0)
+    const float xnorm = __builtin_amdgcn_sqrtf(x2);  // (within the bounds' slack)
+    uint32_t bits = 0u, am = 0u;  // sign bits; hyperplanes whose sign float32 cannot certify
+    float dl[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = 4 * g + i;
-      if (p < nb) {
-        const float s = acc[i];
-        const float bound = kc * xnorm * rnorm[i] + 0x1p-90f;
-        amb |= fabsf(s) <= bound;
-        if (s > 0.f) bits |= 1u << p;
-        if (P == 2) {
-          const float dist = fabsf(s) * irn[i];  // within 2^-22 relative of the quotient
-          if (dist < nr.d1) {
-            nr.d2 = nr.d1;
-            nr.d1 = dist;
-            nr.j1 = p;
-          } else if (dist < nr.d2) {
-            nr.d2 = dist;
-          }
-        }
-      }
+      const float s = acc[i];
+      bits |= (s > 0.f ? 1u : 0u) << p;
+      am |= fabsf(s) <= fmaf(kb[i], xnorm, 0x1p-90f) ? 1u << p : 0u;
+      dl[i] = fabsf(s) * irn[i];  // within 2^-22 relative of the quotient
     }
     bits = or_xor32(or_xor16(bits));
-    amb = (int)or_xor32(or_xor16((uint32_t)amb));
+    am = or_xor32(or_xor16(am));
     // a zero row (every element +-0, from the bits: no underflow question):
     // every projection is exactly 0 (id 0) and every distance 0, so the
     // probes flip bits 0, 1, .. in order (ties to the smaller index);
     // nothing to certify
-    uint32_t nzb = 0u;
+    const bool zero = or_xor32(or_xor16(nzb)) == 0u;
+    Nearest nr{INFINITY, INFINITY, 0};
+    bool near_amb = false;
+    uint32_t nearu = 0u;  // hyperplanes whose distance may be the row's smallest
+    if (PT == 3 || P == 2) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) nzb |= (xu[c].x | xu[c].y | xu[c].z | xu[c].w) & 0x7FFF7FFFu;
-    const bool zero = valid && or_xor32(or_xor16(nzb)) == 0u;
-    if (P == 2) {
-      nearest_merge(nr, 16);
-      nearest_merge(nr, 32);
+      for (int i = 0; i < 4; ++i) {
+        const bool lt = dl[i] < nr.d1;  // (a NaN distance, past nb, is never taken)
+        nr.d2 = lt ? nr.d1 : (dl[i] < nr.d2 ? dl[i] : nr.d2);
+        nr.j1 = lt ? 4 * g + i : nr.j1;
+        nr.d1 = lt ? dl[i] : nr.d1;
+      }
+      nearest_merge_pl<16>(nr);
+      nearest_merge_pl<32>(nr);
       // each distance is known to within kc*|x| (plus the rounding of the
       // reciprocal norm and of the product)
-      const float err = 2.f * kc * xnorm + (nr.d1 + nr.d2) * 0x1p-20f + 0x1p-90f;
-      if (nr.d2 - nr.d1 <= err) amb = 1;
-    }
-    if (zero) {
-      amb = 0;
-      nr.j1 = 0;
+      const float e0 = 2.f * kc * xnorm + 0x1p-90f;
+      near_amb = P == 2 && nr.d2 - nr.d1 <= e0 + (nr.d1 + nr.d2) * 0x1p-20f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nearu |= (dl[i] - nr.d1 <= e0 + (nr.d1 + dl[i]) * 0x1p-20f) ? 1u << (4 * g + i) : 0u;
+      nearu = or_xor32(or_xor16(nearu));
     }
     // more probes: every lane of the row gathers the row's 16 distances and
     // ranks its own 4 planes
     int rk[4] = {0, 0, 0, 0};
-    if (P > 2) {
-      float dl[4], da[16];
+    bool amb = am != 0u || near_amb;
+    if constexpr (PT == 3) {
+      if (P > 2) {
+        float da[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dl[i] = (4 * g + i < nb) ? fabsf(acc[i]) * irn[i] : INFINITY;
+        for (int g2 = 0; g2 < 4; ++g2)
 #pragma unroll
-      for (int g2 = 0; g2 < 4; ++g2)
+          for (int i = 0; i < 4; ++i) da[4 * g2 + i] = __shfl(dl[i], 16 * g2 + col, FASTAR_WAVE);
+        const bool a2 = probe_ranks(dl, da, 4 * g, nb, P, 2.f * kc * xnorm + 0x1p-90f, rk);
+        amb = or_xor32(or_xor16(amb || a2 ? 1u : 0u)) != 0u;
+        if (zero) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) da[4 * g2 + i] = __shfl(dl[i], 16 * g2 + col, FASTAR_WAVE);
-      const bool a2 = probe_ranks(dl, da, 4 * g, nb, P, 2.f * kc * xnorm + 0x1p-90f, rk);
-      amb = (int)or_xor32(or_xor16((uint32_t)(amb | (a2 ? 1 : 0))));
-      if (zero) {
-        amb = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rk[i] = 4 * g + i;
+          for (int i = 0; i < 4; ++i) rk[i] = 4 * g + i;
+        }
       }
     }
+    if (zero) {
+      amb = false;
+      nr.j1 = 0;
+    }
+    int32_t* const orow = w.bucket + ((int64_t)w.h * w.N + row) * P;
     if (valid && g == 0 && !amb) {
-      int32_t* o = w.bucket + ((int64_t)w.h * w.N + row) * P;
-      o[0] = (int32_t)bits;
-      if (P == 2) o[1] = (int32_t)(bits ^ (1u << nr.j1));
+      orow[0] = (int32_t)bits;
+      if (P == 2) orow[1] = (int32_t)(bits ^ (1u << nr.j1));
     }
-    if (P > 2 && valid && !amb) {
-      int32_t* o = w.bucket + ((int64_t)w.h * w.N + row) * P;
+    if constexpr (PT == 3) {
+      if (P > 2 && valid && !amb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * g + i < nb && rk[i] < P - 1) o[1 + rk[i]] = (int32_t)(bits ^ (1u << (4 * g + i)));
-    }
-    // rows float32 cannot certify: float64 by the whole wave, one at a
-    // time, from an LDS copy
-    uint64_t ab = ballot64(valid && g == 0 && amb);  // bit = the row's column
-    while (ab) {
-      const int r = __builtin_ctzll(ab);  // wave-uniform
-      ab &= ab - 1;
-      if (col == r) {
-        // the 4 lanes holding row r copy its dims 32c + 8g .. +8
-#pragma unroll
-        for (int c = 0; c < NC; ++c) *reinterpret_cast<uint4*>(&sxr[wv][32 * c + 8 * g]) = xu[c];
+        for (int i = 0; i < 4; ++i)
+          if (4 * g + i < nb && rk[i] < P - 1) orow[1 + rk[i]] = (int32_t)(bits ^ (1u << (4 * g + i)));
       }
-      hash_fixup_row<uint16_t, D>(sxr[wv], spl, kPst, w.bucket + ((int64_t)w.h * w.N + w.r0 + r) * P,
-                                  P, nb, hc, ex[wv], de[wv]);
+    }
+    uint64_t ab = ballot64(valid && g == 0 && amb);  // bit = the row's column
+    if (ab) {
+      // the tile's rows to LDS (read by the re-evaluations; in order within the wave)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) *reinterpret_cast<uint4*>(&trow[wv][col][32 * c + 8 * g]) = xu[c];
+      uint64_t whole = ab;  // rows for the whole-row pass
+      if (PT == 2 || P <= 2) {
+        // (row, hyperplane) pairs in row order, each row's in hyperplane order
+        const uint32_t um = am | (near_amb ? nearu : 0u);
+        const int cnt = (g == 0 && valid && amb && __builtin_popcount(um) <= kRefineRowMax) ? __builtin_popcount(um) : 0;
+        const int incl = (int)wave_incl_scan_dpp((uint32_t)cnt);  // lanes 0..15: within their row
+        const int excl = incl - cnt;
+        const bool fits = cnt > 0 && incl <= kRefinePairs;
+        if (fits) {
+          uint32_t m = um;
+          for (int k = excl; m; ++k) {
+            pairs[wv][k] = (uint8_t)(col | (__builtin_ctz(m) << 4));
+            m &= m - 1u;
+          }
+        }
+        const int npairs = __builtin_amdgcn_readfirstlane(wave_reduce_dpp(fits ? incl : 0, [](int a, int b) { return max(a, b); }));
+        if (!have_rn64) {
+          // the hyperplanes' norms in float64 (squares of bf16 values are
+          // exact), from the A operand: lane (p, g) holds a quarter of plane p
+          double n2 = 0.0;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const uint4 u = __builtin_bit_cast(uint4, aop[c]);
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const double lo = (double)bf16_bits_to_f32(wd[k] & 0xFFFFu);
+              const double hi = (double)__uint_as_float(wd[k] & 0xFFFF0000u);
+              n2 = fma(lo, lo, n2);
+              n2 = fma(hi, hi, n2);
+            }
+          }
+          n2 = sum4_d(n2);
+          if (g == 0) rn64[wv][col] = sqrt(n2);
+          have_rn64 = true;
+        }
+        // four pairs at a time: lane j of quarter q takes dims EPL j .. +EPL
+        const int q = l >> 4, j = l & 15;
+        for (int k0 = 0; k0 < npairs; k0 += 4) {
+          const int k = k0 + q;
+          double s = 0.0, a = 0.0;
+          if (k < npairs) {
+            const int pr = pairs[wv][k];
+            const uint16_t* xp = &trow[wv][pr & 15][EPL * j];
+            const uint16_t* rp = &spl[(pr >> 4) * kPst + EPL * j];
+            uint32_t xw[EPL / 2], rw[EPL / 2];
+            if constexpr (EPL == 8) {
+              const uint4 xv = *reinterpret_cast<const uint4*>(xp), rv = *reinterpret_cast<const uint4*>(rp);
+              xw[0] = xv.x, xw[1] = xv.y, xw[2] = xv.z, xw[3] = xv.w;
+              rw[0] = rv.x, rw[1] = rv.y, rw[2] = rv.z, rw[3] = rv.w;
+            } else {
+              const uint2 xv = *reinterpret_cast<const uint2*>(xp), rv = *reinterpret_cast<const uint2*>(rp);
+              xw[0] = xv.x, xw[1] = xv.y;
+              rw[0] = rv.x, rw[1] = rv.y;
+            }
+#pragma unroll
+            for (int e = 0; e < EPL / 2; ++e) {
+              // products of bf16 values are exact in float64
+              const double x0 = (double)bf16_bits_to_f32(xw[e] & 0xFFFFu), x1 = (double)__uint_as_float(xw[e] & 0xFFFF0000u);
+              const double r0 = (double)bf16_bits_to_f32(rw[e] & 0xFFFFu), r1 = (double)__uint_as_float(rw[e] & 0xFFFF0000u);
+              s = fma(x0, r0, s);
+              s = fma(x1, r1, s);
+              a = fma(fabs(x0), fabs(r0), a);
+              a = fma(fabs(x1), fabs(r1), a);
+            }
+          }
+          s = row16_sum_d(s);
+          a = row16_sum_d(a);
+          if (j == 0 && k < npairs) {
+            rs[wv][0][k] = s;
+            rs[wv][1][k] = a;
+          }
+        }
+        // each refined row's decisions, by its lane of g == 0
+        bool settled = false;
+        if (fits) {
+          uint32_t fb = bits;
+          bool ok = true;
+          int m = -1;
+          double dm = 0.0, em = 0.0, lb = INFINITY;  // nearest so far, its error; the others' lower bound
+          for (int k = excl; k < incl; ++k) {
+            const int p = pairs[wv][k] >> 4;
+            const double s = rs[wv][0][k];
+            // any order of the D additions is within this bound
+            const double bound = 2.0 * (D + 8) * 0x1p-53 * rs[wv][1][k];
+            if ((am >> p) & 1u) {
+              if (fabs(s) > bound) fb = (fb & ~(1u << p)) | ((s > 0.0 ? 1u : 0u) << p);
+              else ok = false;
+            }
+            if (near_amb && ((nearu >> p) & 1u)) {
+              const double rn = rn64[wv][p];
+              if (!(rn > 0.0)) {
+                ok = false;
+              } else {
+                const double dp = fabs(s) / rn;
+                const double ep = bound / rn + dp * (2 * D + 8) * 0x1p-53;
+                if (m < 0 || dp < dm) {  // hyperplanes come in index order: ties stay with the smaller
+                  if (m >= 0) lb = fmin(lb, dm - em);
+                  m = p, dm = dp, em = ep;
+                } else {
+                  lb = fmin(lb, dp - ep);
+                }
+              }
+            }
+          }
+          // the hyperplanes outside nearu are farther than the row's
+          // nearest by the float32 bounds; the float64 nearest must stand
+          // apart from the other candidates
+          if (near_amb && ok && !(lb > dm + em)) ok = false;
+          if (ok) {
+            orow[0] = (int32_t)fb;
+            if (P == 2) orow[1] = (int32_t)(fb ^ (1u << (near_amb ? m : nr.j1)));
+            settled = true;
+          }
+        }
+        whole = ballot64(settled) ^ ab;
+      }
+      hc.rows += (uint32_t)(__builtin_popcountll(ab) - __builtin_popcountll(whole));
+      while (whole) {
+        const int r = __builtin_ctzll(whole);  // wave-uniform
+        whole &= whole - 1;
+        hash_fixup_row<uint16_t, D>(&trow[wv][r][0], spl, kPst, w.bucket + ((int64_t)w.h * w.N + w.r0 + r) * P,
+                                    P, nb, hc, ex[wv], de[wv]);
+      }
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) xu[c] = xn[c];
+    w = wn;
   }
-  hash_counts_flush(hc, diag);
+  // the workgroup's counts, then one device atomic per counter: many waves
+  // adding to the same word at the end of a launch held it up
+  if (diag) {
+    if (lane_id() == 0) {
+      if (hc.rows) atomicAdd(&wgcount[0], hc.rows);
+      if (hc.signs) atomicAdd(&wgcount[1], hc.signs);
+      if (hc.unresolved) atomicAdd(&wgcount[2], hc.unresolved);
+    }
+    lds_barrier();
+    if (threadIdx.x == 0) {
+      HashCounts wc;
+      wc.rows = wgcount[0], wc.signs = wgcount[1], wc.unresolved = wgcount[2];
+      hash_counts_flush(wc, diag);
+    }
+  }
 }
 
 

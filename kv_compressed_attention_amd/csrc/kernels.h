@@ -96,7 +96,7 @@ struct MergeWs {
   int32_t* mrange;    // [H][n_frames][ceil(T / 64)][4]
   int32_t* index_ws;  // bucket index scratch
   const IndexJob* also_index = nullptr;  // direct-index job for the representatives' index launch, or none
-  // bf16 rows (the queries) that extra workgroups of the match launch hash
+  // bf16 rows (the queries, one or two probes) that extra workgroups of the match launch hash
   // with hash_planes and hash_bits (same dim as the cache), or none
   const HashJobs* also_hash = nullptr;
   const void* hash_planes = nullptr;

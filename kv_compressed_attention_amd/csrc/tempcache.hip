@@ -1058,7 +1058,8 @@ __device__ __forceinline__ void match_group(const SegCtx<T, D>& x, const MergeAr
 
 // The workgroups of the planes past the frames (blockIdx.z >= F, dispatched
 // last; bf16 only) hash the jobs qh instead: flat index ((z - F) * gridDim.y
-// + y) * gridDim.x + x < qblocks is hashing block that index.
+// + y) * gridDim.x + x < qblocks is hashing block that index (jobs of one
+// or two probes).
 template <typename T, int D>
 __global__ __launch_bounds__(256, 4) void tc_match_kernel(
     const T* __restrict__ rep_k, const T* __restrict__ knew, int64_t k_sh, int64_t k_st,
@@ -1072,8 +1073,8 @@ __global__ __launch_bounds__(256, 4) void tc_match_kernel(
     if constexpr (sizeof(T) == 2) {
       static_assert(hash_bf16_lds<D>() <= match_lds_words<T, D>() * sizeof(int32_t), "hashing fits the LDS");
       const int qb = (int)(((blockIdx.z - a.F) * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x);
-      if (qb < qblocks)
-        hash_bf16_body<D>(qh, qplanes, qnb, diag, qb, qblocks, reinterpret_cast<char*>(lds));
+      if (qb < qblocks)  // (jobs of at most two probes)
+        hash_bf16_body<D, 2>(qh, qplanes, qnb, diag, qb, qblocks, reinterpret_cast<char*>(lds));
     }
     return;  // the whole workgroup
   }
@@ -1458,6 +1459,8 @@ hipError_t merge_td(const fastar_cache_t& c, const fastar_tensor_t& kn, const fa
   int qblocks = 0, qz = 0;
   if (ws.also_hash && sizeof(T) == 2) {
     const int64_t tiles = hash_tiles(*ws.also_hash, &qh);
+    // tiles are numbered in 32 bits; the riding hash takes one or two probes
+    if (tiles >= (int64_t)1 << 31 || hash_probe_class(qh) != 2) return hipErrorInvalidValue;
     const int64_t plane = (int64_t)match_groups(Tf) * H;
     const int64_t want = (tiles + 4 * kMatchHashTiles - 1) / (4 * kMatchHashTiles);
     qblocks = (int)(want < kMatchHashPlanes * plane ? want : kMatchHashPlanes * plane);
