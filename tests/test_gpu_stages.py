@@ -329,6 +329,37 @@ def test_list_and_dense_modes_match_oracle(fa, dtype, d):
     assert torch.all(o_list[1] == 0) and torch.all(torch.isinf(l_list[1]))
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_list_mode_long_lists_bias_and_lse(fa, d):
+    """bf16 list mode against the oracle's dense attention over the listed keys
+    (with their + ln m biases), outputs and lse: lists shorter than, equal to
+    and longer than the 256 keys a workgroup keeps resident (the longer ones
+    pass through in windows), in any order and with a repeated key (it counts
+    twice, as in the list), over rows that end inside a step."""
+    print(f"list d{d}", flush=True)
+    H, nq, nk = 4, 600, 700
+    q = gaussian((H, nq, d), 91, "bf16")
+    k = gaussian((H, nk, d), 92, "bf16")
+    v = gaussian((H, nk, d), 93, "bf16")
+    rng = np.random.default_rng(94)
+    kb = np.log(rng.integers(1, 6, (H, nk)).astype(np.float64)).astype(np.float32)
+    lens = [300, 256, 257, 61]
+    lists = np.zeros((H, nk), np.int64)
+    for h, n in enumerate(lens):
+        lists[h, :n] = rng.permutation(nk)[:n]
+    lists[3, 5] = lists[3, 9]  # a repeated key
+    out, lse = fa.fastar_bucket_attention(dev_tensor(q, "bf16"), dev_tensor(k, "bf16"), dev_tensor(v, "bf16"),
+                                          key_bias=torch.tensor(kb, device="cuda"), key_list=i32(lists),
+                                          n_key_list=i32(np.array(lens)))
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for h, n in enumerate(lens):
+        idx = lists[h, :n]
+        o_ref, lse_ref = oracle.dense_attention(q[h], k[h][idx], v[h][idx], bias=kb[h][idx])
+        assert np.max(np.abs(out[h] - o_ref)) <= TOL["bf16"], f"head {h}"
+        assert np.max(np.abs(lse[h] - lse_ref)) <= TOL["bf16"], f"head {h}"
+
+
 def test_attention_lemma_duplicates_on_gpu(fa):
     # Lemma 5.1 on the GPU: attention over the merged representatives with
     # the bf16 group means and + ln m equals the oracle's dense attention
