@@ -17,9 +17,9 @@
 // sign, or the distances that may be a row's smallest) are re-evaluated in
 // float64 together (products of bf16 values are exact there); a row that
 // still cannot be certified, every uncertain row with more probes and every
-// uncertain fp32 row are re-evaluated whole by their wave in float64, and a
+// uncertain fp32 row are re-evaluated whole by their wave in float64; a
 // sign float64 still cannot certify is settled exactly with an error-free
-// expansion sum.
+// expansion sum, and an order of two probe distances by integer arithmetic.
 
 #include "common.h"
 #include "hash_body.h"

@@ -96,6 +96,40 @@ def test_hash_and_index_match_oracle(fa, dtype, H, n, d, b, P):
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_hash_two_probe_ties_and_near_ties(fa, dtype, d):
+    """Second probes of rows whose two nearest hyperplanes lie at exactly the
+    same distance (planes 2 = s e0 and 5 = s e1, rows with x0 = x1 = 2^-6: the
+    smaller index wins, decided in integer arithmetic) or 2^-25 apart
+    relatively (planes 7 = s e2 and 8 = s (e3 + 2^-12 e4), rows with x2 = x3
+    = 2^-6: plane 8 is nearer, below float32's bound and decided in float64):
+    ids equal the oracle's and no decision is left unresolved."""
+    print(f"hash ties {dtype} d{d}", flush=True)
+    b, n = 10, 600
+    planes = gaussian((b, d), 112, dtype)
+    s = 0.75
+    for j in (2, 5, 7, 8):
+        planes[j] = 0.0
+    planes[2, 0] = planes[5, 1] = planes[7, 2] = planes[8, 3] = s
+    planes[8, 4] = s * 2.0 ** -12
+    x = gaussian((1, n, d), 113, dtype)
+    a = 2.0 ** -6
+    x[0, 0::2, 0] = x[0, 0::2, 1] = a          # exact ties
+    x[0, 0::2, 2] = x[0, 0::2, 3] = 1.0
+    x[0, 1::2, 2] = x[0, 1::2, 3] = a          # near ties
+    x[0, 1::2, 4] = 0.0
+    x[0, 1::2, 0] = x[0, 1::2, 1] = 1.0
+    for P in (2, 3):
+        diag = fa.new_diag()
+        ids, _, _ = fa.fastar_hash(dev_tensor(x, dtype), dev_tensor(planes, dtype), b, P, diag=diag)
+        torch.cuda.synchronize()
+        ref = oracle.simhash(x[0], planes, P)
+        got = ids.cpu().numpy()[0]
+        assert np.array_equal(got, ref), f"P={P}: {np.sum(np.any(got != ref, axis=1))} rows differ"
+        dg = diag.cpu().numpy()
+        assert dg[3] == 0 and dg[0] > 0, dg.tolist()
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64)])
 def test_hash_multi_matches_oracle(fa, dtype, d):
     """Queries (two probes), keys and prompt keys of different head and row
     counts in one call: each tensor's ids equal the oracle's, and an empty

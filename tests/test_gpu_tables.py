@@ -69,6 +69,8 @@ def test_multi_probe_hash_matches_oracle(fa, dtype, H, n, d, b, P):
             assert np.array_equal(ids[h], ref), f"head {h}: {np.sum(np.any(ids[h] != ref, axis=1))} rows differ"
             r_off, r_perm = oracle.bucket_index(ref, b)
             assert np.array_equal(off[h], r_off) and np.array_equal(perm[h], r_perm)
+        # exact ties of two distances are decided exactly, not left unresolved
+        assert diag.cpu().numpy()[3] == 0, diag.tolist()
 
 
 def _tables_case(dtype, L, H, nq, nk, d, b, P, seed):
