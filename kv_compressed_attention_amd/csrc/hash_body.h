@@ -5,6 +5,7 @@
 #pragma once
 
 #include "common.h"
+#include "exact_int.h"
 #include "kernels.h"
 
 namespace fastar {
@@ -83,154 +84,6 @@ __device__ __forceinline__ double sum4_d(double v) {
   return w + dswap32(w);
 }
 
-// ---------------------------------------------------------------------------
-// Exact order of two hyperplane distances |x.r_a| / |r_a| and |x.r_b| / |r_b|,
-// for the probe orders float64 cannot certify: the sign of
-// (x.r_a)^2 |r_b|^2 - (x.r_b)^2 |r_a|^2 in integer arithmetic.  Every stored
-// value is m 2^e with an integer significand m (bf16: |m| < 2^8; float32:
-// |m| < 2^24), so a dot product and a squared norm are integers times a power
-// of two; they are accumulated into little-endian 32-bit limbs, squared and
-// multiplied, all in a caller-given LDS word array.
-// ---------------------------------------------------------------------------
-template <typename T> struct ExactVal;
-template <> struct ExactVal<uint16_t> {  // bf16 bits
-  static constexpr int kSigBits = 8;
-  static __device__ __forceinline__ void split(uint16_t h, int64_t& m, int& e) {
-    const int ex = (h >> 7) & 0xFF, fr = h & 0x7F;
-    m = ex ? (fr | 0x80) : fr;
-    e = (ex ? ex : 1) - 134;  // (1 + fr / 2^7) 2^(ex - 127), or fr 2^-133
-    if (h & 0x8000) m = -m;
-  }
-};
-template <> struct ExactVal<float> {
-  static constexpr int kSigBits = 24;
-  static __device__ __forceinline__ void split(float f, int64_t& m, int& e) {
-    const uint32_t u = __float_as_uint(f);
-    const int ex = (u >> 23) & 0xFF;
-    const int64_t fr = u & 0x7FFFFF;
-    m = ex ? (fr | 0x800000) : fr;
-    e = (ex ? ex : 1) - 150;  // (1 + fr / 2^23) 2^(ex - 127), or fr 2^-149
-    if (u >> 31) m = -m;
-  }
-};
-
-// v[0 .. n) += val 2^bit (the sum fits in n limbs)
-__device__ inline void big_add_shifted(uint32_t* v, int n, uint64_t val, int bit) {
-  int k = bit >> 5;
-  const int sh = bit & 31;
-  const uint64_t lo = val << sh;
-  const uint32_t w[3] = {(uint32_t)lo, (uint32_t)(lo >> 32), sh ? (uint32_t)(val >> (64 - sh)) : 0u};
-  uint64_t carry = 0;
-  for (int i = 0; k < n && (i < 3 || carry); ++i, ++k) {
-    const uint64_t t = (uint64_t)v[k] + (i < 3 ? w[i] : 0u) + carry;
-    v[k] = (uint32_t)t;
-    carry = t >> 32;
-  }
-}
-// -1, 0, 1 as a < b, a == b, a > b (n limbs each)
-__device__ inline int big_cmp(const uint32_t* a, const uint32_t* b, int n) {
-  for (int i = n - 1; i >= 0; --i)
-    if (a[i] != b[i]) return a[i] < b[i] ? -1 : 1;
-  return 0;
-}
-// a -= b (a >= b)
-__device__ inline void big_sub(uint32_t* a, const uint32_t* b, int n) {
-  int64_t borrow = 0;
-  for (int i = 0; i < n; ++i) {
-    const int64_t t = (int64_t)a[i] - b[i] - borrow;
-    a[i] = (uint32_t)t;
-    borrow = t < 0 ? 1 : 0;
-  }
-}
-// c[0 .. na + nb) = a[0 .. na) b[0 .. nb)
-__device__ inline void big_mul(uint32_t* c, const uint32_t* a, int na, const uint32_t* b, int nb) {
-  for (int i = 0; i < na + nb; ++i) c[i] = 0u;
-  for (int i = 0; i < na; ++i) {
-    uint64_t carry = 0;
-    for (int j = 0; j < nb; ++j) {
-      const uint64_t t = (uint64_t)a[i] * b[j] + c[i + j] + carry;
-      c[i + j] = (uint32_t)t;
-      carry = t >> 32;
-    }
-    c[i + nb] = (uint32_t)carry;
-  }
-}
-
-// The sign of d_a - d_b for the distances of row x to hyperplanes ra and rb
-// (D values each, read through generic pointers): -1, 0 or 1; 2 when the
-// integers need more than cap words of W or a hyperplane is zero.  One lane.
-template <typename T, int D>
-__device__ int exact_dist_cmp(const T* x, const T* ra, const T* rb, uint32_t* W, int cap) {
-  using EV = ExactVal<T>;
-  // the exponent ranges of the nonzero products and squares
-  int e0 = INT_MAX, e1 = INT_MIN, f0 = INT_MAX, f1 = INT_MIN;
-  for (int d = 0; d < D; ++d) {
-    int64_t mx, ma, mb;
-    int ex, ea, eb;
-    EV::split(x[d], mx, ex);
-    EV::split(ra[d], ma, ea);
-    EV::split(rb[d], mb, eb);
-    if (mx && ma) e0 = min(e0, ex + ea), e1 = max(e1, ex + ea);
-    if (mx && mb) e0 = min(e0, ex + eb), e1 = max(e1, ex + eb);
-    if (ma) f0 = min(f0, 2 * ea), f1 = max(f1, 2 * ea);
-    if (mb) f0 = min(f0, 2 * eb), f1 = max(f1, 2 * eb);
-  }
-  if (f0 == INT_MAX) return 2;                 // both hyperplanes zero
-  if (e0 == INT_MAX) return 0;                 // both dot products exactly 0
-  // limbs: the products' spread, their significand bits, 2^8 terms of carry
-  const int n = (e1 - e0 + 2 * EV::kSigBits + 8 + 31) / 32 + 1;
-  const int m = (f1 - f0 + 2 * EV::kSigBits + 8 + 31) / 32 + 1;
-  if (8 * n + 4 * m > cap) return 2;
-  uint32_t* sa = W;           // |x.ra|   n
-  uint32_t* sb = sa + n;      // |x.rb|   n
-  uint32_t* tn = sb + n;      // negative parts   n
-  uint32_t* na = tn + n;      // |ra|^2   m
-  uint32_t* nbv = na + m;     // |rb|^2   m
-  uint32_t* sq = nbv + m;     // a square   2n
-  uint32_t* pa = sq + 2 * n;  // (x.ra)^2 |rb|^2   2n + m
-  uint32_t* pb = pa + 2 * n + m;
-  for (int i = 0; i < 3 * n + 2 * m; ++i) W[i] = 0u;
-  // |x.r| for both hyperplanes: positive and negative products apart, then
-  // the difference
-  for (int side = 0; side < 2; ++side) {
-    uint32_t* s = side ? sb : sa;
-    const T* r = side ? rb : ra;
-    for (int i = 0; i < n; ++i) tn[i] = 0u;
-    for (int d = 0; d < D; ++d) {
-      int64_t mx, mr;
-      int ex, er;
-      EV::split(x[d], mx, ex);
-      EV::split(r[d], mr, er);
-      if (!mx || !mr) continue;
-      const int64_t pr = mx * mr;  // |pr| < 2^(2 kSigBits)
-      big_add_shifted(pr > 0 ? s : tn, n, (uint64_t)(pr > 0 ? pr : -pr), ex + er - e0);
-    }
-    if (big_cmp(s, tn, n) >= 0) {
-      big_sub(s, tn, n);
-    } else {
-      big_sub(tn, s, n);
-      for (int i = 0; i < n; ++i) s[i] = tn[i];
-    }
-  }
-  for (int d = 0; d < D; ++d) {
-    int64_t ma, mb;
-    int ea, eb;
-    EV::split(ra[d], ma, ea);
-    EV::split(rb[d], mb, eb);
-    if (ma) big_add_shifted(na, m, (uint64_t)(ma * ma), 2 * ea - f0);
-    if (mb) big_add_shifted(nbv, m, (uint64_t)(mb * mb), 2 * eb - f0);
-  }
-  // a zero hyperplane: its distance is not defined by this comparison
-  bool za = true, zb = true;
-  for (int i = 0; i < m; ++i) za = za && na[i] == 0u, zb = zb && nbv[i] == 0u;
-  if (za || zb) return 2;
-  big_mul(sq, sa, n, sa, n);
-  big_mul(pa, sq, 2 * n, nbv, m);
-  big_mul(sq, sb, n, sb, n);
-  big_mul(pb, sq, 2 * n, na, m);
-  return big_cmp(pa, pb, 2 * n + m);
-}
-
 // Re-evaluates one row in float64 and writes its ids (o: the row's output,
 // the same in every lane).  Lane 16s + p takes the dims [s D/4, (s+1) D/4)
 // of hyperplane p: serial sums of exact products, then added over the four
@@ -238,7 +91,7 @@ __device__ int exact_dist_cmp(const T* x, const T* ra, const T* rb, uint32_t* W,
 // LDS or global memory) are read through generic pointers.  A sign float64
 // cannot certify is settled exactly with an expansion sum in E (D + 2
 // doubles of LDS), and so is an order of two probe distances (integers in
-// E's words: exact_dist_cmp); the distances and their error bounds go
+// E's words: exact_ratio_cmp); the distances and their error bounds go
 // through DE (32 doubles of LDS).
 template <typename T, int D>
 __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t* __restrict__ o, int P,
@@ -324,8 +177,8 @@ __device__ inline void hash_fixup_row(const T* xr, const T* ps, int pst, int32_t
         } else if (dist[q] - derr[q] > dist[jb] + derr[jb]) {
           nearer = false;
         } else {
-          const int c = exact_dist_cmp<T, D>(xr, ps + q * pst, ps + jb * pst, reinterpret_cast<uint32_t*>(E),
-                                             2 * (D + 2));
+          const int c = exact_ratio_cmp<T, D>(xr, ps + q * pst, ps + jb * pst, reinterpret_cast<uint32_t*>(E),
+                                              2 * (D + 2), nullptr, nullptr);
           if (c == 2) unresolved = true;
           nearer = c == 2 ? dist[q] < dist[jb] : c < 0;
         }
