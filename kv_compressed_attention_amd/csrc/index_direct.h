@@ -70,6 +70,7 @@ __host__ __device__ inline DirectShape direct_shape(int n_bits, bool wide, int n
 }
 // 32-bit counters for n items
 inline bool direct_index_wide(int64_t n) { return n > kDirectNarrowItems; }
+constexpr int ilog2_c(int v) { return v > 1 ? 1 + ilog2_c(v >> 1) : 0; }
 // buckets of one part of a head in range mode
 __host__ __device__ constexpr int range_part_buckets(bool wide) { return kRangeRowBytes / (wide ? 4 : 2); }
 // The parts (workgroups) per head for n items
@@ -348,7 +349,7 @@ __device__ __forceinline__ void range_index_body(int h, int part, int nparts,
                                                  int32_t* __restrict__ perm, int4* lds4) {
   constexpr int nbk = 1 << NBITS;
   constexpr int R = range_part_buckets(WIDE);
-  constexpr int RB = NBITS - (WIDE ? 10 : 11);  // bits of the part index
+  constexpr int RB = NBITS - ilog2_c(R);  // bits of the part index
   static_assert(R * (1 << RB) == nbk && R % kDirectThreads == 0 || R < kDirectThreads, "range split");
   constexpr int BPT = R / kDirectThreads > 0 ? R / kDirectThreads : 1;  // buckets per thread
   using CT = typename std::conditional<WIDE, uint32_t, uint16_t>::type;
@@ -378,37 +379,58 @@ __device__ __forceinline__ void range_index_body(int h, int part, int nparts,
     if (WIDE) atomicAdd(&cnt32[i], 1u);
     else atomicAdd(&cnt32[i >> 1], 1u << (16 * (b & 1u)));
   };
-  // the wave's slice [wbeg, wend), walked in tiles of kTile ids per lane
+  // the wave's slice [wbeg, wend), walked in tiles of kTile ids per lane; a
+  // slice of at most kResTiles tiles is loaded once, all tiles at a time, and
+  // kept in registers for the scatter pass.  Two tiles keep the kernel within
+  // 64 VGPRs: a 16-wave workgroup then still finds room on a CU beside the
+  // attention waves of the other stream (at 72 it waits for them)
   const int chunk = (nh + kDirectWaves - 1) / kDirectWaves;
   const int wbeg = wave * chunk < nh ? wave * chunk : nh;
   const int wend = wbeg + chunk < nh ? wbeg + chunk : nh;
   constexpr int kTile = 8;
+  constexpr int kResTiles = 2;
   const int last = nh - 1;
-  uint32_t b[kTile];
-  auto load_tile = [&](int t0) {
+  const bool resident = wend - wbeg <= kResTiles * kTile * FASTAR_WAVE;
+  uint32_t b[kResTiles][kTile];
+  auto load_tile = [&](uint32_t* bt, int t0) {
 #pragma unroll
     for (int r = 0; r < kTile; ++r) {
       const int i = t0 + r * FASTAR_WAVE + lane;
       const uint32_t v = index_key(ids, i < last ? i : last, P) & bmask;
-      b[r] = i < wend ? v : 0xFFFFFFFFu;
+      bt[r] = i < wend ? v : 0xFFFFFFFFu;
     }
   };
-  load_tile(wbeg);
+  if (resident) {
+#pragma unroll
+    for (int u = 0; u < kResTiles; ++u)
+      if (wbeg + u * kTile * FASTAR_WAVE < wend) load_tile(b[u], wbeg + u * kTile * FASTAR_WAVE);
+  } else {
+    load_tile(b[0], wbeg);
+  }
   for (int i = threadIdx.x; i < kDirectWaves * R * (int)sizeof(CT) / 16; i += kDirectThreads)
     lds4[i] = make_int4(0, 0, 0, 0);
   lds_barrier();
   int below = 0;  // this lane's items below the range
-  for (int t0 = wbeg; t0 < wend;) {
+  auto count_tile = [&](const uint32_t* bt) {
 #pragma unroll
     for (int r = 0; r < kTile; ++r) {
-      if (b[r] == 0xFFFFFFFFu) continue;
-      const uint32_t d = b[r] - lo;
+      if (bt[r] == 0xFFFFFFFFu) continue;
+      const uint32_t d = bt[r] - lo;
       if (d < (uint32_t)R) inc(wave, d);
-      else if (b[r] < lo) ++below;
+      else if (bt[r] < lo) ++below;
     }
-    t0 += kTile * FASTAR_WAVE;
-    if (t0 >= wend) break;
-    load_tile(t0);
+  };
+  if (resident) {
+#pragma unroll
+    for (int u = 0; u < kResTiles; ++u)
+      if (wbeg + u * kTile * FASTAR_WAVE < wend) count_tile(b[u]);
+  } else {
+    for (int t0 = wbeg; t0 < wend;) {
+      count_tile(b[0]);
+      t0 += kTile * FASTAR_WAVE;
+      if (t0 >= wend) break;
+      load_tile(b[0], t0);
+    }
   }
   below = wave_sum_dpp(below);
   if (lane == 0) wbelow[wave] = below;
@@ -451,13 +473,12 @@ __device__ __forceinline__ void range_index_body(int h, int part, int nparts,
   }
   lds_barrier();
   // stable scatter of the in-range items: each wave walks its slice in order
-  for (int t0 = wbeg; t0 < wend; t0 += kTile * FASTAR_WAVE) {
-    load_tile(t0);
+  auto scatter_tile = [&](const uint32_t* bt, int t0) {
 #pragma unroll
     for (int r = 0; r < kTile; ++r) {
       if (t0 + r * FASTAR_WAVE >= wend) break;  // uniform
       const int i = t0 + r * FASTAR_WAVE + lane;
-      const uint32_t d = b[r] - lo;  // past the end: 0xFFFFFFFF - lo, not in range
+      const uint32_t d = bt[r] - lo;  // past the end: 0xFFFFFFFF - lo, not in range
       const bool inr = d < (uint32_t)R;
       // lanes of this row with the same bucket: in range, and agreeing on the
       // bits of d
@@ -477,6 +498,16 @@ __device__ __forceinline__ void range_index_body(int h, int part, int nparts,
         // the lowest peer (rank 0) advances the counter
         if (rank == 0) cnt[wave * R + (int)d] = (CT)(pos + __popcll(peers));
       }
+    }
+  };
+  if (resident) {
+#pragma unroll
+    for (int u = 0; u < kResTiles; ++u)
+      if (wbeg + u * kTile * FASTAR_WAVE < wend) scatter_tile(b[u], wbeg + u * kTile * FASTAR_WAVE);
+  } else {
+    for (int t0 = wbeg; t0 < wend; t0 += kTile * FASTAR_WAVE) {
+      load_tile(b[0], t0);
+      scatter_tile(b[0], t0);
     }
   }
 }
