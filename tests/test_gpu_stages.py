@@ -183,6 +183,9 @@ def test_hash_strided_input(fa):
                                    (20000, 13, 2), (70000, 13, 1), (93600, 12, 1), (66000, 3, 1),
                                    (5000, 15, 1), (70000, 14, 1), (65535, 15, 2), (70000, 15, 1),
                                    (40, 13, 1),
+                                   # range mode: every wave's slice in registers (two tiles,
+                                   # 1024 ids) and one id past it
+                                   (16384, 14, 1), (16385, 14, 2),
                                    # the radix fallback
                                    (3000, 2, 2)])
 def test_bucket_index_of_given_ids(fa, n, b, P):
