@@ -192,10 +192,23 @@ __device__ void scan_buckets(int nb, int32_t* st, int32_t* copy, int32_t* st2 = 
     // each wave scans a contiguous segment, 64 buckets per step (lane l:
     // bucket base + l: no bank conflicts, contiguous stores)
     const int seg = nb / nwv, b0 = wave * seg;
+    // four consecutive buckets per lane and step where the segment allows
+    const bool wide4 = seg % (4 * FASTAR_WAVE) == 0;
     int sum = 0, sum2 = 0;
-    for (int i = lane; i < seg; i += FASTAR_WAVE) {
-      sum += st[b0 + i];
-      if (st2) sum2 += st2[b0 + i];
+    if (wide4) {
+      for (int i = 4 * lane; i < seg; i += 4 * FASTAR_WAVE) {
+        const int4 v = *reinterpret_cast<const int4*>(st + b0 + i);
+        sum += v.x + v.y + v.z + v.w;
+        if (st2) {
+          const int4 v2 = *reinterpret_cast<const int4*>(st2 + b0 + i);
+          sum2 += v2.x + v2.y + v2.z + v2.w;
+        }
+      }
+    } else {
+      for (int i = lane; i < seg; i += FASTAR_WAVE) {
+        sum += st[b0 + i];
+        if (st2) sum2 += st2[b0 + i];
+      }
     }
     sum = wave_sum_dpp(sum);
     sum2 = wave_sum_dpp(sum2);
@@ -206,7 +219,26 @@ __device__ void scan_buckets(int nb, int32_t* st, int32_t* copy, int32_t* st2 = 
     lds_barrier();
     const int wt = lane < nwv ? wtot[0][lane] : 0, wt2 = lane < nwv ? wtot[1][lane] : 0;
     int carry = wave_sum_dpp(lane < wave ? wt : 0), carry2 = wave_sum_dpp(lane < wave ? wt2 : 0);
-    for (int i = 0; i < seg; i += FASTAR_WAVE) {
+    auto scan4 = [&](int32_t* a, int b, int& c, int32_t* cp) {
+      const int4 v = *reinterpret_cast<const int4*>(a + b);
+      const int l4 = v.x + v.y + v.z + v.w;
+      const int inc = (int)wave_incl_scan_dpp((uint32_t)l4);
+      const int base = c + inc - l4;
+      const int4 o = make_int4(base, base + v.x, base + v.x + v.y, base + v.x + v.y + v.z);
+      *reinterpret_cast<int4*>(a + b) = o;
+      if (cp) {
+        cp[b] = o.x;
+        cp[b + 1] = o.y;
+        cp[b + 2] = o.z;
+        cp[b + 3] = o.w;
+      }
+      c += __builtin_amdgcn_readlane(inc, FASTAR_WAVE - 1);
+    };
+    for (int i = 0; wide4 && i < seg; i += 4 * FASTAR_WAVE) {
+      scan4(st, b0 + i + 4 * lane, carry, copy);
+      if (st2) scan4(st2, b0 + i + 4 * lane, carry2, nullptr);
+    }
+    for (int i = 0; !wide4 && i < seg; i += FASTAR_WAVE) {
       const int b = b0 + i + lane;
       const int v = st[b];
       const int inc = (int)wave_incl_scan_dpp((uint32_t)v);
@@ -304,9 +336,14 @@ __device__ void csr_build(int nbits, const TabTok& tt, int32_t* lds, int32_t* of
   const int nb = 1 << nbits;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  for (int s = tid; s <= nb; s += nthr) {
-    lds[s] = 0;
-    if (tc) st[s] = 0;
+  // (lds and st are 16-byte aligned)
+  for (int s = 4 * tid; s < nb; s += 4 * nthr) {
+    *reinterpret_cast<int4*>(lds + s) = make_int4(0, 0, 0, 0);
+    if (tc) *reinterpret_cast<int4*>(st + s) = make_int4(0, 0, 0, 0);
+  }
+  if (tid == 0) {
+    lds[nb] = 0;
+    if (tc) st[nb] = 0;
   }
   lds_barrier();
 #pragma unroll
